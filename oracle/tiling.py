@@ -1,0 +1,293 @@
+"""Shape tiling, header, tile ranges and the element -> tile map
+(test infrastructure; an independent statement of the encoder's rules).
+
+Source: the DVM paper review page, section 4.2 (shape tiling: find the
+dominant shape S_d, start from the largest tile L = S_d, shrink tiles from the
+outer dims inward, prune candidates by hardware resource limits and a
+lightweight cost model; hardware_align_div takes the least-cost tile size and
+rounds it up to a multiple of the hardware instruction width), section 4.3
+(header: tile count block_dim, tiles per core body_tile, kernel type) and
+section 4.4 (each core computes its tile count and its tile range, then runs
+the bytecode per tile).  Section 7 of that page adds that tiling uses
+dedicated templates and needs no measurement on hardware.
+
+Readings taken where the page leaves a step open (each also listed in the
+design notes):
+
+* Iteration space.  The dominant shape is collapsed to two dims [R, C]: C is
+  the innermost dim, R the product of the outer dims.  Elementwise graphs whose
+  every operand is contiguous (or a scalar) collapse further to [1, numel].
+* Per-core resource.  A core is one workgroup of T = 256 lanes; a tile row is
+  spread over g lanes, each holding up to NV_MAX = 4 chunks of V = 8 elements
+  in registers.  Rows of a tile go to P = next_pow2(tr) lane groups of
+  g = T / P lanes.  A tile is feasible iff P <= T and
+  NV = ceil((tc + pad) / (g V)) <= NV_MAX.
+* Alignment pad.  pad = V - 1 if some unit-stride operand does not start every
+  row on a 16-byte boundary, else 0: a misaligned row may need one more chunk.
+* hardware_align_div(n, k, W) = W * ceil(ceil(n / k) / W) with W = 64 V = 512
+  (one wave of 16-byte vectors of the narrowest type), clamped to C.
+* Shrink path (outer -> inner).  Row-reduce graphs pin tc = C and try
+  tr = ceil(R / k) for k = 1, 2, 4, ... down to 1.  Elementwise and
+  reduce-all graphs first try tr = ceil(R / k) with the widest aligned tc,
+  then, at tr = 1, tc = min(C, had(C, k, W)) for k = 2, 4, ... until tc stops
+  changing or reaches W.  Consecutive duplicates are dropped.
+* Cost (integer "ticks", 1 tick = 1/31250 us): G = 512 resident workgroups
+  (two per compute unit), A = 15625 ticks (0.5 us) of fixed work per tile, and
+  2 ticks per byte a workgroup moves (8 TB/s shared by G workgroups):
+  cost = ceil(n_tiles / G) * (A + 2 * var_bytes) + 2 * inv_bytes, where
+  var_bytes are the bytes one tile touches in operands that change from tile
+  to tile and inv_bytes those of tile-invariant operands, loaded once per
+  workgroup.  The least cost wins; ties go to the earlier candidate (the
+  larger tile).
+* Header and ranges: block_dim = n_tiles; body_tile = ceil(block_dim / min(G,
+  block_dim)); grid = ceil(block_dim / body_tile); workgroup b owns tiles
+  [b body_tile, min((b + 1) body_tile, block_dim)).  Tile id -> (ir, ic) is
+  row-major with the column index fastest.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+T_LANES = 256
+VEC = 8
+NV_MAX = 4
+W_ALIGN = 64 * VEC
+G_WG = 512
+A_TICKS = 15625
+BYTE_TICKS = 2
+
+ELEMWISE, ROWREDUCE, ALLREDUCE, MATMUL = "elemwise", "rowreduce", "allreduce", "matmul"
+
+
+def cdiv(a: int, b: int) -> int:
+    return -(-a // b)
+
+
+def next_pow2(x: int) -> int:
+    p = 1
+    while p < x:
+        p *= 2
+    return p
+
+
+def had(n: int, k: int, w: int) -> int:
+    """hardware_align_div: ceil(n / k) rounded up to a multiple of w."""
+    return w * cdiv(cdiv(n, k), w)
+
+
+@dataclass
+class Operand:
+    """A global operand in the collapsed [R, C] space (strides in elements)."""
+    esize: int
+    s_r: int
+    s_c: int
+    base_mod16: int = 0
+
+
+@dataclass
+class Plan:
+    template: str
+    R: int
+    C: int
+    pad: int
+    path: list
+    tr: int = 0
+    tc: int = 0
+    g: int = 0
+    nv: int = 0
+    P: int = 0
+    n_r: int = 0
+    n_c: int = 0
+    block_dim: int = 0
+    body_tile: int = 0
+    grid: int = 0
+    costs: list = field(default_factory=list)
+
+
+# ---------------------------------------------------------------------------
+# Dim collapse
+# ---------------------------------------------------------------------------
+def _drop_unit(shape, strides):
+    keep = [i for i, d in enumerate(shape) if d != 1]
+    return [shape[i] for i in keep], [[s[i] for i in keep] for s in strides]
+
+
+def collapse(template, shape, op_strides):
+    """Collapse the dominant shape to [R, C].
+
+    ``op_strides``: per global operand, its strides over ``shape`` (0 on a
+    broadcast dim).  Returns (R, C, [(s_r, s_c)]) or None when some operand's
+    outer dims cannot be merged into one row index.
+    """
+    numel = 1
+    for d in shape:
+        numel *= d
+    if numel == 0:
+        return 0, 0, [(0, 0) for _ in op_strides]
+    dims, strides = _drop_unit(list(shape), [list(s) for s in op_strides])
+    if not dims:
+        return 1, 1, [(0, 0) for _ in op_strides]
+
+    def mergeable(s, lo, hi):
+        # dims lo..hi-1 of one operand merge into one index
+        return all(s[i] == s[i + 1] * dims[i + 1] for i in range(lo, hi - 1))
+
+    if template in (ELEMWISE, ALLREDUCE) and all(mergeable(s, 0, len(dims)) for s in strides):
+        return 1, numel, [(0, s[-1]) for s in strides]
+    # two dims: innermost dim of the dominant shape (even if it has size 1)
+    C = shape[-1] if len(shape) else 1
+    if C == 1:
+        outer_dims = dims
+        outer_strides = strides
+    else:
+        outer_dims = dims[:-1]
+        outer_strides = [s[:-1] for s in strides]
+    R = 1
+    for d in outer_dims:
+        R *= d
+    out = []
+    for s_full, s in zip(strides, outer_strides):
+        if not all(s[i] == s[i + 1] * outer_dims[i + 1] for i in range(len(outer_dims) - 1)):
+            return None
+        s_r = s[-1] if outer_dims else 0
+        s_c = s_full[-1] if C != 1 else 0
+        out.append((s_r, s_c))
+    return R, C, out
+
+
+# ---------------------------------------------------------------------------
+# Geometry, path, cost, choice
+# ---------------------------------------------------------------------------
+def alignment_pad(R: int, ops) -> int:
+    for o in ops:
+        if o.s_c != 1:
+            continue
+        if o.base_mod16 % 16 != 0:
+            return VEC - 1
+        if R > 1 and (o.s_r * o.esize) % 16 != 0:
+            return VEC - 1
+    return 0
+
+
+def geometry(tr: int, tc: int, pad: int):
+    """(P, g, NV, feasible) of a tr x tc tile."""
+    P = next_pow2(tr)
+    if P > T_LANES:
+        return P, 0, 0, False
+    g = T_LANES // P
+    nv = cdiv(tc + pad, g * VEC)
+    return P, g, nv, nv <= NV_MAX
+
+
+def shrink_path(template: str, R: int, C: int):
+    path = []
+
+    def push(t):
+        if not path or path[-1] != t:
+            path.append(t)
+
+    if template == ROWREDUCE:
+        k = 1
+        while True:
+            tr = cdiv(R, k)
+            push((tr, C))
+            if tr <= 1:
+                break
+            k *= 2
+        return path
+    tc0 = min(C, had(C, 1, W_ALIGN))
+    k = 1
+    while True:
+        tr = cdiv(R, k)
+        push((tr, tc0))
+        if tr <= 1:
+            break
+        k *= 2
+    prev = tc0
+    k = 2
+    while prev > W_ALIGN:
+        tc = min(C, had(C, k, W_ALIGN))
+        if tc == prev:
+            break
+        push((1, tc))
+        prev = tc
+        k *= 2
+    return path
+
+
+def cost(R: int, C: int, tr: int, tc: int, ops) -> int:
+    n_r, n_c = cdiv(R, tr), cdiv(C, tc)
+    n_tiles = n_r * n_c
+    var_b, inv_b = 0, 0
+    for o in ops:
+        touched = (tr if o.s_r != 0 else 1) * (tc if o.s_c != 0 else 1) * o.esize
+        invariant = (o.s_r == 0 or n_r == 1) and (o.s_c == 0 or n_c == 1)
+        if invariant:
+            inv_b += touched
+        else:
+            var_b += touched
+    rounds = cdiv(n_tiles, G_WG)
+    return rounds * (A_TICKS + BYTE_TICKS * var_b) + BYTE_TICKS * inv_b
+
+
+def plan(template: str, R: int, C: int, ops) -> Plan:
+    """Tile choice and header for a vector-template graph over [R, C]."""
+    pad = alignment_pad(R, ops)
+    p = Plan(template, R, C, pad, [])
+    if R == 0 or C == 0:
+        return p
+    p.path = shrink_path(template, R, C)
+    best = None
+    for (tr, tc) in p.path:
+        P, g, nv, ok = geometry(tr, tc, pad)
+        if not ok:
+            p.costs.append(None)
+            continue
+        c = cost(R, C, tr, tc, ops)
+        p.costs.append(c)
+        if best is None or c < best[0]:
+            best = (c, tr, tc, P, g, nv)
+    if best is None:
+        raise ValueError("no feasible tile")
+    _, p.tr, p.tc, p.P, p.g, p.nv = best
+    p.n_r, p.n_c = cdiv(R, p.tr), cdiv(C, p.tc)
+    p.block_dim = p.n_r * p.n_c
+    p.body_tile, p.grid = header(p.block_dim)
+    return p
+
+
+def header(block_dim: int):
+    if block_dim == 0:
+        return 0, 0
+    gp = min(G_WG, block_dim)
+    body_tile = cdiv(block_dim, gp)
+    grid = cdiv(block_dim, body_tile)
+    return body_tile, grid
+
+
+def tile_range(b: int, body_tile: int, block_dim: int):
+    """[begin, end) tile ids owned by workgroup b."""
+    return b * body_tile, min((b + 1) * body_tile, block_dim)
+
+
+def tile_box(tile_id: int, tr: int, tc: int, R: int, C: int, n_c: int):
+    ir, ic = divmod(tile_id, n_c)
+    return (ir * tr, min(ir * tr + tr, R)), (ic * tc, min(ic * tc + tc, C))
+
+
+def element_tile_map(p: Plan):
+    """For every element (r, c) of [R, C]: the id of the tile that holds it
+    and the workgroup that runs that tile, built by walking every tile's box
+    (no closed form, so it checks coverage independently)."""
+    import numpy as np
+    tiles = np.full((p.R, p.C), -1, dtype=np.int64)
+    wgs = np.full((p.R, p.C), -1, dtype=np.int64)
+    for b in range(p.grid):
+        lo, hi = tile_range(b, p.body_tile, p.block_dim)
+        for t in range(lo, hi):
+            (r0, r1), (c0, c1) = tile_box(t, p.tr, p.tc, p.R, p.C, p.n_c)
+            if (tiles[r0:r1, c0:c1] != -1).any():
+                raise AssertionError("element covered twice")
+            tiles[r0:r1, c0:c1] = t
+            wgs[r0:r1, c0:c1] = b
+    return tiles, wgs

@@ -1,0 +1,129 @@
+"""Pins for oracle/tiling.py: hand-worked shrink paths and choices, geometry
+limits, dim collapse cases, coverage by brute force, and the header/range
+invariants (no GPU)."""
+import numpy as np
+import pytest
+
+from oracle import tiling as TL
+from oracle.tiling import Operand
+
+
+def f32(s_r=0, s_c=1):
+    return Operand(4, s_r, s_c, 0)
+
+
+def test_had():
+    assert TL.had(528903, 2, 512) == 264704
+    assert TL.had(528903, 2048, 512) == 512
+    assert TL.had(1000, 1, 512) == 1024
+    assert TL.had(7, 3, 1) == 3
+
+
+def test_sqrt_add_workload_choice_by_hand():
+    # c = sqrt(a + b) over (513, 1031) fp32, three contiguous operands
+    R, C, st = TL.collapse(TL.ELEMWISE, (513, 1031), [(1031, 1)] * 3)
+    assert (R, C) == (1, 528903) and st == [(0, 1)] * 3
+    ops = [Operand(4, s, c) for s, c in st]
+    p = TL.plan(TL.ELEMWISE, R, C, ops)
+    assert [tc for _, tc in p.path] == [528903, 264704, 132608, 66560, 33280, 16896, 8704,
+                                        4608, 2560, 1536, 1024, 512]
+    # costs worked by hand: rounds * (15625 + 2*12*tc) for the feasible tail
+    assert p.costs[7:] == [126217, 77065, 52489, 80402, 83739]
+    assert p.costs[:7] == [None] * 7
+    assert (p.tr, p.tc, p.block_dim, p.body_tile, p.grid) == (1, 1536, 345, 1, 345)
+    assert (p.P, p.g, p.nv, p.pad) == (1, 256, 1, 0)
+
+
+def test_layernorm_rows_choice_by_hand():
+    x = Operand(2, 5120, 1)
+    y = Operand(2, 5120, 1)
+    gam = Operand(4, 0, 1)
+    bet = Operand(4, 0, 1)
+    p = TL.plan(TL.ROWREDUCE, 1000, 5120, [x, gam, bet, y])
+    assert [tr for tr, _ in p.path] == [1000, 500, 250, 125, 63, 32, 16, 8, 4, 2, 1]
+    assert p.costs[:-1] == [None] * 10          # 2+ rows of 5120 need > 4 chunks per lane
+    assert p.costs[-1] == 2 * (15625 + 2 * 20480) + 2 * 40960
+    assert (p.tr, p.tc, p.block_dim, p.body_tile, p.grid, p.g, p.nv) == (1, 5120, 1000, 2, 500, 256, 3)
+
+
+def test_softmax_misaligned_rows_by_hand():
+    s = Operand(2, 3001, 1)
+    o = Operand(2, 3001, 1)
+    assert TL.alignment_pad(280, [s, o]) == 7
+    assert TL.geometry(2, 3001, 7) == (2, 128, 3, True)
+    assert TL.geometry(3, 3001, 7) == (4, 64, 6, False)
+    p = TL.plan(TL.ROWREDUCE, 280, 3001, [s, o])
+    assert p.tr == 1 and p.block_dim == 280
+    p = TL.plan(TL.ROWREDUCE, 4000, 3001, [s, o])
+    # tr=2: 2000 tiles, 4 rounds of (15625 + 2*2*3001*2*2); tr=1: 8 rounds of (15625 + 2*12004)
+    i2 = [tr for tr, _ in p.path].index(2)
+    assert p.costs[i2] == 4 * 63641 and p.costs[-1] == 8 * 39633
+    assert p.tr == 2 and p.block_dim == 2000
+
+
+def test_feasibility_edges():
+    assert TL.geometry(1, 8192, 0)[3] is True
+    assert TL.geometry(1, 8192, 7)[3] is False
+    assert TL.geometry(1, 8185, 7)[3] is True
+    assert TL.geometry(256, 8, 0) == (256, 1, 1, True)
+    assert TL.geometry(257, 8, 0)[3] is False
+    with pytest.raises(ValueError):
+        TL.plan(TL.ROWREDUCE, 10, 8192, [Operand(2, 8193, 1)])   # misaligned 8192-wide rows
+
+
+def test_alignment_pad_rules():
+    assert TL.alignment_pad(5, [Operand(4, 4, 1)]) == 0        # 16-byte rows
+    assert TL.alignment_pad(5, [Operand(4, 6, 1)]) == 7        # 24-byte rows
+    assert TL.alignment_pad(1, [Operand(4, 6, 1)]) == 0        # a single row
+    assert TL.alignment_pad(5, [Operand(2, 8, 1, 4)]) == 7      # base off by 4 bytes
+    assert TL.alignment_pad(5, [Operand(2, 3, 7)]) == 0        # strided inner: element path
+
+
+def test_collapse_cases():
+    # [C] broadcast operand keeps two dims
+    assert TL.collapse(TL.ELEMWISE, (4, 6), [(6, 1), (0, 1)]) == (4, 6, [(6, 1), (0, 1)])
+    # swapped outer dims cannot merge
+    assert TL.collapse(TL.ROWREDUCE, (4, 6, 8), [(8, 32, 1)]) is None
+    # unit dims dropped; contiguous -> 1-D
+    assert TL.collapse(TL.ELEMWISE, (1, 4, 1, 6), [(24, 6, 6, 1)]) == (1, 24, [(0, 1)])
+    # row reduce over a 3-D shape, with a [.., 1] row output
+    assert TL.collapse(TL.ROWREDUCE, (2, 3, 5), [(15, 5, 1), (3, 1, 0)]) == (6, 5, [(5, 1), (1, 0)])
+    # scalar operand
+    assert TL.collapse(TL.ELEMWISE, (3, 3), [(3, 1), (0, 0)]) == (1, 9, [(0, 1), (0, 0)])
+    # empty
+    assert TL.collapse(TL.ELEMWISE, (0, 5), [(5, 1)])[:2] == (0, 0)
+
+
+def test_coverage_and_ranges_brute_force():
+    g = np.random.default_rng(7)
+    for _ in range(40):
+        tmpl = [TL.ELEMWISE, TL.ROWREDUCE][int(g.integers(0, 2))]
+        R = int(g.integers(1, 700))
+        C = int(g.integers(1, 3000))
+        if tmpl == TL.ELEMWISE and g.random() < 0.5:
+            R, C = 1, R * C
+        ops = [Operand(4, C if R > 1 else 0, 1), Operand(2, 0, 1)]
+        p = TL.plan(tmpl, R, C, ops)
+        tiles, wgs = TL.element_tile_map(p)
+        assert (tiles >= 0).all()
+        # workgroup ranges are contiguous, disjoint and cover [0, block_dim)
+        seen = []
+        for b in range(p.grid):
+            lo, hi = TL.tile_range(b, p.body_tile, p.block_dim)
+            assert 0 < hi - lo <= p.body_tile
+            seen.extend(range(lo, hi))
+        assert seen == list(range(p.block_dim))
+        assert p.grid <= TL.G_WG
+        # the choice is a least-cost feasible candidate, earliest on ties
+        feas = [(c, i) for i, c in enumerate(p.costs) if c is not None]
+        cmin = min(c for c, _ in feas)
+        first = min(i for c, i in feas if c == cmin)
+        assert p.path[first] == (p.tr, p.tc)
+
+
+def test_header_formula_cases():
+    assert TL.header(0) == (0, 0)
+    assert TL.header(1) == (1, 1)
+    assert TL.header(512) == (1, 512)
+    assert TL.header(513) == (2, 257)
+    assert TL.header(1025) == (3, 342)
