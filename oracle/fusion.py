@@ -35,8 +35,9 @@ Readings taken (the pages give only "shape compatibility and dependence"):
   write storage the buffered graph may still write (WAW).  A value is carried
   on chip only when the consumer names the producer's value.
 * Resources (F7): at most 64 ops; at most 24 distinct external tensors; at
-  every op at most 4 tile-shaped values in flight (live values plus the op's
-  output) and at most 4 row values in flight; and a feasible tile exists.
+  every op at most 3 tile-shaped values in flight (live values plus the op's
+  output: the device keeps a tile in at most three register sets) and at most
+  4 row values in flight; and a feasible tile exists.
 * A value is stored when its graph is flushed if it is marked live, or if the
   caller has not released it by then.
 """
@@ -48,7 +49,7 @@ from . import tiling as TL
 
 MAX_OPS = 64
 MAX_EXT = 24
-MAX_TILE_VALUES = 4
+MAX_TILE_VALUES = 3
 MAX_ROW_VALUES = 4
 
 ESIZE = {"f32": 4, "bf16": 2, "u8": 1}

@@ -111,22 +111,24 @@ def test_resource_limits():
     graphs = Stream().run(ev)
     assert [len(g[0]) for g in graphs] == [64, 1]
     assert graphs[0][1] == "resource"
-    # five tile values in flight at once exceed the register slots
+    # more than three tile values in flight exceed the device's tile registers
     ev = [inp(f"x{i}", sh, "f32", i * MB) for i in range(5)]
-    grp = [op("add", ["x0", "x1"], "a", sh), op("add", ["x2", "x3"], "b", sh),
-           op("add", ["x4", "a"], "c", sh), op("add", ["c", "b"], "d", sh, live=True, addr=9 * MB)]
     s = Stream()
-    s.run(ev + [("group", grp[:2])])
-    # a, b live; adding x4 + a: live {a, b, x4} + output c = 4 -> fits
-    assert s.demand(grp, (2, 512))["tile"] == 4
-    grp2 = [op("add", ["x0", "x1"], "a", sh), op("add", ["x2", "x3"], "b", sh),
-            op("mul", ["x4", 2.0], "c", sh), op("add", ["a", "b"], "d", sh),
-            op("add", ["d", "c"], "e", sh), op("add", ["e", "x4"], "f", sh, live=True, addr=9 * MB)]
-    # at op 2: a, b, x4 live + output c = 4; at op 3: a, b, c, x4 live + d = 5
-    assert s.demand(grp2, (2, 512))["tile"] == 5
+    s.run(ev)
+    chain = [op("add", ["x0", "x1"], "a", sh), op("mul", ["a", "x2"], "b", sh),
+             op("add", ["b", 1.0], "c", sh, live=True, addr=9 * MB)]
+    # op 0: x0, x1 live + a = 3; op 1: a, x2 + b = 3; op 2: b + c = 2
+    assert s.demand(chain, sh)["tile"] == 3
+    grp = [op("add", ["x0", "x1"], "a", sh), op("add", ["x2", "x3"], "b", sh),
+           op("add", ["a", "b"], "d", sh, live=True, addr=9 * MB)]
+    # at op 1: a, x2, x3 live + output b = 4
+    assert s.demand(grp, sh)["tile"] == 4
     s2 = Stream()
-    s2.run(ev + [("group", grp2)])
+    s2.run(ev + [("group", grp)])
     assert s2.unsupported and s2.unsupported[0][1] == "resource"
+    s3 = Stream()
+    s3.run(ev + [("group", chain), ("release", "a"), ("release", "b"), ("flush",)])
+    assert len(s3.graphs) == 1 and not s3.unsupported
 
 
 def test_matmul_only_first_and_epilogue_fuses():
