@@ -1,0 +1,282 @@
+"""MI355X-native DVM hot path: streaming fuser, tile-level bytecode encoder and
+resident VM kernels, behind the C ABI of include/dvm.h.
+
+This package is a thin binding: argument marshalling only.  PyTorch supplies
+device memory and streams.  Every computation runs in libdvm.so (host C++ for
+fusion, tiling and encoding; HIP kernels on gfx950 for execution).
+"""
+from __future__ import annotations
+
+import contextlib
+import ctypes as C
+from dataclasses import dataclass
+
+from . import _lib as L
+from ._lib import DvmError, check, lib
+
+__all__ = ["Context", "Graph", "Program", "Value", "TensorDesc", "DvmError", "lib"]
+
+
+@dataclass
+class TensorDesc:
+    """A tensor described without torch: device address, dtype name, shape and
+    element strides (used by encode-only callers and tests)."""
+    addr: int
+    dtype: str
+    shape: tuple
+    strides: tuple = None
+
+    def __post_init__(self):
+        self.shape = tuple(int(d) for d in self.shape)
+        if self.strides is None:
+            st, acc = [], 1
+            for d in reversed(self.shape):
+                st.append(acc)
+                acc *= d
+            self.strides = tuple(reversed(st))
+        self.strides = tuple(int(s) for s in self.strides)
+
+
+def _torch_dtype_code(t):
+    import torch
+    m = {torch.float32: L.F32, torch.bfloat16: L.BF16, torch.uint8: L.U8}
+    if t.dtype not in m:
+        raise TypeError(f"unsupported dtype {t.dtype}")
+    return m[t.dtype]
+
+
+def to_c(t, dtype=None, shape=None) -> L.DvmTensor:
+    """dvm_tensor from a torch tensor, a TensorDesc, or (None, dtype, shape)."""
+    d = L.DvmTensor()
+    if t is None:
+        d.data = None
+        d.dtype = L.DTYPE_CODES[dtype]
+        shape = tuple(shape)
+        d.ndim = len(shape)
+        acc = 1
+        for i in range(len(shape) - 1, -1, -1):
+            d.shape[i] = shape[i]
+            d.stride[i] = acc
+            acc *= shape[i]
+        return d
+    if isinstance(t, TensorDesc):
+        d.data = t.addr or None
+        d.dtype = L.DTYPE_CODES[t.dtype]
+        d.ndim = len(t.shape)
+        for i, (n, s) in enumerate(zip(t.shape, t.strides)):
+            d.shape[i] = n
+            d.stride[i] = s
+        return d
+    d.data = t.data_ptr() or None
+    d.dtype = _torch_dtype_code(t)
+    d.ndim = t.dim()
+    if d.ndim > 4:
+        raise ValueError("at most 4 dims")
+    for i in range(t.dim()):
+        d.shape[i] = t.shape[i]
+        d.stride[i] = t.stride(i)
+    return d
+
+
+class Context:
+    """device >= 0: launches on that HIP device; device < 0: encode-only."""
+
+    def __init__(self, device: int = 0):
+        h = C.c_void_p()
+        check(lib.dvm_context_create(int(device), C.byref(h)))
+        self.h = h
+        self.device = device
+
+    def close(self):
+        if self.h:
+            lib.dvm_context_destroy(self.h)
+            self.h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+@dataclass
+class Value:
+    h: int
+    shape: tuple
+    dtype: str
+    storage: object = None  # keeps the storage tensor alive
+
+
+class Program:
+    def __init__(self, h, ctx):
+        self.h = h
+        self.ctx = ctx
+
+    def header(self) -> dict:
+        hd = L.DvmHeader()
+        check(lib.dvm_program_header(self.h, C.byref(hd)))
+        return {f: getattr(hd, f) for f, _ in L.DvmHeader._fields_}
+
+    def words(self) -> list:
+        n = C.c_size_t(0)
+        check(lib.dvm_program_words(self.h, None, C.byref(n)))
+        buf = (C.c_uint32 * n.value)()
+        cap = C.c_size_t(n.value)
+        check(lib.dvm_program_words(self.h, buf, C.byref(cap)))
+        return list(buf)
+
+    def launch(self, stream=None):
+        check(lib.dvm_launch(self.ctx.h, self.h, _stream_handle(stream)))
+
+    def debug_tilemap(self, tile_out, wg_out) -> "Program":
+        q = C.c_void_p()
+        a, b = to_c(tile_out), to_c(wg_out)
+        check(lib.dvm_program_debug_tilemap(self.h, C.byref(a), C.byref(b), C.byref(q)))
+        return Program(q, self.ctx)
+
+    def __del__(self):
+        try:
+            if self.h:
+                lib.dvm_program_free(self.h)
+                self.h = None
+        except Exception:
+            pass
+
+
+def _stream_handle(stream):
+    if stream is None:
+        try:
+            import torch
+            if torch.cuda.is_available():
+                return C.c_void_p(torch.cuda.current_stream().cuda_stream)
+        except Exception:
+            pass
+        return None
+    if isinstance(stream, int):
+        return C.c_void_p(stream)
+    return C.c_void_p(stream.cuda_stream)
+
+
+class Graph:
+    """A streaming fusion buffer (DVM: capture ops in order, fuse while the
+    conditions hold, flush at boundaries) bound to a stream."""
+
+    def __init__(self, ctx: Context, stream=None):
+        self.ctx = ctx
+        h = C.c_void_p()
+        self._stream = _stream_handle(stream) if ctx.device >= 0 else None
+        check(lib.dvm_graph_create(ctx.h, self._stream, C.byref(h)))
+        self.h = h
+        self._in_group = False
+        self.flushes = 0
+
+    def close(self):
+        if self.h:
+            lib.dvm_graph_destroy(self.h)
+            self.h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    # -- values ----------------------------------------------------------
+    def input(self, t) -> Value:
+        d = to_c(t)
+        v = C.c_int64()
+        check(lib.dvm_graph_input(self.h, C.byref(d), C.byref(v)))
+        shape = tuple(d.shape[i] for i in range(d.ndim))
+        return Value(v.value, shape, L.DTYPE_NAMES[d.dtype], t)
+
+    def infer_shape(self, name, *ins, axis=-1):
+        hs, n_in, attrs = self._inputs(name, ins, axis)
+        out = L.DvmTensor()
+        check(lib.dvm_graph_infer_shape(self.h, L.OP_CODES[name], hs, n_in, C.byref(attrs), C.byref(out)))
+        return tuple(out.shape[i] for i in range(out.ndim))
+
+    def _inputs(self, name, ins, axis):
+        attrs = L.DvmAttrs(axis, -1, 0.0)
+        vals = []
+        for pos, x in enumerate(ins):
+            if isinstance(x, Value):
+                vals.append(x.h)
+            else:
+                if name not in L.BINARY or attrs.scalar_pos != -1:
+                    raise TypeError(f"{name}: scalar operand not allowed here")
+                attrs.scalar_pos = pos
+                attrs.scalar = float(x)
+        hs = (C.c_int64 * max(len(vals), 1))(*vals)
+        return hs, len(vals), attrs
+
+    def op(self, name, *ins, out=None, dtype=None, live=False, axis=-1) -> Value:
+        """Append a primitive op.  ins: Values or one python float (binary ops).
+        out: storage (torch tensor / TensorDesc) or None (no storage; the value
+        must be released before its graph is flushed)."""
+        hs, n_in, attrs = self._inputs(name, ins, axis)
+        if out is None:
+            shape = self.infer_shape(name, *ins, axis=axis)
+            if dtype is None:
+                dtype = "u8" if name == "isfinite" else next(x.dtype for x in ins if isinstance(x, Value))
+            d = to_c(None, dtype, shape)
+        else:
+            d = to_c(out)
+            shape = tuple(d.shape[i] for i in range(d.ndim))
+            dtype = L.DTYPE_NAMES[d.dtype]
+        v = C.c_int64()
+        st = lib.dvm_graph_add_op(self.h, L.OP_CODES[name], hs, n_in, C.byref(attrs), C.byref(d),
+                                  L.OUT_LIVE if live else 0, C.byref(v))
+        check(st)
+        return Value(v.value, shape, dtype, out)
+
+    def release(self, *vals):
+        for v in vals:
+            check(lib.dvm_graph_release(self.h, v.h))
+
+    @contextlib.contextmanager
+    def group(self):
+        check(lib.dvm_graph_begin_group(self.h))
+        self._in_group = True
+        try:
+            yield self
+        finally:
+            self._in_group = False
+            fl = C.c_int32(0)
+            check(lib.dvm_graph_end_group(self.h, C.byref(fl)))
+            self.flushes += fl.value
+
+    # -- flushing --------------------------------------------------------
+    def flush(self):
+        """Encode the buffered graph (no launch); returns a Program or None."""
+        q = C.c_void_p()
+        check(lib.dvm_flush(self.h, C.byref(q)))
+        return Program(q, self.ctx) if q.value else None
+
+    def flush_launch(self) -> bool:
+        fl = C.c_int32(0)
+        check(lib.dvm_graph_flush_launch(self.h, C.byref(fl)))
+        return bool(fl.value)
+
+    def sync(self):
+        check(lib.dvm_sync(self.h))
+
+    def flush_log(self) -> list:
+        """[(n_ops, reason name)] for every graph flushed so far."""
+        n = C.c_size_t(0)
+        check(lib.dvm_graph_flush_log(self.h, None, None, C.byref(n)))
+        k = n.value
+        ops = (C.c_int32 * max(k, 1))()
+        rs = (C.c_int32 * max(k, 1))()
+        cap = C.c_size_t(k)
+        check(lib.dvm_graph_flush_log(self.h, ops, rs, C.byref(cap)))
+        return [(ops[i], L.FLUSH_REASONS[rs[i]]) for i in range(k)]
+
+    def stats(self) -> dict:
+        s = L.DvmStats()
+        check(lib.dvm_graph_stats(self.h, C.byref(s)))
+        return {
+            "graphs": s.graphs, "launches": s.launches, "ops": s.ops, "groups": s.groups,
+            "unsupported": s.unsupported,
+            "flush_reason": {L.FLUSH_REASONS[i]: s.flush_reason[i] for i in range(7)},
+            "encode_us_total": s.encode_us_total, "encode_us_max": s.encode_us_max,
+        }

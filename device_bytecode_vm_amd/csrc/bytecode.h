@@ -1,0 +1,141 @@
+// Tile-level bytecode program format shared by the host encoder and the
+// device VM kernels.
+//
+// A program is one flat array of 32-bit words that travels to the device as
+// the VM kernel's argument (the kernarg segment), so the kernel reads it with
+// wave-uniform scalar loads.  Layout:
+//
+//   words [0, HDR_WORDS)                  code header
+//   words [ARG_BASE, ARG_BASE + 8 n_args) argument table (global operands)
+//   words [instr_base, ...)               code body, 2 words per instruction
+//
+// The header holds the fields the DVM paper review page names for its code
+// header (section 4.3: tile count block_dim, tiles per core body_tile, kernel
+// type) plus the tile geometry the VM needs; the body holds one instruction
+// per tile-level virtual instruction (Table 1 of that page: Load/Store, Copy,
+// Broadcast, elementwise ops; plus the binary ops, reductions and the syncs
+// the encoder inserts).
+#pragma once
+#include <stdint.h>
+
+namespace dvmbc {
+
+constexpr uint32_t MAGIC = 0x314d5644u;  // "DVM1"
+constexpr uint32_t VERSION = 1;
+
+// Device geometry constants: one workgroup of T lanes runs a tile; a tile row
+// is spread over g lanes, each holding up to NV_MAX chunks of V elements.
+constexpr int T_LANES = 256;
+constexpr int VEC = 8;
+constexpr int NV_MAX = 4;
+constexpr int E_MAX = VEC * NV_MAX;   // elements per lane per tile register
+constexpr int N_TREG = 3;             // tile registers: 0 = ACC, 1..2 slots
+constexpr int N_RREG = 4;             // row registers
+constexpr int N_LDSBUF = 8;           // cross-wave reduction buffers
+constexpr int MAX_WORDS = 1000;       // whole program, <= 4000 bytes of kernarg
+constexpr int HDR_WORDS = 32;
+constexpr int ARG_BASE = HDR_WORDS;
+constexpr int ARG_WORDS = 8;
+constexpr int MAX_ARGS = 32;
+
+enum KernelType : uint32_t { KT_VECTOR = 0, KT_MIX = 1 };
+enum Template : uint32_t { TM_ELEMWISE = 0, TM_ROWREDUCE = 1, TM_ALLREDUCE = 2, TM_MATMUL = 3 };
+
+// Header word offsets.
+enum Hdr : int {
+  H_MAGIC = 0,
+  H_VERSION = 1,
+  H_KTYPE = 2,
+  H_TEMPLATE = 3,
+  H_BLOCK_DIM = 4,   // number of tiles
+  H_BODY_TILE = 5,   // tiles per workgroup
+  H_GRID = 6,        // workgroups launched
+  H_TR = 7,          // tile rows
+  H_TC = 8,          // tile columns
+  H_G = 9,           // lanes per tile row
+  H_NV = 10,         // chunks per lane
+  H_P = 11,          // lane groups (rows) per workgroup
+  H_NC = 12,         // column tiles
+  H_NARGS = 13,
+  H_PRO_BEGIN = 14,  // prologue (tile-invariant) instruction word range
+  H_PRO_END = 15,
+  H_BODY_BEGIN = 16, // per-tile instruction word range
+  H_BODY_END = 17,
+  H_R_LO = 18,
+  H_R_HI = 19,
+  H_C_LO = 20,
+  H_C_HI = 21,
+  H_ALL_KIND = 22,   // reduce-all: 0 sum, 1 max
+  H_ALL_OUT = 23,    // reduce-all: arg index of the scalar output
+  H_ALL_SCRATCH = 24,// reduce-all: arg index of the scratch (counter + partials)
+  H_N_INSTR = 25,
+  H_FLAGS = 26,
+};
+
+// Argument table entry (8 words): pointer, dtype, flags, column stride, row
+// stride (elements, in the collapsed [R, C] iteration space) and the byte
+// extent of the tensor (one past its last element), which bounds every access
+// the VM makes to it.
+enum ArgW : int { A_PTR_LO = 0, A_PTR_HI = 1, A_DTYPE = 2, A_FLAGS = 3, A_SR_LO = 4, A_SR_HI = 5,
+                  A_SC = 6, A_EXTENT = 7 };
+// The extent word holds min(extent, 2^31) - the VM addresses one tile through a
+// buffer resource with 32-bit lane offsets, so a tile must span < 2^31 bytes.
+constexpr uint32_t EXTENT_CAP = 0x80000000u;
+enum DType : uint32_t { DT_F32 = 0, DT_BF16 = 1, DT_U8 = 2 };
+enum ArgFlag : uint32_t {
+  AF_VEC = 1u,       // every full chunk is 16-byte aligned: 128-bit path
+};
+
+// Opcodes (bits [7:0] of word 0).
+enum Op : uint32_t {
+  OP_END = 0,
+  OP_LOAD = 1,       // treg[dst] <- arg[w1] tile           (Load / ViewLoad)
+  OP_LOAD_ROW = 2,   // rreg[dst] <- arg[w1] row value
+  OP_STORE = 3,      // arg[w1] <- treg[a] tile              (Store / ViewStore)
+  OP_STORE_ROW = 4,  // arg[w1] <- rreg[a]
+  OP_COPY = 5,       // treg[dst] <- treg[a]                 (Copy)
+  OP_BIN = 6,        // treg[0] <- treg[0] (op) B, or B (op) treg[0]
+  OP_UN = 7,         // treg[0] <- f(treg[0])
+  OP_RBIN = 8,       // rreg[dst] <- rreg[a] (op) (rreg[b] | imm)
+  OP_RUN = 9,        // rreg[dst] <- f(rreg[a])
+  OP_RED = 10,       // row reduce of treg[a]: rreg[dst] (and LDS buffer b if the row spans waves)
+  OP_RED_FIN = 11,   // rreg[dst] <- combine of LDS buffer b for this lane's row
+  OP_SYNC = 12,      // workgroup barrier inserted by the encoder
+  OP_ALL = 13,       // reduce-all partial of treg[a] into LDS buffer b
+  OP_ALL_FIN = 14,   // tile partial from LDS buffer b -> scratch[tile]
+  OP_BCAST = 15,     // treg[dst] <- rreg[a] broadcast along the row (Broadcast)
+  OP_DBG = 16,       // treg[dst] <- tile id (sub 0) / workgroup id (sub 1)
+  OP_COUNT
+};
+
+// ALU sub-ops (bits [23:20]).
+enum Alu : uint32_t {
+  ALU_ADD = 0, ALU_SUB = 1, ALU_MUL = 2, ALU_DIV = 3, ALU_MAX = 4, ALU_MIN = 5, ALU_POW = 6,
+};
+enum Una : uint32_t {
+  UN_SQRT = 0, UN_ABS = 1, UN_LOG = 2, UN_EXP = 3, UN_ROUND = 4, UN_FLOOR = 5, UN_ISFINITE = 6,
+  UN_NEG = 7, UN_RECIP = 8, UN_TOBF16 = 9, UN_IDENT = 10,
+};
+enum BKind : uint32_t { BK_TREG = 0, BK_RREG = 1, BK_IMM = 2, BK_MEM = 3 };  // BK_MEM: B loaded from arg[w1]
+enum RedKind : uint32_t { RK_SUM = 0, RK_MAX = 1 };
+
+// Word 0 fields.
+__host__ __device__ constexpr uint32_t enc0(uint32_t op, uint32_t dst, uint32_t a, uint32_t b,
+                                            uint32_t sub, uint32_t bk, uint32_t flags) {
+  return (op & 0xffu) | ((dst & 0xfu) << 8) | ((a & 0xfu) << 12) | ((b & 0xfu) << 16) |
+         ((sub & 0xfu) << 20) | ((bk & 0xfu) << 24) | ((flags & 0xfu) << 28);
+}
+__host__ __device__ constexpr uint32_t f_op(uint32_t w) { return w & 0xffu; }
+__host__ __device__ constexpr uint32_t f_dst(uint32_t w) { return (w >> 8) & 0xfu; }
+__host__ __device__ constexpr uint32_t f_a(uint32_t w) { return (w >> 12) & 0xfu; }
+__host__ __device__ constexpr uint32_t f_b(uint32_t w) { return (w >> 16) & 0xfu; }
+__host__ __device__ constexpr uint32_t f_sub(uint32_t w) { return (w >> 20) & 0xfu; }
+__host__ __device__ constexpr uint32_t f_bk(uint32_t w) { return (w >> 24) & 0xfu; }
+__host__ __device__ constexpr uint32_t f_flags(uint32_t w) { return (w >> 28) & 0xfu; }
+constexpr uint32_t FL_REV = 1u;  // BIN: B (op) ACC instead of ACC (op) B
+
+struct Program {
+  uint32_t w[MAX_WORDS];
+};
+
+}  // namespace dvmbc

@@ -1,0 +1,1597 @@
+// Host side of the DVM hot path: streaming fuser, shape tiling, bytecode
+// encoder and the C ABI declared in include/dvm.h.
+//
+// Sources: the DVM paper review page (section 4.2 shape tiling, 4.3 bytecode
+// format, 4.4 VM execution, 5.1 pattern fusion, 5.2 dynamic-graph streaming
+// fusion) and the MindSpore DVM summary page (sections 3.2-3.3: runtime
+// capture, flush at unsupported ops / fusion boundaries / sync interfaces).
+// The readings taken where the pages are silent are stated next to the code.
+#include <hip/hip_runtime_api.h>
+
+#include <algorithm>
+#include <array>
+#include <chrono>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "bytecode.h"
+#include "dvm.h"
+
+using namespace dvmbc;
+
+extern "C" hipError_t dvm_launch_vector_kernel(const Program* p, unsigned grid, hipStream_t s);
+
+namespace {
+
+thread_local std::string g_err;
+
+dvm_status fail(dvm_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return s;
+}
+
+int esize(int32_t dt) { return dt == DVM_F32 ? 4 : dt == DVM_BF16 ? 2 : 1; }
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// ===========================================================================
+// Shapes
+// ===========================================================================
+struct Shape {
+  int nd = 0;
+  int64_t d[4] = {0, 0, 0, 0};
+  int64_t numel() const {
+    int64_t n = 1;
+    for (int i = 0; i < nd; ++i) n *= d[i];
+    return n;
+  }
+  bool operator==(const Shape& o) const {
+    if (nd != o.nd) return false;
+    for (int i = 0; i < nd; ++i)
+      if (d[i] != o.d[i]) return false;
+    return true;
+  }
+  bool operator!=(const Shape& o) const { return !(*this == o); }
+};
+
+Shape shape_of(const dvm_tensor& t) {
+  Shape s;
+  s.nd = t.ndim;
+  for (int i = 0; i < t.ndim; ++i) s.d[i] = t.shape[i];
+  return s;
+}
+
+Shape row_shape(const Shape& s) {
+  Shape r = s;
+  if (r.nd) r.d[r.nd - 1] = 1;
+  return r;
+}
+
+bool broadcast(const Shape& a, const Shape& b, Shape* out) {
+  Shape o;
+  o.nd = std::max(a.nd, b.nd);
+  for (int i = 0; i < o.nd; ++i) {
+    const int ia = a.nd - o.nd + i, ib = b.nd - o.nd + i;
+    const int64_t da = ia >= 0 ? a.d[ia] : 1, db = ib >= 0 ? b.d[ib] : 1;
+    if (da != db && da != 1 && db != 1) return false;
+    o.d[i] = da == 1 ? db : da;
+  }
+  *out = o;
+  return true;
+}
+
+// strides of a tensor broadcast (numpy rules) to target
+void bcast_strides(const dvm_tensor& t, const Shape& target, int64_t* out) {
+  const int off = target.nd - t.ndim;
+  for (int j = 0; j < target.nd; ++j) out[j] = 0;
+  for (int i = 0; i < t.ndim; ++i) {
+    const int j = off + i;
+    out[j] = (t.shape[i] == 1 && target.d[j] != 1) ? 0 : t.stride[i];
+  }
+}
+
+// Bytes spanned by a tensor (one past its last element).
+int64_t extent_bytes(const dvm_tensor& t) {
+  int64_t n = 1, last = 0;
+  for (int i = 0; i < t.ndim; ++i) {
+    n *= t.shape[i];
+    last += (t.shape[i] - 1) * t.stride[i];
+  }
+  if (n == 0) return 0;
+  return (last + 1) * esize(t.dtype);
+}
+
+// ===========================================================================
+// Shape tiling (DVM review page, section 4.2)
+//
+// Readings taken (the page gives the steps, not the constants):
+//  * the dominant shape is collapsed to [R, C] (C innermost); elementwise
+//    graphs whose operands are all contiguous collapse to [1, numel];
+//  * a tile is tr x tc; its rows go to P = next_pow2(tr) lane groups of
+//    g = T / P lanes; each lane holds NV = ceil((tc + pad) / (g V)) chunks of
+//    V elements and the tile is feasible iff P <= T and NV <= NV_MAX (the
+//    per-core resource limit: the lane's share of a tile register);
+//  * pad = V - 1 if some unit-stride operand's rows are not 16-byte aligned;
+//  * hardware_align_div(n, k, W) = W ceil(ceil(n / k) / W), W = 64 V, is the
+//    width one wave moves with 16-byte accesses of the narrowest type;
+//  * the shrink path goes outer -> inner (rows first, then columns) by
+//    doubling the split count k;
+//  * cost in integer ticks (1/31250 us): G = 512 resident workgroups,
+//    A = 15625 ticks per tile, 2 ticks per byte per workgroup;
+//    cost = ceil(n_tiles / G) (A + 2 var_bytes) + 2 inv_bytes; least cost
+//    wins, earlier (larger) candidates win ties.
+// ===========================================================================
+namespace tiling {
+constexpr int64_t T = T_LANES, V = VEC, NVM = NV_MAX, W = 64 * VEC, G = 512, A = 15625, BT = 2;
+
+struct Operand {
+  int64_t esize, sr, sc, base_mod16;
+};
+
+struct Plan {
+  int tmpl = 0;
+  int64_t R = 0, C = 0, pad = 0;
+  int64_t tr = 0, tc = 0, g = 0, nv = 0, P = 0, n_r = 0, n_c = 0, block_dim = 0, body_tile = 0, grid = 0;
+};
+
+int64_t next_pow2(int64_t x) {
+  int64_t p = 1;
+  while (p < x) p *= 2;
+  return p;
+}
+int64_t had(int64_t n, int64_t k, int64_t w) { return w * cdiv(cdiv(n, k), w); }
+
+// Collapse the dominant shape to [R, C].  strides: per operand, strides over
+// shape.  Returns false if some operand's outer dims cannot merge.
+bool collapse(int tmpl, const Shape& shape, const std::vector<std::array<int64_t, 4>>& strides, int64_t* R,
+              int64_t* C, std::vector<std::pair<int64_t, int64_t>>* out) {
+  out->clear();
+  const int64_t numel = shape.numel();
+  if (numel == 0) {
+    *R = 0;
+    *C = 0;
+    for (size_t i = 0; i < strides.size(); ++i) out->push_back({0, 0});
+    return true;
+  }
+  // drop unit dims
+  int keep[4], nk = 0;
+  for (int i = 0; i < shape.nd; ++i)
+    if (shape.d[i] != 1) keep[nk++] = i;
+  if (nk == 0) {
+    *R = 1;
+    *C = 1;
+    for (size_t i = 0; i < strides.size(); ++i) out->push_back({0, 0});
+    return true;
+  }
+  auto mergeable = [&](const std::array<int64_t, 4>& s, int lo, int hi) {
+    for (int i = lo; i < hi - 1; ++i)
+      if (s[keep[i]] != s[keep[i + 1]] * shape.d[keep[i + 1]]) return false;
+    return true;
+  };
+  if (tmpl == TM_ELEMWISE || tmpl == TM_ALLREDUCE) {
+    bool all = true;
+    for (auto& s : strides) all = all && mergeable(s, 0, nk);
+    if (all) {
+      *R = 1;
+      *C = numel;
+      for (auto& s : strides) out->push_back({0, s[keep[nk - 1]]});
+      return true;
+    }
+  }
+  const int64_t Cd = shape.nd ? shape.d[shape.nd - 1] : 1;
+  const int no = Cd == 1 ? nk : nk - 1;  // outer (kept) dims
+  int64_t Rr = 1;
+  for (int i = 0; i < no; ++i) Rr *= shape.d[keep[i]];
+  for (auto& s : strides) {
+    if (!mergeable(s, 0, no)) return false;
+    const int64_t sr = no ? s[keep[no - 1]] : 0;
+    const int64_t sc = Cd != 1 ? s[shape.nd - 1] : 0;
+    out->push_back({sr, sc});
+  }
+  *R = Rr;
+  *C = Cd;
+  return true;
+}
+
+int64_t alignment_pad(int64_t R, const std::vector<Operand>& ops) {
+  for (auto& o : ops) {
+    if (o.sc != 1) continue;
+    if (o.base_mod16 % 16 != 0) return V - 1;
+    if (R > 1 && ((o.sr * o.esize) % 16 + 16) % 16 != 0) return V - 1;
+  }
+  return 0;
+}
+
+bool geometry(int64_t tr, int64_t tc, int64_t pad, int64_t* P, int64_t* g, int64_t* nv) {
+  *P = next_pow2(tr);
+  if (*P > T) return false;
+  *g = T / *P;
+  *nv = cdiv(tc + pad, *g * V);
+  return *nv <= NVM;
+}
+
+void shrink_path(int tmpl, int64_t R, int64_t C, std::vector<std::pair<int64_t, int64_t>>* path) {
+  path->clear();
+  auto push = [&](int64_t a, int64_t b) {
+    if (path->empty() || path->back() != std::make_pair(a, b)) path->push_back({a, b});
+  };
+  if (tmpl == TM_ROWREDUCE) {
+    for (int64_t k = 1;; k *= 2) {
+      const int64_t tr = cdiv(R, k);
+      push(tr, C);
+      if (tr <= 1) break;
+    }
+    return;
+  }
+  const int64_t tc0 = std::min(C, had(C, 1, W));
+  for (int64_t k = 1;; k *= 2) {
+    const int64_t tr = cdiv(R, k);
+    push(tr, tc0);
+    if (tr <= 1) break;
+  }
+  int64_t prev = tc0;
+  for (int64_t k = 2; prev > W; k *= 2) {
+    const int64_t tc = std::min(C, had(C, k, W));
+    if (tc == prev) break;
+    push(1, tc);
+    prev = tc;
+  }
+}
+
+int64_t cost(int64_t R, int64_t C, int64_t tr, int64_t tc, const std::vector<Operand>& ops) {
+  const int64_t n_r = cdiv(R, tr), n_c = cdiv(C, tc), n_tiles = n_r * n_c;
+  int64_t var_b = 0, inv_b = 0;
+  for (auto& o : ops) {
+    const int64_t touched = (o.sr != 0 ? tr : 1) * (o.sc != 0 ? tc : 1) * o.esize;
+    const bool invariant = (o.sr == 0 || n_r == 1) && (o.sc == 0 || n_c == 1);
+    (invariant ? inv_b : var_b) += touched;
+  }
+  return cdiv(n_tiles, G) * (A + BT * var_b) + BT * inv_b;
+}
+
+void header(int64_t block_dim, int64_t* body_tile, int64_t* grid) {
+  if (block_dim == 0) {
+    *body_tile = 0;
+    *grid = 0;
+    return;
+  }
+  const int64_t gp = std::min(G, block_dim);
+  *body_tile = cdiv(block_dim, gp);
+  *grid = cdiv(block_dim, *body_tile);
+}
+
+bool plan(int tmpl, int64_t R, int64_t C, const std::vector<Operand>& ops, Plan* p) {
+  *p = Plan();
+  p->tmpl = tmpl;
+  p->R = R;
+  p->C = C;
+  p->pad = alignment_pad(R, ops);
+  if (R == 0 || C == 0) return true;
+  std::vector<std::pair<int64_t, int64_t>> path;
+  shrink_path(tmpl, R, C, &path);
+  bool found = false;
+  int64_t best = 0;
+  for (auto& [tr, tc] : path) {
+    int64_t P, g, nv;
+    if (!geometry(tr, tc, p->pad, &P, &g, &nv)) continue;
+    const int64_t c = cost(R, C, tr, tc, ops);
+    if (!found || c < best) {
+      found = true;
+      best = c;
+      p->tr = tr;
+      p->tc = tc;
+      p->P = P;
+      p->g = g;
+      p->nv = nv;
+    }
+  }
+  if (!found) return false;
+  p->n_r = cdiv(R, p->tr);
+  p->n_c = cdiv(C, p->tc);
+  p->block_dim = p->n_r * p->n_c;
+  header(p->block_dim, &p->body_tile, &p->grid);
+  return true;
+}
+}  // namespace tiling
+
+// ===========================================================================
+// Graph state
+// ===========================================================================
+enum ValKind : int { VK_INPUT = 0, VK_OP = 1 };
+
+struct Val {
+  uint32_t gen = 0;
+  bool alive = false;  // slot in use
+  int kind = VK_INPUT;
+  dvm_tensor t{};       // inputs: the tensor; op outputs: dtype, shape, storage (data may be NULL)
+  Shape shape;
+  bool live = false;      // DVM_OUT_LIVE
+  bool released = false;
+  bool pending = false;   // produced by an op in the buffered graph or the open group
+  bool stored = false;    // materialised in its storage by a flushed graph
+  bool lost = false;      // its graph was flushed without storing it
+};
+
+struct OpRec {
+  int32_t op = 0;
+  int n_in = 0;
+  int64_t in[2] = {-1, -1};
+  int scalar_pos = -1;
+  float scalar = 0.f;
+  int axis = -1;
+  int64_t out = -1;  // value slot index
+};
+
+bool is_reduce(int op) { return op == DVM_OP_REDUCE_SUM || op == DVM_OP_REDUCE_MAX; }
+bool is_reduce_all(const OpRec& o) { return is_reduce(o.op) && o.axis == DVM_AXIS_ALL; }
+bool is_binary(int op) { return op <= DVM_OP_POW; }
+
+enum FlushReason { FR_EXPLICIT = 0, FR_SYNC = 1, FR_REDUCE_ALL = 2, FR_SHAPE = 3, FR_PATTERN = 4, FR_DEPENDENCE = 5,
+                   FR_RESOURCE = 6 };
+
+}  // namespace
+
+struct dvm_context {
+  int device = -1;
+  void* scratch = nullptr;  // reduce-all counter (4 bytes) + per-tile partials from byte 256
+  size_t scratch_bytes = 0;
+};
+
+struct dvm_program {
+  Program prog;
+  uint32_t n_words = 0;
+  uint32_t n_instr = 0;
+  int64_t R = 0, C = 0;
+  uint32_t pad = 0;
+  uint32_t grid_launch = 0;   // workgroups actually launched (reduce-all always launches >= 1)
+};
+
+struct dvm_graph {
+  dvm_context* ctx = nullptr;
+  hipStream_t stream = nullptr;
+  std::vector<Val> vals;
+  std::vector<int64_t> free_slots;
+  std::vector<OpRec> buf;   // buffered (fused) graph
+  std::vector<OpRec> grp;   // open group
+  bool in_group = false;
+  dvm_stats stats{};
+  std::vector<std::pair<int32_t, int32_t>> flush_log;  // (ops, reason) per flushed graph
+};
+
+namespace {
+
+// value handle = slot | gen << 32
+dvm_value handle(const dvm_graph* g, int64_t slot) { return (dvm_value)(slot | ((int64_t)g->vals[slot].gen << 32)); }
+
+bool resolve(const dvm_graph* g, dvm_value h, int64_t* slot) {
+  const int64_t s = h & 0xffffffffLL;
+  const uint32_t gen = (uint32_t)((uint64_t)h >> 32);
+  if (s < 0 || s >= (int64_t)g->vals.size()) return false;
+  const Val& v = g->vals[s];
+  if (!v.alive || v.gen != gen) return false;
+  *slot = s;
+  return true;
+}
+
+int64_t new_slot(dvm_graph* g) {
+  int64_t s;
+  if (!g->free_slots.empty()) {
+    s = g->free_slots.back();
+    g->free_slots.pop_back();
+  } else {
+    s = (int64_t)g->vals.size();
+    g->vals.emplace_back();
+  }
+  Val& v = g->vals[s];
+  const uint32_t gen = v.gen + 1;
+  v = Val();
+  v.gen = gen;
+  v.alive = true;
+  return s;
+}
+
+void recycle(dvm_graph* g, int64_t s) {
+  Val& v = g->vals[s];
+  v.alive = false;
+  g->free_slots.push_back(s);
+}
+
+// ===========================================================================
+// Fusion rules (DVM review page, section 5.2; MindSpore summary, 3.2-3.3).
+//
+// Readings taken:
+//  * the unit of decision is a group (one op, or a composite the caller
+//    brackets); the group joins the buffered graph or the graph is flushed;
+//  * iteration shape: elementwise op = its output shape, reduce = its input
+//    shape, matmul = its [M, N] output; the dominant shape S_d is the
+//    iteration shape of largest rank, then numel, then the earliest;
+//  * pattern: reduces iterate over S_d, every other op over S_d or row(S_d);
+//    matmul only as the first op and with no reduce; a reduce-all is the last
+//    op (the graph closes) and does not mix with row reduces;
+//  * dependence through memory: no WAR, RAW or WAW between the new group and
+//    the buffered graph except through values;
+//  * resources: <= 64 ops, <= 24 external tensors, <= 3 tile values and <= 4
+//    row values in flight at every op, and a feasible tiling.
+// ===========================================================================
+constexpr int MAX_OPS = 64, MAX_EXT = 24, MAX_TILE_VALUES = 3, MAX_ROW_VALUES = 4;
+
+struct Checker {
+  dvm_graph* g;
+  const std::vector<OpRec>& ops;
+  std::vector<char> produced;  // per slot: produced inside ops
+
+  Checker(dvm_graph* gr, const std::vector<OpRec>& o) : g(gr), ops(o) {
+    produced.assign(g->vals.size(), 0);
+    for (auto& r : ops) produced[r.out] = 1;
+  }
+  bool external(int64_t s) const { return !produced[s]; }
+  const Shape& shp(int64_t s) const { return g->vals[s].shape; }
+
+  Shape iter_shape(const OpRec& o) const { return is_reduce(o.op) ? shp(o.in[0]) : shp(o.out); }
+
+  Shape dominant() const {
+    Shape best;
+    int64_t kr = -1, kn = -1;
+    for (auto& o : ops) {
+      const Shape s = iter_shape(o);
+      const int64_t n = s.numel();
+      if (s.nd > kr || (s.nd == kr && n > kn)) {
+        best = s;
+        kr = s.nd;
+        kn = n;
+      }
+    }
+    return best;
+  }
+
+  int tmpl() const {
+    if (ops[0].op == DVM_OP_MATMUL) return TM_MATMUL;
+    bool all = false, row = false;
+    for (auto& o : ops) {
+      if (is_reduce(o.op)) (o.axis == DVM_AXIS_ALL ? all : row) = true;
+    }
+    return all ? TM_ALLREDUCE : row ? TM_ROWREDUCE : TM_ELEMWISE;
+  }
+
+  // external operands read by non-matmul ops, first-use order
+  std::vector<int64_t> ext_operands() const {
+    std::vector<int64_t> out;
+    for (auto& o : ops) {
+      if (o.op == DVM_OP_MATMUL) continue;
+      for (int k = 0; k < o.n_in; ++k) {
+        const int64_t s = o.in[k];
+        if (external(s) && std::find(out.begin(), out.end(), s) == out.end()) out.push_back(s);
+      }
+    }
+    return out;
+  }
+
+  // outputs that may be stored (have storage), in op order
+  std::vector<int64_t> storable_outputs() const {
+    std::vector<int64_t> out;
+    for (auto& o : ops) {
+      if (o.op == DVM_OP_MATMUL || is_reduce_all(o)) continue;
+      if (g->vals[o.out].t.data) out.push_back(o.out);
+    }
+    return out;
+  }
+
+  bool collapse(const Shape& sd, const std::vector<int64_t>& operands, int64_t* R, int64_t* C,
+                std::vector<std::pair<int64_t, int64_t>>* st) const {
+    std::vector<std::array<int64_t, 4>> strides;
+    for (int64_t s : operands) {
+      const dvm_tensor& t = g->vals[s].t;
+      if (t.ndim > sd.nd) return false;
+      Shape b;
+      if (!broadcast(shp(s), sd, &b) || b != sd) return false;
+      std::array<int64_t, 4> a{};
+      bcast_strides(t, sd, a.data());
+      strides.push_back(a);
+    }
+    return tiling::collapse(tmpl(), sd, strides, R, C, st);
+  }
+
+  int check_pattern() const {
+    const Shape sd = dominant();
+    const Shape rs = row_shape(sd);
+    int n_all = 0, n_row = 0;
+    for (size_t i = 0; i < ops.size(); ++i) {
+      const OpRec& o = ops[i];
+      if (o.op == DVM_OP_MATMUL) {
+        if (i != 0) return FR_PATTERN;
+        continue;
+      }
+      if (is_reduce(o.op)) {
+        if (iter_shape(o) != sd) return FR_SHAPE;
+        if (o.axis == DVM_AXIS_ALL) {
+          ++n_all;
+          if (i != ops.size() - 1) return FR_PATTERN;
+        } else {
+          ++n_row;
+        }
+        continue;
+      }
+      const Shape s = shp(o.out);
+      if (s != sd && s != rs) return FR_SHAPE;
+    }
+    if (ops[0].op == DVM_OP_MATMUL && (n_all || n_row)) return FR_PATTERN;
+    if (n_all && n_row) return FR_PATTERN;
+    if (n_all > 1) return FR_PATTERN;
+    if (tmpl() == TM_MATMUL) return -1;  // matmul graphs: epilogue operands checked at encode
+    std::vector<int64_t> operands = ext_operands();
+    for (int64_t s : storable_outputs()) operands.push_back(s);
+    int64_t R, C;
+    std::vector<std::pair<int64_t, int64_t>> st;
+    if (!collapse(sd, operands, &R, &C, &st)) return FR_SHAPE;
+    return -1;
+  }
+
+  // tile / row class of every value used or produced (mirrors the spec)
+  void classes(std::vector<char>* cls) const {  // 0 none, 1 tile, 2 row
+    const Shape sd = dominant(), rs = row_shape(sd);
+    const int tm = tmpl();
+    cls->assign(g->vals.size(), -1);
+    for (auto& o : ops) {
+      char oc;
+      if (tm == TM_ROWREDUCE && (is_reduce(o.op) || (shp(o.out) == rs && rs != sd))) oc = 2;
+      else if (is_reduce_all(o)) oc = 0;
+      else oc = 1;
+      (*cls)[o.out] = oc;
+      for (int k = 0; k < o.n_in; ++k) {
+        const int64_t s = o.in[k];
+        if (external(s) && (*cls)[s] == -1) {
+          if (o.op == DVM_OP_MATMUL) (*cls)[s] = 0;
+          else if (oc == 2 && !is_reduce(o.op)) (*cls)[s] = 2;
+          else (*cls)[s] = 1;
+        }
+      }
+    }
+  }
+
+  void demand(int* tile_peak, int* row_peak) const {
+    std::vector<char> cls;
+    classes(&cls);
+    const size_t n = g->vals.size();
+    std::vector<int> first(n, -1), last(n, -1), def(n, -1);
+    for (size_t i = 0; i < ops.size(); ++i) {
+      def[ops[i].out] = (int)i;
+      for (int k = 0; k < ops[i].n_in; ++k) {
+        const int64_t s = ops[i].in[k];
+        if (first[s] < 0) first[s] = (int)i;
+        last[s] = (int)i;
+      }
+    }
+    std::vector<int64_t> used;
+    for (size_t s = 0; s < n; ++s)
+      if (last[s] >= 0) used.push_back((int64_t)s);
+    *tile_peak = 0;
+    *row_peak = 0;
+    for (size_t i = 0; i < ops.size(); ++i) {
+      int nt = 0, nr = 0;
+      for (int64_t s : used) {
+        const int start = external(s) ? first[s] : def[s] + 1;
+        if (start <= (int)i && (int)i <= last[s]) {
+          if (cls[s] == 1) ++nt;
+          else if (cls[s] == 2) ++nr;
+        }
+      }
+      const char oc = cls[ops[i].out];
+      if (oc == 1) ++nt;
+      else if (oc == 2) ++nr;
+      *tile_peak = std::max(*tile_peak, nt);
+      *row_peak = std::max(*row_peak, nr);
+    }
+  }
+
+  static bool overlap(const std::pair<uintptr_t, int64_t>& a, const std::pair<uintptr_t, int64_t>& b) {
+    return a.first < b.first + (uintptr_t)b.second && b.first < a.first + (uintptr_t)a.second;
+  }
+
+  int check_dependence(size_t n_old) const {
+    if (n_old == 0) return -1;
+    auto range = [&](int64_t s) { return std::make_pair((uintptr_t)g->vals[s].t.data, extent_bytes(g->vals[s].t)); };
+    std::vector<std::pair<uintptr_t, int64_t>> old_reads, old_writes, new_reads, new_writes;
+    std::vector<char> prod_old(g->vals.size(), 0);
+    for (size_t i = 0; i < n_old; ++i) prod_old[ops[i].out] = 1;
+    for (size_t i = 0; i < n_old; ++i)
+      for (int k = 0; k < ops[i].n_in; ++k) {
+        const int64_t s = ops[i].in[k];
+        if (!prod_old[s] && g->vals[s].t.data && extent_bytes(g->vals[s].t)) old_reads.push_back(range(s));
+      }
+    for (size_t i = 0; i < n_old; ++i) {
+      const Val& v = g->vals[ops[i].out];
+      if (v.t.data && (v.live || !v.released)) old_writes.push_back(range(ops[i].out));
+    }
+    for (size_t i = n_old; i < ops.size(); ++i) {
+      for (int k = 0; k < ops[i].n_in; ++k) {
+        const int64_t s = ops[i].in[k];
+        if (external(s) && g->vals[s].t.data && extent_bytes(g->vals[s].t)) new_reads.push_back(range(s));
+      }
+      if (g->vals[ops[i].out].t.data) new_writes.push_back(range(ops[i].out));
+    }
+    for (auto& w : new_writes) {
+      for (auto& r : old_reads)
+        if (overlap(w, r)) return FR_DEPENDENCE;
+      for (auto& r : old_writes)
+        if (overlap(w, r)) return FR_DEPENDENCE;
+    }
+    for (auto& r : new_reads)
+      for (auto& w : old_writes)
+        if (overlap(r, w)) return FR_DEPENDENCE;
+    return -1;
+  }
+
+  bool tile_operands(const Shape& sd, const std::vector<int64_t>& operands, int64_t* R, int64_t* C,
+                     std::vector<tiling::Operand>* out, std::vector<std::pair<int64_t, int64_t>>* st) const {
+    if (!collapse(sd, operands, R, C, st)) return false;
+    out->clear();
+    for (size_t i = 0; i < operands.size(); ++i) {
+      const dvm_tensor& t = g->vals[operands[i]].t;
+      out->push_back({esize(t.dtype), (*st)[i].first, (*st)[i].second, (int64_t)((uintptr_t)t.data % 16)});
+    }
+    return true;
+  }
+
+  int check_resources() const {
+    if (ops.size() > (size_t)MAX_OPS) return FR_RESOURCE;
+    std::vector<int64_t> exts;
+    for (auto& o : ops)
+      for (int k = 0; k < o.n_in; ++k)
+        if (external(o.in[k]) && std::find(exts.begin(), exts.end(), o.in[k]) == exts.end()) exts.push_back(o.in[k]);
+    if (exts.size() > (size_t)MAX_EXT) return FR_RESOURCE;
+    int tp, rp;
+    demand(&tp, &rp);
+    if (tp > MAX_TILE_VALUES || rp > MAX_ROW_VALUES) return FR_RESOURCE;
+    if (tmpl() == TM_MATMUL) return -1;
+    const Shape sd = dominant();
+    std::vector<int64_t> operands = ext_operands();
+    for (int64_t s : storable_outputs()) operands.push_back(s);
+    int64_t R, C;
+    std::vector<tiling::Operand> tops;
+    std::vector<std::pair<int64_t, int64_t>> st;
+    if (!tile_operands(sd, operands, &R, &C, &tops, &st)) return FR_SHAPE;
+    tiling::Plan p;
+    if (!tiling::plan(tmpl(), R, C, tops, &p)) return FR_RESOURCE;
+    return -1;
+  }
+
+  int check(size_t n_old) const {
+    int r = check_pattern();
+    if (r >= 0) return r;
+    r = check_dependence(n_old);
+    if (r >= 0) return r;
+    return check_resources();
+  }
+};
+
+// ===========================================================================
+// Encoder: lowers a fused graph to a tile-level bytecode program
+// (DVM review page, section 4.3: code header + per-op bytecode + the syncs the
+// encoder inserts).
+// ===========================================================================
+struct Encoder {
+  dvm_graph* g;
+  const std::vector<OpRec>& ops;
+  Checker ck;
+  dvm_program* prog;
+  uint32_t* W;
+  std::vector<uint32_t> body;
+  int n_args = 0;
+  std::vector<int> arg_of;        // slot -> arg index
+  std::vector<int> last_use, n_uses;
+  std::vector<char> cls;
+  int treg[N_TREG];               // value slot held by each tile register (-1 none)
+  int rreg[N_RREG];
+  std::vector<int> tloc, rloc;    // slot -> register (-1 none)
+  std::vector<char> store_it;
+  tiling::Plan plan;
+  int n_red = 0;
+  bool cross_wave = false;
+
+  Encoder(dvm_graph* gr, const std::vector<OpRec>& o, dvm_program* p) : g(gr), ops(o), ck(gr, o), prog(p), W(p->prog.w) {}
+
+  void emit(uint32_t w0, uint32_t w1) {
+    body.push_back(w0);
+    body.push_back(w1);
+  }
+
+  int add_arg(int64_t slot, int64_t sr, int64_t sc) {
+    const dvm_tensor& t = g->vals[slot].t;
+    const int i = n_args++;
+    uint32_t* a = W + ARG_BASE + i * ARG_WORDS;
+    const uint64_t p = (uint64_t)(uintptr_t)t.data;
+    a[A_PTR_LO] = (uint32_t)p;
+    a[A_PTR_HI] = (uint32_t)(p >> 32);
+    a[A_DTYPE] = (uint32_t)t.dtype;
+    const int64_t es = esize(t.dtype);
+    const int64_t al = std::min<int64_t>(16, 8 * es);
+    bool vec = sc == 1 && (int64_t)(p % al) == 0 && (plan.R <= 1 || ((sr * es) % al + al) % al == 0) &&
+               (plan.n_c <= 1 || (plan.tc * es) % al == 0);
+    a[A_FLAGS] = vec ? AF_VEC : 0u;
+    a[A_SR_LO] = (uint32_t)(uint64_t)sr;
+    a[A_SR_HI] = (uint32_t)((uint64_t)sr >> 32);
+    a[A_SC] = (uint32_t)(int32_t)sc;
+    const int64_t ext = extent_bytes(t);
+    a[A_EXTENT] = (uint32_t)std::min<int64_t>(ext, EXTENT_CAP);
+    arg_of[slot] = i;
+    return i;
+  }
+
+  bool live_after(int64_t s, int i) const { return last_use[s] > i; }
+
+  int free_treg(int avoid0 = 1) const {
+    for (int k = avoid0; k < N_TREG; ++k)
+      if (treg[k] < 0) return k;
+    return -1;
+  }
+
+  void bind_t(int k, int64_t s) {
+    if (treg[k] >= 0) tloc[treg[k]] = -1;
+    treg[k] = (int)s;
+    if (s >= 0) tloc[s] = k;
+  }
+  void unbind_t(int k) {
+    if (treg[k] >= 0) tloc[treg[k]] = -1;
+    treg[k] = -1;
+  }
+
+  // Make room in register k: move or drop what it holds if still needed.
+  dvm_status evict(int k, int i, int64_t keep_a) {
+    const int64_t v = treg[k];
+    if (v < 0 || v == keep_a) return DVM_OK;
+    bool needed = live_after(v, i);
+    const OpRec& o = ops[i];
+    for (int q = 0; q < o.n_in; ++q) needed = needed || o.in[q] == v;
+    if (!needed) {
+      unbind_t(k);
+      return DVM_OK;
+    }
+    const int f = free_treg();
+    if (f >= 0) {
+      emit(enc0(OP_COPY, f, k, 0, 0, 0, 0), 0);
+      bind_t(f, v);
+      treg[k] = -1;
+      return DVM_OK;
+    }
+    if (ck.external(v)) {  // an external value can always be reloaded
+      unbind_t(k);
+      return DVM_OK;
+    }
+    return fail(DVM_ERR_RESOURCE, "tile registers exhausted at op %d", i);
+  }
+
+  // Bring tile value s into the accumulator, preserving it elsewhere if it is
+  // still needed after op i.
+  dvm_status to_acc(int64_t s, int i) {
+    dvm_status st = evict(0, i, s);
+    if (st != DVM_OK) return st;
+    const int k = tloc[s];
+    if (k == 0) {
+      if (live_after(s, i)) {
+        const int f = free_treg();
+        if (f >= 0) {
+          emit(enc0(OP_COPY, f, 0, 0, 0, 0, 0), 0);
+          treg[f] = (int)s;
+          tloc[s] = f;
+          treg[0] = -1;
+        } else if (ck.external(s)) {
+          unbind_t(0);
+        } else {
+          return fail(DVM_ERR_RESOURCE, "tile registers exhausted at op %d", i);
+        }
+      } else {
+        unbind_t(0);
+      }
+      return DVM_OK;
+    }
+    if (k > 0) {
+      emit(enc0(OP_COPY, 0, k, 0, 0, 0, 0), 0);
+      if (!live_after(s, i)) {
+        bool again = false;
+        for (int q = 0; q < ops[i].n_in; ++q) again = again || (ops[i].in[q] == s && q > 0);
+        if (!again) unbind_t(k);
+      }
+      return DVM_OK;
+    }
+    // external, not in a register
+    emit(enc0(OP_LOAD, 0, 0, 0, 0, 0, 0), (uint32_t)arg_of[s]);
+    return DVM_OK;
+  }
+
+  int free_rreg() const {
+    for (int k = 0; k < N_RREG; ++k)
+      if (rreg[k] < 0) return k;
+    return -1;
+  }
+
+  // Row register holding row value s (loading an external row operand).
+  int row_of(int64_t s) {
+    if (rloc[s] >= 0) return rloc[s];
+    const int f = free_rreg();
+    if (f < 0) return -1;
+    emit(enc0(OP_LOAD_ROW, f, 0, 0, 0, 0, 0), (uint32_t)arg_of[s]);
+    rreg[f] = (int)s;
+    rloc[s] = f;
+    return f;
+  }
+
+  void free_dead(int i) {
+    const OpRec& o = ops[i];
+    for (int q = 0; q < o.n_in; ++q) {
+      const int64_t s = o.in[q];
+      if (last_use[s] > i) continue;
+      if (tloc[s] >= 0 && treg[tloc[s]] == s) unbind_t(tloc[s]);
+      if (rloc[s] >= 0) {
+        rreg[rloc[s]] = -1;
+        rloc[s] = -1;
+      }
+    }
+  }
+
+  uint32_t alu_of(int op) const {
+    switch (op) {
+      case DVM_OP_ADD: return ALU_ADD;
+      case DVM_OP_SUB: return ALU_SUB;
+      case DVM_OP_MUL: return ALU_MUL;
+      case DVM_OP_DIV: return ALU_DIV;
+      case DVM_OP_MAX: return ALU_MAX;
+      case DVM_OP_MIN: return ALU_MIN;
+      default: return ALU_POW;
+    }
+  }
+  uint32_t un_of(const OpRec& o) const {
+    switch (o.op) {
+      case DVM_OP_SQRT: return UN_SQRT;
+      case DVM_OP_ABS: return UN_ABS;
+      case DVM_OP_LOG: return UN_LOG;
+      case DVM_OP_EXP: return UN_EXP;
+      case DVM_OP_ROUND: return UN_ROUND;
+      case DVM_OP_FLOOR: return UN_FLOOR;
+      case DVM_OP_ISFINITE: return UN_ISFINITE;
+      case DVM_OP_NEG: return UN_NEG;
+      case DVM_OP_RECIP: return UN_RECIP;
+      default: return UN_IDENT;  // cast / copy: the dtype rounding follows
+    }
+  }
+
+  // Rounding to the op's output dtype when later ops read the value.
+  void round_out(int64_t s, int i, bool in_acc, int rr) {
+    if (g->vals[s].t.dtype != DVM_BF16 || !live_after(s, i)) return;
+    if (in_acc) emit(enc0(OP_UN, 0, 0, 0, UN_TOBF16, 0, 0), 0);
+    else emit(enc0(OP_RUN, rr, rr, 0, UN_TOBF16, 0, 0), 0);
+  }
+
+  dvm_status tile_op(int i) {
+    const OpRec& o = ops[i];
+    // operands: tile values / external tiles, row values, scalar
+    int64_t in[2] = {o.in[0], o.n_in > 1 ? o.in[1] : -1};
+    const bool binary = is_binary(o.op);
+    int64_t a = -1, b = -1;
+    bool rev = false;
+    if (!binary) {
+      a = in[0];
+    } else if (o.n_in == 1) {  // scalar operand
+      a = in[0];
+      rev = o.scalar_pos == 0;
+    } else {
+      const bool t0 = cls[in[0]] == 1, t1 = cls[in[1]] == 1;
+      if (t0 && t1) {
+        // prefer a value already in the accumulator, then one that dies here
+        int pick = 0;
+        auto score = [&](int q) {
+          const int64_t s = in[q];
+          int sc = 0;
+          if (tloc[s] == 0) sc += 4;
+          if (!live_after(s, i)) sc += 2;
+          if (tloc[s] >= 0) sc += 1;
+          return sc;
+        };
+        if (in[0] != in[1] && score(1) > score(0)) pick = 1;
+        a = in[pick];
+        b = in[1 - pick];
+        rev = pick == 1;
+      } else if (t0) {
+        a = in[0];
+        b = in[1];
+      } else {
+        a = in[1];
+        b = in[0];
+        rev = true;
+      }
+    }
+    dvm_status st = to_acc(a, i);
+    if (st != DVM_OK) return st;
+    if (!binary) {
+      const uint32_t f = un_of(o);
+      if (f != UN_IDENT) emit(enc0(OP_UN, 0, 0, 0, f, 0, 0), 0);
+    } else {
+      uint32_t bk, bi = 0, w1 = 0;
+      if (o.n_in == 1) {
+        bk = BK_IMM;
+        float s = o.scalar;
+        std::memcpy(&w1, &s, 4);
+      } else if (b == a) {
+        bk = BK_TREG;
+        bi = 0;
+      } else if (cls[b] == 2) {
+        const int r = row_of(b);
+        if (r < 0) return fail(DVM_ERR_RESOURCE, "row registers exhausted at op %d", i);
+        bk = BK_RREG;
+        bi = (uint32_t)r;
+      } else if (tloc[b] >= 0) {
+        bk = BK_TREG;
+        bi = (uint32_t)tloc[b];
+      } else {
+        // external tile operand: keep it in a free register if it is read again
+        const int f = free_treg();
+        if (n_uses[b] > 1 && live_after(b, i) && f >= 0) {
+          emit(enc0(OP_LOAD, f, 0, 0, 0, 0, 0), (uint32_t)arg_of[b]);
+          bind_t(f, b);
+          bk = BK_TREG;
+          bi = (uint32_t)f;
+        } else {
+          bk = BK_MEM;
+          w1 = (uint32_t)arg_of[b];
+        }
+      }
+      emit(enc0(OP_BIN, 0, 0, bi, alu_of(o.op), bk, rev ? FL_REV : 0), w1);
+    }
+    free_dead(i);
+    if (treg[0] >= 0 && treg[0] != o.out) unbind_t(0);
+    bind_t(0, o.out);
+    round_out(o.out, i, true, 0);
+    if (store_it[o.out]) emit(enc0(OP_STORE, 0, 0, 0, 0, 0, 0), (uint32_t)arg_of[o.out]);
+    if (last_use[o.out] <= i) unbind_t(0);
+    return DVM_OK;
+  }
+
+  dvm_status row_op(int i) {
+    const OpRec& o = ops[i];
+    const bool binary = is_binary(o.op);
+    int ra = -1, rb = -1;
+    bool imm = false, rev = false;
+    uint32_t w1 = 0;
+    if (binary && o.n_in == 1) {
+      ra = row_of(o.in[0]);
+      imm = true;
+      rev = o.scalar_pos == 0;
+      float s = o.scalar;
+      std::memcpy(&w1, &s, 4);
+    } else {
+      ra = row_of(o.in[0]);
+      if (binary) rb = row_of(o.in[1]);
+    }
+    if (ra < 0 || (binary && !imm && rb < 0)) return fail(DVM_ERR_RESOURCE, "row registers exhausted at op %d", i);
+    // destination: an input register that dies here, else a free one
+    int dst = -1;
+    if (!live_after(o.in[0], i) && rloc[o.in[0]] == ra) dst = ra;
+    else if (binary && !imm && !live_after(o.in[1], i) && rloc[o.in[1]] == rb) dst = rb;
+    else dst = free_rreg();
+    if (dst < 0) return fail(DVM_ERR_RESOURCE, "row registers exhausted at op %d", i);
+    if (binary) {
+      emit(enc0(OP_RBIN, dst, ra, imm ? 0 : rb, alu_of(o.op), imm ? BK_IMM : BK_RREG, rev ? FL_REV : 0), w1);
+    } else {
+      emit(enc0(OP_RUN, dst, ra, 0, un_of(o), 0, 0), 0);
+    }
+    free_dead(i);
+    if (rreg[dst] >= 0 && rreg[dst] != o.out) rloc[rreg[dst]] = -1;
+    rreg[dst] = (int)o.out;
+    rloc[o.out] = dst;
+    round_out(o.out, i, false, dst);
+    if (store_it[o.out]) emit(enc0(OP_STORE_ROW, 0, dst, 0, 0, 0, 0), (uint32_t)arg_of[o.out]);
+    if (last_use[o.out] <= i) {
+      rreg[dst] = -1;
+      rloc[o.out] = -1;
+    }
+    return DVM_OK;
+  }
+
+  // tile register holding tile value s (loading an external one)
+  dvm_status tile_src(int64_t s, int i, int* k) {
+    if (tloc[s] >= 0) {
+      *k = tloc[s];
+      return DVM_OK;
+    }
+    int f = free_treg(0);
+    if (f < 0) {
+      dvm_status st = evict(0, i, -1);
+      if (st != DVM_OK) return st;
+      f = 0;
+    }
+    emit(enc0(OP_LOAD, f, 0, 0, 0, 0, 0), (uint32_t)arg_of[s]);
+    bind_t(f, s);
+    *k = f;
+    return DVM_OK;
+  }
+
+  dvm_status reduce_op(int i) {
+    const OpRec& o = ops[i];
+    const uint32_t kind = o.op == DVM_OP_REDUCE_SUM ? RK_SUM : RK_MAX;
+    int k;
+    dvm_status st = tile_src(o.in[0], i, &k);
+    if (st != DVM_OK) return st;
+    if (o.axis == DVM_AXIS_ALL) {
+      const uint32_t buf = (uint32_t)(n_red++ % N_LDSBUF);
+      emit(enc0(OP_ALL, 0, k, buf, kind, 0, 0), 0);
+      emit(enc0(OP_SYNC, 0, 0, 0, 0, 0, 0), 0);
+      emit(enc0(OP_ALL_FIN, 0, 0, buf, kind, 0, 0), 0);
+      W[H_ALL_KIND] = kind;
+      cross_wave = true;
+      free_dead(i);
+      return DVM_OK;
+    }
+    int dst = free_rreg();
+    if (dst < 0) return fail(DVM_ERR_RESOURCE, "row registers exhausted at op %d", i);
+    if (plan.g > 64) {
+      const uint32_t buf = (uint32_t)(n_red++ % N_LDSBUF);
+      emit(enc0(OP_RED, dst, k, buf, kind, 0, 0), 0);
+      emit(enc0(OP_SYNC, 0, 0, 0, 0, 0, 0), 0);
+      emit(enc0(OP_RED_FIN, dst, 0, buf, kind, 0, 0), 0);
+      cross_wave = true;
+    } else {
+      emit(enc0(OP_RED, dst, k, 0, kind, 0, 0), 0);
+    }
+    free_dead(i);
+    rreg[dst] = (int)o.out;
+    rloc[o.out] = dst;
+    round_out(o.out, i, false, dst);
+    if (store_it[o.out]) emit(enc0(OP_STORE_ROW, 0, dst, 0, 0, 0, 0), (uint32_t)arg_of[o.out]);
+    if (last_use[o.out] <= i) {
+      rreg[dst] = -1;
+      rloc[o.out] = -1;
+    }
+    return DVM_OK;
+  }
+
+  dvm_status run() {
+    std::memset(W, 0, sizeof(uint32_t) * HDR_WORDS);
+    const size_t n = g->vals.size();
+    arg_of.assign(n, -1);
+    last_use.assign(n, -1);
+    n_uses.assign(n, 0);
+    tloc.assign(n, -1);
+    rloc.assign(n, -1);
+    store_it.assign(n, 0);
+    for (int k = 0; k < N_TREG; ++k) treg[k] = -1;
+    for (int k = 0; k < N_RREG; ++k) rreg[k] = -1;
+    for (size_t i = 0; i < ops.size(); ++i)
+      for (int q = 0; q < ops[i].n_in; ++q) {
+        last_use[ops[i].in[q]] = (int)i;
+        n_uses[ops[i].in[q]]++;
+      }
+    const int tm = ck.tmpl();
+    if (tm == TM_MATMUL) return fail(DVM_ERR_UNSUPPORTED, "matmul graphs are not supported by this build");
+    // stored outputs: live, or not released by flush time
+    std::vector<int64_t> stored;
+    for (auto& o : ops) {
+      const Val& v = g->vals[o.out];
+      if (v.live || !v.released) {
+        if (!v.t.data) return fail(DVM_ERR_INVALID_ARG, "a value without storage escapes its graph");
+        if (!is_reduce_all(o)) stored.push_back(o.out);
+        store_it[o.out] = 1;
+      }
+    }
+    const Shape sd = ck.dominant();
+    std::vector<int64_t> operands = ck.ext_operands();
+    const size_t n_ext = operands.size();
+    for (int64_t s : stored) operands.push_back(s);
+    int64_t R, C;
+    std::vector<tiling::Operand> tops;
+    std::vector<std::pair<int64_t, int64_t>> st;
+    if (!ck.tile_operands(sd, operands, &R, &C, &tops, &st))
+      return fail(DVM_ERR_SHAPE, "operands do not collapse to two dims");
+    if (!tiling::plan(tm, R, C, tops, &plan)) return fail(DVM_ERR_RESOURCE, "no feasible tile");
+    // 32-bit lane offsets: a tile must span < 2^31 bytes in every operand
+    for (size_t q = 0; q < operands.size(); ++q) {
+      const int64_t span = ((plan.tr - 1) * std::llabs(st[q].first) + plan.tc * std::llabs(st[q].second) + 1) *
+                           tops[q].esize;
+      if (span >= (int64_t)EXTENT_CAP) return fail(DVM_ERR_RESOURCE, "tile spans >= 2^31 bytes");
+    }
+    if (operands.size() + 2 > (size_t)MAX_ARGS) return fail(DVM_ERR_RESOURCE, "too many operands");
+    for (size_t q = 0; q < operands.size(); ++q) add_arg(operands[q], st[q].first, st[q].second);
+    (void)n_ext;
+    cls.clear();
+    ck.classes(&cls);
+    // reduce-all output and scratch
+    if (tm == TM_ALLREDUCE) {
+      const OpRec& last = ops.back();
+      const int ai = n_args++;
+      uint32_t* a = W + ARG_BASE + ai * ARG_WORDS;
+      const uint64_t p = (uint64_t)(uintptr_t)g->vals[last.out].t.data;
+      a[A_PTR_LO] = (uint32_t)p;
+      a[A_PTR_HI] = (uint32_t)(p >> 32);
+      a[A_DTYPE] = (uint32_t)g->vals[last.out].t.dtype;
+      a[A_EXTENT] = 4;
+      W[H_ALL_OUT] = (uint32_t)ai;
+      const int si = n_args++;
+      uint32_t* b = W + ARG_BASE + si * ARG_WORDS;
+      const uint64_t q = (uint64_t)(uintptr_t)g->ctx->scratch;
+      b[A_PTR_LO] = (uint32_t)q;
+      b[A_PTR_HI] = (uint32_t)(q >> 32);
+      b[A_DTYPE] = DT_F32;
+      b[A_EXTENT] = (uint32_t)std::min<size_t>(g->ctx->scratch_bytes, EXTENT_CAP);
+      W[H_ALL_SCRATCH] = (uint32_t)si;
+      if (g->ctx->scratch && (size_t)(256 + 4 * plan.block_dim) > g->ctx->scratch_bytes)
+        return fail(DVM_ERR_RESOURCE, "reduce-all needs %lld partials", (long long)plan.block_dim);
+    }
+    for (size_t i = 0; i < ops.size(); ++i) {
+      const OpRec& o = ops[i];
+      dvm_status s;
+      if (is_reduce(o.op)) s = reduce_op((int)i);
+      else if (cls[o.out] == 2) s = row_op((int)i);
+      else s = tile_op((int)i);
+      if (s != DVM_OK) return s;
+    }
+    // Sync at the end of the body when the next tile's first cross-wave
+    // reduction could overwrite an LDS buffer some wave is still reading.
+    if (cross_wave && n_red < 2) emit(enc0(OP_SYNC, 0, 0, 0, 0, 0, 0), 0);
+    // header
+    const uint32_t instr_base = ARG_BASE + (uint32_t)n_args * ARG_WORDS;
+    if (instr_base + body.size() > (size_t)MAX_WORDS) return fail(DVM_ERR_RESOURCE, "program too large");
+    std::copy(body.begin(), body.end(), W + instr_base);
+    W[H_MAGIC] = MAGIC;
+    W[H_VERSION] = VERSION;
+    W[H_KTYPE] = KT_VECTOR;
+    W[H_TEMPLATE] = (uint32_t)tm;
+    W[H_BLOCK_DIM] = (uint32_t)plan.block_dim;
+    W[H_BODY_TILE] = (uint32_t)plan.body_tile;
+    W[H_GRID] = (uint32_t)plan.grid;
+    W[H_TR] = (uint32_t)plan.tr;
+    W[H_TC] = (uint32_t)plan.tc;
+    W[H_G] = (uint32_t)(plan.g ? plan.g : 1);
+    W[H_NV] = (uint32_t)plan.nv;
+    W[H_P] = (uint32_t)plan.P;
+    W[H_NC] = (uint32_t)(plan.n_c ? plan.n_c : 1);
+    W[H_NARGS] = (uint32_t)n_args;
+    W[H_PRO_BEGIN] = instr_base;
+    W[H_PRO_END] = instr_base;
+    W[H_BODY_BEGIN] = instr_base;
+    W[H_BODY_END] = instr_base + (uint32_t)body.size();
+    W[H_R_LO] = (uint32_t)(uint64_t)R;
+    W[H_R_HI] = (uint32_t)((uint64_t)R >> 32);
+    W[H_C_LO] = (uint32_t)(uint64_t)C;
+    W[H_C_HI] = (uint32_t)((uint64_t)C >> 32);
+    W[H_N_INSTR] = (uint32_t)(body.size() / 2);
+    prog->n_words = instr_base + (uint32_t)body.size();
+    prog->n_instr = (uint32_t)(body.size() / 2);
+    prog->R = R;
+    prog->C = C;
+    prog->pad = (uint32_t)plan.pad;
+    prog->grid_launch = (uint32_t)plan.grid;
+    if (tm == TM_ALLREDUCE && prog->grid_launch == 0) prog->grid_launch = 1;
+    return DVM_OK;
+  }
+};
+
+// ===========================================================================
+// Flushing
+// ===========================================================================
+dvm_status encode_buffer(dvm_graph* g, dvm_program** out) {
+  *out = nullptr;
+  if (g->buf.empty()) return DVM_OK;
+  auto t0 = std::chrono::steady_clock::now();
+  dvm_program* p = new (std::nothrow) dvm_program();
+  if (!p) return fail(DVM_ERR_INTERNAL, "out of host memory");
+  Encoder enc(g, g->buf, p);
+  dvm_status st = enc.run();
+  // the buffered values leave the buffer whatever the outcome
+  for (auto& o : g->buf) {
+    Val& v = g->vals[o.out];
+    v.pending = false;
+    const bool stored = st == DVM_OK && (v.live || !v.released) && v.t.data;
+    v.stored = stored;
+    v.lost = !stored;
+    if (v.released) recycle(g, o.out);
+  }
+  g->buf.clear();
+  auto t1 = std::chrono::steady_clock::now();
+  const double us = std::chrono::duration<double, std::micro>(t1 - t0).count();
+  g->stats.graphs++;
+  g->stats.encode_us_total += us;
+  g->stats.encode_us_max = std::max(g->stats.encode_us_max, us);
+  if (st != DVM_OK) {
+    delete p;
+    return st;
+  }
+  *out = p;
+  return DVM_OK;
+}
+
+dvm_status launch(dvm_context* ctx, const dvm_program* p, hipStream_t s) {
+  if (!ctx || ctx->device < 0) return fail(DVM_ERR_DEVICE, "encode-only context cannot launch");
+  if (p->grid_launch == 0) return DVM_OK;
+  hipError_t e = dvm_launch_vector_kernel(&p->prog, p->grid_launch, s);
+  if (e != hipSuccess) return fail(DVM_ERR_DEVICE, "launch failed: %s", hipGetErrorString(e));
+  return DVM_OK;
+}
+
+dvm_status flush_launch(dvm_graph* g, int reason, int32_t* launched) {
+  if (launched) *launched = 0;
+  if (g->buf.empty()) return DVM_OK;
+  g->stats.flush_reason[reason]++;
+  g->flush_log.push_back({(int32_t)g->buf.size(), (int32_t)reason});
+  dvm_program* p = nullptr;
+  dvm_status st = encode_buffer(g, &p);
+  if (st != DVM_OK) return st;
+  if (g->ctx->device >= 0) {
+    st = launch(g->ctx, p, g->stream);
+    if (st == DVM_OK) {
+      g->stats.launches++;
+      if (launched) *launched = 1;
+    }
+  }
+  delete p;
+  return st;
+}
+
+bool infer(const dvm_graph* g, int32_t op, const int64_t* in, int n_in, const dvm_attrs* at, Shape* out) {
+  if (op < 0 || op >= DVM_OP_COUNT) return false;
+  auto sh = [&](int k) { return g->vals[in[k]].shape; };
+  if (op == DVM_OP_MATMUL) {
+    if (n_in != 2) return false;
+    const Shape a = sh(0), b = sh(1);
+    if (a.nd != 2 || b.nd != 2 || a.d[1] != b.d[0]) return false;
+    out->nd = 2;
+    out->d[0] = a.d[0];
+    out->d[1] = b.d[1];
+    return true;
+  }
+  if (is_reduce(op)) {
+    if (n_in != 1) return false;
+    const Shape a = sh(0);
+    if (at && at->axis == DVM_AXIS_ALL) {
+      out->nd = 0;
+      return true;
+    }
+    if (a.nd == 0) return false;
+    *out = row_shape(a);
+    return true;
+  }
+  if (is_binary(op)) {
+    if (n_in == 2) return broadcast(sh(0), sh(1), out);
+    if (n_in == 1 && at && (at->scalar_pos == 0 || at->scalar_pos == 1)) {
+      *out = sh(0);
+      return true;
+    }
+    return false;
+  }
+  if (n_in != 1) return false;
+  *out = sh(0);
+  return true;
+}
+
+dvm_status check_tensor(const dvm_tensor* t) {
+  if (!t) return fail(DVM_ERR_INVALID_ARG, "null tensor");
+  if (t->ndim < 0 || t->ndim > 4) return fail(DVM_ERR_INVALID_ARG, "ndim %d out of range", t->ndim);
+  if (t->dtype < 0 || t->dtype > DVM_U8) return fail(DVM_ERR_INVALID_ARG, "bad dtype %d", t->dtype);
+  for (int i = 0; i < t->ndim; ++i) {
+    if (t->shape[i] < 0) return fail(DVM_ERR_INVALID_ARG, "negative dim");
+    if (t->stride[i] < 0) return fail(DVM_ERR_INVALID_ARG, "negative stride");
+  }
+  return DVM_OK;
+}
+
+dvm_status end_group_impl(dvm_graph* g, int32_t* flushed) {
+  if (flushed) *flushed = 0;
+  g->in_group = false;
+  if (g->grp.empty()) return DVM_OK;
+  g->stats.groups++;
+  std::vector<OpRec> grp;
+  grp.swap(g->grp);
+  if (!g->buf.empty()) {
+    std::vector<OpRec> cand = g->buf;
+    cand.insert(cand.end(), grp.begin(), grp.end());
+    Checker ck(g, cand);
+    const int why = ck.check(g->buf.size());
+    if (why < 0) {
+      g->buf.swap(cand);
+      g->stats.ops += grp.size();
+      if (is_reduce_all(g->buf.back())) return flush_launch(g, FR_REDUCE_ALL, flushed);
+      return DVM_OK;
+    }
+    dvm_status st = flush_launch(g, why, flushed);
+    if (flushed) *flushed = 1;
+    if (st != DVM_OK) return st;
+  }
+  Checker ck(g, grp);
+  const int why = ck.check(0);
+  if (why >= 0) {
+    g->stats.unsupported++;
+    for (auto& o : grp) {
+      Val& v = g->vals[o.out];
+      v.pending = false;
+      v.lost = true;
+    }
+    return fail(DVM_ERR_UNSUPPORTED, "group cannot run on the VM (rule %d)", why);
+  }
+  g->buf = std::move(grp);
+  g->stats.ops += g->buf.size();
+  if (is_reduce_all(g->buf.back())) return flush_launch(g, FR_REDUCE_ALL, flushed);
+  return DVM_OK;
+}
+
+}  // namespace
+
+// ===========================================================================
+// C ABI
+// ===========================================================================
+extern "C" {
+
+const char* dvm_last_error(void) { return g_err.c_str(); }
+
+dvm_status dvm_context_create(int device, dvm_context** out) {
+  if (!out) return fail(DVM_ERR_INVALID_ARG, "null out");
+  *out = nullptr;
+  dvm_context* c = new (std::nothrow) dvm_context();
+  if (!c) return fail(DVM_ERR_INTERNAL, "out of host memory");
+  c->device = device;
+  if (device >= 0) {
+    if (hipSetDevice(device) != hipSuccess) {
+      delete c;
+      return fail(DVM_ERR_DEVICE, "hipSetDevice(%d) failed", device);
+    }
+    c->scratch_bytes = 4u << 20;
+    if (hipMalloc(&c->scratch, c->scratch_bytes) != hipSuccess) {
+      delete c;
+      return fail(DVM_ERR_DEVICE, "scratch allocation failed");
+    }
+    if (hipMemset(c->scratch, 0, c->scratch_bytes) != hipSuccess || hipDeviceSynchronize() != hipSuccess) {
+      (void)hipFree(c->scratch);
+      delete c;
+      return fail(DVM_ERR_DEVICE, "scratch init failed");
+    }
+  }
+  *out = c;
+  return DVM_OK;
+}
+
+void dvm_context_destroy(dvm_context* ctx) {
+  if (!ctx) return;
+  if (ctx->scratch) {
+    (void)hipDeviceSynchronize();
+    (void)hipFree(ctx->scratch);
+  }
+  delete ctx;
+}
+
+dvm_status dvm_graph_create(dvm_context* ctx, void* stream, dvm_graph** out) {
+  if (!ctx || !out) return fail(DVM_ERR_INVALID_ARG, "null argument");
+  dvm_graph* g = new (std::nothrow) dvm_graph();
+  if (!g) return fail(DVM_ERR_INTERNAL, "out of host memory");
+  g->ctx = ctx;
+  g->stream = (hipStream_t)stream;
+  *out = g;
+  return DVM_OK;
+}
+
+void dvm_graph_destroy(dvm_graph* g) { delete g; }
+
+dvm_status dvm_graph_input(dvm_graph* g, const dvm_tensor* t, dvm_value* out) {
+  if (!g || !out) return fail(DVM_ERR_INVALID_ARG, "null argument");
+  dvm_status st = check_tensor(t);
+  if (st != DVM_OK) return st;
+  const int64_t s = new_slot(g);
+  Val& v = g->vals[s];
+  v.kind = VK_INPUT;
+  v.t = *t;
+  v.shape = shape_of(*t);
+  v.stored = true;
+  *out = handle(g, s);
+  return DVM_OK;
+}
+
+dvm_status dvm_graph_begin_group(dvm_graph* g) {
+  if (!g) return fail(DVM_ERR_INVALID_ARG, "null graph");
+  if (g->in_group) return fail(DVM_ERR_INVALID_ARG, "group already open");
+  g->in_group = true;
+  return DVM_OK;
+}
+
+dvm_status dvm_graph_end_group(dvm_graph* g, int32_t* flushed) {
+  if (!g) return fail(DVM_ERR_INVALID_ARG, "null graph");
+  if (!g->in_group) return fail(DVM_ERR_INVALID_ARG, "no open group");
+  return end_group_impl(g, flushed);
+}
+
+dvm_status dvm_graph_infer_shape(dvm_graph* g, int32_t op, const dvm_value* in, int32_t n_in,
+                                 const dvm_attrs* attrs, dvm_tensor* out_shape) {
+  if (!g || !out_shape || n_in < 0 || n_in > 2) return fail(DVM_ERR_INVALID_ARG, "bad argument");
+  int64_t slots[2];
+  for (int k = 0; k < n_in; ++k)
+    if (!resolve(g, in[k], &slots[k])) return fail(DVM_ERR_INVALID_ARG, "unknown value");
+  Shape s;
+  if (!infer(g, op, slots, n_in, attrs, &s)) return fail(DVM_ERR_SHAPE, "shapes do not fit op %d", op);
+  out_shape->ndim = s.nd;
+  for (int i = 0; i < s.nd; ++i) out_shape->shape[i] = s.d[i];
+  return DVM_OK;
+}
+
+dvm_status dvm_graph_add_op(dvm_graph* g, int32_t op, const dvm_value* in, int32_t n_in, const dvm_attrs* attrs,
+                            const dvm_tensor* out, uint32_t flags, dvm_value* out_value) {
+  if (!g || !out || !out_value || (n_in > 0 && !in)) return fail(DVM_ERR_INVALID_ARG, "null argument");
+  if (n_in < 1 || n_in > 2) return fail(DVM_ERR_INVALID_ARG, "n_in %d", n_in);
+  dvm_status st = check_tensor(out);
+  if (st != DVM_OK) return st;
+  OpRec r;
+  r.op = op;
+  r.n_in = n_in;
+  for (int k = 0; k < n_in; ++k) {
+    if (!resolve(g, in[k], &r.in[k])) return fail(DVM_ERR_INVALID_ARG, "unknown or released value");
+    const Val& v = g->vals[r.in[k]];
+    if (v.released) return fail(DVM_ERR_INVALID_ARG, "input was released");
+    if (v.lost) return fail(DVM_ERR_INVALID_ARG, "input's graph was flushed without storing it");
+  }
+  if (attrs) {
+    r.axis = attrs->axis;
+    r.scalar_pos = attrs->scalar_pos;
+    r.scalar = attrs->scalar;
+  }
+  if (is_binary(op) && n_in == 1 && !(attrs && (attrs->scalar_pos == 0 || attrs->scalar_pos == 1)))
+    return fail(DVM_ERR_INVALID_ARG, "binary op needs two inputs or a scalar operand");
+  if (is_reduce(op) && r.axis != -1 && r.axis != DVM_AXIS_ALL) return fail(DVM_ERR_UNSUPPORTED, "reduce axis");
+  Shape s;
+  if (!infer(g, op, r.in, n_in, attrs, &s)) return fail(DVM_ERR_SHAPE, "shapes do not fit op %d", op);
+  if (shape_of(*out) != s) return fail(DVM_ERR_SHAPE, "out shape differs from the inferred shape");
+  // F1: the op set and dtypes the VM runs
+  if (op == DVM_OP_ISFINITE && out->dtype != DVM_U8) return fail(DVM_ERR_UNSUPPORTED, "isfinite writes u8");
+  if (op != DVM_OP_ISFINITE && out->dtype == DVM_U8) return fail(DVM_ERR_UNSUPPORTED, "u8 output");
+  if (op == DVM_OP_MATMUL) return fail(DVM_ERR_UNSUPPORTED, "matmul is not supported by this build");
+  const int64_t slot = new_slot(g);
+  Val& v = g->vals[slot];
+  v.kind = VK_OP;
+  v.t = *out;
+  v.shape = s;
+  v.live = (flags & DVM_OUT_LIVE) != 0;
+  v.pending = true;
+  r.out = slot;
+  *out_value = handle(g, slot);
+  g->grp.push_back(r);
+  if (!g->in_group) {
+    int32_t fl;
+    return end_group_impl(g, &fl);
+  }
+  return DVM_OK;
+}
+
+dvm_status dvm_graph_release(dvm_graph* g, dvm_value h) {
+  int64_t s;
+  if (!g || !resolve(g, h, &s)) return fail(DVM_ERR_INVALID_ARG, "unknown value");
+  Val& v = g->vals[s];
+  v.released = true;
+  if (!v.pending) recycle(g, s);
+  return DVM_OK;
+}
+
+dvm_status dvm_flush(dvm_graph* g, dvm_program** out) {
+  if (!g || !out) return fail(DVM_ERR_INVALID_ARG, "null argument");
+  if (!g->buf.empty()) {
+    g->stats.flush_reason[FR_EXPLICIT]++;
+    g->flush_log.push_back({(int32_t)g->buf.size(), (int32_t)FR_EXPLICIT});
+  }
+  return encode_buffer(g, out);
+}
+
+dvm_status dvm_launch(dvm_context* ctx, const dvm_program* p, void* stream) {
+  if (!ctx || !p) return fail(DVM_ERR_INVALID_ARG, "null argument");
+  return launch(ctx, p, (hipStream_t)stream);
+}
+
+dvm_status dvm_graph_flush_launch(dvm_graph* g, int32_t* launched) {
+  if (!g) return fail(DVM_ERR_INVALID_ARG, "null graph");
+  if (g->in_group) return fail(DVM_ERR_INVALID_ARG, "group still open");
+  return flush_launch(g, FR_EXPLICIT, launched);
+}
+
+dvm_status dvm_sync(dvm_graph* g) {
+  if (!g) return fail(DVM_ERR_INVALID_ARG, "null graph");
+  if (g->in_group) return fail(DVM_ERR_INVALID_ARG, "group still open");
+  dvm_status st = flush_launch(g, FR_SYNC, nullptr);
+  if (st != DVM_OK) return st;
+  if (g->ctx->device >= 0) {
+    hipError_t e = hipStreamSynchronize(g->stream);
+    if (e != hipSuccess) return fail(DVM_ERR_DEVICE, "stream sync: %s", hipGetErrorString(e));
+  }
+  return DVM_OK;
+}
+
+dvm_status dvm_program_header(const dvm_program* p, dvm_header* out) {
+  if (!p || !out) return fail(DVM_ERR_INVALID_ARG, "null argument");
+  const uint32_t* W = p->prog.w;
+  out->kernel_type = W[H_KTYPE];
+  out->tmpl = W[H_TEMPLATE];
+  out->block_dim = W[H_BLOCK_DIM];
+  out->body_tile = W[H_BODY_TILE];
+  out->grid = W[H_GRID];
+  out->tr = W[H_TR];
+  out->tc = W[H_TC];
+  out->g = W[H_G];
+  out->nv = W[H_NV];
+  out->p = W[H_P];
+  out->R = p->R;
+  out->C = p->C;
+  out->n_instr = p->n_instr;
+  out->n_args = W[H_NARGS];
+  out->pad = p->pad;
+  out->n_words = p->n_words;
+  return DVM_OK;
+}
+
+dvm_status dvm_program_words(const dvm_program* p, uint32_t* buf, size_t* n_words) {
+  if (!p || !n_words) return fail(DVM_ERR_INVALID_ARG, "null argument");
+  const size_t cap = *n_words;
+  *n_words = p->n_words;
+  if (buf) std::memcpy(buf, p->prog.w, sizeof(uint32_t) * std::min<size_t>(cap, p->n_words));
+  return DVM_OK;
+}
+
+void dvm_program_free(dvm_program* p) { delete p; }
+
+dvm_status dvm_program_debug_tilemap(const dvm_program* p, const dvm_tensor* tile_out, const dvm_tensor* wg_out,
+                                     dvm_program** out) {
+  if (!p || !tile_out || !wg_out || !out) return fail(DVM_ERR_INVALID_ARG, "null argument");
+  if (p->prog.w[H_KTYPE] != KT_VECTOR) return fail(DVM_ERR_UNSUPPORTED, "vector programs only");
+  for (const dvm_tensor* t : {tile_out, wg_out}) {
+    if (t->dtype != DVM_F32 || t->ndim != 2 || t->shape[0] != p->R || t->shape[1] != p->C || t->stride[1] != 1 ||
+        t->stride[0] != p->C)
+      return fail(DVM_ERR_SHAPE, "tilemap outputs must be dense fp32 [R, C]");
+  }
+  dvm_program* q = new (std::nothrow) dvm_program(*p);
+  if (!q) return fail(DVM_ERR_INTERNAL, "out of host memory");
+  uint32_t* W = q->prog.w;
+  const uint32_t n_args = 2;
+  W[H_NARGS] = n_args;
+  W[H_TEMPLATE] = TM_ELEMWISE;  // same tiling; no reduce-all epilogue
+  int k = 0;
+  for (const dvm_tensor* t : {tile_out, wg_out}) {
+    uint32_t* a = W + ARG_BASE + k * ARG_WORDS;
+    const uint64_t ptr = (uint64_t)(uintptr_t)t->data;
+    a[A_PTR_LO] = (uint32_t)ptr;
+    a[A_PTR_HI] = (uint32_t)(ptr >> 32);
+    a[A_DTYPE] = DT_F32;
+    a[A_FLAGS] = 0;
+    const int64_t sr = p->R > 1 ? p->C : 0;
+    a[A_SR_LO] = (uint32_t)(uint64_t)sr;
+    a[A_SR_HI] = (uint32_t)((uint64_t)sr >> 32);
+    a[A_SC] = 1;
+    a[A_EXTENT] = (uint32_t)std::min<int64_t>(extent_bytes(*t), EXTENT_CAP);
+    ++k;
+  }
+  const uint32_t base = ARG_BASE + n_args * ARG_WORDS;
+  const uint32_t code[] = {enc0(OP_DBG, 0, 0, 0, 0, 0, 0), 0, enc0(OP_STORE, 0, 0, 0, 0, 0, 0), 0,
+                           enc0(OP_DBG, 0, 0, 0, 1, 0, 0), 0, enc0(OP_STORE, 0, 0, 0, 0, 0, 0), 1};
+  std::memcpy(W + base, code, sizeof code);
+  W[H_PRO_BEGIN] = W[H_PRO_END] = W[H_BODY_BEGIN] = base;
+  W[H_BODY_END] = base + 8;
+  W[H_N_INSTR] = 4;
+  q->n_words = base + 8;
+  q->n_instr = 4;
+  q->grid_launch = W[H_GRID];
+  *out = q;
+  return DVM_OK;
+}
+
+dvm_status dvm_graph_flush_log(const dvm_graph* g, int32_t* n_ops, int32_t* reasons, size_t* n) {
+  if (!g || !n) return fail(DVM_ERR_INVALID_ARG, "null argument");
+  const size_t cap = *n;
+  *n = g->flush_log.size();
+  for (size_t i = 0; i < std::min(cap, g->flush_log.size()); ++i) {
+    if (n_ops) n_ops[i] = g->flush_log[i].first;
+    if (reasons) reasons[i] = g->flush_log[i].second;
+  }
+  return DVM_OK;
+}
+
+dvm_status dvm_graph_stats(const dvm_graph* g, dvm_stats* out) {
+  if (!g || !out) return fail(DVM_ERR_INVALID_ARG, "null argument");
+  *out = g->stats;
+  return DVM_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,201 @@
+/*
+ * dvm.h -- C ABI of the MI355X DVM hot path: a streaming fuser, a tile-level
+ * bytecode encoder and a resident bytecode-interpreting VM kernel.
+ *
+ * The flow follows the DVM pages: ops are captured in order into a fusion
+ * buffer and fused while the fusion conditions hold; the buffer is flushed when
+ * an op cannot join, at a fusion boundary or at a synchronisation point
+ * (MindSpore DVM summary page, sections 3.2-3.3; DVM paper review page,
+ * section 5.2); a flushed graph is shape-tiled and encoded into a tile-level
+ * bytecode program on the host (review page, sections 4.2-4.3) and run by a
+ * resident VM kernel that interprets it tile by tile (review page, section
+ * 4.4).  No machine code is generated at run time: a new shape only needs a new
+ * program.
+ *
+ * Conventions
+ * - All functions return a dvm_status; on failure dvm_last_error() returns a
+ *   thread-local message.  No C++ exception crosses this boundary.
+ * - Device memory is always the caller's.  Pointers inside dvm_tensor are
+ *   borrowed: they must stay valid until the launch that reads or writes them
+ *   has completed on the stream it was issued on.
+ * - Contexts, graphs and programs are library-owned opaque handles.  A graph
+ *   is not thread-safe; separate graphs may be used from separate threads.
+ * - Strides are in elements; shapes have at most 4 dims.
+ */
+#ifndef DVM_H
+#define DVM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  DVM_OK = 0,
+  DVM_ERR_INVALID_ARG = 1,  /* malformed call, unknown value, missing storage */
+  DVM_ERR_UNSUPPORTED = 2,  /* the op (group) cannot run on the VM; run it elsewhere */
+  DVM_ERR_SHAPE = 3,        /* shapes do not broadcast / do not match */
+  DVM_ERR_RESOURCE = 4,     /* no feasible tiling / program too large */
+  DVM_ERR_DEVICE = 5,       /* HIP error (launch, sync, allocation) or no device */
+  DVM_ERR_INTERNAL = 6
+} dvm_status;
+
+typedef enum { DVM_F32 = 0, DVM_BF16 = 1, DVM_U8 = 2 } dvm_dtype;
+
+/* Primitive ops.  Elementwise ops broadcast their inputs numpy-style; every op
+ * computes in fp32 on the device and rounds its result to the output dtype
+ * (bf16: round to nearest even).  Table 1 of the DVM review page lists
+ * Sqrt/Abs/Log/Exp/Pow/Round/Floor/IsFinite and Copy/Broadcast; the binary
+ * ops, reductions, cast and matmul are the ones its fusion patterns use
+ * (section 5.1: c = a + b then sqrt; cube-vector fusion). */
+typedef enum {
+  DVM_OP_ADD = 0, DVM_OP_SUB, DVM_OP_MUL, DVM_OP_DIV, DVM_OP_MAX, DVM_OP_MIN, DVM_OP_POW,
+  DVM_OP_SQRT, DVM_OP_ABS, DVM_OP_LOG, DVM_OP_EXP, DVM_OP_ROUND, DVM_OP_FLOOR,
+  DVM_OP_ISFINITE,   /* output dtype u8 (0/1) */
+  DVM_OP_NEG, DVM_OP_RECIP,
+  DVM_OP_CAST,       /* to the output dtype */
+  DVM_OP_COPY,
+  DVM_OP_REDUCE_SUM, /* attrs.axis: -1 = innermost axis (keepdim), DVM_AXIS_ALL = all axes */
+  DVM_OP_REDUCE_MAX,
+  DVM_OP_MATMUL,     /* [M, K] x [K, N] -> [M, N], fp32 accumulate */
+  DVM_OP_COUNT
+} dvm_op;
+
+#define DVM_AXIS_ALL 0x7fffffff
+
+typedef struct {
+  void* data;        /* device pointer; may be NULL for an output that never needs storage */
+  int32_t dtype;     /* dvm_dtype */
+  int32_t ndim;      /* 0..4 */
+  int64_t shape[4];
+  int64_t stride[4]; /* elements */
+} dvm_tensor;
+
+typedef int64_t dvm_value;   /* graph-scoped value handle */
+
+typedef struct {
+  int32_t axis;        /* reductions: -1 or DVM_AXIS_ALL */
+  int32_t scalar_pos;  /* binary ops with a scalar operand: -1 none, 0 scalar is the left input, 1 the right */
+  float scalar;
+} dvm_attrs;
+
+/* add_op flags */
+#define DVM_OUT_LIVE 1u   /* store the output when its graph is flushed, even if released */
+
+typedef struct dvm_context dvm_context;
+typedef struct dvm_graph dvm_graph;
+typedef struct dvm_program dvm_program;
+
+/* Code header of an encoded program (DVM review page, section 4.3: tile
+ * count block_dim, tiles per core body_tile, kernel type) plus the tiling. */
+typedef struct {
+  uint32_t kernel_type;  /* 0 VECTOR, 1 MIX (matmul) */
+  uint32_t tmpl;         /* 0 elementwise, 1 row reduce, 2 reduce-all, 3 matmul */
+  uint32_t block_dim;    /* number of tiles */
+  uint32_t body_tile;    /* tiles per workgroup */
+  uint32_t grid;         /* workgroups launched */
+  uint32_t tr, tc;       /* tile rows / columns in the collapsed [R, C] space */
+  uint32_t g, nv, p;     /* lanes per tile row, chunks per lane, row groups */
+  int64_t R, C;          /* collapsed iteration space */
+  uint32_t n_instr;      /* instructions (prologue + body) */
+  uint32_t n_args;       /* global operands */
+  uint32_t pad;          /* alignment slack used by the tiling */
+  uint32_t n_words;      /* program size in 32-bit words */
+} dvm_header;
+
+typedef struct {
+  uint64_t graphs;            /* programs encoded */
+  uint64_t launches;          /* programs launched */
+  uint64_t ops;               /* ops accepted */
+  uint64_t groups;
+  uint64_t unsupported;       /* groups rejected (caller ran them elsewhere) */
+  uint64_t flush_reason[8];   /* 0 explicit, 1 sync, 2 reduce_all, 3 shape, 4 pattern, 5 dependence, 6 resource */
+  double encode_us_total;
+  double encode_us_max;
+} dvm_stats;
+
+/* Contexts.  device >= 0: the HIP device whose resident VM kernels run the
+ * programs; a small scratch area (reduce-all partials) is allocated on it.
+ * device < 0: an encode-only context (tiling and bytecode, no launches). */
+dvm_status dvm_context_create(int device, dvm_context** out);
+void dvm_context_destroy(dvm_context* ctx);
+
+/* A graph is a streaming fusion buffer bound to a HIP stream (hipStream_t,
+ * NULL = default stream); implicit flushes launch on that stream. */
+dvm_status dvm_graph_create(dvm_context* ctx, void* stream, dvm_graph** out);
+void dvm_graph_destroy(dvm_graph* g);
+
+/* Registers an external tensor (read by ops, never written through this
+ * handle). */
+dvm_status dvm_graph_input(dvm_graph* g, const dvm_tensor* t, dvm_value* out);
+
+/* Groups: ops added between begin and end are decided together (a composite
+ * such as LayerNorm).  An op added outside a group is a group of its own.
+ * end_group fuses the group into the buffered graph or, when the fusion
+ * conditions fail, flushes the buffered graph (encode + launch on the graph's
+ * stream) and starts a new graph with the group (*flushed = 1).  A group the
+ * VM cannot run at all returns DVM_ERR_UNSUPPORTED after flushing; its
+ * values are then invalid and the caller computes them elsewhere. */
+dvm_status dvm_graph_begin_group(dvm_graph* g);
+dvm_status dvm_graph_end_group(dvm_graph* g, int32_t* flushed);
+
+/* Appends one op.  in[] are value handles; n_in counts tensor inputs (1 for a
+ * binary op with a scalar operand, see dvm_attrs).  out gives the output's
+ * dtype and storage (shape must equal the inferred shape; data may be NULL if
+ * the value is released before its graph is flushed).  Writes the new value's
+ * handle to *out_value. */
+dvm_status dvm_graph_add_op(dvm_graph* g, int32_t op, const dvm_value* in, int32_t n_in,
+                            const dvm_attrs* attrs, const dvm_tensor* out, uint32_t flags,
+                            dvm_value* out_value);
+
+/* The caller will not use the value again (neither as an input nor by reading
+ * its storage).  A released value whose graph has not been flushed yet is
+ * never stored unless DVM_OUT_LIVE was given. */
+dvm_status dvm_graph_release(dvm_graph* g, dvm_value v);
+
+/* Output shape of an op (for allocating out). */
+dvm_status dvm_graph_infer_shape(dvm_graph* g, int32_t op, const dvm_value* in, int32_t n_in,
+                                 const dvm_attrs* attrs, dvm_tensor* out_shape);
+
+/* Encodes the buffered graph into a program (shape tiling + bytecode) and
+ * empties the buffer; *out = NULL when the buffer is empty.  The program is
+ * immutable and never cached; free it with dvm_program_free. */
+dvm_status dvm_flush(dvm_graph* g, dvm_program** out);
+
+/* Launches a program on the resident VM kernel of its kernel type, on
+ * stream (hipStream_t).  Asynchronous. */
+dvm_status dvm_launch(dvm_context* ctx, const dvm_program* p, void* stream);
+
+/* dvm_flush + dvm_launch on the graph's stream (no-op when empty). */
+dvm_status dvm_graph_flush_launch(dvm_graph* g, int32_t* launched);
+
+/* Synchronisation point: flush + launch, then wait for the graph's stream.
+ * Asynchronous device errors surface here as DVM_ERR_DEVICE. */
+dvm_status dvm_sync(dvm_graph* g);
+
+dvm_status dvm_program_header(const dvm_program* p, dvm_header* out);
+/* Copies the program words; *n_words in: capacity, out: size. */
+dvm_status dvm_program_words(const dvm_program* p, uint32_t* buf, size_t* n_words);
+void dvm_program_free(dvm_program* p);
+
+/* Debug program for tiling parity: same header and tiling as p, whose body
+ * writes, for every element of the collapsed [R, C] space, the id of the tile
+ * that holds it into tile_out and the workgroup that ran it into wg_out (both
+ * dense fp32 [R, C]). */
+dvm_status dvm_program_debug_tilemap(const dvm_program* p, const dvm_tensor* tile_out,
+                                     const dvm_tensor* wg_out, dvm_program** out);
+
+dvm_status dvm_graph_stats(const dvm_graph* g, dvm_stats* out);
+
+/* Partition record of the graphs flushed so far, oldest first: graph i held
+ * n_ops[i] ops and was flushed for reason reasons[i] (the dvm_stats
+ * flush_reason index).  *n in: capacity, out: number of graphs recorded. */
+dvm_status dvm_graph_flush_log(const dvm_graph* g, int32_t* n_ops, int32_t* reasons, size_t* n);
+const char* dvm_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DVM_H */

@@ -1,0 +1,231 @@
+"""GPU parity of the VM against the oracle, through the C ABI.
+
+Every case prints its name before it launches anything, so a failing run
+names the case.  Sizes span several tiles and ragged tails; tolerances:
+fp32 max|d|/max|ref| <= 1e-5, bf16 <= 2 ulp (floored), predicted-bit-exact
+chains (sqrt(a + b), the if-else branch) compared bit for bit, tiling and
+tile maps compared exactly.
+"""
+import numpy as np
+import pytest
+
+import workloads as W
+from oracle import numerics as N
+from oracle import ops as O
+from oracle import tiling as TL
+from oracle.graph import evaluate
+from tests.dvm_helpers import empty_dev, host64, torch_dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dvm():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import device_bytecode_vm_amd as m
+    return m
+
+
+@pytest.fixture(scope="module")
+def ctx(dvm):
+    return dvm.Context(0)
+
+
+def say(*a):
+    print("CASE", *a, flush=True)
+
+
+def test_sqrt_add_bit_exact(dvm, ctx):
+    import torch
+    for shape in [(513, 1031), (1, 1), (1, 7), (3, 5), (64, 4096)]:
+        say("sqrt_add", shape)
+        a, b = W.vv_sqrt_add(0, shape)
+        da, db = torch_dev(a, "f32"), torch_dev(b, "f32")
+        out = empty_dev(shape, "f32")
+        g = dvm.Graph(ctx)
+        va, vb = g.input(da), g.input(db)
+        t = g.op("add", va, vb)
+        g.op("sqrt", t, out=out, live=True)
+        g.release(t)
+        g.sync()
+        torch.cuda.synchronize()
+        ref, _ = evaluate([{"op": "add", "in": ["a", "b"], "out": "t", "dtype": "f32"},
+                           {"op": "sqrt", "in": ["t"], "out": "c", "dtype": "f32"}],
+                          {"a": a, "b": b}, emulate_f32=True)
+        got = host64(out)
+        assert np.array_equal(got, ref["c"]), f"{shape}: {np.sum(got != ref['c'])} mismatches"
+
+
+def _ln(dvm, ctx, x, gam, bet, eps=W.LN_EPS):
+    from device_bytecode_vm_amd import composites as CP
+    dx, dg, db = torch_dev(x, "bf16"), torch_dev(gam, "f32"), torch_dev(bet, "f32")
+    out = empty_dev(x.shape, "bf16")
+    g = dvm.Graph(ctx)
+    CP.layer_norm(g, g.input(dx), g.input(dg), g.input(db), eps, out=out)
+    g.sync()
+    return host64(out)
+
+
+@pytest.mark.parametrize("rows,h", [(1, 5120), (3, 5120), (37, 5120), (5, 96), (9, 1001), (2, 8192), (300, 24)])
+def test_layernorm(dvm, ctx, rows, h):
+    say("layernorm", rows, h)
+    x = W.layernorm_x(0, rows, rows, h)
+    gam, bet = W.layernorm_params(h)
+    got = _ln(dvm, ctx, x, gam, bet)
+    ref = O.layer_norm(x, gam, bet, W.LN_EPS)
+    ok, d = N.check_bf16(got, ref)
+    assert ok, f"max ulp {d}"
+
+
+def test_layernorm_workload_sampled(dvm, ctx):
+    """Two calls of the LayerNorm stream at full size; rows sampled."""
+    shapes = W.layernorm_shapes(0, 64)
+    gam, bet = W.layernorm_params()
+    g = np.random.default_rng(99)
+    for i in (0, int(np.argmax([r for r, _ in shapes]))):
+        rows, h = shapes[i]
+        say("layernorm_stream", i, rows)
+        x = W.layernorm_x(0, i, rows, h)
+        got = _ln(dvm, ctx, x, gam, bet)
+        idx = np.unique(np.concatenate([[0, rows - 1], g.integers(0, rows, 256)]))
+        ref = O.layer_norm(x[idx], gam, bet, W.LN_EPS)
+        ok, d = N.check_bf16(got[idx], ref)
+        assert ok, f"call {i}: max ulp {d}"
+
+
+@pytest.mark.parametrize("rows,cols", [(1, 16), (7, 3001), (40, 512), (3, 8192), (513, 17)])
+def test_softmax(dvm, ctx, rows, cols):
+    from device_bytecode_vm_amd import composites as CP
+    say("softmax", rows, cols)
+    x = W.normal(np.random.default_rng(rows * 7 + cols), (rows, cols), 0, 1, "bf16")
+    dx = torch_dev(x, "bf16")
+    out = empty_dev(x.shape, "bf16")
+    g = dvm.Graph(ctx)
+    CP.softmax(g, g.input(dx), out=out)
+    g.sync()
+    ok, d = N.check_bf16(host64(out), O.softmax(x))
+    assert ok, f"max ulp {d}"
+
+
+@pytest.mark.parametrize("rows", [1, 5, 33])
+def test_add_rmsnorm_fused(dvm, ctx, rows):
+    from device_bytecode_vm_amd import composites as CP
+    say("add_rmsnorm", rows)
+    h = 5120
+    rg = np.random.default_rng(rows)
+    h0 = W.normal(rg, (rows, h), 0, 1, "bf16")
+    r0 = W.normal(rg, (rows, h), 0, 1, "bf16")
+    w = W.normal(rg, (h,), 1, 0.1)
+    d0, dr, dw = torch_dev(h0, "bf16"), torch_dev(r0, "bf16"), torch_dev(w, "f32")
+    h1 = empty_dev((rows, h), "bf16")
+    n = empty_dev((rows, h), "bf16")
+    g = dvm.Graph(ctx)
+    vh = g.op("add", g.input(d0), g.input(dr), out=h1)
+    CP.rms_norm(g, vh, g.input(dw), W.RMS_EPS, out=n)
+    g.sync()
+    st = g.stats()
+    assert st["graphs"] == 1, st          # residual add and RMSNorm fused into one graph
+    h1_ref = N.round_bf16(h0.astype(np.float64) + r0)
+    assert np.array_equal(host64(h1), h1_ref)
+    ok, d = N.check_bf16(host64(n), O.rms_norm(h1_ref, w, W.RMS_EPS))
+    assert ok, f"max ulp {d}"
+
+
+@pytest.mark.parametrize("rows,cols", [(3, 17408), (1, 100), (17, 777)])
+def test_swiglu(dvm, ctx, rows, cols):
+    from device_bytecode_vm_amd import composites as CP
+    say("swiglu", rows, cols)
+    rg = np.random.default_rng(cols)
+    gt = W.normal(rg, (rows, cols), 0, 1, "bf16")
+    up = W.normal(rg, (rows, cols), 0, 1, "bf16")
+    out = empty_dev((rows, cols), "bf16")
+    g = dvm.Graph(ctx)
+    CP.swiglu(g, g.input(torch_dev(gt, "bf16")), g.input(torch_dev(up, "bf16")), out=out)
+    g.sync()
+    ok, d = N.check_bf16(host64(out), O.swiglu(gt, up))
+    assert ok, f"max ulp {d}"
+
+
+def _if_else(dvm, ctx, x, y):
+    dx, dy = torch_dev(x, "f32"), torch_dev(y, "f32")
+    s = empty_dev((), "f32")
+    g = dvm.Graph(ctx)
+    vx, vy = g.input(dx), g.input(dy)
+    g.op("reduce_sum", vx, out=s, live=True, axis=0x7FFFFFFF)
+    g.sync()
+    sv = float(s.item())
+    out = empty_dev(x.shape, "f32")
+    g.op("add" if sv > 0 else "sub", vx, vy, out=out, live=True)
+    g.sync()
+    return sv, host64(out)
+
+
+@pytest.mark.parametrize("n", [1, 2, 37, 1000])
+def test_if_else_add(dvm, ctx, n):
+    for i in range(2):
+        say("if_else_add", n, i)
+        x, y, sign = W.ifelse_inputs(n, i, (n, 4096))
+        sv, got = _if_else(dvm, ctx, x, y)
+        ref, branch, s64 = O.if_else_add(x, y)
+        band = O.sum_guard_band(x)
+        assert abs(s64) > band
+        assert abs(sv - s64) <= band
+        assert (sv > 0) == branch
+        assert np.array_equal(got, ref.astype(np.float32).astype(np.float64))
+
+
+def test_reduce_all_max_and_empty(dvm, ctx):
+    say("reduce_all_max")
+    x = W.normal(np.random.default_rng(3), (999, 31), 0, 1)
+    s = empty_dev((), "f32")
+    g = dvm.Graph(ctx)
+    g.op("reduce_max", g.input(torch_dev(x, "f32")), out=s, live=True, axis=0x7FFFFFFF)
+    g.sync()
+    assert float(s.item()) == float(x.max())
+
+
+def _collapsed_operands(shape, n):
+    st, acc = [], 1
+    for d in reversed(shape):
+        st.append(acc)
+        acc *= d
+    return [tuple(reversed(st))] * n
+
+
+@pytest.mark.parametrize("tmpl,shape", [("elemwise", (513, 1031)), ("rowreduce", (1000, 5120)),
+                                        ("rowreduce", (280, 3001)), ("elemwise", (3, 9)),
+                                        ("rowreduce", (777, 16))])
+def test_tilemap_bit_exact(dvm, ctx, tmpl, shape):
+    """The VM's element -> tile and tile -> workgroup maps equal the oracle's."""
+    import torch
+    say("tilemap", tmpl, shape)
+    x = torch.zeros(shape, dtype=torch.float32, device="cuda")
+    out = empty_dev(shape, "f32")
+    g = dvm.Graph(ctx)
+    vx = g.input(x)
+    if tmpl == "elemwise":
+        g.op("exp", vx, out=out, live=True)
+    else:
+        m = g.op("reduce_max", vx)
+        g.op("sub", vx, m, out=out, live=True)
+        g.release(m)
+    p = g.flush()
+    h = p.header()
+    R, Cc = h["R"], h["C"]
+    tiles = empty_dev((R, Cc), "f32")
+    wgs = empty_dev((R, Cc), "f32")
+    dbg = p.debug_tilemap(tiles, wgs)
+    dbg.launch()
+    torch.cuda.synchronize()
+    # oracle: same workload through the tiling rules
+    tm = TL.ELEMWISE if tmpl == "elemwise" else TL.ROWREDUCE
+    col = TL.collapse(tm, shape, _collapsed_operands(shape, 2))
+    ops = [TL.Operand(4, s_r, s_c, 0) for s_r, s_c in col[2]]
+    plan = TL.plan(tm, col[0], col[1], ops)
+    assert (h["tr"], h["tc"], h["block_dim"], h["body_tile"], h["grid"], h["g"], h["nv"]) == \
+        (plan.tr, plan.tc, plan.block_dim, plan.body_tile, plan.grid, plan.g, plan.nv)
+    et, ew = TL.element_tile_map(plan)
+    assert np.array_equal(host64(tiles), et)
+    assert np.array_equal(host64(wgs), ew)
