@@ -1,0 +1,250 @@
+"""Benchmark of the DVM hot path on one MI355X.
+
+A step is one pass of the whole path over one batch of synthetic input: for
+the LayerNorm stream (the metric's workload) that is 64 LayerNorm calls, each
+with a new row count R = B*S (B ~ U{1..32}, S ~ U{1..4096}) over H = 5120,
+each captured through the C ABI as a fused group, shape-tiled, encoded to
+bytecode on the host and run by the resident VM kernel.  The timed region
+includes capture, fusion decisions, encoding and launches; inputs are already
+in HBM.  Throughput counts algorithmic bytes: x read and y written (bf16) plus
+gamma/beta (fp32) per call.
+
+Prints one JSON line.  --config selects another workload for a separate run
+(sqrt_add, ifelse, stream); those lines use the same fields.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "VM-interpreted fused-op HBM GB/s (% of peak) + bytecode encode µs per graph"
+HBM_PEAK_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", default="layernorm", choices=["layernorm", "sqrt_add", "ifelse", "stream"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    return ap.parse_args()
+
+
+def pctl(xs, q):
+    return float(np.percentile(np.asarray(xs), q)) if len(xs) else 0.0
+
+
+# ---------------------------------------------------------------------------
+# LayerNorm stream
+# ---------------------------------------------------------------------------
+def layernorm_bench(args):
+    import torch
+    import device_bytecode_vm_amd as dvm
+    from device_bytecode_vm_amd import composites as CP
+    import workloads as W
+
+    shapes = W.layernorm_shapes(0, 64)
+    H = W.H_LN
+    ctx = dvm.Context(0)
+    stream = torch.cuda.current_stream()
+    xs = [W.device_normal((r, H), seed=1000 + i, dtype="bf16") for i, (r, _) in enumerate(shapes)]
+    gam = W.device_normal((H,), seed=1, mu=1.0, sd=0.1)
+    bet = W.device_normal((H,), seed=2, mu=0.0, sd=0.1)
+    rmax = max(r for r, _ in shapes)
+    ybuf = torch.empty((rmax, H), dtype=torch.bfloat16, device="cuda")
+    ys = [ybuf[:r] for r, _ in shapes]
+    call_bytes = [r * H * 2 * 2 + 2 * H * 4 for r, _ in shapes]
+    step_bytes = float(sum(call_bytes))
+    torch.cuda.synchronize()
+
+    def one_step(g):
+        for x, y in zip(xs, ys):
+            CP.layer_norm(g, g.input(x), g.input(gam), g.input(bet), W.LN_EPS, out=y)
+        g.flush_launch()
+
+    g = dvm.Graph(ctx, stream)
+    for _ in range(args.warmup):
+        one_step(g)
+    torch.cuda.synchronize()
+    s0 = g.stats()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        one_step(g)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    s1 = g.stats()
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    e2e_gbs = step_bytes * args.steps / (t1 - t0) / 1e9
+    graphs = s1["graphs"] - s0["graphs"]
+    enc_mean = (s1["encode_us_total"] - s0["encode_us_total"]) / max(graphs, 1)
+
+    # encode latency distribution: encode-only passes (no launch)
+    ectx = dvm.Context(-1)
+    enc_us = []
+    for rep in range(3):
+        for x, y in zip(xs, ys):
+            ge = dvm.Graph(ectx)
+            CP.layer_norm(ge, ge.input(x), ge.input(gam), ge.input(bet), W.LN_EPS, out=y)
+            tt0 = time.perf_counter()
+            p = ge.flush()
+            enc_us.append((time.perf_counter() - tt0) * 1e6)
+            del p
+
+    # kernel-only: pre-encoded programs, HIP events on the launch stream
+    progs = []
+    for x, y in zip(xs, ys):
+        gp = dvm.Graph(ctx, stream)
+        CP.layer_norm(gp, gp.input(x), gp.input(gam), gp.input(bet), W.LN_EPS, out=y)
+        progs.append(gp.flush())
+    for p in progs:
+        p.launch(stream)
+    torch.cuda.synchronize()
+    reps = max(1, min(args.steps, 5))
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in progs]
+    kern_ms = np.zeros(len(progs))
+    for _ in range(reps):
+        for p, (a, b) in zip(progs, ev):
+            a.record(stream)
+            p.launch(stream)
+            b.record(stream)
+        torch.cuda.synchronize()
+        kern_ms += np.array([a.elapsed_time(b) for a, b in ev])
+    kern_ms /= reps
+    kern_gbs = step_bytes / (kern_ms.sum() * 1e-3) / 1e9
+    hdr = progs[int(np.argmax([r for r, _ in shapes]))].header()
+
+    out = {
+        "metric": METRIC, "value": round(e2e_gbs, 2), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "layernorm_stream", "calls_per_step": 64, "hidden": H,
+                   "rows": "R=B*S, B~U{1..32}, S~U{1..4096}, seed 0",
+                   "rows_total_per_step": int(sum(r for r, _ in shapes)), "eps": W.LN_EPS,
+                   "x_dtype": "bf16", "gamma_beta_dtype": "f32", "y_dtype": "bf16"},
+        "encode_us": {"p50": round(pctl(enc_us, 50), 2), "p99": round(pctl(enc_us, 99), 2),
+                      "max": round(max(enc_us), 2), "mean_in_stream": round(enc_mean, 2)},
+        "device_only_gbs": round(kern_gbs, 2),
+        "graphs_per_step": graphs / args.steps,
+        "roofline": {"bound": "hbm", "achieved": round(kern_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(kern_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "dvm_vm_vector", "launches_per_step": len(progs),
+                     "avg_launch_us": round(float(kern_ms.mean()) * 1e3, 3),
+                     "bytes_per_launch_avg": round(step_bytes / len(progs), 1)},
+        "largest_call_header": {k: hdr[k] for k in ("block_dim", "body_tile", "grid", "tr", "tc", "g", "nv",
+                                                    "n_instr")},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = layernorm_cpu_baseline(args.cpu_seconds)
+    return out
+
+
+def layernorm_cpu_baseline(budget_s):
+    """The oracle's LayerNorm (numpy fp64) on a bounded sample of the same
+    workload: the first calls of the stream, row-sampled to fit the budget."""
+    from oracle import ops as O
+    import workloads as W
+    shapes = W.layernorm_shapes(0, 64)
+    gam, bet = W.layernorm_params()
+    H = W.H_LN
+    done_rows, t_total, calls = 0, 0.0, 0
+    for i, (r, _) in enumerate(shapes):
+        rows = min(r, 4096)
+        x = W.layernorm_x(0, i, rows, H)
+        t0 = time.perf_counter()
+        O.layer_norm(x, gam, bet, W.LN_EPS)
+        t_total += time.perf_counter() - t0
+        done_rows += rows
+        calls += 1
+        if t_total >= budget_s:
+            break
+    gbs = done_rows * H * 4 / t_total / 1e9
+    return {"value": round(gbs, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{calls} calls of the LayerNorm stream, first min(R, 4096) rows each "
+                      f"({done_rows} rows x 5120), numpy fp64, {t_total:.1f} s"}
+
+
+# ---------------------------------------------------------------------------
+# other workloads (separate runs)
+# ---------------------------------------------------------------------------
+def sqrt_add_bench(args):
+    import torch
+    import device_bytecode_vm_amd as dvm
+    import workloads as W
+    ctx = dvm.Context(0)
+    stream = torch.cuda.current_stream()
+    a = W.device_uniform((513, 1031), 1)
+    b = W.device_uniform((513, 1031), 2)
+    c = torch.empty_like(a)
+    nbytes = 3 * a.numel() * 4
+    g = dvm.Graph(ctx, stream)
+
+    def one():
+        t = g.op("add", g.input(a), g.input(b))
+        g.op("sqrt", t, out=c, live=True)
+        g.release(t)
+        g.flush_launch()
+
+    for _ in range(args.warmup):
+        one()
+    torch.cuda.synchronize()
+    n = max(args.steps, 1) * 50
+    t0 = time.perf_counter()
+    for _ in range(n):
+        one()
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / n
+    gp = dvm.Graph(ctx, stream)
+    t = gp.op("add", gp.input(a), gp.input(b))
+    gp.op("sqrt", t, out=c, live=True)
+    gp.release(t)
+    p = gp.flush()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for _ in range(10):
+        p.launch(stream)
+    e0.record(stream)
+    for _ in range(200):
+        p.launch(stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    kus = e0.elapsed_time(e1) / 200 * 1e3
+    return {"metric": METRIC, "value": round(nbytes / dt / 1e9, 2), "unit": "GB/s", "n_gpus": 1,
+            "steps": n, "warmup": args.warmup, "ms_per_step": round(dt * 1e3, 4), "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+            "config": {"workload": "sqrt_add", "shape": [513, 1031]},
+            "device_only_gbs": round(nbytes / (kus * 1e-6) / 1e9, 2), "kernel_us_warm": round(kus, 3),
+            "header": p.header()}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this build has no "
+              "multi-GPU path", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    if args.config == "layernorm":
+        out = layernorm_bench(args)
+    elif args.config == "sqrt_add":
+        out = sqrt_add_bench(args)
+    else:
+        print(f"config {args.config} not available yet", file=sys.stderr)
+        sys.exit(2)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -317,6 +317,7 @@ struct Val {
   bool pending = false;   // produced by an op in the buffered graph or the open group
   bool stored = false;    // materialised in its storage by a flushed graph
   bool lost = false;      // its graph was flushed without storing it
+  int uses = 0;           // inputs of ops still in the buffer or the open group
 };
 
 struct OpRec {
@@ -401,6 +402,22 @@ void recycle(dvm_graph* g, int64_t s) {
   Val& v = g->vals[s];
   v.alive = false;
   g->free_slots.push_back(s);
+}
+
+// A released value's slot is reused only once no buffered op refers to it.
+void maybe_recycle(dvm_graph* g, int64_t s) {
+  Val& v = g->vals[s];
+  if (v.alive && v.released && !v.pending && v.uses == 0) recycle(g, s);
+}
+
+// The ops leave the buffer (flushed or rejected): drop their input references.
+void drop_uses(dvm_graph* g, const std::vector<OpRec>& ops) {
+  for (auto& o : ops)
+    for (int k = 0; k < o.n_in; ++k) g->vals[o.in[k]].uses--;
+  for (auto& o : ops) {
+    for (int k = 0; k < o.n_in; ++k) maybe_recycle(g, o.in[k]);
+    maybe_recycle(g, o.out);
+  }
 }
 
 // ===========================================================================
@@ -1188,9 +1205,10 @@ dvm_status encode_buffer(dvm_graph* g, dvm_program** out) {
     const bool stored = st == DVM_OK && (v.live || !v.released) && v.t.data;
     v.stored = stored;
     v.lost = !stored;
-    if (v.released) recycle(g, o.out);
   }
-  g->buf.clear();
+  std::vector<OpRec> done;
+  done.swap(g->buf);
+  drop_uses(g, done);
   auto t1 = std::chrono::steady_clock::now();
   const double us = std::chrono::duration<double, std::micro>(t1 - t0).count();
   g->stats.graphs++;
@@ -1309,6 +1327,7 @@ dvm_status end_group_impl(dvm_graph* g, int32_t* flushed) {
       v.pending = false;
       v.lost = true;
     }
+    drop_uses(g, grp);
     return fail(DVM_ERR_UNSUPPORTED, "group cannot run on the VM (rule %d)", why);
   }
   g->buf = std::move(grp);
@@ -1452,6 +1471,7 @@ dvm_status dvm_graph_add_op(dvm_graph* g, int32_t op, const dvm_value* in, int32
   v.pending = true;
   r.out = slot;
   *out_value = handle(g, slot);
+  for (int k = 0; k < n_in; ++k) g->vals[r.in[k]].uses++;
   g->grp.push_back(r);
   if (!g->in_group) {
     int32_t fl;
@@ -1465,7 +1485,7 @@ dvm_status dvm_graph_release(dvm_graph* g, dvm_value h) {
   if (!g || !resolve(g, h, &s)) return fail(DVM_ERR_INVALID_ARG, "unknown value");
   Val& v = g->vals[s];
   v.released = true;
-  if (!v.pending) recycle(g, s);
+  maybe_recycle(g, s);
   return DVM_OK;
 }
 
