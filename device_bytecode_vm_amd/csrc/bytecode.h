@@ -25,9 +25,9 @@ constexpr uint32_t VERSION = 1;
 
 // Device geometry constants: one workgroup of T lanes runs a tile; a tile row
 // is spread over g lanes, each holding up to NV_MAX chunks of V elements.
-constexpr int T_LANES = 256;
+constexpr int T_LANES = 512;
 constexpr int VEC = 8;
-constexpr int NV_MAX = 4;
+constexpr int NV_MAX = 2;
 constexpr int E_MAX = VEC * NV_MAX;   // elements per lane per tile register
 constexpr int N_TREG = 3;             // tile registers: 0 = ACC, 1..2 slots
 constexpr int N_RREG = 4;             // row registers
@@ -70,7 +70,21 @@ enum Hdr : int {
   H_ALL_SCRATCH = 24,// reduce-all: arg index of the scratch (counter + partials)
   H_N_INSTR = 25,
   H_FLAGS = 26,
+  H_LDS_BYTES = 27,  // dynamic LDS of the launch (staging areas below)
+  H_PF_OFF0 = 28,    // byte offset of prefetch slot 0 / 1 (double-buffered next-tile loads)
+  H_PF_OFF1 = 29,
+  H_INV_OFF0 = 30,   // byte offset of LDS-resident invariant operand 0 / 1
+  H_INV_OFF1 = 31,
 };
+
+// LDS staging (per workgroup, dynamic):
+//  * prefetch slot: two buffers (tile parity) of NV chunks x T lanes x 16 bytes
+//    x (element size / 2) halves; lane t's data for chunk j, half h sits at
+//    ((j * halves + h) * T + t) * 16, written by a direct-to-LDS buffer load of
+//    that lane and read back by the same lane;
+//  * invariant slot: an operand that is the same for every tile, held as fp32,
+//    NV chunks x T lanes x 32 bytes, lane-private.
+constexpr uint32_t LDS_BUDGET = 150u * 1024u;  // one workgroup per CU
 
 // Argument table entry (8 words): pointer, dtype, flags, column stride, row
 // stride (elements, in the collapsed [R, C] iteration space) and the byte
@@ -105,6 +119,8 @@ enum Op : uint32_t {
   OP_ALL_FIN = 14,   // tile partial from LDS buffer b -> scratch[tile]
   OP_BCAST = 15,     // treg[dst] <- rreg[a] broadcast along the row (Broadcast)
   OP_DBG = 16,       // treg[dst] <- tile id (sub 0) / workgroup id (sub 1)
+  OP_LDS_INV = 17,   // prologue: invariant slot dst <- arg[w1] (fp32, lane-private)
+  OP_PF = 18,        // prologue: prefetch slot b <- arg[w1] for the first tile
   OP_COUNT
 };
 
@@ -132,7 +148,19 @@ __host__ __device__ constexpr uint32_t f_b(uint32_t w) { return (w >> 16) & 0xfu
 __host__ __device__ constexpr uint32_t f_sub(uint32_t w) { return (w >> 20) & 0xfu; }
 __host__ __device__ constexpr uint32_t f_bk(uint32_t w) { return (w >> 24) & 0xfu; }
 __host__ __device__ constexpr uint32_t f_flags(uint32_t w) { return (w >> 28) & 0xfu; }
-constexpr uint32_t FL_REV = 1u;  // BIN: B (op) ACC instead of ACC (op) B
+constexpr uint32_t FL_REV = 1u;    // BIN: B (op) ACC instead of ACC (op) B
+constexpr uint32_t FL_PF = 2u;     // LOAD / BIN BK_MEM: read the operand from prefetch slot b
+constexpr uint32_t FL_ISSUE = 4u;  // ... then prefetch the workgroup's next tile into the other buffer
+constexpr uint32_t FL_INV = 8u;    // LOAD / BIN BK_MEM: read the operand from invariant slot b
+
+// Prefetch reads wait with vmcnt(n), n = a lower bound (computed by the
+// encoder for full tiles) on the vector-memory instructions this wave issued
+// after the prefetch being read; vmcnt retires in issue order, so the wait
+// covers the prefetch without waiting for later stores.  LOAD keeps n in
+// fields a | sub << 4, BIN (memory operand) in dst | a << 4.
+__host__ __device__ constexpr uint32_t vmc_load(uint32_t w) { return ((w >> 12) & 0xfu) | (((w >> 20) & 0xfu) << 4); }
+__host__ __device__ constexpr uint32_t vmc_bin(uint32_t w) { return ((w >> 8) & 0xfu) | (((w >> 12) & 0xfu) << 4); }
+constexpr uint32_t VMC_MAX = 63;
 
 struct Program {
   uint32_t w[MAX_WORDS];

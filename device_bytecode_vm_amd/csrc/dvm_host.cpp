@@ -123,13 +123,13 @@ int64_t extent_bytes(const dvm_tensor& t) {
 //    width one wave moves with 16-byte accesses of the narrowest type;
 //  * the shrink path goes outer -> inner (rows first, then columns) by
 //    doubling the split count k;
-//  * cost in integer ticks (1/31250 us): G = 512 resident workgroups,
-//    A = 15625 ticks per tile, 2 ticks per byte per workgroup;
-//    cost = ceil(n_tiles / G) (A + 2 var_bytes) + 2 inv_bytes; least cost
-//    wins, earlier (larger) candidates win ties.
+//  * cost in integer ticks (1/31250 us): G = 256 resident workgroups (one
+//    per CU), A = 15625 ticks per tile, 1 tick per byte per workgroup;
+//    cost = ceil(n_tiles / G) (A + var_bytes) + inv_bytes; least cost wins,
+//    earlier (larger) candidates win ties.
 // ===========================================================================
 namespace tiling {
-constexpr int64_t T = T_LANES, V = VEC, NVM = NV_MAX, W = 64 * VEC, G = 512, A = 15625, BT = 2;
+constexpr int64_t T = T_LANES, V = VEC, NVM = NV_MAX, W = 64 * VEC, G = 256, A = 15625, BT = 1;
 
 struct Operand {
   int64_t esize, sr, sc, base_mod16;
@@ -711,6 +711,16 @@ struct Encoder {
   tiling::Plan plan;
   int n_red = 0;
   bool cross_wave = false;
+  std::vector<int> pf_slot, inv_slot;   // slot -> LDS staging slot (-1 none)
+  bool pf_issued[2] = {false, false};
+  struct Consume {
+    size_t pos;      // word index of the instruction in body
+    uint32_t slot;
+    bool is_bin;
+  };
+  std::vector<Consume> consumes;
+  long issue_pos[2] = {-1, -1};
+  std::vector<uint32_t> pro;            // prologue (once per workgroup)
 
   Encoder(dvm_graph* gr, const std::vector<OpRec>& o, dvm_program* p) : g(gr), ops(o), ck(gr, o), prog(p), W(p->prog.w) {}
 
@@ -818,7 +828,7 @@ struct Encoder {
       return DVM_OK;
     }
     // external, not in a register
-    emit(enc0(OP_LOAD, 0, 0, 0, 0, 0, 0), (uint32_t)arg_of[s]);
+    emit_load(0, s);
     return DVM_OK;
   }
 
@@ -929,7 +939,7 @@ struct Encoder {
       const uint32_t f = un_of(o);
       if (f != UN_IDENT) emit(enc0(OP_UN, 0, 0, 0, f, 0, 0), 0);
     } else {
-      uint32_t bk, bi = 0, w1 = 0;
+      uint32_t bk, bi = 0, w1 = 0, mflags = 0;
       if (o.n_in == 1) {
         bk = BK_IMM;
         float s = o.scalar;
@@ -949,16 +959,18 @@ struct Encoder {
         // external tile operand: keep it in a free register if it is read again
         const int f = free_treg();
         if (n_uses[b] > 1 && live_after(b, i) && f >= 0) {
-          emit(enc0(OP_LOAD, f, 0, 0, 0, 0, 0), (uint32_t)arg_of[b]);
+          emit_load(f, b);
           bind_t(f, b);
           bk = BK_TREG;
           bi = (uint32_t)f;
         } else {
           bk = BK_MEM;
           w1 = (uint32_t)arg_of[b];
+          mflags = src_flags(b, &bi);
         }
       }
-      emit(enc0(OP_BIN, 0, 0, bi, alu_of(o.op), bk, rev ? FL_REV : 0), w1);
+      emit(enc0(OP_BIN, 0, 0, bi, alu_of(o.op), bk, (rev ? FL_REV : 0) | mflags), w1);
+      if (bk == BK_MEM) note_consume(mflags, bi, true);
     }
     free_dead(i);
     if (treg[0] >= 0 && treg[0] != o.out) unbind_t(0);
@@ -1022,7 +1034,7 @@ struct Encoder {
       if (st != DVM_OK) return st;
       f = 0;
     }
-    emit(enc0(OP_LOAD, f, 0, 0, 0, 0, 0), (uint32_t)arg_of[s]);
+    emit_load(f, s);
     bind_t(f, s);
     *k = f;
     return DVM_OK;
@@ -1067,6 +1079,136 @@ struct Encoder {
     return DVM_OK;
   }
 
+  // Flags and staging slot for a read of external operand s.
+  uint32_t src_flags(int64_t s, uint32_t* slot) {
+    *slot = 0;
+    if (inv_slot[s] >= 0) {
+      *slot = (uint32_t)inv_slot[s];
+      return FL_INV;
+    }
+    if (pf_slot[s] >= 0) {
+      *slot = (uint32_t)pf_slot[s];
+      uint32_t f = FL_PF;
+      if (!pf_issued[*slot]) {
+        pf_issued[*slot] = true;
+        f |= FL_ISSUE;
+      }
+      return f;
+    }
+    return 0;
+  }
+
+  void note_consume(uint32_t f, uint32_t slot, bool is_bin) {
+    if (!(f & FL_PF)) return;
+    const size_t pos = body.size() - 2;
+    consumes.push_back({pos, slot, is_bin});
+    if (f & FL_ISSUE) issue_pos[slot] = (long)pos;
+  }
+
+  void emit_load(int k, int64_t s) {
+    uint32_t slot;
+    const uint32_t f = src_flags(s, &slot);
+    emit(enc0(OP_LOAD, k, 0, slot, 0, 0, f), (uint32_t)arg_of[s]);
+    note_consume(f, slot, false);
+  }
+
+  // Lower bound of the vector-memory instructions one wave issues for an
+  // instruction in a full tile (the VM's 128-bit paths; ragged tiles take the
+  // element paths and issue more).
+  uint32_t halves(uint32_t arg) const { return W[ARG_BASE + arg * ARG_WORDS + A_DTYPE] == DT_F32 ? 2u : 1u; }
+  uint32_t load_ops(uint32_t arg) const {
+    const uint32_t* a = W + ARG_BASE + arg * ARG_WORDS;
+    const int32_t sc = (int32_t)a[A_SC];
+    if ((a[A_FLAGS] & AF_VEC) && sc == 1) return (uint32_t)plan.nv * halves(arg);
+    if (sc == 0) return 1u;
+    return 8u * (uint32_t)plan.nv;
+  }
+  uint32_t store_ops(uint32_t arg) const {
+    const uint32_t* a = W + ARG_BASE + arg * ARG_WORDS;
+    if ((a[A_FLAGS] & AF_VEC) && (int32_t)a[A_SC] == 1) return (uint32_t)plan.nv * halves(arg);
+    return 8u * (uint32_t)plan.nv;
+  }
+  uint32_t src_ops(uint32_t w0, uint32_t w1) const {
+    const uint32_t f = f_flags(w0);
+    if (f & FL_INV) return 0;
+    if (f & FL_PF) return (f & FL_ISSUE) ? (uint32_t)plan.nv * halves(w1) : 0u;
+    return load_ops(w1);
+  }
+  uint32_t vm_ops(uint32_t w0, uint32_t w1) const {
+    switch (f_op(w0)) {
+      case OP_LOAD: return src_ops(w0, w1);
+      case OP_BIN: return f_bk(w0) == BK_MEM ? src_ops(w0, w1) : 0u;
+      case OP_STORE: return store_ops(w1);
+      case OP_LOAD_ROW:
+      case OP_STORE_ROW: return 1u;
+      case OP_PF: return (uint32_t)plan.nv * halves(w1);
+      case OP_LDS_INV: return load_ops(w1);
+      default: return 0u;
+    }
+  }
+
+  // Wait counts of prefetch reads: instructions issued after the prefetch of
+  // the tile being read, counted over the end of the previous tile's body (or
+  // the prologue, for the first tile) plus this body up to the read.
+  void patch_waits() {
+    auto sum = [&](const std::vector<uint32_t>& v, size_t lo, size_t hi) {
+      uint32_t n = 0;
+      for (size_t q = lo; q < hi; q += 2) n += vm_ops(v[q], v[q + 1]);
+      return n;
+    };
+    for (const Consume& c : consumes) {
+      const size_t ip = (size_t)issue_pos[c.slot];
+      const uint32_t after_issue = sum(body, ip + 2, body.size());
+      size_t pp = 0;
+      for (size_t q = 0; q < pro.size(); q += 2)
+        if (f_op(pro[q]) == OP_PF && f_b(pro[q]) == c.slot) pp = q;
+      const uint32_t after_pro = sum(pro, pp + 2, pro.size());
+      uint32_t n = std::min(after_issue, after_pro) + sum(body, 0, c.pos);
+      n = std::min<uint32_t>(n, VMC_MAX);
+      uint32_t& w = body[c.pos];
+      if (c.is_bin) w = (w & ~0xff00u) | ((n & 0xfu) << 8) | (((n >> 4) & 0xfu) << 12);
+      else w = (w & ~0x00f0f000u) | ((n & 0xfu) << 12) | (((n >> 4) & 0xfu) << 20);
+    }
+  }
+
+  // LDS staging (worth it when a workgroup runs several tiles): tile-invariant
+  // operands are held in LDS once per workgroup; tile-varying streamed
+  // operands are prefetched one tile ahead into LDS by direct-to-LDS loads.
+  void decide_lds(const std::vector<int64_t>& exts, const std::vector<std::pair<int64_t, int64_t>>& st) {
+    uint32_t off = 0;
+    int n_pf = 0, n_inv = 0;
+    if (plan.body_tile >= 2) {
+      for (size_t q = 0; q < exts.size(); ++q) {
+        const int64_t s = exts[q];
+        if (cls[s] != 1) continue;
+        const int64_t sr = st[q].first, sc = st[q].second;
+        const int es = esize(g->vals[s].t.dtype);
+        const bool invariant = (sr == 0 || plan.n_r == 1) && (sc == 0 || plan.n_c == 1);
+        const uint32_t* a = W + ARG_BASE + arg_of[s] * ARG_WORDS;
+        if (invariant && n_inv < 2) {
+          const uint32_t sz = (uint32_t)plan.nv * T_LANES * 32u;
+          if (off + sz > LDS_BUDGET) continue;
+          inv_slot[s] = n_inv;
+          W[H_INV_OFF0 + n_inv] = off;
+          off += sz;
+          pro.push_back(enc0(OP_LDS_INV, n_inv, 0, 0, 0, 0, 0));
+          pro.push_back((uint32_t)arg_of[s]);
+          ++n_inv;
+        } else if (!invariant && n_pf < 2 && (a[A_FLAGS] & AF_VEC) && sc == 1 && (es == 2 || es == 4)) {
+          const uint32_t sz = 2u * (uint32_t)plan.nv * T_LANES * 16u * (uint32_t)(es / 2);
+          if (off + sz > LDS_BUDGET) continue;
+          pf_slot[s] = n_pf;
+          W[H_PF_OFF0 + n_pf] = off;
+          off += sz;
+          pro.insert(pro.begin(), (uint32_t)arg_of[s]);
+          pro.insert(pro.begin(), enc0(OP_PF, 0, 0, n_pf, 0, 0, 0));
+          ++n_pf;
+        }
+      }
+    }
+    W[H_LDS_BYTES] = off;
+  }
+
   dvm_status run() {
     std::memset(W, 0, sizeof(uint32_t) * HDR_WORDS);
     const size_t n = g->vals.size();
@@ -1076,6 +1218,8 @@ struct Encoder {
     tloc.assign(n, -1);
     rloc.assign(n, -1);
     store_it.assign(n, 0);
+    pf_slot.assign(n, -1);
+    inv_slot.assign(n, -1);
     for (int k = 0; k < N_TREG; ++k) treg[k] = -1;
     for (int k = 0; k < N_RREG; ++k) rreg[k] = -1;
     for (size_t i = 0; i < ops.size(); ++i)
@@ -1113,9 +1257,13 @@ struct Encoder {
     }
     if (operands.size() + 2 > (size_t)MAX_ARGS) return fail(DVM_ERR_RESOURCE, "too many operands");
     for (size_t q = 0; q < operands.size(); ++q) add_arg(operands[q], st[q].first, st[q].second);
-    (void)n_ext;
     cls.clear();
     ck.classes(&cls);
+    {
+      std::vector<int64_t> exts(operands.begin(), operands.begin() + n_ext);
+      std::vector<std::pair<int64_t, int64_t>> est(st.begin(), st.begin() + n_ext);
+      decide_lds(exts, est);
+    }
     // reduce-all output and scratch
     if (tm == TM_ALLREDUCE) {
       const OpRec& last = ops.back();
@@ -1146,13 +1294,16 @@ struct Encoder {
       else s = tile_op((int)i);
       if (s != DVM_OK) return s;
     }
+    patch_waits();
     // Sync at the end of the body when the next tile's first cross-wave
     // reduction could overwrite an LDS buffer some wave is still reading.
     if (cross_wave && n_red < 2) emit(enc0(OP_SYNC, 0, 0, 0, 0, 0, 0), 0);
     // header
     const uint32_t instr_base = ARG_BASE + (uint32_t)n_args * ARG_WORDS;
-    if (instr_base + body.size() > (size_t)MAX_WORDS) return fail(DVM_ERR_RESOURCE, "program too large");
-    std::copy(body.begin(), body.end(), W + instr_base);
+    const uint32_t body_base = instr_base + (uint32_t)pro.size();
+    if (body_base + body.size() > (size_t)MAX_WORDS) return fail(DVM_ERR_RESOURCE, "program too large");
+    std::copy(pro.begin(), pro.end(), W + instr_base);
+    std::copy(body.begin(), body.end(), W + body_base);
     W[H_MAGIC] = MAGIC;
     W[H_VERSION] = VERSION;
     W[H_KTYPE] = KT_VECTOR;
@@ -1168,16 +1319,16 @@ struct Encoder {
     W[H_NC] = (uint32_t)(plan.n_c ? plan.n_c : 1);
     W[H_NARGS] = (uint32_t)n_args;
     W[H_PRO_BEGIN] = instr_base;
-    W[H_PRO_END] = instr_base;
-    W[H_BODY_BEGIN] = instr_base;
-    W[H_BODY_END] = instr_base + (uint32_t)body.size();
+    W[H_PRO_END] = body_base;
+    W[H_BODY_BEGIN] = body_base;
+    W[H_BODY_END] = body_base + (uint32_t)body.size();
     W[H_R_LO] = (uint32_t)(uint64_t)R;
     W[H_R_HI] = (uint32_t)((uint64_t)R >> 32);
     W[H_C_LO] = (uint32_t)(uint64_t)C;
     W[H_C_HI] = (uint32_t)((uint64_t)C >> 32);
-    W[H_N_INSTR] = (uint32_t)(body.size() / 2);
-    prog->n_words = instr_base + (uint32_t)body.size();
-    prog->n_instr = (uint32_t)(body.size() / 2);
+    W[H_N_INSTR] = (uint32_t)((pro.size() + body.size()) / 2);
+    prog->n_words = body_base + (uint32_t)body.size();
+    prog->n_instr = (uint32_t)((pro.size() + body.size()) / 2);
     prog->R = R;
     prog->C = C;
     prog->pad = (uint32_t)plan.pad;
@@ -1568,6 +1719,7 @@ dvm_status dvm_program_debug_tilemap(const dvm_program* p, const dvm_tensor* til
   const uint32_t n_args = 2;
   W[H_NARGS] = n_args;
   W[H_TEMPLATE] = TM_ELEMWISE;  // same tiling; no reduce-all epilogue
+  W[H_LDS_BYTES] = 0;
   int k = 0;
   for (const dvm_tensor* t : {tile_out, wg_out}) {
     uint32_t* a = W + ARG_BASE + k * ARG_WORDS;

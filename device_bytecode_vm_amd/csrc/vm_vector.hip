@@ -164,23 +164,26 @@ __device__ __forceinline__ float una_rt(uint32_t f, float x) {
   }
 }
 
-// row registers: one value per lane (the lane's row); the index is wave-uniform
-__device__ __forceinline__ float rget(const float (&rw)[N_RREG], uint32_t i) {
-  float v = rw[0];
-  v = i == 1 ? rw[1] : v;
-  v = i == 2 ? rw[2] : v;
-  v = i == 3 ? rw[3] : v;
-  return v;
+// Row registers: one value per lane (the lane's row).  Four named variables,
+// not an array, so that a wave-uniform index selects among registers instead
+// of becoming an indexed private (scratch) access.
+struct RowRegs {
+  float r0, r1, r2, r3;
+};
+__device__ __forceinline__ float rget(const RowRegs& rw, uint32_t i) {
+  const float a = (i & 1u) ? rw.r1 : rw.r0;
+  const float b = (i & 1u) ? rw.r3 : rw.r2;
+  return (i & 2u) ? b : a;
 }
-__device__ __forceinline__ void rset(float (&rw)[N_RREG], uint32_t i, float v) {
-  rw[0] = i == 0 ? v : rw[0];
-  rw[1] = i == 1 ? v : rw[1];
-  rw[2] = i == 2 ? v : rw[2];
-  rw[3] = i == 3 ? v : rw[3];
+__device__ __forceinline__ void rset(RowRegs& rw, uint32_t i, float v) {
+  if (i == 0) rw.r0 = v;
+  else if (i == 1) rw.r1 = v;
+  else if (i == 2) rw.r2 = v;
+  else rw.r3 = v;
 }
 
-typedef float Chunks[E_MAX];
-typedef float TReg[N_TREG][E_MAX];
+typedef float Chunks __attribute__((ext_vector_type(E_MAX)));
+typedef Chunks TReg[N_TREG];
 
 // Lane coordinates inside the tile.
 struct Lane {
@@ -212,7 +215,7 @@ __device__ __forceinline__ void load_chunks(Chunks& dst, const ArgD& a, const Ge
     // full chunks, 16-byte aligned: 128-bit accesses; a chunk is wholly in or out
 #pragma unroll
     for (int j = 0; j < NV_MAX; ++j) {
-      if (j < G.nv) {
+      {  // chunks past the row's last one fall out of range and are masked
         const int ct = (j * G.g + L.lane) * VEC;
         const int off = (L.rok && ct < tl.tce) ? (roff + ct) * ES : OOB;
         if constexpr (DT == DT_F32) {
@@ -242,7 +245,7 @@ __device__ __forceinline__ void load_chunks(Chunks& dst, const ArgD& a, const Ge
     // element path: ragged tiles, unaligned or strided operands
 #pragma unroll
     for (int j = 0; j < NV_MAX; ++j) {
-      if (j < G.nv) {
+      {
         const int ct = (j * G.g + L.lane) * VEC;
 #pragma unroll
         for (int i = 0; i < VEC; ++i) {
@@ -268,7 +271,7 @@ __device__ __forceinline__ void store_chunks(const Chunks& src, const ArgD& a, c
   if ((a.fl & AF_VEC) && a.sc == 1 && (tl.tce & (VEC - 1)) == 0) {
 #pragma unroll
     for (int j = 0; j < NV_MAX; ++j) {
-      if (j < G.nv) {
+      {  // chunks past the row's last one fall out of range and are masked
         const int ct = (j * G.g + L.lane) * VEC;
         const int off = (L.rok && ct < tl.tce) ? (roff + ct) * ES : OOB;
         if constexpr (DT == DT_F32) {
@@ -300,7 +303,7 @@ __device__ __forceinline__ void store_chunks(const Chunks& src, const ArgD& a, c
   } else {
 #pragma unroll
     for (int j = 0; j < NV_MAX; ++j) {
-      if (j < G.nv) {
+      {
         const int ct = (j * G.g + L.lane) * VEC;
 #pragma unroll
         for (int i = 0; i < VEC; ++i) {
@@ -336,7 +339,6 @@ __device__ __forceinline__ void store_any(const Chunks& src, const ArgD& a, cons
 __device__ __forceinline__ void copy_c(Chunks& d, const Chunks& s, int nv) {
 #pragma unroll
   for (int j = 0; j < NV_MAX; ++j)
-    if (j < nv)
 #pragma unroll
       for (int i = 0; i < VEC; ++i) d[j * VEC + i] = s[j * VEC + i];
 }
@@ -346,7 +348,6 @@ template <uint32_t OPK, bool REV>
 __device__ __forceinline__ void bin_cc(Chunks& acc, const Chunks& b, int nv) {
 #pragma unroll
   for (int j = 0; j < NV_MAX; ++j)
-    if (j < nv)
 #pragma unroll
       for (int i = 0; i < VEC; ++i) {
         const float x = acc[j * VEC + i], y = b[j * VEC + i];
@@ -358,7 +359,6 @@ template <uint32_t OPK, bool REV>
 __device__ __forceinline__ void bin_cs(Chunks& acc, float s, int nv) {
 #pragma unroll
   for (int j = 0; j < NV_MAX; ++j)
-    if (j < nv)
 #pragma unroll
       for (int i = 0; i < VEC; ++i) {
         const float x = acc[j * VEC + i];
@@ -370,14 +370,13 @@ template <uint32_t F>
 __device__ __forceinline__ void un_c(Chunks& acc, int nv) {
 #pragma unroll
   for (int j = 0; j < NV_MAX; ++j)
-    if (j < nv)
 #pragma unroll
       for (int i = 0; i < VEC; ++i) acc[j * VEC + i] = una<F>(acc[j * VEC + i]);
 }
 
 template <uint32_t OPK>
-__device__ __forceinline__ void bin_op(TReg& t, uint32_t w0, uint32_t w1, float rowv, const ArgD* mem,
-                                       const Geo& G, const Tile& tl, const Lane& L) {
+__device__ __forceinline__ void bin_op(TReg& t, uint32_t w0, uint32_t w1, float rowv, const Chunks& memv,
+                                       const Geo& G) {
   const uint32_t bk = f_bk(w0), b = f_b(w0);
   const bool rev = (f_flags(w0) & FL_REV) != 0;
   const int nv = G.nv;
@@ -391,10 +390,8 @@ __device__ __forceinline__ void bin_op(TReg& t, uint32_t w0, uint32_t w1, float 
       default: bin_cc<OPK, true>(t[0], t[2], nv); break;
     }
   } else if (bk == BK_MEM) {
-    Chunks tmp;
-    load_any(tmp, *mem, G, tl, L);
-    if (rev) bin_cc<OPK, true>(t[0], tmp, nv);
-    else bin_cc<OPK, false>(t[0], tmp, nv);
+    if (rev) bin_cc<OPK, true>(t[0], memv, nv);
+    else bin_cc<OPK, false>(t[0], memv, nv);
   } else {
     const float s = bk == BK_RREG ? rowv : __uint_as_float(w1);
     if (rev) bin_cs<OPK, true>(t[0], s, nv);
@@ -403,8 +400,8 @@ __device__ __forceinline__ void bin_op(TReg& t, uint32_t w0, uint32_t w1, float 
 }
 
 // ---------------------------------------------------------------------------
-// Cross-lane reductions: ds_swizzle butterflies inside 32 lanes, a lane
-// exchange across the two halves of the wave, LDS across waves.
+// Cross-lane reductions: DPP and permlane swaps inside a wave, LDS across
+// waves.
 // ---------------------------------------------------------------------------
 template <uint32_t KIND>
 __device__ __forceinline__ float comb(float a, float b) {
@@ -412,19 +409,29 @@ __device__ __forceinline__ float comb(float a, float b) {
   else return (a != a || b != b) ? a + b : fmaxf(a, b);
 }
 
-template <int XOR>
-__device__ __forceinline__ float swz(float v) {
-  return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), (XOR << 10) | 0x1f));
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
 }
 
+// Symmetric all-reduce over aligned groups of gs lanes (gs a power of two <=
+// 64): DPP quad permutes and row mirrors inside 16 lanes, then the gfx950
+// permlane16/permlane32 swaps across rows and wave halves.  Each step pairs
+// every lane with one lane of the other half of its group.
 template <uint32_t KIND>
 __device__ __forceinline__ float group_reduce(float acc, int gs) {
-  if (gs > 1) acc = comb<KIND>(acc, swz<1>(acc));
-  if (gs > 2) acc = comb<KIND>(acc, swz<2>(acc));
-  if (gs > 4) acc = comb<KIND>(acc, swz<4>(acc));
-  if (gs > 8) acc = comb<KIND>(acc, swz<8>(acc));
-  if (gs > 16) acc = comb<KIND>(acc, swz<16>(acc));
-  if (gs > 32) acc = comb<KIND>(acc, __shfl_xor(acc, 32, 64));
+  if (gs > 1) acc = comb<KIND>(acc, dpp<0xB1>(acc));   // quad_perm [1,0,3,2]
+  if (gs > 2) acc = comb<KIND>(acc, dpp<0x4E>(acc));   // quad_perm [2,3,0,1]
+  if (gs > 4) acc = comb<KIND>(acc, dpp<0x141>(acc));  // row_half_mirror
+  if (gs > 8) acc = comb<KIND>(acc, dpp<0x140>(acc));  // row_mirror
+  if (gs > 16) {
+    const auto p = __builtin_amdgcn_permlane16_swap(__float_as_int(acc), __float_as_int(acc), false, false);
+    acc = comb<KIND>(__int_as_float(p[0]), __int_as_float(p[1]));
+  }
+  if (gs > 32) {
+    const auto p = __builtin_amdgcn_permlane32_swap(__float_as_int(acc), __float_as_int(acc), false, false);
+    acc = comb<KIND>(__int_as_float(p[0]), __int_as_float(p[1]));
+  }
   return acc;
 }
 
@@ -436,8 +443,7 @@ __device__ __forceinline__ float lane_partial(const Chunks& c, const Geo& G, con
   float acc = id;
   if ((tl.tce & (VEC - 1)) == 0) {
 #pragma unroll
-    for (int j = 0; j < NV_MAX; ++j)
-      if (j < G.nv) {
+    for (int j = 0; j < NV_MAX; ++j) {
         float s = c[j * VEC];
 #pragma unroll
         for (int i = 1; i < VEC; ++i) s = comb<KIND>(s, c[j * VEC + i]);
@@ -446,8 +452,7 @@ __device__ __forceinline__ float lane_partial(const Chunks& c, const Geo& G, con
       }
   } else {
 #pragma unroll
-    for (int j = 0; j < NV_MAX; ++j)
-      if (j < G.nv) {
+    for (int j = 0; j < NV_MAX; ++j) {
         const int ct = (j * G.g + L.lane) * VEC;
 #pragma unroll
         for (int i = 0; i < VEC; ++i) acc = comb<KIND>(acc, (L.rok && ct + i < tl.tce) ? c[j * VEC + i] : id);
@@ -483,6 +488,171 @@ __device__ __forceinline__ void fill_c(Chunks& c, float v) {
   for (int e = 0; e < E_MAX; ++e) c[e] = v;
 }
 
+// ---------------------------------------------------------------------------
+// LDS staging: next-tile prefetch (direct-to-LDS buffer loads, two buffers
+// by tile parity) and LDS-resident tile-invariant operands.  Every lane reads
+// back exactly the bytes its own loads or stores put in LDS, so no barrier is
+// needed, only the wait for its own outstanding loads.
+// ---------------------------------------------------------------------------
+typedef __attribute__((address_space(3))) void lds_void;
+
+__device__ __forceinline__ Tile make_tile(const Geo& G, uint32_t id) {
+  Tile tl;
+  const uint32_t ir = id / (uint32_t)G.nc;
+  const uint32_t ic = id - ir * (uint32_t)G.nc;
+  tl.id = id;
+  tl.r0 = (int64_t)ir * G.tr;
+  tl.c0 = (int64_t)ic * G.tc;
+  const int64_t remc = G.C - tl.c0;
+  tl.tce = remc < G.tc ? (int)remc : G.tc;
+  const int64_t remr = G.R - tl.r0;
+  tl.tre = remr < G.tr ? (int)remr : G.tr;
+  return tl;
+}
+
+// a tile whose columns end on a chunk boundary is staged whole
+__device__ __forceinline__ bool tile_full(const Tile& tl) { return (tl.tce & (VEC - 1)) == 0; }
+
+__device__ __forceinline__ uint32_t pf_buf_bytes(const Geo& G, uint32_t dt) {
+  return (uint32_t)G.nv * T_LANES * 16u * (dt == DT_F32 ? 2u : 1u);
+}
+
+__device__ __forceinline__ void pf_issue(char* slot, const ArgD& a, const Geo& G, const Tile& tl, int tid) {
+  const int es = esize(a.dt);
+  const int halves = a.dt == DT_F32 ? 2 : 1;
+  char* base = slot + (tl.id & 1u) * pf_buf_bytes(G, a.dt);
+  const Rsrc rs = tile_rsrc(a, tl);
+  const int row = tid >> G.lg, lane = tid & (G.g - 1);
+  const bool rok = row < tl.tre;
+  const int roff = row * (int)a.sr;
+  const int wave = tid >> 6;
+#pragma unroll
+  for (int j = 0; j < NV_MAX; ++j) {
+    if (j < G.nv) {
+      const int ct = (j * G.g + lane) * VEC;
+      const int off = (rok && ct < tl.tce) ? (roff + ct) * es : OOB;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        if (h < halves) {
+          lds_void* dst = (lds_void*)(base + ((j * halves + h) * T_LANES + wave * 64) * 16);
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst, 16, off == OOB ? OOB : off + 16 * h, 0, 0, 0);
+        }
+      }
+    }
+  }
+}
+
+template <uint32_t DT>
+__device__ __forceinline__ void pf_read(Chunks& dst, const char* slot, const Geo& G, const Tile& tl, int tid) {
+  constexpr int HV = DT == DT_F32 ? 2 : 1;
+  const char* base = slot + (tl.id & 1u) * pf_buf_bytes(G, DT);
+#pragma unroll
+  for (int j = 0; j < NV_MAX; ++j) {
+    {  // a chunk past nv re-reads chunk 0 (its values are masked downstream)
+      const int jj = j < G.nv ? j : 0;
+      const u4 v = *(const u4*)(base + ((jj * HV) * T_LANES + tid) * 16);
+      if constexpr (DT == DT_F32) {
+        const u4 w = *(const u4*)(base + ((jj * HV + 1) * T_LANES + tid) * 16);
+        dst[j * VEC + 0] = __uint_as_float(v.x); dst[j * VEC + 1] = __uint_as_float(v.y);
+        dst[j * VEC + 2] = __uint_as_float(v.z); dst[j * VEC + 3] = __uint_as_float(v.w);
+        dst[j * VEC + 4] = __uint_as_float(w.x); dst[j * VEC + 5] = __uint_as_float(w.y);
+        dst[j * VEC + 6] = __uint_as_float(w.z); dst[j * VEC + 7] = __uint_as_float(w.w);
+      } else {
+        dst[j * VEC + 0] = bf2f(v.x & 0xffffu); dst[j * VEC + 1] = __uint_as_float(v.x & 0xffff0000u);
+        dst[j * VEC + 2] = bf2f(v.y & 0xffffu); dst[j * VEC + 3] = __uint_as_float(v.y & 0xffff0000u);
+        dst[j * VEC + 4] = bf2f(v.z & 0xffffu); dst[j * VEC + 5] = __uint_as_float(v.z & 0xffff0000u);
+        dst[j * VEC + 6] = bf2f(v.w & 0xffffu); dst[j * VEC + 7] = __uint_as_float(v.w & 0xffff0000u);
+      }
+    }
+  }
+}
+
+__device__ __forceinline__ void inv_write(const Chunks& c, char* slot, const Geo& G, int tid) {
+#pragma unroll
+  for (int j = 0; j < NV_MAX; ++j) {
+    if (j < G.nv) {
+      f4 a = {c[j * VEC + 0], c[j * VEC + 1], c[j * VEC + 2], c[j * VEC + 3]};
+      f4 b = {c[j * VEC + 4], c[j * VEC + 5], c[j * VEC + 6], c[j * VEC + 7]};
+      *(f4*)(slot + (j * T_LANES + tid) * 32) = a;
+      *(f4*)(slot + (j * T_LANES + tid) * 32 + 16) = b;
+    }
+  }
+}
+
+__device__ __forceinline__ void inv_read(Chunks& c, const char* slot, const Geo& G, int tid) {
+#pragma unroll
+  for (int j = 0; j < NV_MAX; ++j) {
+    {
+      const int jj = j < G.nv ? j : 0;
+      const f4 a = *(const f4*)(slot + (jj * T_LANES + tid) * 32);
+      const f4 b = *(const f4*)(slot + (jj * T_LANES + tid) * 32 + 16);
+      c[j * VEC + 0] = a.x; c[j * VEC + 1] = a.y; c[j * VEC + 2] = a.z; c[j * VEC + 3] = a.w;
+      c[j * VEC + 4] = b.x; c[j * VEC + 5] = b.y; c[j * VEC + 6] = b.z; c[j * VEC + 7] = b.w;
+    }
+  }
+}
+
+// s_waitcnt vmcnt(n) for a wave-uniform n (0..63): the count is an immediate
+// of the instruction, so a switch selects it.
+#define DVM_VMC_CASE(n) case n: asm volatile("s_waitcnt vmcnt(" #n ")" ::: "memory"); break;
+__device__ __forceinline__ void wait_vm(uint32_t n) {
+  switch (n) {
+    DVM_VMC_CASE(0) DVM_VMC_CASE(1) DVM_VMC_CASE(2) DVM_VMC_CASE(3) DVM_VMC_CASE(4) DVM_VMC_CASE(5)
+    DVM_VMC_CASE(6) DVM_VMC_CASE(7) DVM_VMC_CASE(8) DVM_VMC_CASE(9) DVM_VMC_CASE(10) DVM_VMC_CASE(11)
+    DVM_VMC_CASE(12) DVM_VMC_CASE(13) DVM_VMC_CASE(14) DVM_VMC_CASE(15) DVM_VMC_CASE(16) DVM_VMC_CASE(17)
+    DVM_VMC_CASE(18) DVM_VMC_CASE(19) DVM_VMC_CASE(20) DVM_VMC_CASE(21) DVM_VMC_CASE(22) DVM_VMC_CASE(23)
+    DVM_VMC_CASE(24) DVM_VMC_CASE(25) DVM_VMC_CASE(26) DVM_VMC_CASE(27) DVM_VMC_CASE(28) DVM_VMC_CASE(29)
+    DVM_VMC_CASE(30) DVM_VMC_CASE(31) DVM_VMC_CASE(32) DVM_VMC_CASE(33) DVM_VMC_CASE(34) DVM_VMC_CASE(35)
+    DVM_VMC_CASE(36) DVM_VMC_CASE(37) DVM_VMC_CASE(38) DVM_VMC_CASE(39) DVM_VMC_CASE(40) DVM_VMC_CASE(41)
+    DVM_VMC_CASE(42) DVM_VMC_CASE(43) DVM_VMC_CASE(44) DVM_VMC_CASE(45) DVM_VMC_CASE(46) DVM_VMC_CASE(47)
+    DVM_VMC_CASE(48) DVM_VMC_CASE(49) DVM_VMC_CASE(50) DVM_VMC_CASE(51) DVM_VMC_CASE(52) DVM_VMC_CASE(53)
+    DVM_VMC_CASE(54) DVM_VMC_CASE(55) DVM_VMC_CASE(56) DVM_VMC_CASE(57) DVM_VMC_CASE(58) DVM_VMC_CASE(59)
+    DVM_VMC_CASE(60) DVM_VMC_CASE(61) DVM_VMC_CASE(62)
+    default: asm volatile("s_waitcnt vmcnt(63)" ::: "memory"); break;
+  }
+}
+#undef DVM_VMC_CASE
+
+// Staging context shared by the operand readers; slot addresses are
+// re-derived from the header at each use (scalar loads) instead of being kept
+// live across the interpreter loop.
+struct Stage {
+  const uint32_t* W;
+  char* lds;
+  uint32_t tile, t_end;
+  int tid;
+  __device__ __forceinline__ char* pf(uint32_t k) const { return lds + W[H_PF_OFF0 + k]; }
+  __device__ __forceinline__ char* inv(uint32_t k) const { return lds + W[H_INV_OFF0 + k]; }
+};
+
+// Operand read for LOAD and memory operands: from an invariant slot, from the
+// prefetch slot (then prefetch the next tile), or straight from memory.
+__device__ __forceinline__ void read_operand(Chunks& dst, uint32_t w0, uint32_t vmc, const ArgD& a, const Geo& G,
+                                             const Tile& tl, const Lane& L, const Stage& S) {
+  const uint32_t fl = f_flags(w0), slot = f_b(w0) & 1u;
+  if (fl & FL_INV) {
+    inv_read(dst, S.inv(slot), G, S.tid);
+    return;
+  }
+  if (fl & FL_PF) {
+    if (tile_full(tl)) {
+      // the previous tile may have been ragged (more instructions issued after
+      // the prefetch): the count stays a lower bound, so the wait stays exact
+      wait_vm(vmc);
+      if (a.dt == DT_F32) pf_read<DT_F32>(dst, S.pf(slot), G, tl, S.tid);
+      else pf_read<DT_BF16>(dst, S.pf(slot), G, tl, S.tid);
+    } else {
+      load_any(dst, a, G, tl, L);
+    }
+    if ((fl & FL_ISSUE) && S.tile + 1 < S.t_end) {
+      const Tile nt = make_tile(G, S.tile + 1);
+      if (tile_full(nt)) pf_issue(S.pf(slot), a, G, nt, S.tid);
+    }
+    return;
+  }
+  load_any(dst, a, G, tl, L);
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------------------
@@ -492,6 +662,7 @@ extern "C" __global__ void __launch_bounds__(T_LANES) __attribute__((amdgpu_wave
 dvm_vm_vector(const Program prog) {
   __shared__ float s_red[N_LDSBUF][T_LANES / 64];
   __shared__ int s_last;
+  extern __shared__ __attribute__((aligned(16))) char dlds[];
 
   const uint32_t* W = prog.w;
   const uint32_t block_dim = W[H_BLOCK_DIM];
@@ -517,7 +688,7 @@ dvm_vm_vector(const Program prog) {
   TReg t;
 #pragma unroll
   for (int k = 0; k < N_TREG; ++k) fill_c(t[k], 0.f);
-  float rw[N_RREG] = {0.f, 0.f, 0.f, 0.f};
+  RowRegs rw = {0.f, 0.f, 0.f, 0.f};
 
   Tile tl;
   auto set_tile = [&](uint32_t id) {
@@ -531,6 +702,12 @@ dvm_vm_vector(const Program prog) {
     const int64_t remr = G.R - tl.r0;
     tl.tre = remr < G.tr ? (int)remr : G.tr;
   };
+
+  Stage S;
+  S.W = W;
+  S.lds = dlds;
+  S.t_end = t_end;
+  S.tid = tid;
 
   uint32_t tile = t_begin;
   uint32_t pc = W[H_PRO_BEGIN], pc_end = W[H_PRO_END];
@@ -564,15 +741,30 @@ dvm_vm_vector(const Program prog) {
     L.row = tidv >> G.lg;
     L.lane = tidv & (G.g - 1);
     L.rok = L.row < tl.tre;
+    S.tile = tile;
+    S.tid = tidv;
 
     switch (f_op(w0)) {
       case OP_LOAD: {
-        const ArgD a = read_arg(W, w1);
+        Chunks tmp;
+        read_operand(tmp, w0, vmc_load(w0), read_arg(W, w1), G, tl, L, S);
         switch (f_dst(w0)) {
-          case 0: load_any(t[0], a, G, tl, L); break;
-          case 1: load_any(t[1], a, G, tl, L); break;
-          default: load_any(t[2], a, G, tl, L); break;
+          case 0: copy_c(t[0], tmp, NV_MAX); break;
+          case 1: copy_c(t[1], tmp, NV_MAX); break;
+          default: copy_c(t[2], tmp, NV_MAX); break;
         }
+        break;
+      }
+      case OP_PF: {
+        const ArgD a = read_arg(W, w1);
+        if (tile_full(tl)) pf_issue(S.pf(f_b(w0) & 1u), a, G, tl, tidv);
+        break;
+      }
+      case OP_LDS_INV: {
+        const ArgD a = read_arg(W, w1);
+        Chunks tmp;
+        load_any(tmp, a, G, tl, L);
+        inv_write(tmp, S.inv(f_dst(w0) & 1u), G, tidv);
         break;
       }
       case OP_STORE: {
@@ -621,16 +813,16 @@ dvm_vm_vector(const Program prog) {
       }
       case OP_BIN: {
         const float rowv = f_bk(w0) == BK_RREG ? rget(rw, f_b(w0)) : 0.f;
-        ArgD ma;
-        if (f_bk(w0) == BK_MEM) ma = read_arg(W, w1);
+        Chunks tmp;
+        if (f_bk(w0) == BK_MEM) read_operand(tmp, w0, vmc_bin(w0), read_arg(W, w1), G, tl, L, S);
         switch (f_sub(w0)) {
-          case ALU_ADD: bin_op<ALU_ADD>(t, w0, w1, rowv, &ma, G, tl, L); break;
-          case ALU_SUB: bin_op<ALU_SUB>(t, w0, w1, rowv, &ma, G, tl, L); break;
-          case ALU_MUL: bin_op<ALU_MUL>(t, w0, w1, rowv, &ma, G, tl, L); break;
-          case ALU_DIV: bin_op<ALU_DIV>(t, w0, w1, rowv, &ma, G, tl, L); break;
-          case ALU_MAX: bin_op<ALU_MAX>(t, w0, w1, rowv, &ma, G, tl, L); break;
-          case ALU_MIN: bin_op<ALU_MIN>(t, w0, w1, rowv, &ma, G, tl, L); break;
-          default: bin_op<ALU_POW>(t, w0, w1, rowv, &ma, G, tl, L); break;
+          case ALU_ADD: bin_op<ALU_ADD>(t, w0, w1, rowv, tmp, G); break;
+          case ALU_SUB: bin_op<ALU_SUB>(t, w0, w1, rowv, tmp, G); break;
+          case ALU_MUL: bin_op<ALU_MUL>(t, w0, w1, rowv, tmp, G); break;
+          case ALU_DIV: bin_op<ALU_DIV>(t, w0, w1, rowv, tmp, G); break;
+          case ALU_MAX: bin_op<ALU_MAX>(t, w0, w1, rowv, tmp, G); break;
+          case ALU_MIN: bin_op<ALU_MIN>(t, w0, w1, rowv, tmp, G); break;
+          default: bin_op<ALU_POW>(t, w0, w1, rowv, tmp, G); break;
         }
         break;
       }
@@ -761,6 +953,13 @@ dvm_vm_vector(const Program prog) {
 
 // Host-side launch of the VECTOR VM kernel with one program as its argument.
 extern "C" hipError_t dvm_launch_vector_kernel(const Program* p, unsigned grid, hipStream_t s) {
-  hipLaunchKernelGGL(dvm_vm_vector, dim3(grid), dim3(T_LANES), 0, s, *p);
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute((const void*)dvm_vm_vector, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       (int)LDS_BUDGET);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  hipLaunchKernelGGL(dvm_vm_vector, dim3(grid), dim3(T_LANES), p->w[H_LDS_BYTES], s, *p);
   return hipGetLastError();
 }
