@@ -18,6 +18,13 @@ if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() "
                       "(or python device_bytecode_vm_amd/build.py)")
 
+# libdvm.so shares streams and device allocations with PyTorch, so it must
+# bind to the HIP runtime PyTorch loads.  torch's libamdhip64 carries the same
+# soname (libamdhip64.so.7) as the system one libdvm.so names, so loading torch
+# first makes the dynamic linker reuse it; loading libdvm.so first would bring
+# in a second, separate runtime.
+import torch  # noqa: E402,F401  (load order only)
+
 lib = C.CDLL(LIB_PATH)
 
 # dvm_status

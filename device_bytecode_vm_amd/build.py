@@ -13,6 +13,11 @@ FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
          # no packed-fp32 VALU forms in device code
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-Wno-unused-command-line-argument"]
+# Device sources: the interpreter loop branches only on wave-uniform values
+# (opcode, operand kinds, tile geometry), so its regions need no conversion
+# to exec-masked form; skipping that keeps the tile registers in place across
+# the opcode dispatch instead of copying them at every join.
+DEVICE_FLAGS = ["-mllvm", "-structurizecfg-skip-uniform-regions=true"]
 
 
 def build(verbose=False):
@@ -20,7 +25,8 @@ def build(verbose=False):
     objs = []
     for src in SOURCES:
         obj = os.path.join(CSRC, os.path.splitext(src)[0] + ".o")
-        cmd = [hipcc] + [f for f in FLAGS if f != "-shared"] + ["-c", os.path.join(CSRC, src),
+        extra = DEVICE_FLAGS if src.endswith(".hip") else []
+        cmd = [hipcc] + [f for f in FLAGS if f != "-shared"] + extra + ["-c", os.path.join(CSRC, src),
                                                                   "-I", os.path.join(ROOT, "include"),
                                                                   "-I", CSRC, "-o", obj]
         if verbose:

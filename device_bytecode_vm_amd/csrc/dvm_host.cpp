@@ -1503,19 +1503,23 @@ dvm_status dvm_context_create(int device, dvm_context** out) {
   if (!c) return fail(DVM_ERR_INTERNAL, "out of host memory");
   c->device = device;
   if (device >= 0) {
-    if (hipSetDevice(device) != hipSuccess) {
+    hipError_t e = hipSetDevice(device);
+    if (e != hipSuccess) {
       delete c;
-      return fail(DVM_ERR_DEVICE, "hipSetDevice(%d) failed", device);
+      return fail(DVM_ERR_DEVICE, "hipSetDevice(%d) failed: %s", device, hipGetErrorString(e));
     }
     c->scratch_bytes = 4u << 20;
-    if (hipMalloc(&c->scratch, c->scratch_bytes) != hipSuccess) {
+    e = hipMalloc(&c->scratch, c->scratch_bytes);
+    if (e != hipSuccess) {
       delete c;
-      return fail(DVM_ERR_DEVICE, "scratch allocation failed");
+      return fail(DVM_ERR_DEVICE, "scratch allocation failed: %s", hipGetErrorString(e));
     }
-    if (hipMemset(c->scratch, 0, c->scratch_bytes) != hipSuccess || hipDeviceSynchronize() != hipSuccess) {
+    e = hipMemset(c->scratch, 0, c->scratch_bytes);
+    if (e == hipSuccess) e = hipDeviceSynchronize();
+    if (e != hipSuccess) {
       (void)hipFree(c->scratch);
       delete c;
-      return fail(DVM_ERR_DEVICE, "scratch init failed");
+      return fail(DVM_ERR_DEVICE, "scratch init failed: %s", hipGetErrorString(e));
     }
   }
   *out = c;

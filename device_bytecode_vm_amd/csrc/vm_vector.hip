@@ -192,6 +192,12 @@ struct Lane {
   bool rok;  // row exists
 };
 
+// Lane masks are applied with selects over values computed on every lane:
+// the arguments are evaluated before the call, so no lane-dependent branch
+// (and no divergent join inside the interpreter loop) is formed.
+__device__ __forceinline__ int lane_off(bool ok, int off) { return ok ? off : OOB; }
+__device__ __forceinline__ float lane_sel(bool ok, float v, float other) { return ok ? v : other; }
+
 // ---------------------------------------------------------------------------
 // Load / Store (Table 1: Load/ViewLoad/Store/ViewStore)
 // ---------------------------------------------------------------------------
@@ -204,7 +210,7 @@ __device__ __forceinline__ void load_chunks(Chunks& dst, const ArgD& a, const Ge
   const int roff = L.row * (int)a.sr;  // tile spans < 2^31 bytes (host checked)
   if (a.sc == 0) {
     // broadcast along the row: one element per row
-    const int off = L.rok ? roff * ES : OOB;
+    const int off = lane_off(L.rok, roff * ES);
     float v;
     if constexpr (DT == DT_F32) v = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, 0));
     else if constexpr (DT == DT_BF16) v = bf2f(__builtin_amdgcn_raw_buffer_load_b16(rs, off, 0, 0));
@@ -217,7 +223,7 @@ __device__ __forceinline__ void load_chunks(Chunks& dst, const ArgD& a, const Ge
     for (int j = 0; j < NV_MAX; ++j) {
       {  // chunks past the row's last one fall out of range and are masked
         const int ct = (j * G.g + L.lane) * VEC;
-        const int off = (L.rok && ct < tl.tce) ? (roff + ct) * ES : OOB;
+        const int off = lane_off(L.rok & (ct < tl.tce), (roff + ct) * ES);
         if constexpr (DT == DT_F32) {
           const u4 v0 = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
           const u4 v1 = __builtin_amdgcn_raw_buffer_load_b128(rs, off == OOB ? OOB : off + 16, 0, 0);
@@ -250,7 +256,7 @@ __device__ __forceinline__ void load_chunks(Chunks& dst, const ArgD& a, const Ge
 #pragma unroll
         for (int i = 0; i < VEC; ++i) {
           const int c = ct + i;
-          const int off = (L.rok && c < tl.tce) ? (roff + c * a.sc) * ES : OOB;
+          const int off = lane_off(L.rok & (c < tl.tce), (roff + c * a.sc) * ES);
           float v;
           if constexpr (DT == DT_F32) v = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, 0));
           else if constexpr (DT == DT_BF16) v = bf2f(__builtin_amdgcn_raw_buffer_load_b16(rs, off, 0, 0));
@@ -273,7 +279,7 @@ __device__ __forceinline__ void store_chunks(const Chunks& src, const ArgD& a, c
     for (int j = 0; j < NV_MAX; ++j) {
       {  // chunks past the row's last one fall out of range and are masked
         const int ct = (j * G.g + L.lane) * VEC;
-        const int off = (L.rok && ct < tl.tce) ? (roff + ct) * ES : OOB;
+        const int off = lane_off(L.rok & (ct < tl.tce), (roff + ct) * ES);
         if constexpr (DT == DT_F32) {
           u4 v0, v1;
           v0.x = __float_as_uint(src[j * VEC + 0]); v0.y = __float_as_uint(src[j * VEC + 1]);
@@ -308,7 +314,7 @@ __device__ __forceinline__ void store_chunks(const Chunks& src, const ArgD& a, c
 #pragma unroll
         for (int i = 0; i < VEC; ++i) {
           const int c = ct + i;
-          const int off = (L.rok && c < tl.tce) ? (roff + c * a.sc) * ES : OOB;
+          const int off = lane_off(L.rok & (c < tl.tce), (roff + c * a.sc) * ES);
           const float v = src[j * VEC + i];
           if constexpr (DT == DT_F32) __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), rs, off, 0, 0);
           else if constexpr (DT == DT_BF16)
@@ -448,14 +454,14 @@ __device__ __forceinline__ float lane_partial(const Chunks& c, const Geo& G, con
 #pragma unroll
         for (int i = 1; i < VEC; ++i) s = comb<KIND>(s, c[j * VEC + i]);
         const int ct = (j * G.g + L.lane) * VEC;
-        acc = comb<KIND>(acc, (L.rok && ct < tl.tce) ? s : id);
+        acc = comb<KIND>(acc, lane_sel(L.rok & (ct < tl.tce), s, id));
       }
   } else {
 #pragma unroll
     for (int j = 0; j < NV_MAX; ++j) {
         const int ct = (j * G.g + L.lane) * VEC;
 #pragma unroll
-        for (int i = 0; i < VEC; ++i) acc = comb<KIND>(acc, (L.rok && ct + i < tl.tce) ? c[j * VEC + i] : id);
+        for (int i = 0; i < VEC; ++i) acc = comb<KIND>(acc, lane_sel(L.rok & (ct + i < tl.tce), c[j * VEC + i], id));
       }
   }
   return acc;
@@ -530,7 +536,7 @@ __device__ __forceinline__ void pf_issue(char* slot, const ArgD& a, const Geo& G
   for (int j = 0; j < NV_MAX; ++j) {
     if (j < G.nv) {
       const int ct = (j * G.g + lane) * VEC;
-      const int off = (rok && ct < tl.tce) ? (roff + ct) * es : OOB;
+      const int off = lane_off(rok & (ct < tl.tce), (roff + ct) * es);
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         if (h < halves) {
@@ -780,7 +786,7 @@ dvm_vm_vector(const Program prog) {
         const ArgD a = read_arg(W, w1);
         const Rsrc rs = tile_rsrc(a, tl);
         const int es = esize(a.dt);
-        const int off = L.rok ? L.row * (int)a.sr * es : OOB;
+        const int off = lane_off(L.rok, L.row * (int)a.sr * es);
         float v;
         if (a.dt == DT_BF16) v = bf2f(__builtin_amdgcn_raw_buffer_load_b16(rs, off, 0, 0));
         else if (a.dt == DT_F32) v = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, 0));
@@ -792,7 +798,7 @@ dvm_vm_vector(const Program prog) {
         const ArgD a = read_arg(W, w1);
         const Rsrc rs = tile_rsrc(a, tl);
         const int es = esize(a.dt);
-        const int off = (L.rok && L.lane == 0) ? L.row * (int)a.sr * es : OOB;
+        const int off = lane_off(L.rok & (L.lane == 0), L.row * (int)a.sr * es);
         const float v = rget(rw, f_a(w0));
         if (a.dt == DT_BF16) __builtin_amdgcn_raw_buffer_store_b16((uint16_t)(f2bf_pack(v, 0.f) & 0xffffu), rs, off, 0, 0);
         else if (a.dt == DT_F32) __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), rs, off, 0, 0);
@@ -865,8 +871,10 @@ dvm_vm_vector(const Program prog) {
         const uint32_t kind = f_sub(w0);
         float acc = lane_partial_any(t, f_a(w0), G, tl, L, kind);
         acc = group_reduce_k(acc, gs, kind);
+        // after the 64-lane all-reduce every lane of a wave holds the same
+        // value, so every lane stores it (no lane-dependent branch in the loop)
         if (G.g <= 64) rset(rw, f_dst(w0), acc);
-        else if ((tid & 63) == 0) s_red[f_b(w0)][wave] = acc;
+        else s_red[f_b(w0)][wave] = acc;
         break;
       }
       case OP_RED_FIN: {
@@ -886,19 +894,22 @@ dvm_vm_vector(const Program prog) {
         const uint32_t kind = f_sub(w0);
         float acc = lane_partial_any(t, f_a(w0), G, tl, L, kind);
         acc = group_reduce_k(acc, 64, kind);
-        if ((tid & 63) == 0) s_red[f_b(w0)][wave] = acc;
+        s_red[f_b(w0)][wave] = acc;
         break;
       }
       case OP_ALL_FIN: {
-        if (tid == 0) {
-          const uint32_t kind = f_sub(w0);
-          const float* buf = s_red[f_b(w0)];
-          float acc = buf[0];
-          for (int k = 1; k < T_LANES / 64; ++k) acc = comb_k(acc, buf[k], kind);
-          const ArgD a = read_arg(W, W[H_ALL_SCRATCH]);
-          float* part = reinterpret_cast<float*>(const_cast<char*>(a.p) + 256);
-          __hip_atomic_store(part + tl.id, acc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
+        // every lane combines the per-wave partials (LDS broadcast reads);
+        // lane 0 alone stores the tile's partial, the others are masked by
+        // an out-of-range offset
+        const uint32_t kind = f_sub(w0);
+        const float* buf = s_red[f_b(w0)];
+        float acc = buf[0];
+        for (int k = 1; k < T_LANES / 64; ++k) acc = comb_k(acc, buf[k], kind);
+        const ArgD a = read_arg(W, W[H_ALL_SCRATCH]);
+        const Rsrc rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(a.p) + 256, 0, (int)(block_dim * 4u),
+                                                          RSRC_W3);
+        const int off = tidv == 0 ? (int)(tl.id * 4u) : OOB;
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc), rs, off, 0, 0);
         break;
       }
       case OP_DBG: {

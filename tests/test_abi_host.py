@@ -307,3 +307,18 @@ def test_fuser_resource_split_matches_oracle(ectx):
     sim = Stream()
     sim.run(tw.events)
     assert tw.g.flush_log() == [(len(o), w) for o, w, _ in sim.graphs] == [(64, "resource"), (6, "explicit")]
+
+
+def test_single_hip_runtime_in_process():
+    """Importing the binding before torch must still leave one HIP runtime
+    mapped in the process (libdvm.so binds to the one torch loads)."""
+    import subprocess
+    import sys
+    code = ("import device_bytecode_vm_amd, torch\n"
+            "maps = open('/proc/self/maps').read().split('\\n')\n"
+            "paths = sorted({l.split()[-1] for l in maps if 'libamdhip64' in l})\n"
+            "print(len(paths)); print(paths)\n")
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=300,
+                       cwd=os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+    assert r.returncode == 0, r.stderr
+    assert r.stdout.split("\n")[0] == "1", r.stdout
