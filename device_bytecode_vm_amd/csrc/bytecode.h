@@ -21,19 +21,23 @@
 namespace dvmbc {
 
 constexpr uint32_t MAGIC = 0x314d5644u;  // "DVM1"
-constexpr uint32_t VERSION = 1;
+constexpr uint32_t VERSION = 2;
 
 // Device geometry constants: one workgroup of T lanes runs a tile; a tile row
-// is spread over g lanes, each holding up to NV_MAX chunks of V elements.
-constexpr int T_LANES = 512;
+// is spread over g lanes, each holding up to NV_MAX chunks of V elements.  Two
+// workgroups are resident per compute unit (their waves share each SIMD and
+// run different tiles, so one wave's scalar decode overlaps the other's
+// vector work).
+constexpr int T_LANES = 256;
 constexpr int VEC = 8;
-constexpr int NV_MAX = 2;
+constexpr int NV_MAX = 5;
 constexpr int E_MAX = VEC * NV_MAX;   // elements per lane per tile register
 constexpr int N_TREG = 3;             // tile registers: 0 = ACC, 1..2 slots
 constexpr int N_RREG = 4;             // row registers
 constexpr int N_LDSBUF = 8;           // cross-wave reduction buffers
 constexpr int MAX_WORDS = 1000;       // whole program, <= 4000 bytes of kernarg
-constexpr int HDR_WORDS = 32;
+constexpr int PAD_WORDS = 2;          // unused words after the body (the VM reads one instruction ahead)
+constexpr int HDR_WORDS = 40;
 constexpr int ARG_BASE = HDR_WORDS;
 constexpr int ARG_WORDS = 8;
 constexpr int MAX_ARGS = 32;
@@ -71,20 +75,27 @@ enum Hdr : int {
   H_N_INSTR = 25,
   H_FLAGS = 26,
   H_LDS_BYTES = 27,  // dynamic LDS of the launch (staging areas below)
-  H_PF_OFF0 = 28,    // byte offset of prefetch slot 0 / 1 (double-buffered next-tile loads)
+  H_PF_OFF0 = 28,    // byte offset of prefetch slot 0 / 1 (next-tile loads)
   H_PF_OFF1 = 29,
   H_INV_OFF0 = 30,   // byte offset of LDS-resident invariant operand 0 / 1
   H_INV_OFF1 = 31,
+  H_INV_SHARED0 = 32,// 1: invariant slot 0 / 1 is one row shared by all row groups
+  H_INV_SHARED1 = 33,
 };
 
 // LDS staging (per workgroup, dynamic):
-//  * prefetch slot: two buffers (tile parity) of NV chunks x T lanes x 16 bytes
-//    x (element size / 2) halves; lane t's data for chunk j, half h sits at
-//    ((j * halves + h) * T + t) * 16, written by a direct-to-LDS buffer load of
-//    that lane and read back by the same lane;
+//  * prefetch slot: NV chunks x T lanes x 16 bytes x (element size / 2)
+//    halves; lane t's data for chunk j, half h sits at ((j * halves + h) * T +
+//    t) * 16, written by a direct-to-LDS buffer load of that lane and read back
+//    by the same lane, which then issues the next tile's load into the same
+//    bytes (one buffer: the read completes before the refill is issued);
 //  * invariant slot: an operand that is the same for every tile, held as fp32,
-//    NV chunks x T lanes x 32 bytes, lane-private.
-constexpr uint32_t LDS_BUDGET = 150u * 1024u;  // one workgroup per CU
+//    8 elements (32 bytes) per lane and chunk.  A slot shared by the row groups
+//    (the operand does not vary along rows) holds one row: NV x g x 32 bytes,
+//    indexed by the lane's position in its row; otherwise NV x T x 32 bytes,
+//    indexed by the lane.
+// The budget keeps two workgroups resident per compute unit (160 KB of LDS).
+constexpr uint32_t LDS_BUDGET = 76u * 1024u;
 
 // Argument table entry (8 words): pointer, dtype, flags, column stride, row
 // stride (elements, in the collapsed [R, C] iteration space) and the byte
@@ -124,6 +135,45 @@ enum Op : uint32_t {
   OP_COUNT
 };
 
+// Handler ids.  The encoder emits the generic opcodes above and, as its last
+// step, rewrites bits [7:0] of every word 0 into the id of the specialised VM
+// routine that runs it: register numbers, ALU op, operand form and dtype are
+// folded into the id, so the VM decodes one byte with one switch and the
+// routine itself has no further branches on them.  The other fields keep their
+// meaning (staging slot, wait count, row register, scalar / argument word).
+enum Handler : uint32_t {
+  HD_END = 0,
+  HD_LD_F32 = 1,     // + d: treg[d] <- arg[w1] tile, f32, straight from memory
+  HD_LD_BF16 = 4,    // + d
+  HD_LD_U8 = 7,      // + d
+  HD_LD_PF16 = 10,   // + d: bf16 from prefetch slot b (then refill it, if FL_ISSUE)
+  HD_LD_PF32 = 13,   // + d: f32 from prefetch slot b
+  HD_LD_INV = 16,    // + d: from invariant slot b
+  HD_ST_F32 = 19,    // + a: arg[w1] <- treg[a]
+  HD_ST_BF16 = 22,   // + a
+  HD_ST_U8 = 25,     // + a
+  HD_COPY = 28,      // + 3 d + a: treg[d] <- treg[a]
+  HD_UN = 37,        // + f (Una): ACC <- f(ACC)
+  HD_BIN = 48,       // + 10 alu + form: ACC <- ACC (op) B; forms 0..2: B = treg[form],
+                     //   3: B = row register b or the immediate w1, 4: B = memory
+                     //   operand arg[w1]; + 5: reversed, B (op) ACC
+  HD_RED = 118,      // + 3 kind + a: row reduce of treg[a] into rreg[dst] / LDS buffer b
+  HD_RED_FIN = 124,  // + kind
+  HD_ALL = 126,      // + 3 kind + a
+  HD_ALL_FIN = 132,  // + kind
+  HD_BCAST = 134,    // + d
+  HD_RBIN = 137,
+  HD_RUN = 138,
+  HD_SYNC = 139,
+  HD_LD_ROW = 140,
+  HD_ST_ROW = 141,
+  HD_DBG = 142,
+  HD_LDS_INV = 143,
+  HD_PF = 144,
+  HD_COUNT = 145
+};
+enum BinForm : uint32_t { BF_T0 = 0, BF_T1 = 1, BF_T2 = 2, BF_SCALAR = 3, BF_MEM = 4, BF_REV = 5 };
+
 // ALU sub-ops (bits [23:20]).
 enum Alu : uint32_t {
   ALU_ADD = 0, ALU_SUB = 1, ALU_MUL = 2, ALU_DIV = 3, ALU_MAX = 4, ALU_MIN = 5, ALU_POW = 6,
@@ -150,7 +200,7 @@ __host__ __device__ constexpr uint32_t f_bk(uint32_t w) { return (w >> 24) & 0xf
 __host__ __device__ constexpr uint32_t f_flags(uint32_t w) { return (w >> 28) & 0xfu; }
 constexpr uint32_t FL_REV = 1u;    // BIN: B (op) ACC instead of ACC (op) B
 constexpr uint32_t FL_PF = 2u;     // LOAD / BIN BK_MEM: read the operand from prefetch slot b
-constexpr uint32_t FL_ISSUE = 4u;  // ... then prefetch the workgroup's next tile into the other buffer
+constexpr uint32_t FL_ISSUE = 4u;  // ... then prefetch the workgroup's next tile into the same slot
 constexpr uint32_t FL_INV = 8u;    // LOAD / BIN BK_MEM: read the operand from invariant slot b
 
 // Prefetch reads wait with vmcnt(n), n = a lower bound (computed by the

@@ -123,13 +123,14 @@ int64_t extent_bytes(const dvm_tensor& t) {
 //    width one wave moves with 16-byte accesses of the narrowest type;
 //  * the shrink path goes outer -> inner (rows first, then columns) by
 //    doubling the split count k;
-//  * cost in integer ticks (1/31250 us): G = 256 resident workgroups (one
-//    per CU), A = 15625 ticks per tile, 1 tick per byte per workgroup;
+//  * cost in integer ticks (1/15625 us): G = 512 resident workgroups (two
+//    per CU), A = 7812 ticks (about 0.5 us) per tile, 1 tick per byte per
+//    workgroup (8 TB/s shared by G workgroups);
 //    cost = ceil(n_tiles / G) (A + var_bytes) + inv_bytes; least cost wins,
 //    earlier (larger) candidates win ties.
 // ===========================================================================
 namespace tiling {
-constexpr int64_t T = T_LANES, V = VEC, NVM = NV_MAX, W = 64 * VEC, G = 256, A = 15625, BT = 1;
+constexpr int64_t T = T_LANES, V = VEC, NVM = NV_MAX, W = 64 * VEC, G = 512, A = 7812, BT = 1;
 
 struct Operand {
   int64_t esize, sr, sc, base_mod16;
@@ -1112,21 +1113,22 @@ struct Encoder {
     note_consume(f, slot, false);
   }
 
-  // Lower bound of the vector-memory instructions one wave issues for an
-  // instruction in a full tile (the VM's 128-bit paths; ragged tiles take the
-  // element paths and issue more).
+  // Vector-memory instructions one wave issues for an instruction in a full
+  // tile (a lower bound: ragged tiles take the element paths and issue
+  // more).  Direct loads and stores run all NV_MAX chunks (out-of-range ones
+  // masked); prefetch refills issue the tile's nv chunks.
   uint32_t halves(uint32_t arg) const { return W[ARG_BASE + arg * ARG_WORDS + A_DTYPE] == DT_F32 ? 2u : 1u; }
   uint32_t load_ops(uint32_t arg) const {
     const uint32_t* a = W + ARG_BASE + arg * ARG_WORDS;
     const int32_t sc = (int32_t)a[A_SC];
-    if ((a[A_FLAGS] & AF_VEC) && sc == 1) return (uint32_t)plan.nv * halves(arg);
     if (sc == 0) return 1u;
-    return 8u * (uint32_t)plan.nv;
+    if ((a[A_FLAGS] & AF_VEC) && sc == 1) return (uint32_t)NV_MAX * halves(arg);
+    return 8u * (uint32_t)NV_MAX;
   }
   uint32_t store_ops(uint32_t arg) const {
     const uint32_t* a = W + ARG_BASE + arg * ARG_WORDS;
-    if ((a[A_FLAGS] & AF_VEC) && (int32_t)a[A_SC] == 1) return (uint32_t)plan.nv * halves(arg);
-    return 8u * (uint32_t)plan.nv;
+    if ((a[A_FLAGS] & AF_VEC) && (int32_t)a[A_SC] == 1) return (uint32_t)NV_MAX * halves(arg);
+    return 8u * (uint32_t)NV_MAX;
   }
   uint32_t src_ops(uint32_t w0, uint32_t w1) const {
     const uint32_t f = f_flags(w0);
@@ -1186,16 +1188,20 @@ struct Encoder {
         const bool invariant = (sr == 0 || plan.n_r == 1) && (sc == 0 || plan.n_c == 1);
         const uint32_t* a = W + ARG_BASE + arg_of[s] * ARG_WORDS;
         if (invariant && n_inv < 2) {
-          const uint32_t sz = (uint32_t)plan.nv * T_LANES * 32u;
+          // an operand that does not vary along rows is held once (one row),
+          // shared by the lane groups of all rows
+          const bool shared = sr == 0;
+          const uint32_t sz = (uint32_t)plan.nv * (uint32_t)(shared ? plan.g : T_LANES) * 32u;
           if (off + sz > LDS_BUDGET) continue;
           inv_slot[s] = n_inv;
           W[H_INV_OFF0 + n_inv] = off;
+          W[H_INV_SHARED0 + n_inv] = shared ? 1u : 0u;
           off += sz;
           pro.push_back(enc0(OP_LDS_INV, n_inv, 0, 0, 0, 0, 0));
           pro.push_back((uint32_t)arg_of[s]);
           ++n_inv;
         } else if (!invariant && n_pf < 2 && (a[A_FLAGS] & AF_VEC) && sc == 1 && (es == 2 || es == 4)) {
-          const uint32_t sz = 2u * (uint32_t)plan.nv * T_LANES * 16u * (uint32_t)(es / 2);
+          const uint32_t sz = (uint32_t)plan.nv * T_LANES * 16u * (uint32_t)(es / 2);
           if (off + sz > LDS_BUDGET) continue;
           pf_slot[s] = n_pf;
           W[H_PF_OFF0 + n_pf] = off;
@@ -1207,6 +1213,47 @@ struct Encoder {
       }
     }
     W[H_LDS_BYTES] = off;
+  }
+
+  // Handler id of one instruction (generic opcode and fields -> the VM's
+  // specialised routine).  Commutative ALU ops ignore the reversed flag.
+  uint32_t handler_of(uint32_t w0, uint32_t w1) const {
+    auto dt = [&](uint32_t arg) { return W[ARG_BASE + arg * ARG_WORDS + A_DTYPE]; };
+    const uint32_t d = f_dst(w0), a = f_a(w0), sub = f_sub(w0), fl = f_flags(w0);
+    switch (f_op(w0)) {
+      case OP_LOAD:
+        if (fl & FL_INV) return HD_LD_INV + d;
+        if (fl & FL_PF) return (dt(w1) == DT_F32 ? HD_LD_PF32 : HD_LD_PF16) + d;
+        return (dt(w1) == DT_F32 ? HD_LD_F32 : dt(w1) == DT_BF16 ? HD_LD_BF16 : HD_LD_U8) + d;
+      case OP_STORE:
+        return (dt(w1) == DT_F32 ? HD_ST_F32 : dt(w1) == DT_BF16 ? HD_ST_BF16 : HD_ST_U8) + a;
+      case OP_COPY: return HD_COPY + 3 * d + a;
+      case OP_UN: return HD_UN + sub;
+      case OP_BIN: {
+        const uint32_t bk = f_bk(w0);
+        const uint32_t form = bk == BK_TREG ? f_b(w0) : bk == BK_MEM ? (uint32_t)BF_MEM : (uint32_t)BF_SCALAR;
+        const bool comm = sub == ALU_ADD || sub == ALU_MUL || sub == ALU_MAX || sub == ALU_MIN;
+        const bool rev = !comm && (fl & FL_REV);
+        return HD_BIN + 10 * sub + form + (rev ? (uint32_t)BF_REV : 0u);
+      }
+      case OP_RED: return HD_RED + 3 * sub + a;
+      case OP_RED_FIN: return HD_RED_FIN + sub;
+      case OP_ALL: return HD_ALL + 3 * sub + a;
+      case OP_ALL_FIN: return HD_ALL_FIN + sub;
+      case OP_BCAST: return HD_BCAST + d;
+      case OP_RBIN: return HD_RBIN;
+      case OP_RUN: return HD_RUN;
+      case OP_SYNC: return HD_SYNC;
+      case OP_LOAD_ROW: return HD_LD_ROW;
+      case OP_STORE_ROW: return HD_ST_ROW;
+      case OP_DBG: return HD_DBG;
+      case OP_LDS_INV: return HD_LDS_INV;
+      case OP_PF: return HD_PF;
+      default: return HD_END;
+    }
+  }
+  void to_handlers(std::vector<uint32_t>& v) const {
+    for (size_t q = 0; q < v.size(); q += 2) v[q] = (v[q] & ~0xffu) | handler_of(v[q], v[q + 1]);
   }
 
   dvm_status run() {
@@ -1301,7 +1348,9 @@ struct Encoder {
     // header
     const uint32_t instr_base = ARG_BASE + (uint32_t)n_args * ARG_WORDS;
     const uint32_t body_base = instr_base + (uint32_t)pro.size();
-    if (body_base + body.size() > (size_t)MAX_WORDS) return fail(DVM_ERR_RESOURCE, "program too large");
+    if (body_base + body.size() + PAD_WORDS > (size_t)MAX_WORDS) return fail(DVM_ERR_RESOURCE, "program too large");
+    to_handlers(pro);
+    to_handlers(body);
     std::copy(pro.begin(), pro.end(), W + instr_base);
     std::copy(body.begin(), body.end(), W + body_base);
     W[H_MAGIC] = MAGIC;
@@ -1740,8 +1789,8 @@ dvm_status dvm_program_debug_tilemap(const dvm_program* p, const dvm_tensor* til
     ++k;
   }
   const uint32_t base = ARG_BASE + n_args * ARG_WORDS;
-  const uint32_t code[] = {enc0(OP_DBG, 0, 0, 0, 0, 0, 0), 0, enc0(OP_STORE, 0, 0, 0, 0, 0, 0), 0,
-                           enc0(OP_DBG, 0, 0, 0, 1, 0, 0), 0, enc0(OP_STORE, 0, 0, 0, 0, 0, 0), 1};
+  const uint32_t code[] = {enc0(HD_DBG, 0, 0, 0, 0, 0, 0), 0, enc0(HD_ST_F32, 0, 0, 0, 0, 0, 0), 0,
+                           enc0(HD_DBG, 0, 0, 0, 1, 0, 0), 0, enc0(HD_ST_F32, 0, 0, 0, 0, 0, 0), 1};
   std::memcpy(W + base, code, sizeof code);
   W[H_PRO_BEGIN] = W[H_PRO_END] = W[H_BODY_BEGIN] = base;
   W[H_BODY_END] = base + 8;

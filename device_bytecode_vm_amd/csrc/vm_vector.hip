@@ -4,21 +4,24 @@
 // It follows the VM algorithm of the DVM paper review page (section 4.4):
 // each workgroup computes its tile count and its tile range from the code
 // header, and for every tile decodes the body instruction by instruction and
-// calls the matching virtual-instruction function.  Decoding is wave-uniform:
+// runs the matching virtual-instruction routine.  Decoding is wave-uniform:
 // the program sits in the kernarg segment and every word is read with a scalar
-// load, so the opcode switch is a chain of scalar compares and branches (the
-// counterpart of the page's decode on the Scalar unit), and the instruction
-// bodies run on the vector ALUs, the LDS and the vector memory pipeline.
+// load (the next instruction's words are fetched while the current one runs),
+// so the dispatch is a tree of scalar compares on one pre-decoded handler byte
+// (the counterpart of the page's decode on the Scalar unit), and the routines
+// run on the vector ALUs, the LDS and the vector memory pipeline.
 //
-// Tiles are staged in registers, not in LDS: each lane owns up to NV_MAX
-// chunks of VEC consecutive columns of its row, so elementwise chains never
-// leave the VGPR file (the page's "intermediate results stay in local memory"
-// of section 5.1, with the CU's register file as that local memory).  LDS
-// carries only what crosses lanes: the per-wave partials of a reduction whose
-// row spans several waves, and the reduce-all partials.  Every register index
-// is a compile-time constant: compute instructions have the two-address form
-// treg[0] <- treg[0] (op) B, and each instruction body is instantiated for
-// every register it can name.
+// Tiles are staged in registers: each lane owns up to NV_MAX chunks of VEC
+// consecutive columns of its row, so elementwise chains never leave the VGPR
+// file (the page's "intermediate results stay in local memory" of section
+// 5.1, with the register file as that local memory).  Every register number
+// is folded into the handler id, so each routine names its registers
+// statically; compute has the two-address form ACC <- ACC (op) B.
+//
+// The interpreter loop branches only on wave-uniform values.  Lane masks are
+// selects over values every lane computes (out-of-range buffer offsets for
+// memory), so the compiler keeps the tile registers in place across the
+// dispatch instead of merging copies of them at divergent joins.
 //
 // Global memory is reached through buffer resources: one scalar descriptor
 // per operand and tile (base = the tile's first element, size = the bytes left
@@ -35,12 +38,24 @@ using namespace dvmbc;
 namespace {
 
 typedef float f4 __attribute__((ext_vector_type(4)));
+typedef float V8 __attribute__((ext_vector_type(8)));
 typedef uint32_t u4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u2 __attribute__((ext_vector_type(2)));
+typedef float f2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
 typedef __amdgpu_buffer_rsrc_t Rsrc;
+typedef __attribute__((address_space(3))) void lds_void;
+// Program words are read in place in the kernarg segment (constant address
+// space, scalar loads); the kernel never takes a copy of its argument.
+typedef const __attribute__((address_space(4))) uint32_t KW;
 
 constexpr int OOB = 0x7fffffff;                 // lane offset beyond any descriptor size
 constexpr int RSRC_W3 = 0x00020000;             // raw buffer, 32-bit data format
+
+// One tile register: NV_MAX chunks of VEC fp32 values per lane.
+struct Ch {
+  V8 c[NV_MAX];
+};
 
 struct ArgD {
   const char* p;
@@ -63,12 +78,20 @@ struct Tile {
   uint32_t id;
 };
 
-__device__ __forceinline__ uint64_t w64(const uint32_t* w, int lo) {
+// Lane coordinates inside the tile.
+struct Lane {
+  int tid;
+  int row;   // row group of the lane (row inside the tile)
+  int lane;  // position inside the row group
+  bool rok;  // the row exists
+};
+
+__device__ __forceinline__ uint64_t w64(KW* w, int lo) {
   return ((uint64_t)w[lo + 1] << 32) | (uint64_t)w[lo];
 }
 
-__device__ __forceinline__ ArgD read_arg(const uint32_t* W, uint32_t i) {
-  const uint32_t* a = W + ARG_BASE + i * ARG_WORDS;
+__device__ __forceinline__ ArgD read_arg(KW* W, uint32_t i) {
+  KW* a = W + ARG_BASE + i * ARG_WORDS;
   ArgD d;
   d.p = reinterpret_cast<const char*>(w64(a, A_PTR_LO));
   d.dt = a[A_DTYPE];
@@ -79,25 +102,45 @@ __device__ __forceinline__ ArgD read_arg(const uint32_t* W, uint32_t i) {
   return d;
 }
 
+template <uint32_t DT>
+constexpr int esize_c() { return DT == DT_F32 ? 4 : DT == DT_BF16 ? 2 : 1; }
 __device__ __forceinline__ int esize(uint32_t dt) { return dt == DT_F32 ? 4 : dt == DT_BF16 ? 2 : 1; }
 
 // Descriptor over the operand's part of the tile: base at the tile's first
 // element, size = bytes left in the tensor (capped).
-__device__ __forceinline__ Rsrc tile_rsrc(const ArgD& a, const Tile& tl) {
-  const int64_t es = esize(a.dt);
+__device__ __forceinline__ Rsrc tile_rsrc(const ArgD& a, const Tile& tl, int es) {
   const int64_t ob = (tl.r0 * a.sr + tl.c0 * (int64_t)a.sc) * es;
   const int64_t left = (int64_t)a.extent - ob;
   const int n = left <= 0 ? 0 : (left >= (int64_t)EXTENT_CAP ? (int)(EXTENT_CAP - 1) : (int)left);
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(a.p + ob), 0, n, RSRC_W3);
 }
 
+__device__ __forceinline__ Tile make_tile(const Geo& G, uint32_t id) {
+  Tile tl;
+  const uint32_t ir = id / (uint32_t)G.nc;
+  const uint32_t ic = id - ir * (uint32_t)G.nc;
+  tl.id = id;
+  tl.r0 = (int64_t)ir * G.tr;
+  tl.c0 = (int64_t)ic * G.tc;
+  const int64_t remc = G.C - tl.c0;
+  tl.tce = remc < G.tc ? (int)remc : G.tc;
+  const int64_t remr = G.R - tl.r0;
+  tl.tre = remr < G.tr ? (int)remr : G.tr;
+  return tl;
+}
+
+// a tile whose columns end on a chunk boundary moves whole chunks
+__device__ __forceinline__ bool tile_full(const Tile& tl) { return (tl.tce & (VEC - 1)) == 0; }
+
+// Lane masks: selects over values computed on every lane (the arguments are
+// evaluated before the call), so no lane-dependent branch is formed.
+__device__ __forceinline__ int lane_off(bool ok, int off) { return ok ? off : OOB; }
+__device__ __forceinline__ float lane_sel(bool ok, float v, float other) { return ok ? v : other; }
+
 // ---------------------------------------------------------------------------
 // element conversions
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ float bf2f(uint32_t h) { return __uint_as_float(h << 16); }
-
-typedef float f2 __attribute__((ext_vector_type(2)));
-typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ uint32_t f2bf_pack(float lo, float hi) {
   f2 v = {lo, hi};
@@ -106,6 +149,22 @@ __device__ __forceinline__ uint32_t f2bf_pack(float lo, float hi) {
 }
 
 __device__ __forceinline__ float round_bf16(float x) { return bf2f(f2bf_pack(x, 0.f) & 0xffffu); }
+
+__device__ __forceinline__ V8 unpack_bf16(u4 v) {
+  V8 r;
+  r[0] = bf2f(v.x & 0xffffu); r[1] = __uint_as_float(v.x & 0xffff0000u);
+  r[2] = bf2f(v.y & 0xffffu); r[3] = __uint_as_float(v.y & 0xffff0000u);
+  r[4] = bf2f(v.z & 0xffffu); r[5] = __uint_as_float(v.z & 0xffff0000u);
+  r[6] = bf2f(v.w & 0xffffu); r[7] = __uint_as_float(v.w & 0xffff0000u);
+  return r;
+}
+
+__device__ __forceinline__ V8 unpack_f32(u4 a, u4 b) {
+  V8 r;
+  r[0] = __uint_as_float(a.x); r[1] = __uint_as_float(a.y); r[2] = __uint_as_float(a.z); r[3] = __uint_as_float(a.w);
+  r[4] = __uint_as_float(b.x); r[5] = __uint_as_float(b.y); r[6] = __uint_as_float(b.z); r[7] = __uint_as_float(b.w);
+  return r;
+}
 
 // ---------------------------------------------------------------------------
 // ALU
@@ -182,68 +241,51 @@ __device__ __forceinline__ void rset(RowRegs& rw, uint32_t i, float v) {
   else rw.r3 = v;
 }
 
-typedef float Chunks __attribute__((ext_vector_type(E_MAX)));
-typedef Chunks TReg[N_TREG];
-
-// Lane coordinates inside the tile.
-struct Lane {
-  int row;   // row inside the tile
-  int lane;  // lane inside the row group
-  bool rok;  // row exists
-};
-
-// Lane masks are applied with selects over values computed on every lane:
-// the arguments are evaluated before the call, so no lane-dependent branch
-// (and no divergent join inside the interpreter loop) is formed.
-__device__ __forceinline__ int lane_off(bool ok, int off) { return ok ? off : OOB; }
-__device__ __forceinline__ float lane_sel(bool ok, float v, float other) { return ok ? v : other; }
+__device__ __forceinline__ void fill(Ch& d, float v) {
+#pragma unroll
+  for (int j = 0; j < NV_MAX; ++j) d.c[j] = (V8)v;
+}
 
 // ---------------------------------------------------------------------------
 // Load / Store (Table 1: Load/ViewLoad/Store/ViewStore)
 // ---------------------------------------------------------------------------
-// Fill dst (one tile register's worth) from operand a for this tile.
+// Fill d (one tile register) from operand a for this tile.  `any_row` loads
+// as if every row of the tile existed (for operands that do not vary along
+// rows, whose row offset is zero).
 template <uint32_t DT>
-__device__ __forceinline__ void load_chunks(Chunks& dst, const ArgD& a, const Geo& G, const Tile& tl,
-                                            const Lane& L) {
-  constexpr int ES = DT == DT_F32 ? 4 : DT == DT_BF16 ? 2 : 1;
-  const Rsrc rs = tile_rsrc(a, tl);
-  const int roff = L.row * (int)a.sr;  // tile spans < 2^31 bytes (host checked)
+__device__ __forceinline__ void load_dir(Ch& d, const ArgD& a, const Geo& G, const Tile& tl, const Lane& L,
+                                         bool any_row = false) {
+  constexpr int ES = esize_c<DT>();
+  const Rsrc rs = tile_rsrc(a, tl, ES);
+  const int roff = L.row * (int)a.sr;  // a tile spans < 2^31 bytes (host checked)
+  const bool rok = any_row | L.rok;
   if (a.sc == 0) {
     // broadcast along the row: one element per row
-    const int off = lane_off(L.rok, roff * ES);
+    const int off = lane_off(rok, roff * ES);
     float v;
     if constexpr (DT == DT_F32) v = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, 0));
     else if constexpr (DT == DT_BF16) v = bf2f(__builtin_amdgcn_raw_buffer_load_b16(rs, off, 0, 0));
     else v = (float)__builtin_amdgcn_raw_buffer_load_b8(rs, off, 0, 0);
-#pragma unroll
-    for (int e = 0; e < E_MAX; ++e) dst[e] = v;
-  } else if ((a.fl & AF_VEC) && a.sc == 1 && (tl.tce & (VEC - 1)) == 0) {
-    // full chunks, 16-byte aligned: 128-bit accesses; a chunk is wholly in or out
+    fill(d, v);
+  } else if ((a.fl & AF_VEC) && a.sc == 1 && tile_full(tl)) {
+    // full chunks, 16-byte aligned: 128-bit accesses; a chunk is wholly in or
+    // out (chunks past the row's last one fall out of range and are masked)
 #pragma unroll
     for (int j = 0; j < NV_MAX; ++j) {
-      {  // chunks past the row's last one fall out of range and are masked
-        const int ct = (j * G.g + L.lane) * VEC;
-        const int off = lane_off(L.rok & (ct < tl.tce), (roff + ct) * ES);
-        if constexpr (DT == DT_F32) {
-          const u4 v0 = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
-          const u4 v1 = __builtin_amdgcn_raw_buffer_load_b128(rs, off == OOB ? OOB : off + 16, 0, 0);
-          dst[j * VEC + 0] = __uint_as_float(v0.x); dst[j * VEC + 1] = __uint_as_float(v0.y);
-          dst[j * VEC + 2] = __uint_as_float(v0.z); dst[j * VEC + 3] = __uint_as_float(v0.w);
-          dst[j * VEC + 4] = __uint_as_float(v1.x); dst[j * VEC + 5] = __uint_as_float(v1.y);
-          dst[j * VEC + 6] = __uint_as_float(v1.z); dst[j * VEC + 7] = __uint_as_float(v1.w);
-        } else if constexpr (DT == DT_BF16) {
-          const u4 v = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
-          dst[j * VEC + 0] = bf2f(v.x & 0xffffu); dst[j * VEC + 1] = __uint_as_float(v.x & 0xffff0000u);
-          dst[j * VEC + 2] = bf2f(v.y & 0xffffu); dst[j * VEC + 3] = __uint_as_float(v.y & 0xffff0000u);
-          dst[j * VEC + 4] = bf2f(v.z & 0xffffu); dst[j * VEC + 5] = __uint_as_float(v.z & 0xffff0000u);
-          dst[j * VEC + 6] = bf2f(v.w & 0xffffu); dst[j * VEC + 7] = __uint_as_float(v.w & 0xffff0000u);
-        } else {
-          const u2 v = __builtin_amdgcn_raw_buffer_load_b64(rs, off, 0, 0);
+      const int ct = (j * G.g + L.lane) * VEC;
+      const int off = lane_off(rok & (ct < tl.tce), (roff + ct) * ES);
+      if constexpr (DT == DT_F32) {
+        const u4 v0 = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
+        const u4 v1 = __builtin_amdgcn_raw_buffer_load_b128(rs, off == OOB ? OOB : off + 16, 0, 0);
+        d.c[j] = unpack_f32(v0, v1);
+      } else if constexpr (DT == DT_BF16) {
+        d.c[j] = unpack_bf16(__builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0));
+      } else {
+        const u2 v = __builtin_amdgcn_raw_buffer_load_b64(rs, off, 0, 0);
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            dst[j * VEC + i] = (float)((v.x >> (8 * i)) & 0xffu);
-            dst[j * VEC + 4 + i] = (float)((v.y >> (8 * i)) & 0xffu);
-          }
+        for (int i = 0; i < 4; ++i) {
+          d.c[j][i] = (float)((v.x >> (8 * i)) & 0xffu);
+          d.c[j][4 + i] = (float)((v.y >> (8 * i)) & 0xffu);
         }
       }
     }
@@ -251,158 +293,269 @@ __device__ __forceinline__ void load_chunks(Chunks& dst, const ArgD& a, const Ge
     // element path: ragged tiles, unaligned or strided operands
 #pragma unroll
     for (int j = 0; j < NV_MAX; ++j) {
-      {
-        const int ct = (j * G.g + L.lane) * VEC;
+      const int ct = (j * G.g + L.lane) * VEC;
 #pragma unroll
-        for (int i = 0; i < VEC; ++i) {
-          const int c = ct + i;
-          const int off = lane_off(L.rok & (c < tl.tce), (roff + c * a.sc) * ES);
-          float v;
-          if constexpr (DT == DT_F32) v = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, 0));
-          else if constexpr (DT == DT_BF16) v = bf2f(__builtin_amdgcn_raw_buffer_load_b16(rs, off, 0, 0));
-          else v = (float)__builtin_amdgcn_raw_buffer_load_b8(rs, off, 0, 0);
-          dst[j * VEC + i] = v;
+      for (int i = 0; i < VEC; ++i) {
+        const int c = ct + i;
+        const int off = lane_off(rok & (c < tl.tce), (roff + c * a.sc) * ES);
+        float v;
+        if constexpr (DT == DT_F32) v = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, 0));
+        else if constexpr (DT == DT_BF16) v = bf2f(__builtin_amdgcn_raw_buffer_load_b16(rs, off, 0, 0));
+        else v = (float)__builtin_amdgcn_raw_buffer_load_b8(rs, off, 0, 0);
+        d.c[j][i] = v;
+      }
+    }
+  }
+}
+
+__device__ __forceinline__ void load_any(Ch& d, const ArgD& a, const Geo& G, const Tile& tl, const Lane& L,
+                                         bool any_row = false) {
+  if (a.dt == DT_BF16) load_dir<DT_BF16>(d, a, G, tl, L, any_row);
+  else if (a.dt == DT_F32) load_dir<DT_F32>(d, a, G, tl, L, any_row);
+  else load_dir<DT_U8>(d, a, G, tl, L, any_row);
+}
+
+template <uint32_t DT>
+__device__ __forceinline__ void store_dir(const Ch& s, const ArgD& a, const Geo& G, const Tile& tl, const Lane& L) {
+  constexpr int ES = esize_c<DT>();
+  const Rsrc rs = tile_rsrc(a, tl, ES);
+  const int roff = L.row * (int)a.sr;
+  if ((a.fl & AF_VEC) && a.sc == 1 && tile_full(tl)) {
+#pragma unroll
+    for (int j = 0; j < NV_MAX; ++j) {
+      const int ct = (j * G.g + L.lane) * VEC;
+      const int off = lane_off(L.rok & (ct < tl.tce), (roff + ct) * ES);
+      const V8 x = s.c[j];
+      if constexpr (DT == DT_F32) {
+        u4 v0, v1;
+        v0.x = __float_as_uint(x[0]); v0.y = __float_as_uint(x[1]); v0.z = __float_as_uint(x[2]); v0.w = __float_as_uint(x[3]);
+        v1.x = __float_as_uint(x[4]); v1.y = __float_as_uint(x[5]); v1.z = __float_as_uint(x[6]); v1.w = __float_as_uint(x[7]);
+        __builtin_amdgcn_raw_buffer_store_b128(v0, rs, off, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(v1, rs, off == OOB ? OOB : off + 16, 0, 0);
+      } else if constexpr (DT == DT_BF16) {
+        u4 v;
+        v.x = f2bf_pack(x[0], x[1]);
+        v.y = f2bf_pack(x[2], x[3]);
+        v.z = f2bf_pack(x[4], x[5]);
+        v.w = f2bf_pack(x[6], x[7]);
+        __builtin_amdgcn_raw_buffer_store_b128(v, rs, off, 0, 0);
+      } else {
+        u2 v = {0u, 0u};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          v.x |= ((uint32_t)x[i] & 0xffu) << (8 * i);
+          v.y |= ((uint32_t)x[4 + i] & 0xffu) << (8 * i);
         }
+        __builtin_amdgcn_raw_buffer_store_b64(v, rs, off, 0, 0);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < NV_MAX; ++j) {
+      const int ct = (j * G.g + L.lane) * VEC;
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) {
+        const int c = ct + i;
+        const int off = lane_off(L.rok & (c < tl.tce), (roff + c * a.sc) * ES);
+        const float v = s.c[j][i];
+        if constexpr (DT == DT_F32) __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), rs, off, 0, 0);
+        else if constexpr (DT == DT_BF16)
+          __builtin_amdgcn_raw_buffer_store_b16((uint16_t)(f2bf_pack(v, 0.f) & 0xffffu), rs, off, 0, 0);
+        else __builtin_amdgcn_raw_buffer_store_b8((uint8_t)v, rs, off, 0, 0);
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// LDS staging: next-tile prefetch (direct-to-LDS buffer loads) and
+// LDS-resident tile-invariant operands.  A lane reads back only bytes that
+// its own loads or stores put in LDS (or, for a shared invariant row, bytes
+// that every lane of its column position wrote with the same values), so no
+// barrier is needed, only waits on the lane's own outstanding operations.
+// ---------------------------------------------------------------------------
+// Issue the loads of tile nt of operand a into a prefetch slot (nv chunks).
+template <uint32_t DT>
+__device__ __forceinline__ void pf_issue(char* slot, const ArgD& a, const Geo& G, const Tile& nt, const Lane& L) {
+  constexpr int ES = esize_c<DT>();
+  constexpr int HV = DT == DT_F32 ? 2 : 1;
+  const Rsrc rs = tile_rsrc(a, nt, ES);
+  const bool rok = L.row < nt.tre;
+  const int roff = L.row * (int)a.sr;
+  const int wave = L.tid >> 6;
+#pragma unroll
+  for (int j = 0; j < NV_MAX; ++j) {
+    if (j < G.nv) {
+      const int ct = (j * G.g + L.lane) * VEC;
+      const int off = lane_off(rok & (ct < nt.tce), (roff + ct) * ES);
+#pragma unroll
+      for (int h = 0; h < HV; ++h) {
+        lds_void* dst = (lds_void*)(slot + ((j * HV + h) * T_LANES + wave * 64) * 16);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst, 16, off == OOB ? OOB : off + 16 * h, 0, 0, 0);
       }
     }
   }
 }
 
 template <uint32_t DT>
-__device__ __forceinline__ void store_chunks(const Chunks& src, const ArgD& a, const Geo& G, const Tile& tl,
-                                             const Lane& L) {
-  constexpr int ES = DT == DT_F32 ? 4 : DT == DT_BF16 ? 2 : 1;
-  const Rsrc rs = tile_rsrc(a, tl);
-  const int roff = L.row * (int)a.sr;
-  if ((a.fl & AF_VEC) && a.sc == 1 && (tl.tce & (VEC - 1)) == 0) {
+__device__ __forceinline__ void pf_read(Ch& d, const char* slot, const Geo& G, int tid) {
+  constexpr int HV = DT == DT_F32 ? 2 : 1;
 #pragma unroll
-    for (int j = 0; j < NV_MAX; ++j) {
-      {  // chunks past the row's last one fall out of range and are masked
-        const int ct = (j * G.g + L.lane) * VEC;
-        const int off = lane_off(L.rok & (ct < tl.tce), (roff + ct) * ES);
-        if constexpr (DT == DT_F32) {
-          u4 v0, v1;
-          v0.x = __float_as_uint(src[j * VEC + 0]); v0.y = __float_as_uint(src[j * VEC + 1]);
-          v0.z = __float_as_uint(src[j * VEC + 2]); v0.w = __float_as_uint(src[j * VEC + 3]);
-          v1.x = __float_as_uint(src[j * VEC + 4]); v1.y = __float_as_uint(src[j * VEC + 5]);
-          v1.z = __float_as_uint(src[j * VEC + 6]); v1.w = __float_as_uint(src[j * VEC + 7]);
-          __builtin_amdgcn_raw_buffer_store_b128(v0, rs, off, 0, 0);
-          __builtin_amdgcn_raw_buffer_store_b128(v1, rs, off == OOB ? OOB : off + 16, 0, 0);
-        } else if constexpr (DT == DT_BF16) {
-          u4 v;
-          v.x = f2bf_pack(src[j * VEC + 0], src[j * VEC + 1]);
-          v.y = f2bf_pack(src[j * VEC + 2], src[j * VEC + 3]);
-          v.z = f2bf_pack(src[j * VEC + 4], src[j * VEC + 5]);
-          v.w = f2bf_pack(src[j * VEC + 6], src[j * VEC + 7]);
-          __builtin_amdgcn_raw_buffer_store_b128(v, rs, off, 0, 0);
-        } else {
-          u2 v = {0u, 0u};
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            v.x |= ((uint32_t)src[j * VEC + i] & 0xffu) << (8 * i);
-            v.y |= ((uint32_t)src[j * VEC + 4 + i] & 0xffu) << (8 * i);
-          }
-          __builtin_amdgcn_raw_buffer_store_b64(v, rs, off, 0, 0);
-        }
-      }
-    }
-  } else {
-#pragma unroll
-    for (int j = 0; j < NV_MAX; ++j) {
-      {
-        const int ct = (j * G.g + L.lane) * VEC;
-#pragma unroll
-        for (int i = 0; i < VEC; ++i) {
-          const int c = ct + i;
-          const int off = lane_off(L.rok & (c < tl.tce), (roff + c * a.sc) * ES);
-          const float v = src[j * VEC + i];
-          if constexpr (DT == DT_F32) __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), rs, off, 0, 0);
-          else if constexpr (DT == DT_BF16)
-            __builtin_amdgcn_raw_buffer_store_b16((uint16_t)(f2bf_pack(v, 0.f) & 0xffffu), rs, off, 0, 0);
-          else __builtin_amdgcn_raw_buffer_store_b8((uint8_t)v, rs, off, 0, 0);
-        }
-      }
+  for (int j = 0; j < NV_MAX; ++j) {
+    // a chunk past nv re-reads chunk 0 (its values are masked downstream)
+    const int jj = j < G.nv ? j : 0;
+    const u4 v = *(const u4*)(slot + ((jj * HV) * T_LANES + tid) * 16);
+    if constexpr (DT == DT_F32) {
+      const u4 w = *(const u4*)(slot + ((jj * HV + 1) * T_LANES + tid) * 16);
+      d.c[j] = unpack_f32(v, w);
+    } else {
+      d.c[j] = unpack_bf16(v);
     }
   }
 }
 
-__device__ __forceinline__ void load_any(Chunks& dst, const ArgD& a, const Geo& G, const Tile& tl, const Lane& L) {
-  if (a.dt == DT_BF16) load_chunks<DT_BF16>(dst, a, G, tl, L);
-  else if (a.dt == DT_F32) load_chunks<DT_F32>(dst, a, G, tl, L);
-  else load_chunks<DT_U8>(dst, a, G, tl, L);
+// Invariant slot addressing: a shared slot is indexed by the lane's position
+// in its row (stride g), a lane-private one by the lane (stride T).
+__device__ __forceinline__ int inv_base(KW* W, uint32_t k, const Geo& G, const Lane& L, int* stride) {
+  const bool shared = W[H_INV_SHARED0 + k] != 0;
+  *stride = shared ? G.g : T_LANES;
+  return shared ? L.lane : L.tid;
 }
 
-__device__ __forceinline__ void store_any(const Chunks& src, const ArgD& a, const Geo& G, const Tile& tl,
-                                          const Lane& L) {
-  if (a.dt == DT_BF16) store_chunks<DT_BF16>(src, a, G, tl, L);
-  else if (a.dt == DT_F32) store_chunks<DT_F32>(src, a, G, tl, L);
-  else store_chunks<DT_U8>(src, a, G, tl, L);
+__device__ __forceinline__ void inv_write(const Ch& c, char* slot, const Geo& G, int idx, int stride) {
+#pragma unroll
+  for (int j = 0; j < NV_MAX; ++j) {
+    if (j < G.nv) {
+      const V8 x = c.c[j];
+      const f4 a = {x[0], x[1], x[2], x[3]};
+      const f4 b = {x[4], x[5], x[6], x[7]};
+      *(f4*)(slot + (j * stride + idx) * 32) = a;
+      *(f4*)(slot + (j * stride + idx) * 32 + 16) = b;
+    }
+  }
+}
+
+__device__ __forceinline__ void inv_read(Ch& c, const char* slot, const Geo& G, int idx, int stride) {
+#pragma unroll
+  for (int j = 0; j < NV_MAX; ++j) {
+    const int jj = j < G.nv ? j : 0;
+    const f4 a = *(const f4*)(slot + (jj * stride + idx) * 32);
+    const f4 b = *(const f4*)(slot + (jj * stride + idx) * 32 + 16);
+    V8 r;
+    r[0] = a.x; r[1] = a.y; r[2] = a.z; r[3] = a.w;
+    r[4] = b.x; r[5] = b.y; r[6] = b.z; r[7] = b.w;
+    c.c[j] = r;
+  }
+}
+
+// s_waitcnt vmcnt(n) for a wave-uniform n (0..63): the count is an immediate
+// of the instruction, so a switch selects it.
+#define DVM_VMC_CASE(n) case n: asm volatile("s_waitcnt vmcnt(" #n ")" ::: "memory"); break;
+__device__ __forceinline__ void wait_vm(uint32_t n) {
+  switch (n) {
+    DVM_VMC_CASE(0) DVM_VMC_CASE(1) DVM_VMC_CASE(2) DVM_VMC_CASE(3) DVM_VMC_CASE(4) DVM_VMC_CASE(5)
+    DVM_VMC_CASE(6) DVM_VMC_CASE(7) DVM_VMC_CASE(8) DVM_VMC_CASE(9) DVM_VMC_CASE(10) DVM_VMC_CASE(11)
+    DVM_VMC_CASE(12) DVM_VMC_CASE(13) DVM_VMC_CASE(14) DVM_VMC_CASE(15) DVM_VMC_CASE(16) DVM_VMC_CASE(17)
+    DVM_VMC_CASE(18) DVM_VMC_CASE(19) DVM_VMC_CASE(20) DVM_VMC_CASE(21) DVM_VMC_CASE(22) DVM_VMC_CASE(23)
+    DVM_VMC_CASE(24) DVM_VMC_CASE(25) DVM_VMC_CASE(26) DVM_VMC_CASE(27) DVM_VMC_CASE(28) DVM_VMC_CASE(29)
+    DVM_VMC_CASE(30) DVM_VMC_CASE(31) DVM_VMC_CASE(32) DVM_VMC_CASE(33) DVM_VMC_CASE(34) DVM_VMC_CASE(35)
+    DVM_VMC_CASE(36) DVM_VMC_CASE(37) DVM_VMC_CASE(38) DVM_VMC_CASE(39) DVM_VMC_CASE(40) DVM_VMC_CASE(41)
+    DVM_VMC_CASE(42) DVM_VMC_CASE(43) DVM_VMC_CASE(44) DVM_VMC_CASE(45) DVM_VMC_CASE(46) DVM_VMC_CASE(47)
+    DVM_VMC_CASE(48) DVM_VMC_CASE(49) DVM_VMC_CASE(50) DVM_VMC_CASE(51) DVM_VMC_CASE(52) DVM_VMC_CASE(53)
+    DVM_VMC_CASE(54) DVM_VMC_CASE(55) DVM_VMC_CASE(56) DVM_VMC_CASE(57) DVM_VMC_CASE(58) DVM_VMC_CASE(59)
+    DVM_VMC_CASE(60) DVM_VMC_CASE(61) DVM_VMC_CASE(62)
+    default: asm volatile("s_waitcnt vmcnt(63)" ::: "memory"); break;
+  }
+}
+#undef DVM_VMC_CASE
+
+// Per-workgroup context shared by the routines; slot addresses are
+// re-derived from the header at each use (scalar loads) instead of being kept
+// live across the interpreter loop.
+struct Ctx {
+  KW* W;
+  char* lds;
+  uint32_t tile, t_end;
+  __device__ __forceinline__ char* pf(uint32_t k) const { return lds + W[H_PF_OFF0 + k]; }
+  __device__ __forceinline__ char* inv(uint32_t k) const { return lds + W[H_INV_OFF0 + k]; }
+};
+
+// Read from prefetch slot `slot` (the tile was fetched while the previous one
+// ran), then refill the slot with this workgroup's next tile.
+template <uint32_t DT>
+__device__ __forceinline__ void read_pf(Ch& d, uint32_t w0, uint32_t vmc, const ArgD& a, const Geo& G,
+                                        const Tile& tl, const Lane& L, const Ctx& S) {
+  const uint32_t slot = f_b(w0) & 1u;
+  if (tile_full(tl)) {
+    // the previous tile may have been ragged (more instructions issued after
+    // the prefetch): the count stays a lower bound, so the wait stays exact
+    wait_vm(vmc);
+    pf_read<DT>(d, S.pf(slot), G, L.tid);
+  } else {
+    load_dir<DT>(d, a, G, tl, L);
+  }
+  if ((f_flags(w0) & FL_ISSUE) && S.tile + 1 < S.t_end) {
+    const Tile nt = make_tile(G, S.tile + 1);
+    if (tile_full(nt)) {
+      // this lane's reads of the slot have completed before the refill starts
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      pf_issue<DT>(S.pf(slot), a, G, nt, L);
+    }
+  }
+}
+
+__device__ __forceinline__ void read_inv(Ch& d, uint32_t w0, const Geo& G, const Lane& L, const Ctx& S) {
+  const uint32_t k = f_b(w0) & 1u;
+  int stride;
+  const int idx = inv_base(S.W, k, G, L, &stride);
+  inv_read(d, S.inv(k), G, idx, stride);
+}
+
+// Memory operand of a compute instruction: invariant slot, prefetch slot or
+// memory, in the operand's dtype.
+__device__ __forceinline__ void read_mem(Ch& d, uint32_t w0, uint32_t vmc, const ArgD& a, const Geo& G,
+                                         const Tile& tl, const Lane& L, const Ctx& S) {
+  const uint32_t fl = f_flags(w0);
+  if (fl & FL_INV) read_inv(d, w0, G, L, S);
+  else if (fl & FL_PF) {
+    if (a.dt == DT_F32) read_pf<DT_F32>(d, w0, vmc, a, G, tl, L, S);
+    else read_pf<DT_BF16>(d, w0, vmc, a, G, tl, L, S);
+  } else {
+    load_any(d, a, G, tl, L);
+  }
 }
 
 // ---------------------------------------------------------------------------
-// Compute instructions on tile registers
+// Compute routines on tile registers
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ void copy_c(Chunks& d, const Chunks& s, int nv) {
-#pragma unroll
-  for (int j = 0; j < NV_MAX; ++j)
-#pragma unroll
-      for (int i = 0; i < VEC; ++i) d[j * VEC + i] = s[j * VEC + i];
-}
-
-// acc <- acc (op) b, or b (op) acc
 template <uint32_t OPK, bool REV>
-__device__ __forceinline__ void bin_cc(Chunks& acc, const Chunks& b, int nv) {
+__device__ __forceinline__ void bin_cc(Ch& acc, const Ch& b) {
 #pragma unroll
   for (int j = 0; j < NV_MAX; ++j)
 #pragma unroll
-      for (int i = 0; i < VEC; ++i) {
-        const float x = acc[j * VEC + i], y = b[j * VEC + i];
-        acc[j * VEC + i] = REV ? alu<OPK>(y, x) : alu<OPK>(x, y);
-      }
+    for (int i = 0; i < VEC; ++i) {
+      const float x = acc.c[j][i], y = b.c[j][i];
+      acc.c[j][i] = REV ? alu<OPK>(y, x) : alu<OPK>(x, y);
+    }
 }
 
 template <uint32_t OPK, bool REV>
-__device__ __forceinline__ void bin_cs(Chunks& acc, float s, int nv) {
+__device__ __forceinline__ void bin_cs(Ch& acc, float s) {
 #pragma unroll
   for (int j = 0; j < NV_MAX; ++j)
 #pragma unroll
-      for (int i = 0; i < VEC; ++i) {
-        const float x = acc[j * VEC + i];
-        acc[j * VEC + i] = REV ? alu<OPK>(s, x) : alu<OPK>(x, s);
-      }
+    for (int i = 0; i < VEC; ++i) {
+      const float x = acc.c[j][i];
+      acc.c[j][i] = REV ? alu<OPK>(s, x) : alu<OPK>(x, s);
+    }
 }
 
 template <uint32_t F>
-__device__ __forceinline__ void un_c(Chunks& acc, int nv) {
+__device__ __forceinline__ void un_c(Ch& acc) {
 #pragma unroll
   for (int j = 0; j < NV_MAX; ++j)
 #pragma unroll
-      for (int i = 0; i < VEC; ++i) acc[j * VEC + i] = una<F>(acc[j * VEC + i]);
-}
-
-template <uint32_t OPK>
-__device__ __forceinline__ void bin_op(TReg& t, uint32_t w0, uint32_t w1, float rowv, const Chunks& memv,
-                                       const Geo& G) {
-  const uint32_t bk = f_bk(w0), b = f_b(w0);
-  const bool rev = (f_flags(w0) & FL_REV) != 0;
-  const int nv = G.nv;
-  if (bk == BK_TREG) {
-    switch (b * 2 + (rev ? 1 : 0)) {
-      case 0: bin_cc<OPK, false>(t[0], t[0], nv); break;
-      case 1: bin_cc<OPK, true>(t[0], t[0], nv); break;
-      case 2: bin_cc<OPK, false>(t[0], t[1], nv); break;
-      case 3: bin_cc<OPK, true>(t[0], t[1], nv); break;
-      case 4: bin_cc<OPK, false>(t[0], t[2], nv); break;
-      default: bin_cc<OPK, true>(t[0], t[2], nv); break;
-    }
-  } else if (bk == BK_MEM) {
-    if (rev) bin_cc<OPK, true>(t[0], memv, nv);
-    else bin_cc<OPK, false>(t[0], memv, nv);
-  } else {
-    const float s = bk == BK_RREG ? rowv : __uint_as_float(w1);
-    if (rev) bin_cs<OPK, true>(t[0], s, nv);
-    else bin_cs<OPK, false>(t[0], s, nv);
-  }
+    for (int i = 0; i < VEC; ++i) acc.c[j][i] = una<F>(acc.c[j][i]);
 }
 
 // ---------------------------------------------------------------------------
@@ -444,219 +597,42 @@ __device__ __forceinline__ float group_reduce(float acc, int gs) {
 // Partial over this lane's valid elements.  Full tiles mask whole chunks; only
 // ragged tiles mask element by element.
 template <uint32_t KIND>
-__device__ __forceinline__ float lane_partial(const Chunks& c, const Geo& G, const Tile& tl, const Lane& L) {
+__device__ __forceinline__ float lane_partial(const Ch& c, const Geo& G, const Tile& tl, const Lane& L) {
   const float id = KIND == RK_SUM ? 0.f : -__builtin_huge_valf();
   float acc = id;
-  if ((tl.tce & (VEC - 1)) == 0) {
+  if (tile_full(tl)) {
 #pragma unroll
     for (int j = 0; j < NV_MAX; ++j) {
-        float s = c[j * VEC];
+      float s = c.c[j][0];
 #pragma unroll
-        for (int i = 1; i < VEC; ++i) s = comb<KIND>(s, c[j * VEC + i]);
-        const int ct = (j * G.g + L.lane) * VEC;
-        acc = comb<KIND>(acc, lane_sel(L.rok & (ct < tl.tce), s, id));
-      }
+      for (int i = 1; i < VEC; ++i) s = comb<KIND>(s, c.c[j][i]);
+      const int ct = (j * G.g + L.lane) * VEC;
+      acc = comb<KIND>(acc, lane_sel(L.rok & (ct < tl.tce), s, id));
+    }
   } else {
 #pragma unroll
     for (int j = 0; j < NV_MAX; ++j) {
-        const int ct = (j * G.g + L.lane) * VEC;
+      const int ct = (j * G.g + L.lane) * VEC;
 #pragma unroll
-        for (int i = 0; i < VEC; ++i) acc = comb<KIND>(acc, lane_sel(L.rok & (ct + i < tl.tce), c[j * VEC + i], id));
-      }
+      for (int i = 0; i < VEC; ++i) acc = comb<KIND>(acc, lane_sel(L.rok & (ct + i < tl.tce), c.c[j][i], id));
+    }
   }
   return acc;
 }
 
-__device__ __forceinline__ float lane_partial_k(const Chunks& c, const Geo& G, const Tile& tl, const Lane& L,
-                                                uint32_t kind) {
-  return kind == RK_SUM ? lane_partial<RK_SUM>(c, G, tl, L) : lane_partial<RK_MAX>(c, G, tl, L);
-}
-
-__device__ __forceinline__ float lane_partial_any(const TReg& t, uint32_t k, const Geo& G, const Tile& tl,
-                                                  const Lane& L, uint32_t kind) {
-  switch (k) {
-    case 0: return lane_partial_k(t[0], G, tl, L, kind);
-    case 1: return lane_partial_k(t[1], G, tl, L, kind);
-    default: return lane_partial_k(t[2], G, tl, L, kind);
-  }
-}
-
-__device__ __forceinline__ float group_reduce_k(float acc, int gs, uint32_t kind) {
-  return kind == RK_SUM ? group_reduce<RK_SUM>(acc, gs) : group_reduce<RK_MAX>(acc, gs);
-}
-
-__device__ __forceinline__ float comb_k(float a, float b, uint32_t kind) {
-  return kind == RK_SUM ? a + b : comb<RK_MAX>(a, b);
-}
-
-__device__ __forceinline__ void fill_c(Chunks& c, float v) {
-#pragma unroll
-  for (int e = 0; e < E_MAX; ++e) c[e] = v;
-}
-
 // ---------------------------------------------------------------------------
-// LDS staging: next-tile prefetch (direct-to-LDS buffer loads, two buffers
-// by tile parity) and LDS-resident tile-invariant operands.  Every lane reads
-// back exactly the bytes its own loads or stores put in LDS, so no barrier is
-// needed, only the wait for its own outstanding loads.
+// Register file of one lane: three tile registers and four row registers.
 // ---------------------------------------------------------------------------
-typedef __attribute__((address_space(3))) void lds_void;
-
-__device__ __forceinline__ Tile make_tile(const Geo& G, uint32_t id) {
-  Tile tl;
-  const uint32_t ir = id / (uint32_t)G.nc;
-  const uint32_t ic = id - ir * (uint32_t)G.nc;
-  tl.id = id;
-  tl.r0 = (int64_t)ir * G.tr;
-  tl.c0 = (int64_t)ic * G.tc;
-  const int64_t remc = G.C - tl.c0;
-  tl.tce = remc < G.tc ? (int)remc : G.tc;
-  const int64_t remr = G.R - tl.r0;
-  tl.tre = remr < G.tr ? (int)remr : G.tr;
-  return tl;
-}
-
-// a tile whose columns end on a chunk boundary is staged whole
-__device__ __forceinline__ bool tile_full(const Tile& tl) { return (tl.tce & (VEC - 1)) == 0; }
-
-__device__ __forceinline__ uint32_t pf_buf_bytes(const Geo& G, uint32_t dt) {
-  return (uint32_t)G.nv * T_LANES * 16u * (dt == DT_F32 ? 2u : 1u);
-}
-
-__device__ __forceinline__ void pf_issue(char* slot, const ArgD& a, const Geo& G, const Tile& tl, int tid) {
-  const int es = esize(a.dt);
-  const int halves = a.dt == DT_F32 ? 2 : 1;
-  char* base = slot + (tl.id & 1u) * pf_buf_bytes(G, a.dt);
-  const Rsrc rs = tile_rsrc(a, tl);
-  const int row = tid >> G.lg, lane = tid & (G.g - 1);
-  const bool rok = row < tl.tre;
-  const int roff = row * (int)a.sr;
-  const int wave = tid >> 6;
-#pragma unroll
-  for (int j = 0; j < NV_MAX; ++j) {
-    if (j < G.nv) {
-      const int ct = (j * G.g + lane) * VEC;
-      const int off = lane_off(rok & (ct < tl.tce), (roff + ct) * es);
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        if (h < halves) {
-          lds_void* dst = (lds_void*)(base + ((j * halves + h) * T_LANES + wave * 64) * 16);
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst, 16, off == OOB ? OOB : off + 16 * h, 0, 0, 0);
-        }
-      }
-    }
-  }
-}
-
-template <uint32_t DT>
-__device__ __forceinline__ void pf_read(Chunks& dst, const char* slot, const Geo& G, const Tile& tl, int tid) {
-  constexpr int HV = DT == DT_F32 ? 2 : 1;
-  const char* base = slot + (tl.id & 1u) * pf_buf_bytes(G, DT);
-#pragma unroll
-  for (int j = 0; j < NV_MAX; ++j) {
-    {  // a chunk past nv re-reads chunk 0 (its values are masked downstream)
-      const int jj = j < G.nv ? j : 0;
-      const u4 v = *(const u4*)(base + ((jj * HV) * T_LANES + tid) * 16);
-      if constexpr (DT == DT_F32) {
-        const u4 w = *(const u4*)(base + ((jj * HV + 1) * T_LANES + tid) * 16);
-        dst[j * VEC + 0] = __uint_as_float(v.x); dst[j * VEC + 1] = __uint_as_float(v.y);
-        dst[j * VEC + 2] = __uint_as_float(v.z); dst[j * VEC + 3] = __uint_as_float(v.w);
-        dst[j * VEC + 4] = __uint_as_float(w.x); dst[j * VEC + 5] = __uint_as_float(w.y);
-        dst[j * VEC + 6] = __uint_as_float(w.z); dst[j * VEC + 7] = __uint_as_float(w.w);
-      } else {
-        dst[j * VEC + 0] = bf2f(v.x & 0xffffu); dst[j * VEC + 1] = __uint_as_float(v.x & 0xffff0000u);
-        dst[j * VEC + 2] = bf2f(v.y & 0xffffu); dst[j * VEC + 3] = __uint_as_float(v.y & 0xffff0000u);
-        dst[j * VEC + 4] = bf2f(v.z & 0xffffu); dst[j * VEC + 5] = __uint_as_float(v.z & 0xffff0000u);
-        dst[j * VEC + 6] = bf2f(v.w & 0xffffu); dst[j * VEC + 7] = __uint_as_float(v.w & 0xffff0000u);
-      }
-    }
-  }
-}
-
-__device__ __forceinline__ void inv_write(const Chunks& c, char* slot, const Geo& G, int tid) {
-#pragma unroll
-  for (int j = 0; j < NV_MAX; ++j) {
-    if (j < G.nv) {
-      f4 a = {c[j * VEC + 0], c[j * VEC + 1], c[j * VEC + 2], c[j * VEC + 3]};
-      f4 b = {c[j * VEC + 4], c[j * VEC + 5], c[j * VEC + 6], c[j * VEC + 7]};
-      *(f4*)(slot + (j * T_LANES + tid) * 32) = a;
-      *(f4*)(slot + (j * T_LANES + tid) * 32 + 16) = b;
-    }
-  }
-}
-
-__device__ __forceinline__ void inv_read(Chunks& c, const char* slot, const Geo& G, int tid) {
-#pragma unroll
-  for (int j = 0; j < NV_MAX; ++j) {
-    {
-      const int jj = j < G.nv ? j : 0;
-      const f4 a = *(const f4*)(slot + (jj * T_LANES + tid) * 32);
-      const f4 b = *(const f4*)(slot + (jj * T_LANES + tid) * 32 + 16);
-      c[j * VEC + 0] = a.x; c[j * VEC + 1] = a.y; c[j * VEC + 2] = a.z; c[j * VEC + 3] = a.w;
-      c[j * VEC + 4] = b.x; c[j * VEC + 5] = b.y; c[j * VEC + 6] = b.z; c[j * VEC + 7] = b.w;
-    }
-  }
-}
-
-// s_waitcnt vmcnt(n) for a wave-uniform n (0..63): the count is an immediate
-// of the instruction, so a switch selects it.
-#define DVM_VMC_CASE(n) case n: asm volatile("s_waitcnt vmcnt(" #n ")" ::: "memory"); break;
-__device__ __forceinline__ void wait_vm(uint32_t n) {
-  switch (n) {
-    DVM_VMC_CASE(0) DVM_VMC_CASE(1) DVM_VMC_CASE(2) DVM_VMC_CASE(3) DVM_VMC_CASE(4) DVM_VMC_CASE(5)
-    DVM_VMC_CASE(6) DVM_VMC_CASE(7) DVM_VMC_CASE(8) DVM_VMC_CASE(9) DVM_VMC_CASE(10) DVM_VMC_CASE(11)
-    DVM_VMC_CASE(12) DVM_VMC_CASE(13) DVM_VMC_CASE(14) DVM_VMC_CASE(15) DVM_VMC_CASE(16) DVM_VMC_CASE(17)
-    DVM_VMC_CASE(18) DVM_VMC_CASE(19) DVM_VMC_CASE(20) DVM_VMC_CASE(21) DVM_VMC_CASE(22) DVM_VMC_CASE(23)
-    DVM_VMC_CASE(24) DVM_VMC_CASE(25) DVM_VMC_CASE(26) DVM_VMC_CASE(27) DVM_VMC_CASE(28) DVM_VMC_CASE(29)
-    DVM_VMC_CASE(30) DVM_VMC_CASE(31) DVM_VMC_CASE(32) DVM_VMC_CASE(33) DVM_VMC_CASE(34) DVM_VMC_CASE(35)
-    DVM_VMC_CASE(36) DVM_VMC_CASE(37) DVM_VMC_CASE(38) DVM_VMC_CASE(39) DVM_VMC_CASE(40) DVM_VMC_CASE(41)
-    DVM_VMC_CASE(42) DVM_VMC_CASE(43) DVM_VMC_CASE(44) DVM_VMC_CASE(45) DVM_VMC_CASE(46) DVM_VMC_CASE(47)
-    DVM_VMC_CASE(48) DVM_VMC_CASE(49) DVM_VMC_CASE(50) DVM_VMC_CASE(51) DVM_VMC_CASE(52) DVM_VMC_CASE(53)
-    DVM_VMC_CASE(54) DVM_VMC_CASE(55) DVM_VMC_CASE(56) DVM_VMC_CASE(57) DVM_VMC_CASE(58) DVM_VMC_CASE(59)
-    DVM_VMC_CASE(60) DVM_VMC_CASE(61) DVM_VMC_CASE(62)
-    default: asm volatile("s_waitcnt vmcnt(63)" ::: "memory"); break;
-  }
-}
-#undef DVM_VMC_CASE
-
-// Staging context shared by the operand readers; slot addresses are
-// re-derived from the header at each use (scalar loads) instead of being kept
-// live across the interpreter loop.
-struct Stage {
-  const uint32_t* W;
-  char* lds;
-  uint32_t tile, t_end;
-  int tid;
-  __device__ __forceinline__ char* pf(uint32_t k) const { return lds + W[H_PF_OFF0 + k]; }
-  __device__ __forceinline__ char* inv(uint32_t k) const { return lds + W[H_INV_OFF0 + k]; }
+struct Regs {
+  Ch t0, t1, t2;
+  RowRegs rw;
 };
 
-// Operand read for LOAD and memory operands: from an invariant slot, from the
-// prefetch slot (then prefetch the next tile), or straight from memory.
-__device__ __forceinline__ void read_operand(Chunks& dst, uint32_t w0, uint32_t vmc, const ArgD& a, const Geo& G,
-                                             const Tile& tl, const Lane& L, const Stage& S) {
-  const uint32_t fl = f_flags(w0), slot = f_b(w0) & 1u;
-  if (fl & FL_INV) {
-    inv_read(dst, S.inv(slot), G, S.tid);
-    return;
-  }
-  if (fl & FL_PF) {
-    if (tile_full(tl)) {
-      // the previous tile may have been ragged (more instructions issued after
-      // the prefetch): the count stays a lower bound, so the wait stays exact
-      wait_vm(vmc);
-      if (a.dt == DT_F32) pf_read<DT_F32>(dst, S.pf(slot), G, tl, S.tid);
-      else pf_read<DT_BF16>(dst, S.pf(slot), G, tl, S.tid);
-    } else {
-      load_any(dst, a, G, tl, L);
-    }
-    if ((fl & FL_ISSUE) && S.tile + 1 < S.t_end) {
-      const Tile nt = make_tile(G, S.tile + 1);
-      if (tile_full(nt)) pf_issue(S.pf(slot), a, G, nt, S.tid);
-    }
-    return;
-  }
-  load_any(dst, a, G, tl, L);
+template <int K>
+__device__ __forceinline__ Ch& treg(Regs& r) {
+  if constexpr (K == 0) return r.t0;
+  else if constexpr (K == 1) return r.t1;
+  else return r.t2;
 }
 
 }  // namespace
@@ -670,7 +646,8 @@ dvm_vm_vector(const Program prog) {
   __shared__ int s_last;
   extern __shared__ __attribute__((aligned(16))) char dlds[];
 
-  const uint32_t* W = prog.w;
+  (void)prog;
+  KW* W = (KW*)__builtin_amdgcn_kernarg_segment_ptr();
   const uint32_t block_dim = W[H_BLOCK_DIM];
   const uint32_t body_tile = W[H_BODY_TILE];
 
@@ -691,239 +668,231 @@ dvm_vm_vector(const Program prog) {
   uint32_t t_end = t_begin + body_tile;
   if (t_end > block_dim) t_end = block_dim;
 
-  TReg t;
-#pragma unroll
-  for (int k = 0; k < N_TREG; ++k) fill_c(t[k], 0.f);
-  RowRegs rw = {0.f, 0.f, 0.f, 0.f};
+  Regs R;
+  fill(R.t0, 0.f);
+  fill(R.t1, 0.f);
+  fill(R.t2, 0.f);
+  R.rw = {0.f, 0.f, 0.f, 0.f};
 
-  Tile tl;
-  auto set_tile = [&](uint32_t id) {
-    const uint32_t ir = id / (uint32_t)G.nc;
-    const uint32_t ic = id - ir * (uint32_t)G.nc;
-    tl.id = id;
-    tl.r0 = (int64_t)ir * G.tr;
-    tl.c0 = (int64_t)ic * G.tc;
-    const int64_t remc = G.C - tl.c0;
-    tl.tce = remc < G.tc ? (int)remc : G.tc;
-    const int64_t remr = G.R - tl.r0;
-    tl.tre = remr < G.tr ? (int)remr : G.tr;
-  };
-
-  Stage S;
+  Ctx S;
   S.W = W;
   S.lds = dlds;
   S.t_end = t_end;
-  S.tid = tid;
 
+  Tile tl;
   uint32_t tile = t_begin;
   uint32_t pc = W[H_PRO_BEGIN], pc_end = W[H_PRO_END];
   bool in_pro = true;
   if (t_begin < t_end) {
-    set_tile(t_begin);
+    tl = make_tile(G, t_begin);
   } else {
     pc = pc_end = 0;
     in_pro = false;
     tile = t_end;
+    tl = make_tile(G, 0);
   }
+  // the next instruction's words, fetched one dispatch ahead (the encoder
+  // leaves spare words after the body, so this never reads past the program)
+  uint32_t nw0 = W[pc], nw1 = W[pc + 1];
 
   while (true) {
     if (pc >= pc_end) {
       if (in_pro) in_pro = false;
       else ++tile;
       if (tile >= t_end) break;
-      set_tile(tile);
+      tl = make_tile(G, tile);
       pc = W[H_BODY_BEGIN];
       pc_end = W[H_BODY_END];
+      nw0 = W[pc];
+      nw1 = W[pc + 1];
       continue;
     }
-    const uint32_t w0 = W[pc];
-    const uint32_t w1 = W[pc + 1];
+    const uint32_t w0 = nw0, w1 = nw1;
     pc += 2;
+    // Fetch the next instruction only once this one's words have arrived:
+    // scalar loads return out of order, so a wait for the current words
+    // issued after the next fetch would also wait for that fetch.  The opaque
+    // copy of pc makes the fetch address depend on the current words.
+    uint32_t pcn = pc;
+    asm volatile("" : "+s"(pcn) : "s"(w0), "s"(w1));
+    nw0 = W[pcn];
+    nw1 = W[pcn + 1];
     // Lane coordinates are recomputed per instruction (a few ALU ops) rather
     // than kept live across the whole interpreter loop.
     int tidv = tid;
     asm volatile("" : "+v"(tidv));
     Lane L;
+    L.tid = tidv;
     L.row = tidv >> G.lg;
     L.lane = tidv & (G.g - 1);
     L.rok = L.row < tl.tre;
     S.tile = tile;
-    S.tid = tidv;
+
+#define ARG read_arg(W, w1)
+#define CASE_LD(d)                                                                           \
+  case HD_LD_F32 + d: load_dir<DT_F32>(treg<d>(R), ARG, G, tl, L); break;                     \
+  case HD_LD_BF16 + d: load_dir<DT_BF16>(treg<d>(R), ARG, G, tl, L); break;                   \
+  case HD_LD_U8 + d: load_dir<DT_U8>(treg<d>(R), ARG, G, tl, L); break;                       \
+  case HD_LD_PF16 + d: read_pf<DT_BF16>(treg<d>(R), w0, vmc_load(w0), ARG, G, tl, L, S); break; \
+  case HD_LD_PF32 + d: read_pf<DT_F32>(treg<d>(R), w0, vmc_load(w0), ARG, G, tl, L, S); break;  \
+  case HD_LD_INV + d: read_inv(treg<d>(R), w0, G, L, S); break;                               \
+  case HD_ST_F32 + d: store_dir<DT_F32>(treg<d>(R), ARG, G, tl, L); break;                    \
+  case HD_ST_BF16 + d: store_dir<DT_BF16>(treg<d>(R), ARG, G, tl, L); break;                  \
+  case HD_ST_U8 + d: store_dir<DT_U8>(treg<d>(R), ARG, G, tl, L); break;                      \
+  case HD_BCAST + d: fill(treg<d>(R), rget(R.rw, f_a(w0))); break;
+#define CASE_COPY(d, a) \
+  case HD_COPY + 3 * d + a: treg<d>(R) = treg<a>(R); break;
+#define SCALAR_B (f_bk(w0) == BK_IMM ? __uint_as_float(w1) : rget(R.rw, f_b(w0)))
+#define CASE_BIN_DIR(k, rev)                                                                               \
+  case HD_BIN + 10 * k + 5 * rev + BF_T0: bin_cc<k, rev>(R.t0, R.t0); break;                              \
+  case HD_BIN + 10 * k + 5 * rev + BF_T1: bin_cc<k, rev>(R.t0, R.t1); break;                              \
+  case HD_BIN + 10 * k + 5 * rev + BF_T2: bin_cc<k, rev>(R.t0, R.t2); break;                              \
+  case HD_BIN + 10 * k + 5 * rev + BF_SCALAR: bin_cs<k, rev>(R.t0, SCALAR_B); break;                      \
+  case HD_BIN + 10 * k + 5 * rev + BF_MEM: {                                                              \
+    Ch m;                                                                                                  \
+    read_mem(m, w0, vmc_bin(w0), ARG, G, tl, L, S);                                                        \
+    bin_cc<k, rev>(R.t0, m);                                                                               \
+    break;                                                                                                 \
+  }
+#define CASE_BIN_COMM(k) CASE_BIN_DIR(k, false)
+#define CASE_BIN_NC(k) CASE_BIN_DIR(k, false) CASE_BIN_DIR(k, true)
+#define CASE_RED(kind, a)                                                                  \
+  case HD_RED + 3 * kind + a: {                                                            \
+    float acc = lane_partial<kind>(treg<a>(R), G, tl, L);                                  \
+    acc = group_reduce<kind>(acc, gs);                                                     \
+    /* after the 64-lane all-reduce every lane of a wave holds the same value, */          \
+    /* so every lane stores it (no lane-dependent branch in the loop) */                   \
+    if (G.g <= 64) rset(R.rw, f_dst(w0), acc);                                             \
+    else s_red[f_b(w0)][wave] = acc;                                                       \
+    break;                                                                                 \
+  }                                                                                        \
+  case HD_ALL + 3 * kind + a: {                                                            \
+    float acc = lane_partial<kind>(treg<a>(R), G, tl, L);                                  \
+    acc = group_reduce<kind>(acc, 64);                                                     \
+    s_red[f_b(w0)][wave] = acc;                                                            \
+    break;                                                                                 \
+  }
 
     switch (f_op(w0)) {
-      case OP_LOAD: {
-        Chunks tmp;
-        read_operand(tmp, w0, vmc_load(w0), read_arg(W, w1), G, tl, L, S);
-        switch (f_dst(w0)) {
-          case 0: copy_c(t[0], tmp, NV_MAX); break;
-          case 1: copy_c(t[1], tmp, NV_MAX); break;
-          default: copy_c(t[2], tmp, NV_MAX); break;
-        }
+      CASE_LD(0) CASE_LD(1) CASE_LD(2)
+      CASE_COPY(0, 1) CASE_COPY(0, 2) CASE_COPY(1, 0) CASE_COPY(1, 2) CASE_COPY(2, 0) CASE_COPY(2, 1)
+      case HD_UN + UN_SQRT: un_c<UN_SQRT>(R.t0); break;
+      case HD_UN + UN_ABS: un_c<UN_ABS>(R.t0); break;
+      case HD_UN + UN_LOG: un_c<UN_LOG>(R.t0); break;
+      case HD_UN + UN_EXP: un_c<UN_EXP>(R.t0); break;
+      case HD_UN + UN_ROUND: un_c<UN_ROUND>(R.t0); break;
+      case HD_UN + UN_FLOOR: un_c<UN_FLOOR>(R.t0); break;
+      case HD_UN + UN_ISFINITE: un_c<UN_ISFINITE>(R.t0); break;
+      case HD_UN + UN_NEG: un_c<UN_NEG>(R.t0); break;
+      case HD_UN + UN_RECIP: un_c<UN_RECIP>(R.t0); break;
+      case HD_UN + UN_TOBF16: un_c<UN_TOBF16>(R.t0); break;
+      CASE_BIN_COMM(ALU_ADD) CASE_BIN_NC(ALU_SUB) CASE_BIN_COMM(ALU_MUL) CASE_BIN_NC(ALU_DIV)
+      CASE_BIN_COMM(ALU_MAX) CASE_BIN_COMM(ALU_MIN) CASE_BIN_NC(ALU_POW)
+      CASE_RED(RK_SUM, 0) CASE_RED(RK_SUM, 1) CASE_RED(RK_SUM, 2)
+      CASE_RED(RK_MAX, 0) CASE_RED(RK_MAX, 1) CASE_RED(RK_MAX, 2)
+      case HD_RED_FIN + RK_SUM:
+      case HD_RED_FIN + RK_MAX: {
+        const uint32_t kind = f_op(w0) - HD_RED_FIN;
+        const int nw = G.g >> 6;
+        const float* buf = s_red[f_b(w0)] + L.row * nw;
+        float acc = buf[0];
+        for (int k = 1; k < nw; ++k) acc = kind == RK_SUM ? acc + buf[k] : comb<RK_MAX>(acc, buf[k]);
+        rset(R.rw, f_dst(w0), acc);
         break;
       }
-      case OP_PF: {
-        const ArgD a = read_arg(W, w1);
-        if (tile_full(tl)) pf_issue(S.pf(f_b(w0) & 1u), a, G, tl, tidv);
+      case HD_ALL_FIN + RK_SUM:
+      case HD_ALL_FIN + RK_MAX: {
+        // every lane combines the per-wave partials (LDS broadcast reads);
+        // lane 0 alone stores the tile's partial, the others are masked by an
+        // out-of-range offset
+        const uint32_t kind = f_op(w0) - HD_ALL_FIN;
+        const float* buf = s_red[f_b(w0)];
+        float acc = buf[0];
+        for (int k = 1; k < T_LANES / 64; ++k) acc = kind == RK_SUM ? acc + buf[k] : comb<RK_MAX>(acc, buf[k]);
+        const ArgD a = read_arg(W, W[H_ALL_SCRATCH]);
+        const Rsrc rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(a.p) + 256, 0, (int)(block_dim * 4u),
+                                                          RSRC_W3);
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc), rs, lane_off(tidv == 0, (int)(tl.id * 4u)), 0, 0);
         break;
       }
-      case OP_LDS_INV: {
-        const ArgD a = read_arg(W, w1);
-        Chunks tmp;
-        load_any(tmp, a, G, tl, L);
-        inv_write(tmp, S.inv(f_dst(w0) & 1u), G, tidv);
+      case HD_SYNC:
+        // LDS exchange only: wait for this wave's LDS operations, then meet
+        // the other waves (no wait on outstanding global loads, so prefetches
+        // stay in flight across the barrier)
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        break;
+      case HD_RBIN: {
+        const float x = rget(R.rw, f_a(w0));
+        const float y = f_bk(w0) == BK_RREG ? rget(R.rw, f_b(w0)) : __uint_as_float(w1);
+        const bool rev = (f_flags(w0) & FL_REV) != 0;
+        rset(R.rw, f_dst(w0), rev ? alu_rt(f_sub(w0), y, x) : alu_rt(f_sub(w0), x, y));
         break;
       }
-      case OP_STORE: {
-        const ArgD a = read_arg(W, w1);
-        switch (f_a(w0)) {
-          case 0: store_any(t[0], a, G, tl, L); break;
-          case 1: store_any(t[1], a, G, tl, L); break;
-          default: store_any(t[2], a, G, tl, L); break;
-        }
+      case HD_RUN:
+        rset(R.rw, f_dst(w0), una_rt(f_sub(w0), rget(R.rw, f_a(w0))));
         break;
-      }
-      case OP_LOAD_ROW: {
-        const ArgD a = read_arg(W, w1);
-        const Rsrc rs = tile_rsrc(a, tl);
+      case HD_LD_ROW: {
+        const ArgD a = ARG;
         const int es = esize(a.dt);
+        const Rsrc rs = tile_rsrc(a, tl, es);
         const int off = lane_off(L.rok, L.row * (int)a.sr * es);
         float v;
         if (a.dt == DT_BF16) v = bf2f(__builtin_amdgcn_raw_buffer_load_b16(rs, off, 0, 0));
         else if (a.dt == DT_F32) v = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, 0));
         else v = (float)__builtin_amdgcn_raw_buffer_load_b8(rs, off, 0, 0);
-        rset(rw, f_dst(w0), v);
+        rset(R.rw, f_dst(w0), v);
         break;
       }
-      case OP_STORE_ROW: {
-        const ArgD a = read_arg(W, w1);
-        const Rsrc rs = tile_rsrc(a, tl);
+      case HD_ST_ROW: {
+        const ArgD a = ARG;
         const int es = esize(a.dt);
+        const Rsrc rs = tile_rsrc(a, tl, es);
         const int off = lane_off(L.rok & (L.lane == 0), L.row * (int)a.sr * es);
-        const float v = rget(rw, f_a(w0));
+        const float v = rget(R.rw, f_a(w0));
         if (a.dt == DT_BF16) __builtin_amdgcn_raw_buffer_store_b16((uint16_t)(f2bf_pack(v, 0.f) & 0xffffu), rs, off, 0, 0);
         else if (a.dt == DT_F32) __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), rs, off, 0, 0);
         else __builtin_amdgcn_raw_buffer_store_b8((uint8_t)v, rs, off, 0, 0);
         break;
       }
-      case OP_COPY: {
-        switch (f_dst(w0) * 4 + f_a(w0)) {
-          case 1: copy_c(t[0], t[1], G.nv); break;
-          case 2: copy_c(t[0], t[2], G.nv); break;
-          case 4: copy_c(t[1], t[0], G.nv); break;
-          case 6: copy_c(t[1], t[2], G.nv); break;
-          case 8: copy_c(t[2], t[0], G.nv); break;
-          case 9: copy_c(t[2], t[1], G.nv); break;
-          default: break;
-        }
-        break;
-      }
-      case OP_BIN: {
-        const float rowv = f_bk(w0) == BK_RREG ? rget(rw, f_b(w0)) : 0.f;
-        Chunks tmp;
-        if (f_bk(w0) == BK_MEM) read_operand(tmp, w0, vmc_bin(w0), read_arg(W, w1), G, tl, L, S);
-        switch (f_sub(w0)) {
-          case ALU_ADD: bin_op<ALU_ADD>(t, w0, w1, rowv, tmp, G); break;
-          case ALU_SUB: bin_op<ALU_SUB>(t, w0, w1, rowv, tmp, G); break;
-          case ALU_MUL: bin_op<ALU_MUL>(t, w0, w1, rowv, tmp, G); break;
-          case ALU_DIV: bin_op<ALU_DIV>(t, w0, w1, rowv, tmp, G); break;
-          case ALU_MAX: bin_op<ALU_MAX>(t, w0, w1, rowv, tmp, G); break;
-          case ALU_MIN: bin_op<ALU_MIN>(t, w0, w1, rowv, tmp, G); break;
-          default: bin_op<ALU_POW>(t, w0, w1, rowv, tmp, G); break;
-        }
-        break;
-      }
-      case OP_UN: {
-        switch (f_sub(w0)) {
-          case UN_SQRT: un_c<UN_SQRT>(t[0], G.nv); break;
-          case UN_ABS: un_c<UN_ABS>(t[0], G.nv); break;
-          case UN_LOG: un_c<UN_LOG>(t[0], G.nv); break;
-          case UN_EXP: un_c<UN_EXP>(t[0], G.nv); break;
-          case UN_ROUND: un_c<UN_ROUND>(t[0], G.nv); break;
-          case UN_FLOOR: un_c<UN_FLOOR>(t[0], G.nv); break;
-          case UN_ISFINITE: un_c<UN_ISFINITE>(t[0], G.nv); break;
-          case UN_NEG: un_c<UN_NEG>(t[0], G.nv); break;
-          case UN_RECIP: un_c<UN_RECIP>(t[0], G.nv); break;
-          case UN_TOBF16: un_c<UN_TOBF16>(t[0], G.nv); break;
-          default: break;
-        }
-        break;
-      }
-      case OP_RBIN: {
-        const float x = rget(rw, f_a(w0));
-        const float y = f_bk(w0) == BK_RREG ? rget(rw, f_b(w0)) : __uint_as_float(w1);
-        const bool rev = (f_flags(w0) & FL_REV) != 0;
-        rset(rw, f_dst(w0), rev ? alu_rt(f_sub(w0), y, x) : alu_rt(f_sub(w0), x, y));
-        break;
-      }
-      case OP_RUN:
-        rset(rw, f_dst(w0), una_rt(f_sub(w0), rget(rw, f_a(w0))));
-        break;
-      case OP_BCAST: {
-        const float v = rget(rw, f_a(w0));
-        switch (f_dst(w0)) {
-          case 0: fill_c(t[0], v); break;
-          case 1: fill_c(t[1], v); break;
-          default: fill_c(t[2], v); break;
-        }
-        break;
-      }
-      case OP_RED: {
-        const uint32_t kind = f_sub(w0);
-        float acc = lane_partial_any(t, f_a(w0), G, tl, L, kind);
-        acc = group_reduce_k(acc, gs, kind);
-        // after the 64-lane all-reduce every lane of a wave holds the same
-        // value, so every lane stores it (no lane-dependent branch in the loop)
-        if (G.g <= 64) rset(rw, f_dst(w0), acc);
-        else s_red[f_b(w0)][wave] = acc;
-        break;
-      }
-      case OP_RED_FIN: {
-        const uint32_t kind = f_sub(w0);
-        const int nw = G.g >> 6;
-        const int base = L.row * nw;
-        const float* buf = s_red[f_b(w0)];
-        float acc = buf[base];
-        for (int k = 1; k < nw; ++k) acc = comb_k(acc, buf[base + k], kind);
-        rset(rw, f_dst(w0), acc);
-        break;
-      }
-      case OP_SYNC:
-        __syncthreads();
-        break;
-      case OP_ALL: {
-        const uint32_t kind = f_sub(w0);
-        float acc = lane_partial_any(t, f_a(w0), G, tl, L, kind);
-        acc = group_reduce_k(acc, 64, kind);
-        s_red[f_b(w0)][wave] = acc;
-        break;
-      }
-      case OP_ALL_FIN: {
-        // every lane combines the per-wave partials (LDS broadcast reads);
-        // lane 0 alone stores the tile's partial, the others are masked by
-        // an out-of-range offset
-        const uint32_t kind = f_sub(w0);
-        const float* buf = s_red[f_b(w0)];
-        float acc = buf[0];
-        for (int k = 1; k < T_LANES / 64; ++k) acc = comb_k(acc, buf[k], kind);
-        const ArgD a = read_arg(W, W[H_ALL_SCRATCH]);
-        const Rsrc rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(a.p) + 256, 0, (int)(block_dim * 4u),
-                                                          RSRC_W3);
-        const int off = tidv == 0 ? (int)(tl.id * 4u) : OOB;
-        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc), rs, off, 0, 0);
-        break;
-      }
-      case OP_DBG: {
+      case HD_DBG: {
         const float v = f_sub(w0) == 0 ? (float)tl.id : (float)blockIdx.x;
-        switch (f_dst(w0)) {
-          case 0: fill_c(t[0], v); break;
-          case 1: fill_c(t[1], v); break;
-          default: fill_c(t[2], v); break;
+        if (f_dst(w0) == 0) fill(R.t0, v);
+        else if (f_dst(w0) == 1) fill(R.t1, v);
+        else fill(R.t2, v);
+        break;
+      }
+      case HD_LDS_INV: {
+        // prologue: the invariant operand's tile view, as fp32, into its slot
+        const uint32_t k = f_dst(w0) & 1u;
+        int stride;
+        const int idx = inv_base(W, k, G, L, &stride);
+        Ch tmp;
+        load_any(tmp, ARG, G, tl, L, stride != T_LANES);
+        inv_write(tmp, S.inv(k), G, idx, stride);
+        break;
+      }
+      case HD_PF: {
+        // prologue: fetch the workgroup's first tile into the prefetch slot
+        const ArgD a = ARG;
+        if (tile_full(tl)) {
+          if (a.dt == DT_F32) pf_issue<DT_F32>(S.pf(f_b(w0) & 1u), a, G, tl, L);
+          else pf_issue<DT_BF16>(S.pf(f_b(w0) & 1u), a, G, tl, L);
         }
         break;
       }
       default:
         break;
     }
+#undef ARG
+#undef CASE_LD
+#undef CASE_COPY
+#undef SCALAR_B
+#undef CASE_BIN_DIR
+#undef CASE_BIN_COMM
+#undef CASE_BIN_NC
+#undef CASE_RED
   }
 
   // Reduce-all epilogue: the last workgroup to finish combines the per-tile
@@ -943,14 +912,16 @@ dvm_vm_vector(const Program prog) {
     if (s_last) {
       __atomic_thread_fence(__ATOMIC_ACQUIRE);
       float acc = kind == RK_SUM ? 0.f : -__builtin_huge_valf();
-      for (uint32_t i = (uint32_t)tid; i < block_dim; i += T_LANES)
-        acc = comb_k(acc, __hip_atomic_load(part + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT), kind);
-      acc = group_reduce_k(acc, 64, kind);
+      for (uint32_t i = (uint32_t)tid; i < block_dim; i += T_LANES) {
+        const float v = __hip_atomic_load(part + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        acc = kind == RK_SUM ? acc + v : comb<RK_MAX>(acc, v);
+      }
+      acc = kind == RK_SUM ? group_reduce<RK_SUM>(acc, 64) : group_reduce<RK_MAX>(acc, 64);
       if ((tid & 63) == 0) s_red[0][wave] = acc;
       __syncthreads();
       if (tid == 0) {
         float r = s_red[0][0];
-        for (int k = 1; k < T_LANES / 64; ++k) r = comb_k(r, s_red[0][k], kind);
+        for (int k = 1; k < T_LANES / 64; ++k) r = kind == RK_SUM ? r + s_red[0][k] : comb<RK_MAX>(r, s_red[0][k]);
         const ArgD oa = read_arg(W, W[H_ALL_OUT]);
         if (oa.dt == DT_BF16)
           *reinterpret_cast<uint16_t*>(const_cast<char*>(oa.p)) = (uint16_t)(f2bf_pack(r, 0.f) & 0xffffu);

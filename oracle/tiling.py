@@ -17,11 +17,11 @@ design notes):
 * Iteration space.  The dominant shape is collapsed to two dims [R, C]: C is
   the innermost dim, R the product of the outer dims.  Elementwise graphs whose
   every operand is contiguous (or a scalar) collapse further to [1, numel].
-* Per-core resource.  A core is one workgroup of T = 512 lanes; a tile row is
-  spread over g lanes, each holding up to NV_MAX = 2 chunks of V = 8 elements
-  in registers.  Rows of a tile go to P = next_pow2(tr) lane groups of
-  g = T / P lanes.  A tile is feasible iff P <= T and
-  NV = ceil((tc + pad) / (g V)) <= NV_MAX.
+* Per-core resource.  A core is one workgroup of T = 256 lanes, two of them
+  resident per compute unit; a tile row is spread over g lanes, each holding
+  up to NV_MAX = 5 chunks of V = 8 elements in registers.  Rows of a tile go
+  to P = next_pow2(tr) lane groups of g = T / P lanes.  A tile is feasible iff
+  P <= T and NV = ceil((tc + pad) / (g V)) <= NV_MAX.
 * Alignment pad.  pad = V - 1 if some unit-stride operand does not start every
   row on a 16-byte boundary, else 0: a misaligned row may need one more chunk.
 * hardware_align_div(n, k, W) = W * ceil(ceil(n / k) / W) with W = 64 V = 512
@@ -31,10 +31,10 @@ design notes):
   reduce-all graphs first try tr = ceil(R / k) with the widest aligned tc,
   then, at tr = 1, tc = min(C, had(C, k, W)) for k = 2, 4, ... until tc stops
   changing or reaches W.  Consecutive duplicates are dropped.
-* Cost (integer "ticks", 1 tick = 1/31250 us): G = 256 resident workgroups
-  (one per compute unit), A = 15625 ticks (0.5 us) of fixed work per tile,
-  and 1 tick per byte a workgroup moves (8 TB/s shared by G workgroups is
-  31250 bytes/us each):
+* Cost (integer "ticks", 1 tick = 1/15625 us): G = 512 resident workgroups
+  (two per compute unit), A = 7812 ticks (about 0.5 us) of fixed work per
+  tile, and 1 tick per byte a workgroup moves (8 TB/s shared by G workgroups
+  is 15625 bytes/us each):
   cost = ceil(n_tiles / G) * (A + var_bytes) + inv_bytes, where
   var_bytes are the bytes one tile touches in operands that change from tile
   to tile and inv_bytes those of tile-invariant operands, loaded once per
@@ -49,12 +49,12 @@ from __future__ import annotations
 
 from dataclasses import dataclass, field
 
-T_LANES = 512
+T_LANES = 256
 VEC = 8
-NV_MAX = 2
+NV_MAX = 5
 W_ALIGN = 64 * VEC
-G_WG = 256
-A_TICKS = 15625
+G_WG = 512
+A_TICKS = 7812
 BYTE_TICKS = 1
 
 ELEMWISE, ROWREDUCE, ALLREDUCE, MATMUL = "elemwise", "rowreduce", "allreduce", "matmul"

@@ -27,11 +27,13 @@ def test_sqrt_add_workload_choice_by_hand():
     p = TL.plan(TL.ELEMWISE, R, C, ops)
     assert [tc for _, tc in p.path] == [528903, 264704, 132608, 66560, 33280, 16896, 8704,
                                         4608, 2560, 1536, 1024, 512]
-    # costs worked by hand: ceil(tiles/256) * (15625 + 12*tc) for the feasible tail
-    assert p.costs[7:] == [70921, 46345, 68114, 83739, 108845]
-    assert p.costs[:7] == [None] * 7
-    assert (p.tr, p.tc, p.block_dim, p.body_tile, p.grid) == (1, 2560, 207, 1, 207)
-    assert (p.P, p.g, p.nv, p.pad) == (1, 512, 1, 0)
+    # one 256-lane row holds at most 5 * 256 * 8 = 10240 columns; costs worked
+    # by hand: ceil(tiles / 512) * (7812 + 12 * tc) for the feasible tail
+    # (61, 115, 207, 345, 517, 1034 tiles)
+    assert p.costs[:6] == [None] * 6
+    assert p.costs[6:] == [112260, 63108, 38532, 26244, 2 * 20100, 3 * 13956]
+    assert (p.tr, p.tc, p.block_dim, p.body_tile, p.grid) == (1, 1536, 345, 1, 345)
+    assert (p.P, p.g, p.nv, p.pad) == (1, 256, 1, 0)
 
 
 def test_layernorm_rows_choice_by_hand():
@@ -41,36 +43,42 @@ def test_layernorm_rows_choice_by_hand():
     bet = Operand(4, 0, 1)
     p = TL.plan(TL.ROWREDUCE, 1000, 5120, [x, gam, bet, y])
     assert [tr for tr, _ in p.path] == [1000, 500, 250, 125, 63, 32, 16, 8, 4, 2, 1]
-    assert p.costs[:-1] == [None] * 10          # 2+ rows of 5120 need > 2 chunks per lane
-    assert p.costs[-1] == 4 * (15625 + 20480) + 40960
-    assert (p.tr, p.tc, p.block_dim, p.body_tile, p.grid, p.g, p.nv) == (1, 5120, 1000, 4, 250, 512, 2)
+    # 4 rows of 5120 need 10 chunks per lane; 2 rows need 5 (g = 128)
+    assert p.costs[:-2] == [None] * 9
+    # tr=2: 500 tiles in one round, x and y vary (2*5120*2 bytes each), gamma
+    # and beta are invariant (5120*4 bytes each); tr=1: 1000 tiles, two rounds
+    assert p.costs[-2:] == [(7812 + 40960) + 40960, 2 * (7812 + 20480) + 40960]
+    assert (p.tr, p.tc, p.block_dim, p.body_tile, p.grid, p.g, p.nv) == (2, 5120, 500, 1, 500, 128, 5)
 
 
 def test_softmax_misaligned_rows_by_hand():
     s = Operand(2, 3001, 1)
     o = Operand(2, 3001, 1)
     assert TL.alignment_pad(280, [s, o]) == 7
-    assert TL.geometry(2, 3001, 7) == (2, 256, 2, True)
-    assert TL.geometry(3, 3001, 7) == (4, 128, 3, False)
+    assert TL.geometry(2, 3001, 7) == (2, 128, 3, True)
+    assert TL.geometry(3, 3001, 7) == (4, 64, 6, False)
     p = TL.plan(TL.ROWREDUCE, 280, 3001, [s, o])
-    # tr=2: 140 tiles, 1 round of (15625 + 2*3001*2*2); tr=1: 2 rounds of (15625 + 3001*2*2)
-    assert p.costs[-2:] == [39633, 2 * 27629]
-    assert p.tr == 2 and p.block_dim == 140
+    # tr=2: 140 tiles, 1 round of (7812 + 2*3001*2*2); tr=1: 280 tiles, still
+    # 1 round, of (7812 + 3001*2*2): the smaller tile wins
+    assert p.costs[-2:] == [31820, 19816]
+    assert p.tr == 1 and p.block_dim == 280
+    # with 4000 rows the rounds differ (4 against 8) and the 2-row tile wins
     p = TL.plan(TL.ROWREDUCE, 4000, 3001, [s, o])
     i2 = [tr for tr, _ in p.path].index(2)
-    assert p.costs[i2] == 8 * 39633 and p.costs[-1] == 16 * 27629
+    assert p.costs[i2] == 4 * 31820 and p.costs[-1] == 8 * 19816
     assert p.tr == 2 and p.block_dim == 2000
 
 
 def test_feasibility_edges():
-    assert TL.geometry(1, 8192, 0)[3] is True
-    assert TL.geometry(1, 8192, 7)[3] is False
-    assert TL.geometry(1, 8185, 7)[3] is True
-    assert TL.geometry(256, 8, 0) == (256, 2, 1, True)
-    assert TL.geometry(512, 8, 0) == (512, 1, 1, True)
-    assert TL.geometry(513, 8, 0)[3] is False
+    assert TL.geometry(1, 10240, 0)[3] is True
+    assert TL.geometry(1, 10240, 7)[3] is False
+    assert TL.geometry(1, 10233, 7)[3] is True
+    assert TL.geometry(1, 10241, 0)[3] is False
+    assert TL.geometry(256, 8, 0) == (256, 1, 1, True)
+    assert TL.geometry(128, 8, 0) == (128, 2, 1, True)
+    assert TL.geometry(257, 8, 0)[3] is False
     with pytest.raises(ValueError):
-        TL.plan(TL.ROWREDUCE, 10, 8192, [Operand(2, 8193, 1)])   # misaligned 8192-wide rows
+        TL.plan(TL.ROWREDUCE, 10, 10240, [Operand(2, 10241, 1)])   # misaligned 10240-wide rows
 
 
 def test_alignment_pad_rules():
@@ -126,7 +134,7 @@ def test_coverage_and_ranges_brute_force():
 def test_header_formula_cases():
     assert TL.header(0) == (0, 0)
     assert TL.header(1) == (1, 1)
-    assert TL.header(256) == (1, 256)
-    assert TL.header(512) == (2, 256)
-    assert TL.header(513) == (3, 171)
-    assert TL.header(1025) == (5, 205)
+    assert TL.header(512) == (1, 512)
+    assert TL.header(513) == (2, 257)
+    assert TL.header(1024) == (2, 512)
+    assert TL.header(1025) == (3, 342)
