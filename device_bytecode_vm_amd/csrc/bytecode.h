@@ -124,7 +124,7 @@ enum Op : uint32_t {
   OP_RBIN = 8,       // rreg[dst] <- rreg[a] (op) (rreg[b] | imm)
   OP_RUN = 9,        // rreg[dst] <- f(rreg[a])
   OP_RED = 10,       // row reduce of treg[a]: rreg[dst] (and LDS buffer b if the row spans waves)
-  OP_RED_FIN = 11,   // rreg[dst] <- combine of LDS buffer b for this lane's row
+  OP_RED_FIN = 11,   // (unused: cross-wave row reductions are OP_REDX)
   OP_SYNC = 12,      // workgroup barrier inserted by the encoder
   OP_ALL = 13,       // reduce-all partial of treg[a] into LDS buffer b
   OP_ALL_FIN = 14,   // tile partial from LDS buffer b -> scratch[tile]
@@ -132,6 +132,8 @@ enum Op : uint32_t {
   OP_DBG = 16,       // treg[dst] <- tile id (sub 0) / workgroup id (sub 1)
   OP_LDS_INV = 17,   // prologue: invariant slot dst <- arg[w1] (fp32, lane-private)
   OP_PF = 18,        // prologue: prefetch slot b <- arg[w1] for the first tile
+  OP_REDX = 19,      // row reduce of treg[a] across waves: partial into LDS buffer b,
+                     //   workgroup barrier, combine of the row's partials into rreg[dst]
   OP_COUNT
 };
 
@@ -143,34 +145,36 @@ enum Op : uint32_t {
 // meaning (staging slot, wait count, row register, scalar / argument word).
 enum Handler : uint32_t {
   HD_END = 0,
-  HD_LD_F32 = 1,     // + d: treg[d] <- arg[w1] tile, f32, straight from memory
-  HD_LD_BF16 = 4,    // + d
-  HD_LD_U8 = 7,      // + d
+  HD_LD_DIR = 1,     // + d: treg[d] <- arg[w1] tile, straight from memory (any dtype)
   HD_LD_PF16 = 10,   // + d: bf16 from prefetch slot b (then refill it, if FL_ISSUE)
   HD_LD_PF32 = 13,   // + d: f32 from prefetch slot b
   HD_LD_INV = 16,    // + d: from invariant slot b
-  HD_ST_F32 = 19,    // + a: arg[w1] <- treg[a]
-  HD_ST_BF16 = 22,   // + a
-  HD_ST_U8 = 25,     // + a
+  HD_ST_DIR = 19,    // + a: arg[w1] <- treg[a] (any dtype)
+  HD_ST_BF16 = 22,   // arg[w1] <- ACC, bf16
+  HD_ST_F32 = 23,    // arg[w1] <- ACC, f32
   HD_COPY = 28,      // + 3 d + a: treg[d] <- treg[a]
   HD_UN = 37,        // + f (Una): ACC <- f(ACC)
   HD_BIN = 48,       // + 10 alu + form: ACC <- ACC (op) B; forms 0..2: B = treg[form],
-                     //   3: B = row register b or the immediate w1, 4: B = memory
-                     //   operand arg[w1]; + 5: reversed, B (op) ACC
-  HD_RED = 118,      // + 3 kind + a: row reduce of treg[a] into rreg[dst] / LDS buffer b
-  HD_RED_FIN = 124,  // + kind
-  HD_ALL = 126,      // + 3 kind + a
-  HD_ALL_FIN = 132,  // + kind
-  HD_BCAST = 134,    // + d
-  HD_RBIN = 137,
-  HD_RUN = 138,
-  HD_SYNC = 139,
-  HD_LD_ROW = 140,
-  HD_ST_ROW = 141,
-  HD_DBG = 142,
-  HD_LDS_INV = 143,
-  HD_PF = 144,
-  HD_COUNT = 145
+                     //   3: B = row register b or the immediate w1; + 5: reversed,
+                     //   B (op) ACC (pow, division by a register and memory operands
+                     //   have handlers of their own)
+  HD_RED = 118,      // + 3 kind + a: row reduce of treg[a] into rreg[dst] (rows inside a wave)
+  HD_REDX = 124,     // + 3 kind + a: OP_REDX (rows across waves)
+  HD_ALL = 130,      // + 3 kind + a: reduce-all partial of treg[a] into LDS buffer b
+  HD_ALL_FIN = 136,  // + kind
+  HD_BCAST = 138,    // + d
+  HD_RBIN = 141,
+  HD_RUN = 142,
+  HD_SYNC = 143,
+  HD_LD_ROW = 144,
+  HD_ST_ROW = 145,
+  HD_DBG = 146,
+  HD_LDS_INV = 147,
+  HD_PF = 148,
+  HD_BIN_POW = 149,  // ACC <- ACC pow B (or B pow ACC), B of forms 0..3 (from bk, b)
+  HD_BIN_MEM = 150,  // ACC <- ACC (op) B for a memory operand, any ALU op (sub, FL_REV)
+  HD_DIV_T = 151,    // ACC <- ACC / treg[b] (or treg[b] / ACC)
+  HD_COUNT = 152
 };
 enum BinForm : uint32_t { BF_T0 = 0, BF_T1 = 1, BF_T2 = 2, BF_SCALAR = 3, BF_MEM = 4, BF_REV = 5 };
 

@@ -1061,9 +1061,7 @@ struct Encoder {
     if (dst < 0) return fail(DVM_ERR_RESOURCE, "row registers exhausted at op %d", i);
     if (plan.g > 64) {
       const uint32_t buf = (uint32_t)(n_red++ % N_LDSBUF);
-      emit(enc0(OP_RED, dst, k, buf, kind, 0, 0), 0);
-      emit(enc0(OP_SYNC, 0, 0, 0, 0, 0, 0), 0);
-      emit(enc0(OP_RED_FIN, dst, 0, buf, kind, 0, 0), 0);
+      emit(enc0(OP_REDX, dst, k, buf, kind, 0, 0), 0);
       cross_wave = true;
     } else {
       emit(enc0(OP_RED, dst, k, 0, kind, 0, 0), 0);
@@ -1224,20 +1222,25 @@ struct Encoder {
       case OP_LOAD:
         if (fl & FL_INV) return HD_LD_INV + d;
         if (fl & FL_PF) return (dt(w1) == DT_F32 ? HD_LD_PF32 : HD_LD_PF16) + d;
-        return (dt(w1) == DT_F32 ? HD_LD_F32 : dt(w1) == DT_BF16 ? HD_LD_BF16 : HD_LD_U8) + d;
+        return HD_LD_DIR + d;
       case OP_STORE:
-        return (dt(w1) == DT_F32 ? HD_ST_F32 : dt(w1) == DT_BF16 ? HD_ST_BF16 : HD_ST_U8) + a;
+        if (a == 0 && dt(w1) == DT_BF16) return HD_ST_BF16;
+        if (a == 0 && dt(w1) == DT_F32) return HD_ST_F32;
+        return HD_ST_DIR + a;
       case OP_COPY: return HD_COPY + 3 * d + a;
       case OP_UN: return HD_UN + sub;
       case OP_BIN: {
         const uint32_t bk = f_bk(w0);
-        const uint32_t form = bk == BK_TREG ? f_b(w0) : bk == BK_MEM ? (uint32_t)BF_MEM : (uint32_t)BF_SCALAR;
+        if (bk == BK_MEM) return HD_BIN_MEM;
+        if (sub == ALU_POW) return HD_BIN_POW;
+        if (sub == ALU_DIV && bk == BK_TREG) return HD_DIV_T;
+        const uint32_t form = bk == BK_TREG ? f_b(w0) : (uint32_t)BF_SCALAR;
         const bool comm = sub == ALU_ADD || sub == ALU_MUL || sub == ALU_MAX || sub == ALU_MIN;
         const bool rev = !comm && (fl & FL_REV);
         return HD_BIN + 10 * sub + form + (rev ? (uint32_t)BF_REV : 0u);
       }
       case OP_RED: return HD_RED + 3 * sub + a;
-      case OP_RED_FIN: return HD_RED_FIN + sub;
+      case OP_REDX: return HD_REDX + 3 * sub + a;
       case OP_ALL: return HD_ALL + 3 * sub + a;
       case OP_ALL_FIN: return HD_ALL_FIN + sub;
       case OP_BCAST: return HD_BCAST + d;

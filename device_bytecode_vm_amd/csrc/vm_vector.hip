@@ -115,6 +115,20 @@ __device__ __forceinline__ Rsrc tile_rsrc(const ArgD& a, const Tile& tl, int es)
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(a.p + ob), 0, n, RSRC_W3);
 }
 
+// The same descriptor as four scalar words (for inline assembly).
+__device__ __forceinline__ u4 tile_rsrc_words(const ArgD& a, const Tile& tl, int es) {
+  const int64_t ob = (tl.r0 * a.sr + tl.c0 * (int64_t)a.sc) * es;
+  const int64_t left = (int64_t)a.extent - ob;
+  const int n = left <= 0 ? 0 : (left >= (int64_t)EXTENT_CAP ? (int)(EXTENT_CAP - 1) : (int)left);
+  const uint64_t base = (uint64_t)(uintptr_t)(a.p + ob);
+  u4 r;
+  r.x = (uint32_t)base;
+  r.y = (uint32_t)(base >> 32) & 0xffffu;  // stride 0
+  r.z = (uint32_t)n;
+  r.w = (uint32_t)RSRC_W3;
+  return r;
+}
+
 __device__ __forceinline__ Tile make_tile(const Geo& G, uint32_t id) {
   Tile tl;
   const uint32_t ir = id / (uint32_t)G.nc;
@@ -246,6 +260,21 @@ __device__ __forceinline__ void fill(Ch& d, float v) {
   for (int j = 0; j < NV_MAX; ++j) d.c[j] = (V8)v;
 }
 
+// Make every value of a freshly loaded tile register available before the
+// routine returns (an empty use of each value).  A routine that left loads
+// outstanding into its destination would make the compiler wait, in every
+// routine after the dispatch merge, for all outstanding vector memory.
+__device__ __forceinline__ void settle(Ch& d) {
+#pragma unroll
+  for (int j = 0; j < NV_MAX; ++j) {
+    float x0 = d.c[j][0], x1 = d.c[j][1], x2 = d.c[j][2], x3 = d.c[j][3];
+    float x4 = d.c[j][4], x5 = d.c[j][5], x6 = d.c[j][6], x7 = d.c[j][7];
+    asm volatile("" : "+v"(x0), "+v"(x1), "+v"(x2), "+v"(x3), "+v"(x4), "+v"(x5), "+v"(x6), "+v"(x7));
+    d.c[j][0] = x0; d.c[j][1] = x1; d.c[j][2] = x2; d.c[j][3] = x3;
+    d.c[j][4] = x4; d.c[j][5] = x5; d.c[j][6] = x6; d.c[j][7] = x7;
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Load / Store (Table 1: Load/ViewLoad/Store/ViewStore)
 // ---------------------------------------------------------------------------
@@ -367,6 +396,12 @@ __device__ __forceinline__ void store_dir(const Ch& s, const ArgD& a, const Geo&
   }
 }
 
+__device__ __forceinline__ void store_any(const Ch& v, const ArgD& a, const Geo& G, const Tile& tl, const Lane& L) {
+  if (a.dt == DT_BF16) store_dir<DT_BF16>(v, a, G, tl, L);
+  else if (a.dt == DT_F32) store_dir<DT_F32>(v, a, G, tl, L);
+  else store_dir<DT_U8>(v, a, G, tl, L);
+}
+
 // ---------------------------------------------------------------------------
 // LDS staging: next-tile prefetch (direct-to-LDS buffer loads) and
 // LDS-resident tile-invariant operands.  A lane reads back only bytes that
@@ -375,14 +410,21 @@ __device__ __forceinline__ void store_dir(const Ch& s, const ArgD& a, const Geo&
 // barrier is needed, only waits on the lane's own outstanding operations.
 // ---------------------------------------------------------------------------
 // Issue the loads of tile nt of operand a into a prefetch slot (nv chunks).
+// The direct-to-LDS loads are issued from inline assembly, so the compiler
+// does not track them: it would otherwise make every later LDS read, and every
+// instruction after a merge of paths, wait for all outstanding vector memory
+// (the prefetch included).  Their completion is awaited explicitly, with the
+// counted wait before the slot is read; waits the compiler places for its own
+// loads stay correct (extra outstanding operations only make them stricter).
 template <uint32_t DT>
 __device__ __forceinline__ void pf_issue(char* slot, const ArgD& a, const Geo& G, const Tile& nt, const Lane& L) {
   constexpr int ES = esize_c<DT>();
   constexpr int HV = DT == DT_F32 ? 2 : 1;
-  const Rsrc rs = tile_rsrc(a, nt, ES);
+  const u4 rs = tile_rsrc_words(a, nt, ES);
   const bool rok = L.row < nt.tre;
   const int roff = L.row * (int)a.sr;
   const int wave = L.tid >> 6;
+  const uint32_t base = (uint32_t)(uintptr_t)(lds_void*)slot;
 #pragma unroll
   for (int j = 0; j < NV_MAX; ++j) {
     if (j < G.nv) {
@@ -390,8 +432,12 @@ __device__ __forceinline__ void pf_issue(char* slot, const ArgD& a, const Geo& G
       const int off = lane_off(rok & (ct < nt.tce), (roff + ct) * ES);
 #pragma unroll
       for (int h = 0; h < HV; ++h) {
-        lds_void* dst = (lds_void*)(slot + ((j * HV + h) * T_LANES + wave * 64) * 16);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst, 16, off == OOB ? OOB : off + 16 * h, 0, 0, 0);
+        const uint32_t dst = __builtin_amdgcn_readfirstlane(base + (uint32_t)(((j * HV + h) * T_LANES + wave * 64) * 16));
+        const int o = off == OOB ? OOB : off + 16 * h;
+        asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                     :
+                     : "s"(dst), "v"(o), "s"(rs)
+                     : "memory", "m0");
       }
     }
   }
@@ -620,6 +666,42 @@ __device__ __forceinline__ float lane_partial(const Ch& c, const Geo& G, const T
   return acc;
 }
 
+// ACC <- ACC pow B (B pow ACC if rev), one chunk at a time: the chunk in
+// position 0 is computed and both registers rotate by one chunk, NV_MAX times,
+// so the long pow expansion appears once per routine instead of once per
+// element.
+__device__ __forceinline__ void pow_rot(Ch& acc, Ch& b, bool rev) {
+#pragma nounroll
+  for (int k = 0; k < NV_MAX; ++k) {
+    const V8 x = acc.c[0], y = b.c[0];
+    V8 r;
+#pragma unroll
+    for (int i = 0; i < VEC; ++i) {
+      const float u = rev ? y[i] : x[i], v = rev ? x[i] : y[i];
+      r[i] = powf(u, v);
+    }
+#pragma unroll
+    for (int j = 0; j < NV_MAX - 1; ++j) {
+      acc.c[j] = acc.c[j + 1];
+      b.c[j] = b.c[j + 1];
+    }
+    acc.c[NV_MAX - 1] = r;
+    b.c[NV_MAX - 1] = y;
+  }
+}
+
+// One row-register instruction (RBIN / RUN).
+__device__ __forceinline__ void row_op(RowRegs& rw, uint32_t w0, uint32_t w1) {
+  if (f_op(w0) == HD_RBIN) {
+    const float x = rget(rw, f_a(w0));
+    const float y = f_bk(w0) == BK_RREG ? rget(rw, f_b(w0)) : __uint_as_float(w1);
+    const bool rev = (f_flags(w0) & FL_REV) != 0;
+    rset(rw, f_dst(w0), rev ? alu_rt(f_sub(w0), y, x) : alu_rt(f_sub(w0), x, y));
+  } else {
+    rset(rw, f_dst(w0), una_rt(f_sub(w0), rget(rw, f_a(w0))));
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Register file of one lane: three tile registers and four row registers.
 // ---------------------------------------------------------------------------
@@ -729,16 +811,10 @@ dvm_vm_vector(const Program prog) {
     S.tile = tile;
 
 #define ARG read_arg(W, w1)
-#define CASE_LD(d)                                                                           \
-  case HD_LD_F32 + d: load_dir<DT_F32>(treg<d>(R), ARG, G, tl, L); break;                     \
-  case HD_LD_BF16 + d: load_dir<DT_BF16>(treg<d>(R), ARG, G, tl, L); break;                   \
-  case HD_LD_U8 + d: load_dir<DT_U8>(treg<d>(R), ARG, G, tl, L); break;                       \
-  case HD_LD_PF16 + d: read_pf<DT_BF16>(treg<d>(R), w0, vmc_load(w0), ARG, G, tl, L, S); break; \
-  case HD_LD_PF32 + d: read_pf<DT_F32>(treg<d>(R), w0, vmc_load(w0), ARG, G, tl, L, S); break;  \
-  case HD_LD_INV + d: read_inv(treg<d>(R), w0, G, L, S); break;                               \
-  case HD_ST_F32 + d: store_dir<DT_F32>(treg<d>(R), ARG, G, tl, L); break;                    \
-  case HD_ST_BF16 + d: store_dir<DT_BF16>(treg<d>(R), ARG, G, tl, L); break;                  \
-  case HD_ST_U8 + d: store_dir<DT_U8>(treg<d>(R), ARG, G, tl, L); break;                      \
+#define CASE_LD(d)                                                                                          \
+  case HD_LD_PF16 + d: read_pf<DT_BF16>(treg<d>(R), w0, vmc_load(w0), ARG, G, tl, L, S); settle(treg<d>(R)); break; \
+  case HD_LD_PF32 + d: read_pf<DT_F32>(treg<d>(R), w0, vmc_load(w0), ARG, G, tl, L, S); settle(treg<d>(R)); break;  \
+  case HD_LD_INV + d: read_inv(treg<d>(R), w0, G, L, S); settle(treg<d>(R)); break;                          \
   case HD_BCAST + d: fill(treg<d>(R), rget(R.rw, f_a(w0))); break;
 #define CASE_COPY(d, a) \
   case HD_COPY + 3 * d + a: treg<d>(R) = treg<a>(R); break;
@@ -747,34 +823,63 @@ dvm_vm_vector(const Program prog) {
   case HD_BIN + 10 * k + 5 * rev + BF_T0: bin_cc<k, rev>(R.t0, R.t0); break;                              \
   case HD_BIN + 10 * k + 5 * rev + BF_T1: bin_cc<k, rev>(R.t0, R.t1); break;                              \
   case HD_BIN + 10 * k + 5 * rev + BF_T2: bin_cc<k, rev>(R.t0, R.t2); break;                              \
-  case HD_BIN + 10 * k + 5 * rev + BF_SCALAR: bin_cs<k, rev>(R.t0, SCALAR_B); break;                      \
-  case HD_BIN + 10 * k + 5 * rev + BF_MEM: {                                                              \
-    Ch m;                                                                                                  \
-    read_mem(m, w0, vmc_bin(w0), ARG, G, tl, L, S);                                                        \
-    bin_cc<k, rev>(R.t0, m);                                                                               \
-    break;                                                                                                 \
-  }
+  case HD_BIN + 10 * k + 5 * rev + BF_SCALAR: bin_cs<k, rev>(R.t0, SCALAR_B); break;
 #define CASE_BIN_COMM(k) CASE_BIN_DIR(k, false)
 #define CASE_BIN_NC(k) CASE_BIN_DIR(k, false) CASE_BIN_DIR(k, true)
 #define CASE_RED(kind, a)                                                                  \
-  case HD_RED + 3 * kind + a: {                                                            \
-    float acc = lane_partial<kind>(treg<a>(R), G, tl, L);                                  \
-    acc = group_reduce<kind>(acc, gs);                                                     \
-    /* after the 64-lane all-reduce every lane of a wave holds the same value, */          \
-    /* so every lane stores it (no lane-dependent branch in the loop) */                   \
-    if (G.g <= 64) rset(R.rw, f_dst(w0), acc);                                             \
-    else s_red[f_b(w0)][wave] = acc;                                                       \
-    break;                                                                                 \
-  }                                                                                        \
+  case HD_RED + 3 * kind + a:                                                              \
+  case HD_REDX + 3 * kind + a:                                                             \
   case HD_ALL + 3 * kind + a: {                                                            \
+    const uint32_t h = f_op(w0);                                                           \
     float acc = lane_partial<kind>(treg<a>(R), G, tl, L);                                  \
-    acc = group_reduce<kind>(acc, 64);                                                     \
-    s_red[f_b(w0)][wave] = acc;                                                            \
+    if (h == HD_RED + 3 * kind + a) {                                                      \
+      /* rows inside one wave: the group all-reduce leaves the row's value */              \
+      rset(R.rw, f_dst(w0), group_reduce<kind>(acc, gs));                                  \
+    } else {                                                                               \
+      /* per-wave partial into LDS (after the 64-lane all-reduce every lane */             \
+      /* holds it, so every lane stores it: no lane-dependent branch) */                   \
+      acc = group_reduce<kind>(acc, 64);                                                   \
+      float* buf = s_red[f_b(w0)];                                                         \
+      buf[wave] = acc;                                                                     \
+      if (h == HD_REDX + 3 * kind + a) {                                                   \
+        /* rows across waves: barrier, then combine the row's partials */                  \
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");                                 \
+        __builtin_amdgcn_s_barrier();                                                      \
+        asm volatile("" ::: "memory");                                                     \
+        const int nw = G.g >> 6;                                                           \
+        const float* rb = buf + L.row * nw;                                                \
+        float r = rb[0];                                                                   \
+        for (int k = 1; k < nw; ++k) r = comb<kind>(r, rb[k]);                             \
+        rset(R.rw, f_dst(w0), r);                                                          \
+      }                                                                                    \
+    }                                                                                      \
     break;                                                                                 \
   }
 
     switch (f_op(w0)) {
       CASE_LD(0) CASE_LD(1) CASE_LD(2)
+      case HD_LD_DIR + 0:
+      case HD_LD_DIR + 1:
+      case HD_LD_DIR + 2: {
+        Ch m;
+        load_any(m, ARG, G, tl, L);
+        settle(m);
+        if (f_dst(w0) == 0) R.t0 = m;
+        else if (f_dst(w0) == 1) R.t1 = m;
+        else R.t2 = m;
+        break;
+      }
+      case HD_ST_BF16: store_dir<DT_BF16>(R.t0, ARG, G, tl, L); break;
+      case HD_ST_F32: store_dir<DT_F32>(R.t0, ARG, G, tl, L); break;
+      case HD_ST_DIR + 0: store_any(R.t0, ARG, G, tl, L); break;
+      case HD_ST_DIR + 1:
+      case HD_ST_DIR + 2: {
+        Ch m;
+        if (f_a(w0) == 1) m = R.t1;
+        else m = R.t2;
+        store_any(m, ARG, G, tl, L);
+        break;
+      }
       CASE_COPY(0, 1) CASE_COPY(0, 2) CASE_COPY(1, 0) CASE_COPY(1, 2) CASE_COPY(2, 0) CASE_COPY(2, 1)
       case HD_UN + UN_SQRT: un_c<UN_SQRT>(R.t0); break;
       case HD_UN + UN_ABS: un_c<UN_ABS>(R.t0); break;
@@ -786,20 +891,45 @@ dvm_vm_vector(const Program prog) {
       case HD_UN + UN_NEG: un_c<UN_NEG>(R.t0); break;
       case HD_UN + UN_RECIP: un_c<UN_RECIP>(R.t0); break;
       case HD_UN + UN_TOBF16: un_c<UN_TOBF16>(R.t0); break;
-      CASE_BIN_COMM(ALU_ADD) CASE_BIN_NC(ALU_SUB) CASE_BIN_COMM(ALU_MUL) CASE_BIN_NC(ALU_DIV)
-      CASE_BIN_COMM(ALU_MAX) CASE_BIN_COMM(ALU_MIN) CASE_BIN_NC(ALU_POW)
-      CASE_RED(RK_SUM, 0) CASE_RED(RK_SUM, 1) CASE_RED(RK_SUM, 2)
-      CASE_RED(RK_MAX, 0) CASE_RED(RK_MAX, 1) CASE_RED(RK_MAX, 2)
-      case HD_RED_FIN + RK_SUM:
-      case HD_RED_FIN + RK_MAX: {
-        const uint32_t kind = f_op(w0) - HD_RED_FIN;
-        const int nw = G.g >> 6;
-        const float* buf = s_red[f_b(w0)] + L.row * nw;
-        float acc = buf[0];
-        for (int k = 1; k < nw; ++k) acc = kind == RK_SUM ? acc + buf[k] : comb<RK_MAX>(acc, buf[k]);
-        rset(R.rw, f_dst(w0), acc);
+      CASE_BIN_COMM(ALU_ADD) CASE_BIN_NC(ALU_SUB) CASE_BIN_COMM(ALU_MUL)
+      case HD_BIN + 10 * ALU_DIV + BF_SCALAR: bin_cs<ALU_DIV, false>(R.t0, SCALAR_B); break;
+      case HD_BIN + 10 * ALU_DIV + BF_REV + BF_SCALAR: bin_cs<ALU_DIV, true>(R.t0, SCALAR_B); break;
+      case HD_DIV_T: {
+        Ch b;
+        if (f_b(w0) == 0) b = R.t0;
+        else if (f_b(w0) == 1) b = R.t1;
+        else b = R.t2;
+        if (f_flags(w0) & FL_REV) bin_cc<ALU_DIV, true>(R.t0, b);
+        else bin_cc<ALU_DIV, false>(R.t0, b);
         break;
       }
+      CASE_BIN_COMM(ALU_MAX) CASE_BIN_COMM(ALU_MIN)
+      case HD_BIN_POW: {
+        Ch b;
+        if (f_bk(w0) != BK_TREG) fill(b, SCALAR_B);
+        else if (f_b(w0) == 0) b = R.t0;
+        else if (f_b(w0) == 1) b = R.t1;
+        else b = R.t2;
+        pow_rot(R.t0, b, (f_flags(w0) & FL_REV) != 0);
+        break;
+      }
+      case HD_BIN_MEM: {
+        Ch m;
+        read_mem(m, w0, vmc_bin(w0), ARG, G, tl, L, S);
+        const bool rev = (f_flags(w0) & FL_REV) != 0;
+        switch (f_sub(w0)) {
+          case ALU_ADD: bin_cc<ALU_ADD, false>(R.t0, m); break;
+          case ALU_SUB: if (rev) bin_cc<ALU_SUB, true>(R.t0, m); else bin_cc<ALU_SUB, false>(R.t0, m); break;
+          case ALU_MUL: bin_cc<ALU_MUL, false>(R.t0, m); break;
+          case ALU_DIV: if (rev) bin_cc<ALU_DIV, true>(R.t0, m); else bin_cc<ALU_DIV, false>(R.t0, m); break;
+          case ALU_MAX: bin_cc<ALU_MAX, false>(R.t0, m); break;
+          case ALU_MIN: bin_cc<ALU_MIN, false>(R.t0, m); break;
+          default: pow_rot(R.t0, m, rev); break;
+        }
+        break;
+      }
+      CASE_RED(RK_SUM, 0) CASE_RED(RK_SUM, 1) CASE_RED(RK_SUM, 2)
+      CASE_RED(RK_MAX, 0) CASE_RED(RK_MAX, 1) CASE_RED(RK_MAX, 2)
       case HD_ALL_FIN + RK_SUM:
       case HD_ALL_FIN + RK_MAX: {
         // every lane combines the per-wave partials (LDS broadcast reads);
@@ -823,16 +953,26 @@ dvm_vm_vector(const Program prog) {
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
         break;
-      case HD_RBIN: {
-        const float x = rget(R.rw, f_a(w0));
-        const float y = f_bk(w0) == BK_RREG ? rget(R.rw, f_b(w0)) : __uint_as_float(w1);
-        const bool rev = (f_flags(w0) & FL_REV) != 0;
-        rset(R.rw, f_dst(w0), rev ? alu_rt(f_sub(w0), y, x) : alu_rt(f_sub(w0), x, y));
+      case HD_RBIN:
+      case HD_RUN: {
+        // a run of row-register instructions executes here, without going
+        // back through the dispatch
+        uint32_t a0 = w0, a1 = w1;
+        while (true) {
+          row_op(R.rw, a0, a1);
+          if (pc >= pc_end) break;
+          const uint32_t h = f_op(nw0);
+          if (h != HD_RBIN && h != HD_RUN) break;
+          a0 = nw0;
+          a1 = nw1;
+          pc += 2;
+          uint32_t pcr = pc;
+          asm volatile("" : "+s"(pcr) : "s"(a0), "s"(a1));
+          nw0 = W[pcr];
+          nw1 = W[pcr + 1];
+        }
         break;
       }
-      case HD_RUN:
-        rset(R.rw, f_dst(w0), una_rt(f_sub(w0), rget(R.rw, f_a(w0))));
-        break;
       case HD_LD_ROW: {
         const ArgD a = ARG;
         const int es = esize(a.dt);
@@ -842,6 +982,7 @@ dvm_vm_vector(const Program prog) {
         if (a.dt == DT_BF16) v = bf2f(__builtin_amdgcn_raw_buffer_load_b16(rs, off, 0, 0));
         else if (a.dt == DT_F32) v = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, 0));
         else v = (float)__builtin_amdgcn_raw_buffer_load_b8(rs, off, 0, 0);
+        asm volatile("" : "+v"(v));  // settled before the routine returns
         rset(R.rw, f_dst(w0), v);
         break;
       }
