@@ -37,7 +37,83 @@ def parse():
     ap.add_argument("--config", default="layernorm", choices=["layernorm", "sqrt_add", "ifelse", "stream"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="run only a plain device copy of known size (counter calibration)")
+    ap.add_argument("--traffic-from", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
+                    help="derive the VM kernel's HBM bytes per launch from rocprofv3 counter files and store them")
     return ap.parse_args()
+
+
+COPY_BYTES = 512 << 20          # bytes read (and written) by the calibration copy
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_dvm_vm_vector_layernorm_stream.txt")
+KERNEL_SOURCES = [os.path.join(ROOT, "device_bytecode_vm_amd", "csrc", f) for f in ("vm_vector.hip", "bytecode.h")]
+
+
+def kernel_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic():
+    """HBM bytes per launch measured by counters for the current kernel
+    sources, or None when the kernel changed since they were taken."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            rec = json.loads(fh.read().split("\n", 1)[1])
+    except (OSError, ValueError, IndexError):
+        return None
+    if rec.get("kernel_sha256_16") != kernel_hash():
+        return None
+    return rec
+
+
+def counter_per_dispatch(path, kernel):
+    import csv
+    per = {}
+    with open(path) as fh:
+        for r in csv.DictReader(fh):
+            if kernel in r["Kernel_Name"]:
+                per[r["Dispatch_Id"]] = per.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
+    return per
+
+
+def traffic_from(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv):
+    """FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the VM kernel over one
+    bench step, each scaled by what the counter reads for a plain copy of
+    COPY_BYTES; averaged per launch."""
+    cf = counter_per_dispatch(copy_fetch_csv, "")
+    cw = counter_per_dispatch(copy_write_csv, "")
+    big_f = max(cf.values())          # the calibration copy is the largest dispatch
+    big_w = max(cw.values())
+    f_scale = COPY_BYTES / (big_f * 1024.0)
+    w_scale = COPY_BYTES / (big_w * 1024.0)
+    vf = counter_per_dispatch(fetch_csv, "dvm_vm_vector")
+    vw = counter_per_dispatch(write_csv, "dvm_vm_vector")
+    n = min(len(vf), len(vw))
+    fetch = sum(vf.values()) / len(vf) * 1024.0 * f_scale
+    write = sum(vw.values()) / len(vw) * 1024.0 * w_scale
+    rec = {"kernel_sha256_16": kernel_hash(), "dispatches": n, "fetch_bytes_per_launch": round(fetch),
+           "write_bytes_per_launch": round(write), "traffic_bytes_per_launch": round(fetch + write),
+           "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4)}
+    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
+    with open(TRAFFIC_FILE, "w") as fh:
+        fh.write("# HBM traffic of dvm_vm_vector on the LayerNorm stream (see the counter commands in "
+                 "profiles/README.md)\n" + json.dumps(rec) + "\n")
+    return rec
+
+
+def calibrate_copy():
+    import torch
+    a = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration_copy_bytes": COPY_BYTES}), flush=True)
 
 
 def pctl(xs, q):
@@ -122,6 +198,8 @@ def layernorm_bench(args):
     kern_ms /= reps
     kern_gbs = step_bytes / (kern_ms.sum() * 1e-3) / 1e9
     hdr = progs[int(np.argmax([r for r, _ in shapes]))].header()
+    tr = stored_traffic()
+    traffic = tr["traffic_bytes_per_launch"] if tr else None
 
     out = {
         "metric": METRIC, "value": round(e2e_gbs, 2), "unit": "GB/s", "n_gpus": 1,
@@ -137,7 +215,7 @@ def layernorm_bench(args):
         "device_only_gbs": round(kern_gbs, 2),
         "graphs_per_step": graphs / args.steps,
         "roofline": {"bound": "hbm", "achieved": round(kern_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(kern_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(kern_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "kernel": "dvm_vm_vector", "launches_per_step": len(progs),
                      "avg_launch_us": round(float(kern_ms.mean()) * 1e3, 3),
                      "bytes_per_launch_avg": round(step_bytes / len(progs), 1)},
@@ -228,6 +306,9 @@ def sqrt_add_bench(args):
 
 def main():
     args = parse()
+    if args.traffic_from:
+        print(json.dumps(traffic_from(*args.traffic_from)))
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this build has no "
               "multi-GPU path", file=sys.stderr)
@@ -236,6 +317,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
     if args.config == "layernorm":
         out = layernorm_bench(args)
     elif args.config == "sqrt_add":
