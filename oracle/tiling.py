@@ -40,6 +40,15 @@ design notes):
   to tile and inv_bytes those of tile-invariant operands, loaded once per
   workgroup.  The least cost wins; ties go to the earlier candidate (the
   larger tile).
+* MATMUL graphs (a matmul [M, K] x [K, N] first, elementwise ops on its [M, N]
+  output after it): K is pinned (every tile runs the whole K loop) and the
+  output is tiled tm x tn from the MIX kernel's tile menu MM_TILES, largest
+  first (the matrix-core analogue of hardware_align_div: tm and tn are
+  multiples of 32, the MFMA block).  Cost per candidate, in the same ticks:
+  ceil(n_tiles / G) * (A + var_bytes + flop_ticks) with var_bytes the A and B
+  panels one tile reads (tm K + K tn elements) plus its epilogue operand and
+  output bytes, and flop_ticks = 2 tm tn K / 312.5 (bf16 matrix peak 2.5
+  PFLOP/s shared by G workgroups is 312.5 flop per tick each).
 * Header and ranges: block_dim = n_tiles; body_tile = ceil(block_dim / min(G,
   block_dim)); grid = ceil(block_dim / body_tile); workgroup b owns tiles
   [b body_tile, min((b + 1) body_tile, block_dim)).  Tile id -> (ir, ic) is
@@ -58,6 +67,10 @@ A_TICKS = 7812
 BYTE_TICKS = 1
 
 ELEMWISE, ROWREDUCE, ALLREDUCE, MATMUL = "elemwise", "rowreduce", "allreduce", "matmul"
+
+# (tm, tn) output tiles the MIX kernel implements, largest first
+MM_TILES = [(128, 128)]
+MM_FLOP_PER_TICK = 312.5
 
 
 def cdiv(a: int, b: int) -> int:
@@ -252,6 +265,38 @@ def plan(template: str, R: int, C: int, ops) -> Plan:
         raise ValueError("no feasible tile")
     _, p.tr, p.tc, p.P, p.g, p.nv = best
     p.n_r, p.n_c = cdiv(R, p.tr), cdiv(C, p.tc)
+    p.block_dim = p.n_r * p.n_c
+    p.body_tile, p.grid = header(p.block_dim)
+    return p
+
+
+def plan_matmul(M: int, N: int, K: int, a_esize: int, b_esize: int, epi_ops) -> Plan:
+    """Tile choice and header for a MATMUL graph over its [M, N] output.
+    ``epi_ops``: the epilogue's global operands (inputs and stored outputs) in
+    the [M, N] space, as Operand(esize, s_r, s_c)."""
+    p = Plan(MATMUL, M, N, 0, [])
+    if M == 0 or N == 0:
+        return p
+    p.path = list(MM_TILES)
+    best = None
+    for (tm, tn) in p.path:
+        n_tiles = cdiv(M, tm) * cdiv(N, tn)
+        var_b = tm * K * a_esize + K * tn * b_esize
+        inv_b = 0
+        for o in epi_ops:
+            touched = (tm if o.s_r != 0 else 1) * (tn if o.s_c != 0 else 1) * o.esize
+            invariant = (o.s_r == 0 or cdiv(M, tm) == 1) and (o.s_c == 0 or cdiv(N, tn) == 1)
+            if invariant:
+                inv_b += touched
+            else:
+                var_b += touched
+        flop_ticks = cdiv(2 * tm * tn * K * 2, int(2 * MM_FLOP_PER_TICK))
+        c = cdiv(n_tiles, G_WG) * (A_TICKS + BYTE_TICKS * var_b + flop_ticks) + BYTE_TICKS * inv_b
+        p.costs.append(c)
+        if best is None or c < best[0]:
+            best = (c, tm, tn)
+    _, p.tr, p.tc = best
+    p.n_r, p.n_c = cdiv(M, p.tr), cdiv(N, p.tc)
     p.block_dim = p.n_r * p.n_c
     p.body_tile, p.grid = header(p.block_dim)
     return p

@@ -138,3 +138,25 @@ def test_header_formula_cases():
     assert TL.header(513) == (2, 257)
     assert TL.header(1024) == (2, 512)
     assert TL.header(1025) == (3, 342)
+
+
+def test_matmul_plan_by_hand():
+    bias = Operand(4, 0, 1)
+    y = Operand(2, 17408, 1)
+    # one row of A: 136 column tiles of 128, one round
+    p = TL.plan_matmul(1, 17408, 5120, 2, 2, [bias, y])
+    assert (p.tr, p.tc, p.n_r, p.n_c, p.block_dim, p.body_tile, p.grid) == (128, 128, 1, 136, 136, 1, 136)
+    # tile bytes: A panel 128*5120*2, B panel 5120*128*2, y tile 128*128*2, bias 128*4 (it varies
+    # across the 136 column tiles); flops 2*128*128*5120 at 312.5 per tick, rounded up
+    assert p.costs == [7812 + 1310720 + 1310720 + 32768 + 512 + 536871]
+    # 8192 rows: 64 x 136 = 8704 tiles, 17 per workgroup, 512 workgroups
+    p = TL.plan_matmul(8192, 17408, 5120, 2, 2, [bias, y])
+    assert (p.n_r, p.n_c, p.block_dim, p.body_tile, p.grid) == (64, 136, 8704, 17, 512)
+    assert p.costs == [17 * (7812 + 1310720 + 1310720 + 32768 + 512 + 536871)]
+    # ragged edges: 300 x 1000 -> 3 x 8 tiles, the last row and column tiles partial
+    p = TL.plan_matmul(300, 1000, 64, 2, 2, [])
+    assert (p.n_r, p.n_c, p.block_dim) == (3, 8, 24)
+    tiles, wgs = TL.element_tile_map(p)
+    assert tiles[299, 999] == 23 and tiles[256, 0] == 16 and tiles[0, 896] == 7
+    assert (tiles >= 0).all()
+    assert TL.plan_matmul(0, 5, 8, 2, 2, []).block_dim == 0
