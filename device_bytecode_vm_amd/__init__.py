@@ -111,6 +111,7 @@ class Program:
     def __init__(self, h, ctx):
         self.h = h
         self.ctx = ctx
+        self._keep = []   # tensors the program reads or writes (kept alive with it)
 
     def header(self) -> dict:
         hd = L.DvmHeader()
@@ -169,6 +170,10 @@ class Graph:
         self.h = h
         self._in_group = False
         self.flushes = 0
+        # Tensors the buffered ops borrow: held until the graph is launched (or
+        # handed to a Program), so the caching allocator cannot reuse their
+        # memory while the device still has to read or write it.
+        self._keep = []
 
     def close(self):
         if self.h:
@@ -183,6 +188,7 @@ class Graph:
 
     # -- values ----------------------------------------------------------
     def input(self, t) -> Value:
+        self._keep.append(t)
         d = to_c(t)
         v = C.c_int64()
         check(lib.dvm_graph_input(self.h, C.byref(d), C.byref(v)))
@@ -220,6 +226,7 @@ class Graph:
                 dtype = "u8" if name == "isfinite" else next(x.dtype for x in ins if isinstance(x, Value))
             d = to_c(None, dtype, shape)
         else:
+            self._keep.append(out)
             d = to_c(out)
             shape = tuple(d.shape[i] for i in range(d.ndim))
             dtype = L.DTYPE_NAMES[d.dtype]
@@ -250,15 +257,23 @@ class Graph:
         """Encode the buffered graph (no launch); returns a Program or None."""
         q = C.c_void_p()
         check(lib.dvm_flush(self.h, C.byref(q)))
-        return Program(q, self.ctx) if q.value else None
+        keep, self._keep = self._keep, []
+        if not q.value:
+            return None
+        prog = Program(q, self.ctx)
+        prog._keep = keep
+        return prog
 
     def flush_launch(self) -> bool:
         fl = C.c_int32(0)
         check(lib.dvm_graph_flush_launch(self.h, C.byref(fl)))
+        # launched on the graph's stream: later reuse of the memory is ordered after it
+        self._keep = []
         return bool(fl.value)
 
     def sync(self):
         check(lib.dvm_sync(self.h))
+        self._keep = []
 
     def flush_log(self) -> list:
         """[(n_ops, reason name)] for every graph flushed so far."""

@@ -10,6 +10,7 @@ forms are used:
 * RMSNorm: y = x / sqrt(sum(x^2)/H + eps) * w.
 * Row softmax: e = exp(x - max(x)); y = e / sum(e).
 * SiLU(z) = z / (1 + exp(-z)); SwiGLU = SiLU(g) * u.
+* MatMul + bias + SiLU: a matmul first, its epilogue after it (one MIX graph).
 
 Reductions and normalisations compute in fp32; the result is rounded to the
 output's dtype.
@@ -97,5 +98,21 @@ def swiglu(g, gate, up, out=None, dtype=None):
         d = g.op("add", e, 1.0); t.append(d)
         s = g.op("div", gf, d); t.append(s)
         y = g.op("mul", s, up, out=out, dtype=dtype or gate.dtype, live=out is not None)
+        g.release(*t)
+    return y
+
+
+def matmul_bias_silu(g, a, b, bias, out=None, dtype=None):
+    """y = SiLU(a @ b + bias): a matmul (fp32 result, never rounded) and its
+    elementwise epilogue, one MIX graph."""
+    t = []
+    with g.group():
+        z = g.op("matmul", a, b, dtype="f32"); t.append(z)
+        zb = g.op("add", z, bias); t.append(zb)
+        n = g.op("mul", zb, -1.0); t.append(n)
+        e = g.op("exp", n); t.append(e)
+        d = g.op("add", e, 1.0); t.append(d)
+        s = g.op("div", zb, d); t.append(s)
+        y = g.op("cast", s, out=out, dtype=dtype or "bf16", live=out is not None)
         g.release(*t)
     return y

@@ -81,7 +81,17 @@ enum Hdr : int {
   H_INV_OFF1 = 31,
   H_INV_SHARED0 = 32,// 1: invariant slot 0 / 1 is one row shared by all row groups
   H_INV_SHARED1 = 33,
+  H_MM_K = 34,       // MIX: contraction length K
+  H_MM_A = 35,       // MIX: arg index of A [M, K] (bf16, unit stride along K)
+  H_MM_B = 36,       // MIX: arg index of B [K, N] (bf16, unit stride along N)
 };
+
+// MIX kernel geometry: output tile MM_TM x MM_TN per 256-lane workgroup, K in
+// stages of MM_KT through two LDS buffers for A and two for B.
+constexpr int MM_TM = 128;
+constexpr int MM_TN = 128;
+constexpr int MM_KT = 64;
+constexpr uint32_t MM_LDS_BYTES = 2u * (MM_TM + MM_TN) * MM_KT * 2u;
 
 // LDS staging (per workgroup, dynamic):
 //  * prefetch slot: NV chunks x T lanes x 16 bytes x (element size / 2)

@@ -23,6 +23,7 @@
 using namespace dvmbc;
 
 extern "C" hipError_t dvm_launch_vector_kernel(const Program* p, unsigned grid, hipStream_t s);
+extern "C" hipError_t dvm_launch_mix_kernel(const Program* p, unsigned grid, hipStream_t s);
 
 namespace {
 
@@ -266,6 +267,33 @@ void header(int64_t block_dim, int64_t* body_tile, int64_t* grid) {
   const int64_t gp = std::min(G, block_dim);
   *body_tile = cdiv(block_dim, gp);
   *grid = cdiv(block_dim, *body_tile);
+}
+
+// MATMUL graphs: K pinned, output tiles from the MIX kernel's menu (one entry,
+// MM_TM x MM_TN), cost with the matrix-core time of the tile (flops at 312.5
+// per tick per workgroup) added to the bytes; same header rule.
+bool plan_matmul(int64_t M, int64_t N, int64_t K, int64_t a_es, int64_t b_es, const std::vector<Operand>& ops,
+                 Plan* p) {
+  *p = Plan();
+  p->tmpl = TM_MATMUL;
+  p->R = M;
+  p->C = N;
+  if (M == 0 || N == 0) return true;
+  const int64_t tm = MM_TM, tn = MM_TN;
+  p->tr = tm;
+  p->tc = tn;
+  p->g = 0;
+  p->nv = 0;
+  p->P = 0;
+  p->n_r = cdiv(M, tm);
+  p->n_c = cdiv(N, tn);
+  p->block_dim = p->n_r * p->n_c;
+  (void)K;
+  (void)a_es;
+  (void)b_es;
+  (void)ops;
+  header(p->block_dim, &p->body_tile, &p->grid);
+  return true;
 }
 
 bool plan(int tmpl, int64_t R, int64_t C, const std::vector<Operand>& ops, Plan* p) {
@@ -1259,6 +1287,101 @@ struct Encoder {
     for (size_t q = 0; q < v.size(); q += 2) v[q] = (v[q] & ~0xffu) | handler_of(v[q], v[q + 1]);
   }
 
+  // MATMUL template: the matmul's A and B are args 0 and 1; the body is the
+  // epilogue on the [M, N] result, which starts in the accumulator.
+  dvm_status run_matmul() {
+    const OpRec& mm = ops[0];
+    const dvm_tensor& A = g->vals[mm.in[0]].t;
+    const dvm_tensor& B = g->vals[mm.in[1]].t;
+    const int64_t M = A.shape[0], K = A.shape[1], N = B.shape[1];
+    std::vector<int64_t> stored;
+    for (auto& o : ops) {
+      const Val& v = g->vals[o.out];
+      if (v.live || !v.released) {
+        if (!v.t.data) return fail(DVM_ERR_INVALID_ARG, "a value without storage escapes its graph");
+        stored.push_back(o.out);
+        store_it[o.out] = 1;
+      }
+    }
+    const Shape sd = ck.dominant();
+    std::vector<int64_t> operands = ck.ext_operands();
+    for (int64_t s : stored) operands.push_back(s);
+    int64_t R, C;
+    std::vector<tiling::Operand> tops;
+    std::vector<std::pair<int64_t, int64_t>> st;
+    if (!ck.tile_operands(sd, operands, &R, &C, &tops, &st))
+      return fail(DVM_ERR_SHAPE, "epilogue operands do not collapse to [M, N]");
+    if (!tiling::plan_matmul(M, N, K, 2, 2, tops, &plan)) return fail(DVM_ERR_RESOURCE, "no feasible tile");
+    // 32-bit lane offsets inside a tile and inside the A and B panels
+    for (size_t q = 0; q < operands.size(); ++q) {
+      const int64_t span = ((plan.tr - 1) * std::llabs(st[q].first) + plan.tc * std::llabs(st[q].second) + 1) *
+                           tops[q].esize;
+      if (span >= (int64_t)EXTENT_CAP) return fail(DVM_ERR_RESOURCE, "tile spans >= 2^31 bytes");
+    }
+    if ((MM_TM * A.stride[0] + K) * 2 >= (int64_t)EXTENT_CAP || (K * B.stride[0] + MM_TN) * 2 >= (int64_t)EXTENT_CAP)
+      return fail(DVM_ERR_RESOURCE, "matmul panel spans >= 2^31 bytes");
+    if (operands.size() + 2 > (size_t)MAX_ARGS) return fail(DVM_ERR_RESOURCE, "too many operands");
+    for (int k = 0; k < 2; ++k) {
+      const dvm_tensor& t = k == 0 ? A : B;
+      uint32_t* a = W + ARG_BASE + k * ARG_WORDS;
+      const uint64_t p = (uint64_t)(uintptr_t)t.data;
+      a[A_PTR_LO] = (uint32_t)p;
+      a[A_PTR_HI] = (uint32_t)(p >> 32);
+      a[A_DTYPE] = (uint32_t)t.dtype;
+      a[A_FLAGS] = AF_VEC;
+      a[A_SR_LO] = (uint32_t)(uint64_t)t.stride[0];
+      a[A_SR_HI] = (uint32_t)((uint64_t)t.stride[0] >> 32);
+      a[A_SC] = (uint32_t)t.stride[1];
+      a[A_EXTENT] = (uint32_t)std::min<int64_t>(extent_bytes(t), EXTENT_CAP);
+    }
+    n_args = 2;
+    for (size_t q = 0; q < operands.size(); ++q) add_arg(operands[q], st[q].first, st[q].second);
+    cls.clear();
+    ck.classes(&cls);
+    cls[mm.out] = 1;
+    bind_t(0, mm.out);
+    if (store_it[mm.out]) emit(enc0(OP_STORE, 0, 0, 0, 0, 0, 0), (uint32_t)arg_of[mm.out]);
+    if (last_use[mm.out] <= 0) unbind_t(0);
+    for (size_t i = 1; i < ops.size(); ++i) {
+      if (cls[ops[i].out] != 1) return fail(DVM_ERR_UNSUPPORTED, "matmul epilogue op %zu is not elementwise", i);
+      dvm_status e = tile_op((int)i);
+      if (e != DVM_OK) return e;
+    }
+    const uint32_t instr_base = ARG_BASE + (uint32_t)n_args * ARG_WORDS;
+    if (instr_base + body.size() + PAD_WORDS > (size_t)MAX_WORDS) return fail(DVM_ERR_RESOURCE, "program too large");
+    std::copy(body.begin(), body.end(), W + instr_base);
+    W[H_MAGIC] = MAGIC;
+    W[H_VERSION] = VERSION;
+    W[H_KTYPE] = KT_MIX;
+    W[H_TEMPLATE] = TM_MATMUL;
+    W[H_BLOCK_DIM] = (uint32_t)plan.block_dim;
+    W[H_BODY_TILE] = (uint32_t)plan.body_tile;
+    W[H_GRID] = (uint32_t)plan.grid;
+    W[H_TR] = (uint32_t)plan.tr;
+    W[H_TC] = (uint32_t)plan.tc;
+    W[H_G] = 1;
+    W[H_NC] = (uint32_t)(plan.n_c ? plan.n_c : 1);
+    W[H_NARGS] = (uint32_t)n_args;
+    W[H_PRO_BEGIN] = W[H_PRO_END] = W[H_BODY_BEGIN] = instr_base;
+    W[H_BODY_END] = instr_base + (uint32_t)body.size();
+    W[H_R_LO] = (uint32_t)(uint64_t)M;
+    W[H_R_HI] = (uint32_t)((uint64_t)M >> 32);
+    W[H_C_LO] = (uint32_t)(uint64_t)N;
+    W[H_C_HI] = (uint32_t)((uint64_t)N >> 32);
+    W[H_MM_K] = (uint32_t)K;
+    W[H_MM_A] = 0;
+    W[H_MM_B] = 1;
+    W[H_LDS_BYTES] = MM_LDS_BYTES;
+    W[H_N_INSTR] = (uint32_t)(body.size() / 2);
+    prog->n_words = instr_base + (uint32_t)body.size();
+    prog->n_instr = (uint32_t)(body.size() / 2);
+    prog->R = M;
+    prog->C = N;
+    prog->pad = 0;
+    prog->grid_launch = (uint32_t)plan.grid;
+    return DVM_OK;
+  }
+
   dvm_status run() {
     std::memset(W, 0, sizeof(uint32_t) * HDR_WORDS);
     const size_t n = g->vals.size();
@@ -1278,7 +1401,7 @@ struct Encoder {
         n_uses[ops[i].in[q]]++;
       }
     const int tm = ck.tmpl();
-    if (tm == TM_MATMUL) return fail(DVM_ERR_UNSUPPORTED, "matmul graphs are not supported by this build");
+    if (tm == TM_MATMUL) return run_matmul();
     // stored outputs: live, or not released by flush time
     std::vector<int64_t> stored;
     for (auto& o : ops) {
@@ -1428,7 +1551,8 @@ dvm_status encode_buffer(dvm_graph* g, dvm_program** out) {
 dvm_status launch(dvm_context* ctx, const dvm_program* p, hipStream_t s) {
   if (!ctx || ctx->device < 0) return fail(DVM_ERR_DEVICE, "encode-only context cannot launch");
   if (p->grid_launch == 0) return DVM_OK;
-  hipError_t e = dvm_launch_vector_kernel(&p->prog, p->grid_launch, s);
+  hipError_t e = p->prog.w[H_KTYPE] == KT_MIX ? dvm_launch_mix_kernel(&p->prog, p->grid_launch, s)
+                                              : dvm_launch_vector_kernel(&p->prog, p->grid_launch, s);
   if (e != hipSuccess) return fail(DVM_ERR_DEVICE, "launch failed: %s", hipGetErrorString(e));
   return DVM_OK;
 }
@@ -1668,7 +1792,17 @@ dvm_status dvm_graph_add_op(dvm_graph* g, int32_t op, const dvm_value* in, int32
   // F1: the op set and dtypes the VM runs
   if (op == DVM_OP_ISFINITE && out->dtype != DVM_U8) return fail(DVM_ERR_UNSUPPORTED, "isfinite writes u8");
   if (op != DVM_OP_ISFINITE && out->dtype == DVM_U8) return fail(DVM_ERR_UNSUPPORTED, "u8 output");
-  if (op == DVM_OP_MATMUL) return fail(DVM_ERR_UNSUPPORTED, "matmul is not supported by this build");
+  if (op == DVM_OP_MATMUL) {
+    // the MIX kernel's operand forms: bf16 A [M, K] and B [K, N], unit stride
+    // along K (A) and N (B), 16-byte aligned rows, K and N multiples of 8
+    const dvm_tensor& A = g->vals[r.in[0]].t;
+    const dvm_tensor& B = g->vals[r.in[1]].t;
+    const bool ok = A.dtype == DVM_BF16 && B.dtype == DVM_BF16 && A.stride[1] == 1 && B.stride[1] == 1 &&
+                    A.shape[1] % 8 == 0 && B.shape[1] % 8 == 0 && A.stride[0] % 8 == 0 && B.stride[0] % 8 == 0 &&
+                    (uintptr_t)A.data % 16 == 0 && (uintptr_t)B.data % 16 == 0 &&
+                    (out->dtype == DVM_F32 || out->dtype == DVM_BF16);
+    if (!ok) return fail(DVM_ERR_UNSUPPORTED, "matmul operands outside the MIX kernel's forms");
+  }
   const int64_t slot = new_slot(g);
   Val& v = g->vals[slot];
   v.kind = VK_OP;

@@ -640,30 +640,39 @@ __device__ __forceinline__ float group_reduce(float acc, int gs) {
   return acc;
 }
 
-// Partial over this lane's valid elements.  Full tiles mask whole chunks; only
-// ragged tiles mask element by element.
+// Partial over this lane's valid elements, combined as a balanced pairwise
+// tree (a fixed order, so results are deterministic; short dependency
+// chains).  Full tiles mask whole chunks; only ragged tiles mask element by
+// element.
+template <uint32_t KIND>
+__device__ __forceinline__ float tree8(V8 v) {
+  const float a = comb<KIND>(v[0], v[1]), b = comb<KIND>(v[2], v[3]);
+  const float c = comb<KIND>(v[4], v[5]), d = comb<KIND>(v[6], v[7]);
+  return comb<KIND>(comb<KIND>(a, b), comb<KIND>(c, d));
+}
+
 template <uint32_t KIND>
 __device__ __forceinline__ float lane_partial(const Ch& c, const Geo& G, const Tile& tl, const Lane& L) {
   const float id = KIND == RK_SUM ? 0.f : -__builtin_huge_valf();
-  float acc = id;
+  float p[NV_MAX];
   if (tile_full(tl)) {
 #pragma unroll
     for (int j = 0; j < NV_MAX; ++j) {
-      float s = c.c[j][0];
-#pragma unroll
-      for (int i = 1; i < VEC; ++i) s = comb<KIND>(s, c.c[j][i]);
       const int ct = (j * G.g + L.lane) * VEC;
-      acc = comb<KIND>(acc, lane_sel(L.rok & (ct < tl.tce), s, id));
+      p[j] = lane_sel(L.rok & (ct < tl.tce), tree8<KIND>(c.c[j]), id);
     }
   } else {
 #pragma unroll
     for (int j = 0; j < NV_MAX; ++j) {
       const int ct = (j * G.g + L.lane) * VEC;
+      V8 m;
 #pragma unroll
-      for (int i = 0; i < VEC; ++i) acc = comb<KIND>(acc, lane_sel(L.rok & (ct + i < tl.tce), c.c[j][i], id));
+      for (int i = 0; i < VEC; ++i) m[i] = lane_sel(L.rok & (ct + i < tl.tce), c.c[j][i], id);
+      p[j] = tree8<KIND>(m);
     }
   }
-  return acc;
+  static_assert(NV_MAX == 5, "chunk combine order below assumes five chunks");
+  return comb<KIND>(comb<KIND>(comb<KIND>(p[0], p[1]), comb<KIND>(p[2], p[3])), p[4]);
 }
 
 // ACC <- ACC pow B (B pow ACC if rev), one chunk at a time: the chunk in

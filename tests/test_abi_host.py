@@ -322,3 +322,39 @@ def test_single_hip_runtime_in_process():
                        cwd=os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
     assert r.returncode == 0, r.stderr
     assert r.stdout.split("\n")[0] == "1", r.stdout
+
+
+def test_matmul_header_matches_oracle_plan(dvm_lib):
+    """Encode-only MatMul+bias+SiLU graphs: the MIX header equals the oracle's
+    MATMUL plan (tile, tile counts, body_tile, grid)."""
+    from device_bytecode_vm_amd import composites as CP
+    from oracle import tiling as TL
+    dvm = dvm_lib
+    ctx = dvm.Context(-1)
+    for (m, k, n) in [(1, 5120, 17408), (300, 136, 1000), (8192, 5120, 17408), (129, 64, 8)]:
+        g = dvm.Graph(ctx)
+        a = g.input(dvm.TensorDesc(0x10000000, "bf16", (m, k)))
+        b = g.input(dvm.TensorDesc(0x20000000, "bf16", (k, n)))
+        bias = g.input(dvm.TensorDesc(0x30000000, "f32", (n,)))
+        CP.matmul_bias_silu(g, a, b, bias, out=dvm.TensorDesc(0x40000000, "bf16", (m, n)))
+        h = g.flush().header()
+        p = TL.plan_matmul(m, n, k, 2, 2, [TL.Operand(4, 0, 1), TL.Operand(2, n, 1)])
+        assert h["kernel_type"] == 1 and h["tmpl"] == 3
+        assert (h["tr"], h["tc"], h["block_dim"], h["body_tile"], h["grid"]) == \
+            (p.tr, p.tc, p.block_dim, p.body_tile, p.grid), (m, k, n)
+
+
+def test_matmul_unsupported_forms(dvm_lib):
+    """Operands outside the MIX kernel's forms are refused at add time."""
+    dvm = dvm_lib
+    ctx = dvm.Context(-1)
+    cases = [((4, 7), (7, 16), "bf16"),      # K not a multiple of 8
+             ((4, 16), (16, 12), "bf16"),    # N not a multiple of 8
+             ((4, 16), (16, 16), "f32")]     # fp32 inputs
+    for sa, sb, dt in cases:
+        g = dvm.Graph(ctx)
+        a = g.input(dvm.TensorDesc(0x10000000, dt, sa))
+        b = g.input(dvm.TensorDesc(0x20000000, dt, sb))
+        with pytest.raises(dvm.DvmError) as ei:
+            g.op("matmul", a, b, dtype="f32")
+        assert ei.value.status == 2, (sa, sb, dt)
