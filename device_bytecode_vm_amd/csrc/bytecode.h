@@ -86,12 +86,11 @@ enum Hdr : int {
   H_MM_B = 36,       // MIX: arg index of B [K, N] (bf16, unit stride along N)
 };
 
-// MIX kernel geometry: output tile MM_TM x MM_TN per 256-lane workgroup, K in
-// stages of MM_KT through two LDS buffers for A and two for B.
-constexpr int MM_TM = 128;
-constexpr int MM_TN = 128;
+// MIX kernel geometry: the output tile (header H_TR x H_TC) is one of the MIX
+// kernel's variants (128 x 128 per 256-lane workgroup, two workgroups per
+// compute unit); K runs in stages of MM_KT through two LDS buffers for A and
+// two for B (2 (tm + tn) MM_KT bf16 values of LDS).
 constexpr int MM_KT = 64;
-constexpr uint32_t MM_LDS_BYTES = 2u * (MM_TM + MM_TN) * MM_KT * 2u;
 
 // LDS staging (per workgroup, dynamic):
 //  * prefetch slot: NV chunks x T lanes x 16 bytes x (element size / 2)

@@ -258,20 +258,27 @@ int64_t cost(int64_t R, int64_t C, int64_t tr, int64_t tc, const std::vector<Ope
   return cdiv(n_tiles, G) * (A + BT * var_b) + BT * inv_b;
 }
 
-void header(int64_t block_dim, int64_t* body_tile, int64_t* grid) {
+void header(int64_t block_dim, int64_t* body_tile, int64_t* grid, int64_t g_res = G) {
   if (block_dim == 0) {
     *body_tile = 0;
     *grid = 0;
     return;
   }
-  const int64_t gp = std::min(G, block_dim);
+  const int64_t gp = std::min(g_res, block_dim);
   *body_tile = cdiv(block_dim, gp);
   *grid = cdiv(block_dim, *body_tile);
 }
 
-// MATMUL graphs: K pinned, output tiles from the MIX kernel's menu (one entry,
-// MM_TM x MM_TN), cost with the matrix-core time of the tile (flops at 312.5
-// per tick per workgroup) added to the bytes; same header rule.
+// MATMUL graphs: K pinned; output tiles from the MIX kernel's variants (tm,
+// tn, resident workgroups G_e), largest first.  With G_e workgroups sharing
+// 8 TB/s and 2.5 PFLOP/s, a byte costs G_e / 512 ticks and a flop G_e / 160000:
+// cost = ceil(n_tiles / G_e) (A + ceil(var_bytes G_e / 512) + ceil(2 tm tn K G_e / 160000))
+//        + ceil(inv_bytes G_e / 512); least cost wins, ties to the earlier entry.
+struct MmTile {
+  int64_t tm, tn, g;
+};
+constexpr MmTile MM_TILES[] = {{128, 128, 512}};
+
 bool plan_matmul(int64_t M, int64_t N, int64_t K, int64_t a_es, int64_t b_es, const std::vector<Operand>& ops,
                  Plan* p) {
   *p = Plan();
@@ -279,20 +286,30 @@ bool plan_matmul(int64_t M, int64_t N, int64_t K, int64_t a_es, int64_t b_es, co
   p->R = M;
   p->C = N;
   if (M == 0 || N == 0) return true;
-  const int64_t tm = MM_TM, tn = MM_TN;
-  p->tr = tm;
-  p->tc = tn;
-  p->g = 0;
-  p->nv = 0;
-  p->P = 0;
-  p->n_r = cdiv(M, tm);
-  p->n_c = cdiv(N, tn);
+  bool found = false;
+  int64_t best = 0, best_g = G;
+  for (const MmTile& t : MM_TILES) {
+    const int64_t n_r = cdiv(M, t.tm), n_c = cdiv(N, t.tn);
+    int64_t var_b = t.tm * K * a_es + K * t.tn * b_es, inv_b = 0;
+    for (auto& o : ops) {
+      const int64_t touched = (o.sr != 0 ? t.tm : 1) * (o.sc != 0 ? t.tn : 1) * o.esize;
+      const bool invariant = (o.sr == 0 || n_r == 1) && (o.sc == 0 || n_c == 1);
+      (invariant ? inv_b : var_b) += touched;
+    }
+    const int64_t per_tile = A + cdiv(var_b * t.g, 512) + cdiv(2 * t.tm * t.tn * K * t.g, 160000);
+    const int64_t c = cdiv(n_r * n_c, t.g) * per_tile + cdiv(inv_b * t.g, 512);
+    if (!found || c < best) {
+      found = true;
+      best = c;
+      best_g = t.g;
+      p->tr = t.tm;
+      p->tc = t.tn;
+    }
+  }
+  p->n_r = cdiv(M, p->tr);
+  p->n_c = cdiv(N, p->tc);
   p->block_dim = p->n_r * p->n_c;
-  (void)K;
-  (void)a_es;
-  (void)b_es;
-  (void)ops;
-  header(p->block_dim, &p->body_tile, &p->grid);
+  header(p->block_dim, &p->body_tile, &p->grid, best_g);
   return true;
 }
 
@@ -1318,7 +1335,7 @@ struct Encoder {
                            tops[q].esize;
       if (span >= (int64_t)EXTENT_CAP) return fail(DVM_ERR_RESOURCE, "tile spans >= 2^31 bytes");
     }
-    if ((MM_TM * A.stride[0] + K) * 2 >= (int64_t)EXTENT_CAP || (K * B.stride[0] + MM_TN) * 2 >= (int64_t)EXTENT_CAP)
+    if ((plan.tr * A.stride[0] + K) * 2 >= (int64_t)EXTENT_CAP || (K * B.stride[0] + plan.tc) * 2 >= (int64_t)EXTENT_CAP)
       return fail(DVM_ERR_RESOURCE, "matmul panel spans >= 2^31 bytes");
     if (operands.size() + 2 > (size_t)MAX_ARGS) return fail(DVM_ERR_RESOURCE, "too many operands");
     for (int k = 0; k < 2; ++k) {
@@ -1371,7 +1388,7 @@ struct Encoder {
     W[H_MM_K] = (uint32_t)K;
     W[H_MM_A] = 0;
     W[H_MM_B] = 1;
-    W[H_LDS_BYTES] = MM_LDS_BYTES;
+    W[H_LDS_BYTES] = (uint32_t)(2 * (plan.tr + plan.tc) * MM_KT * 2);
     W[H_N_INSTR] = (uint32_t)(body.size() / 2);
     prog->n_words = instr_base + (uint32_t)body.size();
     prog->n_instr = (uint32_t)(body.size() / 2);

@@ -8,8 +8,9 @@
 // block_dim / body_tile, section 4.4); per tile it runs the whole K loop on
 // the matrix cores and then interprets the program body on the accumulator.
 //
-// Tile: 128 x 128 outputs per 256-lane workgroup; the four waves own 64 x 64
-// quadrants, each as 2 x 2 blocks of v_mfma_f32_32x32x16_bf16.  Lane layout of
+// Tile: 128 x 128 outputs per 256-lane workgroup (the body is templated on
+// the wave tile); the four waves own 64 x 64 quadrants, each as 2 x 2 blocks
+// of v_mfma_f32_32x32x16_bf16.  Lane layout of
 // that instruction (checked on the device): lane l supplies A[l % 32][8 (l /
 // 32) + j] and B[8 (l / 32) + j][l % 32] for j < 8, and holds
 // D[8 (i / 4) + 4 (l / 32) + i % 4][l % 32] in accumulator register i.
@@ -44,9 +45,7 @@ typedef const __attribute__((address_space(4))) uint32_t KW;
 
 constexpr int OOB = 0x7fffffff;
 constexpr int RSRC_W3 = 0x00020000;
-constexpr int MT = MM_TM, NT = MM_TN, KT = MM_KT;
-constexpr int A_STAGE = MT * KT * 2;  // bytes of one A stage (16 KB)
-constexpr int B_STAGE = NT * KT * 2;  // bytes of one B stage (16 KB)
+constexpr int KT = MM_KT;
 constexpr int ROW_BYTES = KT * 2;     // one LDS row: 64 bf16 = 8 chunks of 16 bytes
 
 struct ArgD {
@@ -119,49 +118,79 @@ __device__ __forceinline__ float una_rt(uint32_t f, float x) {
 }
 
 // ---------------------------------------------------------------------------
-// K loop
+// K loop (templated on the wave tile: BM x BN blocks of 32 x 32 per wave,
+// four waves in a 2 x 2 arrangement)
 // ---------------------------------------------------------------------------
 // Byte offset of chunk kc (8 bf16 along K) of LDS row r, swizzled by s.
 __device__ __forceinline__ int chunk_at(int r, int kc, int s) { return r * ROW_BYTES + ((kc ^ (s & 7)) << 4); }
 __device__ __forceinline__ int a_swz(int row) { return row; }
 __device__ __forceinline__ int b_swz(int n) { return n ^ (n >> 3); }
 
-struct Stage {
-  u4 a[4], b[4];  // this lane's 16-byte chunks of the next A and B stages
+template <int BM, int BN>
+struct Cfg {
+  static constexpr int TM = 64 * BM, TN = 64 * BN;       // workgroup tile
+  static constexpr int QA = TM * (KT / 8) / 256;         // A chunks per lane per stage
+  static constexpr int QB = TN * (KT / 8) / 256;         // B chunks per lane per stage
+  static constexpr int NCH = TN / 8;                     // B chunks per K row
+  static constexpr int A_BYTES = TM * ROW_BYTES;         // one A stage
+  static constexpr int B_BYTES = TN * ROW_BYTES;         // one B stage
+  static constexpr int LDS = 2 * (A_BYTES + B_BYTES);
 };
 
-// Global loads of the stage at k0: A chunks (row, kc) and B chunks (k row,
-// 8 columns), 4 of each per lane; masked chunks read as zeros.
-__device__ __forceinline__ void load_stage(Stage& st, const Rsrc& ra, const Rsrc& rb, const ArgD& A, const ArgD& B,
-                                           int64_t m0, int64_t n0, int k0, int64_t M, int64_t N, int K, int tid) {
+// A chunk c of a stage: row c / 8, K chunk c % 8 (eight lanes read one row's
+// 128 contiguous bytes).  B chunk c: eight K rows by eight column chunks per
+// wave (each column chunk's 128-byte line is still read whole by one wave),
+// so the transposed 16-bit LDS writes of a wave spread over all banks.
+__device__ __forceinline__ void a_chunk(int c, int& row, int& kc) {
+  row = c >> 3;
+  kc = c & 7;
+}
+template <int NCH>
+__device__ __forceinline__ void b_chunk(int c, int& kr, int& nc) {
+  const int rest = c >> 6;
+  kr = ((rest & 7) << 3) | (c & 7);
+  nc = ((rest >> 3) << 3) | ((c >> 3) & 7);
+}
+
+template <class CF>
+struct Stage {
+  u4 a[CF::QA], b[CF::QB];  // this lane's 16-byte chunks of the next A and B stages
+};
+
+// Global loads of the stage at k0; masked chunks read as zeros.
+template <class CF>
+__device__ __forceinline__ void load_stage(Stage<CF>& st, const Rsrc& ra, const Rsrc& rb, const ArgD& A,
+                                           const ArgD& B, int64_t m0, int64_t n0, int k0, int64_t M, int64_t N,
+                                           int K, int tid) {
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int c = tid + 256 * q;
-    const int row = c >> 3, kc = c & 7;
+  for (int q = 0; q < CF::QA; ++q) {
+    int row, kc;
+    a_chunk(tid + 256 * q, row, kc);
     const bool ok = (m0 + row < M) & (k0 + kc * 8 < K);
     st.a[q] = __builtin_amdgcn_raw_buffer_load_b128(ra, lane_off(ok, (row * (int)A.sr + k0 + kc * 8) * 2), 0, 0);
   }
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int c = tid + 256 * q;
-    const int kr = c >> 4, nc = c & 15;
+  for (int q = 0; q < CF::QB; ++q) {
+    int kr, nc;
+    b_chunk<CF::NCH>(tid + 256 * q, kr, nc);
     const bool ok = (k0 + kr < K) & (n0 + nc * 8 < N);
     st.b[q] = __builtin_amdgcn_raw_buffer_load_b128(rb, lane_off(ok, ((k0 + kr) * (int)B.sr + nc * 8) * 2), 0, 0);
   }
 }
 
 // Writes of the loaded stage to LDS buffers (A row-major, B transposed).
-__device__ __forceinline__ void write_stage(const Stage& st, char* abuf, char* bbuf, int tid) {
+template <class CF>
+__device__ __forceinline__ void write_stage(const Stage<CF>& st, char* abuf, char* bbuf, int tid) {
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int c = tid + 256 * q;
-    const int row = c >> 3, kc = c & 7;
+  for (int q = 0; q < CF::QA; ++q) {
+    int row, kc;
+    a_chunk(tid + 256 * q, row, kc);
     *(u4*)(abuf + chunk_at(row, kc, a_swz(row))) = st.a[q];
   }
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int c = tid + 256 * q;
-    const int kr = c >> 4, nc = c & 15;
+  for (int q = 0; q < CF::QB; ++q) {
+    int kr, nc;
+    b_chunk<CF::NCH>(tid + 256 * q, kr, nc);
     const u4 v = st.b[q];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
@@ -177,22 +206,28 @@ __device__ __forceinline__ bf8 read_frag(const char* buf, int r, int kc, int s) 
   return *(const bf8*)(buf + chunk_at(r, kc, s));
 }
 
-// One stage of 64 K values on this wave's 2 x 2 blocks.
-__device__ __forceinline__ void mma_stage(f16v& c00, f16v& c01, f16v& c10, f16v& c11, const char* abuf,
-                                          const char* bbuf, int wm, int wn, int lane) {
-  const int ra0 = wm * 64 + (lane & 31), ra1 = ra0 + 32;
-  const int nb0 = wn * 64 + (lane & 31), nb1 = nb0 + 32;
+// One stage of KT values of K on this wave's BM x BN blocks.
+template <int BM, int BN>
+__device__ __forceinline__ void mma_stage(f16v (&c)[BM][BN], const char* abuf, const char* bbuf, int wm, int wn,
+                                          int lane) {
 #pragma unroll
   for (int kk = 0; kk < KT / 16; ++kk) {
     const int kc = kk * 2 + (lane >> 5);
-    const bf8 a0 = read_frag(abuf, ra0, kc, a_swz(ra0));
-    const bf8 a1 = read_frag(abuf, ra1, kc, a_swz(ra1));
-    const bf8 b0 = read_frag(bbuf, nb0, kc, b_swz(nb0));
-    const bf8 b1 = read_frag(bbuf, nb1, kc, b_swz(nb1));
-    c00 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b0, c00, 0, 0, 0);
-    c01 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b1, c01, 0, 0, 0);
-    c10 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b0, c10, 0, 0, 0);
-    c11 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b1, c11, 0, 0, 0);
+    bf8 a[BM], b[BN];
+#pragma unroll
+    for (int i = 0; i < BM; ++i) {
+      const int r = wm * 32 * BM + i * 32 + (lane & 31);
+      a[i] = read_frag(abuf, r, kc, a_swz(r));
+    }
+#pragma unroll
+    for (int j = 0; j < BN; ++j) {
+      const int n = wn * 32 * BN + j * 32 + (lane & 31);
+      b[j] = read_frag(bbuf, n, kc, b_swz(n));
+    }
+#pragma unroll
+    for (int i = 0; i < BM; ++i)
+#pragma unroll
+      for (int j = 0; j < BN; ++j) c[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], c[i][j], 0, 0, 0);
   }
 }
 
@@ -339,12 +374,9 @@ __device__ __forceinline__ void to16(T16& d, const f16v& c) {
   for (int i = 0; i < 16; ++i) d.v[i] = c[i];
 }
 
-}  // namespace
-
-extern "C" __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
-dvm_vm_mix(const Program prog) {
-  extern __shared__ __attribute__((aligned(16))) char lds[];
-  (void)prog;
+template <int BM, int BN>
+__device__ __forceinline__ void mix_body(char* lds) {
+  using CF = Cfg<BM, BN>;
   KW* W = (KW*)__builtin_amdgcn_kernarg_segment_ptr();
   const uint32_t block_dim = W[H_BLOCK_DIM];
   const uint32_t body_tile = W[H_BODY_TILE];
@@ -359,6 +391,8 @@ dvm_vm_mix(const Program prog) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int wm = wave >> 1, wn = wave & 1;
   const int n_stage = (K + KT - 1) / KT;
+  char* const abuf0 = lds;
+  char* const bbuf0 = lds + 2 * CF::A_BYTES;
 
   const uint32_t t_begin = blockIdx.x * body_tile;
   uint32_t t_end = t_begin + body_tile;
@@ -366,52 +400,69 @@ dvm_vm_mix(const Program prog) {
 
   for (uint32_t tile = t_begin; tile < t_end; ++tile) {
     const uint32_t ir = tile / nct, ic = tile - ir * nct;
-    const int64_t m0 = (int64_t)ir * MT, n0 = (int64_t)ic * NT;
+    const int64_t m0 = (int64_t)ir * CF::TM, n0 = (int64_t)ic * CF::TN;
     const Rsrc ra = rsrc_at(A, m0 * A.sr * 2);
     const Rsrc rb = rsrc_at(Bm, n0 * 2);
-    f16v c00 = {}, c01 = {}, c10 = {}, c11 = {};
+    f16v c[BM][BN];
+#pragma unroll
+    for (int i = 0; i < BM; ++i)
+#pragma unroll
+      for (int j = 0; j < BN; ++j) c[i][j] = (f16v)0.f;
 
-    Stage st;
-    load_stage(st, ra, rb, A, Bm, m0, n0, 0, M, N, K, tid);
-    write_stage(st, lds, lds + 2 * A_STAGE, tid);
+    Stage<CF> st;
+    load_stage<CF>(st, ra, rb, A, Bm, m0, n0, 0, M, N, K, tid);
+    write_stage<CF>(st, abuf0, bbuf0, tid);
     lds_barrier();
     for (int s = 0; s < n_stage; ++s) {
       const int cur = s & 1;
       const bool more = s + 1 < n_stage;
-      if (more) load_stage(st, ra, rb, A, Bm, m0, n0, (s + 1) * KT, M, N, K, tid);
-      mma_stage(c00, c01, c10, c11, lds + cur * A_STAGE, lds + 2 * A_STAGE + cur * B_STAGE, wm, wn, lane);
-      if (more) write_stage(st, lds + (cur ^ 1) * A_STAGE, lds + 2 * A_STAGE + (cur ^ 1) * B_STAGE, tid);
+      if (more) load_stage<CF>(st, ra, rb, A, Bm, m0, n0, (s + 1) * KT, M, N, K, tid);
+      mma_stage<BM, BN>(c, abuf0 + cur * CF::A_BYTES, bbuf0 + cur * CF::B_BYTES, wm, wn, lane);
+      if (more) write_stage<CF>(st, abuf0 + (cur ^ 1) * CF::A_BYTES, bbuf0 + (cur ^ 1) * CF::B_BYTES, tid);
       lds_barrier();
     }
 
-    // epilogue per 32 x 32 block; the blocks rotate through c00
+    // epilogue per 32 x 32 block
     Blk B;
     B.M = M;
     B.N = N;
     B.lane = lane;
 #pragma nounroll
-    for (int blk = 0; blk < 4; ++blk) {
-      B.mb = m0 + wm * 64 + (blk >> 1) * 32;
-      B.nb = n0 + wn * 64 + (blk & 1) * 32;
+    for (int blk = 0; blk < BM * BN; ++blk) {
+      const int bi = blk / BN, bj = blk % BN;
+      B.mb = m0 + wm * 32 * BM + bi * 32;
+      B.nb = n0 + wn * 32 * BN + bj * 32;
       T16 t0;
-      to16(t0, c00);
+#pragma unroll
+      for (int q = 0; q < BM * BN; ++q)
+        if (q == blk) to16(t0, c[q / BN][q % BN]);
       run_epilogue(W, t0, B);
-      c00 = c01;
-      c01 = c10;
-      c10 = c11;
     }
   }
 }
 
-// Host-side launch of the MIX VM kernel with one program as its argument.
+}  // namespace
+
+// 128 x 128 tiles, two workgroups per compute unit.
+extern "C" __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+dvm_vm_mix_128(const Program prog) {
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  (void)prog;
+  mix_body<2, 2>(lds);
+}
+
+// Host-side launch of the MIX VM kernel matching the program's tile.
 extern "C" hipError_t dvm_launch_mix_kernel(const Program* p, unsigned grid, hipStream_t s) {
+  using Small = Cfg<2, 2>;
+  constexpr int lds_small = Small::LDS;
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)dvm_vm_mix, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       (int)MM_LDS_BYTES);
+    hipError_t e = hipFuncSetAttribute((const void*)dvm_vm_mix_128, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       lds_small);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  hipLaunchKernelGGL(dvm_vm_mix, dim3(grid), dim3(256), MM_LDS_BYTES, s, *p);
+  if (p->w[H_TR] != (uint32_t)Small::TM || p->w[H_TC] != (uint32_t)Small::TN) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(dvm_vm_mix_128, dim3(grid), dim3(256), lds_small, s, *p);
   return hipGetLastError();
 }

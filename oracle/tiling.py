@@ -42,13 +42,16 @@ design notes):
   larger tile).
 * MATMUL graphs (a matmul [M, K] x [K, N] first, elementwise ops on its [M, N]
   output after it): K is pinned (every tile runs the whole K loop) and the
-  output is tiled tm x tn from the MIX kernel's tile menu MM_TILES, largest
-  first (the matrix-core analogue of hardware_align_div: tm and tn are
-  multiples of 32, the MFMA block).  Cost per candidate, in the same ticks:
-  ceil(n_tiles / G) * (A + var_bytes + flop_ticks) with var_bytes the A and B
-  panels one tile reads (tm K + K tn elements) plus its epilogue operand and
-  output bytes, and flop_ticks = 2 tm tn K / 312.5 (bf16 matrix peak 2.5
-  PFLOP/s shared by G workgroups is 312.5 flop per tick each).
+  output is tiled tm x tn from the MIX kernel's tile menu MM_TILES (multiples
+  of 32, the MFMA block; the matrix-core analogue of hardware_align_div).
+  Each entry runs with its own number G_e of resident workgroups, which share
+  the chip's 8 TB/s and 2.5 PFLOP/s (bf16 matrix peak).  In the same ticks a
+  byte costs G_e / 512 and a flop G_e / 160000, so a candidate costs
+  ceil(n_tiles / G_e) * (A + ceil(var_bytes G_e / 512) + ceil(flops G_e / 160000))
+  + ceil(inv_bytes G_e / 512), with var_bytes the A and B panels one tile reads
+  (tm K + K tn elements) plus its varying epilogue operand and output bytes and
+  flops = 2 tm tn K.  The least cost wins; ties go to the earlier (larger)
+  entry.
 * Header and ranges: block_dim = n_tiles; body_tile = ceil(block_dim / min(G,
   block_dim)); grid = ceil(block_dim / body_tile); workgroup b owns tiles
   [b body_tile, min((b + 1) body_tile, block_dim)).  Tile id -> (ir, ic) is
@@ -68,9 +71,8 @@ BYTE_TICKS = 1
 
 ELEMWISE, ROWREDUCE, ALLREDUCE, MATMUL = "elemwise", "rowreduce", "allreduce", "matmul"
 
-# (tm, tn) output tiles the MIX kernel implements, largest first
-MM_TILES = [(128, 128)]
-MM_FLOP_PER_TICK = 312.5
+# (tm, tn, resident workgroups) of the MIX kernel's tile variants, largest first
+MM_TILES = [(128, 128, 512)]
 
 
 def cdiv(a: int, b: int) -> int:
@@ -277,35 +279,35 @@ def plan_matmul(M: int, N: int, K: int, a_esize: int, b_esize: int, epi_ops) -> 
     p = Plan(MATMUL, M, N, 0, [])
     if M == 0 or N == 0:
         return p
-    p.path = list(MM_TILES)
+    p.path = [(tm, tn) for tm, tn, _ in MM_TILES]
     best = None
-    for (tm, tn) in p.path:
-        n_tiles = cdiv(M, tm) * cdiv(N, tn)
+    for (tm, tn, ge) in MM_TILES:
+        n_r, n_c = cdiv(M, tm), cdiv(N, tn)
         var_b = tm * K * a_esize + K * tn * b_esize
         inv_b = 0
         for o in epi_ops:
             touched = (tm if o.s_r != 0 else 1) * (tn if o.s_c != 0 else 1) * o.esize
-            invariant = (o.s_r == 0 or cdiv(M, tm) == 1) and (o.s_c == 0 or cdiv(N, tn) == 1)
+            invariant = (o.s_r == 0 or n_r == 1) and (o.s_c == 0 or n_c == 1)
             if invariant:
                 inv_b += touched
             else:
                 var_b += touched
-        flop_ticks = cdiv(2 * tm * tn * K * 2, int(2 * MM_FLOP_PER_TICK))
-        c = cdiv(n_tiles, G_WG) * (A_TICKS + BYTE_TICKS * var_b + flop_ticks) + BYTE_TICKS * inv_b
+        per_tile = A_TICKS + cdiv(var_b * ge, 512) + cdiv(2 * tm * tn * K * ge, 160000)
+        c = cdiv(n_r * n_c, ge) * per_tile + cdiv(inv_b * ge, 512)
         p.costs.append(c)
         if best is None or c < best[0]:
-            best = (c, tm, tn)
-    _, p.tr, p.tc = best
+            best = (c, tm, tn, ge)
+    _, p.tr, p.tc, ge = best
     p.n_r, p.n_c = cdiv(M, p.tr), cdiv(N, p.tc)
     p.block_dim = p.n_r * p.n_c
-    p.body_tile, p.grid = header(p.block_dim)
+    p.body_tile, p.grid = header(p.block_dim, ge)
     return p
 
 
-def header(block_dim: int):
+def header(block_dim: int, g_res: int = G_WG):
     if block_dim == 0:
         return 0, 0
-    gp = min(G_WG, block_dim)
+    gp = min(g_res, block_dim)
     body_tile = cdiv(block_dim, gp)
     grid = cdiv(block_dim, body_tile)
     return body_tile, grid

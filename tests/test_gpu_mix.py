@@ -42,7 +42,7 @@ def _inputs(seed, m, k, n):
 
 
 @pytest.mark.parametrize("m,k,n", [(1, 64, 128), (37, 72, 200), (128, 128, 128), (300, 136, 1000),
-                                   (129, 5120, 264), (256, 5120, 1024)])
+                                   (129, 5120, 264), (256, 5120, 1024), (4096, 256, 4096), (2100, 136, 4000)])
 def test_matmul_bias_silu(dvm, ctx, m, k, n):
     import torch
     from device_bytecode_vm_amd import composites as CP
@@ -53,7 +53,9 @@ def test_matmul_bias_silu(dvm, ctx, m, k, n):
     CP.matmul_bias_silu(g, g.input(torch_dev(a, "bf16")), g.input(torch_dev(b, "bf16")),
                         g.input(torch_dev(bias, "f32")), out=y)
     hdr = g.flush().header()
-    assert hdr["kernel_type"] == 1 and hdr["block_dim"] == -(-m // 128) * -(-n // 128)
+    from oracle import tiling as TL
+    plan = TL.plan_matmul(m, n, k, 2, 2, [TL.Operand(4, 0, 1), TL.Operand(2, n, 1)])
+    assert hdr["kernel_type"] == 1 and (hdr["tr"], hdr["block_dim"]) == (plan.tr, plan.block_dim)
     g2 = dvm.Graph(ctx)
     CP.matmul_bias_silu(g2, g2.input(torch_dev(a, "bf16")), g2.input(torch_dev(b, "bf16")),
                         g2.input(torch_dev(bias, "f32")), out=y)

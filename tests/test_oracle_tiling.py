@@ -143,19 +143,30 @@ def test_header_formula_cases():
 def test_matmul_plan_by_hand():
     bias = Operand(4, 0, 1)
     y = Operand(2, 17408, 1)
-    # one row of A: 136 column tiles of 128, one round
+    # per-tile ticks of a 128 x 128 tile (G = 512), worked by hand:
+    #   7812 + (128*5120*2 + 5120*128*2 + 128*128*2 + 128*4) + 2*128*128*5120/312.5
+    #   = 7812 + 2654720 + 536871 = 3199403
+    t128 = 3199403
     p = TL.plan_matmul(1, 17408, 5120, 2, 2, [bias, y])
+    assert p.costs == [t128]
     assert (p.tr, p.tc, p.n_r, p.n_c, p.block_dim, p.body_tile, p.grid) == (128, 128, 1, 136, 136, 1, 136)
-    # tile bytes: A panel 128*5120*2, B panel 5120*128*2, y tile 128*128*2, bias 128*4 (it varies
-    # across the 136 column tiles); flops 2*128*128*5120 at 312.5 per tick, rounded up
-    assert p.costs == [7812 + 1310720 + 1310720 + 32768 + 512 + 536871]
-    # 8192 rows: 64 x 136 = 8704 tiles, 17 per workgroup, 512 workgroups
+    # 8192 rows: 64 x 136 = 8704 tiles, 17 rounds of 512, 17 per workgroup
     p = TL.plan_matmul(8192, 17408, 5120, 2, 2, [bias, y])
+    assert p.costs == [17 * t128]
     assert (p.n_r, p.n_c, p.block_dim, p.body_tile, p.grid) == (64, 136, 8704, 17, 512)
-    assert p.costs == [17 * (7812 + 1310720 + 1310720 + 32768 + 512 + 536871)]
+    # the per-entry residency: a variant with G_e = 256 resident workgroups pays
+    # half a tick per byte and G_e / 160000 per flop (worked by hand)
+    saved = TL.MM_TILES
+    try:
+        TL.MM_TILES = [(256, 256, 256)]
+        p = TL.plan_matmul(8192, 17408, 5120, 2, 2, [bias, y])
+        assert p.costs == [9 * (7812 + 2687488 + 1073742)]
+        assert (p.block_dim, p.body_tile, p.grid) == (2176, 9, 242)
+    finally:
+        TL.MM_TILES = saved
     # ragged edges: 300 x 1000 -> 3 x 8 tiles, the last row and column tiles partial
     p = TL.plan_matmul(300, 1000, 64, 2, 2, [])
-    assert (p.n_r, p.n_c, p.block_dim) == (3, 8, 24)
+    assert (p.tr, p.n_r, p.n_c, p.block_dim) == (128, 3, 8, 24)
     tiles, wgs = TL.element_tile_map(p)
     assert tiles[299, 999] == 23 and tiles[256, 0] == 16 and tiles[0, 896] == 7
     assert (tiles >= 0).all()
