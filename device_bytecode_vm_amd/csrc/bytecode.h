@@ -117,7 +117,7 @@ enum ArgW : int { A_PTR_LO = 0, A_PTR_HI = 1, A_DTYPE = 2, A_FLAGS = 3, A_SR_LO 
 constexpr uint32_t EXTENT_CAP = 0x80000000u;
 enum DType : uint32_t { DT_F32 = 0, DT_BF16 = 1, DT_U8 = 2 };
 enum ArgFlag : uint32_t {
-  AF_VEC = 1u,       // every full chunk is 16-byte aligned: 128-bit path
+  AF_VEC = 1u,       // every chunk start is dword aligned: 128-bit path
 };
 
 // Opcodes (bits [7:0] of word 0).

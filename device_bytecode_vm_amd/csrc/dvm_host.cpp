@@ -783,8 +783,10 @@ struct Encoder {
     a[A_PTR_LO] = (uint32_t)p;
     a[A_PTR_HI] = (uint32_t)(p >> 32);
     a[A_DTYPE] = (uint32_t)t.dtype;
+    // vector accesses (8-element chunks) need dword-aligned chunk starts: the
+    // base, every row start and every tile start
     const int64_t es = esize(t.dtype);
-    const int64_t al = std::min<int64_t>(16, 8 * es);
+    const int64_t al = 4;
     bool vec = sc == 1 && (int64_t)(p % al) == 0 && (plan.R <= 1 || ((sr * es) % al + al) % al == 0) &&
                (plan.n_c <= 1 || (plan.tc * es) % al == 0);
     a[A_FLAGS] = vec ? AF_VEC : 0u;

@@ -275,6 +275,75 @@ __device__ __forceinline__ void settle(Ch& d) {
   }
 }
 
+// In a ragged tile (its columns do not end on a chunk boundary) the chunk
+// that holds a row's last column is moved element by element, so that no
+// access reaches past the row's end.  Each lane owns at most one such chunk;
+// its values and column are picked with selects over the chunks (constant
+// register indices: no indexed access into the tile register).
+template <uint32_t DT>
+__device__ __forceinline__ float load_elem(const Rsrc& rs, int off) {
+  if constexpr (DT == DT_F32) return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, 0));
+  else if constexpr (DT == DT_BF16) return bf2f(__builtin_amdgcn_raw_buffer_load_b16(rs, off, 0, 0));
+  else return (float)__builtin_amdgcn_raw_buffer_load_b8(rs, off, 0, 0);
+}
+
+template <uint32_t DT>
+__device__ __forceinline__ void store_elem(const Rsrc& rs, int off, float v) {
+  if constexpr (DT == DT_F32) __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), rs, off, 0, 0);
+  else if constexpr (DT == DT_BF16)
+    __builtin_amdgcn_raw_buffer_store_b16((uint16_t)(f2bf_pack(v, 0.f) & 0xffffu), rs, off, 0, 0);
+  else __builtin_amdgcn_raw_buffer_store_b8((uint8_t)v, rs, off, 0, 0);
+}
+
+// column of this lane's row-end chunk (or -1) and, per chunk, whether it is it
+__device__ __forceinline__ int tail_col(const Geo& G, const Tile& tl, const Lane& L, bool (&part)[NV_MAX]) {
+  int col = -1;
+#pragma unroll
+  for (int j = 0; j < NV_MAX; ++j) {
+    const int ct = (j * G.g + L.lane) * VEC;
+    part[j] = (ct < tl.tce) & (ct + VEC > tl.tce);
+    col = part[j] ? ct : col;
+  }
+  return col;
+}
+
+template <uint32_t DT>
+__device__ __forceinline__ void load_tail(Ch& d, const Rsrc& rs, int roff, const Geo& G, const Tile& tl,
+                                          const Lane& L, bool rok) {
+  constexpr int ES = esize_c<DT>();
+  if (tile_full(tl)) return;
+  bool part[NV_MAX];
+  const int col = tail_col(G, tl, L, part);
+  float v[VEC];
+#pragma unroll
+  for (int i = 0; i < VEC; ++i)
+    v[i] = load_elem<DT>(rs, lane_off(rok & (col >= 0) & (col + i < tl.tce), (roff + col + i) * ES));
+  // wait for these loads on this path: left pending, they would make the
+  // compiler wait at the join for all outstanding vector memory (a prefetch
+  // issued later included), also on the path that skips them
+  asm volatile("" : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]), "+v"(v[4]), "+v"(v[5]), "+v"(v[6]), "+v"(v[7]));
+#pragma unroll
+  for (int j = 0; j < NV_MAX; ++j)
+#pragma unroll
+    for (int i = 0; i < VEC; ++i) d.c[j][i] = lane_sel(part[j], v[i], d.c[j][i]);
+}
+
+template <uint32_t DT>
+__device__ __forceinline__ void store_tail(const Ch& s, const Rsrc& rs, int roff, const Geo& G, const Tile& tl,
+                                           const Lane& L) {
+  constexpr int ES = esize_c<DT>();
+  if (tile_full(tl)) return;
+  bool part[NV_MAX];
+  const int col = tail_col(G, tl, L, part);
+#pragma unroll
+  for (int i = 0; i < VEC; ++i) {
+    float v = s.c[0][i];
+#pragma unroll
+    for (int j = 1; j < NV_MAX; ++j) v = lane_sel(part[j], s.c[j][i], v);
+    store_elem<DT>(rs, lane_off(L.rok & (col >= 0) & (col + i < tl.tce), (roff + col + i) * ES), v);
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Load / Store (Table 1: Load/ViewLoad/Store/ViewStore)
 // ---------------------------------------------------------------------------
@@ -296,13 +365,14 @@ __device__ __forceinline__ void load_dir(Ch& d, const ArgD& a, const Geo& G, con
     else if constexpr (DT == DT_BF16) v = bf2f(__builtin_amdgcn_raw_buffer_load_b16(rs, off, 0, 0));
     else v = (float)__builtin_amdgcn_raw_buffer_load_b8(rs, off, 0, 0);
     fill(d, v);
-  } else if ((a.fl & AF_VEC) && a.sc == 1 && tile_full(tl)) {
-    // full chunks, 16-byte aligned: 128-bit accesses; a chunk is wholly in or
-    // out (chunks past the row's last one fall out of range and are masked)
+  } else if ((a.fl & AF_VEC) && a.sc == 1) {
+    // dword-aligned chunks: 128-bit accesses for every chunk that lies wholly
+    // inside the row (the others are masked); in a ragged tile the one chunk
+    // per row that holds the row's end is completed element by element
 #pragma unroll
     for (int j = 0; j < NV_MAX; ++j) {
       const int ct = (j * G.g + L.lane) * VEC;
-      const int off = lane_off(rok & (ct < tl.tce), (roff + ct) * ES);
+      const int off = lane_off(rok & (ct + VEC <= tl.tce), (roff + ct) * ES);
       if constexpr (DT == DT_F32) {
         const u4 v0 = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
         const u4 v1 = __builtin_amdgcn_raw_buffer_load_b128(rs, off == OOB ? OOB : off + 16, 0, 0);
@@ -318,8 +388,9 @@ __device__ __forceinline__ void load_dir(Ch& d, const ArgD& a, const Geo& G, con
         }
       }
     }
+    load_tail<DT>(d, rs, roff, G, tl, L, rok);
   } else {
-    // element path: ragged tiles, unaligned or strided operands
+    // element path: unaligned or strided operands
 #pragma unroll
     for (int j = 0; j < NV_MAX; ++j) {
       const int ct = (j * G.g + L.lane) * VEC;
@@ -349,11 +420,11 @@ __device__ __forceinline__ void store_dir(const Ch& s, const ArgD& a, const Geo&
   constexpr int ES = esize_c<DT>();
   const Rsrc rs = tile_rsrc(a, tl, ES);
   const int roff = L.row * (int)a.sr;
-  if ((a.fl & AF_VEC) && a.sc == 1 && tile_full(tl)) {
+  if ((a.fl & AF_VEC) && a.sc == 1) {
 #pragma unroll
     for (int j = 0; j < NV_MAX; ++j) {
       const int ct = (j * G.g + L.lane) * VEC;
-      const int off = lane_off(L.rok & (ct < tl.tce), (roff + ct) * ES);
+      const int off = lane_off(L.rok & (ct + VEC <= tl.tce), (roff + ct) * ES);
       const V8 x = s.c[j];
       if constexpr (DT == DT_F32) {
         u4 v0, v1;
@@ -378,6 +449,7 @@ __device__ __forceinline__ void store_dir(const Ch& s, const ArgD& a, const Geo&
         __builtin_amdgcn_raw_buffer_store_b64(v, rs, off, 0, 0);
       }
     }
+    store_tail<DT>(s, rs, roff, G, tl, L);
   } else {
 #pragma unroll
     for (int j = 0; j < NV_MAX; ++j) {
@@ -429,7 +501,7 @@ __device__ __forceinline__ void pf_issue(char* slot, const ArgD& a, const Geo& G
   for (int j = 0; j < NV_MAX; ++j) {
     if (j < G.nv) {
       const int ct = (j * G.g + L.lane) * VEC;
-      const int off = lane_off(rok & (ct < nt.tce), (roff + ct) * ES);
+      const int off = lane_off(rok & (ct + VEC <= nt.tce), (roff + ct) * ES);  // whole chunks only
 #pragma unroll
       for (int h = 0; h < HV; ++h) {
         const uint32_t dst = __builtin_amdgcn_readfirstlane(base + (uint32_t)(((j * HV + h) * T_LANES + wave * 64) * 16));
@@ -532,21 +604,17 @@ template <uint32_t DT>
 __device__ __forceinline__ void read_pf(Ch& d, uint32_t w0, uint32_t vmc, const ArgD& a, const Geo& G,
                                         const Tile& tl, const Lane& L, const Ctx& S) {
   const uint32_t slot = f_b(w0) & 1u;
-  if (tile_full(tl)) {
-    // the previous tile may have been ragged (more instructions issued after
-    // the prefetch): the count stays a lower bound, so the wait stays exact
-    wait_vm(vmc);
-    pf_read<DT>(d, S.pf(slot), G, L.tid);
-  } else {
-    load_dir<DT>(d, a, G, tl, L);
-  }
+  // The count is a lower bound of the instructions issued after the
+  // prefetch (ragged tiles issue more), so the wait covers the prefetch.
+  wait_vm(vmc);
+  pf_read<DT>(d, S.pf(slot), G, L.tid);
+  // the prefetch moved whole chunks only: complete the row-end chunk
+  load_tail<DT>(d, tile_rsrc(a, tl, esize_c<DT>()), L.row * (int)a.sr, G, tl, L, L.rok);
   if ((f_flags(w0) & FL_ISSUE) && S.tile + 1 < S.t_end) {
     const Tile nt = make_tile(G, S.tile + 1);
-    if (tile_full(nt)) {
-      // this lane's reads of the slot have completed before the refill starts
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-      pf_issue<DT>(S.pf(slot), a, G, nt, L);
-    }
+    // this lane's reads of the slot have completed before the refill starts
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    pf_issue<DT>(S.pf(slot), a, G, nt, L);
   }
 }
 
@@ -1026,10 +1094,8 @@ dvm_vm_vector(const Program prog) {
       case HD_PF: {
         // prologue: fetch the workgroup's first tile into the prefetch slot
         const ArgD a = ARG;
-        if (tile_full(tl)) {
-          if (a.dt == DT_F32) pf_issue<DT_F32>(S.pf(f_b(w0) & 1u), a, G, tl, L);
-          else pf_issue<DT_BF16>(S.pf(f_b(w0) & 1u), a, G, tl, L);
-        }
+        if (a.dt == DT_F32) pf_issue<DT_F32>(S.pf(f_b(w0) & 1u), a, G, tl, L);
+        else pf_issue<DT_BF16>(S.pf(f_b(w0) & 1u), a, G, tl, L);
         break;
       }
       default:

@@ -68,7 +68,8 @@ def _ln(dvm, ctx, x, gam, bet, eps=W.LN_EPS):
     return host64(out)
 
 
-@pytest.mark.parametrize("rows,h", [(1, 5120), (3, 5120), (37, 5120), (5, 96), (9, 1001), (2, 8192), (300, 24)])
+@pytest.mark.parametrize("rows,h", [(1, 5120), (3, 5120), (37, 5120), (5, 96), (9, 1001), (2, 8192), (300, 24),
+                                    (1500, 5122), (700, 1030)])
 def test_layernorm(dvm, ctx, rows, h):
     say("layernorm", rows, h)
     x = W.layernorm_x(0, rows, rows, h)
@@ -95,7 +96,8 @@ def test_layernorm_workload_sampled(dvm, ctx):
         assert ok, f"call {i}: max ulp {d}"
 
 
-@pytest.mark.parametrize("rows,cols", [(1, 16), (7, 3001), (40, 512), (3, 8192), (513, 17)])
+@pytest.mark.parametrize("rows,cols", [(1, 16), (7, 3001), (40, 512), (3, 8192), (513, 17), (1200, 6484),
+                                       (900, 1030)])
 def test_softmax(dvm, ctx, rows, cols):
     from device_bytecode_vm_amd import composites as CP
     say("softmax", rows, cols)
@@ -133,7 +135,7 @@ def test_add_rmsnorm_fused(dvm, ctx, rows):
     assert ok, f"max ulp {d}"
 
 
-@pytest.mark.parametrize("rows,cols", [(3, 17408), (1, 100), (17, 777)])
+@pytest.mark.parametrize("rows,cols", [(3, 17408), (1, 100), (17, 777), (600, 2052)])
 def test_swiglu(dvm, ctx, rows, cols):
     from device_bytecode_vm_amd import composites as CP
     say("swiglu", rows, cols)
