@@ -88,9 +88,17 @@ enum Hdr : int {
 
 // MIX kernel geometry: the output tile (header H_TR x H_TC) is one of the MIX
 // kernel's variants (128 x 128 per 256-lane workgroup, two workgroups per
-// compute unit); K runs in stages of MM_KT through two LDS buffers for A and
-// two for B (2 (tm + tn) MM_KT bf16 values of LDS).
-constexpr int MM_KT = 64;
+// compute unit); K runs in stages of MM_KT through a ring of MM_STAGES LDS
+// stages, each holding tm x MM_KT of A and MM_KT x tn of B (bf16).  After
+// the K loop the fp32 output tile is staged in LDS with rows of tn + MM_OPAD
+// values; the ring and the staged tile share the same bytes.
+constexpr int MM_KT = 32;
+constexpr int MM_STAGES = 4;
+constexpr int MM_OPAD = 8;
+__host__ __device__ constexpr int mm_lds_bytes(int tm, int tn) {
+  return MM_STAGES * (tm + tn) * MM_KT * 2 > tm * (tn + MM_OPAD) * 4 ? MM_STAGES * (tm + tn) * MM_KT * 2
+                                                                    : tm * (tn + MM_OPAD) * 4;
+}
 
 // LDS staging (per workgroup, dynamic):
 //  * prefetch slot: NV chunks x T lanes x 16 bytes x (element size / 2)

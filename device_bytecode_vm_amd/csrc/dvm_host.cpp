@@ -1390,7 +1390,7 @@ struct Encoder {
     W[H_MM_K] = (uint32_t)K;
     W[H_MM_A] = 0;
     W[H_MM_B] = 1;
-    W[H_LDS_BYTES] = (uint32_t)(2 * (plan.tr + plan.tc) * MM_KT * 2);
+    W[H_LDS_BYTES] = (uint32_t)mm_lds_bytes((int)plan.tr, (int)plan.tc);
     W[H_N_INSTR] = (uint32_t)(body.size() / 2);
     prog->n_words = instr_base + (uint32_t)body.size();
     prog->n_instr = (uint32_t)(body.size() / 2);

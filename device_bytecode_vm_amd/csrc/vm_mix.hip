@@ -15,17 +15,23 @@
 // 32) + j] and B[8 (l / 32) + j][l % 32] for j < 8, and holds
 // D[8 (i / 4) + 4 (l / 32) + i % 4][l % 32] in accumulator register i.
 //
-// K runs in stages of 64 through two LDS buffers: while stage s is multiplied,
-// the global loads of stage s + 1 are in flight (128-bit loads into registers,
-// written to the other buffer after the stage).  A is stored row-major, B is
-// stored transposed (one row per output column), so both operands are read
-// with one 128-bit LDS load per lane; the 16-byte chunks of every row are
-// XOR-swizzled so that the eight lanes of a read phase hit distinct banks.
+// K runs in stages of MM_KT through a ring of MM_STAGES LDS stages filled by
+// direct-to-LDS buffer loads issued MM_STAGES - 1 stages ahead of the stage
+// being multiplied (no register staging); A is stored row-major and read with
+// one 128-bit LDS load per lane and block, B is stored row-major too and read
+// with transposing LDS loads, which give each lane its eight consecutive K
+// values of one column.
 //
-// The epilogue (the program body) runs per 32 x 32 accumulator block with
-// three 16-value tile registers (register 0 starts as the block of the matmul
+// The epilogue (the program body) runs on the output tile staged in LDS as
+// fp32, one row-major chunk of 8 columns per lane at a time, with three
+// 8-value tile registers (register 0 starts as the chunk of the matmul
 // result); memory operands and stores address element (m, n) of the [M, N]
 // space through buffer resources, out-of-range offsets masking the edges.
+//
+// Tile order: a workgroup takes every grid-th tile of a grouped order (eight
+// row tiles, walked column by column), starting from an XCD-aware slot, so
+// the tiles in flight on one XCD at a time form an 8 x 8 block and share
+// their A and B panels through that XCD's L2.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -46,7 +52,6 @@ typedef const __attribute__((address_space(4))) uint32_t KW;
 constexpr int OOB = 0x7fffffff;
 constexpr int RSRC_W3 = 0x00020000;
 constexpr int KT = MM_KT;
-constexpr int ROW_BYTES = KT * 2;     // one LDS row: 64 bf16 = 8 chunks of 16 bytes
 
 struct ArgD {
   const char* p;
@@ -121,108 +126,127 @@ __device__ __forceinline__ float una_rt(uint32_t f, float x) {
 // K loop (templated on the wave tile: BM x BN blocks of 32 x 32 per wave,
 // four waves in a 2 x 2 arrangement)
 // ---------------------------------------------------------------------------
-// Byte offset of chunk kc (8 bf16 along K) of LDS row r, swizzled by s.
-__device__ __forceinline__ int chunk_at(int r, int kc, int s) { return r * ROW_BYTES + ((kc ^ (s & 7)) << 4); }
-__device__ __forceinline__ int a_swz(int row) { return row; }
-__device__ __forceinline__ int b_swz(int n) { return n ^ (n >> 3); }
+// LDS ring of MM_STAGES stages of KT = MM_KT values of K.  A stage holds
+//  * A as TM rows of KT bf16 (KT / 8 16-byte units per row), unit kc of row r
+//    stored at position kc ^ a_swz(r): the 16 rows read together by a quarter
+//    wave (same kc) then cover all 64 banks;
+//  * B row-major as KT rows of TN bf16 (TN / 8 units per row), unit cc of row
+//    k stored at position cc ^ 4 (k & 3): the four rows read together by a
+//    16-lane group of a transposing read land on disjoint banks.
+// Both are written by direct-to-LDS buffer loads (lane i of a wave writes the
+// 16 bytes at M0 + 16 i), so the swizzle is applied by choosing which global
+// unit each lane fetches.  Out-of-range units (rows past M, columns past N,
+// K past its end) read as zeros.
+//
+// Fragments: A as one 128-bit read per block (row l % 32, K unit 2 kk + l /
+// 32); B with two transposing reads (ds_read_b64_tr_b16).  Within each group
+// of 16 lanes such a read hands lane 4a + b the element b of the 8-byte words
+// read by lanes a, a + 4, a + 8 and a + 12 (checked on the device), so lanes
+// a + 4c reading row k0 + c at columns 4a .. 4a + 3 give lane 4a + b column
+// 4a + b at K = k0 .. k0 + 3, the B operand layout of the matrix instruction.
+typedef short s4 __attribute__((ext_vector_type(4)));
+typedef short s8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) s4 lds_s4;
+typedef __attribute__((address_space(3))) void lds_void;
 
 template <int BM, int BN>
 struct Cfg {
-  static constexpr int TM = 64 * BM, TN = 64 * BN;       // workgroup tile
-  static constexpr int QA = TM * (KT / 8) / 256;         // A chunks per lane per stage
-  static constexpr int QB = TN * (KT / 8) / 256;         // B chunks per lane per stage
-  static constexpr int NCH = TN / 8;                     // B chunks per K row
-  static constexpr int A_BYTES = TM * ROW_BYTES;         // one A stage
-  static constexpr int B_BYTES = TN * ROW_BYTES;         // one B stage
-  static constexpr int LDS = 2 * (A_BYTES + B_BYTES);
+  static constexpr int TM = 64 * BM, TN = 64 * BN;      // workgroup tile
+  static constexpr int UA = KT / 8, UB = TN / 8;        // 16-byte units per A row, per B row
+  static constexpr int A_BYTES = TM * KT * 2;
+  static constexpr int B_BYTES = KT * TN * 2;
+  static constexpr int STAGE = A_BYTES + B_BYTES;
+  static constexpr int QA = A_BYTES / (256 * 16);       // loads per lane per stage
+  static constexpr int QB = B_BYTES / (256 * 16);
+  static constexpr int Q = QA + QB;
+  static constexpr int LDS = mm_lds_bytes(TM, TN);
+  static_assert(A_BYTES % (256 * 16) == 0 && B_BYTES % (256 * 16) == 0, "whole loads per lane");
+  static_assert(UB >= 16, "B swizzle needs 16 units per row");
 };
 
-// A chunk c of a stage: row c / 8, K chunk c % 8 (eight lanes read one row's
-// 128 contiguous bytes).  B chunk c: eight K rows by eight column chunks per
-// wave (each column chunk's 128-byte line is still read whole by one wave),
-// so the transposed 16-bit LDS writes of a wave spread over all banks.
-__device__ __forceinline__ void a_chunk(int c, int& row, int& kc) {
-  row = c >> 3;
-  kc = c & 7;
-}
-template <int NCH>
-__device__ __forceinline__ void b_chunk(int c, int& kr, int& nc) {
-  const int rest = c >> 6;
-  kr = ((rest & 7) << 3) | (c & 7);
-  nc = ((rest >> 3) << 3) | ((c >> 3) & 7);
+// A: the rows sharing a 256-byte bank line differ in the swizzle
+template <int UA>
+__device__ __forceinline__ int a_swz(int r) { return (r / (16 / UA)) & (UA - 1); }
+
+__device__ __forceinline__ void dma16(uint32_t lds_dst, int voff, const u4& rs) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(lds_dst), "v"(voff), "s"(rs)
+               : "memory", "m0");
 }
 
-template <class CF>
-struct Stage {
-  u4 a[CF::QA], b[CF::QB];  // this lane's 16-byte chunks of the next A and B stages
+// Waits until at most N of this lane's direct-to-LDS loads are in flight.
+template <int N>
+__device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory"); }
+
+__device__ __forceinline__ u4 rsrc_words(const ArgD& a, int64_t ob) {
+  const int64_t left = (int64_t)a.extent - ob;
+  const int n = left <= 0 ? 0 : (left >= (int64_t)EXTENT_CAP ? (int)(EXTENT_CAP - 1) : (int)left);
+  const uint64_t base = (uint64_t)(uintptr_t)(a.p + ob);
+  u4 r;
+  r.x = (uint32_t)base;
+  r.y = (uint32_t)(base >> 32) & 0xffffu;  // stride 0
+  r.z = (uint32_t)n;
+  r.w = (uint32_t)RSRC_W3;
+  return r;
+}
+
+struct Panels {
+  u4 ra, rb;          // A from row m0, B from column n0
+  int64_t m0, n0;
 };
 
-// Global loads of the stage at k0; masked chunks read as zeros.
+// Issue the direct-to-LDS loads of stage s (K from s KT) into ring slot `slot`.
 template <class CF>
-__device__ __forceinline__ void load_stage(Stage<CF>& st, const Rsrc& ra, const Rsrc& rb, const ArgD& A,
-                                           const ArgD& B, int64_t m0, int64_t n0, int k0, int64_t M, int64_t N,
-                                           int K, int tid) {
+__device__ __forceinline__ void issue_stage(uint32_t ring, int slot, int s, const Panels& P, const ArgD& A,
+                                            const ArgD& B, int64_t M, int64_t N, int K, int wave, int lane) {
+  const uint32_t base = ring + (uint32_t)(slot * CF::STAGE);
+  const int k0 = s * KT;
 #pragma unroll
   for (int q = 0; q < CF::QA; ++q) {
-    int row, kc;
-    a_chunk(tid + 256 * q, row, kc);
-    const bool ok = (m0 + row < M) & (k0 + kc * 8 < K);
-    st.a[q] = __builtin_amdgcn_raw_buffer_load_b128(ra, lane_off(ok, (row * (int)A.sr + k0 + kc * 8) * 2), 0, 0);
+    const int u = (q * 4 + wave) * 64 + lane;    // unit written by this lane
+    const int r = u / CF::UA, pos = u % CF::UA;
+    const int kc = pos ^ a_swz<CF::UA>(r);
+    const bool ok = (P.m0 + r < M) & (k0 + kc * 8 < K);
+    dma16(__builtin_amdgcn_readfirstlane(base + (uint32_t)((q * 4 + wave) * 64 * 16)),
+          lane_off(ok, (r * (int)A.sr + k0 + kc * 8) * 2), P.ra);
   }
 #pragma unroll
   for (int q = 0; q < CF::QB; ++q) {
-    int kr, nc;
-    b_chunk<CF::NCH>(tid + 256 * q, kr, nc);
-    const bool ok = (k0 + kr < K) & (n0 + nc * 8 < N);
-    st.b[q] = __builtin_amdgcn_raw_buffer_load_b128(rb, lane_off(ok, ((k0 + kr) * (int)B.sr + nc * 8) * 2), 0, 0);
+    const int u = (q * 4 + wave) * 64 + lane;
+    const int k = u / CF::UB, pos = u % CF::UB;
+    const int cc = pos ^ ((k & 3) << 2);
+    const bool ok = (k0 + k < K) & (P.n0 + cc * 8 < N);
+    dma16(__builtin_amdgcn_readfirstlane(base + (uint32_t)(CF::A_BYTES + (q * 4 + wave) * 64 * 16)),
+          lane_off(ok, ((k0 + k) * (int)B.sr + cc * 8) * 2), P.rb);
   }
 }
 
-// Writes of the loaded stage to LDS buffers (A row-major, B transposed).
-template <class CF>
-__device__ __forceinline__ void write_stage(const Stage<CF>& st, char* abuf, char* bbuf, int tid) {
-#pragma unroll
-  for (int q = 0; q < CF::QA; ++q) {
-    int row, kc;
-    a_chunk(tid + 256 * q, row, kc);
-    *(u4*)(abuf + chunk_at(row, kc, a_swz(row))) = st.a[q];
-  }
-#pragma unroll
-  for (int q = 0; q < CF::QB; ++q) {
-    int kr, nc;
-    b_chunk<CF::NCH>(tid + 256 * q, kr, nc);
-    const u4 v = st.b[q];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int n = nc * 8 + j;
-      const uint32_t w = j < 2 ? v.x : j < 4 ? v.y : j < 6 ? v.z : v.w;
-      const uint16_t h = (uint16_t)((j & 1) ? (w >> 16) : (w & 0xffffu));
-      *(uint16_t*)(bbuf + chunk_at(n, kr >> 3, b_swz(n)) + (kr & 7) * 2) = h;
-    }
-  }
-}
-
-__device__ __forceinline__ bf8 read_frag(const char* buf, int r, int kc, int s) {
-  return *(const bf8*)(buf + chunk_at(r, kc, s));
-}
-
-// One stage of KT values of K on this wave's BM x BN blocks.
-template <int BM, int BN>
-__device__ __forceinline__ void mma_stage(f16v (&c)[BM][BN], const char* abuf, const char* bbuf, int wm, int wn,
-                                          int lane) {
+// One stage of KT values of K on this wave's BM x BN blocks, from ring slot
+// bytes `st`.
+template <class CF, int BM, int BN>
+__device__ __forceinline__ void mma_stage(f16v (&c)[BM][BN], const char* st, int wm, int wn, int lane) {
+  const char* abuf = st;
+  const char* bbuf = st + CF::A_BYTES;
+  const int g = lane >> 4, p = lane & 15;
 #pragma unroll
   for (int kk = 0; kk < KT / 16; ++kk) {
-    const int kc = kk * 2 + (lane >> 5);
     bf8 a[BM], b[BN];
 #pragma unroll
     for (int i = 0; i < BM; ++i) {
       const int r = wm * 32 * BM + i * 32 + (lane & 31);
-      a[i] = read_frag(abuf, r, kc, a_swz(r));
+      const int kc = kk * 2 + (lane >> 5);
+      a[i] = *(const bf8*)(abuf + (r * CF::UA + (kc ^ a_swz<CF::UA>(r))) * 16);
     }
 #pragma unroll
     for (int j = 0; j < BN; ++j) {
-      const int n = wn * 32 * BN + j * 32 + (lane & 31);
-      b[j] = read_frag(bbuf, n, kc, b_swz(n));
+      const int k = kk * 16 + 8 * (g >> 1) + (p >> 2);
+      const int n = wn * 32 * BN + j * 32 + 16 * (g & 1) + 4 * (p & 3);
+      const int off = (k * CF::UB + ((n >> 3) ^ ((k & 3) << 2))) * 16 + ((n >> 2) & 1) * 8;
+      const s4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(lds_void*)(bbuf + off));
+      const s4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(lds_void*)(bbuf + off + 4 * CF::UB * 16));
+      const s8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+      b[j] = __builtin_bit_cast(bf8, v);
     }
 #pragma unroll
     for (int i = 0; i < BM; ++i)
@@ -238,79 +262,132 @@ __device__ __forceinline__ void lds_barrier() {
 }
 
 // ---------------------------------------------------------------------------
-// Epilogue: the program body on one 32 x 32 block
+// Epilogue: the program body on the tile, staged in LDS
 // ---------------------------------------------------------------------------
-struct T16 {
-  float v[16];
+// After the K loop the accumulators go to LDS as an fp32 [TM][OSTR] tile
+// (rows padded by 8 floats so the two half-waves of a write hit disjoint
+// banks).  The body then runs on row-major chunks of 8 columns per lane:
+// 128-bit LDS reads, and 128-bit global accesses for operands whose chunks
+// are contiguous and dword aligned.  N is a multiple of 8, so a chunk is
+// wholly inside or wholly outside the output.
+
+struct T8 {
+  float v[8];
 };
 
-struct Blk {
-  int64_t mb, nb;  // block origin in [M, N]
-  int64_t M, N;
-  int lane;
+struct Chunk {
+  int64_t m0, n0;  // tile origin in [M, N]
+  int r, c8;       // chunk row and first column inside the tile
+  bool ok;         // chunk inside [M, N]
 };
 
-// row of accumulator register i for this lane, relative to the block
-__device__ __forceinline__ int dm_of(int i, int lane) { return 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3); }
+__device__ __forceinline__ u4 ld128(const Rsrc& rs, int off) { return __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0); }
 
-__device__ __forceinline__ void epi_load(T16& d, const ArgD& a, const Blk& B) {
+__device__ __forceinline__ void epi_load(T8& d, const ArgD& a, const Chunk& C) {
   const int es = esize(a.dt);
-  const Rsrc rs = rsrc_at(a, (B.mb * a.sr + B.nb * (int64_t)a.sc) * es);
-  const int dn = B.lane & 31;
-  const bool nok = B.nb + dn < B.N;
+  const Rsrc rs = rsrc_at(a, (C.m0 * a.sr + C.n0 * (int64_t)a.sc) * es);
+  const int base = (C.r * (int)a.sr + C.c8 * a.sc) * es;
+  if ((a.fl & AF_VEC) && a.sc == 1) {
+    if (a.dt == DT_F32) {
+      const u4 x = ld128(rs, lane_off(C.ok, base)), y = ld128(rs, lane_off(C.ok, base + 16));
+      d.v[0] = __uint_as_float(x.x); d.v[1] = __uint_as_float(x.y); d.v[2] = __uint_as_float(x.z); d.v[3] = __uint_as_float(x.w);
+      d.v[4] = __uint_as_float(y.x); d.v[5] = __uint_as_float(y.y); d.v[6] = __uint_as_float(y.z); d.v[7] = __uint_as_float(y.w);
+    } else if (a.dt == DT_BF16) {
+      const u4 x = ld128(rs, lane_off(C.ok, base));
+      const uint32_t w[4] = {x.x, x.y, x.z, x.w};
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int dm = dm_of(i, B.lane);
-    const int off = lane_off(nok & (B.mb + dm < B.M), (dm * (int)a.sr + dn * a.sc) * es);
+      for (int j = 0; j < 4; ++j) {
+        d.v[2 * j] = bf2f(w[j] & 0xffffu);
+        d.v[2 * j + 1] = __uint_as_float(w[j] & 0xffff0000u);
+      }
+    } else {
+      const uint32_t lo = __builtin_amdgcn_raw_buffer_load_b32(rs, lane_off(C.ok, base), 0, 0);
+      const uint32_t hi = __builtin_amdgcn_raw_buffer_load_b32(rs, lane_off(C.ok, base + 4), 0, 0);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        d.v[j] = (float)((lo >> (8 * j)) & 0xffu);
+        d.v[4 + j] = (float)((hi >> (8 * j)) & 0xffu);
+      }
+    }
+    return;
+  }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int off = lane_off(C.ok, base + j * a.sc * es);
     float x;
     if (a.dt == DT_BF16) x = bf2f(__builtin_amdgcn_raw_buffer_load_b16(rs, off, 0, 0));
     else if (a.dt == DT_F32) x = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, 0));
     else x = (float)__builtin_amdgcn_raw_buffer_load_b8(rs, off, 0, 0);
-    d.v[i] = x;
+    d.v[j] = x;
   }
 }
 
-__device__ __forceinline__ void epi_store(const T16& s, const ArgD& a, const Blk& B) {
+__device__ __forceinline__ void epi_store(const T8& s, const ArgD& a, const Chunk& C) {
   const int es = esize(a.dt);
-  const Rsrc rs = rsrc_at(a, (B.mb * a.sr + B.nb * (int64_t)a.sc) * es);
-  const int dn = B.lane & 31;
-  const bool nok = B.nb + dn < B.N;
+  const Rsrc rs = rsrc_at(a, (C.m0 * a.sr + C.n0 * (int64_t)a.sc) * es);
+  const int base = (C.r * (int)a.sr + C.c8 * a.sc) * es;
+  if ((a.fl & AF_VEC) && a.sc == 1) {
+    if (a.dt == DT_F32) {
+      const u4 x = {__float_as_uint(s.v[0]), __float_as_uint(s.v[1]), __float_as_uint(s.v[2]), __float_as_uint(s.v[3])};
+      const u4 y = {__float_as_uint(s.v[4]), __float_as_uint(s.v[5]), __float_as_uint(s.v[6]), __float_as_uint(s.v[7])};
+      __builtin_amdgcn_raw_buffer_store_b128(x, rs, lane_off(C.ok, base), 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b128(y, rs, lane_off(C.ok, base + 16), 0, 0);
+    } else if (a.dt == DT_BF16) {
+      const u4 x = {f2bf_pack(s.v[0], s.v[1]), f2bf_pack(s.v[2], s.v[3]), f2bf_pack(s.v[4], s.v[5]),
+                    f2bf_pack(s.v[6], s.v[7])};
+      __builtin_amdgcn_raw_buffer_store_b128(x, rs, lane_off(C.ok, base), 0, 0);
+    } else {
+      uint32_t lo = 0, hi = 0;
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int dm = dm_of(i, B.lane);
-    const int off = lane_off(nok & (B.mb + dm < B.M), (dm * (int)a.sr + dn * a.sc) * es);
-    const float x = s.v[i];
+      for (int j = 0; j < 4; ++j) {
+        lo |= (uint32_t)(uint8_t)s.v[j] << (8 * j);
+        hi |= (uint32_t)(uint8_t)s.v[4 + j] << (8 * j);
+      }
+      __builtin_amdgcn_raw_buffer_store_b32(lo, rs, lane_off(C.ok, base), 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b32(hi, rs, lane_off(C.ok, base + 4), 0, 0);
+    }
+    return;
+  }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int off = lane_off(C.ok, base + j * a.sc * es);
+    const float x = s.v[j];
     if (a.dt == DT_BF16) __builtin_amdgcn_raw_buffer_store_b16((uint16_t)(f2bf_pack(x, 0.f) & 0xffffu), rs, off, 0, 0);
     else if (a.dt == DT_F32) __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x), rs, off, 0, 0);
     else __builtin_amdgcn_raw_buffer_store_b8((uint8_t)x, rs, off, 0, 0);
   }
 }
 
-__device__ __forceinline__ void pick(T16& d, uint32_t k, const T16& t0, const T16& t1, const T16& t2) {
-  if (k == 0) d = t0;
-  else if (k == 1) d = t1;
-  else d = t2;
+// Register k (wave-uniform) selected element by element, which keeps the
+// three registers in VGPRs (a whole-struct copy under a dynamic k becomes
+// an indexed stack array).
+__device__ __forceinline__ void pick(T8& d, uint32_t k, const T8& t0, const T8& t1, const T8& t2) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) d.v[i] = k == 0 ? t0.v[i] : k == 1 ? t1.v[i] : t2.v[i];
 }
 
-__device__ __forceinline__ void put(uint32_t k, const T16& s, T16& t0, T16& t1, T16& t2) {
-  if (k == 0) t0 = s;
-  else if (k == 1) t1 = s;
-  else t2 = s;
+__device__ __forceinline__ void put(uint32_t k, const T8& s, T8& t0, T8& t1, T8& t2) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    t0.v[i] = k == 0 ? s.v[i] : t0.v[i];
+    t1.v[i] = k == 1 ? s.v[i] : t1.v[i];
+    t2.v[i] = k == 2 ? s.v[i] : t2.v[i];
+  }
 }
 
 template <uint32_t OPK>
-__device__ __forceinline__ void bin16(T16& acc, const T16& b, bool rev) {
+__device__ __forceinline__ void bin8(T8& acc, const T8& b, bool rev) {
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
+  for (int i = 0; i < 8; ++i) {
     const float x = acc.v[i], y = b.v[i];
     acc.v[i] = rev ? alu_rt(OPK, y, x) : alu_rt(OPK, x, y);
   }
 }
 
-__device__ __forceinline__ void run_epilogue(KW* W, T16& t0, const Blk& B) {
-  T16 t1, t2;
+__device__ __forceinline__ void run_epilogue(KW* W, T8& t0, const Chunk& C) {
+  T8 t1, t2;
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
+  for (int i = 0; i < 8; ++i) {
     t1.v[i] = 0.f;
     t2.v[i] = 0.f;
   }
@@ -319,48 +396,48 @@ __device__ __forceinline__ void run_epilogue(KW* W, T16& t0, const Blk& B) {
     const uint32_t w0 = W[pc], w1 = W[pc + 1];
     switch (f_op(w0)) {
       case OP_LOAD: {
-        T16 m;
-        epi_load(m, read_arg(W, w1), B);
+        T8 m;
+        epi_load(m, read_arg(W, w1), C);
         put(f_dst(w0), m, t0, t1, t2);
         break;
       }
       case OP_STORE: {
-        T16 m;
+        T8 m;
         pick(m, f_a(w0), t0, t1, t2);
-        epi_store(m, read_arg(W, w1), B);
+        epi_store(m, read_arg(W, w1), C);
         break;
       }
       case OP_COPY: {
-        T16 m;
+        T8 m;
         pick(m, f_a(w0), t0, t1, t2);
         put(f_dst(w0), m, t0, t1, t2);
         break;
       }
       case OP_BIN: {
-        T16 b;
+        T8 b;
         const uint32_t bk = f_bk(w0);
-        if (bk == BK_MEM) epi_load(b, read_arg(W, w1), B);
+        if (bk == BK_MEM) epi_load(b, read_arg(W, w1), C);
         else if (bk == BK_TREG) pick(b, f_b(w0), t0, t1, t2);
         else {
 #pragma unroll
-          for (int i = 0; i < 16; ++i) b.v[i] = __uint_as_float(w1);
+          for (int i = 0; i < 8; ++i) b.v[i] = __uint_as_float(w1);
         }
         const bool rev = (f_flags(w0) & FL_REV) != 0;
         switch (f_sub(w0)) {
-          case ALU_ADD: bin16<ALU_ADD>(t0, b, rev); break;
-          case ALU_SUB: bin16<ALU_SUB>(t0, b, rev); break;
-          case ALU_MUL: bin16<ALU_MUL>(t0, b, rev); break;
-          case ALU_DIV: bin16<ALU_DIV>(t0, b, rev); break;
-          case ALU_MAX: bin16<ALU_MAX>(t0, b, rev); break;
-          case ALU_MIN: bin16<ALU_MIN>(t0, b, rev); break;
-          default: bin16<ALU_POW>(t0, b, rev); break;
+          case ALU_ADD: bin8<ALU_ADD>(t0, b, rev); break;
+          case ALU_SUB: bin8<ALU_SUB>(t0, b, rev); break;
+          case ALU_MUL: bin8<ALU_MUL>(t0, b, rev); break;
+          case ALU_DIV: bin8<ALU_DIV>(t0, b, rev); break;
+          case ALU_MAX: bin8<ALU_MAX>(t0, b, rev); break;
+          case ALU_MIN: bin8<ALU_MIN>(t0, b, rev); break;
+          default: bin8<ALU_POW>(t0, b, rev); break;
         }
         break;
       }
       case OP_UN: {
         const uint32_t f = f_sub(w0);
 #pragma unroll
-        for (int i = 0; i < 16; ++i) t0.v[i] = una_rt(f, t0.v[i]);
+        for (int i = 0; i < 8; ++i) t0.v[i] = una_rt(f, t0.v[i]);
         break;
       }
       default:
@@ -369,18 +446,80 @@ __device__ __forceinline__ void run_epilogue(KW* W, T16& t0, const Blk& B) {
   }
 }
 
-__device__ __forceinline__ void to16(T16& d, const f16v& c) {
+// Row of accumulator register i of this lane inside its 32 x 32 block.
+__device__ __forceinline__ int dm_of(int i, int lane) { return 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3); }
+
+// Accumulators of this wave to the fp32 LDS tile.
+template <int BM, int BN>
+__device__ __forceinline__ void acc_to_lds(const f16v (&c)[BM][BN], float* ot, int wm, int wn, int lane) {
+  constexpr int OSTR = 64 * BN + MM_OPAD;
 #pragma unroll
-  for (int i = 0; i < 16; ++i) d.v[i] = c[i];
+  for (int i = 0; i < BM; ++i)
+#pragma unroll
+    for (int j = 0; j < BN; ++j)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const int row = wm * 32 * BM + i * 32 + dm_of(q, lane);
+        const int col = wn * 32 * BN + j * 32 + (lane & 31);
+        ot[row * OSTR + col] = c[i][j][q];
+      }
+}
+
+// The body on every chunk of the staged tile.
+template <int BM, int BN>
+__device__ __forceinline__ void epilogue_tile(KW* W, const float* ot, int64_t m0, int64_t n0, int64_t M, int64_t N,
+                                              int tid) {
+  constexpr int TM = 64 * BM, TN = 64 * BN, OSTR = TN + MM_OPAD;
+  constexpr int LPR = TN / 8;         // lanes per tile row
+  constexpr int RPP = 256 / LPR;      // rows per pass
+  Chunk C;
+  C.m0 = m0;
+  C.n0 = n0;
+  C.c8 = (tid % LPR) * 8;
+#pragma nounroll
+  for (int p = 0; p < TM / RPP; ++p) {
+    C.r = p * RPP + tid / LPR;
+    C.ok = (m0 + C.r < M) & (n0 + C.c8 < N);
+    const float* src = ot + C.r * OSTR + C.c8;
+    T8 t0;
+    const float4 x = *(const float4*)src, y = *(const float4*)(src + 4);
+    t0.v[0] = x.x; t0.v[1] = x.y; t0.v[2] = x.z; t0.v[3] = x.w;
+    t0.v[4] = y.x; t0.v[5] = y.y; t0.v[6] = y.z; t0.v[7] = y.w;
+    run_epilogue(W, t0, C);
+  }
+}
+
+// Linear tile v -> (row tile, column tile): groups of GM row tiles, walked
+// column by column inside a group, so that consecutive tiles share A panels
+// and B panels.
+constexpr uint32_t GM = 8;
+
+__device__ __forceinline__ void tile_rc(uint32_t v, uint32_t nrt, uint32_t nct, uint32_t& ir, uint32_t& ic) {
+  const uint32_t per = GM * nct;
+  const uint32_t g = v / per, w = v - g * per;
+  const uint32_t r0 = g * GM;
+  const uint32_t gm = nrt - r0 < GM ? nrt - r0 : GM;
+  ir = r0 + w % gm;
+  ic = w / gm;
+}
+
+// Workgroups are dealt round-robin over the eight XCDs (each with its own
+// L2).  Slot of workgroup b: the workgroups of one XCD get consecutive
+// slots, so the tiles that run together on an XCD are consecutive in the
+// grouped order; the tail beyond a multiple of eight keeps its index.
+__device__ __forceinline__ uint32_t xcd_slot(uint32_t b, uint32_t G) {
+  const uint32_t G8 = G & ~7u;
+  return b < G8 ? (b & 7u) * (G8 >> 3) + (b >> 3) : b;
 }
 
 template <int BM, int BN>
 __device__ __forceinline__ void mix_body(char* lds) {
   using CF = Cfg<BM, BN>;
+  constexpr int D = MM_STAGES - 1;  // stages in flight ahead of the one multiplied
   KW* W = (KW*)__builtin_amdgcn_kernarg_segment_ptr();
   const uint32_t block_dim = W[H_BLOCK_DIM];
-  const uint32_t body_tile = W[H_BODY_TILE];
   const uint32_t nct = W[H_NC];
+  const uint32_t nrt = block_dim / nct;
   const int64_t M = (int64_t)w64(W, H_R_LO);
   const int64_t N = (int64_t)w64(W, H_C_LO);
   const int K = (int)W[H_MM_K];
@@ -391,53 +530,40 @@ __device__ __forceinline__ void mix_body(char* lds) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int wm = wave >> 1, wn = wave & 1;
   const int n_stage = (K + KT - 1) / KT;
-  char* const abuf0 = lds;
-  char* const bbuf0 = lds + 2 * CF::A_BYTES;
+  const uint32_t ring = (uint32_t)(uintptr_t)(lds_void*)lds;
+  const uint32_t G = gridDim.x;
 
-  const uint32_t t_begin = blockIdx.x * body_tile;
-  uint32_t t_end = t_begin + body_tile;
-  if (t_end > block_dim) t_end = block_dim;
-
-  for (uint32_t tile = t_begin; tile < t_end; ++tile) {
-    const uint32_t ir = tile / nct, ic = tile - ir * nct;
-    const int64_t m0 = (int64_t)ir * CF::TM, n0 = (int64_t)ic * CF::TN;
-    const Rsrc ra = rsrc_at(A, m0 * A.sr * 2);
-    const Rsrc rb = rsrc_at(Bm, n0 * 2);
+  for (uint32_t v = xcd_slot(blockIdx.x, G); v < block_dim; v += G) {
+    uint32_t ir, ic;
+    tile_rc(v, nrt, nct, ir, ic);
+    Panels P;
+    P.m0 = (int64_t)ir * CF::TM;
+    P.n0 = (int64_t)ic * CF::TN;
+    P.ra = rsrc_words(A, P.m0 * A.sr * 2);
+    P.rb = rsrc_words(Bm, P.n0 * 2);
     f16v c[BM][BN];
 #pragma unroll
     for (int i = 0; i < BM; ++i)
 #pragma unroll
       for (int j = 0; j < BN; ++j) c[i][j] = (f16v)0.f;
 
-    Stage<CF> st;
-    load_stage<CF>(st, ra, rb, A, Bm, m0, n0, 0, M, N, K, tid);
-    write_stage<CF>(st, abuf0, bbuf0, tid);
-    lds_barrier();
-    for (int s = 0; s < n_stage; ++s) {
-      const int cur = s & 1;
-      const bool more = s + 1 < n_stage;
-      if (more) load_stage<CF>(st, ra, rb, A, Bm, m0, n0, (s + 1) * KT, M, N, K, tid);
-      mma_stage<BM, BN>(c, abuf0 + cur * CF::A_BYTES, bbuf0 + cur * CF::B_BYTES, wm, wn, lane);
-      if (more) write_stage<CF>(st, abuf0 + (cur ^ 1) * CF::A_BYTES, bbuf0 + (cur ^ 1) * CF::B_BYTES, tid);
-      lds_barrier();
-    }
-
-    // epilogue per 32 x 32 block
-    Blk B;
-    B.M = M;
-    B.N = N;
-    B.lane = lane;
-#pragma nounroll
-    for (int blk = 0; blk < BM * BN; ++blk) {
-      const int bi = blk / BN, bj = blk % BN;
-      B.mb = m0 + wm * 32 * BM + bi * 32;
-      B.nb = n0 + wn * 32 * BN + bj * 32;
-      T16 t0;
 #pragma unroll
-      for (int q = 0; q < BM * BN; ++q)
-        if (q == blk) to16(t0, c[q / BN][q % BN]);
-      run_epilogue(W, t0, B);
+    for (int s = 0; s < D; ++s)
+      if (s < n_stage) issue_stage<CF>(ring, s, s, P, A, Bm, M, N, K, wave, lane);
+    for (int s = 0; s < n_stage; ++s) {
+      // this lane's loads of stage s have landed; after the barrier so have
+      // every lane's, and every wave is done with the slot refilled next
+      if (s + D <= n_stage) wait_dma<(D - 1) * CF::Q>();
+      else wait_dma<0>();
+      lds_barrier();
+      if (s + D < n_stage) issue_stage<CF>(ring, (s + D) % MM_STAGES, s + D, P, A, Bm, M, N, K, wave, lane);
+      mma_stage<CF, BM, BN>(c, lds + (s % MM_STAGES) * CF::STAGE, wm, wn, lane);
     }
+    lds_barrier();
+    acc_to_lds<BM, BN>(c, (float*)lds, wm, wn, lane);
+    lds_barrier();
+    epilogue_tile<BM, BN>(W, (const float*)lds, P.m0, P.n0, M, N, tid);
+    lds_barrier();
   }
 }
 
