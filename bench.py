@@ -313,7 +313,11 @@ MFMA_PEAK_TFLOPS = 2500.0
 
 
 def _event_time(stream, fn, reps):
+    """Device time per call of fn (seconds), HIP events on `stream`, after one
+    untimed call (library set-up, allocator growth)."""
     import torch
+    fn()
+    torch.cuda.synchronize()
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     a.record(stream)
     for _ in range(reps):

@@ -92,8 +92,8 @@ enum Hdr : int {
 // stages, each holding tm x MM_KT of A and MM_KT x tn of B (bf16).  After
 // the K loop the fp32 output tile is staged in LDS with rows of tn + MM_OPAD
 // values; the ring and the staged tile share the same bytes.
-constexpr int MM_KT = 32;
-constexpr int MM_STAGES = 4;
+constexpr int MM_KT = 64;
+constexpr int MM_STAGES = 2;
 constexpr int MM_OPAD = 8;
 __host__ __device__ constexpr int mm_lds_bytes(int tm, int tn) {
   return MM_STAGES * (tm + tn) * MM_KT * 2 > tm * (tn + MM_OPAD) * 4 ? MM_STAGES * (tm + tn) * MM_KT * 2
