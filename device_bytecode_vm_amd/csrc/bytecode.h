@@ -176,22 +176,22 @@ enum Handler : uint32_t {
                      //   B (op) ACC (pow, division by a register and memory operands
                      //   have handlers of their own)
   HD_RED = 118,      // + 3 kind + a: row reduce of treg[a] into rreg[dst] (rows inside a wave)
-  HD_REDX = 124,     // + 3 kind + a: OP_REDX (rows across waves)
-  HD_ALL = 130,      // + 3 kind + a: reduce-all partial of treg[a] into LDS buffer b
-  HD_ALL_FIN = 136,  // + kind
-  HD_BCAST = 138,    // + d
-  HD_RBIN = 141,
-  HD_RUN = 142,
-  HD_SYNC = 143,
-  HD_LD_ROW = 144,
-  HD_ST_ROW = 145,
-  HD_DBG = 146,
-  HD_LDS_INV = 147,
-  HD_PF = 148,
-  HD_BIN_POW = 149,  // ACC <- ACC pow B (or B pow ACC), B of forms 0..3 (from bk, b)
-  HD_BIN_MEM = 150,  // ACC <- ACC (op) B for a memory operand, any ALU op (sub, FL_REV)
-  HD_DIV_T = 151,    // ACC <- ACC / treg[b] (or treg[b] / ACC)
-  HD_COUNT = 152
+  HD_REDX = 127,     // + 3 kind + a: OP_REDX (rows across waves)
+  HD_ALL = 136,      // + 3 kind + a: reduce-all partial of treg[a] into LDS buffer b (sum, max)
+  HD_ALL_FIN = 142,  // + kind
+  HD_BCAST = 144,    // + d
+  HD_RBIN = 147,
+  HD_RUN = 148,
+  HD_SYNC = 149,
+  HD_LD_ROW = 150,
+  HD_ST_ROW = 151,
+  HD_DBG = 152,
+  HD_LDS_INV = 153,
+  HD_PF = 154,
+  HD_BIN_POW = 155,  // ACC <- ACC pow B (or B pow ACC), B of forms 0..3 (from bk, b)
+  HD_BIN_MEM = 156,  // ACC <- ACC (op) B for a memory operand, any ALU op (sub, FL_REV)
+  HD_DIV_T = 157,    // ACC <- ACC / treg[b] (or treg[b] / ACC)
+  HD_COUNT = 158
 };
 enum BinForm : uint32_t { BF_T0 = 0, BF_T1 = 1, BF_T2 = 2, BF_SCALAR = 3, BF_MEM = 4, BF_REV = 5 };
 
@@ -204,7 +204,9 @@ enum Una : uint32_t {
   UN_NEG = 7, UN_RECIP = 8, UN_TOBF16 = 9, UN_IDENT = 10,
 };
 enum BKind : uint32_t { BK_TREG = 0, BK_RREG = 1, BK_IMM = 2, BK_MEM = 3 };  // BK_MEM: B loaded from arg[w1]
-enum RedKind : uint32_t { RK_SUM = 0, RK_MAX = 1 };
+// RK_SUMSQ: sum of the squares of treg[a] (a reduce of x * x whose product is
+// not needed otherwise; row reduces only).
+enum RedKind : uint32_t { RK_SUM = 0, RK_MAX = 1, RK_SUMSQ = 2 };
 
 // Word 0 fields.
 __host__ __device__ constexpr uint32_t enc0(uint32_t op, uint32_t dst, uint32_t a, uint32_t b,

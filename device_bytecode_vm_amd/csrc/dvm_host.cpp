@@ -1088,12 +1088,26 @@ struct Encoder {
     return DVM_OK;
   }
 
-  dvm_status reduce_op(int i) {
+  // A reduce_sum at op i whose input is mul(a, a) at op i - 1, an f32 tile
+  // value read by nothing else: one sum-of-squares reduce of a.
+  bool sumsq_pair(size_t i) const {
+    if (i + 1 >= ops.size()) return false;
+    const OpRec& m = ops[i];
+    const OpRec& r = ops[i + 1];
+    return m.op == DVM_OP_MUL && m.n_in == 2 && m.in[0] == m.in[1] && cls[m.out] == 1 && cls[m.in[0]] == 1 &&
+           g->vals[m.out].t.dtype == DVM_F32 && !store_it[m.out] && n_uses[m.out] == 1 &&
+           r.op == DVM_OP_REDUCE_SUM && r.axis != DVM_AXIS_ALL && r.n_in == 1 && r.in[0] == m.out;
+  }
+
+  // Row reduce (or reduce-all) of op i.  With src >= 0: a sum-of-squares
+  // reduce of tile value src, fusing the square at op i_sq.
+  dvm_status reduce_op(int i, int64_t src = -1, int i_sq = -1) {
     const OpRec& o = ops[i];
-    const uint32_t kind = o.op == DVM_OP_REDUCE_SUM ? RK_SUM : RK_MAX;
+    const uint32_t kind = src >= 0 ? RK_SUMSQ : o.op == DVM_OP_REDUCE_SUM ? RK_SUM : RK_MAX;
     int k;
-    dvm_status st = tile_src(o.in[0], i, &k);
+    dvm_status st = tile_src(src >= 0 ? src : o.in[0], i, &k);
     if (st != DVM_OK) return st;
+    if (i_sq >= 0) free_dead(i_sq);
     if (o.axis == DVM_AXIS_ALL) {
       const uint32_t buf = (uint32_t)(n_red++ % N_LDSBUF);
       emit(enc0(OP_ALL, 0, k, buf, kind, 0, 0), 0);
@@ -1481,9 +1495,16 @@ struct Encoder {
     for (size_t i = 0; i < ops.size(); ++i) {
       const OpRec& o = ops[i];
       dvm_status s;
-      if (is_reduce(o.op)) s = reduce_op((int)i);
-      else if (cls[o.out] == 2) s = row_op((int)i);
-      else s = tile_op((int)i);
+      if (sumsq_pair(i)) {
+        s = reduce_op((int)i + 1, o.in[0], (int)i);
+        ++i;
+      } else if (is_reduce(o.op)) {
+        s = reduce_op((int)i);
+      } else if (cls[o.out] == 2) {
+        s = row_op((int)i);
+      } else {
+        s = tile_op((int)i);
+      }
       if (s != DVM_OK) return s;
     }
     patch_waits();

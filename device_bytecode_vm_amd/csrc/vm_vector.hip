@@ -48,6 +48,16 @@ typedef __attribute__((address_space(3))) void lds_void;
 // Program words are read in place in the kernarg segment (constant address
 // space, scalar loads); the kernel never takes a copy of its argument.
 typedef const __attribute__((address_space(4))) uint32_t KW;
+typedef uint32_t u2w __attribute__((ext_vector_type(2)));
+typedef const __attribute__((address_space(4))) u2w KW2;
+
+// The two words of the instruction at word pc (even, so 8-byte aligned in the
+// kernarg segment) with one scalar load.
+__device__ __forceinline__ void fetch2(KW* W, uint32_t pc, uint32_t& a, uint32_t& b) {
+  const u2w v = *(KW2*)(W + pc);
+  a = v.x;
+  b = v.y;
+}
 
 constexpr int OOB = 0x7fffffff;                 // lane offset beyond any descriptor size
 constexpr int RSRC_W3 = 0x00020000;             // raw buffer, 32-bit data format
@@ -678,7 +688,7 @@ __device__ __forceinline__ void un_c(Ch& acc) {
 // ---------------------------------------------------------------------------
 template <uint32_t KIND>
 __device__ __forceinline__ float comb(float a, float b) {
-  if constexpr (KIND == RK_SUM) return a + b;
+  if constexpr (KIND == RK_SUM || KIND == RK_SUMSQ) return a + b;
   else return (a != a || b != b) ? a + b : fmaxf(a, b);
 }
 
@@ -720,22 +730,29 @@ __device__ __forceinline__ float tree8(V8 v) {
 }
 
 template <uint32_t KIND>
+__device__ __forceinline__ V8 lane_terms(const V8& v) {
+  if constexpr (KIND == RK_SUMSQ) return v * v;
+  else return v;
+}
+
+template <uint32_t KIND>
 __device__ __forceinline__ float lane_partial(const Ch& c, const Geo& G, const Tile& tl, const Lane& L) {
-  const float id = KIND == RK_SUM ? 0.f : -__builtin_huge_valf();
+  const float id = KIND == RK_MAX ? -__builtin_huge_valf() : 0.f;
   float p[NV_MAX];
   if (tile_full(tl)) {
 #pragma unroll
     for (int j = 0; j < NV_MAX; ++j) {
       const int ct = (j * G.g + L.lane) * VEC;
-      p[j] = lane_sel(L.rok & (ct < tl.tce), tree8<KIND>(c.c[j]), id);
+      p[j] = lane_sel(L.rok & (ct < tl.tce), tree8<KIND>(lane_terms<KIND>(c.c[j])), id);
     }
   } else {
 #pragma unroll
     for (int j = 0; j < NV_MAX; ++j) {
       const int ct = (j * G.g + L.lane) * VEC;
+      const V8 t = lane_terms<KIND>(c.c[j]);
       V8 m;
 #pragma unroll
-      for (int i = 0; i < VEC; ++i) m[i] = lane_sel(L.rok & (ct + i < tl.tce), c.c[j][i], id);
+      for (int i = 0; i < VEC; ++i) m[i] = lane_sel(L.rok & (ct + i < tl.tce), t[i], id);
       p[j] = tree8<KIND>(m);
     }
   }
@@ -852,7 +869,8 @@ dvm_vm_vector(const Program prog) {
   }
   // the next instruction's words, fetched one dispatch ahead (the encoder
   // leaves spare words after the body, so this never reads past the program)
-  uint32_t nw0 = W[pc], nw1 = W[pc + 1];
+  uint32_t nw0, nw1;
+  fetch2(W, pc, nw0, nw1);
 
   while (true) {
     if (pc >= pc_end) {
@@ -862,8 +880,7 @@ dvm_vm_vector(const Program prog) {
       tl = make_tile(G, tile);
       pc = W[H_BODY_BEGIN];
       pc_end = W[H_BODY_END];
-      nw0 = W[pc];
-      nw1 = W[pc + 1];
+      fetch2(W, pc, nw0, nw1);
       continue;
     }
     const uint32_t w0 = nw0, w1 = nw1;
@@ -874,8 +891,7 @@ dvm_vm_vector(const Program prog) {
     // copy of pc makes the fetch address depend on the current words.
     uint32_t pcn = pc;
     asm volatile("" : "+s"(pcn) : "s"(w0), "s"(w1));
-    nw0 = W[pcn];
-    nw1 = W[pcn + 1];
+    fetch2(W, pcn, nw0, nw1);
     // Lane coordinates are recomputed per instruction (a few ALU ops) rather
     // than kept live across the whole interpreter loop.
     int tidv = tid;
@@ -888,6 +904,17 @@ dvm_vm_vector(const Program prog) {
     S.tile = tile;
 
 #define ARG read_arg(W, w1)
+// Row-register instructions that follow run here, without going back
+// through the dispatch.
+#define ROW_RUN_TAIL()                                              \
+  while (pc < pc_end && (f_op(nw0) == HD_RBIN || f_op(nw0) == HD_RUN)) { \
+    const uint32_t a0 = nw0, a1 = nw1;                              \
+    pc += 2;                                                        \
+    uint32_t pcr = pc;                                              \
+    asm volatile("" : "+s"(pcr) : "s"(a0), "s"(a1));                \
+    fetch2(W, pcr, nw0, nw1);                                       \
+    row_op(R.rw, a0, a1);                                           \
+  }
 #define CASE_LD(d)                                                                                          \
   case HD_LD_PF16 + d: read_pf<DT_BF16>(treg<d>(R), w0, vmc_load(w0), ARG, G, tl, L, S); settle(treg<d>(R)); break; \
   case HD_LD_PF32 + d: read_pf<DT_F32>(treg<d>(R), w0, vmc_load(w0), ARG, G, tl, L, S); settle(treg<d>(R)); break;  \
@@ -903,15 +930,16 @@ dvm_vm_vector(const Program prog) {
   case HD_BIN + 10 * k + 5 * rev + BF_SCALAR: bin_cs<k, rev>(R.t0, SCALAR_B); break;
 #define CASE_BIN_COMM(k) CASE_BIN_DIR(k, false)
 #define CASE_BIN_NC(k) CASE_BIN_DIR(k, false) CASE_BIN_DIR(k, true)
-#define CASE_RED(kind, a)                                                                  \
+#define CASE_RED(kind, a) case HD_ALL + 3 * kind + a: CASE_RED_ROW(kind, a)
+#define CASE_RED_ROW(kind, a)                                                              \
   case HD_RED + 3 * kind + a:                                                              \
-  case HD_REDX + 3 * kind + a:                                                             \
-  case HD_ALL + 3 * kind + a: {                                                            \
+  case HD_REDX + 3 * kind + a: {                                                           \
     const uint32_t h = f_op(w0);                                                           \
     float acc = lane_partial<kind>(treg<a>(R), G, tl, L);                                  \
     if (h == HD_RED + 3 * kind + a) {                                                      \
       /* rows inside one wave: the group all-reduce leaves the row's value */              \
       rset(R.rw, f_dst(w0), group_reduce<kind>(acc, gs));                                  \
+      ROW_RUN_TAIL();                                                                      \
     } else {                                                                               \
       /* per-wave partial into LDS (after the 64-lane all-reduce every lane */             \
       /* holds it, so every lane stores it: no lane-dependent branch) */                   \
@@ -928,6 +956,7 @@ dvm_vm_vector(const Program prog) {
         float r = rb[0];                                                                   \
         for (int k = 1; k < nw; ++k) r = comb<kind>(r, rb[k]);                             \
         rset(R.rw, f_dst(w0), r);                                                          \
+        ROW_RUN_TAIL();                                                                    \
       }                                                                                    \
     }                                                                                      \
     break;                                                                                 \
@@ -1007,6 +1036,7 @@ dvm_vm_vector(const Program prog) {
       }
       CASE_RED(RK_SUM, 0) CASE_RED(RK_SUM, 1) CASE_RED(RK_SUM, 2)
       CASE_RED(RK_MAX, 0) CASE_RED(RK_MAX, 1) CASE_RED(RK_MAX, 2)
+      CASE_RED_ROW(RK_SUMSQ, 0) CASE_RED_ROW(RK_SUMSQ, 1) CASE_RED_ROW(RK_SUMSQ, 2)
       case HD_ALL_FIN + RK_SUM:
       case HD_ALL_FIN + RK_MAX: {
         // every lane combines the per-wave partials (LDS broadcast reads);
@@ -1031,25 +1061,11 @@ dvm_vm_vector(const Program prog) {
         asm volatile("" ::: "memory");
         break;
       case HD_RBIN:
-      case HD_RUN: {
-        // a run of row-register instructions executes here, without going
-        // back through the dispatch
-        uint32_t a0 = w0, a1 = w1;
-        while (true) {
-          row_op(R.rw, a0, a1);
-          if (pc >= pc_end) break;
-          const uint32_t h = f_op(nw0);
-          if (h != HD_RBIN && h != HD_RUN) break;
-          a0 = nw0;
-          a1 = nw1;
-          pc += 2;
-          uint32_t pcr = pc;
-          asm volatile("" : "+s"(pcr) : "s"(a0), "s"(a1));
-          nw0 = W[pcr];
-          nw1 = W[pcr + 1];
-        }
+      case HD_RUN:
+        // a run of row-register instructions executes here
+        row_op(R.rw, w0, w1);
+        ROW_RUN_TAIL();
         break;
-      }
       case HD_LD_ROW: {
         const ArgD a = ARG;
         const int es = esize(a.dt);
