@@ -987,7 +987,7 @@ struct Encoder {
       const uint32_t f = un_of(o);
       if (f != UN_IDENT) emit(enc0(OP_UN, 0, 0, 0, f, 0, 0), 0);
     } else {
-      uint32_t bk, bi = 0, w1 = 0, mflags = 0;
+      uint32_t bk, bi = 0, w1 = 0, mflags = 0, alu = alu_of(o.op);
       if (o.n_in == 1) {
         bk = BK_IMM;
         float s = o.scalar;
@@ -1000,6 +1000,16 @@ struct Encoder {
         if (r < 0) return fail(DVM_ERR_RESOURCE, "row registers exhausted at op %d", i);
         bk = BK_RREG;
         bi = (uint32_t)r;
+        // tile / row value: one reciprocal per row, then a multiply per element
+        // (in place when the row value dies here, else in a spare register)
+        if (o.op == DVM_OP_DIV && !rev) {
+          const int rr = live_after(b, i) ? free_rreg() : r;
+          if (rr >= 0) {
+            emit(enc0(OP_RUN, rr, r, 0, UN_RECIP, 0, 0), 0);
+            bi = (uint32_t)rr;
+            alu = ALU_MUL;
+          }
+        }
       } else if (tloc[b] >= 0) {
         bk = BK_TREG;
         bi = (uint32_t)tloc[b];
@@ -1017,7 +1027,7 @@ struct Encoder {
           mflags = src_flags(b, &bi);
         }
       }
-      emit(enc0(OP_BIN, 0, 0, bi, alu_of(o.op), bk, (rev ? FL_REV : 0) | mflags), w1);
+      emit(enc0(OP_BIN, 0, 0, bi, alu, bk, (rev ? FL_REV : 0) | mflags), w1);
       if (bk == BK_MEM) note_consume(mflags, bi, true);
     }
     free_dead(i);
