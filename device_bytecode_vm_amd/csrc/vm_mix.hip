@@ -99,8 +99,8 @@ __device__ __forceinline__ float alu_rt(uint32_t k, float x, float y) {
     case ALU_SUB: return x - y;
     case ALU_MUL: return x * y;
     case ALU_DIV: return x / y;
-    case ALU_MAX: return (x != x || y != y) ? x + y : fmaxf(x, y);
-    case ALU_MIN: return (x != x || y != y) ? x + y : fminf(x, y);
+    case ALU_MAX: return __builtin_elementwise_maximum(x, y);  // NaN-propagating
+    case ALU_MIN: return __builtin_elementwise_minimum(x, y);
     default: return powf(x, y);
   }
 }
@@ -110,7 +110,7 @@ __device__ __forceinline__ float una_rt(uint32_t f, float x) {
     case UN_SQRT: return sqrtf(x);
     case UN_ABS: return fabsf(x);
     case UN_LOG: return logf(x);
-    case UN_EXP: return expf(x);
+    case UN_EXP: return __expf(x);  // v_exp_f32 of x log2(e)
     case UN_ROUND: return rintf(x);
     case UN_FLOOR: return floorf(x);
     case UN_ISFINITE: return isfinite(x) ? 1.f : 0.f;

@@ -199,8 +199,9 @@ __device__ __forceinline__ float alu(float x, float y) {
   else if constexpr (OPK == ALU_SUB) return x - y;
   else if constexpr (OPK == ALU_MUL) return x * y;
   else if constexpr (OPK == ALU_DIV) return x / y;
-  else if constexpr (OPK == ALU_MAX) return (x != x || y != y) ? x + y : fmaxf(x, y);
-  else if constexpr (OPK == ALU_MIN) return (x != x || y != y) ? x + y : fminf(x, y);
+  // NaN-propagating (IEEE 754-2019 maximum / minimum: v_maximum3_f32 / v_minimum3_f32)
+  else if constexpr (OPK == ALU_MAX) return __builtin_elementwise_maximum(x, y);
+  else if constexpr (OPK == ALU_MIN) return __builtin_elementwise_minimum(x, y);
   else return powf(x, y);
 }
 
@@ -221,7 +222,7 @@ __device__ __forceinline__ float una(float x) {
   if constexpr (F == UN_SQRT) return sqrtf(x);
   else if constexpr (F == UN_ABS) return fabsf(x);
   else if constexpr (F == UN_LOG) return logf(x);
-  else if constexpr (F == UN_EXP) return expf(x);
+  else if constexpr (F == UN_EXP) return __expf(x);  // v_exp_f32 of x log2(e)
   else if constexpr (F == UN_ROUND) return rintf(x);
   else if constexpr (F == UN_FLOOR) return floorf(x);
   else if constexpr (F == UN_ISFINITE) return isfinite(x) ? 1.f : 0.f;
@@ -236,7 +237,7 @@ __device__ __forceinline__ float una_rt(uint32_t f, float x) {
     case UN_SQRT: return sqrtf(x);
     case UN_ABS: return fabsf(x);
     case UN_LOG: return logf(x);
-    case UN_EXP: return expf(x);
+    case UN_EXP: return __expf(x);
     case UN_ROUND: return rintf(x);
     case UN_FLOOR: return floorf(x);
     case UN_ISFINITE: return isfinite(x) ? 1.f : 0.f;
@@ -689,7 +690,7 @@ __device__ __forceinline__ void un_c(Ch& acc) {
 template <uint32_t KIND>
 __device__ __forceinline__ float comb(float a, float b) {
   if constexpr (KIND == RK_SUM || KIND == RK_SUMSQ) return a + b;
-  else return (a != a || b != b) ? a + b : fmaxf(a, b);
+  else return __builtin_elementwise_maximum(a, b);  // NaN-propagating
 }
 
 template <int CTRL>
