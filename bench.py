@@ -405,7 +405,7 @@ def ifelse_bench(args):
     import torch
     import device_bytecode_vm_amd as dvm
     import workloads as W
-    calls = args.calls or 64
+    calls = args.calls or 256
     shapes = W.ifelse_shapes(0)[:calls]
     coin = W.rng(0).random(calls) < 0.5
     nmax = max(r for r, _ in shapes)

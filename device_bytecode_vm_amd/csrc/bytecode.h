@@ -151,6 +151,8 @@ enum Op : uint32_t {
   OP_PF = 18,        // prologue: prefetch slot b <- arg[w1] for the first tile
   OP_REDX = 19,      // row reduce of treg[a] across waves: partial into LDS buffer b,
                      //   workgroup barrier, combine of the row's partials into rreg[dst]
+  OP_FMA_INV = 20,   // treg[0] <- treg[0] * inv[b] + inv[a] (a multiply by one tile-invariant
+                     //   operand followed by an add of another, in one rounding)
   OP_COUNT
 };
 
@@ -191,7 +193,8 @@ enum Handler : uint32_t {
   HD_BIN_POW = 155,  // ACC <- ACC pow B (or B pow ACC), B of forms 0..3 (from bk, b)
   HD_BIN_MEM = 156,  // ACC <- ACC (op) B for a memory operand, any ALU op (sub, FL_REV)
   HD_DIV_T = 157,    // ACC <- ACC / treg[b] (or treg[b] / ACC)
-  HD_COUNT = 158
+  HD_FMA_INV = 158,  // OP_FMA_INV
+  HD_COUNT = 159
 };
 enum BinForm : uint32_t { BF_T0 = 0, BF_T1 = 1, BF_T2 = 2, BF_SCALAR = 3, BF_MEM = 4, BF_REV = 5 };
 

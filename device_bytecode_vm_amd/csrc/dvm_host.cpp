@@ -1323,9 +1323,37 @@ struct Encoder {
       case OP_DBG: return HD_DBG;
       case OP_LDS_INV: return HD_LDS_INV;
       case OP_PF: return HD_PF;
+      case OP_FMA_INV: return HD_FMA_INV;
       default: return HD_END;
     }
   }
+  // ACC * inv[s1] followed by ACC + inv[s2] (both tile-invariant operands in
+  // LDS, an f32 product: no rounding step between them) -> one OP_FMA_INV.
+  // Invariant reads issue no vector-memory instructions, so the waits patched
+  // into the body stay valid.
+  static void fuse_scale_shift(std::vector<uint32_t>& v) {
+    std::vector<uint32_t> out;
+    out.reserve(v.size());
+    for (size_t q = 0; q < v.size(); q += 2) {
+      const uint32_t a0 = v[q];
+      if (q + 2 < v.size()) {
+        const uint32_t b0 = v[q + 2];
+        auto inv_bin = [](uint32_t w, uint32_t alu) {
+          return f_op(w) == OP_BIN && f_bk(w) == BK_MEM && (f_flags(w) & FL_INV) && f_sub(w) == alu;
+        };
+        if (inv_bin(a0, ALU_MUL) && inv_bin(b0, ALU_ADD)) {
+          out.push_back(enc0(OP_FMA_INV, 0, f_b(b0), f_b(a0), 0, 0, 0));
+          out.push_back(0);
+          q += 2;
+          continue;
+        }
+      }
+      out.push_back(a0);
+      out.push_back(v[q + 1]);
+    }
+    v.swap(out);
+  }
+
   void to_handlers(std::vector<uint32_t>& v) const {
     for (size_t q = 0; q < v.size(); q += 2) v[q] = (v[q] & ~0xffu) | handler_of(v[q], v[q + 1]);
   }
@@ -1518,6 +1546,7 @@ struct Encoder {
       if (s != DVM_OK) return s;
     }
     patch_waits();
+    fuse_scale_shift(body);
     // Sync at the end of the body when the next tile's first cross-wave
     // reduction could overwrite an LDS buffer some wave is still reading.
     if (cross_wave && n_red < 2) emit(enc0(OP_SYNC, 0, 0, 0, 0, 0, 0), 0);

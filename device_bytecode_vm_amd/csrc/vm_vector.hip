@@ -1020,6 +1020,20 @@ dvm_vm_vector(const Program prog) {
         pow_rot(R.t0, b, (f_flags(w0) & FL_REV) != 0);
         break;
       }
+      case HD_FMA_INV: {
+        // ACC * inv[b] + inv[a], one rounding
+        Ch sc, sh;
+        read_inv(sc, w0, G, L, S);
+        int stride;
+        const uint32_t k2 = f_a(w0) & 1u;
+        const int idx = inv_base(W, k2, G, L, &stride);
+        inv_read(sh, S.inv(k2), G, idx, stride);
+#pragma unroll
+        for (int j = 0; j < NV_MAX; ++j)
+#pragma unroll
+          for (int i = 0; i < VEC; ++i) R.t0.c[j][i] = __builtin_fmaf(R.t0.c[j][i], sc.c[j][i], sh.c[j][i]);
+        break;
+      }
       case HD_BIN_MEM: {
         Ch m;
         read_mem(m, w0, vmc_bin(w0), ARG, G, tl, L, S);
