@@ -231,3 +231,53 @@ def test_tilemap_bit_exact(dvm, ctx, tmpl, shape):
     et, ew = TL.element_tile_map(plan)
     assert np.array_equal(host64(tiles), et)
     assert np.array_equal(host64(wgs), ew)
+
+
+def _with_specials(rg, shape):
+    """N(0, 1) values with NaN, +inf, -inf and signed zeros sprinkled in."""
+    x = W.normal(rg, shape, 0, 1)
+    flat = x.reshape(-1)
+    k = max(1, flat.size // 50)
+    for v in (np.nan, np.inf, -np.inf, 0.0, -0.0):
+        flat[rg.choice(flat.size, size=k, replace=False)] = v
+    return x
+
+
+@pytest.mark.parametrize("op", ["max", "min"])
+def test_max_min_nan_propagation(dvm, ctx, op):
+    """Binary max/min propagate NaN (IEEE 754-2019 maximum/minimum), as the
+    oracle's; values compared exactly, NaN positions included."""
+    say("binary", op, "nan")
+    rg = np.random.default_rng(5)
+    a = _with_specials(rg, (77, 1031))
+    b = _with_specials(rg, (77, 1031))
+    out = empty_dev(a.shape, "f32")
+    g = dvm.Graph(ctx)
+    g.op(op, g.input(torch_dev(a, "f32")), g.input(torch_dev(b, "f32")), out=out, live=True)
+    g.sync()
+    ref = O.maximum(a, b) if op == "max" else O.minimum(a, b)
+    got = host64(out)
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+    ok = ~np.isnan(ref)
+    assert np.array_equal(got[ok], ref[ok])
+
+
+def test_row_max_nan_propagation(dvm, ctx):
+    """A row max (rows inside one wave and rows across waves) is NaN exactly
+    where the row holds a NaN, else the row's largest value."""
+    for shape in [(61, 300), (9, 5120)]:
+        say("row_max", "nan", shape)
+        rg = np.random.default_rng(shape[1])
+        x = W.normal(rg, shape, 0, 1)
+        x[3, 7] = np.nan
+        x[5, shape[1] - 1] = np.nan
+        x[6, 0] = np.inf
+        m = empty_dev((shape[0], 1), "f32")
+        g = dvm.Graph(ctx)
+        g.op("reduce_max", g.input(torch_dev(x, "f32")), out=m, live=True)
+        g.sync()
+        ref = O.reduce_max(x)
+        got = host64(m)
+        assert np.array_equal(np.isnan(got), np.isnan(ref))
+        ok = ~np.isnan(ref)
+        assert np.array_equal(got[ok], ref[ok])
