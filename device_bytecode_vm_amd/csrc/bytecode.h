@@ -151,8 +151,9 @@ enum Op : uint32_t {
   OP_PF = 18,        // prologue: prefetch slot b <- arg[w1] for the first tile
   OP_REDX = 19,      // row reduce of treg[a] across waves: partial into LDS buffer b,
                      //   workgroup barrier, combine of the row's partials into rreg[dst]
-  OP_FMA_INV = 20,   // treg[0] <- treg[0] * inv[b] + inv[a] (a multiply by one tile-invariant
-                     //   operand followed by an add of another, in one rounding)
+  OP_FMA_INV = 20,   // treg[0] <- (treg[0] * r) * inv[b] + inv[a]: a multiply by one tile-
+                     //   invariant operand and an add of another in one rounding, r =
+                     //   rreg[dst] if bk == BK_RREG (a row scale applied first) else 1
   OP_COUNT
 };
 

@@ -1328,7 +1328,8 @@ struct Encoder {
     }
   }
   // ACC * inv[s1] followed by ACC + inv[s2] (both tile-invariant operands in
-  // LDS, an f32 product: no rounding step between them) -> one OP_FMA_INV.
+  // LDS, an f32 product: no rounding step between them) -> one OP_FMA_INV,
+  // with a preceding ACC * row register folded in as its row scale.
   // Invariant reads issue no vector-memory instructions, so the waits patched
   // into the body stay valid.
   static void fuse_scale_shift(std::vector<uint32_t>& v) {
@@ -1342,7 +1343,15 @@ struct Encoder {
           return f_op(w) == OP_BIN && f_bk(w) == BK_MEM && (f_flags(w) & FL_INV) && f_sub(w) == alu;
         };
         if (inv_bin(a0, ALU_MUL) && inv_bin(b0, ALU_ADD)) {
-          out.push_back(enc0(OP_FMA_INV, 0, f_b(b0), f_b(a0), 0, 0, 0));
+          // a multiply by a row register just before folds in as well
+          uint32_t rscale = 0, bk = 0;
+          const size_t n = out.size();
+          if (n >= 2 && f_op(out[n - 2]) == OP_BIN && f_bk(out[n - 2]) == BK_RREG && f_sub(out[n - 2]) == ALU_MUL) {
+            rscale = f_b(out[n - 2]);
+            bk = BK_RREG;
+            out.resize(n - 2);
+          }
+          out.push_back(enc0(OP_FMA_INV, rscale, f_b(b0), f_b(a0), 0, bk, 0));
           out.push_back(0);
           q += 2;
           continue;

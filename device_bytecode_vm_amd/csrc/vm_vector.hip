@@ -1021,7 +1021,8 @@ dvm_vm_vector(const Program prog) {
         break;
       }
       case HD_FMA_INV: {
-        // ACC * inv[b] + inv[a], one rounding
+        // (ACC * r) * inv[b] + inv[a], the last two in one rounding
+        const float r = f_bk(w0) == BK_RREG ? rget(R.rw, f_dst(w0)) : 1.f;
         Ch sc, sh;
         read_inv(sc, w0, G, L, S);
         int stride;
@@ -1031,7 +1032,7 @@ dvm_vm_vector(const Program prog) {
 #pragma unroll
         for (int j = 0; j < NV_MAX; ++j)
 #pragma unroll
-          for (int i = 0; i < VEC; ++i) R.t0.c[j][i] = __builtin_fmaf(R.t0.c[j][i], sc.c[j][i], sh.c[j][i]);
+          for (int i = 0; i < VEC; ++i) R.t0.c[j][i] = __builtin_fmaf(R.t0.c[j][i] * r, sc.c[j][i], sh.c[j][i]);
         break;
       }
       case HD_BIN_MEM: {
