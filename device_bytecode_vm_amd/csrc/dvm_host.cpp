@@ -45,6 +45,12 @@ int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // ===========================================================================
 // Shapes
 // ===========================================================================
+static int64_t numel_of(const dvm_tensor& t) {
+  int64_t n = 1;
+  for (int i = 0; i < t.ndim; ++i) n *= t.shape[i];
+  return n;
+}
+
 struct Shape {
   int nd = 0;
   int64_t d[4] = {0, 0, 0, 0};
@@ -1378,7 +1384,8 @@ struct Encoder {
     for (auto& o : ops) {
       const Val& v = g->vals[o.out];
       if (v.live || !v.released) {
-        if (!v.t.data) return fail(DVM_ERR_INVALID_ARG, "a value without storage escapes its graph");
+        // (an empty value needs no storage: nothing is stored)
+        if (!v.t.data && numel_of(v.t) > 0) return fail(DVM_ERR_INVALID_ARG, "a value without storage escapes its graph");
         stored.push_back(o.out);
         store_it[o.out] = 1;
       }
@@ -1487,7 +1494,8 @@ struct Encoder {
     for (auto& o : ops) {
       const Val& v = g->vals[o.out];
       if (v.live || !v.released) {
-        if (!v.t.data) return fail(DVM_ERR_INVALID_ARG, "a value without storage escapes its graph");
+        // (an empty value needs no storage: nothing is stored)
+        if (!v.t.data && numel_of(v.t) > 0) return fail(DVM_ERR_INVALID_ARG, "a value without storage escapes its graph");
         if (!is_reduce_all(o)) stored.push_back(o.out);
         store_it[o.out] = 1;
       }
@@ -1885,9 +1893,11 @@ dvm_status dvm_graph_add_op(dvm_graph* g, int32_t op, const dvm_value* in, int32
     // along K (A) and N (B), 16-byte aligned rows, K and N multiples of 8
     const dvm_tensor& A = g->vals[r.in[0]].t;
     const dvm_tensor& B = g->vals[r.in[1]].t;
-    const bool ok = A.dtype == DVM_BF16 && B.dtype == DVM_BF16 && A.stride[1] == 1 && B.stride[1] == 1 &&
-                    A.shape[1] % 8 == 0 && B.shape[1] % 8 == 0 && A.stride[0] % 8 == 0 && B.stride[0] % 8 == 0 &&
-                    (uintptr_t)A.data % 16 == 0 && (uintptr_t)B.data % 16 == 0 &&
+    // (with K = 0 nothing of A or B is read: their layout does not matter)
+    const bool k0 = A.shape[1] == 0;
+    const bool ok = A.dtype == DVM_BF16 && B.dtype == DVM_BF16 && B.shape[1] % 8 == 0 &&
+                    (k0 || (A.stride[1] == 1 && B.stride[1] == 1 && A.shape[1] % 8 == 0 && A.stride[0] % 8 == 0 &&
+                            B.stride[0] % 8 == 0 && (uintptr_t)A.data % 16 == 0 && (uintptr_t)B.data % 16 == 0)) &&
                     (out->dtype == DVM_F32 || out->dtype == DVM_BF16);
     if (!ok) return fail(DVM_ERR_UNSUPPORTED, "matmul operands outside the MIX kernel's forms");
   }

@@ -281,3 +281,55 @@ def test_row_max_nan_propagation(dvm, ctx):
         assert np.array_equal(np.isnan(got), np.isnan(ref))
         ok = ~np.isnan(ref)
         assert np.array_equal(got[ok], ref[ok])
+
+
+def test_empty_inputs(dvm, ctx):
+    """Zero-size operands: nothing is launched for tile programs (outputs keep
+    their contents), a reduce-all of nothing is the reduction's identity, and
+    a MatMul with K = 0 is its epilogue on zeros."""
+    import torch
+    from device_bytecode_vm_amd import composites as CP
+    for shape in [(0, 5120), (5, 0), (0,)]:
+        say("empty elementwise", shape)
+        x = torch.zeros(shape, dtype=torch.float32, device="cuda")
+        out = torch.full(shape, 7.0, dtype=torch.float32, device="cuda")
+        g = dvm.Graph(ctx)
+        g.op("exp", g.input(x), out=out, live=True)
+        g.sync()
+        assert out.numel() == 0 or bool((out == 7.0).all())
+    say("empty layernorm")
+    x = torch.zeros((0, 5120), dtype=torch.bfloat16, device="cuda")
+    y = torch.empty_like(x)
+    gam = torch.ones(5120, device="cuda")
+    bet = torch.zeros(5120, device="cuda")
+    g = dvm.Graph(ctx)
+    CP.layer_norm(g, g.input(x), g.input(gam), g.input(bet), W.LN_EPS, out=y)
+    g.sync()
+    for op, ident in [("reduce_sum", 0.0), ("reduce_max", -np.inf)]:
+        say("empty reduce-all", op)
+        x = torch.zeros((0, 4096), dtype=torch.float32, device="cuda")
+        s = torch.full((), 7.0, dtype=torch.float32, device="cuda")
+        g = dvm.Graph(ctx)
+        g.op(op, g.input(x), out=s, live=True, axis=0x7FFFFFFF)
+        g.sync()
+        assert float(s.item()) == ident
+    say("matmul M = 0")
+    a = torch.zeros((0, 64), dtype=torch.bfloat16, device="cuda")
+    b = torch.zeros((64, 128), dtype=torch.bfloat16, device="cuda")
+    bias = torch.zeros(128, device="cuda")
+    y = torch.empty((0, 128), dtype=torch.bfloat16, device="cuda")
+    g = dvm.Graph(ctx)
+    CP.matmul_bias_silu(g, g.input(a), g.input(b), g.input(bias), out=y)
+    g.sync()
+    say("matmul K = 0")
+    bias_h = W.normal(np.random.default_rng(8), (136,), 0, 1)
+    a = torch.zeros((37, 0), dtype=torch.bfloat16, device="cuda")
+    b = torch.zeros((0, 136), dtype=torch.bfloat16, device="cuda")
+    y = empty_dev((37, 136), "bf16")
+    g = dvm.Graph(ctx)
+    CP.matmul_bias_silu(g, g.input(a), g.input(b), g.input(torch_dev(bias_h, "f32")), out=y)
+    g.sync()
+    torch.cuda.synchronize()
+    ref = O.matmul_bias_silu(np.zeros((37, 0)), np.zeros((0, 136)), bias_h)
+    ok, e = N.check_matmul(host64(y), ref)
+    assert ok, f"max rel err {e:.3g}"
