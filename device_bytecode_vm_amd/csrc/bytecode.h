@@ -120,9 +120,19 @@ constexpr uint32_t LDS_BUDGET = 76u * 1024u;
 // the VM makes to it.
 enum ArgW : int { A_PTR_LO = 0, A_PTR_HI = 1, A_DTYPE = 2, A_FLAGS = 3, A_SR_LO = 4, A_SR_HI = 5,
                   A_SC = 6, A_EXTENT = 7 };
-// The extent word holds min(extent, 2^31) - the VM addresses one tile through a
-// buffer resource with 32-bit lane offsets, so a tile must span < 2^31 bytes.
+// The operand's byte extent is 64-bit: bits [31:0] in word A_EXTENT, bits
+// [55:32] in bits [31:8] of word A_FLAGS (whose bits [7:0] hold the flags).
+// The VM addresses one tile through a buffer resource based at the tile with
+// 32-bit lane offsets, so a tile must span < EXTENT_CAP bytes; the resource's
+// record count is the extent left after the tile start, capped the same way.
 constexpr uint32_t EXTENT_CAP = 0x80000000u;
+__host__ __device__ constexpr uint32_t arg_flag_bits(uint32_t w_flags) { return w_flags & 0xffu; }
+__host__ __device__ constexpr uint64_t arg_extent(uint32_t w_flags, uint32_t w_extent) {
+  return ((uint64_t)(w_flags >> 8) << 32) | (uint64_t)w_extent;
+}
+__host__ __device__ constexpr uint32_t arg_flags_word(uint32_t flags, uint64_t extent) {
+  return (flags & 0xffu) | ((uint32_t)(extent >> 32) << 8);
+}
 enum DType : uint32_t { DT_F32 = 0, DT_BF16 = 1, DT_U8 = 2 };
 enum ArgFlag : uint32_t {
   AF_VEC = 1u,       // every chunk start is dword aligned: 128-bit path

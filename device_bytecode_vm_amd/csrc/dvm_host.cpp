@@ -795,12 +795,12 @@ struct Encoder {
     const int64_t al = 4;
     bool vec = sc == 1 && (int64_t)(p % al) == 0 && (plan.R <= 1 || ((sr * es) % al + al) % al == 0) &&
                (plan.n_c <= 1 || (plan.tc * es) % al == 0);
-    a[A_FLAGS] = vec ? AF_VEC : 0u;
+    const int64_t ext = extent_bytes(t);
+    a[A_FLAGS] = arg_flags_word(vec ? AF_VEC : 0u, (uint64_t)ext);
     a[A_SR_LO] = (uint32_t)(uint64_t)sr;
     a[A_SR_HI] = (uint32_t)((uint64_t)sr >> 32);
     a[A_SC] = (uint32_t)(int32_t)sc;
-    const int64_t ext = extent_bytes(t);
-    a[A_EXTENT] = (uint32_t)std::min<int64_t>(ext, EXTENT_CAP);
+    a[A_EXTENT] = (uint32_t)(uint64_t)ext;
     arg_of[slot] = i;
     return i;
   }
@@ -1415,11 +1415,11 @@ struct Encoder {
       a[A_PTR_LO] = (uint32_t)p;
       a[A_PTR_HI] = (uint32_t)(p >> 32);
       a[A_DTYPE] = (uint32_t)t.dtype;
-      a[A_FLAGS] = AF_VEC;
+      a[A_FLAGS] = arg_flags_word(AF_VEC, (uint64_t)extent_bytes(t));
       a[A_SR_LO] = (uint32_t)(uint64_t)t.stride[0];
       a[A_SR_HI] = (uint32_t)((uint64_t)t.stride[0] >> 32);
       a[A_SC] = (uint32_t)t.stride[1];
-      a[A_EXTENT] = (uint32_t)std::min<int64_t>(extent_bytes(t), EXTENT_CAP);
+      a[A_EXTENT] = (uint32_t)(uint64_t)extent_bytes(t);
     }
     n_args = 2;
     for (size_t q = 0; q < operands.size(); ++q) add_arg(operands[q], st[q].first, st[q].second);
@@ -1542,7 +1542,8 @@ struct Encoder {
       b[A_PTR_LO] = (uint32_t)q;
       b[A_PTR_HI] = (uint32_t)(q >> 32);
       b[A_DTYPE] = DT_F32;
-      b[A_EXTENT] = (uint32_t)std::min<size_t>(g->ctx->scratch_bytes, EXTENT_CAP);
+      b[A_FLAGS] = arg_flags_word(0, (uint64_t)g->ctx->scratch_bytes);
+      b[A_EXTENT] = (uint32_t)(uint64_t)g->ctx->scratch_bytes;
       W[H_ALL_SCRATCH] = (uint32_t)si;
       if (g->ctx->scratch && (size_t)(256 + 4 * plan.block_dim) > g->ctx->scratch_bytes)
         return fail(DVM_ERR_RESOURCE, "reduce-all needs %lld partials", (long long)plan.block_dim);
@@ -2015,12 +2016,12 @@ dvm_status dvm_program_debug_tilemap(const dvm_program* p, const dvm_tensor* til
     a[A_PTR_LO] = (uint32_t)ptr;
     a[A_PTR_HI] = (uint32_t)(ptr >> 32);
     a[A_DTYPE] = DT_F32;
-    a[A_FLAGS] = 0;
+    a[A_FLAGS] = arg_flags_word(0, (uint64_t)extent_bytes(*t));
     const int64_t sr = p->R > 1 ? p->C : 0;
     a[A_SR_LO] = (uint32_t)(uint64_t)sr;
     a[A_SR_HI] = (uint32_t)((uint64_t)sr >> 32);
     a[A_SC] = 1;
-    a[A_EXTENT] = (uint32_t)std::min<int64_t>(extent_bytes(*t), EXTENT_CAP);
+    a[A_EXTENT] = (uint32_t)(uint64_t)extent_bytes(*t);
     ++k;
   }
   const uint32_t base = ARG_BASE + n_args * ARG_WORDS;

@@ -57,7 +57,7 @@ struct ArgD {
   uint32_t dt, fl;
   int64_t sr;
   int32_t sc;
-  uint32_t extent;
+  uint64_t extent;
 };
 
 __device__ __forceinline__ uint64_t w64(KW* w, int lo) { return ((uint64_t)w[lo + 1] << 32) | (uint64_t)w[lo]; }
@@ -67,10 +67,10 @@ __device__ __forceinline__ ArgD read_arg(KW* W, uint32_t i) {
   ArgD d;
   d.p = reinterpret_cast<const char*>(w64(a, A_PTR_LO));
   d.dt = a[A_DTYPE];
-  d.fl = a[A_FLAGS];
+  d.fl = arg_flag_bits(a[A_FLAGS]);
   d.sr = (int64_t)w64(a, A_SR_LO);
   d.sc = (int32_t)a[A_SC];
-  d.extent = a[A_EXTENT];
+  d.extent = arg_extent(a[A_FLAGS], a[A_EXTENT]);
   return d;
 }
 

@@ -129,3 +129,30 @@ def test_matmul_bias_silu_full_size_sampled_rows(dvm, ctx):
     got = host64(y[torch.as_tensor(rows, device=y.device)])
     ok, e = N.check_matmul(got, ref)
     assert ok, f"max rel err {e:.3g}"
+
+
+def test_matmul_output_beyond_2gib(dvm, ctx):
+    """Y [65536, 17408] bf16 is 2.3 GB: rows past 2^31 bytes from its base are
+    stored through tile-based resources like the others.  K = 64 keeps the
+    run short; sampled rows (first, middle, last, around 2^31 bytes) are
+    checked against the oracle."""
+    import torch
+    from device_bytecode_vm_amd import composites as CP
+    m, k, n = 65536, 64, 17408
+    say("matmul_beyond_2gib", m, k, n)
+    a, b, bias = _inputs(13, m, k, n)
+    y = empty_dev((m, n), "bf16")
+    assert y.numel() * 2 > 2 ** 31
+    g = dvm.Graph(ctx)
+    CP.matmul_bias_silu(g, g.input(torch_dev(a, "bf16")), g.input(torch_dev(b, "bf16")),
+                        g.input(torch_dev(bias, "f32")), out=y)
+    g.sync()
+    torch.cuda.synchronize()
+    boundary = (2 ** 31) // (n * 2)
+    rows = np.array([0, 1, m // 2, boundary - 1, boundary, boundary + 1, m - 2, m - 1])
+    got = host64(y[torch.as_tensor(rows, device=y.device)])
+    ref = O.matmul_bias_silu(a[rows], b, bias)
+    ok, e = N.check_matmul(got, ref)
+    assert ok, f"max rel err {e:.3g}"
+    del y
+    torch.cuda.empty_cache()

@@ -333,3 +333,33 @@ def test_empty_inputs(dvm, ctx):
     ref = O.matmul_bias_silu(np.zeros((37, 0)), np.zeros((0, 136)), bias_h)
     ok, e = N.check_matmul(host64(y), ref)
     assert ok, f"max rel err {e:.3g}"
+
+
+def test_operand_beyond_2gib(dvm, ctx):
+    """One fp32 operand of 2.3 GB (offsets past 2^31 bytes from the base):
+    y = sqrt(x * x + 1) over [70001, 8200], rows near the start, the middle
+    and the end compared bit for bit with the fp32-emulating oracle."""
+    import torch
+    shape = (70001, 8200)
+    say("beyond_2gib", shape)
+    x = W.device_normal(shape, seed=17)
+    y = torch.empty_like(x)
+    g = dvm.Graph(ctx)
+    vx = g.input(x)
+    t = g.op("mul", vx, vx)
+    u = g.op("add", t, 1.0)
+    g.op("sqrt", u, out=y, live=True)
+    g.release(t, u)
+    g.sync()
+    torch.cuda.synchronize()
+    assert x.numel() * 4 > 2 ** 31
+    rows = np.array([0, 1, 2, 35000, 52000, 65500, shape[0] - 2, shape[0] - 1])
+    idx = torch.as_tensor(rows, device="cuda")
+    xs, ys = host64(x[idx]), host64(y[idx])
+    ops = [{"op": "mul", "in": ["x", "x"], "out": "t", "dtype": "f32"},
+           {"op": "add", "in": ["t", 1.0], "out": "u", "dtype": "f32"},
+           {"op": "sqrt", "in": ["u"], "out": "y", "dtype": "f32"}]
+    ref, _ = evaluate(ops, {"x": xs}, emulate_f32=True)
+    assert np.array_equal(ys, ref["y"]), f"{np.sum(ys != ref['y'])} mismatches"
+    del x, y
+    torch.cuda.empty_cache()
