@@ -363,3 +363,65 @@ def test_operand_beyond_2gib(dvm, ctx):
     assert np.array_equal(ys, ref["y"]), f"{np.sum(ys != ref['y'])} mismatches"
     del x, y
     torch.cuda.empty_cache()
+
+
+def test_views_elementwise(dvm, ctx):
+    """ViewLoad/ViewStore: transposed and column-sliced inputs (row stride !=
+    columns, misaligned base), row and column broadcasts, and a strided
+    output view; fp32 chains compared bit for bit with the fp32-emulating
+    oracle."""
+    import torch
+    rg = np.random.default_rng(21)
+    R, C = 301, 1027
+    xt_h = W.normal(rg, (C, R), 0, 1)            # stored [C, R]; used as its transpose
+    wide_h = W.normal(rg, (R, C + 9), 0, 1)      # used as wide[:, 5:5 + C]
+    row_h = W.normal(rg, (C,), 0, 1)             # broadcast along rows
+    col_h = W.normal(rg, (R, 1), 0, 1)           # broadcast along columns
+    xt = torch_dev(xt_h, "f32").t()
+    ws = torch_dev(wide_h, "f32")[:, 5:5 + C]
+    rowv, colv = torch_dev(row_h, "f32"), torch_dev(col_h, "f32")
+    assert not xt.is_contiguous() and not ws.is_contiguous()
+    big = torch.full((R, 2 * C), 7.0, dtype=torch.float32, device="cuda")
+    out = big[:, ::2]                            # strided store, the other columns untouched
+    say("views", R, C)
+    g = dvm.Graph(ctx)
+    t1 = g.op("add", g.input(xt), g.input(ws))
+    t2 = g.op("mul", t1, g.input(rowv))
+    g.op("sub", t2, g.input(colv), out=out, live=True)
+    g.release(t1, t2)
+    g.sync()
+    torch.cuda.synchronize()
+    ops = [{"op": "add", "in": ["a", "b"], "out": "t1", "dtype": "f32"},
+           {"op": "mul", "in": ["t1", "r"], "out": "t2", "dtype": "f32"},
+           {"op": "sub", "in": ["t2", "c"], "out": "y", "dtype": "f32"}]
+    ref, _ = evaluate(ops, {"a": xt_h.T, "b": wide_h[:, 5:5 + C], "r": row_h, "c": col_h}, emulate_f32=True)
+    got = host64(big)
+    assert np.array_equal(got[:, ::2], ref["y"])
+    assert np.all(got[:, 1::2] == 7.0)
+
+
+def test_views_layernorm_and_softmax(dvm, ctx):
+    """Row reductions over views: LayerNorm of a column slice (row stride
+    5200) and softmax over a transposed view (unit stride along rows)."""
+    import torch
+    from device_bytecode_vm_amd import composites as CP
+    say("view layernorm")
+    rg = np.random.default_rng(22)
+    x_wide = W.normal(rg, (45, 5200), 0, 1, "bf16")
+    gam, bet = W.layernorm_params(5120)
+    xv = torch_dev(x_wide, "bf16")[:, 40:40 + 5120]
+    out = empty_dev((45, 5120), "bf16")
+    g = dvm.Graph(ctx)
+    CP.layer_norm(g, g.input(xv), g.input(torch_dev(gam, "f32")), g.input(torch_dev(bet, "f32")), W.LN_EPS, out=out)
+    g.sync()
+    ok, d = N.check_bf16(host64(out), O.layer_norm(x_wide[:, 40:40 + 5120], gam, bet, W.LN_EPS))
+    assert ok, f"layernorm view: max ulp {d}"
+    say("view softmax")
+    s_h = W.normal(rg, (700, 33), 0, 1, "bf16")  # softmax over the 700 axis of its transpose
+    sv = torch_dev(s_h, "bf16").t()
+    out = empty_dev((33, 700), "bf16")
+    g = dvm.Graph(ctx)
+    CP.softmax(g, g.input(sv), out=out)
+    g.sync()
+    ok, d = N.check_bf16(host64(out), O.softmax(s_h.T))
+    assert ok, f"softmax view: max ulp {d}"
