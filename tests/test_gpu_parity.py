@@ -425,3 +425,102 @@ def test_views_layernorm_and_softmax(dvm, ctx):
     g.sync()
     ok, d = N.check_bf16(host64(out), O.softmax(s_h.T))
     assert ok, f"softmax view: max ulp {d}"
+
+
+def _specials_input(seed, shape, positive=False):
+    rg = np.random.default_rng(seed)
+    x = W.normal(rg, shape, 0, 3)
+    if positive:
+        x = np.abs(x) + 1e-3
+    flat = x.reshape(-1)
+    specials = [np.nan, np.inf, -np.inf, 0.0, -0.0, 0.5, -0.5, 1.5, 2.5, -2.5, 1e-30, -1e-30]
+    for i, v in enumerate(specials):
+        flat[(i * 7919) % flat.size] = v
+    return x
+
+
+def _same_specials(got, ref):
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+    fin = np.isfinite(ref)
+    assert np.array_equal(np.isinf(got), np.isinf(ref))
+    assert np.array_equal(got[np.isinf(ref)], ref[np.isinf(ref)])
+    return fin
+
+
+def _check(got, ref, exact):
+    fin = _same_specials(got, ref)
+    if exact:
+        assert np.array_equal(got[fin], ref[fin])
+    else:
+        scale = np.max(np.abs(ref[fin])) if fin.any() else 1.0
+        assert np.max(np.abs(got[fin] - ref[fin])) <= 1e-5 * scale
+
+
+UNARY_CASES = [("sqrt", True), ("abs", True), ("neg", True), ("round", True), ("floor", True),
+               ("recip", True), ("exp", False), ("log", False)]
+
+
+@pytest.mark.parametrize("op,exact", UNARY_CASES)
+def test_unary_ops(dvm, ctx, op, exact):
+    """Each unary instruction against the oracle on fp32 input with NaN, +-inf,
+    signed zeros, ties and tiny values; correctly rounded ops bit for bit."""
+    say("unary", op)
+    shape = (129, 1037)
+    x = _specials_input(31, shape)
+    if op == "exp":
+        # |x| <= 20 keeps max|ref| meaningful for the max-relative tolerance
+        x = np.clip(x, -20, 20)
+        x.reshape(-1)[5] = np.nan
+    out = empty_dev(shape, "f32")
+    g = dvm.Graph(ctx)
+    g.op(op, g.input(torch_dev(x, "f32")), out=out, live=True)
+    g.sync()
+    ref, _ = evaluate([{"op": op, "in": ["x"], "out": "y", "dtype": "f32"}], {"x": x}, emulate_f32=True)
+    _check(host64(out), ref["y"], exact)
+
+
+def test_isfinite_u8(dvm, ctx):
+    say("isfinite")
+    x = _specials_input(32, (33, 515))
+    out = empty_dev(x.shape, "u8")
+    g = dvm.Graph(ctx)
+    g.op("isfinite", g.input(torch_dev(x, "f32")), out=out, live=True)
+    g.sync()
+    assert np.array_equal(host64(out), O.isfinite(x).astype(np.float64))
+
+
+BINARY_CASES = [("add", True), ("sub", True), ("mul", True), ("div", True), ("max", True), ("min", True),
+                ("pow", False)]
+
+
+@pytest.mark.parametrize("op,exact", BINARY_CASES)
+def test_binary_ops(dvm, ctx, op, exact):
+    """Each binary instruction, tile (op) tile in both orders and with a
+    scalar on either side, against the oracle (fp32 emulation)."""
+    shape = (77, 1031)
+    a = _specials_input(41, shape, positive=(op == "pow"))
+    b = _specials_input(42, shape)
+    if op == "pow":
+        b = np.clip(b, -4, 4)
+        b.reshape(-1)[3] = np.nan
+    da, db = torch_dev(a, "f32"), torch_dev(b, "f32")
+    for form in ("tt", "tt_rev", "ts", "st"):
+        say("binary", op, form)
+        out = empty_dev(shape, "f32")
+        g = dvm.Graph(ctx)
+        va, vb = g.input(da), g.input(db)
+        if form == "tt":
+            g.op(op, va, vb, out=out, live=True)
+            ins = ["a", "b"]
+        elif form == "tt_rev":
+            g.op(op, vb, va, out=out, live=True)
+            ins = ["b", "a"]
+        elif form == "ts":
+            g.op(op, va, 1.75, out=out, live=True)
+            ins = ["a", 1.75]
+        else:
+            g.op(op, -0.625, va, out=out, live=True)
+            ins = [-0.625, "a"]
+        g.sync()
+        ref, _ = evaluate([{"op": op, "in": ins, "out": "y", "dtype": "f32"}], {"a": a, "b": b}, emulate_f32=True)
+        _check(host64(out), ref["y"], exact)
