@@ -144,3 +144,53 @@ def test_random_fused_graph(dvm, ctx, seed):
         scale = max(np.max(np.abs(r)), 1e-30)
         err = np.max(np.abs(got - r)) / scale
         assert err <= 1e-5, f"max rel err {err:.3g}"
+
+
+def build_mix_case(dvm, ctx, seed):
+    """A MatMul followed by a random elementwise epilogue (bias row, residual
+    tile, scalars, guarded division, exp, max/min)."""
+    rg = np.random.default_rng(1000 + seed)
+    M = int(rg.integers(1, 700))
+    K = 8 * int(rg.integers(1, 96))
+    N = 8 * int(rg.integers(1, 160))
+    ch = Chain(dvm, ctx, M, N)
+    a = ch.input("a", W.normal(rg, (M, K), 0, 0.1, "bf16"), "bf16")
+    b = ch.input("b", W.normal(rg, (K, N), 0, 0.1, "bf16"), "bf16")
+    others = [ch.input("bias", W.normal(rg, (N,), 0, 0.5), "f32"),
+              ch.input("res", W.normal(rg, (M, N), 0, 0.5, "bf16"), "bf16")]
+    cur, _ = ch.op("matmul", [a, b], (M, N))
+    for _ in range(int(rg.integers(1, 6))):
+        move = int(rg.integers(0, 4))
+        if move == 0:
+            other = others[int(rg.integers(0, 2))]
+            ins = [cur, other] if rg.random() < 0.5 else [other, cur]
+            cur, _ = ch.op(BIN[int(rg.integers(0, 5))], ins, (M, N))
+        elif move == 1:
+            s = float(np.round(rg.normal(0, 2), 3))
+            ins = [cur, s] if rg.random() < 0.5 else [s, cur]
+            cur, _ = ch.op(BIN[int(rg.integers(0, 5))], ins, (M, N))
+        elif move == 2:
+            t, _ = ch.op("abs", [cur], (M, N))
+            u, _ = ch.op("add", [t, 1.0], (M, N))
+            cur, _ = ch.op("div", [cur, u], (M, N))
+        else:
+            t, _ = ch.op("abs", [cur], (M, N))
+            u, _ = ch.op("neg", [t], (M, N))
+            cur, _ = ch.op("exp", [u], (M, N))
+    final_dtype = "bf16" if rg.random() < 0.5 else "f32"
+    y, yout = ch.op("copy" if final_dtype == "f32" else "cast", [cur], (M, N), dtype=final_dtype)
+    return ch, y, yout, final_dtype
+
+
+@pytest.mark.parametrize("seed", list(range(16)))
+def test_random_matmul_epilogue(dvm, ctx, seed):
+    import torch
+    ch, y, yout, dt = build_mix_case(dvm, ctx, seed)
+    print("CASE mix fuzz", seed, ch.R, ch.C, [o["op"] for o in ch.ops], dt, flush=True)
+    g = ch.g
+    g.release(*[ch.dev[o["out"]] for o in ch.ops if o["out"] != y])
+    g.sync()
+    torch.cuda.synchronize()
+    ref, _ = evaluate(ch.ops, ch.inputs)
+    ok, e = N.check_matmul(host64(yout), ref[y])
+    assert ok, f"max rel err {e:.3g}"
