@@ -664,11 +664,15 @@ __device__ __forceinline__ void mix_body(char* lds) {
     load_frag<CF>(f[0], lds, 0, wm, wn, lane);
     for (int s = 0; s < n_stage; ++s) {
       const char* st = lds + (s % CF::NS) * CF::STAGE;
+      // the two workgroups of a compute unit share its SIMDs: a wave in the
+      // middle of its matrix work issues ahead of one waiting at a stage edge
+      __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int kk = 0; kk + 1 < CF::SPS; ++kk) {
         load_frag<CF>(f[(kk + 1) & 1], st, kk + 1, wm, wn, lane);
         mma<CF>(c, f[kk & 1]);
       }
+      __builtin_amdgcn_s_setprio(0);
       if (s + 1 < n_stage) {
         if (s + CF::NS <= n_stage) wait_dma<(CF::NS - 2) * CF::Q>();
         else wait_dma<0>();
