@@ -1120,6 +1120,11 @@ dvm_vm_vector(const Program prog) {
         const int idx = inv_base(W, k, G, L, &stride);
         Ch tmp;
         load_any(tmp, ARG, G, tl, L, stride != T_LANES);
+        // every chunk's load has returned before the handler ends, the ones
+        // past nv (not written to LDS) included: a load left in flight would
+        // make later writes of its registers wait on the vector-memory
+        // counter, which also counts the prefetches
+        settle(tmp);
         inv_write(tmp, S.inv(k), G, idx, stride);
         break;
       }
