@@ -116,25 +116,31 @@ template <uint32_t DT>
 constexpr int esize_c() { return DT == DT_F32 ? 4 : DT == DT_BF16 ? 2 : 1; }
 __device__ __forceinline__ int esize(uint32_t dt) { return dt == DT_F32 ? 4 : dt == DT_BF16 ? 2 : 1; }
 
+// Byte offset of the tile's first element in the operand, and the bytes of
+// the operand from there on (capped): the size of the tile's descriptor.
+__device__ __forceinline__ int64_t tile_offset(const ArgD& a, const Tile& tl, int es) {
+  return (tl.r0 * a.sr + tl.c0 * (int64_t)a.sc) * es;
+}
+
+__device__ __forceinline__ int tile_records(const ArgD& a, const Tile& tl, int es) {
+  const int64_t left = (int64_t)a.extent - tile_offset(a, tl, es);
+  return left <= 0 ? 0 : (left >= (int64_t)EXTENT_CAP ? (int)(EXTENT_CAP - 1) : (int)left);
+}
+
 // Descriptor over the operand's part of the tile: base at the tile's first
 // element, size = bytes left in the tensor (capped).
 __device__ __forceinline__ Rsrc tile_rsrc(const ArgD& a, const Tile& tl, int es) {
-  const int64_t ob = (tl.r0 * a.sr + tl.c0 * (int64_t)a.sc) * es;
-  const int64_t left = (int64_t)a.extent - ob;
-  const int n = left <= 0 ? 0 : (left >= (int64_t)EXTENT_CAP ? (int)(EXTENT_CAP - 1) : (int)left);
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(a.p + ob), 0, n, RSRC_W3);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(a.p + tile_offset(a, tl, es)), 0,
+                                           tile_records(a, tl, es), RSRC_W3);
 }
 
 // The same descriptor as four scalar words (for inline assembly).
 __device__ __forceinline__ u4 tile_rsrc_words(const ArgD& a, const Tile& tl, int es) {
-  const int64_t ob = (tl.r0 * a.sr + tl.c0 * (int64_t)a.sc) * es;
-  const int64_t left = (int64_t)a.extent - ob;
-  const int n = left <= 0 ? 0 : (left >= (int64_t)EXTENT_CAP ? (int)(EXTENT_CAP - 1) : (int)left);
-  const uint64_t base = (uint64_t)(uintptr_t)(a.p + ob);
+  const uint64_t base = (uint64_t)(uintptr_t)(a.p + tile_offset(a, tl, es));
   u4 r;
   r.x = (uint32_t)base;
   r.y = (uint32_t)(base >> 32) & 0xffffu;  // stride 0
-  r.z = (uint32_t)n;
+  r.z = (uint32_t)tile_records(a, tl, es);
   r.w = (uint32_t)RSRC_W3;
   return r;
 }
@@ -286,11 +292,46 @@ __device__ __forceinline__ void settle(Ch& d) {
   }
 }
 
-// In a ragged tile (its columns do not end on a chunk boundary) the chunk
-// that holds a row's last column is moved element by element, so that no
-// access reaches past the row's end.  Each lane owns at most one such chunk;
-// its values and column are picked with selects over the chunks (constant
-// register indices: no indexed access into the tile register).
+// ---------------------------------------------------------------------------
+// Ragged tiles: the tile's columns do not end on a chunk boundary.
+//
+// Every row's last column lies in chunk q = (tce - 1) / VEC of its row, held
+// by lane q mod g of the row group, in chunk slot q / g.  tce and g are the
+// same on every lane, so that slot, that lane and the number of valid columns
+// in the chunk are wave-uniform: the per-element work on the row-end chunk
+// sits behind scalar branches and runs on one chunk, not on every slot.
+//
+// Reads take the row-end chunk with the same 128-bit access as the others
+// when those bytes lie inside the operand's extent: the bytes past the row's
+// end then belong to the next row or to the gap between rows, and their values
+// are never used (stores and reductions mask them).  Only where the tile's
+// last row ends within one chunk of the extent's end is the chunk completed
+// element by element.
+// ---------------------------------------------------------------------------
+struct Tail {
+  int slot;  // chunk slot holding every row's last column
+  int lane;  // lane, inside its row group, that holds it
+  int col;   // first column of that chunk
+  int r;     // valid columns in it (1..VEC-1)
+};
+
+__device__ __forceinline__ Tail tail_of(const Geo& G, const Tile& tl) {
+  static_assert(VEC == 8, "chunk index below divides by eight");
+  const int q = (tl.tce - 1) >> 3;
+  return {q >> G.lg, q & (G.g - 1), q * VEC, tl.tce & (VEC - 1)};
+}
+
+// Columns of the tile that whole-chunk reads may cover, for rows 0..rows-1
+// at row stride a.sr >= 0: up to the end of the row-end chunk when the last
+// row's copy of that chunk lies inside the extent (then every row's does),
+// else the whole chunks only.
+__device__ __forceinline__ int chunk_cols(const ArgD& a, const Tile& tl, int es, int rows) {
+  const int full = tl.tce & ~(VEC - 1);
+  if (full == tl.tce) return full;
+  const int64_t end = ((int64_t)(rows - 1) * a.sr + (full + VEC)) * es;
+  return end <= (int64_t)tile_records(a, tl, es) ? full + VEC : full;
+}
+
 template <uint32_t DT>
 __device__ __forceinline__ float load_elem(const Rsrc& rs, int off) {
   if constexpr (DT == DT_F32) return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, 0));
@@ -298,45 +339,70 @@ __device__ __forceinline__ float load_elem(const Rsrc& rs, int off) {
   else return (float)__builtin_amdgcn_raw_buffer_load_b8(rs, off, 0, 0);
 }
 
-template <uint32_t DT>
-__device__ __forceinline__ void store_elem(const Rsrc& rs, int off, float v) {
-  if constexpr (DT == DT_F32) __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), rs, off, 0, 0);
-  else if constexpr (DT == DT_BF16)
-    __builtin_amdgcn_raw_buffer_store_b16((uint16_t)(f2bf_pack(v, 0.f) & 0xffffu), rs, off, 0, 0);
-  else __builtin_amdgcn_raw_buffer_store_b8((uint8_t)v, rs, off, 0, 0);
-}
-
-// column of this lane's row-end chunk (or -1) and, per chunk, whether it is it
-__device__ __forceinline__ int tail_col(const Geo& G, const Tile& tl, const Lane& L, bool (&part)[NV_MAX]) {
-  int col = -1;
-#pragma unroll
-  for (int j = 0; j < NV_MAX; ++j) {
-    const int ct = (j * G.g + L.lane) * VEC;
-    part[j] = (ct < tl.tce) & (ct + VEC > tl.tce);
-    col = part[j] ? ct : col;
-  }
-  return col;
-}
-
+// Complete the row-end chunk element by element (for reads whose whole-chunk
+// accesses stopped short of it).
 template <uint32_t DT>
 __device__ __forceinline__ void load_tail(Ch& d, const Rsrc& rs, int roff, const Geo& G, const Tile& tl,
                                           const Lane& L, bool rok) {
   constexpr int ES = esize_c<DT>();
-  if (tile_full(tl)) return;
-  bool part[NV_MAX];
-  const int col = tail_col(G, tl, L, part);
+  const Tail T = tail_of(G, tl);
+  const bool mine = rok & (L.lane == T.lane);
   float v[VEC];
 #pragma unroll
-  for (int i = 0; i < VEC; ++i)
-    v[i] = load_elem<DT>(rs, lane_off(rok & (col >= 0) & (col + i < tl.tce), (roff + col + i) * ES));
+  for (int i = 0; i < VEC; ++i) v[i] = load_elem<DT>(rs, lane_off(mine & (i < T.r), (roff + T.col + i) * ES));
   // wait for these loads on this path: left pending, they would make the
   // compiler wait at the join for all outstanding vector memory (a prefetch
   // issued later included), also on the path that skips them
   asm volatile("" : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]), "+v"(v[4]), "+v"(v[5]), "+v"(v[6]), "+v"(v[7]));
 #pragma unroll
   for (int j = 0; j < NV_MAX; ++j)
+    if (j == T.slot)
 #pragma unroll
-    for (int i = 0; i < VEC; ++i) d.c[j][i] = lane_sel(part[j], v[i], d.c[j][i]);
+      for (int i = 0; i < VEC; ++i) d.c[j][i] = lane_sel(mine, v[i], d.c[j][i]);
+}
+
+// Store the first r (1..VEC-1) values of chunk x at byte offset off as pieces
+// of four, two and one elements.
+template <uint32_t DT>
+__device__ __forceinline__ void store_part(const V8& x, const Rsrc& rs, int off, int r) {
+  constexpr int ES = esize_c<DT>();
+  // the two-element piece starts at element r&4, the one-element piece at r&6
+  const int o2 = off == OOB ? OOB : off + (r & 4) * ES;
+  const int o1 = off == OOB ? OOB : off + (r & 6) * ES;
+  const bool h4 = (r & 4) != 0, h2 = (r & 2) != 0;
+  const float y0 = h4 ? x[4] : x[0], y1 = h4 ? x[5] : x[1];
+  const float z = h4 ? (h2 ? x[6] : x[4]) : (h2 ? x[2] : x[0]);
+  if constexpr (DT == DT_F32) {
+    if (r & 4) {
+      u4 v;
+      v.x = __float_as_uint(x[0]); v.y = __float_as_uint(x[1]); v.z = __float_as_uint(x[2]); v.w = __float_as_uint(x[3]);
+      __builtin_amdgcn_raw_buffer_store_b128(v, rs, off, 0, 0);
+    }
+    if (r & 2) {
+      u2 v;
+      v.x = __float_as_uint(y0); v.y = __float_as_uint(y1);
+      __builtin_amdgcn_raw_buffer_store_b64(v, rs, o2, 0, 0);
+    }
+    if (r & 1) __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(z), rs, o1, 0, 0);
+  } else if constexpr (DT == DT_BF16) {
+    if (r & 4) {
+      u2 v;
+      v.x = f2bf_pack(x[0], x[1]); v.y = f2bf_pack(x[2], x[3]);
+      __builtin_amdgcn_raw_buffer_store_b64(v, rs, off, 0, 0);
+    }
+    if (r & 2) __builtin_amdgcn_raw_buffer_store_b32(f2bf_pack(y0, y1), rs, o2, 0, 0);
+    if (r & 1) __builtin_amdgcn_raw_buffer_store_b16((uint16_t)(f2bf_pack(z, 0.f) & 0xffffu), rs, o1, 0, 0);
+  } else {
+    if (r & 4) {
+      uint32_t v = 0u;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v |= ((uint32_t)x[i] & 0xffu) << (8 * i);
+      __builtin_amdgcn_raw_buffer_store_b32(v, rs, off, 0, 0);
+    }
+    if (r & 2)
+      __builtin_amdgcn_raw_buffer_store_b16((uint16_t)(((uint32_t)y0 & 0xffu) | (((uint32_t)y1 & 0xffu) << 8)), rs, o2, 0, 0);
+    if (r & 1) __builtin_amdgcn_raw_buffer_store_b8((uint8_t)z, rs, o1, 0, 0);
+  }
 }
 
 template <uint32_t DT>
@@ -344,15 +410,11 @@ __device__ __forceinline__ void store_tail(const Ch& s, const Rsrc& rs, int roff
                                            const Lane& L) {
   constexpr int ES = esize_c<DT>();
   if (tile_full(tl)) return;
-  bool part[NV_MAX];
-  const int col = tail_col(G, tl, L, part);
+  const Tail T = tail_of(G, tl);
+  const int off = lane_off(L.rok & (L.lane == T.lane), (roff + T.col) * ES);
 #pragma unroll
-  for (int i = 0; i < VEC; ++i) {
-    float v = s.c[0][i];
-#pragma unroll
-    for (int j = 1; j < NV_MAX; ++j) v = lane_sel(part[j], s.c[j][i], v);
-    store_elem<DT>(rs, lane_off(L.rok & (col >= 0) & (col + i < tl.tce), (roff + col + i) * ES), v);
-  }
+  for (int j = 0; j < NV_MAX; ++j)
+    if (j == T.slot) store_part<DT>(s.c[j], rs, off, T.r);
 }
 
 // ---------------------------------------------------------------------------
@@ -377,13 +439,14 @@ __device__ __forceinline__ void load_dir(Ch& d, const ArgD& a, const Geo& G, con
     else v = (float)__builtin_amdgcn_raw_buffer_load_b8(rs, off, 0, 0);
     fill(d, v);
   } else if ((a.fl & AF_VEC) && a.sc == 1) {
-    // dword-aligned chunks: 128-bit accesses for every chunk that lies wholly
-    // inside the row (the others are masked); in a ragged tile the one chunk
-    // per row that holds the row's end is completed element by element
+    // dword-aligned chunks: 128-bit accesses for every chunk inside the
+    // whole-chunk columns (the others are masked); a row-end chunk they do not
+    // cover is completed element by element
+    const int lim = chunk_cols(a, tl, ES, any_row ? (T_LANES >> G.lg) : tl.tre);
 #pragma unroll
     for (int j = 0; j < NV_MAX; ++j) {
       const int ct = (j * G.g + L.lane) * VEC;
-      const int off = lane_off(rok & (ct + VEC <= tl.tce), (roff + ct) * ES);
+      const int off = lane_off(rok & (ct + VEC <= lim), (roff + ct) * ES);
       if constexpr (DT == DT_F32) {
         const u4 v0 = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
         const u4 v1 = __builtin_amdgcn_raw_buffer_load_b128(rs, off == OOB ? OOB : off + 16, 0, 0);
@@ -399,7 +462,7 @@ __device__ __forceinline__ void load_dir(Ch& d, const ArgD& a, const Geo& G, con
         }
       }
     }
-    load_tail<DT>(d, rs, roff, G, tl, L, rok);
+    if (lim < tl.tce) load_tail<DT>(d, rs, roff, G, tl, L, rok);
   } else {
     // element path: unaligned or strided operands
 #pragma unroll
@@ -508,11 +571,12 @@ __device__ __forceinline__ void pf_issue(char* slot, const ArgD& a, const Geo& G
   const int roff = L.row * (int)a.sr;
   const int wave = L.tid >> 6;
   const uint32_t base = (uint32_t)(uintptr_t)(lds_void*)slot;
+  const int lim = chunk_cols(a, nt, ES, nt.tre);
 #pragma unroll
   for (int j = 0; j < NV_MAX; ++j) {
     if (j < G.nv) {
       const int ct = (j * G.g + L.lane) * VEC;
-      const int off = lane_off(rok & (ct + VEC <= nt.tce), (roff + ct) * ES);  // whole chunks only
+      const int off = lane_off(rok & (ct + VEC <= lim), (roff + ct) * ES);  // whole chunks only
 #pragma unroll
       for (int h = 0; h < HV; ++h) {
         const uint32_t dst = __builtin_amdgcn_readfirstlane(base + (uint32_t)(((j * HV + h) * T_LANES + wave * 64) * 16));
@@ -619,8 +683,10 @@ __device__ __forceinline__ void read_pf(Ch& d, uint32_t w0, uint32_t vmc, const 
   // prefetch (ragged tiles issue more), so the wait covers the prefetch.
   wait_vm(vmc);
   pf_read<DT>(d, S.pf(slot), G, L.tid);
-  // the prefetch moved whole chunks only: complete the row-end chunk
-  load_tail<DT>(d, tile_rsrc(a, tl, esize_c<DT>()), L.row * (int)a.sr, G, tl, L, L.rok);
+  // the prefetch moved whole chunks only: complete a row-end chunk they did
+  // not cover
+  if (chunk_cols(a, tl, esize_c<DT>(), tl.tre) < tl.tce)
+    load_tail<DT>(d, tile_rsrc(a, tl, esize_c<DT>()), L.row * (int)a.sr, G, tl, L, L.rok);
   if ((f_flags(w0) & FL_ISSUE) && S.tile + 1 < S.t_end) {
     const Tile nt = make_tile(G, S.tile + 1);
     // this lane's reads of the slot have completed before the refill starts
@@ -747,14 +813,20 @@ __device__ __forceinline__ float lane_partial(const Ch& c, const Geo& G, const T
       p[j] = lane_sel(L.rok & (ct < tl.tce), tree8<KIND>(lane_terms<KIND>(c.c[j])), id);
     }
   } else {
+    // only the row-end slot (wave-uniform) needs a mask per element
+    const int jt = tail_of(G, tl).slot;
 #pragma unroll
     for (int j = 0; j < NV_MAX; ++j) {
       const int ct = (j * G.g + L.lane) * VEC;
       const V8 t = lane_terms<KIND>(c.c[j]);
-      V8 m;
+      if (j == jt) {
+        V8 m;
 #pragma unroll
-      for (int i = 0; i < VEC; ++i) m[i] = lane_sel(L.rok & (ct + i < tl.tce), t[i], id);
-      p[j] = tree8<KIND>(m);
+        for (int i = 0; i < VEC; ++i) m[i] = lane_sel(L.rok & (ct + i < tl.tce), t[i], id);
+        p[j] = tree8<KIND>(m);
+      } else {
+        p[j] = lane_sel(L.rok & (ct < tl.tce), tree8<KIND>(t), id);
+      }
     }
   }
   static_assert(NV_MAX == 5, "chunk combine order below assumes five chunks");
