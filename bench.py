@@ -205,6 +205,7 @@ def layernorm_bench(args):
     hdr = progs[int(np.argmax([r for r, _ in shapes]))].header()
     tr = stored_traffic()
     traffic = tr["traffic_bytes_per_launch"] if tr else None
+    decode = decode_split(progs, stream)
 
     out = {
         "metric": METRIC, "value": round(e2e_gbs, 2), "unit": "GB/s", "n_gpus": 1,
@@ -226,10 +227,32 @@ def layernorm_bench(args):
                      "bytes_per_launch_avg": round(step_bytes / len(progs), 1)},
         "largest_call_header": {k: hdr[k] for k in ("block_dim", "body_tile", "grid", "tr", "tc", "g", "nv",
                                                     "n_instr")},
+        "decode_split": decode,
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = layernorm_cpu_baseline(args.cpu_seconds)
     return out
+
+
+def decode_split(progs, stream):
+    """One pass of the programs through the VM's profiling twin (outside the
+    timed region): the share of each workgroup's cycles spent decoding
+    (instruction fetch, field decode, dispatch), executing handlers and
+    changing tiles, summed over workgroups and programs."""
+    import torch
+    tot = np.zeros(5)
+    for p in progs:
+        n = p.PROF_COUNTERS * p.header()["grid"]
+        c = torch.zeros(max(n, 1), dtype=torch.int64, device="cuda")
+        p.launch_profiled(c, stream)
+        torch.cuda.synchronize()
+        tot += c.view(-1, p.PROF_COUNTERS).sum(0).cpu().numpy().astype(np.float64)
+    total = max(tot[0], 1.0)
+    return {"decode_frac": round(tot[1] / total, 4), "execute_frac": round(tot[2] / total, 4),
+            "tile_change_frac": round(tot[3] / total, 4),
+            "decode_cycles_per_dispatch": round(tot[1] / max(tot[4], 1.0), 1),
+            "execute_cycles_per_dispatch": round(tot[2] / max(tot[4], 1.0), 1),
+            "dispatches": int(tot[4]), "counter": "s_memtime, wave 0 of each workgroup, profiling twin kernel"}
 
 
 def layernorm_cpu_baseline(budget_s):
@@ -301,11 +324,28 @@ def sqrt_add_bench(args):
     e1.record(stream)
     torch.cuda.synchronize()
     kus = e0.elapsed_time(e1) / 200 * 1e3
+    # cold: a 512 MiB write between launches evicts the operands from L2 and
+    # the MALL; median over the launches
+    scratch = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    cold = []
+    for i in range(30):
+        scratch.fill_(i & 0xff)
+        c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        c0.record(stream)
+        p.launch(stream)
+        c1.record(stream)
+        torch.cuda.synchronize()
+        cold.append(c0.elapsed_time(c1) * 1e3)
+    del scratch
+    kus_cold = sorted(cold)[len(cold) // 2]
     return {"metric": METRIC, "value": round(nbytes / dt / 1e9, 2), "unit": "GB/s", "n_gpus": 1,
             "steps": n, "warmup": args.warmup, "ms_per_step": round(dt * 1e3, 4), "higher_is_better": True,
             "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
             "config": {"workload": "sqrt_add", "shape": [513, 1031]},
             "device_only_gbs": round(nbytes / (kus * 1e-6) / 1e9, 2), "kernel_us_warm": round(kus, 3),
+            "kernel_us_cold": round(kus_cold, 3),
+            "device_only_gbs_cold": round(nbytes / (kus_cold * 1e-6) / 1e9, 2),
+            "note": "one 6.3 MB graph is launch-latency bound: 70% of the HBM roofline is out of reach",
             "header": p.header()}
 
 

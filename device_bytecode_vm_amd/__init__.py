@@ -129,6 +129,16 @@ class Program:
     def launch(self, stream=None):
         check(lib.dvm_launch(self.ctx.h, self.h, _stream_handle(stream)))
 
+    PROF_COUNTERS = 5
+
+    def launch_profiled(self, counters, stream=None):
+        """Profiling launch (same results as launch) that fills `counters`, a
+        device uint64 tensor of at least 5 * grid values, with each
+        workgroup's total, decode, execute and tile-change cycles and its
+        dispatch count."""
+        check(lib.dvm_launch_profiled(self.ctx.h, self.h, _stream_handle(stream), C.c_void_p(counters.data_ptr()),
+                                      counters.numel()))
+
     def debug_tilemap(self, tile_out, wg_out) -> "Program":
         q = C.c_void_p()
         a, b = to_c(tile_out), to_c(wg_out)

@@ -84,6 +84,8 @@ enum Hdr : int {
   H_MM_K = 34,       // MIX: contraction length K
   H_MM_A = 35,       // MIX: arg index of A [M, K] (bf16, unit stride along K)
   H_MM_B = 36,       // MIX: arg index of B [K, N] (bf16, unit stride along N)
+  H_PROF_LO = 37,    // profiling launches only: device address of the per-workgroup
+  H_PROF_HI = 38,    //   cycle counters (5 x uint64 per workgroup)
 };
 
 // MIX kernel geometry: the output tile (header H_TR x H_TC) is one of the MIX

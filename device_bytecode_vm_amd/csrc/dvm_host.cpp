@@ -24,6 +24,7 @@ using namespace dvmbc;
 
 extern "C" hipError_t dvm_launch_vector_kernel(const Program* p, unsigned grid, hipStream_t s);
 extern "C" hipError_t dvm_launch_mix_kernel(const Program* p, unsigned grid, hipStream_t s);
+extern "C" hipError_t dvm_launch_vector_prof_kernel(const Program* p, unsigned grid, hipStream_t s);
 
 namespace {
 
@@ -1941,6 +1942,24 @@ dvm_status dvm_flush(dvm_graph* g, dvm_program** out) {
 dvm_status dvm_launch(dvm_context* ctx, const dvm_program* p, void* stream) {
   if (!ctx || !p) return fail(DVM_ERR_INVALID_ARG, "null argument");
   return launch(ctx, p, (hipStream_t)stream);
+}
+
+dvm_status dvm_launch_profiled(dvm_context* ctx, const dvm_program* p, void* stream, uint64_t* counters,
+                               size_t n_counters) {
+  if (!ctx || !p) return fail(DVM_ERR_INVALID_ARG, "null argument");
+  if (ctx->device < 0) return fail(DVM_ERR_DEVICE, "encode-only context cannot launch");
+  if (p->prog.w[H_KTYPE] != KT_VECTOR) return fail(DVM_ERR_UNSUPPORTED, "profiling covers VECTOR programs");
+  if (p->grid_launch == 0) return DVM_OK;
+  if (!counters) return fail(DVM_ERR_INVALID_ARG, "null counter buffer");
+  const size_t need = (size_t)DVM_PROF_COUNTERS * p->grid_launch;
+  if (n_counters < need) return fail(DVM_ERR_INVALID_ARG, "counter buffer holds %zu values, needs %zu", n_counters, need);
+  Program q = p->prog;  // the launch copies its argument: a stack copy is enough
+  const uint64_t a = (uint64_t)(uintptr_t)counters;
+  q.w[H_PROF_LO] = (uint32_t)a;
+  q.w[H_PROF_HI] = (uint32_t)(a >> 32);
+  hipError_t e = dvm_launch_vector_prof_kernel(&q, p->grid_launch, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(DVM_ERR_DEVICE, "launch failed: %s", hipGetErrorString(e));
+  return DVM_OK;
 }
 
 dvm_status dvm_graph_flush_launch(dvm_graph* g, int32_t* launched) {

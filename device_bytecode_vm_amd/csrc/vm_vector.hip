@@ -889,14 +889,19 @@ __device__ __forceinline__ Ch& treg(Regs& r) {
 // ---------------------------------------------------------------------------
 // The kernel
 // ---------------------------------------------------------------------------
-extern "C" __global__ void __launch_bounds__(T_LANES) __attribute__((amdgpu_waves_per_eu(2, 2)))
-dvm_vm_vector(const Program prog) {
-  __shared__ float s_red[N_LDSBUF][T_LANES / 64];
-  __shared__ int s_last;
-  extern __shared__ __attribute__((aligned(16))) char dlds[];
-
-  (void)prog;
+// The interpreter.  PROF = true builds the profiling twin: it reads the
+// cycle counter around every dispatch and splits the workgroup's time into
+// decode (instruction fetch, field decode and the dispatch to the handler),
+// execute (the handler, row-register runs inside it included) and tile
+// changes, written per workgroup at the end.  The product kernel is the
+// PROF = false instance, with no counter reads.
+template <bool PROF>
+__device__ __forceinline__ void vm_main(float (*s_red)[T_LANES / 64], int& s_last, char* dlds) {
   KW* W = (KW*)__builtin_amdgcn_kernarg_segment_ptr();
+  uint64_t p_start = 0, p_top = 0, p_ent = 0, p_dec = 0, p_exe = 0, p_tile = 0, p_n = 0;
+  if constexpr (PROF) p_start = __builtin_amdgcn_s_memtime();
+#define PROF_ENTER() \
+  if constexpr (PROF) p_ent = __builtin_amdgcn_s_memtime();
   const uint32_t block_dim = W[H_BLOCK_DIM];
   const uint32_t body_tile = W[H_BODY_TILE];
 
@@ -946,6 +951,7 @@ dvm_vm_vector(const Program prog) {
   fetch2(W, pc, nw0, nw1);
 
   while (true) {
+    if constexpr (PROF) p_top = __builtin_amdgcn_s_memtime();
     if (pc >= pc_end) {
       if (in_pro) in_pro = false;
       else ++tile;
@@ -954,6 +960,7 @@ dvm_vm_vector(const Program prog) {
       pc = W[H_BODY_BEGIN];
       pc_end = W[H_BODY_END];
       fetch2(W, pc, nw0, nw1);
+      if constexpr (PROF) p_tile += __builtin_amdgcn_s_memtime() - p_top;
       continue;
     }
     const uint32_t w0 = nw0, w1 = nw1;
@@ -989,24 +996,24 @@ dvm_vm_vector(const Program prog) {
     row_op(R.rw, a0, a1);                                           \
   }
 #define CASE_LD(d)                                                                                          \
-  case HD_LD_PF16 + d: read_pf<DT_BF16>(treg<d>(R), w0, vmc_load(w0), ARG, G, tl, L, S); settle(treg<d>(R)); break; \
-  case HD_LD_PF32 + d: read_pf<DT_F32>(treg<d>(R), w0, vmc_load(w0), ARG, G, tl, L, S); settle(treg<d>(R)); break;  \
-  case HD_LD_INV + d: read_inv(treg<d>(R), w0, G, L, S); settle(treg<d>(R)); break;                          \
-  case HD_BCAST + d: fill(treg<d>(R), rget(R.rw, f_a(w0))); break;
+  case HD_LD_PF16 + d: PROF_ENTER() read_pf<DT_BF16>(treg<d>(R), w0, vmc_load(w0), ARG, G, tl, L, S); settle(treg<d>(R)); break; \
+  case HD_LD_PF32 + d: PROF_ENTER() read_pf<DT_F32>(treg<d>(R), w0, vmc_load(w0), ARG, G, tl, L, S); settle(treg<d>(R)); break;  \
+  case HD_LD_INV + d: PROF_ENTER() read_inv(treg<d>(R), w0, G, L, S); settle(treg<d>(R)); break;                          \
+  case HD_BCAST + d: PROF_ENTER() fill(treg<d>(R), rget(R.rw, f_a(w0))); break;
 #define CASE_COPY(d, a) \
-  case HD_COPY + 3 * d + a: treg<d>(R) = treg<a>(R); break;
+  case HD_COPY + 3 * d + a: PROF_ENTER() treg<d>(R) = treg<a>(R); break;
 #define SCALAR_B (f_bk(w0) == BK_IMM ? __uint_as_float(w1) : rget(R.rw, f_b(w0)))
 #define CASE_BIN_DIR(k, rev)                                                                               \
-  case HD_BIN + 10 * k + 5 * rev + BF_T0: bin_cc<k, rev>(R.t0, R.t0); break;                              \
-  case HD_BIN + 10 * k + 5 * rev + BF_T1: bin_cc<k, rev>(R.t0, R.t1); break;                              \
-  case HD_BIN + 10 * k + 5 * rev + BF_T2: bin_cc<k, rev>(R.t0, R.t2); break;                              \
-  case HD_BIN + 10 * k + 5 * rev + BF_SCALAR: bin_cs<k, rev>(R.t0, SCALAR_B); break;
+  case HD_BIN + 10 * k + 5 * rev + BF_T0: PROF_ENTER() bin_cc<k, rev>(R.t0, R.t0); break;                              \
+  case HD_BIN + 10 * k + 5 * rev + BF_T1: PROF_ENTER() bin_cc<k, rev>(R.t0, R.t1); break;                              \
+  case HD_BIN + 10 * k + 5 * rev + BF_T2: PROF_ENTER() bin_cc<k, rev>(R.t0, R.t2); break;                              \
+  case HD_BIN + 10 * k + 5 * rev + BF_SCALAR: PROF_ENTER() bin_cs<k, rev>(R.t0, SCALAR_B); break;
 #define CASE_BIN_COMM(k) CASE_BIN_DIR(k, false)
 #define CASE_BIN_NC(k) CASE_BIN_DIR(k, false) CASE_BIN_DIR(k, true)
-#define CASE_RED(kind, a) case HD_ALL + 3 * kind + a: CASE_RED_ROW(kind, a)
+#define CASE_RED(kind, a) case HD_ALL + 3 * kind + a: PROF_ENTER() CASE_RED_ROW(kind, a)
 #define CASE_RED_ROW(kind, a)                                                              \
-  case HD_RED + 3 * kind + a:                                                              \
-  case HD_REDX + 3 * kind + a: {                                                           \
+  case HD_RED + 3 * kind + a: PROF_ENTER()                                                              \
+  case HD_REDX + 3 * kind + a: PROF_ENTER() {                                                           \
     const uint32_t h = f_op(w0);                                                           \
     float acc = lane_partial<kind>(treg<a>(R), G, tl, L);                                  \
     if (h == HD_RED + 3 * kind + a) {                                                      \
@@ -1037,9 +1044,9 @@ dvm_vm_vector(const Program prog) {
 
     switch (f_op(w0)) {
       CASE_LD(0) CASE_LD(1) CASE_LD(2)
-      case HD_LD_DIR + 0:
-      case HD_LD_DIR + 1:
-      case HD_LD_DIR + 2: {
+      case HD_LD_DIR + 0: PROF_ENTER()
+      case HD_LD_DIR + 1: PROF_ENTER()
+      case HD_LD_DIR + 2: PROF_ENTER() {
         Ch m;
         load_any(m, ARG, G, tl, L);
         settle(m);
@@ -1048,11 +1055,11 @@ dvm_vm_vector(const Program prog) {
         else R.t2 = m;
         break;
       }
-      case HD_ST_BF16: store_dir<DT_BF16>(R.t0, ARG, G, tl, L); break;
-      case HD_ST_F32: store_dir<DT_F32>(R.t0, ARG, G, tl, L); break;
-      case HD_ST_DIR + 0: store_any(R.t0, ARG, G, tl, L); break;
-      case HD_ST_DIR + 1:
-      case HD_ST_DIR + 2: {
+      case HD_ST_BF16: PROF_ENTER() store_dir<DT_BF16>(R.t0, ARG, G, tl, L); break;
+      case HD_ST_F32: PROF_ENTER() store_dir<DT_F32>(R.t0, ARG, G, tl, L); break;
+      case HD_ST_DIR + 0: PROF_ENTER() store_any(R.t0, ARG, G, tl, L); break;
+      case HD_ST_DIR + 1: PROF_ENTER()
+      case HD_ST_DIR + 2: PROF_ENTER() {
         Ch m;
         if (f_a(w0) == 1) m = R.t1;
         else m = R.t2;
@@ -1060,20 +1067,20 @@ dvm_vm_vector(const Program prog) {
         break;
       }
       CASE_COPY(0, 1) CASE_COPY(0, 2) CASE_COPY(1, 0) CASE_COPY(1, 2) CASE_COPY(2, 0) CASE_COPY(2, 1)
-      case HD_UN + UN_SQRT: un_c<UN_SQRT>(R.t0); break;
-      case HD_UN + UN_ABS: un_c<UN_ABS>(R.t0); break;
-      case HD_UN + UN_LOG: un_c<UN_LOG>(R.t0); break;
-      case HD_UN + UN_EXP: un_c<UN_EXP>(R.t0); break;
-      case HD_UN + UN_ROUND: un_c<UN_ROUND>(R.t0); break;
-      case HD_UN + UN_FLOOR: un_c<UN_FLOOR>(R.t0); break;
-      case HD_UN + UN_ISFINITE: un_c<UN_ISFINITE>(R.t0); break;
-      case HD_UN + UN_NEG: un_c<UN_NEG>(R.t0); break;
-      case HD_UN + UN_RECIP: un_c<UN_RECIP>(R.t0); break;
-      case HD_UN + UN_TOBF16: un_c<UN_TOBF16>(R.t0); break;
+      case HD_UN + UN_SQRT: PROF_ENTER() un_c<UN_SQRT>(R.t0); break;
+      case HD_UN + UN_ABS: PROF_ENTER() un_c<UN_ABS>(R.t0); break;
+      case HD_UN + UN_LOG: PROF_ENTER() un_c<UN_LOG>(R.t0); break;
+      case HD_UN + UN_EXP: PROF_ENTER() un_c<UN_EXP>(R.t0); break;
+      case HD_UN + UN_ROUND: PROF_ENTER() un_c<UN_ROUND>(R.t0); break;
+      case HD_UN + UN_FLOOR: PROF_ENTER() un_c<UN_FLOOR>(R.t0); break;
+      case HD_UN + UN_ISFINITE: PROF_ENTER() un_c<UN_ISFINITE>(R.t0); break;
+      case HD_UN + UN_NEG: PROF_ENTER() un_c<UN_NEG>(R.t0); break;
+      case HD_UN + UN_RECIP: PROF_ENTER() un_c<UN_RECIP>(R.t0); break;
+      case HD_UN + UN_TOBF16: PROF_ENTER() un_c<UN_TOBF16>(R.t0); break;
       CASE_BIN_COMM(ALU_ADD) CASE_BIN_NC(ALU_SUB) CASE_BIN_COMM(ALU_MUL)
-      case HD_BIN + 10 * ALU_DIV + BF_SCALAR: bin_cs<ALU_DIV, false>(R.t0, SCALAR_B); break;
-      case HD_BIN + 10 * ALU_DIV + BF_REV + BF_SCALAR: bin_cs<ALU_DIV, true>(R.t0, SCALAR_B); break;
-      case HD_DIV_T: {
+      case HD_BIN + 10 * ALU_DIV + BF_SCALAR: PROF_ENTER() bin_cs<ALU_DIV, false>(R.t0, SCALAR_B); break;
+      case HD_BIN + 10 * ALU_DIV + BF_REV + BF_SCALAR: PROF_ENTER() bin_cs<ALU_DIV, true>(R.t0, SCALAR_B); break;
+      case HD_DIV_T: PROF_ENTER() {
         Ch b;
         if (f_b(w0) == 0) b = R.t0;
         else if (f_b(w0) == 1) b = R.t1;
@@ -1083,7 +1090,7 @@ dvm_vm_vector(const Program prog) {
         break;
       }
       CASE_BIN_COMM(ALU_MAX) CASE_BIN_COMM(ALU_MIN)
-      case HD_BIN_POW: {
+      case HD_BIN_POW: PROF_ENTER() {
         Ch b;
         if (f_bk(w0) != BK_TREG) fill(b, SCALAR_B);
         else if (f_b(w0) == 0) b = R.t0;
@@ -1092,7 +1099,7 @@ dvm_vm_vector(const Program prog) {
         pow_rot(R.t0, b, (f_flags(w0) & FL_REV) != 0);
         break;
       }
-      case HD_FMA_INV: {
+      case HD_FMA_INV: PROF_ENTER() {
         // (ACC * r) * inv[b] + inv[a], the last two in one rounding
         const float r = f_bk(w0) == BK_RREG ? rget(R.rw, f_dst(w0)) : 1.f;
         Ch sc, sh;
@@ -1107,7 +1114,7 @@ dvm_vm_vector(const Program prog) {
           for (int i = 0; i < VEC; ++i) R.t0.c[j][i] = __builtin_fmaf(R.t0.c[j][i] * r, sc.c[j][i], sh.c[j][i]);
         break;
       }
-      case HD_BIN_MEM: {
+      case HD_BIN_MEM: PROF_ENTER() {
         Ch m;
         read_mem(m, w0, vmc_bin(w0), ARG, G, tl, L, S);
         const bool rev = (f_flags(w0) & FL_REV) != 0;
@@ -1125,8 +1132,8 @@ dvm_vm_vector(const Program prog) {
       CASE_RED(RK_SUM, 0) CASE_RED(RK_SUM, 1) CASE_RED(RK_SUM, 2)
       CASE_RED(RK_MAX, 0) CASE_RED(RK_MAX, 1) CASE_RED(RK_MAX, 2)
       CASE_RED_ROW(RK_SUMSQ, 0) CASE_RED_ROW(RK_SUMSQ, 1) CASE_RED_ROW(RK_SUMSQ, 2)
-      case HD_ALL_FIN + RK_SUM:
-      case HD_ALL_FIN + RK_MAX: {
+      case HD_ALL_FIN + RK_SUM: PROF_ENTER()
+      case HD_ALL_FIN + RK_MAX: PROF_ENTER() {
         // every lane combines the per-wave partials (LDS broadcast reads);
         // lane 0 alone stores the tile's partial, the others are masked by an
         // out-of-range offset
@@ -1140,7 +1147,7 @@ dvm_vm_vector(const Program prog) {
         __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc), rs, lane_off(tidv == 0, (int)(tl.id * 4u)), 0, 0);
         break;
       }
-      case HD_SYNC:
+      case HD_SYNC: PROF_ENTER()
         // LDS exchange only: wait for this wave's LDS operations, then meet
         // the other waves (no wait on outstanding global loads, so prefetches
         // stay in flight across the barrier)
@@ -1148,13 +1155,13 @@ dvm_vm_vector(const Program prog) {
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
         break;
-      case HD_RBIN:
-      case HD_RUN:
+      case HD_RBIN: PROF_ENTER()
+      case HD_RUN: PROF_ENTER()
         // a run of row-register instructions executes here
         row_op(R.rw, w0, w1);
         ROW_RUN_TAIL();
         break;
-      case HD_LD_ROW: {
+      case HD_LD_ROW: PROF_ENTER() {
         const ArgD a = ARG;
         const int es = esize(a.dt);
         const Rsrc rs = tile_rsrc(a, tl, es);
@@ -1167,7 +1174,7 @@ dvm_vm_vector(const Program prog) {
         rset(R.rw, f_dst(w0), v);
         break;
       }
-      case HD_ST_ROW: {
+      case HD_ST_ROW: PROF_ENTER() {
         const ArgD a = ARG;
         const int es = esize(a.dt);
         const Rsrc rs = tile_rsrc(a, tl, es);
@@ -1178,14 +1185,14 @@ dvm_vm_vector(const Program prog) {
         else __builtin_amdgcn_raw_buffer_store_b8((uint8_t)v, rs, off, 0, 0);
         break;
       }
-      case HD_DBG: {
+      case HD_DBG: PROF_ENTER() {
         const float v = f_sub(w0) == 0 ? (float)tl.id : (float)blockIdx.x;
         if (f_dst(w0) == 0) fill(R.t0, v);
         else if (f_dst(w0) == 1) fill(R.t1, v);
         else fill(R.t2, v);
         break;
       }
-      case HD_LDS_INV: {
+      case HD_LDS_INV: PROF_ENTER() {
         // prologue: the invariant operand's tile view, as fp32, into its slot
         const uint32_t k = f_dst(w0) & 1u;
         int stride;
@@ -1200,7 +1207,7 @@ dvm_vm_vector(const Program prog) {
         inv_write(tmp, S.inv(k), G, idx, stride);
         break;
       }
-      case HD_PF: {
+      case HD_PF: PROF_ENTER() {
         // prologue: fetch the workgroup's first tile into the prefetch slot
         const ArgD a = ARG;
         if (a.dt == DT_F32) pf_issue<DT_F32>(S.pf(f_b(w0) & 1u), a, G, tl, L);
@@ -1208,7 +1215,14 @@ dvm_vm_vector(const Program prog) {
         break;
       }
       default:
+        PROF_ENTER()
         break;
+    }
+    if constexpr (PROF) {
+      const uint64_t t = __builtin_amdgcn_s_memtime();
+      p_dec += p_ent - p_top;
+      p_exe += t - p_ent;
+      ++p_n;
     }
 #undef ARG
 #undef CASE_LD
@@ -1256,6 +1270,40 @@ dvm_vm_vector(const Program prog) {
       }
     }
   }
+  if constexpr (PROF) {
+    // five counters per workgroup: total, decode, execute, tile-change
+    // cycles, dispatches (wave 0's view; the waves run in lockstep per tile)
+    const uint64_t total = __builtin_amdgcn_s_memtime() - p_start;
+    if (tid == 0) {
+      uint64_t* c = reinterpret_cast<uint64_t*>(w64(W, H_PROF_LO)) + (size_t)blockIdx.x * 5;
+      c[0] = total;
+      c[1] = p_dec;
+      c[2] = p_exe;
+      c[3] = p_tile;
+      c[4] = p_n;
+    }
+  }
+#undef PROF_ENTER
+}
+
+extern "C" __global__ void __launch_bounds__(T_LANES) __attribute__((amdgpu_waves_per_eu(2, 2)))
+dvm_vm_vector(const Program prog) {
+  __shared__ float s_red[N_LDSBUF][T_LANES / 64];
+  __shared__ int s_last;
+  extern __shared__ __attribute__((aligned(16))) char dlds[];
+  (void)prog;
+  vm_main<false>(s_red, s_last, dlds);
+}
+
+// Profiling twin of dvm_vm_vector: same program, same results, plus the
+// per-workgroup cycle split at the address in header words H_PROF_LO/HI.
+extern "C" __global__ void __launch_bounds__(T_LANES) __attribute__((amdgpu_waves_per_eu(2, 2)))
+dvm_vm_vector_prof(const Program prog) {
+  __shared__ float s_red[N_LDSBUF][T_LANES / 64];
+  __shared__ int s_last;
+  extern __shared__ __attribute__((aligned(16))) char dlds[];
+  (void)prog;
+  vm_main<true>(s_red, s_last, dlds);
 }
 
 // Host-side launch of the VECTOR VM kernel with one program as its argument.
@@ -1268,5 +1316,17 @@ extern "C" hipError_t dvm_launch_vector_kernel(const Program* p, unsigned grid, 
     attr_set = true;
   }
   hipLaunchKernelGGL(dvm_vm_vector, dim3(grid), dim3(T_LANES), p->w[H_LDS_BYTES], s, *p);
+  return hipGetLastError();
+}
+
+extern "C" hipError_t dvm_launch_vector_prof_kernel(const Program* p, unsigned grid, hipStream_t s) {
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute((const void*)dvm_vm_vector_prof,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)LDS_BUDGET);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  hipLaunchKernelGGL(dvm_vm_vector_prof, dim3(grid), dim3(T_LANES), p->w[H_LDS_BYTES], s, *p);
   return hipGetLastError();
 }

@@ -168,6 +168,24 @@ dvm_status dvm_flush(dvm_graph* g, dvm_program** out);
  * stream (hipStream_t).  Asynchronous. */
 dvm_status dvm_launch(dvm_context* ctx, const dvm_program* p, void* stream);
 
+/* Profiling launch of a VECTOR program (the decode-overhead measurement: the
+ * paper review page's section 4.4 has the Scalar unit decode the bytecode
+ * while the vector units execute, and claims the decode is cheap next to the
+ * execution).  Runs the profiling twin of the VM kernel, which computes the
+ * same results as dvm_launch and also reads the cycle counter around every
+ * dispatch.  For each workgroup b it writes DVM_PROF_COUNTERS uint64 values to
+ * counters[DVM_PROF_COUNTERS * b + k] (device memory, owned by the caller, at
+ * least DVM_PROF_COUNTERS * grid values, grid = dvm_header.grid):
+ *   k = 0 total cycles of the workgroup, 1 decode cycles (instruction fetch,
+ *   field decode and the dispatch to the handler), 2 execute cycles (the
+ *   handlers, row-register runs inside them included), 3 tile-change cycles,
+ *   4 dispatches.  Counts are wave 0's and approximate: the counter reads
+ *   themselves perturb the schedule.  DVM_ERR_UNSUPPORTED for MIX programs,
+ *   DVM_ERR_INVALID_ARG for a short or null buffer.  Asynchronous. */
+#define DVM_PROF_COUNTERS 5
+dvm_status dvm_launch_profiled(dvm_context* ctx, const dvm_program* p, void* stream, uint64_t* counters,
+                               size_t n_counters);
+
 /* dvm_flush + dvm_launch on the graph's stream (no-op when empty). */
 dvm_status dvm_graph_flush_launch(dvm_graph* g, int32_t* launched);
 
