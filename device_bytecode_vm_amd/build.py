@@ -8,7 +8,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libdvm.so")
 
-SOURCES = ["dvm_host.cpp", "vm_vector.hip", "vm_mix.hip"]
+SOURCES = ["dvm_host.cpp", "vm_vector.hip", "vm_vector_wide.hip", "vm_mix.hip"]
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
          # no packed-fp32 VALU forms in device code
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
@@ -22,20 +22,28 @@ DEVICE_FLAGS = ["-mllvm", "-structurizecfg-skip-uniform-regions=true"]
 
 def build(verbose=False):
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-    objs = []
+    cmds, objs = [], []
     for src in SOURCES:
         obj = os.path.join(CSRC, os.path.splitext(src)[0] + ".o")
         extra = DEVICE_FLAGS if src.endswith(".hip") else []
-        cmd = [hipcc] + [f for f in FLAGS if f != "-shared"] + extra + ["-c", os.path.join(CSRC, src),
-                                                                  "-I", os.path.join(ROOT, "include"),
-                                                                  "-I", CSRC, "-o", obj]
+        cmds.append([hipcc] + [f for f in FLAGS if f != "-shared"] + extra + ["-c", os.path.join(CSRC, src),
+                                                                       "-I", os.path.join(ROOT, "include"),
+                                                                       "-I", CSRC, "-o", obj])
+        objs.append(obj)
+    # the translation units compile independently: run them side by side
+    procs = []
+    for cmd in cmds:
         if verbose:
             print(" ".join(cmd), flush=True)
-        r = subprocess.run(cmd, capture_output=True, text=True)
-        if r.returncode != 0:
-            sys.stderr.write(r.stdout + r.stderr)
-            raise RuntimeError(f"compiling {src} failed")
-        objs.append(obj)
+        procs.append(subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True))
+    failed = []
+    for src, pr in zip(SOURCES, procs):
+        out, err = pr.communicate()
+        if pr.returncode != 0:
+            sys.stderr.write(out + err)
+            failed.append(src)
+    if failed:
+        raise RuntimeError(f"compiling {', '.join(failed)} failed")
     tmp = LIB + ".tmp"
     cmd = [hipcc, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + objs
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -32,6 +32,9 @@ constexpr int T_LANES = 256;
 constexpr int VEC = 8;
 constexpr int NV_MAX = 5;
 constexpr int E_MAX = VEC * NV_MAX;   // elements per lane per tile register
+// The wide VM variant: one tile register of NV_WIDE chunks per lane, for
+// programs that never hold a second tile value (twice the columns per lane).
+constexpr int NV_WIDE = 10;
 constexpr int N_TREG = 3;             // tile registers: 0 = ACC, 1..2 slots
 constexpr int N_RREG = 4;             // row registers
 constexpr int N_LDSBUF = 8;           // cross-wave reduction buffers
@@ -42,7 +45,7 @@ constexpr int ARG_BASE = HDR_WORDS;
 constexpr int ARG_WORDS = 8;
 constexpr int MAX_ARGS = 32;
 
-enum KernelType : uint32_t { KT_VECTOR = 0, KT_MIX = 1 };
+enum KernelType : uint32_t { KT_VECTOR = 0, KT_MIX = 1, KT_VECTOR_WIDE = 2 };
 enum Template : uint32_t { TM_ELEMWISE = 0, TM_ROWREDUCE = 1, TM_ALLREDUCE = 2, TM_MATMUL = 3 };
 
 // Header word offsets.

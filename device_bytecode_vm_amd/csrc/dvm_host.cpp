@@ -25,6 +25,8 @@ using namespace dvmbc;
 extern "C" hipError_t dvm_launch_vector_kernel(const Program* p, unsigned grid, hipStream_t s);
 extern "C" hipError_t dvm_launch_mix_kernel(const Program* p, unsigned grid, hipStream_t s);
 extern "C" hipError_t dvm_launch_vector_prof_kernel(const Program* p, unsigned grid, hipStream_t s);
+extern "C" hipError_t dvm_launch_vector_kernel_wide(const Program* p, unsigned grid, hipStream_t s);
+extern "C" hipError_t dvm_launch_vector_prof_kernel_wide(const Program* p, unsigned grid, hipStream_t s);
 
 namespace {
 
@@ -138,7 +140,7 @@ int64_t extent_bytes(const dvm_tensor& t) {
 //    earlier (larger) candidates win ties.
 // ===========================================================================
 namespace tiling {
-constexpr int64_t T = T_LANES, V = VEC, NVM = NV_MAX, W = 64 * VEC, G = 512, A = 7812, BT = 1;
+constexpr int64_t T = T_LANES, V = VEC, W = 64 * VEC, G = 512, A = 7812, BT = 1;
 
 struct Operand {
   int64_t esize, sr, sc, base_mod16;
@@ -218,12 +220,12 @@ int64_t alignment_pad(int64_t R, const std::vector<Operand>& ops) {
   return 0;
 }
 
-bool geometry(int64_t tr, int64_t tc, int64_t pad, int64_t* P, int64_t* g, int64_t* nv) {
+bool geometry(int64_t tr, int64_t tc, int64_t pad, int64_t nvm, int64_t* P, int64_t* g, int64_t* nv) {
   *P = next_pow2(tr);
   if (*P > T) return false;
   *g = T / *P;
   *nv = cdiv(tc + pad, *g * V);
-  return *nv <= NVM;
+  return *nv <= nvm;
 }
 
 void shrink_path(int tmpl, int64_t R, int64_t C, std::vector<std::pair<int64_t, int64_t>>* path) {
@@ -320,7 +322,8 @@ bool plan_matmul(int64_t M, int64_t N, int64_t K, int64_t a_es, int64_t b_es, co
   return true;
 }
 
-bool plan(int tmpl, int64_t R, int64_t C, const std::vector<Operand>& ops, Plan* p) {
+// nvm: chunks per lane of the VM variant (NV_MAX standard, NV_WIDE wide)
+bool plan(int tmpl, int64_t R, int64_t C, const std::vector<Operand>& ops, Plan* p, int64_t nvm = NV_MAX) {
   *p = Plan();
   p->tmpl = tmpl;
   p->R = R;
@@ -333,7 +336,7 @@ bool plan(int tmpl, int64_t R, int64_t C, const std::vector<Operand>& ops, Plan*
   int64_t best = 0;
   for (auto& [tr, tc] : path) {
     int64_t P, g, nv;
-    if (!geometry(tr, tc, p->pad, &P, &g, &nv)) continue;
+    if (!geometry(tr, tc, p->pad, nvm, &P, &g, &nv)) continue;
     const int64_t c = cost(R, C, tr, tc, ops);
     if (!found || c < best) {
       found = true;
@@ -728,7 +731,7 @@ struct Checker {
     std::vector<std::pair<int64_t, int64_t>> st;
     if (!tile_operands(sd, operands, &R, &C, &tops, &st)) return FR_SHAPE;
     tiling::Plan p;
-    if (!tiling::plan(tmpl(), R, C, tops, &p)) return FR_RESOURCE;
+    if (!tiling::plan(tmpl(), R, C, tops, &p) && !tiling::plan(tmpl(), R, C, tops, &p, NV_WIDE)) return FR_RESOURCE;
     return -1;
   }
 
@@ -774,6 +777,20 @@ struct Encoder {
   std::vector<Consume> consumes;
   long issue_pos[2] = {-1, -1};
   std::vector<uint32_t> pro;            // prologue (once per workgroup)
+  // VM variant the program is encoded for: the standard one (N_TREG tile
+  // registers of NV_MAX chunks) or the wide one (the accumulator alone, of
+  // NV_WIDE chunks)
+  int64_t nvm = NV_MAX;
+  int n_treg = N_TREG;
+  uint32_t ktype = KT_VECTOR;
+  int treg_hi = 0;          // highest tile register the program names
+  bool plan_failed = false; // no tile of this variant fits the shape
+  int staged_pf = 0, staged_inv = 0;
+  void wide() {
+    nvm = NV_WIDE;
+    n_treg = 1;
+    ktype = KT_VECTOR_WIDE;
+  }
 
   Encoder(dvm_graph* gr, const std::vector<OpRec>& o, dvm_program* p) : g(gr), ops(o), ck(gr, o), prog(p), W(p->prog.w) {}
 
@@ -809,12 +826,13 @@ struct Encoder {
   bool live_after(int64_t s, int i) const { return last_use[s] > i; }
 
   int free_treg(int avoid0 = 1) const {
-    for (int k = avoid0; k < N_TREG; ++k)
+    for (int k = avoid0; k < n_treg; ++k)
       if (treg[k] < 0) return k;
     return -1;
   }
 
   void bind_t(int k, int64_t s) {
+    if (s >= 0) treg_hi = std::max(treg_hi, k);
     if (treg[k] >= 0) tloc[treg[k]] = -1;
     treg[k] = (int)s;
     if (s >= 0) tloc[s] = k;
@@ -863,6 +881,7 @@ struct Encoder {
           treg[f] = (int)s;
           tloc[s] = f;
           treg[0] = -1;
+          treg_hi = std::max(treg_hi, f);
         } else if (ck.external(s)) {
           unbind_t(0);
         } else {
@@ -1198,13 +1217,13 @@ struct Encoder {
     const uint32_t* a = W + ARG_BASE + arg * ARG_WORDS;
     const int32_t sc = (int32_t)a[A_SC];
     if (sc == 0) return 1u;
-    if ((a[A_FLAGS] & AF_VEC) && sc == 1) return (uint32_t)NV_MAX * halves(arg);
-    return 8u * (uint32_t)NV_MAX;
+    if ((a[A_FLAGS] & AF_VEC) && sc == 1) return (uint32_t)nvm * halves(arg);
+    return 8u * (uint32_t)nvm;
   }
   uint32_t store_ops(uint32_t arg) const {
     const uint32_t* a = W + ARG_BASE + arg * ARG_WORDS;
-    if ((a[A_FLAGS] & AF_VEC) && (int32_t)a[A_SC] == 1) return (uint32_t)NV_MAX * halves(arg);
-    return 8u * (uint32_t)NV_MAX;
+    if ((a[A_FLAGS] & AF_VEC) && (int32_t)a[A_SC] == 1) return (uint32_t)nvm * halves(arg);
+    return 8u * (uint32_t)nvm;
   }
   uint32_t src_ops(uint32_t w0, uint32_t w1) const {
     const uint32_t f = f_flags(w0);
@@ -1289,6 +1308,8 @@ struct Encoder {
       }
     }
     W[H_LDS_BYTES] = off;
+    staged_pf = n_pf;
+    staged_inv = n_inv;
   }
 
   // Handler id of one instruction (generic opcode and fields -> the VM's
@@ -1510,7 +1531,10 @@ struct Encoder {
     std::vector<std::pair<int64_t, int64_t>> st;
     if (!ck.tile_operands(sd, operands, &R, &C, &tops, &st))
       return fail(DVM_ERR_SHAPE, "operands do not collapse to two dims");
-    if (!tiling::plan(tm, R, C, tops, &plan)) return fail(DVM_ERR_RESOURCE, "no feasible tile");
+    if (!tiling::plan(tm, R, C, tops, &plan, nvm)) {
+      plan_failed = true;
+      return fail(DVM_ERR_RESOURCE, "no feasible tile");
+    }
     // 32-bit lane offsets: a tile must span < 2^31 bytes in every operand
     for (size_t q = 0; q < operands.size(); ++q) {
       const int64_t span = ((plan.tr - 1) * std::llabs(st[q].first) + plan.tc * std::llabs(st[q].second) + 1) *
@@ -1579,7 +1603,7 @@ struct Encoder {
     std::copy(body.begin(), body.end(), W + body_base);
     W[H_MAGIC] = MAGIC;
     W[H_VERSION] = VERSION;
-    W[H_KTYPE] = KT_VECTOR;
+    W[H_KTYPE] = ktype;
     W[H_TEMPLATE] = (uint32_t)tm;
     W[H_BLOCK_DIM] = (uint32_t)plan.block_dim;
     W[H_BODY_TILE] = (uint32_t)plan.body_tile;
@@ -1622,6 +1646,30 @@ dvm_status encode_buffer(dvm_graph* g, dvm_program** out) {
   if (!p) return fail(DVM_ERR_INTERNAL, "out of host memory");
   Encoder enc(g, g->buf, p);
   dvm_status st = enc.run();
+  // The wide VM for programs that keep every tile value in the accumulator:
+  // where a standard tile holds a single row (and a wide one two or more,
+  // with the same LDS staging), or where no standard tile fits the rows.
+  const bool one_row = st == DVM_OK && p->prog.w[H_KTYPE] == KT_VECTOR && enc.treg_hi == 0 &&
+                       enc.plan.tr == 1 && enc.plan.n_c == 1 && enc.plan.block_dim > 0;
+  if (one_row || (st != DVM_OK && enc.plan_failed)) {
+    const std::string err = g_err;
+    dvm_program* q = new (std::nothrow) dvm_program();
+    if (q) {
+      Encoder w(g, g->buf, q);
+      w.wide();
+      const dvm_status sw = w.run();
+      const bool take = sw == DVM_OK && (st != DVM_OK || (w.plan.tr >= 2 && w.staged_pf >= enc.staged_pf &&
+                                                         w.staged_inv >= enc.staged_inv));
+      if (take) {
+        delete p;
+        p = q;
+        st = DVM_OK;
+      } else {
+        delete q;
+        g_err = err;
+      }
+    }
+  }
   // the buffered values leave the buffer whatever the outcome
   for (auto& o : g->buf) {
     Val& v = g->vals[o.out];
@@ -1649,8 +1697,10 @@ dvm_status encode_buffer(dvm_graph* g, dvm_program** out) {
 dvm_status launch(dvm_context* ctx, const dvm_program* p, hipStream_t s) {
   if (!ctx || ctx->device < 0) return fail(DVM_ERR_DEVICE, "encode-only context cannot launch");
   if (p->grid_launch == 0) return DVM_OK;
-  hipError_t e = p->prog.w[H_KTYPE] == KT_MIX ? dvm_launch_mix_kernel(&p->prog, p->grid_launch, s)
-                                              : dvm_launch_vector_kernel(&p->prog, p->grid_launch, s);
+  const uint32_t kt = p->prog.w[H_KTYPE];
+  hipError_t e = kt == KT_MIX           ? dvm_launch_mix_kernel(&p->prog, p->grid_launch, s)
+                 : kt == KT_VECTOR_WIDE ? dvm_launch_vector_kernel_wide(&p->prog, p->grid_launch, s)
+                                        : dvm_launch_vector_kernel(&p->prog, p->grid_launch, s);
   if (e != hipSuccess) return fail(DVM_ERR_DEVICE, "launch failed: %s", hipGetErrorString(e));
   return DVM_OK;
 }
@@ -1948,7 +1998,8 @@ dvm_status dvm_launch_profiled(dvm_context* ctx, const dvm_program* p, void* str
                                size_t n_counters) {
   if (!ctx || !p) return fail(DVM_ERR_INVALID_ARG, "null argument");
   if (ctx->device < 0) return fail(DVM_ERR_DEVICE, "encode-only context cannot launch");
-  if (p->prog.w[H_KTYPE] != KT_VECTOR) return fail(DVM_ERR_UNSUPPORTED, "profiling covers VECTOR programs");
+  const uint32_t kt = p->prog.w[H_KTYPE];
+  if (kt != KT_VECTOR && kt != KT_VECTOR_WIDE) return fail(DVM_ERR_UNSUPPORTED, "profiling covers VECTOR programs");
   if (p->grid_launch == 0) return DVM_OK;
   if (!counters) return fail(DVM_ERR_INVALID_ARG, "null counter buffer");
   const size_t need = (size_t)DVM_PROF_COUNTERS * p->grid_launch;
@@ -1957,7 +2008,8 @@ dvm_status dvm_launch_profiled(dvm_context* ctx, const dvm_program* p, void* str
   const uint64_t a = (uint64_t)(uintptr_t)counters;
   q.w[H_PROF_LO] = (uint32_t)a;
   q.w[H_PROF_HI] = (uint32_t)(a >> 32);
-  hipError_t e = dvm_launch_vector_prof_kernel(&q, p->grid_launch, (hipStream_t)stream);
+  hipError_t e = kt == KT_VECTOR_WIDE ? dvm_launch_vector_prof_kernel_wide(&q, p->grid_launch, (hipStream_t)stream)
+                                      : dvm_launch_vector_prof_kernel(&q, p->grid_launch, (hipStream_t)stream);
   if (e != hipSuccess) return fail(DVM_ERR_DEVICE, "launch failed: %s", hipGetErrorString(e));
   return DVM_OK;
 }
@@ -2015,7 +2067,8 @@ void dvm_program_free(dvm_program* p) { delete p; }
 dvm_status dvm_program_debug_tilemap(const dvm_program* p, const dvm_tensor* tile_out, const dvm_tensor* wg_out,
                                      dvm_program** out) {
   if (!p || !tile_out || !wg_out || !out) return fail(DVM_ERR_INVALID_ARG, "null argument");
-  if (p->prog.w[H_KTYPE] != KT_VECTOR) return fail(DVM_ERR_UNSUPPORTED, "vector programs only");
+  if (p->prog.w[H_KTYPE] != KT_VECTOR && p->prog.w[H_KTYPE] != KT_VECTOR_WIDE)
+    return fail(DVM_ERR_UNSUPPORTED, "vector programs only");
   for (const dvm_tensor* t : {tile_out, wg_out}) {
     if (t->dtype != DVM_F32 || t->ndim != 2 || t->shape[0] != p->R || t->shape[1] != p->C || t->stride[1] != 1 ||
         t->stride[0] != p->C)

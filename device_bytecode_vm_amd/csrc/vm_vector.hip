@@ -11,7 +11,7 @@
 // (the counterpart of the page's decode on the Scalar unit), and the routines
 // run on the vector ALUs, the LDS and the vector memory pipeline.
 //
-// Tiles are staged in registers: each lane owns up to NV_MAX chunks of VEC
+// Tiles are staged in registers: each lane owns up to NVK chunks of VEC
 // consecutive columns of its row, so elementwise chains never leave the VGPR
 // file (the page's "intermediate results stay in local memory" of section
 // 5.1, with the register file as that local memory).  Every register number
@@ -35,7 +35,26 @@
 
 using namespace dvmbc;
 
+// Two builds of this source: the standard VM (three tile registers of NV_MAX
+// chunks per lane) and, with DVM_WIDE defined, the wide VM (one tile register
+// of NV_WIDE chunks), for programs whose values all pass through the
+// accumulator and whose rows are too long for two of them to share a
+// standard tile.  Every symbol of the wide build carries a _wide suffix.
+#ifdef DVM_WIDE
+#define DVM_SYM(name) name##_wide
+#else
+#define DVM_SYM(name) name
+#endif
+
 namespace {
+
+#ifdef DVM_WIDE
+constexpr int NVK = NV_WIDE;  // chunks per lane per tile register
+constexpr int TREGS = 1;      // tile registers
+#else
+constexpr int NVK = NV_MAX;
+constexpr int TREGS = N_TREG;
+#endif
 
 typedef float f4 __attribute__((ext_vector_type(4)));
 typedef float V8 __attribute__((ext_vector_type(8)));
@@ -62,9 +81,9 @@ __device__ __forceinline__ void fetch2(KW* W, uint32_t pc, uint32_t& a, uint32_t
 constexpr int OOB = 0x7fffffff;                 // lane offset beyond any descriptor size
 constexpr int RSRC_W3 = 0x00020000;             // raw buffer, 32-bit data format
 
-// One tile register: NV_MAX chunks of VEC fp32 values per lane.
+// One tile register: NVK chunks of VEC fp32 values per lane.
 struct Ch {
-  V8 c[NV_MAX];
+  V8 c[NVK];
 };
 
 struct ArgD {
@@ -274,7 +293,7 @@ __device__ __forceinline__ void rset(RowRegs& rw, uint32_t i, float v) {
 
 __device__ __forceinline__ void fill(Ch& d, float v) {
 #pragma unroll
-  for (int j = 0; j < NV_MAX; ++j) d.c[j] = (V8)v;
+  for (int j = 0; j < NVK; ++j) d.c[j] = (V8)v;
 }
 
 // Make every value of a freshly loaded tile register available before the
@@ -283,7 +302,7 @@ __device__ __forceinline__ void fill(Ch& d, float v) {
 // routine after the dispatch merge, for all outstanding vector memory.
 __device__ __forceinline__ void settle(Ch& d) {
 #pragma unroll
-  for (int j = 0; j < NV_MAX; ++j) {
+  for (int j = 0; j < NVK; ++j) {
     float x0 = d.c[j][0], x1 = d.c[j][1], x2 = d.c[j][2], x3 = d.c[j][3];
     float x4 = d.c[j][4], x5 = d.c[j][5], x6 = d.c[j][6], x7 = d.c[j][7];
     asm volatile("" : "+v"(x0), "+v"(x1), "+v"(x2), "+v"(x3), "+v"(x4), "+v"(x5), "+v"(x6), "+v"(x7));
@@ -355,7 +374,7 @@ __device__ __forceinline__ void load_tail(Ch& d, const Rsrc& rs, int roff, const
   // issued later included), also on the path that skips them
   asm volatile("" : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]), "+v"(v[4]), "+v"(v[5]), "+v"(v[6]), "+v"(v[7]));
 #pragma unroll
-  for (int j = 0; j < NV_MAX; ++j)
+  for (int j = 0; j < NVK; ++j)
     if (j == T.slot)
 #pragma unroll
       for (int i = 0; i < VEC; ++i) d.c[j][i] = lane_sel(mine, v[i], d.c[j][i]);
@@ -413,7 +432,7 @@ __device__ __forceinline__ void store_tail(const Ch& s, const Rsrc& rs, int roff
   const Tail T = tail_of(G, tl);
   const int off = lane_off(L.rok & (L.lane == T.lane), (roff + T.col) * ES);
 #pragma unroll
-  for (int j = 0; j < NV_MAX; ++j)
+  for (int j = 0; j < NVK; ++j)
     if (j == T.slot) store_part<DT>(s.c[j], rs, off, T.r);
 }
 
@@ -444,7 +463,7 @@ __device__ __forceinline__ void load_dir(Ch& d, const ArgD& a, const Geo& G, con
     // cover is completed element by element
     const int lim = chunk_cols(a, tl, ES, any_row ? (T_LANES >> G.lg) : tl.tre);
 #pragma unroll
-    for (int j = 0; j < NV_MAX; ++j) {
+    for (int j = 0; j < NVK; ++j) {
       const int ct = (j * G.g + L.lane) * VEC;
       const int off = lane_off(rok & (ct + VEC <= lim), (roff + ct) * ES);
       if constexpr (DT == DT_F32) {
@@ -466,7 +485,7 @@ __device__ __forceinline__ void load_dir(Ch& d, const ArgD& a, const Geo& G, con
   } else {
     // element path: unaligned or strided operands
 #pragma unroll
-    for (int j = 0; j < NV_MAX; ++j) {
+    for (int j = 0; j < NVK; ++j) {
       const int ct = (j * G.g + L.lane) * VEC;
 #pragma unroll
       for (int i = 0; i < VEC; ++i) {
@@ -496,7 +515,7 @@ __device__ __forceinline__ void store_dir(const Ch& s, const ArgD& a, const Geo&
   const int roff = L.row * (int)a.sr;
   if ((a.fl & AF_VEC) && a.sc == 1) {
 #pragma unroll
-    for (int j = 0; j < NV_MAX; ++j) {
+    for (int j = 0; j < NVK; ++j) {
       const int ct = (j * G.g + L.lane) * VEC;
       const int off = lane_off(L.rok & (ct + VEC <= tl.tce), (roff + ct) * ES);
       const V8 x = s.c[j];
@@ -526,7 +545,7 @@ __device__ __forceinline__ void store_dir(const Ch& s, const ArgD& a, const Geo&
     store_tail<DT>(s, rs, roff, G, tl, L);
   } else {
 #pragma unroll
-    for (int j = 0; j < NV_MAX; ++j) {
+    for (int j = 0; j < NVK; ++j) {
       const int ct = (j * G.g + L.lane) * VEC;
 #pragma unroll
       for (int i = 0; i < VEC; ++i) {
@@ -573,7 +592,7 @@ __device__ __forceinline__ void pf_issue(char* slot, const ArgD& a, const Geo& G
   const uint32_t base = (uint32_t)(uintptr_t)(lds_void*)slot;
   const int lim = chunk_cols(a, nt, ES, nt.tre);
 #pragma unroll
-  for (int j = 0; j < NV_MAX; ++j) {
+  for (int j = 0; j < NVK; ++j) {
     if (j < G.nv) {
       const int ct = (j * G.g + L.lane) * VEC;
       const int off = lane_off(rok & (ct + VEC <= lim), (roff + ct) * ES);  // whole chunks only
@@ -594,7 +613,7 @@ template <uint32_t DT>
 __device__ __forceinline__ void pf_read(Ch& d, const char* slot, const Geo& G, int tid) {
   constexpr int HV = DT == DT_F32 ? 2 : 1;
 #pragma unroll
-  for (int j = 0; j < NV_MAX; ++j) {
+  for (int j = 0; j < NVK; ++j) {
     // a chunk past nv re-reads chunk 0 (its values are masked downstream)
     const int jj = j < G.nv ? j : 0;
     const u4 v = *(const u4*)(slot + ((jj * HV) * T_LANES + tid) * 16);
@@ -617,7 +636,7 @@ __device__ __forceinline__ int inv_base(KW* W, uint32_t k, const Geo& G, const L
 
 __device__ __forceinline__ void inv_write(const Ch& c, char* slot, const Geo& G, int idx, int stride) {
 #pragma unroll
-  for (int j = 0; j < NV_MAX; ++j) {
+  for (int j = 0; j < NVK; ++j) {
     if (j < G.nv) {
       const V8 x = c.c[j];
       const f4 a = {x[0], x[1], x[2], x[3]};
@@ -630,7 +649,7 @@ __device__ __forceinline__ void inv_write(const Ch& c, char* slot, const Geo& G,
 
 __device__ __forceinline__ void inv_read(Ch& c, const char* slot, const Geo& G, int idx, int stride) {
 #pragma unroll
-  for (int j = 0; j < NV_MAX; ++j) {
+  for (int j = 0; j < NVK; ++j) {
     const int jj = j < G.nv ? j : 0;
     const f4 a = *(const f4*)(slot + (jj * stride + idx) * 32);
     const f4 b = *(const f4*)(slot + (jj * stride + idx) * 32 + 16);
@@ -722,7 +741,7 @@ __device__ __forceinline__ void read_mem(Ch& d, uint32_t w0, uint32_t vmc, const
 template <uint32_t OPK, bool REV>
 __device__ __forceinline__ void bin_cc(Ch& acc, const Ch& b) {
 #pragma unroll
-  for (int j = 0; j < NV_MAX; ++j)
+  for (int j = 0; j < NVK; ++j)
 #pragma unroll
     for (int i = 0; i < VEC; ++i) {
       const float x = acc.c[j][i], y = b.c[j][i];
@@ -733,7 +752,7 @@ __device__ __forceinline__ void bin_cc(Ch& acc, const Ch& b) {
 template <uint32_t OPK, bool REV>
 __device__ __forceinline__ void bin_cs(Ch& acc, float s) {
 #pragma unroll
-  for (int j = 0; j < NV_MAX; ++j)
+  for (int j = 0; j < NVK; ++j)
 #pragma unroll
     for (int i = 0; i < VEC; ++i) {
       const float x = acc.c[j][i];
@@ -744,7 +763,7 @@ __device__ __forceinline__ void bin_cs(Ch& acc, float s) {
 template <uint32_t F>
 __device__ __forceinline__ void un_c(Ch& acc) {
 #pragma unroll
-  for (int j = 0; j < NV_MAX; ++j)
+  for (int j = 0; j < NVK; ++j)
 #pragma unroll
     for (int i = 0; i < VEC; ++i) acc.c[j][i] = una<F>(acc.c[j][i]);
 }
@@ -805,10 +824,10 @@ __device__ __forceinline__ V8 lane_terms(const V8& v) {
 template <uint32_t KIND>
 __device__ __forceinline__ float lane_partial(const Ch& c, const Geo& G, const Tile& tl, const Lane& L) {
   const float id = KIND == RK_MAX ? -__builtin_huge_valf() : 0.f;
-  float p[NV_MAX];
+  float p[NVK];
   if (tile_full(tl)) {
 #pragma unroll
-    for (int j = 0; j < NV_MAX; ++j) {
+    for (int j = 0; j < NVK; ++j) {
       const int ct = (j * G.g + L.lane) * VEC;
       p[j] = lane_sel(L.rok & (ct < tl.tce), tree8<KIND>(lane_terms<KIND>(c.c[j])), id);
     }
@@ -816,7 +835,7 @@ __device__ __forceinline__ float lane_partial(const Ch& c, const Geo& G, const T
     // only the row-end slot (wave-uniform) needs a mask per element
     const int jt = tail_of(G, tl).slot;
 #pragma unroll
-    for (int j = 0; j < NV_MAX; ++j) {
+    for (int j = 0; j < NVK; ++j) {
       const int ct = (j * G.g + L.lane) * VEC;
       const V8 t = lane_terms<KIND>(c.c[j]);
       if (j == jt) {
@@ -829,17 +848,21 @@ __device__ __forceinline__ float lane_partial(const Ch& c, const Geo& G, const T
       }
     }
   }
-  static_assert(NV_MAX == 5, "chunk combine order below assumes five chunks");
-  return comb<KIND>(comb<KIND>(comb<KIND>(p[0], p[1]), comb<KIND>(p[2], p[3])), p[4]);
+  // balanced pairwise combine in a fixed order
+#pragma unroll
+  for (int w = 1; w < NVK; w *= 2)
+#pragma unroll
+    for (int j = 0; j + w < NVK; j += 2 * w) p[j] = comb<KIND>(p[j], p[j + w]);
+  return p[0];
 }
 
 // ACC <- ACC pow B (B pow ACC if rev), one chunk at a time: the chunk in
-// position 0 is computed and both registers rotate by one chunk, NV_MAX times,
+// position 0 is computed and both registers rotate by one chunk, NVK times,
 // so the long pow expansion appears once per routine instead of once per
 // element.
 __device__ __forceinline__ void pow_rot(Ch& acc, Ch& b, bool rev) {
 #pragma nounroll
-  for (int k = 0; k < NV_MAX; ++k) {
+  for (int k = 0; k < NVK; ++k) {
     const V8 x = acc.c[0], y = b.c[0];
     V8 r;
 #pragma unroll
@@ -848,12 +871,12 @@ __device__ __forceinline__ void pow_rot(Ch& acc, Ch& b, bool rev) {
       r[i] = powf(u, v);
     }
 #pragma unroll
-    for (int j = 0; j < NV_MAX - 1; ++j) {
+    for (int j = 0; j < NVK - 1; ++j) {
       acc.c[j] = acc.c[j + 1];
       b.c[j] = b.c[j + 1];
     }
-    acc.c[NV_MAX - 1] = r;
-    b.c[NV_MAX - 1] = y;
+    acc.c[NVK - 1] = r;
+    b.c[NVK - 1] = y;
   }
 }
 
@@ -873,15 +896,15 @@ __device__ __forceinline__ void row_op(RowRegs& rw, uint32_t w0, uint32_t w1) {
 // Register file of one lane: three tile registers and four row registers.
 // ---------------------------------------------------------------------------
 struct Regs {
-  Ch t0, t1, t2;
+  Ch t[TREGS];
   RowRegs rw;
 };
 
+// Tile register K (the wide build has only the accumulator: its encoder
+// never names another register, and those handlers act on the accumulator)
 template <int K>
 __device__ __forceinline__ Ch& treg(Regs& r) {
-  if constexpr (K == 0) return r.t0;
-  else if constexpr (K == 1) return r.t1;
-  else return r.t2;
+  return r.t[K < TREGS ? K : 0];
 }
 
 }  // namespace
@@ -923,9 +946,8 @@ __device__ __forceinline__ void vm_main(float (*s_red)[T_LANES / 64], int& s_las
   if (t_end > block_dim) t_end = block_dim;
 
   Regs R;
-  fill(R.t0, 0.f);
-  fill(R.t1, 0.f);
-  fill(R.t2, 0.f);
+#pragma unroll
+  for (int k = 0; k < TREGS; ++k) fill(R.t[k], 0.f);
   R.rw = {0.f, 0.f, 0.f, 0.f};
 
   Ctx S;
@@ -1004,10 +1026,10 @@ __device__ __forceinline__ void vm_main(float (*s_red)[T_LANES / 64], int& s_las
   case HD_COPY + 3 * d + a: PROF_ENTER() treg<d>(R) = treg<a>(R); break;
 #define SCALAR_B (f_bk(w0) == BK_IMM ? __uint_as_float(w1) : rget(R.rw, f_b(w0)))
 #define CASE_BIN_DIR(k, rev)                                                                               \
-  case HD_BIN + 10 * k + 5 * rev + BF_T0: PROF_ENTER() bin_cc<k, rev>(R.t0, R.t0); break;                              \
-  case HD_BIN + 10 * k + 5 * rev + BF_T1: PROF_ENTER() bin_cc<k, rev>(R.t0, R.t1); break;                              \
-  case HD_BIN + 10 * k + 5 * rev + BF_T2: PROF_ENTER() bin_cc<k, rev>(R.t0, R.t2); break;                              \
-  case HD_BIN + 10 * k + 5 * rev + BF_SCALAR: PROF_ENTER() bin_cs<k, rev>(R.t0, SCALAR_B); break;
+  case HD_BIN + 10 * k + 5 * rev + BF_T0: PROF_ENTER() bin_cc<k, rev>(treg<0>(R), treg<0>(R)); break;                              \
+  case HD_BIN + 10 * k + 5 * rev + BF_T1: PROF_ENTER() bin_cc<k, rev>(treg<0>(R), treg<1>(R)); break;                              \
+  case HD_BIN + 10 * k + 5 * rev + BF_T2: PROF_ENTER() bin_cc<k, rev>(treg<0>(R), treg<2>(R)); break;                              \
+  case HD_BIN + 10 * k + 5 * rev + BF_SCALAR: PROF_ENTER() bin_cs<k, rev>(treg<0>(R), SCALAR_B); break;
 #define CASE_BIN_COMM(k) CASE_BIN_DIR(k, false)
 #define CASE_BIN_NC(k) CASE_BIN_DIR(k, false) CASE_BIN_DIR(k, true)
 #define CASE_RED(kind, a) case HD_ALL + 3 * kind + a: PROF_ENTER() CASE_RED_ROW(kind, a)
@@ -1050,68 +1072,75 @@ __device__ __forceinline__ void vm_main(float (*s_red)[T_LANES / 64], int& s_las
         Ch m;
         load_any(m, ARG, G, tl, L);
         settle(m);
-        if (f_dst(w0) == 0) R.t0 = m;
-        else if (f_dst(w0) == 1) R.t1 = m;
-        else R.t2 = m;
+        if (f_dst(w0) == 0) treg<0>(R) = m;
+        else if (f_dst(w0) == 1) treg<1>(R) = m;
+        else treg<2>(R) = m;
         break;
       }
-      case HD_ST_BF16: PROF_ENTER() store_dir<DT_BF16>(R.t0, ARG, G, tl, L); break;
-      case HD_ST_F32: PROF_ENTER() store_dir<DT_F32>(R.t0, ARG, G, tl, L); break;
-      case HD_ST_DIR + 0: PROF_ENTER() store_any(R.t0, ARG, G, tl, L); break;
+      case HD_ST_BF16: PROF_ENTER() store_dir<DT_BF16>(treg<0>(R), ARG, G, tl, L); break;
+      case HD_ST_F32: PROF_ENTER() store_dir<DT_F32>(treg<0>(R), ARG, G, tl, L); break;
+      case HD_ST_DIR + 0: PROF_ENTER() store_any(treg<0>(R), ARG, G, tl, L); break;
       case HD_ST_DIR + 1: PROF_ENTER()
       case HD_ST_DIR + 2: PROF_ENTER() {
         Ch m;
-        if (f_a(w0) == 1) m = R.t1;
-        else m = R.t2;
+        if (f_a(w0) == 1) m = treg<1>(R);
+        else m = treg<2>(R);
         store_any(m, ARG, G, tl, L);
         break;
       }
       CASE_COPY(0, 1) CASE_COPY(0, 2) CASE_COPY(1, 0) CASE_COPY(1, 2) CASE_COPY(2, 0) CASE_COPY(2, 1)
-      case HD_UN + UN_SQRT: PROF_ENTER() un_c<UN_SQRT>(R.t0); break;
-      case HD_UN + UN_ABS: PROF_ENTER() un_c<UN_ABS>(R.t0); break;
-      case HD_UN + UN_LOG: PROF_ENTER() un_c<UN_LOG>(R.t0); break;
-      case HD_UN + UN_EXP: PROF_ENTER() un_c<UN_EXP>(R.t0); break;
-      case HD_UN + UN_ROUND: PROF_ENTER() un_c<UN_ROUND>(R.t0); break;
-      case HD_UN + UN_FLOOR: PROF_ENTER() un_c<UN_FLOOR>(R.t0); break;
-      case HD_UN + UN_ISFINITE: PROF_ENTER() un_c<UN_ISFINITE>(R.t0); break;
-      case HD_UN + UN_NEG: PROF_ENTER() un_c<UN_NEG>(R.t0); break;
-      case HD_UN + UN_RECIP: PROF_ENTER() un_c<UN_RECIP>(R.t0); break;
-      case HD_UN + UN_TOBF16: PROF_ENTER() un_c<UN_TOBF16>(R.t0); break;
+      case HD_UN + UN_SQRT: PROF_ENTER() un_c<UN_SQRT>(treg<0>(R)); break;
+      case HD_UN + UN_ABS: PROF_ENTER() un_c<UN_ABS>(treg<0>(R)); break;
+      case HD_UN + UN_LOG: PROF_ENTER() un_c<UN_LOG>(treg<0>(R)); break;
+      case HD_UN + UN_EXP: PROF_ENTER() un_c<UN_EXP>(treg<0>(R)); break;
+      case HD_UN + UN_ROUND: PROF_ENTER() un_c<UN_ROUND>(treg<0>(R)); break;
+      case HD_UN + UN_FLOOR: PROF_ENTER() un_c<UN_FLOOR>(treg<0>(R)); break;
+      case HD_UN + UN_ISFINITE: PROF_ENTER() un_c<UN_ISFINITE>(treg<0>(R)); break;
+      case HD_UN + UN_NEG: PROF_ENTER() un_c<UN_NEG>(treg<0>(R)); break;
+      case HD_UN + UN_RECIP: PROF_ENTER() un_c<UN_RECIP>(treg<0>(R)); break;
+      case HD_UN + UN_TOBF16: PROF_ENTER() un_c<UN_TOBF16>(treg<0>(R)); break;
       CASE_BIN_COMM(ALU_ADD) CASE_BIN_NC(ALU_SUB) CASE_BIN_COMM(ALU_MUL)
-      case HD_BIN + 10 * ALU_DIV + BF_SCALAR: PROF_ENTER() bin_cs<ALU_DIV, false>(R.t0, SCALAR_B); break;
-      case HD_BIN + 10 * ALU_DIV + BF_REV + BF_SCALAR: PROF_ENTER() bin_cs<ALU_DIV, true>(R.t0, SCALAR_B); break;
+      case HD_BIN + 10 * ALU_DIV + BF_SCALAR: PROF_ENTER() bin_cs<ALU_DIV, false>(treg<0>(R), SCALAR_B); break;
+      case HD_BIN + 10 * ALU_DIV + BF_REV + BF_SCALAR: PROF_ENTER() bin_cs<ALU_DIV, true>(treg<0>(R), SCALAR_B); break;
       case HD_DIV_T: PROF_ENTER() {
         Ch b;
-        if (f_b(w0) == 0) b = R.t0;
-        else if (f_b(w0) == 1) b = R.t1;
-        else b = R.t2;
-        if (f_flags(w0) & FL_REV) bin_cc<ALU_DIV, true>(R.t0, b);
-        else bin_cc<ALU_DIV, false>(R.t0, b);
+        if (f_b(w0) == 0) b = treg<0>(R);
+        else if (f_b(w0) == 1) b = treg<1>(R);
+        else b = treg<2>(R);
+        if (f_flags(w0) & FL_REV) bin_cc<ALU_DIV, true>(treg<0>(R), b);
+        else bin_cc<ALU_DIV, false>(treg<0>(R), b);
         break;
       }
       CASE_BIN_COMM(ALU_MAX) CASE_BIN_COMM(ALU_MIN)
       case HD_BIN_POW: PROF_ENTER() {
         Ch b;
         if (f_bk(w0) != BK_TREG) fill(b, SCALAR_B);
-        else if (f_b(w0) == 0) b = R.t0;
-        else if (f_b(w0) == 1) b = R.t1;
-        else b = R.t2;
-        pow_rot(R.t0, b, (f_flags(w0) & FL_REV) != 0);
+        else if (f_b(w0) == 0) b = treg<0>(R);
+        else if (f_b(w0) == 1) b = treg<1>(R);
+        else b = treg<2>(R);
+        pow_rot(treg<0>(R), b, (f_flags(w0) & FL_REV) != 0);
         break;
       }
       case HD_FMA_INV: PROF_ENTER() {
         // (ACC * r) * inv[b] + inv[a], the last two in one rounding
         const float r = f_bk(w0) == BK_RREG ? rget(R.rw, f_dst(w0)) : 1.f;
-        Ch sc, sh;
-        read_inv(sc, w0, G, L, S);
-        int stride;
-        const uint32_t k2 = f_a(w0) & 1u;
-        const int idx = inv_base(W, k2, G, L, &stride);
-        inv_read(sh, S.inv(k2), G, idx, stride);
+        // chunk by chunk: the two invariant operands are read from LDS eight
+        // values at a time (no tile-sized temporaries)
+        int s1, s2;
+        const uint32_t k1 = f_b(w0) & 1u, k2 = f_a(w0) & 1u;
+        const int i1 = inv_base(W, k1, G, L, &s1), i2 = inv_base(W, k2, G, L, &s2);
+        const char* b1 = S.inv(k1);
+        const char* b2 = S.inv(k2);
 #pragma unroll
-        for (int j = 0; j < NV_MAX; ++j)
+        for (int j = 0; j < NVK; ++j) {
+          const int jj = j < G.nv ? j : 0;
+          const f4 a0 = *(const f4*)(b1 + (jj * s1 + i1) * 32), a1 = *(const f4*)(b1 + (jj * s1 + i1) * 32 + 16);
+          const f4 c0 = *(const f4*)(b2 + (jj * s2 + i2) * 32), c1 = *(const f4*)(b2 + (jj * s2 + i2) * 32 + 16);
+          const float sc[VEC] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+          const float sh[VEC] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
 #pragma unroll
-          for (int i = 0; i < VEC; ++i) R.t0.c[j][i] = __builtin_fmaf(R.t0.c[j][i] * r, sc.c[j][i], sh.c[j][i]);
+          for (int i = 0; i < VEC; ++i) treg<0>(R).c[j][i] = __builtin_fmaf(treg<0>(R).c[j][i] * r, sc[i], sh[i]);
+        }
         break;
       }
       case HD_BIN_MEM: PROF_ENTER() {
@@ -1119,13 +1148,13 @@ __device__ __forceinline__ void vm_main(float (*s_red)[T_LANES / 64], int& s_las
         read_mem(m, w0, vmc_bin(w0), ARG, G, tl, L, S);
         const bool rev = (f_flags(w0) & FL_REV) != 0;
         switch (f_sub(w0)) {
-          case ALU_ADD: bin_cc<ALU_ADD, false>(R.t0, m); break;
-          case ALU_SUB: if (rev) bin_cc<ALU_SUB, true>(R.t0, m); else bin_cc<ALU_SUB, false>(R.t0, m); break;
-          case ALU_MUL: bin_cc<ALU_MUL, false>(R.t0, m); break;
-          case ALU_DIV: if (rev) bin_cc<ALU_DIV, true>(R.t0, m); else bin_cc<ALU_DIV, false>(R.t0, m); break;
-          case ALU_MAX: bin_cc<ALU_MAX, false>(R.t0, m); break;
-          case ALU_MIN: bin_cc<ALU_MIN, false>(R.t0, m); break;
-          default: pow_rot(R.t0, m, rev); break;
+          case ALU_ADD: bin_cc<ALU_ADD, false>(treg<0>(R), m); break;
+          case ALU_SUB: if (rev) bin_cc<ALU_SUB, true>(treg<0>(R), m); else bin_cc<ALU_SUB, false>(treg<0>(R), m); break;
+          case ALU_MUL: bin_cc<ALU_MUL, false>(treg<0>(R), m); break;
+          case ALU_DIV: if (rev) bin_cc<ALU_DIV, true>(treg<0>(R), m); else bin_cc<ALU_DIV, false>(treg<0>(R), m); break;
+          case ALU_MAX: bin_cc<ALU_MAX, false>(treg<0>(R), m); break;
+          case ALU_MIN: bin_cc<ALU_MIN, false>(treg<0>(R), m); break;
+          default: pow_rot(treg<0>(R), m, rev); break;
         }
         break;
       }
@@ -1187,9 +1216,9 @@ __device__ __forceinline__ void vm_main(float (*s_red)[T_LANES / 64], int& s_las
       }
       case HD_DBG: PROF_ENTER() {
         const float v = f_sub(w0) == 0 ? (float)tl.id : (float)blockIdx.x;
-        if (f_dst(w0) == 0) fill(R.t0, v);
-        else if (f_dst(w0) == 1) fill(R.t1, v);
-        else fill(R.t2, v);
+        if (f_dst(w0) == 0) fill(treg<0>(R), v);
+        else if (f_dst(w0) == 1) fill(treg<1>(R), v);
+        else fill(treg<2>(R), v);
         break;
       }
       case HD_LDS_INV: PROF_ENTER() {
@@ -1287,7 +1316,7 @@ __device__ __forceinline__ void vm_main(float (*s_red)[T_LANES / 64], int& s_las
 }
 
 extern "C" __global__ void __launch_bounds__(T_LANES) __attribute__((amdgpu_waves_per_eu(2, 2)))
-dvm_vm_vector(const Program prog) {
+DVM_SYM(dvm_vm_vector)(const Program prog) {
   __shared__ float s_red[N_LDSBUF][T_LANES / 64];
   __shared__ int s_last;
   extern __shared__ __attribute__((aligned(16))) char dlds[];
@@ -1298,7 +1327,7 @@ dvm_vm_vector(const Program prog) {
 // Profiling twin of dvm_vm_vector: same program, same results, plus the
 // per-workgroup cycle split at the address in header words H_PROF_LO/HI.
 extern "C" __global__ void __launch_bounds__(T_LANES) __attribute__((amdgpu_waves_per_eu(2, 2)))
-dvm_vm_vector_prof(const Program prog) {
+DVM_SYM(dvm_vm_vector_prof)(const Program prog) {
   __shared__ float s_red[N_LDSBUF][T_LANES / 64];
   __shared__ int s_last;
   extern __shared__ __attribute__((aligned(16))) char dlds[];
@@ -1307,26 +1336,26 @@ dvm_vm_vector_prof(const Program prog) {
 }
 
 // Host-side launch of the VECTOR VM kernel with one program as its argument.
-extern "C" hipError_t dvm_launch_vector_kernel(const Program* p, unsigned grid, hipStream_t s) {
+extern "C" hipError_t DVM_SYM(dvm_launch_vector_kernel)(const Program* p, unsigned grid, hipStream_t s) {
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)dvm_vm_vector, hipFuncAttributeMaxDynamicSharedMemorySize,
+    hipError_t e = hipFuncSetAttribute((const void*)DVM_SYM(dvm_vm_vector), hipFuncAttributeMaxDynamicSharedMemorySize,
                                        (int)LDS_BUDGET);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  hipLaunchKernelGGL(dvm_vm_vector, dim3(grid), dim3(T_LANES), p->w[H_LDS_BYTES], s, *p);
+  hipLaunchKernelGGL(DVM_SYM(dvm_vm_vector), dim3(grid), dim3(T_LANES), p->w[H_LDS_BYTES], s, *p);
   return hipGetLastError();
 }
 
-extern "C" hipError_t dvm_launch_vector_prof_kernel(const Program* p, unsigned grid, hipStream_t s) {
+extern "C" hipError_t DVM_SYM(dvm_launch_vector_prof_kernel)(const Program* p, unsigned grid, hipStream_t s) {
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)dvm_vm_vector_prof,
+    hipError_t e = hipFuncSetAttribute((const void*)DVM_SYM(dvm_vm_vector_prof),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)LDS_BUDGET);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  hipLaunchKernelGGL(dvm_vm_vector_prof, dim3(grid), dim3(T_LANES), p->w[H_LDS_BYTES], s, *p);
+  hipLaunchKernelGGL(DVM_SYM(dvm_vm_vector_prof), dim3(grid), dim3(T_LANES), p->w[H_LDS_BYTES], s, *p);
   return hipGetLastError();
 }

@@ -405,8 +405,11 @@ class Stream:
             s_r, s_c = strides[i]
             opnds.append(TL.Operand(ESIZE[o["dtype"]], s_r, s_c, o["addr"] % 16))
             i += 1
-        try:
-            TL.plan(tmpl, R, C, opnds)
-        except ValueError:
-            return "resource"
-        return None
+        # feasible on the standard VM or on its wide variant
+        for nv_max in (TL.NV_MAX, TL.NV_WIDE):
+            try:
+                TL.plan(tmpl, R, C, opnds, nv_max)
+                return None
+            except ValueError:
+                pass
+        return "resource"

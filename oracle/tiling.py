@@ -22,6 +22,13 @@ design notes):
   up to NV_MAX = 5 chunks of V = 8 elements in registers.  Rows of a tile go
   to P = next_pow2(tr) lane groups of g = T / P lanes.  A tile is feasible iff
   P <= T and NV = ceil((tc + pad) / (g V)) <= NV_MAX.
+* Wide variant.  The VM also comes as a wide build whose one tile register
+  holds NV_WIDE = 10 chunks per lane (the same per-lane register budget spent
+  on one tile value instead of three): the same rules with NV_MAX replaced by
+  NV_WIDE.  The encoder uses it for programs that keep every tile value in
+  the accumulator, where the standard plan has no feasible tile, or where it
+  puts one row in a tile and the wide plan at least two with the same LDS
+  staging.  plan() takes the variant's chunk limit.
 * Alignment pad.  pad = V - 1 if some unit-stride operand does not start every
   row on a 16-byte boundary, else 0: a misaligned row may need one more chunk.
 * hardware_align_div(n, k, W) = W * ceil(ceil(n / k) / W) with W = 64 V = 512
@@ -64,6 +71,7 @@ from dataclasses import dataclass, field
 T_LANES = 256
 VEC = 8
 NV_MAX = 5
+NV_WIDE = 10
 W_ALIGN = 64 * VEC
 G_WG = 512
 A_TICKS = 7812
@@ -185,14 +193,14 @@ def alignment_pad(R: int, ops) -> int:
     return 0
 
 
-def geometry(tr: int, tc: int, pad: int):
+def geometry(tr: int, tc: int, pad: int, nv_max: int = NV_MAX):
     """(P, g, NV, feasible) of a tr x tc tile."""
     P = next_pow2(tr)
     if P > T_LANES:
         return P, 0, 0, False
     g = T_LANES // P
     nv = cdiv(tc + pad, g * VEC)
-    return P, g, nv, nv <= NV_MAX
+    return P, g, nv, nv <= nv_max
 
 
 def shrink_path(template: str, R: int, C: int):
@@ -246,8 +254,9 @@ def cost(R: int, C: int, tr: int, tc: int, ops) -> int:
     return rounds * (A_TICKS + BYTE_TICKS * var_b) + BYTE_TICKS * inv_b
 
 
-def plan(template: str, R: int, C: int, ops) -> Plan:
-    """Tile choice and header for a vector-template graph over [R, C]."""
+def plan(template: str, R: int, C: int, ops, nv_max: int = NV_MAX) -> Plan:
+    """Tile choice and header for a vector-template graph over [R, C], for
+    the VM variant whose tile register holds nv_max chunks per lane."""
     pad = alignment_pad(R, ops)
     p = Plan(template, R, C, pad, [])
     if R == 0 or C == 0:
@@ -255,7 +264,7 @@ def plan(template: str, R: int, C: int, ops) -> Plan:
     p.path = shrink_path(template, R, C)
     best = None
     for (tr, tc) in p.path:
-        P, g, nv, ok = geometry(tr, tc, pad)
+        P, g, nv, ok = geometry(tr, tc, pad, nv_max)
         if not ok:
             p.costs.append(None)
             continue

@@ -67,12 +67,19 @@ def test_error_paths(ectx):
     with pytest.raises(dvm.DvmError) as e:
         p.launch()                               # encode-only context
     assert e.value.status == L.ERR_DEVICE
-    # an infeasible row reduce (rows wider than a tile can hold) is unsupported
+    # an infeasible row reduce (rows wider than even a wide tile can hold:
+    # 256 lanes x 10 chunks x 8 = 20480 columns) is unsupported
     g3 = dvm.Graph(ectx)
-    y = g3.input(TD(1 << 20, "f32", (2, 20000)))
+    y = g3.input(TD(1 << 20, "f32", (2, 20481)))
     with pytest.raises(dvm.DvmError) as e:
         g3.op("reduce_sum", y, out=TD(2 << 20, "f32", (2, 1)), live=True)
     assert e.value.status == L.ERR_UNSUPPORTED
+    # rows up to that width run on the wide VM
+    g4 = dvm.Graph(ectx)
+    y = g4.input(TD(1 << 20, "f32", (2, 20480)))
+    g4.op("reduce_sum", y, out=TD(2 << 20, "f32", (2, 1)), live=True)
+    h = g4.flush().header()
+    assert h["kernel_type"] == 2 and h["nv"] == 10 and h["g"] == 256
 
 
 # ---------------------------------------------------------------------------
@@ -89,7 +96,7 @@ def dense(shape):
 ESZ = {"f32": 4, "bf16": 2, "u8": 1}
 
 
-def oracle_plan(tmpl, shape, operands):
+def oracle_plan(tmpl, shape, operands, nv_max=TL.NV_MAX):
     """operands: list of (shape, strides, dtype, addr) over the dominant shape."""
     sts = []
     for sh, st, _, _ in operands:
@@ -100,7 +107,7 @@ def oracle_plan(tmpl, shape, operands):
         sts.append(full)
     R, C, col = TL.collapse(tmpl, shape, sts)
     ops = [TL.Operand(ESZ[dt], sr, sc, addr % 16) for (_, _, dt, addr), (sr, sc) in zip(operands, col)]
-    return TL.plan(tmpl, R, C, ops)
+    return TL.plan(tmpl, R, C, ops, nv_max)
 
 
 def check_header(p, plan):
@@ -144,18 +151,33 @@ def test_encoder_tiling_equals_oracle_rowreduce(ectx):
         base = (1 << 32) + (int(rg.integers(0, 8)) * 2 if rg.random() < 0.3 else 0)
         g = dvm.Graph(ectx)
         x = g.input(TD(base, dt, shape))
+        opnds = [(shape, dense(shape), dt, base), (shape, dense(shape), dt, 5 << 32)]
+        plans = {}
+        for nvm in (TL.NV_MAX, TL.NV_WIDE):
+            try:
+                plans[nvm] = oracle_plan(TL.ROWREDUCE, shape, opnds, nvm)
+            except ValueError:
+                plans[nvm] = None
         try:
             CP.softmax(g, x, out=TD(5 << 32, dt, shape))
         except dvm.DvmError as e:
             assert e.status == L.ERR_UNSUPPORTED
-            with pytest.raises(ValueError):
-                oracle_plan(TL.ROWREDUCE, shape, [(shape, dense(shape), dt, base),
-                                                  (shape, dense(shape), dt, 5 << 32)])
+            assert plans[TL.NV_MAX] is None and plans[TL.NV_WIDE] is None
             continue
         p = g.flush()
-        plan = oracle_plan(TL.ROWREDUCE, shape, [(shape, dense(shape), dt, base),
-                                                 (shape, dense(shape), dt, 5 << 32)])
-        check_header(p, plan)
+        # softmax keeps its one tile value in the accumulator: the wide VM
+        # whenever the standard plan is infeasible or holds one row per tile
+        # and the wide plan holds more with the same staging of x
+        p5, p10 = plans[TL.NV_MAX], plans[TL.NV_WIDE]
+        esz = ESZ[dt]
+        vec = base % 4 == 0 and (len(shape) == 1 or (cols * esz) % 4 == 0)
+
+        def staged(pl):
+            return pl.body_tile >= 2 and vec and pl.nv * 256 * 16 * (esz // 2) <= 76 * 1024
+
+        wide = p5 is None or (p5.tr == 1 and p5.n_c == 1 and p10.tr >= 2 and staged(p10) >= staged(p5))
+        assert p.header()["kernel_type"] == (2 if wide else 0), (shape, dt)
+        check_header(p, p10 if wide else p5)
 
 
 def test_encoder_layernorm_workload_headers(ectx):

@@ -198,7 +198,8 @@ def _collapsed_operands(shape, n):
 
 @pytest.mark.parametrize("tmpl,shape", [("elemwise", (513, 1031)), ("rowreduce", (1000, 5120)),
                                         ("rowreduce", (280, 3001)), ("elemwise", (3, 9)),
-                                        ("rowreduce", (777, 16))])
+                                        ("rowreduce", (777, 16)), ("rowreduce", (3000, 6484)),
+                                        ("rowreduce", (9, 15000))])
 def test_tilemap_bit_exact(dvm, ctx, tmpl, shape):
     """The VM's element -> tile and tile -> workgroup maps equal the oracle's."""
     import torch
@@ -225,7 +226,7 @@ def test_tilemap_bit_exact(dvm, ctx, tmpl, shape):
     tm = TL.ELEMWISE if tmpl == "elemwise" else TL.ROWREDUCE
     col = TL.collapse(tm, shape, _collapsed_operands(shape, 2))
     ops = [TL.Operand(4, s_r, s_c, 0) for s_r, s_c in col[2]]
-    plan = TL.plan(tm, col[0], col[1], ops)
+    plan = TL.plan(tm, col[0], col[1], ops, TL.NV_WIDE if h["kernel_type"] == 2 else TL.NV_MAX)
     assert (h["tr"], h["tc"], h["block_dim"], h["body_tile"], h["grid"], h["g"], h["nv"]) == \
         (plan.tr, plan.tc, plan.block_dim, plan.body_tile, plan.grid, plan.g, plan.nv)
     et, ew = TL.element_tile_map(plan)
