@@ -91,7 +91,7 @@ typedef struct dvm_program dvm_program;
 /* Code header of an encoded program (DVM review page, section 4.3: tile
  * count block_dim, tiles per core body_tile, kernel type) plus the tiling. */
 typedef struct {
-  uint32_t kernel_type;  /* 0 VECTOR, 1 MIX (matmul) */
+  uint32_t kernel_type;  /* 0 VECTOR, 1 MIX (matmul), 2 VECTOR wide (one tile register of 10 chunks) */
   uint32_t tmpl;         /* 0 elementwise, 1 row reduce, 2 reduce-all, 3 matmul */
   uint32_t block_dim;    /* number of tiles */
   uint32_t body_tile;    /* tiles per workgroup */
