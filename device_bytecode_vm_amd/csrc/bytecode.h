@@ -89,6 +89,7 @@ enum Hdr : int {
   H_MM_B = 36,       // MIX: arg index of B [K, N] (bf16, unit stride along N)
   H_PROF_LO = 37,    // profiling launches only: device address of the per-workgroup
   H_PROF_HI = 38,    //   cycle counters (5 x uint64 per workgroup)
+  H_RED_OFF = 39,    // wide build: byte offset of the reduction buffers in dynamic LDS
 };
 
 // MIX kernel geometry: the output tile (header H_TR x H_TC) is one of the MIX
@@ -118,6 +119,11 @@ __host__ __device__ constexpr int mm_lds_bytes(int tm, int tn) {
 //    indexed by the lane.
 // The budget keeps two workgroups resident per compute unit (160 KB of LDS).
 constexpr uint32_t LDS_BUDGET = 76u * 1024u;
+// The wide build keeps its cross-wave reduction buffers (and the reduce-all
+// flag) in the dynamic area, reserved only by programs that use them, so two
+// of its workgroups may take the whole 160 KB.
+constexpr uint32_t LDS_BUDGET_WIDE = 80u * 1024u;
+constexpr uint32_t RED_LDS_BYTES = N_LDSBUF * (T_LANES / 64) * 4 + 16;
 
 // Argument table entry (8 words): pointer, dtype, flags, column stride, row
 // stride (elements, in the collapsed [R, C] iteration space) and the byte

@@ -1315,11 +1315,26 @@ __device__ __forceinline__ void vm_main(float (*s_red)[T_LANES / 64], int& s_las
 #undef PROF_ENTER
 }
 
+// Cross-wave reduction buffers and the reduce-all flag: static arrays in the
+// standard build, a reserved part of the dynamic area in the wide build.
+#ifdef DVM_WIDE
+#define DVM_RED_BUFFERS()                                                                              \
+  extern __shared__ __attribute__((aligned(16))) char dlds[];                                          \
+  const uint32_t red_off = ((KW*)__builtin_amdgcn_kernarg_segment_ptr())[H_RED_OFF];                 \
+  float(*s_red)[T_LANES / 64] = reinterpret_cast<float(*)[T_LANES / 64]>(dlds + red_off);             \
+  int& s_last = *reinterpret_cast<int*>(dlds + red_off + N_LDSBUF * (T_LANES / 64) * 4);
+constexpr uint32_t LDS_CAP = LDS_BUDGET_WIDE;
+#else
+#define DVM_RED_BUFFERS()                                     \
+  __shared__ float s_red[N_LDSBUF][T_LANES / 64];             \
+  __shared__ int s_last;                                      \
+  extern __shared__ __attribute__((aligned(16))) char dlds[];
+constexpr uint32_t LDS_CAP = LDS_BUDGET;
+#endif
+
 extern "C" __global__ void __launch_bounds__(T_LANES) __attribute__((amdgpu_waves_per_eu(2, 2)))
 DVM_SYM(dvm_vm_vector)(const Program prog) {
-  __shared__ float s_red[N_LDSBUF][T_LANES / 64];
-  __shared__ int s_last;
-  extern __shared__ __attribute__((aligned(16))) char dlds[];
+  DVM_RED_BUFFERS()
   (void)prog;
   vm_main<false>(s_red, s_last, dlds);
 }
@@ -1328,9 +1343,7 @@ DVM_SYM(dvm_vm_vector)(const Program prog) {
 // per-workgroup cycle split at the address in header words H_PROF_LO/HI.
 extern "C" __global__ void __launch_bounds__(T_LANES) __attribute__((amdgpu_waves_per_eu(2, 2)))
 DVM_SYM(dvm_vm_vector_prof)(const Program prog) {
-  __shared__ float s_red[N_LDSBUF][T_LANES / 64];
-  __shared__ int s_last;
-  extern __shared__ __attribute__((aligned(16))) char dlds[];
+  DVM_RED_BUFFERS()
   (void)prog;
   vm_main<true>(s_red, s_last, dlds);
 }
@@ -1340,7 +1353,7 @@ extern "C" hipError_t DVM_SYM(dvm_launch_vector_kernel)(const Program* p, unsign
   static bool attr_set = false;
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute((const void*)DVM_SYM(dvm_vm_vector), hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       (int)LDS_BUDGET);
+                                       (int)LDS_CAP);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
@@ -1352,7 +1365,7 @@ extern "C" hipError_t DVM_SYM(dvm_launch_vector_prof_kernel)(const Program* p, u
   static bool attr_set = false;
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute((const void*)DVM_SYM(dvm_vm_vector_prof),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)LDS_BUDGET);
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)LDS_CAP);
     if (e != hipSuccess) return e;
     attr_set = true;
   }

@@ -189,10 +189,28 @@ def test_encoder_layernorm_workload_headers(ectx):
         bt = g.input(TD(3 << 34, "f32", (h,)))
         CP.layer_norm(g, x, gm, bt, W.LN_EPS, out=TD(4 << 34, "bf16", (r, h)))
         p = g.flush()
-        plan = oracle_plan(TL.ROWREDUCE, (r, h), [((r, h), dense((r, h)), "bf16", 1 << 34),
-                                                  ((h,), (1,), "f32", 2 << 34), ((h,), (1,), "f32", 3 << 34),
-                                                  ((r, h), dense((r, h)), "bf16", 4 << 34)])
-        check_header(p, plan)
+        opnds = [((r, h), dense((r, h)), "bf16", 1 << 34), ((h,), (1,), "f32", 2 << 34),
+                 ((h,), (1,), "f32", 3 << 34), ((r, h), dense((r, h)), "bf16", 4 << 34)]
+        p5 = oracle_plan(TL.ROWREDUCE, (r, h), opnds)
+        p10 = oracle_plan(TL.ROWREDUCE, (r, h), opnds, TL.NV_WIDE)
+
+        def staged(pl, budget):
+            # x prefetched (bf16), then gamma and beta held as one shared fp32 row
+            if pl.body_tile < 2:
+                return 0, 0
+            off, pf, inv = 0, 0, 0
+            for sz, kind in ((pl.nv * 256 * 16, "pf"), (pl.nv * pl.g * 32, "inv"), (pl.nv * pl.g * 32, "inv")):
+                if off + sz <= budget:
+                    off += sz
+                    pf, inv = (pf + 1, inv) if kind == "pf" else (pf, inv + 1)
+            return pf, inv
+
+        s5 = staged(p5, 76 * 1024)
+        s10 = staged(p10, 80 * 1024 - (144 if p10.g > 64 else 0))
+        more = p10.tr > p5.tr and s10[0] >= s5[0] and s10[1] >= s5[1]
+        wide = more and (p5.tr == 1 or (p5.g > 64 and s5[1] == 2))
+        assert p.header()["kernel_type"] == (2 if wide else 0), (r, h)
+        check_header(p, p10 if wide else p5)
 
 
 # ---------------------------------------------------------------------------
