@@ -51,7 +51,8 @@ def parse():
 
 COPY_BYTES = 512 << 20          # bytes read (and written) by the calibration copy
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_dvm_vm_vector_layernorm_stream.txt")
-KERNEL_SOURCES = [os.path.join(ROOT, "device_bytecode_vm_amd", "csrc", f) for f in ("vm_vector.hip", "bytecode.h")]
+KERNEL_SOURCES = [os.path.join(ROOT, "device_bytecode_vm_amd", "csrc", f)
+                  for f in ("vm_vector.hip", "vm_vector_wide.hip", "bytecode.h")]
 
 
 def kernel_hash():
@@ -96,8 +97,10 @@ def traffic_from(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv):
     big_w = max(cw.values())
     f_scale = COPY_BYTES / (big_f * 1024.0)
     w_scale = COPY_BYTES / (big_w * 1024.0)
-    vf = counter_per_dispatch(fetch_csv, "dvm_vm_vector")
-    vw = counter_per_dispatch(write_csv, "dvm_vm_vector")
+    vf = {k: v for k, v in counter_per_dispatch(fetch_csv, "dvm_vm_vector").items() if k not in
+          counter_per_dispatch(fetch_csv, "_prof")}
+    vw = {k: v for k, v in counter_per_dispatch(write_csv, "dvm_vm_vector").items() if k not in
+          counter_per_dispatch(write_csv, "_prof")}
     n = min(len(vf), len(vw))
     fetch = sum(vf.values()) / len(vf) * 1024.0 * f_scale
     write = sum(vw.values()) / len(vw) * 1024.0 * w_scale
@@ -106,7 +109,8 @@ def traffic_from(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv):
            "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4)}
     os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
     with open(TRAFFIC_FILE, "w") as fh:
-        fh.write("# HBM traffic of dvm_vm_vector on the LayerNorm stream (see the counter commands in "
+        fh.write("# HBM traffic of the VECTOR VM (dvm_vm_vector, dvm_vm_vector_wide) on the LayerNorm stream "
+                 "(see the counter commands in "
                  "profiles/README.md)\n" + json.dumps(rec) + "\n")
     return rec
 
@@ -222,7 +226,10 @@ def layernorm_bench(args):
         "graphs_per_step": graphs / args.steps,
         "roofline": {"bound": "hbm", "achieved": round(kern_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(kern_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "kernel": "dvm_vm_vector", "launches_per_step": len(progs),
+                     "kernel": "dvm_vm_vector_wide + dvm_vm_vector", "launches_per_step": len(progs),
+                     "launches_by_kernel": {
+                         "dvm_vm_vector_wide": sum(1 for p in progs if p.header()["kernel_type"] == 2),
+                         "dvm_vm_vector": sum(1 for p in progs if p.header()["kernel_type"] == 0)},
                      "avg_launch_us": round(float(kern_ms.mean()) * 1e3, 3),
                      "bytes_per_launch_avg": round(step_bytes / len(progs), 1)},
         "largest_call_header": {k: hdr[k] for k in ("block_dim", "body_tile", "grid", "tr", "tc", "g", "nv",
