@@ -146,7 +146,7 @@ __host__ __device__ constexpr uint32_t arg_flags_word(uint32_t flags, uint64_t e
 }
 enum DType : uint32_t { DT_F32 = 0, DT_BF16 = 1, DT_U8 = 2 };
 enum ArgFlag : uint32_t {
-  AF_VEC = 1u,       // every chunk start is dword aligned: 128-bit path
+  AF_VEC = 1u,       // chunk starts aligned (bf16: to the element, else the dword): 64/128-bit path
 };
 
 // Opcodes (bits [7:0] of word 0).

@@ -807,10 +807,13 @@ struct Encoder {
     a[A_PTR_LO] = (uint32_t)p;
     a[A_PTR_HI] = (uint32_t)(p >> 32);
     a[A_DTYPE] = (uint32_t)t.dtype;
-    // vector accesses (8-element chunks) need dword-aligned chunk starts: the
-    // base, every row start and every tile start
+    // vector accesses (8-element chunks with 64- and 128-bit buffer accesses)
+    // need the base, every row start and every tile start aligned: to the
+    // element for bf16 (buffer accesses run in the unaligned access mode, so
+    // a bf16 row of odd length still moves whole chunks), to the dword for
+    // fp32 and u8
     const int64_t es = esize(t.dtype);
-    const int64_t al = 4;
+    const int64_t al = es == 2 ? 2 : 4;
     bool vec = sc == 1 && (int64_t)(p % al) == 0 && (plan.R <= 1 || ((sr * es) % al + al) % al == 0) &&
                (plan.n_c <= 1 || (plan.tc * es) % al == 0);
     const int64_t ext = extent_bytes(t);

@@ -170,7 +170,8 @@ def test_encoder_tiling_equals_oracle_rowreduce(ectx):
         # and the wide plan holds more with the same staging of x
         p5, p10 = plans[TL.NV_MAX], plans[TL.NV_WIDE]
         esz = ESZ[dt]
-        vec = base % 4 == 0 and (len(shape) == 1 or (cols * esz) % 4 == 0)
+        al = 2 if esz == 2 else 4   # vector accesses: bf16 element-aligned, fp32 dword-aligned
+        vec = base % al == 0 and (len(shape) == 1 or (cols * esz) % al == 0)
 
         def staged(pl):
             return pl.body_tile >= 2 and vec and pl.nv * 256 * 16 * (esz // 2) <= 76 * 1024

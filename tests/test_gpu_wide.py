@@ -40,7 +40,8 @@ def ctx(dvm):
 # cost model puts one row in a tile on either variant); rows of 10241 and
 # more fit only the wide one
 @pytest.mark.parametrize("rows,cols,kt", [(3, 6484, 0), (3000, 6484, WIDE), (3000, 8192, WIDE),
-                                          (64, 10241, WIDE), (40, 16384, WIDE), (7, 20480, WIDE)])
+                                          (64, 10241, WIDE), (40, 16384, WIDE), (7, 20480, WIDE),
+                                          (3000, 6485, WIDE), (3000, 6487, WIDE), (9, 12345, WIDE)])
 @pytest.mark.parametrize("dt", ["bf16", "f32"])
 def test_wide_softmax(dvm, ctx, rows, cols, kt, dt):
     import torch
