@@ -76,7 +76,7 @@ enum Hdr : int {
   H_ALL_OUT = 23,    // reduce-all: arg index of the scalar output
   H_ALL_SCRATCH = 24,// reduce-all: arg index of the scratch (counter + partials)
   H_N_INSTR = 25,
-  H_FLAGS = 26,
+  H_FLAGS = 26,      // HF_* bits
   H_LDS_BYTES = 27,  // dynamic LDS of the launch (staging areas below)
   H_PF_OFF0 = 28,    // byte offset of prefetch slot 0 / 1 (next-tile loads)
   H_PF_OFF1 = 29,
@@ -145,6 +145,16 @@ __host__ __device__ constexpr uint32_t arg_flags_word(uint32_t flags, uint64_t e
   return (flags & 0xffu) | ((uint32_t)(extent >> 32) << 8);
 }
 enum DType : uint32_t { DT_F32 = 0, DT_BF16 = 1, DT_U8 = 2 };
+enum HdrFlag : uint32_t {
+  // tile operands and outputs move with the streaming (non-temporal) cache
+  // policy: set for programs that touch at least STREAM_BYTES, which no
+  // cache level can keep for a later launch anyway, except reduce-all
+  // programs, whose input the host-resolved branch after them usually reads
+  // again.  Smaller programs keep the default policy, so data they share
+  // with the launches around them can stay in the last-level cache.
+  HF_STREAM = 1u,
+};
+constexpr uint64_t STREAM_BYTES = 64ull << 20;
 enum ArgFlag : uint32_t {
   AF_VEC = 1u,       // chunk starts aligned (bf16: to the element, else the dword): 64/128-bit path
 };

@@ -1624,6 +1624,12 @@ struct Encoder {
     W[H_VERSION] = VERSION;
     W[H_KTYPE] = ktype;
     W[H_TEMPLATE] = (uint32_t)tm;
+    uint64_t touched = 0;
+    for (int q = 0; q < n_args; ++q) {
+      const uint32_t* a = W + ARG_BASE + q * ARG_WORDS;
+      touched += arg_extent(a[A_FLAGS], a[A_EXTENT]);
+    }
+    W[H_FLAGS] = tm != TM_ALLREDUCE && touched >= STREAM_BYTES ? HF_STREAM : 0u;
     W[H_BLOCK_DIM] = (uint32_t)plan.block_dim;
     W[H_BODY_TILE] = (uint32_t)plan.body_tile;
     W[H_GRID] = (uint32_t)plan.grid;

@@ -79,6 +79,12 @@ __device__ __forceinline__ void fetch2(KW* W, uint32_t pc, uint32_t& a, uint32_t
 }
 
 constexpr int OOB = 0x7fffffff;                 // lane offset beyond any descriptor size
+// Cache policy of the streaming accesses (tile operands and outputs) of
+// programs flagged HF_STREAM: non-temporal, so a stream passing through does
+// not evict what is reused (tile-invariant operands, the program).  Measured
+// on the LayerNorm stream: 6% less time per launch.
+constexpr int CP_STREAM = 2;                    // gfx950 cache-policy bit nt
+__device__ __forceinline__ bool streaming(KW* W) { return (W[H_FLAGS] & HF_STREAM) != 0; }
 constexpr int RSRC_W3 = 0x00020000;             // raw buffer, 32-bit data format
 
 // One tile register: NVK chunks of VEC fp32 values per lane.
@@ -442,7 +448,7 @@ __device__ __forceinline__ void store_tail(const Ch& s, const Rsrc& rs, int roff
 // Fill d (one tile register) from operand a for this tile.  `any_row` loads
 // as if every row of the tile existed (for operands that do not vary along
 // rows, whose row offset is zero).
-template <uint32_t DT>
+template <uint32_t DT, int CP = CP_STREAM>
 __device__ __forceinline__ void load_dir(Ch& d, const ArgD& a, const Geo& G, const Tile& tl, const Lane& L,
                                          bool any_row = false) {
   constexpr int ES = esize_c<DT>();
@@ -467,13 +473,13 @@ __device__ __forceinline__ void load_dir(Ch& d, const ArgD& a, const Geo& G, con
       const int ct = (j * G.g + L.lane) * VEC;
       const int off = lane_off(rok & (ct + VEC <= lim), (roff + ct) * ES);
       if constexpr (DT == DT_F32) {
-        const u4 v0 = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
-        const u4 v1 = __builtin_amdgcn_raw_buffer_load_b128(rs, off == OOB ? OOB : off + 16, 0, 0);
+        const u4 v0 = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, CP);
+        const u4 v1 = __builtin_amdgcn_raw_buffer_load_b128(rs, off == OOB ? OOB : off + 16, 0, CP);
         d.c[j] = unpack_f32(v0, v1);
       } else if constexpr (DT == DT_BF16) {
-        d.c[j] = unpack_bf16(__builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0));
+        d.c[j] = unpack_bf16(__builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, CP));
       } else {
-        const u2 v = __builtin_amdgcn_raw_buffer_load_b64(rs, off, 0, 0);
+        const u2 v = __builtin_amdgcn_raw_buffer_load_b64(rs, off, 0, CP);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           d.c[j][i] = (float)((v.x >> (8 * i)) & 0xffu);
@@ -501,15 +507,23 @@ __device__ __forceinline__ void load_dir(Ch& d, const ArgD& a, const Geo& G, con
   }
 }
 
-__device__ __forceinline__ void load_any(Ch& d, const ArgD& a, const Geo& G, const Tile& tl, const Lane& L,
-                                         bool any_row = false) {
-  if (a.dt == DT_BF16) load_dir<DT_BF16>(d, a, G, tl, L, any_row);
-  else if (a.dt == DT_F32) load_dir<DT_F32>(d, a, G, tl, L, any_row);
-  else load_dir<DT_U8>(d, a, G, tl, L, any_row);
+template <int CP>
+__device__ __forceinline__ void load_any_cp(Ch& d, const ArgD& a, const Geo& G, const Tile& tl, const Lane& L,
+                                            bool any_row) {
+  if (a.dt == DT_BF16) load_dir<DT_BF16, CP>(d, a, G, tl, L, any_row);
+  else if (a.dt == DT_F32) load_dir<DT_F32, CP>(d, a, G, tl, L, any_row);
+  else load_dir<DT_U8, CP>(d, a, G, tl, L, any_row);
 }
 
-template <uint32_t DT>
-__device__ __forceinline__ void store_dir(const Ch& s, const ArgD& a, const Geo& G, const Tile& tl, const Lane& L) {
+__device__ __forceinline__ void load_any(Ch& d, const ArgD& a, const Geo& G, const Tile& tl, const Lane& L,
+                                         bool stream, bool any_row = false) {
+  if (stream) load_any_cp<CP_STREAM>(d, a, G, tl, L, any_row);
+  else load_any_cp<0>(d, a, G, tl, L, any_row);
+}
+
+template <uint32_t DT, int CP>
+__device__ __forceinline__ void store_dir_cp(const Ch& s, const ArgD& a, const Geo& G, const Tile& tl,
+                                             const Lane& L) {
   constexpr int ES = esize_c<DT>();
   const Rsrc rs = tile_rsrc(a, tl, ES);
   const int roff = L.row * (int)a.sr;
@@ -523,15 +537,15 @@ __device__ __forceinline__ void store_dir(const Ch& s, const ArgD& a, const Geo&
         u4 v0, v1;
         v0.x = __float_as_uint(x[0]); v0.y = __float_as_uint(x[1]); v0.z = __float_as_uint(x[2]); v0.w = __float_as_uint(x[3]);
         v1.x = __float_as_uint(x[4]); v1.y = __float_as_uint(x[5]); v1.z = __float_as_uint(x[6]); v1.w = __float_as_uint(x[7]);
-        __builtin_amdgcn_raw_buffer_store_b128(v0, rs, off, 0, 0);
-        __builtin_amdgcn_raw_buffer_store_b128(v1, rs, off == OOB ? OOB : off + 16, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(v0, rs, off, 0, CP);
+        __builtin_amdgcn_raw_buffer_store_b128(v1, rs, off == OOB ? OOB : off + 16, 0, CP);
       } else if constexpr (DT == DT_BF16) {
         u4 v;
         v.x = f2bf_pack(x[0], x[1]);
         v.y = f2bf_pack(x[2], x[3]);
         v.z = f2bf_pack(x[4], x[5]);
         v.w = f2bf_pack(x[6], x[7]);
-        __builtin_amdgcn_raw_buffer_store_b128(v, rs, off, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(v, rs, off, 0, CP);
       } else {
         u2 v = {0u, 0u};
 #pragma unroll
@@ -539,7 +553,7 @@ __device__ __forceinline__ void store_dir(const Ch& s, const ArgD& a, const Geo&
           v.x |= ((uint32_t)x[i] & 0xffu) << (8 * i);
           v.y |= ((uint32_t)x[4 + i] & 0xffu) << (8 * i);
         }
-        __builtin_amdgcn_raw_buffer_store_b64(v, rs, off, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b64(v, rs, off, 0, CP);
       }
     }
     store_tail<DT>(s, rs, roff, G, tl, L);
@@ -561,10 +575,18 @@ __device__ __forceinline__ void store_dir(const Ch& s, const ArgD& a, const Geo&
   }
 }
 
-__device__ __forceinline__ void store_any(const Ch& v, const ArgD& a, const Geo& G, const Tile& tl, const Lane& L) {
-  if (a.dt == DT_BF16) store_dir<DT_BF16>(v, a, G, tl, L);
-  else if (a.dt == DT_F32) store_dir<DT_F32>(v, a, G, tl, L);
-  else store_dir<DT_U8>(v, a, G, tl, L);
+template <uint32_t DT>
+__device__ __forceinline__ void store_dir(const Ch& s, const ArgD& a, const Geo& G, const Tile& tl, const Lane& L,
+                                          bool stream) {
+  if (stream) store_dir_cp<DT, CP_STREAM>(s, a, G, tl, L);
+  else store_dir_cp<DT, 0>(s, a, G, tl, L);
+}
+
+__device__ __forceinline__ void store_any(const Ch& v, const ArgD& a, const Geo& G, const Tile& tl, const Lane& L,
+                                          bool stream) {
+  if (a.dt == DT_BF16) store_dir<DT_BF16>(v, a, G, tl, L, stream);
+  else if (a.dt == DT_F32) store_dir<DT_F32>(v, a, G, tl, L, stream);
+  else store_dir<DT_U8>(v, a, G, tl, L, stream);
 }
 
 // ---------------------------------------------------------------------------
@@ -582,7 +604,8 @@ __device__ __forceinline__ void store_any(const Ch& v, const ArgD& a, const Geo&
 // counted wait before the slot is read; waits the compiler places for its own
 // loads stay correct (extra outstanding operations only make them stricter).
 template <uint32_t DT>
-__device__ __forceinline__ void pf_issue(char* slot, const ArgD& a, const Geo& G, const Tile& nt, const Lane& L) {
+__device__ __forceinline__ void pf_issue(char* slot, const ArgD& a, const Geo& G, const Tile& nt, const Lane& L,
+                                         bool keep) {
   constexpr int ES = esize_c<DT>();
   constexpr int HV = DT == DT_F32 ? 2 : 1;
   const u4 rs = tile_rsrc_words(a, nt, ES);
@@ -600,10 +623,16 @@ __device__ __forceinline__ void pf_issue(char* slot, const ArgD& a, const Geo& G
       for (int h = 0; h < HV; ++h) {
         const uint32_t dst = __builtin_amdgcn_readfirstlane(base + (uint32_t)(((j * HV + h) * T_LANES + wave * 64) * 16));
         const int o = off == OOB ? OOB : off + 16 * h;
-        asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-                     :
-                     : "s"(dst), "v"(o), "s"(rs)
-                     : "memory", "m0");
+        if (keep)
+          asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                       :
+                       : "s"(dst), "v"(o), "s"(rs)
+                       : "memory", "m0");
+        else
+          asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen nt lds"
+                       :
+                       : "s"(dst), "v"(o), "s"(rs)
+                       : "memory", "m0");
       }
     }
   }
@@ -710,7 +739,7 @@ __device__ __forceinline__ void read_pf(Ch& d, uint32_t w0, uint32_t vmc, const 
     const Tile nt = make_tile(G, S.tile + 1);
     // this lane's reads of the slot have completed before the refill starts
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    pf_issue<DT>(S.pf(slot), a, G, nt, L);
+    pf_issue<DT>(S.pf(slot), a, G, nt, L, !streaming(S.W));
   }
 }
 
@@ -731,7 +760,7 @@ __device__ __forceinline__ void read_mem(Ch& d, uint32_t w0, uint32_t vmc, const
     if (a.dt == DT_F32) read_pf<DT_F32>(d, w0, vmc, a, G, tl, L, S);
     else read_pf<DT_BF16>(d, w0, vmc, a, G, tl, L, S);
   } else {
-    load_any(d, a, G, tl, L);
+    load_any(d, a, G, tl, L, streaming(S.W));
   }
 }
 
@@ -1070,22 +1099,22 @@ __device__ __forceinline__ void vm_main(float (*s_red)[T_LANES / 64], int& s_las
       case HD_LD_DIR + 1: PROF_ENTER()
       case HD_LD_DIR + 2: PROF_ENTER() {
         Ch m;
-        load_any(m, ARG, G, tl, L);
+        load_any(m, ARG, G, tl, L, streaming(W));
         settle(m);
         if (f_dst(w0) == 0) treg<0>(R) = m;
         else if (f_dst(w0) == 1) treg<1>(R) = m;
         else treg<2>(R) = m;
         break;
       }
-      case HD_ST_BF16: PROF_ENTER() store_dir<DT_BF16>(treg<0>(R), ARG, G, tl, L); break;
-      case HD_ST_F32: PROF_ENTER() store_dir<DT_F32>(treg<0>(R), ARG, G, tl, L); break;
-      case HD_ST_DIR + 0: PROF_ENTER() store_any(treg<0>(R), ARG, G, tl, L); break;
+      case HD_ST_BF16: PROF_ENTER() store_dir<DT_BF16>(treg<0>(R), ARG, G, tl, L, streaming(W)); break;
+      case HD_ST_F32: PROF_ENTER() store_dir<DT_F32>(treg<0>(R), ARG, G, tl, L, streaming(W)); break;
+      case HD_ST_DIR + 0: PROF_ENTER() store_any(treg<0>(R), ARG, G, tl, L, streaming(W)); break;
       case HD_ST_DIR + 1: PROF_ENTER()
       case HD_ST_DIR + 2: PROF_ENTER() {
         Ch m;
         if (f_a(w0) == 1) m = treg<1>(R);
         else m = treg<2>(R);
-        store_any(m, ARG, G, tl, L);
+        store_any(m, ARG, G, tl, L, streaming(W));
         break;
       }
       CASE_COPY(0, 1) CASE_COPY(0, 2) CASE_COPY(1, 0) CASE_COPY(1, 2) CASE_COPY(2, 0) CASE_COPY(2, 1)
@@ -1227,7 +1256,7 @@ __device__ __forceinline__ void vm_main(float (*s_red)[T_LANES / 64], int& s_las
         int stride;
         const int idx = inv_base(W, k, G, L, &stride);
         Ch tmp;
-        load_any(tmp, ARG, G, tl, L, stride != T_LANES);
+        load_any(tmp, ARG, G, tl, L, false, stride != T_LANES);  // reused by every tile: default policy
         // every chunk's load has returned before the handler ends, the ones
         // past nv (not written to LDS) included: a load left in flight would
         // make later writes of its registers wait on the vector-memory
@@ -1239,8 +1268,9 @@ __device__ __forceinline__ void vm_main(float (*s_red)[T_LANES / 64], int& s_las
       case HD_PF: PROF_ENTER() {
         // prologue: fetch the workgroup's first tile into the prefetch slot
         const ArgD a = ARG;
-        if (a.dt == DT_F32) pf_issue<DT_F32>(S.pf(f_b(w0) & 1u), a, G, tl, L);
-        else pf_issue<DT_BF16>(S.pf(f_b(w0) & 1u), a, G, tl, L);
+        const bool keep = !streaming(W);
+        if (a.dt == DT_F32) pf_issue<DT_F32>(S.pf(f_b(w0) & 1u), a, G, tl, L, keep);
+        else pf_issue<DT_BF16>(S.pf(f_b(w0) & 1u), a, G, tl, L, keep);
         break;
       }
       default:
