@@ -1482,6 +1482,14 @@ struct Encoder {
     W[H_VERSION] = VERSION;
     W[H_KTYPE] = KT_MIX;
     W[H_TEMPLATE] = TM_MATMUL;
+    {
+      uint64_t touched = 0;
+      for (int q = 0; q < n_args; ++q) {
+        const uint32_t* a = W + ARG_BASE + q * ARG_WORDS;
+        touched += arg_extent(a[A_FLAGS], a[A_EXTENT]);
+      }
+      W[H_FLAGS] = touched >= STREAM_BYTES ? HF_STREAM : 0u;  // epilogue stores only
+    }
     W[H_BLOCK_DIM] = (uint32_t)plan.block_dim;
     W[H_BODY_TILE] = (uint32_t)plan.body_tile;
     W[H_GRID] = (uint32_t)plan.grid;

@@ -372,7 +372,10 @@ __device__ __forceinline__ void epi_load(TV<U>& d, uint32_t ai, KW* W, const Rou
   for (int u = 0; u < U; ++u) chunk_load(d.v + 8 * u, a, C.m0, C.n0, C.r[u], C.c8, C.ok[u]);
 }
 
-template <int U>
+// Output stores take the cache policy CP: non-temporal (2) for programs
+// flagged HF_STREAM, whose output no cache level keeps for a later launch
+// and would otherwise push out the A and B panels the tiles share.
+template <int U, int CP>
 __device__ __forceinline__ void epi_store(const TV<U>& s, const ArgD& a, const Round<U>& C) {
   const int es = esize(a.dt);
   const Rsrc rs = rsrc_at(a, (C.m0 * a.sr + C.n0 * (int64_t)a.sc) * es);
@@ -386,11 +389,11 @@ __device__ __forceinline__ void epi_store(const TV<U>& s, const ArgD& a, const R
       if (a.dt == DT_F32) {
         const u4 p = {__float_as_uint(x[0]), __float_as_uint(x[1]), __float_as_uint(x[2]), __float_as_uint(x[3])};
         const u4 q = {__float_as_uint(x[4]), __float_as_uint(x[5]), __float_as_uint(x[6]), __float_as_uint(x[7])};
-        __builtin_amdgcn_raw_buffer_store_b128(p, rs, lane_off(ok, base), 0, 0);
-        __builtin_amdgcn_raw_buffer_store_b128(q, rs, lane_off(ok, base + 16), 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(p, rs, lane_off(ok, base), 0, CP);
+        __builtin_amdgcn_raw_buffer_store_b128(q, rs, lane_off(ok, base + 16), 0, CP);
       } else if (a.dt == DT_BF16) {
         const u4 p = {f2bf_pack(x[0], x[1]), f2bf_pack(x[2], x[3]), f2bf_pack(x[4], x[5]), f2bf_pack(x[6], x[7])};
-        __builtin_amdgcn_raw_buffer_store_b128(p, rs, lane_off(ok, base), 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(p, rs, lane_off(ok, base), 0, CP);
       } else {
         uint32_t lo = 0, hi = 0;
 #pragma unroll
@@ -398,8 +401,8 @@ __device__ __forceinline__ void epi_store(const TV<U>& s, const ArgD& a, const R
           lo |= (uint32_t)(uint8_t)x[j] << (8 * j);
           hi |= (uint32_t)(uint8_t)x[4 + j] << (8 * j);
         }
-        __builtin_amdgcn_raw_buffer_store_b32(lo, rs, lane_off(ok, base), 0, 0);
-        __builtin_amdgcn_raw_buffer_store_b32(hi, rs, lane_off(ok, base + 4), 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b32(lo, rs, lane_off(ok, base), 0, CP);
+        __builtin_amdgcn_raw_buffer_store_b32(hi, rs, lane_off(ok, base + 4), 0, CP);
       }
     } else {
 #pragma unroll
@@ -463,7 +466,8 @@ __device__ __forceinline__ void run_epilogue(KW* W, TV<U>& t0, const Round<U>& C
       case OP_STORE: {
         TV<U> m;
         pick(m, f_a(w0), t0, t1, t2);
-        epi_store(m, read_arg(W, w1), C);
+        if (W[H_FLAGS] & HF_STREAM) epi_store<U, 2>(m, read_arg(W, w1), C);
+        else epi_store<U, 0>(m, read_arg(W, w1), C);
         break;
       }
       case OP_COPY: {
