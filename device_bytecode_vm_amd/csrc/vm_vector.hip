@@ -2,9 +2,10 @@
 // reduce-all templates) on gfx950.
 //
 // It follows the VM algorithm of the DVM paper review page (section 4.4):
-// each workgroup computes its tile count and its tile range from the code
-// header, and for every tile decodes the body instruction by instruction and
-// runs the matching virtual-instruction routine.  Decoding is wave-uniform:
+// each workgroup finds its tiles from the code header (workgroup b runs
+// tiles b, b + grid, ..., at most body_tile of them), and for every tile
+// decodes the body instruction by instruction and runs the matching
+// virtual-instruction routine.  Decoding is wave-uniform:
 // the program sits in the kernarg segment and every word is read with a scalar
 // load (the next instruction's words are fetched while the current one runs),
 // so the dispatch is a tree of scalar compares on one pre-decoded handler byte
@@ -716,13 +717,13 @@ __device__ __forceinline__ void wait_vm(uint32_t n) {
 struct Ctx {
   KW* W;
   char* lds;
-  uint32_t tile, t_end;
+  uint32_t tile, t_step, t_end;
   __device__ __forceinline__ char* pf(uint32_t k) const { return lds + W[H_PF_OFF0 + k]; }
   __device__ __forceinline__ char* inv(uint32_t k) const { return lds + W[H_INV_OFF0 + k]; }
 };
 
 // Read from prefetch slot `slot` (the tile was fetched while the previous one
-// ran), then refill the slot with this workgroup's next tile.
+// ran), then refill the slot with this workgroup's next tile (t_step on).
 template <uint32_t DT>
 __device__ __forceinline__ void read_pf(Ch& d, uint32_t w0, uint32_t vmc, const ArgD& a, const Geo& G,
                                         const Tile& tl, const Lane& L, const Ctx& S) {
@@ -735,8 +736,8 @@ __device__ __forceinline__ void read_pf(Ch& d, uint32_t w0, uint32_t vmc, const 
   // not cover
   if (chunk_cols(a, tl, esize_c<DT>(), tl.tre) < tl.tce)
     load_tail<DT>(d, tile_rsrc(a, tl, esize_c<DT>()), L.row * (int)a.sr, G, tl, L, L.rok);
-  if ((f_flags(w0) & FL_ISSUE) && S.tile + 1 < S.t_end) {
-    const Tile nt = make_tile(G, S.tile + 1);
+  if ((f_flags(w0) & FL_ISSUE) && S.tile + S.t_step < S.t_end) {
+    const Tile nt = make_tile(G, S.tile + S.t_step);
     // this lane's reads of the slot have completed before the refill starts
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     pf_issue<DT>(S.pf(slot), a, G, nt, L, !streaming(S.W));
@@ -955,7 +956,6 @@ __device__ __forceinline__ void vm_main(float (*s_red)[T_LANES / 64], int& s_las
 #define PROF_ENTER() \
   if constexpr (PROF) p_ent = __builtin_amdgcn_s_memtime();
   const uint32_t block_dim = W[H_BLOCK_DIM];
-  const uint32_t body_tile = W[H_BODY_TILE];
 
   Geo G;
   G.g = (int)W[H_G];
@@ -970,9 +970,12 @@ __device__ __forceinline__ void vm_main(float (*s_red)[T_LANES / 64], int& s_las
   const int gs = G.g < 64 ? G.g : 64;
   const int wave = tid >> 6;
 
-  const uint32_t t_begin = blockIdx.x * body_tile;
-  uint32_t t_end = t_begin + body_tile;
-  if (t_end > block_dim) t_end = block_dim;
+  // Workgroup b runs tiles b, b + grid, b + 2 grid, ... (at most body_tile of
+  // them): at any moment the resident workgroups work on neighbouring tiles,
+  // so the streams they read and write advance together through memory.
+  const uint32_t t_begin = blockIdx.x;
+  const uint32_t t_step = gridDim.x;
+  const uint32_t t_end = block_dim;
 
   Regs R;
 #pragma unroll
@@ -982,6 +985,7 @@ __device__ __forceinline__ void vm_main(float (*s_red)[T_LANES / 64], int& s_las
   Ctx S;
   S.W = W;
   S.lds = dlds;
+  S.t_step = t_step;
   S.t_end = t_end;
 
   Tile tl;
@@ -1005,7 +1009,7 @@ __device__ __forceinline__ void vm_main(float (*s_red)[T_LANES / 64], int& s_las
     if constexpr (PROF) p_top = __builtin_amdgcn_s_memtime();
     if (pc >= pc_end) {
       if (in_pro) in_pro = false;
-      else ++tile;
+      else tile += t_step;
       if (tile >= t_end) break;
       tl = make_tile(G, tile);
       pc = W[H_BODY_BEGIN];

@@ -116,13 +116,15 @@ def test_coverage_and_ranges_brute_force():
         p = TL.plan(tmpl, R, C, ops)
         tiles, wgs = TL.element_tile_map(p)
         assert (tiles >= 0).all()
-        # workgroup ranges are contiguous, disjoint and cover [0, block_dim)
+        # workgroup tile sets are strided by grid, disjoint, at most
+        # body_tile long and together cover [0, block_dim) once
         seen = []
         for b in range(p.grid):
-            lo, hi = TL.tile_range(b, p.body_tile, p.block_dim)
-            assert 0 < hi - lo <= p.body_tile
-            seen.extend(range(lo, hi))
-        assert seen == list(range(p.block_dim))
+            ts = list(TL.workgroup_tiles(b, p.grid, p.block_dim))
+            assert 0 < len(ts) <= p.body_tile and ts[0] == b
+            assert all(t1 - t0 == p.grid for t0, t1 in zip(ts, ts[1:]))
+            seen.extend(ts)
+        assert sorted(seen) == list(range(p.block_dim))
         assert p.grid <= TL.G_WG
         # the choice is a least-cost feasible candidate, earliest on ties
         feas = [(c, i) for i, c in enumerate(p.costs) if c is not None]
