@@ -107,16 +107,18 @@ __host__ __device__ constexpr int mm_lds_bytes(int tm, int tn) {
 }
 
 // LDS staging (per workgroup, dynamic):
-//  * prefetch slot: NV chunks x T lanes x 16 bytes x (element size / 2)
+//  * prefetch slot: NVK chunks x T lanes x 16 bytes x (element size / 2)
+//    (NVK = the VM build's chunk count, NV_MAX or NV_WIDE, whatever the
+//    tile's NV: every chunk position has its bytes)
 //    halves; lane t's data for chunk j, half h sits at ((j * halves + h) * T +
 //    t) * 16, written by a direct-to-LDS buffer load of that lane and read back
 //    by the same lane, which then issues the next tile's load into the same
 //    bytes (one buffer: the read completes before the refill is issued);
 //  * invariant slot: an operand that is the same for every tile, held as fp32,
 //    8 elements (32 bytes) per lane and chunk.  A slot shared by the row groups
-//    (the operand does not vary along rows) holds one row: NV x g x 32 bytes,
-//    indexed by the lane's position in its row; otherwise NV x T x 32 bytes,
-//    indexed by the lane.
+//    (the operand does not vary along rows) holds one row: NVK x g x 32
+//    bytes, indexed by the lane's position in its row; otherwise NVK x T x 32
+//    bytes, indexed by the lane.
 // The budget keeps two workgroups resident per compute unit (160 KB of LDS).
 constexpr uint32_t LDS_BUDGET = 76u * 1024u;
 // The wide build keeps its cross-wave reduction buffers (and the reduce-all

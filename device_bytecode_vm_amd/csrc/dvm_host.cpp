@@ -1231,7 +1231,7 @@ struct Encoder {
   uint32_t src_ops(uint32_t w0, uint32_t w1) const {
     const uint32_t f = f_flags(w0);
     if (f & FL_INV) return 0;
-    if (f & FL_PF) return (f & FL_ISSUE) ? (uint32_t)plan.nv * halves(w1) : 0u;
+    if (f & FL_PF) return (f & FL_ISSUE) ? (uint32_t)nvm * halves(w1) : 0u;
     return load_ops(w1);
   }
   uint32_t vm_ops(uint32_t w0, uint32_t w1) const {
@@ -1241,7 +1241,7 @@ struct Encoder {
       case OP_STORE: return store_ops(w1);
       case OP_LOAD_ROW:
       case OP_STORE_ROW: return 1u;
-      case OP_PF: return (uint32_t)plan.nv * halves(w1);
+      case OP_PF: return (uint32_t)nvm * halves(w1);
       case OP_LDS_INV: return load_ops(w1);
       default: return 0u;
     }
@@ -1300,7 +1300,7 @@ struct Encoder {
           // an operand that does not vary along rows is held once (one row),
           // shared by the lane groups of all rows
           const bool shared = sr == 0;
-          const uint32_t sz = (uint32_t)plan.nv * (uint32_t)(shared ? plan.g : T_LANES) * 32u;
+          const uint32_t sz = (uint32_t)nvm * (uint32_t)(shared ? plan.g : T_LANES) * 32u;
           if (off + sz > budget) continue;
           inv_slot[s] = n_inv;
           W[H_INV_OFF0 + n_inv] = off;
@@ -1310,7 +1310,7 @@ struct Encoder {
           pro.push_back((uint32_t)arg_of[s]);
           ++n_inv;
         } else if (!invariant && n_pf < 2 && (a[A_FLAGS] & AF_VEC) && sc == 1 && (es == 2 || es == 4)) {
-          const uint32_t sz = (uint32_t)plan.nv * T_LANES * 16u * (uint32_t)(es / 2);
+          const uint32_t sz = (uint32_t)nvm * T_LANES * 16u * (uint32_t)(es / 2);
           if (off + sz > budget) continue;
           pf_slot[s] = n_pf;
           W[H_PF_OFF0 + n_pf] = off;

@@ -617,7 +617,9 @@ __device__ __forceinline__ void pf_issue(char* slot, const ArgD& a, const Geo& G
   const int lim = chunk_cols(a, nt, ES, nt.tre);
 #pragma unroll
   for (int j = 0; j < NVK; ++j) {
-    if (j < G.nv) {
+    {
+      // all NVK chunks: those past the tile's columns are masked (their LDS
+      // bytes get zeros)
       const int ct = (j * G.g + L.lane) * VEC;
       const int off = lane_off(rok & (ct + VEC <= lim), (roff + ct) * ES);  // whole chunks only
 #pragma unroll
@@ -645,7 +647,10 @@ __device__ __forceinline__ void pf_read(Ch& d, const char* slot, const Geo& G, i
 #pragma unroll
   for (int j = 0; j < NVK; ++j) {
     // a chunk past nv re-reads chunk 0 (its values are masked downstream)
-    const int jj = j < G.nv ? j : 0;
+    // every slot holds NVK chunks; those past nv hold values that are
+    // masked downstream (no per-chunk condition, so no per-chunk constants
+    // stay live across the interpreter loop)
+    const int jj = j;
     const u4 v = *(const u4*)(slot + ((jj * HV) * T_LANES + tid) * 16);
     if constexpr (DT == DT_F32) {
       const u4 w = *(const u4*)(slot + ((jj * HV + 1) * T_LANES + tid) * 16);
@@ -667,7 +672,7 @@ __device__ __forceinline__ int inv_base(KW* W, uint32_t k, const Geo& G, const L
 __device__ __forceinline__ void inv_write(const Ch& c, char* slot, const Geo& G, int idx, int stride) {
 #pragma unroll
   for (int j = 0; j < NVK; ++j) {
-    if (j < G.nv) {
+    {
       const V8 x = c.c[j];
       const f4 a = {x[0], x[1], x[2], x[3]};
       const f4 b = {x[4], x[5], x[6], x[7]};
@@ -680,7 +685,7 @@ __device__ __forceinline__ void inv_write(const Ch& c, char* slot, const Geo& G,
 __device__ __forceinline__ void inv_read(Ch& c, const char* slot, const Geo& G, int idx, int stride) {
 #pragma unroll
   for (int j = 0; j < NVK; ++j) {
-    const int jj = j < G.nv ? j : 0;
+    const int jj = j;
     const f4 a = *(const f4*)(slot + (jj * stride + idx) * 32);
     const f4 b = *(const f4*)(slot + (jj * stride + idx) * 32 + 16);
     V8 r;
@@ -1166,7 +1171,7 @@ __device__ __forceinline__ void vm_main(float (*s_red)[T_LANES / 64], int& s_las
         const char* b2 = S.inv(k2);
 #pragma unroll
         for (int j = 0; j < NVK; ++j) {
-          const int jj = j < G.nv ? j : 0;
+          const int jj = j;
           const f4 a0 = *(const f4*)(b1 + (jj * s1 + i1) * 32), a1 = *(const f4*)(b1 + (jj * s1 + i1) * 32 + 16);
           const f4 c0 = *(const f4*)(b2 + (jj * s2 + i2) * 32), c1 = *(const f4*)(b2 + (jj * s2 + i2) * 32 + 16);
           const float sc[VEC] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};

@@ -173,10 +173,12 @@ def test_encoder_tiling_equals_oracle_rowreduce(ectx):
         al = 2 if esz == 2 else 4   # vector accesses: bf16 element-aligned, fp32 dword-aligned
         vec = base % al == 0 and (len(shape) == 1 or (cols * esz) % al == 0)
 
-        def staged(pl):
-            return pl.body_tile >= 2 and vec and pl.nv * 256 * 16 * (esz // 2) <= 76 * 1024
+        def staged(pl, nvk):
+            # slots hold the VM build's nvk chunks per lane
+            return pl.body_tile >= 2 and vec and nvk * 256 * 16 * (esz // 2) <= 76 * 1024
 
-        wide = p5 is None or (p5.tr == 1 and p5.n_c == 1 and p10.tr >= 2 and staged(p10) >= staged(p5))
+        wide = p5 is None or (p5.tr == 1 and p5.n_c == 1 and p10.tr >= 2 and
+                              staged(p10, TL.NV_WIDE) >= staged(p5, TL.NV_MAX))
         assert p.header()["kernel_type"] == (2 if wide else 0), (shape, dt)
         check_header(p, p10 if wide else p5)
 
@@ -195,19 +197,20 @@ def test_encoder_layernorm_workload_headers(ectx):
         p5 = oracle_plan(TL.ROWREDUCE, (r, h), opnds)
         p10 = oracle_plan(TL.ROWREDUCE, (r, h), opnds, TL.NV_WIDE)
 
-        def staged(pl, budget):
-            # x prefetched (bf16), then gamma and beta held as one shared fp32 row
+        def staged(pl, budget, nvk):
+            # x prefetched (bf16), then gamma and beta held as one shared fp32
+            # row; slots hold the VM build's nvk chunks per lane
             if pl.body_tile < 2:
                 return 0, 0
             off, pf, inv = 0, 0, 0
-            for sz, kind in ((pl.nv * 256 * 16, "pf"), (pl.nv * pl.g * 32, "inv"), (pl.nv * pl.g * 32, "inv")):
+            for sz, kind in ((nvk * 256 * 16, "pf"), (nvk * pl.g * 32, "inv"), (nvk * pl.g * 32, "inv")):
                 if off + sz <= budget:
                     off += sz
                     pf, inv = (pf + 1, inv) if kind == "pf" else (pf, inv + 1)
             return pf, inv
 
-        s5 = staged(p5, 76 * 1024)
-        s10 = staged(p10, 80 * 1024 - (144 if p10.g > 64 else 0))
+        s5 = staged(p5, 76 * 1024, TL.NV_MAX)
+        s10 = staged(p10, 80 * 1024 - (144 if p10.g > 64 else 0), TL.NV_WIDE)
         more = p10.tr > p5.tr and s10[0] >= s5[0] and s10[1] >= s5[1]
         wide = more and (p5.tr == 1 or (p5.g > 64 and s5[1] == 2))
         assert p.header()["kernel_type"] == (2 if wide else 0), (r, h)
