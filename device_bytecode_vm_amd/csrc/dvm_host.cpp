@@ -1679,18 +1679,15 @@ dvm_status encode_buffer(dvm_graph* g, dvm_program** out) {
   if (!p) return fail(DVM_ERR_INTERNAL, "out of host memory");
   Encoder enc(g, g->buf, p);
   dvm_status st = enc.run();
-  // The wide VM for programs that keep every tile value in the accumulator,
-  // when the wide plan puts more rows in a tile with the same LDS staging and
-  // either a standard tile holds a single row, or the standard rows span
-  // waves and the program scales and shifts by two staged invariant operands
-  // (LayerNorm: its reductions then stay inside a wave; measured 6% faster
-  // at 5120 columns, while softmax and RMSNorm at that width were 5% slower
-  // on the wide VM and stay standard); and where no standard tile fits.
+  // The wide VM for row-reduction programs that keep every tile value in the
+  // accumulator, when the wide plan puts more rows in a tile with the same
+  // LDS staging (half the interpreter work per byte, and rows of up to 2560
+  // columns keep their reductions inside a wave: measured 5-25% faster for
+  // softmax, RMSNorm and LayerNorm bodies at 5120 columns), and wherever no
+  // standard tile fits the rows.  Elementwise programs stay standard.
   const bool acc_only = st == DVM_OK && p->prog.w[H_KTYPE] == KT_VECTOR && enc.treg_hi == 0 &&
-                        enc.plan.n_c == 1 && enc.plan.block_dim > 0;
-  const bool one_row = acc_only && enc.plan.tr == 1;
-  const bool ln_like = acc_only && enc.plan.g > 64 && enc.staged_inv == 2;
-  if (one_row || ln_like || (st != DVM_OK && enc.plan_failed)) {
+                        enc.plan.n_c == 1 && enc.plan.block_dim > 0 && enc.plan.tmpl == TM_ROWREDUCE;
+  if (acc_only || (st != DVM_OK && enc.plan_failed)) {
     const std::string err = g_err;
     dvm_program* q = new (std::nothrow) dvm_program();
     if (q) {

@@ -1,8 +1,9 @@
 """GPU parity of the wide VM variant (one tile register of 10 chunks per lane).
 
-The encoder runs a program on the wide VM when every tile value stays in the
-accumulator and either no standard tile fits its rows (rows of 10241 to 20480
-columns) or a standard tile holds a single row and a wide one two or more.
+The encoder runs a row-reduction program on the wide VM when every tile value
+stays in the accumulator and either no standard tile fits its rows (rows of
+10241 to 20480 columns) or a wide tile holds more rows than a standard one
+with the same LDS staging.
 These cases check that choice from the header and the results against the
 oracle: softmax and RMSNorm over long rows (bf16 within 2 ulp, fp32 within
 1e-5 of the largest value), ragged row ends bit for bit under the oracle's
