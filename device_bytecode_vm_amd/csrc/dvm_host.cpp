@@ -11,6 +11,7 @@
 #include <algorithm>
 #include <array>
 #include <chrono>
+#include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -1669,15 +1670,96 @@ struct Encoder {
 };
 
 // ===========================================================================
+// Bytecode clean-up before tiling: constant propagation and dead-instruction
+// elimination (named as encoder work on the DVM paper review page, section
+// 5.2), restricted to rewrites that leave every stored value bit-identical.
+//  - x * 1, 1 * x, x / 1, x - (+0), x + (-0) and (-0) + x equal x exactly in
+//    IEEE arithmetic (signed zeros, infinities and NaNs included): the op
+//    becomes a cast of x to its output dtype.  (x + (+0) turns -0 into +0 and
+//    stays.)
+//  - A cast to the input's own dtype whose result is not stored is an alias:
+//    later readers read the input itself.
+//  - An op whose result is neither stored (live, or not released by flush
+//    time) nor read by a kept op is dropped; so is, in turn, its producer.
+// Matmul graphs are left as they are.
+// ===========================================================================
+void simplify_ops(const dvm_graph* g, const std::vector<OpRec>& in, std::vector<OpRec>* out) {
+  out->clear();
+  for (const OpRec& o : in)
+    if (o.op == DVM_OP_MATMUL) {
+      *out = in;
+      return;
+    }
+  auto stored = [&](int64_t s) { return g->vals[s].live || !g->vals[s].released; };
+  // graphs hold a few dozen ops: small lists instead of per-slot tables
+  std::vector<std::pair<int64_t, int64_t>> alias;  // (slot, the slot it reads as)
+  std::vector<OpRec> fw;
+  fw.reserve(in.size());
+  for (OpRec o : in) {
+    for (int k = 0; k < o.n_in; ++k)
+      for (const auto& a : alias)
+        if (a.first == o.in[k]) o.in[k] = a.second;
+    if (o.n_in == 1 && (o.scalar_pos == 0 || o.scalar_pos == 1)) {
+      const float c = o.scalar;
+      const bool on_right = o.scalar_pos == 1;
+      const bool pos0 = c == 0.f && !std::signbit(c), neg0 = c == 0.f && std::signbit(c);
+      if ((o.op == DVM_OP_MUL && c == 1.f) || (o.op == DVM_OP_DIV && on_right && c == 1.f) ||
+          (o.op == DVM_OP_SUB && on_right && pos0) || (o.op == DVM_OP_ADD && neg0)) {
+        o.op = DVM_OP_CAST;
+        o.scalar_pos = -1;
+        o.scalar = 0.f;
+      }
+    }
+    if (o.op == DVM_OP_CAST && g->vals[o.in[0]].t.dtype == g->vals[o.out].t.dtype && !stored(o.out)) {
+      alias.emplace_back(o.out, o.in[0]);
+      continue;
+    }
+    fw.push_back(o);
+  }
+  std::vector<int64_t> need;
+  std::vector<char> keep(fw.size(), 0);
+  size_t n_keep = 0;
+  for (size_t i = fw.size(); i-- > 0;) {
+    const OpRec& o = fw[i];
+    if (!stored(o.out) && std::find(need.begin(), need.end(), o.out) == need.end()) continue;
+    keep[i] = 1;
+    ++n_keep;
+    for (int k = 0; k < o.n_in; ++k) need.push_back(o.in[k]);
+  }
+  if (n_keep == fw.size() && alias.empty() && fw.size() == in.size()) {
+    *out = std::move(fw);
+    return;
+  }
+  for (size_t i = 0; i < fw.size(); ++i)
+    if (keep[i]) out->push_back(fw[i]);
+}
+
+// ===========================================================================
 // Flushing
 // ===========================================================================
 dvm_status encode_buffer(dvm_graph* g, dvm_program** out) {
   *out = nullptr;
   if (g->buf.empty()) return DVM_OK;
   auto t0 = std::chrono::steady_clock::now();
+  std::vector<OpRec> ops;
+  simplify_ops(g, g->buf, &ops);
+  if (ops.empty()) {
+    // every op was dead: nothing to run, and nothing is stored
+    for (auto& o : g->buf) {
+      Val& v = g->vals[o.out];
+      v.pending = false;
+      v.stored = false;
+      v.lost = true;
+    }
+    std::vector<OpRec> done;
+    done.swap(g->buf);
+    drop_uses(g, done);
+    g->stats.graphs++;
+    return DVM_OK;
+  }
   dvm_program* p = new (std::nothrow) dvm_program();
   if (!p) return fail(DVM_ERR_INTERNAL, "out of host memory");
-  Encoder enc(g, g->buf, p);
+  Encoder enc(g, ops, p);
   dvm_status st = enc.run();
   // The wide VM for row-reduction programs that keep every tile value in the
   // accumulator, when the wide plan puts more rows in a tile with the same
@@ -1691,7 +1773,7 @@ dvm_status encode_buffer(dvm_graph* g, dvm_program** out) {
     const std::string err = g_err;
     dvm_program* q = new (std::nothrow) dvm_program();
     if (q) {
-      Encoder w(g, g->buf, q);
+      Encoder w(g, ops, q);
       w.wide();
       const dvm_status sw = w.run();
       const bool take = sw == DVM_OK && (st != DVM_OK || (w.plan.tr > enc.plan.tr && w.staged_pf >= enc.staged_pf &&
@@ -1748,7 +1830,7 @@ dvm_status flush_launch(dvm_graph* g, int reason, int32_t* launched) {
   g->flush_log.push_back({(int32_t)g->buf.size(), (int32_t)reason});
   dvm_program* p = nullptr;
   dvm_status st = encode_buffer(g, &p);
-  if (st != DVM_OK) return st;
+  if (st != DVM_OK || !p) return st;
   if (g->ctx->device >= 0) {
     st = launch(g->ctx, p, g->stream);
     if (st == DVM_OK) {
