@@ -135,13 +135,16 @@ int64_t extent_bytes(const dvm_tensor& t) {
 //  * the shrink path goes outer -> inner (rows first, then columns) by
 //    doubling the split count k;
 //  * cost in integer ticks (1/15625 us): G = 512 resident workgroups (two
-//    per CU), A = 7812 ticks (about 0.5 us) per tile, 1 tick per byte per
-//    workgroup (8 TB/s shared by G workgroups);
+//    per CU), A = 78125 ticks (5 us) per round of tiles, 1 tick per byte
+//    per workgroup (8 TB/s shared by G workgroups).  A is the measured
+//    marginal cost of one more round on latency-bound calls (LayerNorm over
+//    1385 rows of 5120: 3 rounds 21.8 us, 2 rounds 15.4 us, of which the
+//    bytes account for about 1.3 us);
 //    cost = ceil(n_tiles / G) (A + var_bytes) + inv_bytes; least cost wins,
 //    earlier (larger) candidates win ties.
 // ===========================================================================
 namespace tiling {
-constexpr int64_t T = T_LANES, V = VEC, W = 64 * VEC, G = 512, A = 7812, BT = 1;
+constexpr int64_t T = T_LANES, V = VEC, W = 64 * VEC, G = 512, A = 78125, A_MM = 7812, BT = 1;
 
 struct Operand {
   int64_t esize, sr, sc, base_mod16;
@@ -282,8 +285,9 @@ void header(int64_t block_dim, int64_t* body_tile, int64_t* grid, int64_t g_res 
 // MATMUL graphs: K pinned; output tiles from the MIX kernel's variants (tm,
 // tn, resident workgroups G_e), largest first.  With G_e workgroups sharing
 // 8 TB/s and 2.5 PFLOP/s, a byte costs G_e / 512 ticks and a flop G_e / 160000:
-// cost = ceil(n_tiles / G_e) (A + ceil(var_bytes G_e / 512) + ceil(2 tm tn K G_e / 160000))
-//        + ceil(inv_bytes G_e / 512); least cost wins, ties to the earlier entry.
+// cost = ceil(n_tiles / G_e) (A_MM + ceil(var_bytes G_e / 512) + ceil(2 tm tn K G_e / 160000))
+//        + ceil(inv_bytes G_e / 512), A_MM = 7812 ticks (0.5 us: a MIX tile's fixed
+// work is small next to its K loop); least cost wins, ties to the earlier entry.
 struct MmTile {
   int64_t tm, tn, g;
 };
@@ -306,7 +310,7 @@ bool plan_matmul(int64_t M, int64_t N, int64_t K, int64_t a_es, int64_t b_es, co
       const bool invariant = (o.sr == 0 || n_r == 1) && (o.sc == 0 || n_c == 1);
       (invariant ? inv_b : var_b) += touched;
     }
-    const int64_t per_tile = A + cdiv(var_b * t.g, 512) + cdiv(2 * t.tm * t.tn * K * t.g, 160000);
+    const int64_t per_tile = A_MM + cdiv(var_b * t.g, 512) + cdiv(2 * t.tm * t.tn * K * t.g, 160000);
     const int64_t c = cdiv(n_r * n_c, t.g) * per_tile + cdiv(inv_b * t.g, 512);
     if (!found || c < best) {
       found = true;
@@ -1762,11 +1766,12 @@ dvm_status encode_buffer(dvm_graph* g, dvm_program** out) {
   Encoder enc(g, ops, p);
   dvm_status st = enc.run();
   // The wide VM for row-reduction programs that keep every tile value in the
-  // accumulator, when the wide plan puts more rows in a tile with the same
-  // LDS staging (half the interpreter work per byte, and rows of up to 2560
-  // columns keep their reductions inside a wave: measured 5-25% faster for
-  // softmax, RMSNorm and LayerNorm bodies at 5120 columns), and wherever no
-  // standard tile fits the rows.  Elementwise programs stay standard.
+  // accumulator, when the wide plan puts more rows in a tile and either keeps
+  // the LDS staging or runs one tile per workgroup (half the interpreter work
+  // per byte, and rows of up to 2560 columns keep their reductions inside a
+  // wave: measured 5-25% faster for softmax, RMSNorm and LayerNorm bodies at
+  // 5120 columns), and wherever no standard tile fits the rows.  Elementwise
+  // programs stay standard.
   const bool acc_only = st == DVM_OK && p->prog.w[H_KTYPE] == KT_VECTOR && enc.treg_hi == 0 &&
                         enc.plan.n_c == 1 && enc.plan.block_dim > 0 && enc.plan.tmpl == TM_ROWREDUCE;
   if (acc_only || (st != DVM_OK && enc.plan_failed)) {
@@ -1776,8 +1781,11 @@ dvm_status encode_buffer(dvm_graph* g, dvm_program** out) {
       Encoder w(g, ops, q);
       w.wide();
       const dvm_status sw = w.run();
-      const bool take = sw == DVM_OK && (st != DVM_OK || (w.plan.tr > enc.plan.tr && w.staged_pf >= enc.staged_pf &&
-                                                         w.staged_inv >= enc.staged_inv));
+      // (staging matters only where a workgroup runs more than one tile)
+      const bool take = sw == DVM_OK &&
+                        (st != DVM_OK || (w.plan.tr > enc.plan.tr &&
+                                          (w.plan.body_tile == 1 ||
+                                           (w.staged_pf >= enc.staged_pf && w.staged_inv >= enc.staged_inv))));
       if (take) {
         delete p;
         p = q;

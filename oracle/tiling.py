@@ -26,9 +26,10 @@ design notes):
   holds NV_WIDE = 10 chunks per lane (the same per-lane register budget spent
   on one tile value instead of three): the same rules with NV_MAX replaced by
   NV_WIDE.  The encoder uses it for programs that keep every tile value in
-  the accumulator, where the standard plan has no feasible tile, or where it
-  puts one row in a tile and the wide plan at least two with the same LDS
-  staging.  plan() takes the variant's chunk limit.
+  the accumulator and reduce rows, where the standard plan has no feasible
+  tile, or where the wide plan puts more rows in a tile and either keeps the
+  LDS staging or runs one tile per workgroup.  plan() takes the variant's
+  chunk limit.
 * Alignment pad.  pad = V - 1 if some unit-stride operand does not start every
   row on a 16-byte boundary, else 0: a misaligned row may need one more chunk.
 * hardware_align_div(n, k, W) = W * ceil(ceil(n / k) / W) with W = 64 V = 512
@@ -39,9 +40,11 @@ design notes):
   then, at tr = 1, tc = min(C, had(C, k, W)) for k = 2, 4, ... until tc stops
   changing or reaches W.  Consecutive duplicates are dropped.
 * Cost (integer "ticks", 1 tick = 1/15625 us): G = 512 resident workgroups
-  (two per compute unit), A = 7812 ticks (about 0.5 us) of fixed work per
-  tile, and 1 tick per byte a workgroup moves (8 TB/s shared by G workgroups
-  is 15625 bytes/us each):
+  (two per compute unit), A = 78125 ticks (5 us) of fixed time per round of
+  tiles, and 1 tick per byte a workgroup moves (8 TB/s shared by G workgroups
+  is 15625 bytes/us each).  A is measured on MI355X: on latency-bound calls
+  (LayerNorm over 1385 rows of 5120) one more round of tiles cost 6.4 us, of
+  which the bytes account for about 1.3 us:
   cost = ceil(n_tiles / G) * (A + var_bytes) + inv_bytes, where
   var_bytes are the bytes one tile touches in operands that change from tile
   to tile and inv_bytes those of tile-invariant operands, loaded once per
@@ -54,8 +57,9 @@ design notes):
   Each entry runs with its own number G_e of resident workgroups, which share
   the chip's 8 TB/s and 2.5 PFLOP/s (bf16 matrix peak).  In the same ticks a
   byte costs G_e / 512 and a flop G_e / 160000, so a candidate costs
-  ceil(n_tiles / G_e) * (A + ceil(var_bytes G_e / 512) + ceil(flops G_e / 160000))
-  + ceil(inv_bytes G_e / 512), with var_bytes the A and B panels one tile reads
+  ceil(n_tiles / G_e) * (A_MM + ceil(var_bytes G_e / 512) + ceil(flops G_e / 160000))
+  + ceil(inv_bytes G_e / 512), with A_MM = 7812 ticks (0.5 us; a MIX tile's
+  fixed work is small next to its K loop), var_bytes the A and B panels one tile reads
   (tm K + K tn elements) plus its varying epilogue operand and output bytes and
   flops = 2 tm tn K.  The least cost wins; ties go to the earlier (larger)
   entry.
@@ -78,7 +82,8 @@ NV_MAX = 5
 NV_WIDE = 10
 W_ALIGN = 64 * VEC
 G_WG = 512
-A_TICKS = 7812
+A_TICKS = 78125
+A_MM_TICKS = 7812
 BYTE_TICKS = 1
 
 ELEMWISE, ROWREDUCE, ALLREDUCE, MATMUL = "elemwise", "rowreduce", "allreduce", "matmul"
@@ -305,7 +310,7 @@ def plan_matmul(M: int, N: int, K: int, a_esize: int, b_esize: int, epi_ops) -> 
                 inv_b += touched
             else:
                 var_b += touched
-        per_tile = A_TICKS + cdiv(var_b * ge, 512) + cdiv(2 * tm * tn * K * ge, 160000)
+        per_tile = A_MM_TICKS + cdiv(var_b * ge, 512) + cdiv(2 * tm * tn * K * ge, 160000)
         c = cdiv(n_r * n_c, ge) * per_tile + cdiv(inv_b * ge, 512)
         p.costs.append(c)
         if best is None or c < best[0]:

@@ -58,7 +58,8 @@ def test_profiled_launch_matches_and_splits(dvm, ctx):
     # runs inside a handler are not dispatches of their own)
     w = p2.words()
     n_pro, n_body = (w[15] - w[14]) // 2, (w[17] - w[16]) // 2
-    tiles = np.minimum(h["body_tile"], h["block_dim"] - np.arange(h["grid"]) * h["body_tile"])
+    # workgroup b runs tiles b, b + grid, ... below block_dim
+    tiles = np.array([len(range(b, h["block_dim"], h["grid"])) for b in range(h["grid"])])
     assert (n >= tiles).all() and (n <= n_pro + tiles * n_body).all()
     for t in np.unique(tiles):
         assert len(np.unique(n[tiles == t])) == 1

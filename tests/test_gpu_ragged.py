@@ -58,9 +58,10 @@ def _device(arr, dtype, gap):
 
 
 # (rows, whole chunks per row, tiles per workgroup at least): one tile of one
-# row over 256 lanes (direct loads); 20 rows of 8 lanes per tile and 1 row of
-# 256 lanes per tile (reduction across waves), both with prefetched loads
-SHAPES = [(3, 37, 1), (20000, 37, 2), (1500, 400, 2)]
+# row over 256 lanes (direct loads); tens of rows of 4 or 8 lanes per tile
+# (the wide or the standard build, by remainder) and 2 rows of 128 lanes per
+# tile (reduction across waves), all with prefetched loads
+SHAPES = [(3, 37, 1), (50000, 37, 2), (5000, 400, 2)]
 
 
 @pytest.mark.parametrize("rem", range(1, 8))

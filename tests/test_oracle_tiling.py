@@ -28,10 +28,10 @@ def test_sqrt_add_workload_choice_by_hand():
     assert [tc for _, tc in p.path] == [528903, 264704, 132608, 66560, 33280, 16896, 8704,
                                         4608, 2560, 1536, 1024, 512]
     # one 256-lane row holds at most 5 * 256 * 8 = 10240 columns; costs worked
-    # by hand: ceil(tiles / 512) * (7812 + 12 * tc) for the feasible tail
+    # by hand: ceil(tiles / 512) * (78125 + 12 * tc) for the feasible tail
     # (61, 115, 207, 345, 517, 1034 tiles)
     assert p.costs[:6] == [None] * 6
-    assert p.costs[6:] == [112260, 63108, 38532, 26244, 2 * 20100, 3 * 13956]
+    assert p.costs[6:] == [182573, 133421, 108845, 96557, 2 * 90413, 3 * 84269]
     assert (p.tr, p.tc, p.block_dim, p.body_tile, p.grid) == (1, 1536, 345, 1, 345)
     assert (p.P, p.g, p.nv, p.pad) == (1, 256, 1, 0)
 
@@ -47,7 +47,7 @@ def test_layernorm_rows_choice_by_hand():
     assert p.costs[:-2] == [None] * 9
     # tr=2: 500 tiles in one round, x and y vary (2*5120*2 bytes each), gamma
     # and beta are invariant (5120*4 bytes each); tr=1: 1000 tiles, two rounds
-    assert p.costs[-2:] == [(7812 + 40960) + 40960, 2 * (7812 + 20480) + 40960]
+    assert p.costs[-2:] == [(78125 + 40960) + 40960, 2 * (78125 + 20480) + 40960]
     assert (p.tr, p.tc, p.block_dim, p.body_tile, p.grid, p.g, p.nv) == (2, 5120, 500, 1, 500, 128, 5)
 
 
@@ -58,14 +58,14 @@ def test_softmax_misaligned_rows_by_hand():
     assert TL.geometry(2, 3001, 7) == (2, 128, 3, True)
     assert TL.geometry(3, 3001, 7) == (4, 64, 6, False)
     p = TL.plan(TL.ROWREDUCE, 280, 3001, [s, o])
-    # tr=2: 140 tiles, 1 round of (7812 + 2*3001*2*2); tr=1: 280 tiles, still
-    # 1 round, of (7812 + 3001*2*2): the smaller tile wins
-    assert p.costs[-2:] == [31820, 19816]
+    # tr=2: 140 tiles, 1 round of (78125 + 2*3001*2*2); tr=1: 280 tiles, still
+    # 1 round, of (78125 + 3001*2*2): the smaller tile wins
+    assert p.costs[-2:] == [102133, 90129]
     assert p.tr == 1 and p.block_dim == 280
     # with 4000 rows the rounds differ (4 against 8) and the 2-row tile wins
     p = TL.plan(TL.ROWREDUCE, 4000, 3001, [s, o])
     i2 = [tr for tr, _ in p.path].index(2)
-    assert p.costs[i2] == 4 * 31820 and p.costs[-1] == 8 * 19816
+    assert p.costs[i2] == 4 * 102133 and p.costs[-1] == 8 * 90129
     assert p.tr == 2 and p.block_dim == 2000
 
 
