@@ -465,6 +465,9 @@ def ifelse_bench(args):
     yy = W.device_normal((nmax, C), seed=13)
     out = torch.empty_like(yy)
     s = torch.empty((), dtype=torch.float32, device="cuda")
+    # the host reads the sum through pinned memory: the copy is queued behind
+    # the reduce-all and the graph's sync waits for both (one round trip)
+    s_host = torch.empty((), dtype=torch.float32, pin_memory=True)
     nbytes = float(sum(16.0 * r * C for r, _ in shapes))
     g = dvm.Graph(ctx, stream)
     taken = []
@@ -475,8 +478,10 @@ def ifelse_bench(args):
             x = (xp if c else xn)[:r]
             vx, vy = g.input(x), g.input(yy[:r])
             g.op("reduce_sum", vx, out=s, live=True, axis=0x7FFFFFFF)
+            g.flush_launch()
+            s_host.copy_(s, non_blocking=True)
             g.sync()
-            sv = float(s.item())
+            sv = float(s_host)
             taken.append(sv > 0)
             g.op("add" if sv > 0 else "sub", vx, vy, out=out[:r], live=True)
             g.flush_launch()
