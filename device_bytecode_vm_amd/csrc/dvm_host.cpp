@@ -237,10 +237,18 @@ void shrink_path(int tmpl, int64_t R, int64_t C, std::vector<std::pair<int64_t, 
   auto push = [&](int64_t a, int64_t b) {
     if (path->empty() || path->back() != std::make_pair(a, b)) path->push_back({a, b});
   };
+  // each row count is followed by its power-of-two floor, the largest tile
+  // whose rows fill their lane groups (tr = 3 leaves one of 4 idle)
+  auto push_rows = [&](int64_t tr, int64_t tc) {
+    push(tr, tc);
+    int64_t f = 1;
+    while (f * 2 <= tr) f *= 2;
+    push(f, tc);
+  };
   if (tmpl == TM_ROWREDUCE) {
     for (int64_t k = 1;; k *= 2) {
       const int64_t tr = cdiv(R, k);
-      push(tr, C);
+      push_rows(tr, C);
       if (tr <= 1) break;
     }
     return;
@@ -248,7 +256,7 @@ void shrink_path(int tmpl, int64_t R, int64_t C, std::vector<std::pair<int64_t, 
   const int64_t tc0 = std::min(C, had(C, 1, W));
   for (int64_t k = 1;; k *= 2) {
     const int64_t tr = cdiv(R, k);
-    push(tr, tc0);
+    push_rows(tr, tc0);
     if (tr <= 1) break;
   }
   int64_t prev = tc0;

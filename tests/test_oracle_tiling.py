@@ -42,13 +42,28 @@ def test_layernorm_rows_choice_by_hand():
     gam = Operand(4, 0, 1)
     bet = Operand(4, 0, 1)
     p = TL.plan(TL.ROWREDUCE, 1000, 5120, [x, gam, bet, y])
-    assert [tr for tr, _ in p.path] == [1000, 500, 250, 125, 63, 32, 16, 8, 4, 2, 1]
+    # ceil(R / k) for k = 1, 2, 4, ..., each followed by its power-of-two floor
+    assert [tr for tr, _ in p.path] == [1000, 512, 500, 256, 250, 128, 125, 64, 63, 32, 16, 8, 4, 2, 1]
     # 4 rows of 5120 need 10 chunks per lane; 2 rows need 5 (g = 128)
-    assert p.costs[:-2] == [None] * 9
+    assert p.costs[:-2] == [None] * 13
     # tr=2: 500 tiles in one round, x and y vary (2*5120*2 bytes each), gamma
     # and beta are invariant (5120*4 bytes each); tr=1: 1000 tiles, two rounds
     assert p.costs[-2:] == [(78125 + 40960) + 40960, 2 * (78125 + 20480) + 40960]
     assert (p.tr, p.tc, p.block_dim, p.body_tile, p.grid, p.g, p.nv) == (2, 5120, 500, 1, 500, 128, 5)
+
+
+def test_row_tiles_fill_their_lane_groups():
+    # 34640 rows of 5120 bf16 on the wide build: ceil(R / 8192) = 5 rows need 8
+    # lane groups of 32 lanes (20 chunks each, infeasible), ceil(R / 16384) = 3
+    # rows leave one of 4 groups idle; its floor 4 fills them and costs fewer
+    # rounds: 8660 tiles in 17 rounds against 11547 in 23
+    x, y = Operand(2, 5120, 1), Operand(2, 5120, 1)
+    p = TL.plan(TL.ROWREDUCE, 34640, 5120, [x, y], TL.NV_WIDE)
+    trs = [tr for tr, _ in p.path]
+    assert trs[trs.index(5):trs.index(5) + 4] == [5, 4, 3, 2]
+    c4, c3 = p.costs[trs.index(4)], p.costs[trs.index(3)]
+    assert c4 == 17 * (78125 + 4 * 5120 * 4) and c3 == 23 * (78125 + 3 * 5120 * 4)
+    assert (p.tr, p.block_dim, p.g, p.nv) == (4, 8660, 64, 10)
 
 
 def test_softmax_misaligned_rows_by_hand():
