@@ -160,8 +160,11 @@ dvm_status dvm_graph_infer_shape(dvm_graph* g, int32_t op, const dvm_value* in, 
                                  const dvm_attrs* attrs, dvm_tensor* out_shape);
 
 /* Encodes the buffered graph into a program (shape tiling + bytecode) and
- * empties the buffer; *out = NULL when the buffer is empty.  The program is
- * immutable and never cached; free it with dvm_program_free. */
+ * empties the buffer; *out = NULL when the buffer is empty or no buffered op
+ * has an effect (every result is released unread: such ops are dropped, as
+ * are x*1, x/1, x-(+0), x+(-0) and same-dtype casts nobody stores, which the
+ * encoder folds into their operand; results are bit-identical either way).
+ * The program is immutable and never cached; free it with dvm_program_free. */
 dvm_status dvm_flush(dvm_graph* g, dvm_program** out);
 
 /* Launches a program on the resident VM kernel of its kernel type, on
@@ -186,7 +189,8 @@ dvm_status dvm_launch(dvm_context* ctx, const dvm_program* p, void* stream);
 dvm_status dvm_launch_profiled(dvm_context* ctx, const dvm_program* p, void* stream, uint64_t* counters,
                                size_t n_counters);
 
-/* dvm_flush + dvm_launch on the graph's stream (no-op when empty). */
+/* dvm_flush + dvm_launch on the graph's stream (no-op when nothing is
+ * encoded; *launched = 0 then). */
 dvm_status dvm_graph_flush_launch(dvm_graph* g, int32_t* launched);
 
 /* Synchronisation point: flush + launch, then wait for the graph's stream.
