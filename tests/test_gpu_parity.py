@@ -81,11 +81,25 @@ def test_layernorm(dvm, ctx, rows, h):
 
 
 def test_layernorm_workload_sampled(dvm, ctx):
-    """Two calls of the LayerNorm stream at full size; rows sampled."""
+    """Three calls of the LayerNorm stream at full size; rows sampled.  The
+    third is tiled 4 rows at a time although no ceil(R / 2^j) equals 4 (the
+    row count comes from the power-of-two floor on the shrink path), so its
+    last tile is ragged in rows."""
     shapes = W.layernorm_shapes(0, 64)
     gam, bet = W.layernorm_params()
     g = np.random.default_rng(99)
-    for i in (0, int(np.argmax([r for r, _ in shapes]))):
+
+    def from_floor(r):
+        return r % 4 != 0 and all(-(-r // (1 << j)) != 4 for j in range(40))
+    i_floor = next(i for i, (r, _) in enumerate(shapes) if r > 20000 and from_floor(r))
+    from device_bytecode_vm_amd import composites as CP
+    from device_bytecode_vm_amd import TensorDesc as TD
+    r_f = shapes[i_floor][0]
+    gh = dvm.Graph(dvm.Context(-1))
+    CP.layer_norm(gh, gh.input(TD(1 << 34, "bf16", (r_f, W.H_LN))), gh.input(TD(2 << 34, "f32", (W.H_LN,))),
+                  gh.input(TD(3 << 34, "f32", (W.H_LN,))), W.LN_EPS, out=TD(4 << 34, "bf16", (r_f, W.H_LN)))
+    assert gh.flush().header()["tr"] == 4
+    for i in (0, int(np.argmax([r for r, _ in shapes])), i_floor):
         rows, h = shapes[i]
         say("layernorm_stream", i, rows)
         x = W.layernorm_x(0, i, rows, h)
