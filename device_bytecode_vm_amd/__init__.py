@@ -126,8 +126,9 @@ class Program:
         check(lib.dvm_program_words(self.h, buf, C.byref(cap)))
         return list(buf)
 
-    def launch(self, stream=None):
-        check(lib.dvm_launch(self.ctx.h, self.h, _stream_handle(stream)))
+    def launch(self, stream=None, ctx=None):
+        """Launch on `ctx` (default: the context that encoded the program)."""
+        check(lib.dvm_launch((ctx or self.ctx).h, self.h, _stream_handle(stream)))
 
     PROF_COUNTERS = 5
 
@@ -273,6 +274,13 @@ class Graph:
         prog = Program(q, self.ctx)
         prog._keep = keep
         return prog
+
+    def take_program(self):
+        """The oldest program an encode-only context flushed implicitly (at a
+        fusion boundary or a reduce-all), or None."""
+        q = C.c_void_p()
+        check(lib.dvm_graph_take_program(self.h, C.byref(q)))
+        return Program(q, self.ctx) if q.value else None
 
     def flush_launch(self) -> bool:
         fl = C.c_int32(0)

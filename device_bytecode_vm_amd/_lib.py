@@ -75,6 +75,7 @@ _sigs = {
     "dvm_context_destroy": (None, [VP]),
     "dvm_graph_create": (C.c_int, [VP, VP, P(VP)]),
     "dvm_graph_destroy": (None, [VP]),
+    "dvm_graph_take_program": (C.c_int, [VP, P(VP)]),
     "dvm_graph_input": (C.c_int, [VP, P(DvmTensor), P(C.c_int64)]),
     "dvm_graph_begin_group": (C.c_int, [VP]),
     "dvm_graph_end_group": (C.c_int, [VP, P(C.c_int32)]),

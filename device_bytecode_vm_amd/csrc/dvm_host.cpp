@@ -15,6 +15,8 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <deque>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -408,10 +410,17 @@ enum FlushReason { FR_EXPLICIT = 0, FR_SYNC = 1, FR_REDUCE_ALL = 2, FR_SHAPE = 3
 
 }  // namespace
 
+// Reduce-all scratch: a counter (4 bytes) and the per-tile partials from byte
+// 256.  One area per stream, allocated at the first reduce-all launched on
+// that stream: launches on one stream run one after another, and launches on
+// different streams never share the counter or the partials.
+constexpr size_t SCRATCH_BYTES = 4u << 20;
+constexpr size_t SCRATCH_PART_OFF = 256;
+
 struct dvm_context {
   int device = -1;
-  void* scratch = nullptr;  // reduce-all counter (4 bytes) + per-tile partials from byte 256
-  size_t scratch_bytes = 0;
+  std::mutex mu;  // guards scratch (graphs of one context may run on separate threads)
+  std::vector<std::pair<hipStream_t, void*>> scratch;
 };
 
 struct dvm_program {
@@ -433,7 +442,16 @@ struct dvm_graph {
   bool in_group = false;
   dvm_stats stats{};
   std::vector<std::pair<int32_t, int32_t>> flush_log;  // (ops, reason) per flushed graph
+  // encode-only contexts cannot launch: programs of implicit flushes wait
+  // here for dvm_graph_take_program (oldest first, at most MAX_HELD)
+  std::deque<dvm_program*> held;
+  ~dvm_graph();
 };
+constexpr size_t MAX_HELD = 4096;
+
+dvm_graph::~dvm_graph() {
+  for (dvm_program* p : held) delete p;
+}
 
 namespace {
 
@@ -840,6 +858,17 @@ struct Encoder {
   }
 
   bool live_after(int64_t s, int i) const { return last_use[s] > i; }
+
+  // Every external operand the program reads must have storage: a value with
+  // elements but no address (never stored, or from a graph that failed) would
+  // make the VM read address 0.
+  dvm_status check_storage(const std::vector<int64_t>& exts) const {
+    for (int64_t s : exts) {
+      const Val& v = g->vals[s];
+      if (!v.t.data && numel_of(v.t) > 0) return fail(DVM_ERR_INVALID_ARG, "an operand the graph reads has no storage");
+    }
+    return DVM_OK;
+  }
 
   int free_treg(int avoid0 = 1) const {
     for (int k = avoid0; k < n_treg; ++k)
@@ -1446,6 +1475,15 @@ struct Encoder {
     }
     const Shape sd = ck.dominant();
     std::vector<int64_t> operands = ck.ext_operands();
+    {
+      std::vector<int64_t> ab = operands;
+      if (M > 0 && N > 0 && K > 0) {
+        ab.push_back(mm.in[0]);
+        ab.push_back(mm.in[1]);
+      }
+      dvm_status sv = check_storage(ab);
+      if (sv != DVM_OK) return sv;
+    }
     for (int64_t s : stored) operands.push_back(s);
     int64_t R, C;
     std::vector<tiling::Operand> tops;
@@ -1565,6 +1603,8 @@ struct Encoder {
     const Shape sd = ck.dominant();
     std::vector<int64_t> operands = ck.ext_operands();
     const size_t n_ext = operands.size();
+    dvm_status sv = check_storage(operands);
+    if (sv != DVM_OK) return sv;
     for (int64_t s : stored) operands.push_back(s);
     int64_t R, C;
     std::vector<tiling::Operand> tops;
@@ -1601,16 +1641,16 @@ struct Encoder {
       a[A_DTYPE] = (uint32_t)g->vals[last.out].t.dtype;
       a[A_EXTENT] = 4;
       W[H_ALL_OUT] = (uint32_t)ai;
+      // the scratch operand: its address is supplied by the launch (the
+      // stream's scratch area); the program records the bytes it needs
       const int si = n_args++;
       uint32_t* b = W + ARG_BASE + si * ARG_WORDS;
-      const uint64_t q = (uint64_t)(uintptr_t)g->ctx->scratch;
-      b[A_PTR_LO] = (uint32_t)q;
-      b[A_PTR_HI] = (uint32_t)(q >> 32);
+      const uint64_t need = SCRATCH_PART_OFF + 4u * (uint64_t)plan.block_dim;
       b[A_DTYPE] = DT_F32;
-      b[A_FLAGS] = arg_flags_word(0, (uint64_t)g->ctx->scratch_bytes);
-      b[A_EXTENT] = (uint32_t)(uint64_t)g->ctx->scratch_bytes;
+      b[A_FLAGS] = arg_flags_word(0, need);
+      b[A_EXTENT] = (uint32_t)need;
       W[H_ALL_SCRATCH] = (uint32_t)si;
-      if (g->ctx->scratch && (size_t)(256 + 4 * plan.block_dim) > g->ctx->scratch_bytes)
+      if (need > SCRATCH_BYTES)
         return fail(DVM_ERR_RESOURCE, "reduce-all needs %lld partials", (long long)plan.block_dim);
     }
     for (size_t i = 0; i < ops.size(); ++i) {
@@ -1632,7 +1672,13 @@ struct Encoder {
     fuse_scale_shift(body);
     // Sync at the end of the body when the next tile's first cross-wave
     // reduction could overwrite an LDS buffer some wave is still reading.
-    if (cross_wave && n_red < 2) emit(enc0(OP_SYNC, 0, 0, 0, 0, 0, 0), 0);
+    // Reduction k of a tile uses buffer k % N_LDSBUF and every reduction
+    // after the k-th ends in a barrier, so the reads of reduction k are
+    // fenced unless k is the tile's last.  The next tile's first reduction
+    // writes buffer 0: it races the last reduction's reads exactly when that
+    // one also used buffer 0, i.e. when (n_red - 1) % N_LDSBUF == 0 (n_red =
+    // 1, 9, 17, ...).
+    if (cross_wave && (n_red - 1) % N_LDSBUF == 0) emit(enc0(OP_SYNC, 0, 0, 0, 0, 0, 0), 0);
     // header
     const uint32_t instr_base = ARG_BASE + (uint32_t)n_args * ARG_WORDS;
     const uint32_t body_base = instr_base + (uint32_t)pro.size();
@@ -1828,13 +1874,63 @@ dvm_status encode_buffer(dvm_graph* g, dvm_program** out) {
   return DVM_OK;
 }
 
+// The reduce-all scratch area of stream s (allocated and zeroed on first use).
+dvm_status stream_scratch(dvm_context* ctx, hipStream_t s, void** out) {
+  std::lock_guard<std::mutex> lk(ctx->mu);
+  for (auto& e : ctx->scratch)
+    if (e.first == s) {
+      *out = e.second;
+      return DVM_OK;
+    }
+  void* p = nullptr;
+  hipError_t e = hipMalloc(&p, SCRATCH_BYTES);
+  if (e != hipSuccess) return fail(DVM_ERR_DEVICE, "scratch allocation failed: %s", hipGetErrorString(e));
+  e = hipMemset(p, 0, SCRATCH_BYTES);
+  if (e == hipSuccess) e = hipDeviceSynchronize();
+  if (e != hipSuccess) {
+    (void)hipFree(p);
+    return fail(DVM_ERR_DEVICE, "scratch init failed: %s", hipGetErrorString(e));
+  }
+  ctx->scratch.push_back({s, p});
+  *out = p;
+  return DVM_OK;
+}
+
+bool needs_scratch(const dvm_program* p) {
+  return p->prog.w[H_KTYPE] != KT_MIX && p->prog.w[H_TEMPLATE] == TM_ALLREDUCE;
+}
+
+// Points the program's reduce-all scratch operand at `area` of `bytes`.
+void set_scratch(Program* q, void* area, uint64_t bytes) {
+  uint32_t* b = q->w + ARG_BASE + q->w[H_ALL_SCRATCH] * ARG_WORDS;
+  const uint64_t a = (uint64_t)(uintptr_t)area;
+  b[A_PTR_LO] = (uint32_t)a;
+  b[A_PTR_HI] = (uint32_t)(a >> 32);
+  b[A_FLAGS] = arg_flags_word(0, bytes);
+  b[A_EXTENT] = (uint32_t)bytes;
+}
+
+hipError_t launch_kernel(const Program* q, uint32_t grid, hipStream_t s) {
+  const uint32_t kt = q->w[H_KTYPE];
+  return kt == KT_MIX           ? dvm_launch_mix_kernel(q, grid, s)
+         : kt == KT_VECTOR_WIDE ? dvm_launch_vector_kernel_wide(q, grid, s)
+                                : dvm_launch_vector_kernel(q, grid, s);
+}
+
 dvm_status launch(dvm_context* ctx, const dvm_program* p, hipStream_t s) {
   if (!ctx || ctx->device < 0) return fail(DVM_ERR_DEVICE, "encode-only context cannot launch");
   if (p->grid_launch == 0) return DVM_OK;
-  const uint32_t kt = p->prog.w[H_KTYPE];
-  hipError_t e = kt == KT_MIX           ? dvm_launch_mix_kernel(&p->prog, p->grid_launch, s)
-                 : kt == KT_VECTOR_WIDE ? dvm_launch_vector_kernel_wide(&p->prog, p->grid_launch, s)
-                                        : dvm_launch_vector_kernel(&p->prog, p->grid_launch, s);
+  hipError_t e;
+  if (needs_scratch(p)) {
+    void* area;
+    dvm_status st = stream_scratch(ctx, s, &area);
+    if (st != DVM_OK) return st;
+    Program q = p->prog;  // the launch copies its argument: a stack copy is enough
+    set_scratch(&q, area, SCRATCH_BYTES);
+    e = launch_kernel(&q, p->grid_launch, s);
+  } else {
+    e = launch_kernel(&p->prog, p->grid_launch, s);
+  }
   if (e != hipSuccess) return fail(DVM_ERR_DEVICE, "launch failed: %s", hipGetErrorString(e));
   return DVM_OK;
 }
@@ -1847,12 +1943,18 @@ dvm_status flush_launch(dvm_graph* g, int reason, int32_t* launched) {
   dvm_program* p = nullptr;
   dvm_status st = encode_buffer(g, &p);
   if (st != DVM_OK || !p) return st;
-  if (g->ctx->device >= 0) {
-    st = launch(g->ctx, p, g->stream);
-    if (st == DVM_OK) {
-      g->stats.launches++;
-      if (launched) *launched = 1;
+  if (g->ctx->device < 0) {
+    if (g->held.size() >= MAX_HELD) {
+      delete g->held.front();
+      g->held.pop_front();
     }
+    g->held.push_back(p);
+    return DVM_OK;
+  }
+  st = launch(g->ctx, p, g->stream);
+  if (st == DVM_OK) {
+    g->stats.launches++;
+    if (launched) *launched = 1;
   }
   delete p;
   return st;
@@ -1925,7 +2027,17 @@ dvm_status end_group_impl(dvm_graph* g, int32_t* flushed) {
     }
     dvm_status st = flush_launch(g, why, flushed);
     if (flushed) *flushed = 1;
-    if (st != DVM_OK) return st;
+    if (st != DVM_OK) {
+      // the buffered graph was not run: the new group, which may read its
+      // values, is dropped too; its results are lost, never pending
+      for (auto& o : grp) {
+        Val& v = g->vals[o.out];
+        v.pending = false;
+        v.lost = true;
+      }
+      drop_uses(g, grp);
+      return st;
+    }
   }
   Checker ck(g, grp);
   const int why = ck.check(0);
@@ -1966,19 +2078,6 @@ dvm_status dvm_context_create(int device, dvm_context** out) {
       delete c;
       return fail(DVM_ERR_DEVICE, "hipSetDevice(%d) failed: %s", device, hipGetErrorString(e));
     }
-    c->scratch_bytes = 4u << 20;
-    e = hipMalloc(&c->scratch, c->scratch_bytes);
-    if (e != hipSuccess) {
-      delete c;
-      return fail(DVM_ERR_DEVICE, "scratch allocation failed: %s", hipGetErrorString(e));
-    }
-    e = hipMemset(c->scratch, 0, c->scratch_bytes);
-    if (e == hipSuccess) e = hipDeviceSynchronize();
-    if (e != hipSuccess) {
-      (void)hipFree(c->scratch);
-      delete c;
-      return fail(DVM_ERR_DEVICE, "scratch init failed: %s", hipGetErrorString(e));
-    }
   }
   *out = c;
   return DVM_OK;
@@ -1986,9 +2085,9 @@ dvm_status dvm_context_create(int device, dvm_context** out) {
 
 void dvm_context_destroy(dvm_context* ctx) {
   if (!ctx) return;
-  if (ctx->scratch) {
+  if (!ctx->scratch.empty()) {
     (void)hipDeviceSynchronize();
-    (void)hipFree(ctx->scratch);
+    for (auto& e : ctx->scratch) (void)hipFree(e.second);
   }
   delete ctx;
 }
@@ -2004,6 +2103,16 @@ dvm_status dvm_graph_create(dvm_context* ctx, void* stream, dvm_graph** out) {
 }
 
 void dvm_graph_destroy(dvm_graph* g) { delete g; }
+
+dvm_status dvm_graph_take_program(dvm_graph* g, dvm_program** out) {
+  if (!g || !out) return fail(DVM_ERR_INVALID_ARG, "null argument");
+  *out = nullptr;
+  if (!g->held.empty()) {
+    *out = g->held.front();
+    g->held.pop_front();
+  }
+  return DVM_OK;
+}
 
 dvm_status dvm_graph_input(dvm_graph* g, const dvm_tensor* t, dvm_value* out) {
   if (!g || !out) return fail(DVM_ERR_INVALID_ARG, "null argument");
@@ -2139,6 +2248,12 @@ dvm_status dvm_launch_profiled(dvm_context* ctx, const dvm_program* p, void* str
   const size_t need = (size_t)DVM_PROF_COUNTERS * p->grid_launch;
   if (n_counters < need) return fail(DVM_ERR_INVALID_ARG, "counter buffer holds %zu values, needs %zu", n_counters, need);
   Program q = p->prog;  // the launch copies its argument: a stack copy is enough
+  if (needs_scratch(p)) {
+    void* area;
+    dvm_status st = stream_scratch(ctx, (hipStream_t)stream, &area);
+    if (st != DVM_OK) return st;
+    set_scratch(&q, area, SCRATCH_BYTES);
+  }
   const uint64_t a = (uint64_t)(uintptr_t)counters;
   q.w[H_PROF_LO] = (uint32_t)a;
   q.w[H_PROF_HI] = (uint32_t)(a >> 32);

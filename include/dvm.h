@@ -117,7 +117,10 @@ typedef struct {
 } dvm_stats;
 
 /* Contexts.  device >= 0: the HIP device whose resident VM kernels run the
- * programs; a small scratch area (reduce-all partials) is allocated on it.
+ * programs.  Reduce-all programs need a scratch area on the device (a counter
+ * and one partial per tile): each stream gets its own 4 MiB area, allocated
+ * and zeroed at the first reduce-all launched on it and freed with the
+ * context, so launches on different streams never share it.
  * device < 0: an encode-only context (tiling and bytecode, no launches). */
 dvm_status dvm_context_create(int device, dvm_context** out);
 void dvm_context_destroy(dvm_context* ctx);
@@ -126,6 +129,14 @@ void dvm_context_destroy(dvm_context* ctx);
  * NULL = default stream); implicit flushes launch on that stream. */
 dvm_status dvm_graph_create(dvm_context* ctx, void* stream, dvm_graph** out);
 void dvm_graph_destroy(dvm_graph* g);
+
+/* A graph of an encode-only context cannot launch what it flushes implicitly
+ * (at a fusion boundary, or when a reduce-all closes its graph): those
+ * programs wait in the graph, at most 4096 of them (older ones are freed).
+ * This hands out the oldest one, or *out = NULL if none waits; the caller
+ * frees it with dvm_program_free.  It may be launched on a device context if
+ * its tensors' addresses are that device's. */
+dvm_status dvm_graph_take_program(dvm_graph* g, dvm_program** out);
 
 /* Registers an external tensor (read by ops, never written through this
  * handle). */

@@ -1,0 +1,121 @@
+"""Host tests (no GPU) of two encoder/fuser guarantees:
+
+* the barrier that keeps a tile's cross-wave reduction buffers from being
+  overwritten by the next tile while a wave still reads them (the syncs the
+  encoder inserts, DVM review page, section 4.3);
+* a failed flush drops the group that triggered it: its values are lost, not
+  pending, and cannot feed later ops.
+
+The handler ids and header word offsets below are the bytecode format of
+csrc/bytecode.h, restated here to read encoded programs.
+"""
+import pytest
+
+import device_bytecode_vm_amd as dvm
+from device_bytecode_vm_amd import TensorDesc as TD
+from device_bytecode_vm_amd import _lib as L
+
+H_BODY_BEGIN, H_BODY_END = 16, 17
+HD_REDX, HD_ALL, HD_SYNC = 127, 136, 149
+N_LDSBUF = 8
+
+
+@pytest.fixture(scope="module")
+def ectx():
+    return dvm.Context(-1)
+
+
+def body(p):
+    w = p.words()
+    b0, b1 = w[H_BODY_BEGIN], w[H_BODY_END]
+    return [(w[i] & 0xFF, (w[i] >> 16) & 0xF) for i in range(b0, b1, 2)]
+
+
+def chained_reductions(ectx, n_red, shape):
+    """x -> (x - rowsum(x)) repeated n_red times: n_red reductions whose rows
+    span several waves (one REDX each)."""
+    g = dvm.Graph(ectx)
+    addr = 1 << 30
+    v = g.input(TD(addr, "f32", shape))
+    for k in range(n_red):
+        s = g.op("reduce_sum", v)
+        last = k == n_red - 1
+        nv = g.op("sub", v, s, out=TD(addr * 2, "f32", shape) if last else None, live=last)
+        g.release(s)
+        if k:
+            g.release(v)
+        v = nv
+    return g.flush()
+
+
+def fenced(instrs, n_tiles=3):
+    """Simulates n_tiles copies of the body and checks every write of a
+    cross-wave buffer against the reads of the same buffer since the last
+    barrier: a write may only follow reads that a barrier separates from it.
+    REDX = write, barrier, read; ALL = write (its SYNC and ALL_FIN follow)."""
+    reads_since_barrier = set()
+    for _ in range(n_tiles):
+        for h, b in instrs:
+            if HD_REDX <= h < HD_REDX + 9:
+                if b in reads_since_barrier:
+                    return False
+                reads_since_barrier = {b}          # its own barrier, then its read
+            elif HD_ALL <= h < HD_ALL + 6:
+                if b in reads_since_barrier:
+                    return False
+            elif h == HD_SYNC:
+                reads_since_barrier = set()
+            elif h == 142 or h == 143:             # ALL_FIN reads its buffer
+                reads_since_barrier.add(b)
+    return True
+
+
+@pytest.mark.parametrize("n_red", [1, 2, 8, 9, 10, 16, 17])
+@pytest.mark.parametrize("shape", [(4096, 6000), (4096, 16384)])
+def test_trailing_sync_fences_buffer_reuse(ectx, n_red, shape):
+    p = chained_reductions(ectx, n_red, shape)
+    h = p.header()
+    assert h["body_tile"] > 1 and h["g"] > 64, h   # several tiles per workgroup, rows across waves
+    ins = body(p)
+    redx = [b for op, b in ins if HD_REDX <= op < HD_REDX + 9]
+    assert redx == [k % N_LDSBUF for k in range(n_red)]
+    assert fenced(ins)
+    trailing = ins[-1][0] == HD_SYNC
+    assert trailing == ((n_red - 1) % N_LDSBUF == 0)
+
+
+def test_failed_flush_drops_the_new_group(ectx):
+    g = dvm.Graph(ectx)
+    a = g.input(TD(1 << 20, "f32", (4, 5)))
+    g.op("exp", a)                                  # no storage and never released: its flush fails
+    b = g.input(TD(2 << 20, "f32", (3, 7)))
+    held = {}
+    with pytest.raises(dvm.DvmError) as e:
+        with g.group():                             # another shape: flushes the first graph first
+            held["c"] = g.op("neg", b, out=TD(3 << 20, "f32", (3, 7)))
+    assert e.value.status == L.ERR_INVALID_ARG
+    # the group that triggered the failing flush was dropped with it: the
+    # value it would have produced holds nothing and cannot be read
+    with pytest.raises(dvm.DvmError) as e:
+        g.op("mul", held["c"], 2.0, out=TD(4 << 20, "f32", (3, 7)), live=True)
+    assert e.value.status == L.ERR_INVALID_ARG
+    assert g.flush() is None                        # nothing pending
+
+
+def test_reduce_all_program_has_no_scratch_address(ectx):
+    """The reduce-all closes its graph; the encode-only context holds the
+    program.  Its scratch operand has no address: each launch supplies its
+    stream's own area, so programs on different streams never share it."""
+    ARG_BASE, ARG_WORDS, H_ALL_SCRATCH = 40, 8, 24
+    g = dvm.Graph(ectx)
+    x = g.input(TD(1 << 30, "f32", (16384, 4096)))
+    g.op("reduce_sum", x, out=TD(2 << 30, "f32", ()), live=True, axis=L.AXIS_ALL)
+    assert g.flush() is None                         # the reduce-all flushed its own graph
+    p = g.take_program()
+    assert g.take_program() is None
+    w = p.words()
+    h = p.header()
+    assert h["tmpl"] == 2 and h["body_tile"] > 1
+    a = ARG_BASE + w[H_ALL_SCRATCH] * ARG_WORDS
+    assert w[a] == 0 and w[a + 1] == 0               # supplied per stream at launch
+    assert w[a + 7] == 256 + 4 * h["block_dim"]      # the bytes the program needs
