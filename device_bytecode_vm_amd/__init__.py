@@ -130,6 +130,11 @@ class Program:
         """Launch on `ctx` (default: the context that encoded the program)."""
         check(lib.dvm_launch((ctx or self.ctx).h, self.h, _stream_handle(stream)))
 
+    def launch_noalloc(self, stream=None, ctx=None):
+        """dvm_launch_noalloc: no device allocation; a reduce-all uses the
+        library's static scratch array (at most 65536 tiles)."""
+        check(lib.dvm_launch_noalloc((ctx or self.ctx).h, self.h, _stream_handle(stream)))
+
     PROF_COUNTERS = 5
 
     def launch_profiled(self, counters, stream=None):

@@ -85,6 +85,7 @@ _sigs = {
     "dvm_graph_infer_shape": (C.c_int, [VP, C.c_int32, P(C.c_int64), C.c_int32, P(DvmAttrs), P(DvmTensor)]),
     "dvm_flush": (C.c_int, [VP, P(VP)]),
     "dvm_launch": (C.c_int, [VP, VP, VP]),
+    "dvm_launch_noalloc": (C.c_int, [VP, VP, VP]),
     "dvm_launch_profiled": (C.c_int, [VP, VP, VP, VP, C.c_size_t]),
     "dvm_graph_flush_launch": (C.c_int, [VP, P(C.c_int32)]),
     "dvm_sync": (C.c_int, [VP]),

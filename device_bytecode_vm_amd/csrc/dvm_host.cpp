@@ -30,6 +30,8 @@ extern "C" hipError_t dvm_launch_mix_kernel(const Program* p, unsigned grid, hip
 extern "C" hipError_t dvm_launch_vector_prof_kernel(const Program* p, unsigned grid, hipStream_t s);
 extern "C" hipError_t dvm_launch_vector_kernel_wide(const Program* p, unsigned grid, hipStream_t s);
 extern "C" hipError_t dvm_launch_vector_prof_kernel_wide(const Program* p, unsigned grid, hipStream_t s);
+extern "C" hipError_t dvm_static_scratch_init(int device, void** ptr, size_t* bytes);
+extern "C" hipError_t dvm_static_scratch_clear(void* area, hipStream_t s);
 
 namespace {
 
@@ -421,6 +423,10 @@ struct dvm_context {
   int device = -1;
   std::mutex mu;  // guards scratch (graphs of one context may run on separate threads)
   std::vector<std::pair<hipStream_t, void*>> scratch;
+  // the device's static scratch array (dvm_launch_noalloc), looked up at creation
+  void* static_scratch = nullptr;
+  size_t static_bytes = 0;
+  hipError_t static_err = hipSuccess;
 };
 
 struct dvm_program {
@@ -2078,6 +2084,8 @@ dvm_status dvm_context_create(int device, dvm_context** out) {
       delete c;
       return fail(DVM_ERR_DEVICE, "hipSetDevice(%d) failed: %s", device, hipGetErrorString(e));
     }
+    // with the device current: the address of its copy of the static scratch
+    c->static_err = dvm_static_scratch_init(device, &c->static_scratch, &c->static_bytes);
   }
   *out = c;
   return DVM_OK;
@@ -2235,6 +2243,30 @@ dvm_status dvm_flush(dvm_graph* g, dvm_program** out) {
 dvm_status dvm_launch(dvm_context* ctx, const dvm_program* p, void* stream) {
   if (!ctx || !p) return fail(DVM_ERR_INVALID_ARG, "null argument");
   return launch(ctx, p, (hipStream_t)stream);
+}
+
+dvm_status dvm_launch_noalloc(dvm_context* ctx, const dvm_program* p, void* stream) {
+  if (!ctx || !p) return fail(DVM_ERR_INVALID_ARG, "null argument");
+  if (ctx->device < 0) return fail(DVM_ERR_DEVICE, "encode-only context cannot launch");
+  if (p->grid_launch == 0) return DVM_OK;
+  const hipStream_t s = (hipStream_t)stream;
+  hipError_t e;
+  if (needs_scratch(p)) {
+    if (!ctx->static_scratch)
+      return fail(DVM_ERR_DEVICE, "static scratch unavailable: %s", hipGetErrorString(ctx->static_err));
+    const uint64_t need = SCRATCH_PART_OFF + 4u * (uint64_t)p->prog.w[H_BLOCK_DIM];
+    if (need > ctx->static_bytes)
+      return fail(DVM_ERR_RESOURCE, "reduce-all over %u tiles: the static scratch holds %zu partials",
+                  p->prog.w[H_BLOCK_DIM], (ctx->static_bytes - SCRATCH_PART_OFF) / 4);
+    Program q = p->prog;
+    set_scratch(&q, ctx->static_scratch, ctx->static_bytes);
+    e = dvm_static_scratch_clear(ctx->static_scratch, s);
+    if (e == hipSuccess) e = launch_kernel(&q, p->grid_launch, s);
+  } else {
+    e = launch_kernel(&p->prog, p->grid_launch, s);
+  }
+  if (e != hipSuccess) return fail(DVM_ERR_DEVICE, "launch failed: %s", hipGetErrorString(e));
+  return DVM_OK;
 }
 
 dvm_status dvm_launch_profiled(dvm_context* ctx, const dvm_program* p, void* stream, uint64_t* counters,

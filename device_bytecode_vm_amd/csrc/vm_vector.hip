@@ -126,6 +126,14 @@ __device__ __forceinline__ uint64_t w64(KW* w, int lo) {
   return ((uint64_t)w[lo + 1] << 32) | (uint64_t)w[lo];
 }
 
+// Bytes of reduce-all partials a program of block_dim tiles writes into a
+// scratch operand of `extent` bytes (counter at byte 0, partials from 256).
+__device__ __forceinline__ uint32_t part_bytes(uint64_t extent, uint32_t block_dim) {
+  const uint64_t room = extent > 256u ? extent - 256u : 0u;
+  const uint64_t need = 4ull * block_dim;
+  return (uint32_t)(need < room ? need : room);
+}
+
 __device__ __forceinline__ ArgD read_arg(KW* W, uint32_t i) {
   KW* a = W + ARG_BASE + i * ARG_WORDS;
   ArgD d;
@@ -1208,9 +1216,11 @@ __device__ __forceinline__ void vm_main(float (*s_red)[T_LANES / 64], int& s_las
         const float* buf = s_red[f_b(w0)];
         float acc = buf[0];
         for (int k = 1; k < T_LANES / 64; ++k) acc = kind == RK_SUM ? acc + buf[k] : comb<RK_MAX>(acc, buf[k]);
+        // the partials' descriptor ends where the scratch operand ends (its
+        // extent is the area the launch supplied)
         const ArgD a = read_arg(W, W[H_ALL_SCRATCH]);
-        const Rsrc rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(a.p) + 256, 0, (int)(block_dim * 4u),
-                                                          RSRC_W3);
+        const Rsrc rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(a.p) + 256, 0,
+                                                          (int)part_bytes(a.extent, block_dim), RSRC_W3);
         __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc), rs, lane_off(tidv == 0, (int)(tl.id * 4u)), 0, 0);
         break;
       }
@@ -1319,7 +1329,8 @@ __device__ __forceinline__ void vm_main(float (*s_red)[T_LANES / 64], int& s_las
     if (s_last) {
       __atomic_thread_fence(__ATOMIC_ACQUIRE);
       float acc = kind == RK_SUM ? 0.f : -__builtin_huge_valf();
-      for (uint32_t i = (uint32_t)tid; i < block_dim; i += T_LANES) {
+      const uint32_t n_part = part_bytes(sa.extent, block_dim) / 4u;  // never past the area
+      for (uint32_t i = (uint32_t)tid; i < n_part; i += T_LANES) {
         const float v = __hip_atomic_load(part + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         acc = kind == RK_SUM ? acc + v : comb<RK_MAX>(acc, v);
       }

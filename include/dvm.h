@@ -182,6 +182,21 @@ dvm_status dvm_flush(dvm_graph* g, dvm_program** out);
  * stream (hipStream_t).  Asynchronous. */
 dvm_status dvm_launch(dvm_context* ctx, const dvm_program* p, void* stream);
 
+/* dvm_launch for callers that cannot allocate device memory (code under HIP
+ * graph capture, serving loops, harnesses that forbid hipMalloc): it calls no
+ * hipMalloc, hipFree or allocating library routine.  Programs other than
+ * reduce-alls launch exactly as with dvm_launch.  A reduce-all runs on the
+ * library's static scratch array instead of the stream's allocated area: one
+ * array per GPU, held until the process ends, of 256 + 4 * 65536 bytes (a
+ * counter and at most 65536 tile partials); a program over more tiles returns
+ * DVM_ERR_RESOURCE without launching.  Before the program the call queues a
+ * one-workgroup kernel that zeroes the counter, on the same stream.  Every call
+ * on a GPU shares that GPU's array and it keeps the last call's contents:
+ * calls whose launches overlap on one GPU (different streams, or graph
+ * replays running concurrently) race on it; callers serialise them.
+ * Asynchronous. */
+dvm_status dvm_launch_noalloc(dvm_context* ctx, const dvm_program* p, void* stream);
+
 /* Profiling launch of a VECTOR program (the decode-overhead measurement: the
  * paper review page's section 4.4 has the Scalar unit decode the bytecode
  * while the vector units execute, and claims the decode is cheap next to the
