@@ -298,15 +298,20 @@ class Graph:
         check(lib.dvm_sync(self.h))
         self._keep = []
 
-    def flush_log(self) -> list:
-        """[(n_ops, reason name)] for every graph flushed so far."""
+    def flush_log(self, detail=False) -> list:
+        """[(n_ops, reason name)] for every graph flushed so far; with
+        detail=True [(n_ops, reason, encode_us, bytes)]."""
         n = C.c_size_t(0)
-        check(lib.dvm_graph_flush_log(self.h, None, None, C.byref(n)))
+        check(lib.dvm_graph_flush_log(self.h, None, None, None, None, C.byref(n)))
         k = n.value
         ops = (C.c_int32 * max(k, 1))()
         rs = (C.c_int32 * max(k, 1))()
+        us = (C.c_float * max(k, 1))()
+        by = (C.c_uint64 * max(k, 1))()
         cap = C.c_size_t(k)
-        check(lib.dvm_graph_flush_log(self.h, ops, rs, C.byref(cap)))
+        check(lib.dvm_graph_flush_log(self.h, ops, rs, us, by, C.byref(cap)))
+        if detail:
+            return [(ops[i], L.FLUSH_REASONS[rs[i]], float(us[i]), int(by[i])) for i in range(k)]
         return [(ops[i], L.FLUSH_REASONS[rs[i]]) for i in range(k)]
 
     def stats(self) -> dict:
@@ -316,5 +321,6 @@ class Graph:
             "graphs": s.graphs, "launches": s.launches, "ops": s.ops, "groups": s.groups,
             "unsupported": s.unsupported,
             "flush_reason": {L.FLUSH_REASONS[i]: s.flush_reason[i] for i in range(7)},
-            "encode_us_total": s.encode_us_total, "encode_us_max": s.encode_us_max,
+            "encode_us_total": s.encode_us_total, "encode_us_max": s.encode_us_max, "bytes": s.bytes,
+            "fuse_us_total": s.fuse_us_total, "launch_us_total": s.launch_us_total,
         }

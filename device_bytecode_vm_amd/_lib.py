@@ -59,13 +59,15 @@ class DvmHeader(C.Structure):
     _fields_ = [("kernel_type", C.c_uint32), ("tmpl", C.c_uint32), ("block_dim", C.c_uint32),
                 ("body_tile", C.c_uint32), ("grid", C.c_uint32), ("tr", C.c_uint32), ("tc", C.c_uint32),
                 ("g", C.c_uint32), ("nv", C.c_uint32), ("p", C.c_uint32), ("R", C.c_int64), ("C", C.c_int64),
-                ("n_instr", C.c_uint32), ("n_args", C.c_uint32), ("pad", C.c_uint32), ("n_words", C.c_uint32)]
+                ("n_instr", C.c_uint32), ("n_args", C.c_uint32), ("pad", C.c_uint32), ("n_words", C.c_uint32),
+                ("bytes", C.c_uint64)]
 
 
 class DvmStats(C.Structure):
     _fields_ = [("graphs", C.c_uint64), ("launches", C.c_uint64), ("ops", C.c_uint64), ("groups", C.c_uint64),
                 ("unsupported", C.c_uint64), ("flush_reason", C.c_uint64 * 8),
-                ("encode_us_total", C.c_double), ("encode_us_max", C.c_double)]
+                ("encode_us_total", C.c_double), ("encode_us_max", C.c_double), ("bytes", C.c_uint64),
+                ("fuse_us_total", C.c_double), ("launch_us_total", C.c_double)]
 
 
 VP = C.c_void_p
@@ -94,7 +96,8 @@ _sigs = {
     "dvm_program_free": (None, [VP]),
     "dvm_program_debug_tilemap": (C.c_int, [VP, P(DvmTensor), P(DvmTensor), P(VP)]),
     "dvm_graph_stats": (C.c_int, [VP, P(DvmStats)]),
-    "dvm_graph_flush_log": (C.c_int, [VP, P(C.c_int32), P(C.c_int32), P(C.c_size_t)]),
+    "dvm_graph_flush_log": (C.c_int, [VP, P(C.c_int32), P(C.c_int32), P(C.c_float), P(C.c_uint64),
+                                      P(C.c_size_t)]),
     "dvm_last_error": (C.c_char_p, []),
 }
 for _name, (_res, _args) in _sigs.items():

@@ -431,6 +431,7 @@ struct dvm_context {
 
 struct dvm_program {
   Program prog;
+  uint64_t bytes = 0;         // physical bytes: every operand read once, every stored output written once
   uint32_t n_words = 0;
   uint32_t n_instr = 0;
   int64_t R = 0, C = 0;
@@ -447,7 +448,12 @@ struct dvm_graph {
   std::vector<OpRec> grp;   // open group
   bool in_group = false;
   dvm_stats stats{};
-  std::vector<std::pair<int32_t, int32_t>> flush_log;  // (ops, reason) per flushed graph
+  struct LogEntry {
+    int32_t ops, reason;
+    float encode_us;
+    uint64_t bytes;
+  };
+  std::vector<LogEntry> flush_log;  // per flushed graph
   // encode-only contexts cannot launch: programs of implicit flushes wait
   // here for dvm_graph_take_program (oldest first, at most MAX_HELD)
   std::deque<dvm_program*> held;
@@ -864,6 +870,14 @@ struct Encoder {
   }
 
   bool live_after(int64_t s, int i) const { return last_use[s] > i; }
+
+  // Bytes of the tensors themselves (their own shapes: a broadcast operand
+  // counts once): what the program reads or writes at the least.
+  uint64_t tensor_bytes(const std::vector<int64_t>& slots) const {
+    uint64_t b = 0;
+    for (int64_t s : slots) b += (uint64_t)numel_of(g->vals[s].t) * (uint64_t)esize(g->vals[s].t.dtype);
+    return b;
+  }
 
   // Every external operand the program reads must have storage: a value with
   // elements but no address (never stored, or from a graph that failed) would
@@ -1521,6 +1535,7 @@ struct Encoder {
     }
     n_args = 2;
     for (size_t q = 0; q < operands.size(); ++q) add_arg(operands[q], st[q].first, st[q].second);
+    prog->bytes = tensor_bytes(operands) + tensor_bytes({mm.in[0], mm.in[1]});
     cls.clear();
     ck.classes(&cls);
     cls[mm.out] = 1;
@@ -1629,6 +1644,8 @@ struct Encoder {
     }
     if (operands.size() + 2 > (size_t)MAX_ARGS) return fail(DVM_ERR_RESOURCE, "too many operands");
     for (size_t q = 0; q < operands.size(); ++q) add_arg(operands[q], st[q].first, st[q].second);
+    prog->bytes = tensor_bytes(operands);
+    if (tm == TM_ALLREDUCE) prog->bytes += (uint64_t)esize(g->vals[ops.back().out].t.dtype);
     cls.clear();
     ck.classes(&cls);
     {
@@ -1872,10 +1889,13 @@ dvm_status encode_buffer(dvm_graph* g, dvm_program** out) {
   g->stats.graphs++;
   g->stats.encode_us_total += us;
   g->stats.encode_us_max = std::max(g->stats.encode_us_max, us);
+  if (!g->flush_log.empty()) g->flush_log.back().encode_us = (float)us;
   if (st != DVM_OK) {
     delete p;
     return st;
   }
+  g->stats.bytes += p->bytes;
+  if (!g->flush_log.empty()) g->flush_log.back().bytes = p->bytes;
   *out = p;
   return DVM_OK;
 }
@@ -1945,7 +1965,7 @@ dvm_status flush_launch(dvm_graph* g, int reason, int32_t* launched) {
   if (launched) *launched = 0;
   if (g->buf.empty()) return DVM_OK;
   g->stats.flush_reason[reason]++;
-  g->flush_log.push_back({(int32_t)g->buf.size(), (int32_t)reason});
+  g->flush_log.push_back({(int32_t)g->buf.size(), (int32_t)reason, 0.f, 0});
   dvm_program* p = nullptr;
   dvm_status st = encode_buffer(g, &p);
   if (st != DVM_OK || !p) return st;
@@ -1957,7 +1977,9 @@ dvm_status flush_launch(dvm_graph* g, int reason, int32_t* launched) {
     g->held.push_back(p);
     return DVM_OK;
   }
+  const auto t0 = std::chrono::steady_clock::now();
   st = launch(g->ctx, p, g->stream);
+  g->stats.launch_us_total += std::chrono::duration<double, std::micro>(std::chrono::steady_clock::now() - t0).count();
   if (st == DVM_OK) {
     g->stats.launches++;
     if (launched) *launched = 1;
@@ -1965,6 +1987,23 @@ dvm_status flush_launch(dvm_graph* g, int reason, int32_t* launched) {
   delete p;
   return st;
 }
+
+// Host time of one fuser call (capture and fusion decisions), without the
+// encodes and launches of the flushes it triggers.
+struct FuseTimer {
+  dvm_graph* g;
+  std::chrono::steady_clock::time_point t0;
+  double enc0, lau0;
+  explicit FuseTimer(dvm_graph* gr)
+      : g(gr), t0(std::chrono::steady_clock::now()), enc0(gr ? gr->stats.encode_us_total : 0.0),
+        lau0(gr ? gr->stats.launch_us_total : 0.0) {}
+  ~FuseTimer() {
+    if (!g) return;
+    const double us = std::chrono::duration<double, std::micro>(std::chrono::steady_clock::now() - t0).count() -
+                      (g->stats.encode_us_total - enc0) - (g->stats.launch_us_total - lau0);
+    g->stats.fuse_us_total += std::max(us, 0.0);
+  }
+};
 
 bool infer(const dvm_graph* g, int32_t op, const int64_t* in, int n_in, const dvm_attrs* at, Shape* out) {
   if (op < 0 || op >= DVM_OP_COUNT) return false;
@@ -2123,6 +2162,7 @@ dvm_status dvm_graph_take_program(dvm_graph* g, dvm_program** out) {
 }
 
 dvm_status dvm_graph_input(dvm_graph* g, const dvm_tensor* t, dvm_value* out) {
+  FuseTimer ft(g);
   if (!g || !out) return fail(DVM_ERR_INVALID_ARG, "null argument");
   dvm_status st = check_tensor(t);
   if (st != DVM_OK) return st;
@@ -2144,6 +2184,7 @@ dvm_status dvm_graph_begin_group(dvm_graph* g) {
 }
 
 dvm_status dvm_graph_end_group(dvm_graph* g, int32_t* flushed) {
+  FuseTimer ft(g);
   if (!g) return fail(DVM_ERR_INVALID_ARG, "null graph");
   if (!g->in_group) return fail(DVM_ERR_INVALID_ARG, "no open group");
   return end_group_impl(g, flushed);
@@ -2164,6 +2205,7 @@ dvm_status dvm_graph_infer_shape(dvm_graph* g, int32_t op, const dvm_value* in, 
 
 dvm_status dvm_graph_add_op(dvm_graph* g, int32_t op, const dvm_value* in, int32_t n_in, const dvm_attrs* attrs,
                             const dvm_tensor* out, uint32_t flags, dvm_value* out_value) {
+  FuseTimer ft(g);
   if (!g || !out || !out_value || (n_in > 0 && !in)) return fail(DVM_ERR_INVALID_ARG, "null argument");
   if (n_in < 1 || n_in > 2) return fail(DVM_ERR_INVALID_ARG, "n_in %d", n_in);
   dvm_status st = check_tensor(out);
@@ -2223,6 +2265,7 @@ dvm_status dvm_graph_add_op(dvm_graph* g, int32_t op, const dvm_value* in, int32
 }
 
 dvm_status dvm_graph_release(dvm_graph* g, dvm_value h) {
+  FuseTimer ft(g);
   int64_t s;
   if (!g || !resolve(g, h, &s)) return fail(DVM_ERR_INVALID_ARG, "unknown value");
   Val& v = g->vals[s];
@@ -2235,7 +2278,7 @@ dvm_status dvm_flush(dvm_graph* g, dvm_program** out) {
   if (!g || !out) return fail(DVM_ERR_INVALID_ARG, "null argument");
   if (!g->buf.empty()) {
     g->stats.flush_reason[FR_EXPLICIT]++;
-    g->flush_log.push_back({(int32_t)g->buf.size(), (int32_t)FR_EXPLICIT});
+    g->flush_log.push_back({(int32_t)g->buf.size(), (int32_t)FR_EXPLICIT, 0.f, 0});
   }
   return encode_buffer(g, out);
 }
@@ -2332,6 +2375,7 @@ dvm_status dvm_program_header(const dvm_program* p, dvm_header* out) {
   out->n_args = W[H_NARGS];
   out->pad = p->pad;
   out->n_words = p->n_words;
+  out->bytes = p->bytes;
   return DVM_OK;
 }
 
@@ -2391,13 +2435,17 @@ dvm_status dvm_program_debug_tilemap(const dvm_program* p, const dvm_tensor* til
   return DVM_OK;
 }
 
-dvm_status dvm_graph_flush_log(const dvm_graph* g, int32_t* n_ops, int32_t* reasons, size_t* n) {
+dvm_status dvm_graph_flush_log(const dvm_graph* g, int32_t* n_ops, int32_t* reasons, float* encode_us,
+                               uint64_t* bytes, size_t* n) {
   if (!g || !n) return fail(DVM_ERR_INVALID_ARG, "null argument");
   const size_t cap = *n;
   *n = g->flush_log.size();
   for (size_t i = 0; i < std::min(cap, g->flush_log.size()); ++i) {
-    if (n_ops) n_ops[i] = g->flush_log[i].first;
-    if (reasons) reasons[i] = g->flush_log[i].second;
+    const dvm_graph::LogEntry& e = g->flush_log[i];
+    if (n_ops) n_ops[i] = e.ops;
+    if (reasons) reasons[i] = e.reason;
+    if (encode_us) encode_us[i] = e.encode_us;
+    if (bytes) bytes[i] = e.bytes;
   }
   return DVM_OK;
 }

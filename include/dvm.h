@@ -103,6 +103,8 @@ typedef struct {
   uint32_t n_args;       /* global operands */
   uint32_t pad;          /* alignment slack used by the tiling */
   uint32_t n_words;      /* program size in 32-bit words */
+  uint64_t bytes;        /* physical bytes of the graph: each operand tensor read once and each
+                            stored output written once (the least HBM traffic of a launch) */
 } dvm_header;
 
 typedef struct {
@@ -112,8 +114,12 @@ typedef struct {
   uint64_t groups;
   uint64_t unsupported;       /* groups rejected (caller ran them elsewhere) */
   uint64_t flush_reason[8];   /* 0 explicit, 1 sync, 2 reduce_all, 3 shape, 4 pattern, 5 dependence, 6 resource */
-  double encode_us_total;
+  double encode_us_total;     /* host time of encoding (tiling + bytecode), all graphs */
   double encode_us_max;
+  uint64_t bytes;             /* physical bytes of the encoded graphs (dvm_header.bytes summed) */
+  double fuse_us_total;       /* host time of capture and fusion decisions (input, add_op, end_group,
+                                 release), without the encodes and launches they trigger */
+  double launch_us_total;     /* host time of the launches of implicit and explicit flushes */
 } dvm_stats;
 
 /* Contexts.  device >= 0: the HIP device whose resident VM kernels run the
@@ -238,9 +244,13 @@ dvm_status dvm_program_debug_tilemap(const dvm_program* p, const dvm_tensor* til
 dvm_status dvm_graph_stats(const dvm_graph* g, dvm_stats* out);
 
 /* Partition record of the graphs flushed so far, oldest first: graph i held
- * n_ops[i] ops and was flushed for reason reasons[i] (the dvm_stats
- * flush_reason index).  *n in: capacity, out: number of graphs recorded. */
-dvm_status dvm_graph_flush_log(const dvm_graph* g, int32_t* n_ops, int32_t* reasons, size_t* n);
+ * n_ops[i] ops, was flushed for reason reasons[i] (the dvm_stats flush_reason
+ * index), took encode_us[i] microseconds of host time to encode and moves
+ * bytes[i] physical bytes (dvm_header.bytes; 0 if its encode failed or it had
+ * no effect).  Any output array may be NULL.  *n in: capacity, out: number of
+ * graphs recorded. */
+dvm_status dvm_graph_flush_log(const dvm_graph* g, int32_t* n_ops, int32_t* reasons, float* encode_us,
+                               uint64_t* bytes, size_t* n);
 const char* dvm_last_error(void);
 
 #ifdef __cplusplus
