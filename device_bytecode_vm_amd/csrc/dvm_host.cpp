@@ -457,6 +457,7 @@ struct dvm_graph {
   // encode-only contexts cannot launch: programs of implicit flushes wait
   // here for dvm_graph_take_program (oldest first, at most MAX_HELD)
   std::deque<dvm_program*> held;
+  std::vector<int32_t> remap;  // slot -> local index while a local view is built (-1 otherwise)
   ~dvm_graph();
 };
 constexpr size_t MAX_HELD = 4096;
@@ -517,6 +518,39 @@ void drop_uses(dvm_graph* g, const std::vector<OpRec>& ops) {
     for (int k = 0; k < o.n_in; ++k) maybe_recycle(g, o.in[k]);
     maybe_recycle(g, o.out);
   }
+}
+
+// A fused graph over dense local value indices: copies of the values its ops
+// use, numbered in order of first appearance.  The checker and the encoder
+// run on it, so their per-value tables are sized by the graph (a few dozen
+// values), not by every value the stream has created so far.
+struct LocalView {
+  dvm_graph lg;                  // only ctx and vals are set
+  std::vector<OpRec> ops;
+};
+
+void make_local(dvm_graph* g, const std::vector<OpRec>& ops, LocalView* L) {
+  std::vector<int32_t>& rm = g->remap;
+  if (rm.size() < g->vals.size()) rm.resize(g->vals.size(), -1);
+  L->lg.ctx = g->ctx;
+  L->lg.stream = g->stream;
+  L->lg.vals.clear();
+  L->ops = ops;
+  std::vector<int64_t> used;
+  used.reserve(3 * ops.size());
+  auto loc = [&](int64_t s) -> int64_t {
+    if (rm[s] < 0) {
+      rm[s] = (int32_t)L->lg.vals.size();
+      L->lg.vals.push_back(g->vals[s]);
+      used.push_back(s);
+    }
+    return rm[s];
+  };
+  for (OpRec& o : L->ops) {
+    for (int k = 0; k < o.n_in; ++k) o.in[k] = loc(o.in[k]);
+    o.out = loc(o.out);
+  }
+  for (int64_t s : used) rm[s] = -1;
 }
 
 // ===========================================================================
@@ -1823,7 +1857,9 @@ dvm_status encode_buffer(dvm_graph* g, dvm_program** out) {
   if (g->buf.empty()) return DVM_OK;
   auto t0 = std::chrono::steady_clock::now();
   std::vector<OpRec> ops;
-  simplify_ops(g, g->buf, &ops);
+  LocalView L;
+  make_local(g, g->buf, &L);
+  simplify_ops(&L.lg, L.ops, &ops);
   if (ops.empty()) {
     // every op was dead: nothing to run, and nothing is stored
     for (auto& o : g->buf) {
@@ -1840,7 +1876,7 @@ dvm_status encode_buffer(dvm_graph* g, dvm_program** out) {
   }
   dvm_program* p = new (std::nothrow) dvm_program();
   if (!p) return fail(DVM_ERR_INTERNAL, "out of host memory");
-  Encoder enc(g, ops, p);
+  Encoder enc(&L.lg, ops, p);
   dvm_status st = enc.run();
   // The wide VM for row-reduction programs that keep every tile value in the
   // accumulator, when the wide plan puts more rows in a tile and either keeps
@@ -1855,7 +1891,7 @@ dvm_status encode_buffer(dvm_graph* g, dvm_program** out) {
     const std::string err = g_err;
     dvm_program* q = new (std::nothrow) dvm_program();
     if (q) {
-      Encoder w(g, ops, q);
+      Encoder w(&L.lg, ops, q);
       w.wide();
       const dvm_status sw = w.run();
       // (staging matters only where a workgroup runs more than one tile)
@@ -2062,7 +2098,9 @@ dvm_status end_group_impl(dvm_graph* g, int32_t* flushed) {
   if (!g->buf.empty()) {
     std::vector<OpRec> cand = g->buf;
     cand.insert(cand.end(), grp.begin(), grp.end());
-    Checker ck(g, cand);
+    LocalView L;
+    make_local(g, cand, &L);
+    Checker ck(&L.lg, L.ops);
     const int why = ck.check(g->buf.size());
     if (why < 0) {
       g->buf.swap(cand);
@@ -2084,7 +2122,9 @@ dvm_status end_group_impl(dvm_graph* g, int32_t* flushed) {
       return st;
     }
   }
-  Checker ck(g, grp);
+  LocalView L;
+  make_local(g, grp, &L);
+  Checker ck(&L.lg, L.ops);
   const int why = ck.check(0);
   if (why >= 0) {
     g->stats.unsupported++;
