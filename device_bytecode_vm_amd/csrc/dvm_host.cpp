@@ -2432,29 +2432,35 @@ void dvm_program_free(dvm_program* p) { delete p; }
 dvm_status dvm_program_debug_tilemap(const dvm_program* p, const dvm_tensor* tile_out, const dvm_tensor* wg_out,
                                      dvm_program** out) {
   if (!p || !tile_out || !wg_out || !out) return fail(DVM_ERR_INVALID_ARG, "null argument");
-  if (p->prog.w[H_KTYPE] != KT_VECTOR && p->prog.w[H_KTYPE] != KT_VECTOR_WIDE)
-    return fail(DVM_ERR_UNSUPPORTED, "vector programs only");
+  const uint32_t kt = p->prog.w[H_KTYPE];
+  if (kt != KT_VECTOR && kt != KT_VECTOR_WIDE && kt != KT_MIX) return fail(DVM_ERR_UNSUPPORTED, "unknown kernel type");
   for (const dvm_tensor* t : {tile_out, wg_out}) {
     if (t->dtype != DVM_F32 || t->ndim != 2 || t->shape[0] != p->R || t->shape[1] != p->C || t->stride[1] != 1 ||
-        t->stride[0] != p->C)
+        t->stride[0] != p->C || (!t->data && p->R * p->C > 0))
       return fail(DVM_ERR_SHAPE, "tilemap outputs must be dense fp32 [R, C]");
   }
   dvm_program* q = new (std::nothrow) dvm_program(*p);
   if (!q) return fail(DVM_ERR_INTERNAL, "out of host memory");
   uint32_t* W = q->prog.w;
-  const uint32_t n_args = 2;
+  // MIX programs keep A and B (args 0 and 1: the K loop still runs, its
+  // result unused) and write the maps from the epilogue
+  const bool mix = kt == KT_MIX;
+  const uint32_t a0 = mix ? 2u : 0u;
+  const uint32_t n_args = a0 + 2;
   W[H_NARGS] = n_args;
-  W[H_TEMPLATE] = TM_ELEMWISE;  // same tiling; no reduce-all epilogue
-  W[H_LDS_BYTES] = 0;
-  int k = 0;
+  if (!mix) {
+    W[H_TEMPLATE] = TM_ELEMWISE;  // same tiling; no reduce-all epilogue
+    W[H_LDS_BYTES] = 0;
+  }
+  uint32_t k = a0;
   for (const dvm_tensor* t : {tile_out, wg_out}) {
     uint32_t* a = W + ARG_BASE + k * ARG_WORDS;
     const uint64_t ptr = (uint64_t)(uintptr_t)t->data;
     a[A_PTR_LO] = (uint32_t)ptr;
     a[A_PTR_HI] = (uint32_t)(ptr >> 32);
     a[A_DTYPE] = DT_F32;
-    a[A_FLAGS] = arg_flags_word(0, (uint64_t)extent_bytes(*t));
-    const int64_t sr = p->R > 1 ? p->C : 0;
+    a[A_FLAGS] = arg_flags_word(mix && ptr % 16 == 0 && p->C % 4 == 0 ? AF_VEC : 0u, (uint64_t)extent_bytes(*t));
+    const int64_t sr = p->R > 1 || mix ? p->C : 0;
     a[A_SR_LO] = (uint32_t)(uint64_t)sr;
     a[A_SR_HI] = (uint32_t)((uint64_t)sr >> 32);
     a[A_SC] = 1;
@@ -2462,8 +2468,11 @@ dvm_status dvm_program_debug_tilemap(const dvm_program* p, const dvm_tensor* til
     ++k;
   }
   const uint32_t base = ARG_BASE + n_args * ARG_WORDS;
-  const uint32_t code[] = {enc0(HD_DBG, 0, 0, 0, 0, 0, 0), 0, enc0(HD_ST_F32, 0, 0, 0, 0, 0, 0), 0,
-                           enc0(HD_DBG, 0, 0, 0, 1, 0, 0), 0, enc0(HD_ST_F32, 0, 0, 0, 0, 0, 0), 1};
+  // vector programs take handler ids, MIX epilogues the generic opcodes
+  const uint32_t dbg = mix ? (uint32_t)OP_DBG : (uint32_t)HD_DBG;
+  const uint32_t st = mix ? (uint32_t)OP_STORE : (uint32_t)HD_ST_F32;
+  const uint32_t code[] = {enc0(dbg, 0, 0, 0, 0, 0, 0), a0, enc0(st, 0, 0, 0, 0, 0, 0), a0,
+                           enc0(dbg, 0, 0, 0, 1, 0, 0), 0, enc0(st, 0, 0, 0, 0, 0, 0), a0 + 1};
   std::memcpy(W + base, code, sizeof code);
   W[H_PRO_BEGIN] = W[H_PRO_END] = W[H_BODY_BEGIN] = base;
   W[H_BODY_END] = base + 8;

@@ -300,6 +300,7 @@ struct TV {
 template <int U>
 struct Round {
   int64_t m0, n0;  // tile origin in [M, N]
+  uint32_t tile;   // row-major tile id (row tile * column tiles + column tile)
   int r[U];        // chunk rows inside the tile
   int c8;          // first column of this lane's chunks inside the tile
   bool ok[U];      // chunk inside [M, N]
@@ -503,6 +504,15 @@ __device__ __forceinline__ void run_epilogue(KW* W, TV<U>& t0, const Round<U>& C
         for (int i = 0; i < 8 * U; ++i) t0.v[i] = una_rt(f, t0.v[i]);
         break;
       }
+      case OP_DBG: {
+        // debug tile maps: the tile's row-major id (sub 0) or the workgroup (sub 1)
+        TV<U> m;
+        const float v = f_sub(w0) == 0 ? (float)C.tile : (float)blockIdx.x;
+#pragma unroll
+        for (int i = 0; i < 8 * U; ++i) m.v[i] = v;
+        put(f_dst(w0), m, t0, t1, t2);
+        break;
+      }
       default:
         break;
     }
@@ -545,7 +555,7 @@ __device__ __forceinline__ void load_invariants(KW* W, Inv& I, int64_t n0, int64
 template <class CF, int S>
 __device__ __forceinline__ void epilogue_slab(KW* W, const f16v (&c)[CF::BM][CF::BN], char* lds, int64_t m0,
                                               int64_t n0, int64_t M, int64_t N, int wm, int wn, int tid,
-                                              const Inv& I) {
+                                              const Inv& I, uint32_t tile) {
   constexpr int U = CF::U;
   const int lane = tid & 63;
   float* ot = (float*)lds;
@@ -563,6 +573,7 @@ __device__ __forceinline__ void epilogue_slab(KW* W, const f16v (&c)[CF::BM][CF:
   Round<U> C;
   C.m0 = m0;
   C.n0 = n0;
+  C.tile = tile;
   C.c8 = (tid % CF::LPR) * 8;
 #pragma nounroll
   for (int p = 0; p < CF::SP; p += U) {
@@ -586,9 +597,9 @@ __device__ __forceinline__ void epilogue_slab(KW* W, const f16v (&c)[CF::BM][CF:
 template <class CF, int S>
 __device__ __forceinline__ void epilogue_slabs(KW* W, const f16v (&c)[CF::BM][CF::BN], char* lds, int64_t m0,
                                                int64_t n0, int64_t M, int64_t N, int wm, int wn, int tid,
-                                               const Inv& I) {
-  epilogue_slab<CF, S>(W, c, lds, m0, n0, M, N, wm, wn, tid, I);
-  if constexpr (S + 1 < CF::NSL) epilogue_slabs<CF, S + 1>(W, c, lds, m0, n0, M, N, wm, wn, tid, I);
+                                               const Inv& I, uint32_t tile) {
+  epilogue_slab<CF, S>(W, c, lds, m0, n0, M, N, wm, wn, tid, I, tile);
+  if constexpr (S + 1 < CF::NSL) epilogue_slabs<CF, S + 1>(W, c, lds, m0, n0, M, N, wm, wn, tid, I, tile);
 }
 
 // ---------------------------------------------------------------------------
@@ -687,7 +698,7 @@ __device__ __forceinline__ void mix_body(char* lds) {
       mma<CF>(c, f[1]);
     }
     lds_barrier();
-    epilogue_slabs<CF, 0>(W, c, lds, P.m0, P.n0, M, N, wm, wn, tid, I);
+    epilogue_slabs<CF, 0>(W, c, lds, P.m0, P.n0, M, N, wm, wn, tid, I, ir * nct + ic);
   }
 }
 

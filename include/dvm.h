@@ -122,8 +122,9 @@ typedef struct {
   double launch_us_total;     /* host time of the launches of implicit and explicit flushes */
 } dvm_stats;
 
-/* Contexts.  device >= 0: the HIP device whose resident VM kernels run the
- * programs.  Reduce-all programs need a scratch area on the device (a counter
+/* Contexts (the VM's code is loaded once and stays resident: MindSpore DVM
+ * summary page, section 3.2).  device >= 0: the HIP device whose resident VM
+ * kernels run the programs.  Reduce-all programs need a scratch area on the device (a counter
  * and one partial per tile): each stream gets its own 4 MiB area, allocated
  * and zeroed at the first reduce-all launched on it and freed with the
  * context, so launches on different streams never share it.
@@ -131,25 +132,34 @@ typedef struct {
 dvm_status dvm_context_create(int device, dvm_context** out);
 void dvm_context_destroy(dvm_context* ctx);
 
-/* A graph is a streaming fusion buffer bound to a HIP stream (hipStream_t,
- * NULL = default stream); implicit flushes launch on that stream. */
+/* A graph is a streaming fusion buffer (the dynamic-graph streaming fusion of
+ * the DVM review page, section 5.2; ops are captured in execution order,
+ * MindSpore summary page, section 3.2) bound to a HIP stream (hipStream_t,
+ * NULL = default stream); implicit flushes launch on that stream.  Errors:
+ * DVM_ERR_INVALID_ARG for a null context or out. */
 dvm_status dvm_graph_create(dvm_context* ctx, void* stream, dvm_graph** out);
 void dvm_graph_destroy(dvm_graph* g);
 
 /* A graph of an encode-only context cannot launch what it flushes implicitly
- * (at a fusion boundary, or when a reduce-all closes its graph): those
+ * (flushes at fusion boundaries and sync points: MindSpore summary page,
+ * section 3.2)
+ * -- at a fusion boundary, or when a reduce-all closes its graph: those
  * programs wait in the graph, at most 4096 of them (older ones are freed).
  * This hands out the oldest one, or *out = NULL if none waits; the caller
  * frees it with dvm_program_free.  It may be launched on a device context if
  * its tensors' addresses are that device's. */
 dvm_status dvm_graph_take_program(dvm_graph* g, dvm_program** out);
 
-/* Registers an external tensor (read by ops, never written through this
- * handle). */
+/* Registers an external tensor (a graph input: the tensors a Load reads,
+ * DVM review page, section 4.1, Table 1) as a value; read by ops, never
+ * written through this handle.  The tensor struct is copied; its memory is
+ * borrowed.  DVM_ERR_INVALID_ARG for a malformed tensor (ndim > 4, negative
+ * dims or strides, unknown dtype). */
 dvm_status dvm_graph_input(dvm_graph* g, const dvm_tensor* t, dvm_value* out);
 
 /* Groups: ops added between begin and end are decided together (a composite
- * such as LayerNorm).  An op added outside a group is a group of its own.
+ * such as LayerNorm; the fusion decision of the DVM review page, section 5.2:
+ * shape compatibility and dependence, flush when they fail).  An op added outside a group is a group of its own.
  * end_group fuses the group into the buffered graph or, when the fusion
  * conditions fail, flushes the buffered graph (encode + launch on the graph's
  * stream) and starts a new graph with the group (*flushed = 1).  A group the
@@ -158,26 +168,34 @@ dvm_status dvm_graph_input(dvm_graph* g, const dvm_tensor* t, dvm_value* out);
 dvm_status dvm_graph_begin_group(dvm_graph* g);
 dvm_status dvm_graph_end_group(dvm_graph* g, int32_t* flushed);
 
-/* Appends one op.  in[] are value handles; n_in counts tensor inputs (1 for a
+/* Appends one op (a primitive of the DVM review page's instruction set,
+ * section 4.1, Table 1, and the binary ops, reductions and matmul its fusion
+ * patterns use, section 5.1).  in[] are value handles; n_in counts tensor inputs (1 for a
  * binary op with a scalar operand, see dvm_attrs).  out gives the output's
  * dtype and storage (shape must equal the inferred shape; data may be NULL if
  * the value is released before its graph is flushed).  Writes the new value's
- * handle to *out_value. */
+ * handle to *out_value.  Errors: DVM_ERR_SHAPE (inputs do not broadcast, or
+ * out's shape differs from the inferred one), DVM_ERR_UNSUPPORTED (dtype or
+ * operand form the VM does not run), DVM_ERR_INVALID_ARG (unknown, released or
+ * lost input); outside a group, also the errors of dvm_graph_end_group. */
 dvm_status dvm_graph_add_op(dvm_graph* g, int32_t op, const dvm_value* in, int32_t n_in,
                             const dvm_attrs* attrs, const dvm_tensor* out, uint32_t flags,
                             dvm_value* out_value);
 
 /* The caller will not use the value again (neither as an input nor by reading
- * its storage).  A released value whose graph has not been flushed yet is
+ * its storage): what the fuser needs to keep intermediate values on chip (DVM
+ * review page, section 5.1: intermediate results stay in local memory).  A released value whose graph has not been flushed yet is
  * never stored unless DVM_OUT_LIVE was given. */
 dvm_status dvm_graph_release(dvm_graph* g, dvm_value v);
 
-/* Output shape of an op (for allocating out). */
+/* Output shape of an op (for allocating out; the shape inference the
+ * streaming fuser runs per op, DVM review page, section 5.2).  DVM_ERR_SHAPE
+ * if the inputs do not fit the op. */
 dvm_status dvm_graph_infer_shape(dvm_graph* g, int32_t op, const dvm_value* in, int32_t n_in,
                                  const dvm_attrs* attrs, dvm_tensor* out_shape);
 
-/* Encodes the buffered graph into a program (shape tiling + bytecode) and
- * empties the buffer; *out = NULL when the buffer is empty or no buffered op
+/* Encodes the buffered graph into a program (shape tiling, DVM review page,
+ * section 4.2; code header and body, section 4.3) and empties the buffer; *out = NULL when the buffer is empty or no buffered op
  * has an effect (every result is released unread: such ops are dropped, as
  * are x*1, x/1, x-(+0), x+(-0) and same-dtype casts nobody stores, which the
  * encoder folds into their operand; results are bit-identical either way).
@@ -185,7 +203,10 @@ dvm_status dvm_graph_infer_shape(dvm_graph* g, int32_t op, const dvm_value* in, 
 dvm_status dvm_flush(dvm_graph* g, dvm_program** out);
 
 /* Launches a program on the resident VM kernel of its kernel type, on
- * stream (hipStream_t).  Asynchronous. */
+ * stream (hipStream_t): each workgroup finds its tiles from the header and
+ * interprets the body tile by tile (DVM review page, section 4.4).  The
+ * program is copied into the launch.  Asynchronous; DVM_ERR_DEVICE for an
+ * encode-only context or a failed launch. */
 dvm_status dvm_launch(dvm_context* ctx, const dvm_program* p, void* stream);
 
 /* dvm_launch for callers that cannot allocate device memory (code under HIP
@@ -221,26 +242,37 @@ dvm_status dvm_launch_noalloc(dvm_context* ctx, const dvm_program* p, void* stre
 dvm_status dvm_launch_profiled(dvm_context* ctx, const dvm_program* p, void* stream, uint64_t* counters,
                                size_t n_counters);
 
-/* dvm_flush + dvm_launch on the graph's stream (no-op when nothing is
- * encoded; *launched = 0 then). */
+/* dvm_flush + dvm_launch on the graph's stream (an explicit flush, MindSpore
+ * summary page, section 3.2; no-op when nothing is encoded; *launched = 0
+ * then). */
 dvm_status dvm_graph_flush_launch(dvm_graph* g, int32_t* launched);
 
-/* Synchronisation point: flush + launch, then wait for the graph's stream.
+/* Synchronisation point (flush at the sync interface, MindSpore summary page,
+ * section 3.2): flush + launch, then wait for the graph's stream.
  * Asynchronous device errors surface here as DVM_ERR_DEVICE. */
 dvm_status dvm_sync(dvm_graph* g);
 
+/* The code header of a program (DVM review page, section 4.3). */
 dvm_status dvm_program_header(const dvm_program* p, dvm_header* out);
-/* Copies the program words; *n_words in: capacity, out: size. */
+/* Copies the program words (header, operand table, body: the bytecode of the
+ * DVM review page, section 4.3); *n_words in: capacity, out: size.  buf may be
+ * NULL to query the size. */
 dvm_status dvm_program_words(const dvm_program* p, uint32_t* buf, size_t* n_words);
 void dvm_program_free(dvm_program* p);
 
-/* Debug program for tiling parity: same header and tiling as p, whose body
- * writes, for every element of the collapsed [R, C] space, the id of the tile
- * that holds it into tile_out and the workgroup that ran it into wg_out (both
- * dense fp32 [R, C]). */
+/* Debug program for tiling parity (the tile range and element-to-tile rules
+ * of the DVM review page, sections 4.2 and 4.4): same header and tiling as p,
+ * whose body writes, for every element of the collapsed [R, C] space (a MIX
+ * program: its [M, N] output), the row-major id of the tile that holds it into
+ * tile_out and the workgroup that ran that tile into wg_out (both dense fp32
+ * [R, C], caller-owned device memory).  A MIX debug program still reads the
+ * matmul operands of p (its K loop runs; the result is unused).
+ * DVM_ERR_SHAPE for outputs of another shape, layout or dtype. */
 dvm_status dvm_program_debug_tilemap(const dvm_program* p, const dvm_tensor* tile_out,
                                      const dvm_tensor* wg_out, dvm_program** out);
 
+/* Counters of the graph's fuser and encoder (the compile-time and fusion
+ * measurements of the DVM review page, section 6). */
 dvm_status dvm_graph_stats(const dvm_graph* g, dvm_stats* out);
 
 /* Partition record of the graphs flushed so far, oldest first: graph i held
@@ -251,6 +283,7 @@ dvm_status dvm_graph_stats(const dvm_graph* g, dvm_stats* out);
  * graphs recorded. */
 dvm_status dvm_graph_flush_log(const dvm_graph* g, int32_t* n_ops, int32_t* reasons, float* encode_us,
                                uint64_t* bytes, size_t* n);
+/* Thread-local message of the last failed call on this thread. */
 const char* dvm_last_error(void);
 
 #ifdef __cplusplus

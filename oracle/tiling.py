@@ -67,14 +67,28 @@ design notes):
   (tm K + K tn elements) plus its varying epilogue operand and output bytes and
   flops = 2 tm tn K.  The least cost wins; ties go to the earlier (larger)
   entry.
-* Header and ranges: block_dim = n_tiles; body_tile = ceil(block_dim / min(G,
-  block_dim)); grid = ceil(block_dim / body_tile).  A core's "tile range"
-  (section 4.4) is read as the strided set b, b + grid, b + 2 grid, ... below
-  block_dim: at most body_tile tiles, and at any moment the resident
-  workgroups run neighbouring tiles, so their streams advance together
-  through memory (on MI355X 6% faster on the LayerNorm stream and up to 14%
-  on copy-like graphs than contiguous ranges).  Tile id -> (ir, ic) is
+* Header: block_dim = n_tiles; body_tile = ceil(block_dim / min(G,
+  block_dim)); grid = ceil(block_dim / body_tile).  Tile id -> (ir, ic) is
   row-major with the column index fastest.
+
+Deviations from the page (stated here because the tile maps follow them):
+
+* Tile range of a core (section 4.4).  The page has each core compute its
+  tile range, which reads most plainly as the contiguous range [b body_tile,
+  (b + 1) body_tile).  This build gives workgroup b the strided set b,
+  b + grid, b + 2 grid, ... below block_dim instead: still at most body_tile
+  tiles, but at any moment the resident workgroups run neighbouring tiles, so
+  their streams advance together through memory (on MI355X 6% faster on the
+  LayerNorm stream and up to 14% on copy-like graphs).
+* MIX tile order.  The MIX kernel keeps block_dim, body_tile and grid, and
+  walks the [M, N] output tiles in a grouped order for the L2 caches of the
+  eight XCDs: row tiles go in groups of MM_GROUP = 8; inside a group the
+  order runs column by column with the group's row tiles fastest.  Workgroups
+  are dispatched to the XCDs in turn (b to XCD b mod 8), and the kernel gives
+  the workgroups of one XCD consecutive starting positions in that order:
+  with grid8 = grid rounded down to a multiple of 8, workgroup b = 8 k + x
+  (b < grid8) starts at position x (grid8 / 8) + k, a workgroup past grid8 at
+  position b; each then takes every grid-th position below block_dim.
 """
 from __future__ import annotations
 
@@ -94,6 +108,8 @@ ELEMWISE, ROWREDUCE, ALLREDUCE, MATMUL = "elemwise", "rowreduce", "allreduce", "
 
 # (tm, tn, resident workgroups) of the MIX kernel's tile variants, largest first
 MM_TILES = [(128, 128, 512)]
+MM_GROUP = 8        # row tiles per group of the MIX tile order
+N_XCD = 8           # accelerator complex dies (each with its own L2)
 
 
 def cdiv(a: int, b: int) -> int:
@@ -366,5 +382,50 @@ def element_tile_map(p: Plan):
             if (tiles[r0:r1, c0:c1] != -1).any():
                 raise AssertionError("element covered twice")
             tiles[r0:r1, c0:c1] = t
+            wgs[r0:r1, c0:c1] = b
+    return tiles, wgs
+
+
+# ---------------------------------------------------------------------------
+# MIX tile order
+# ---------------------------------------------------------------------------
+def mix_tile_coords(v: int, n_r: int, n_c: int):
+    """(row tile, column tile) at position v of the grouped order."""
+    per_group = MM_GROUP * n_c
+    grp, w = divmod(v, per_group)
+    r0 = grp * MM_GROUP
+    rows = min(MM_GROUP, n_r - r0)
+    return r0 + w % rows, w // rows
+
+
+def mix_first_position(b: int, grid: int) -> int:
+    """Starting position of workgroup b in the grouped order."""
+    grid8 = grid - grid % N_XCD
+    if b >= grid8:
+        return b
+    k, x = divmod(b, N_XCD)
+    return x * (grid8 // N_XCD) + k
+
+
+def mix_workgroup_positions(b: int, grid: int, block_dim: int):
+    return range(mix_first_position(b, grid), block_dim, grid)
+
+
+def mix_element_tile_map(p: Plan):
+    """For every element (m, n) of a MATMUL plan's [M, N] output: the
+    row-major id of the tile that holds it and the workgroup that runs it,
+    built by walking every workgroup's positions (so it also checks that the
+    order covers every element exactly once)."""
+    import numpy as np
+    tiles = np.full((p.R, p.C), -1, dtype=np.int64)
+    wgs = np.full((p.R, p.C), -1, dtype=np.int64)
+    for b in range(p.grid):
+        for v in mix_workgroup_positions(b, p.grid, p.block_dim):
+            ir, ic = mix_tile_coords(v, p.n_r, p.n_c)
+            r0, r1 = ir * p.tr, min(ir * p.tr + p.tr, p.R)
+            c0, c1 = ic * p.tc, min(ic * p.tc + p.tc, p.C)
+            if (tiles[r0:r1, c0:c1] != -1).any():
+                raise AssertionError("element covered twice")
+            tiles[r0:r1, c0:c1] = ir * p.n_c + ic
             wgs[r0:r1, c0:c1] = b
     return tiles, wgs

@@ -156,3 +156,33 @@ def test_matmul_output_beyond_2gib(dvm, ctx):
     assert ok, f"max rel err {e:.3g}"
     del y
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("m,n", [(300, 1000), (2000, 17408), (8192, 17408), (1, 128), (129, 4000)])
+def test_mix_tilemap_bit_exact(dvm, ctx, m, n):
+    """The MIX kernel's element -> tile and tile -> workgroup maps equal the
+    oracle's statement of the grouped, XCD-aware tile order."""
+    import torch
+    from device_bytecode_vm_amd import composites as CP
+    from oracle import tiling as TL
+    say("mix_tilemap", m, n)
+    k = 64
+    a = torch.zeros((m, k), dtype=torch.bfloat16, device="cuda")
+    b = torch.zeros((k, n), dtype=torch.bfloat16, device="cuda")
+    bias = torch.zeros((n,), dtype=torch.float32, device="cuda")
+    y = empty_dev((m, n), "bf16")
+    g = dvm.Graph(ctx)
+    CP.matmul_bias_silu(g, g.input(a), g.input(b), g.input(bias), out=y)
+    p = g.flush()
+    h = p.header()
+    plan = TL.plan_matmul(m, n, k, 2, 2, [TL.Operand(4, 0, 1), TL.Operand(2, n, 1)])
+    assert (h["tr"], h["tc"], h["block_dim"], h["body_tile"], h["grid"]) == \
+        (plan.tr, plan.tc, plan.block_dim, plan.body_tile, plan.grid)
+    tiles = torch.full((m, n), -1.0, dtype=torch.float32, device="cuda")
+    wgs = torch.full((m, n), -1.0, dtype=torch.float32, device="cuda")
+    dbg = p.debug_tilemap(tiles, wgs)
+    dbg.launch()
+    torch.cuda.synchronize()
+    et, ew = TL.mix_element_tile_map(plan)
+    assert np.array_equal(host64(tiles), et)
+    assert np.array_equal(host64(wgs), ew)

@@ -188,3 +188,39 @@ def test_matmul_plan_by_hand():
     assert tiles[299, 999] == 23 and tiles[256, 0] == 16 and tiles[0, 896] == 7
     assert (tiles >= 0).all()
     assert TL.plan_matmul(0, 5, 8, 2, 2, []).block_dim == 0
+
+
+# ---------------------------------------------------------------------------
+# MIX tile order (grouped rows, XCD-aware starting positions)
+# ---------------------------------------------------------------------------
+def test_mix_order_hand_worked():
+    # 10 row tiles x 3 column tiles: the first group holds rows 0..7, the
+    # second rows 8..9; inside a group the order walks column by column
+    order = [TL.mix_tile_coords(v, 10, 3) for v in range(30)]
+    assert order[:9] == [(0, 0), (1, 0), (2, 0), (3, 0), (4, 0), (5, 0), (6, 0), (7, 0), (0, 1)]
+    assert order[23] == (7, 2)
+    assert order[24:] == [(8, 0), (9, 0), (8, 1), (9, 1), (8, 2), (9, 2)]
+    # grid 500: grid8 = 496, 62 positions per XCD; workgroup 8k + x starts at 62x + k
+    assert [TL.mix_first_position(b, 500) for b in (0, 1, 7, 8, 9, 495, 496, 499)] == \
+        [0, 62, 434, 1, 63, 495, 496, 499]
+
+
+@pytest.mark.parametrize("n_r,n_c,grid", [(10, 3, 30), (64, 136, 512), (16, 136, 512), (3, 5, 15), (1, 1, 1),
+                                          (9, 7, 63)])
+def test_mix_order_is_a_bijection(n_r, n_c, grid):
+    block_dim = n_r * n_c
+    body_tile = -(-block_dim // min(512, block_dim))
+    seen = set()
+    for b in range(grid):
+        pos = list(TL.mix_workgroup_positions(b, grid, block_dim))
+        assert len(pos) <= body_tile
+        seen.update(TL.mix_tile_coords(v, n_r, n_c) for v in pos)
+    assert seen == {(r, c) for r in range(n_r) for c in range(n_c)}
+    assert sorted(TL.mix_first_position(b, grid) for b in range(grid)) == list(range(grid))
+
+
+def test_mix_element_map_covers_ragged_output():
+    p = TL.plan_matmul(300, 1000, 64, 2, 2, [])
+    tiles, wgs = TL.mix_element_tile_map(p)
+    assert (tiles >= 0).all() and (wgs >= 0).all()
+    assert tiles[299, 999] == (p.n_r - 1) * p.n_c + p.n_c - 1
