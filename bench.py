@@ -607,13 +607,34 @@ def ifelse_bench(args):
         torch.cuda.synchronize()
 
     one_step()
-    n_log0 = len(g.flush_log())
     t0 = time.perf_counter()
     for _ in range(steps):
         one_step()
-    dt = (time.perf_counter() - t0) / steps
-    log = g.flush_log(detail=True)[n_log0:]
+    dt_host = (time.perf_counter() - t0) / steps
     assert taken == [bool(c) for c in coin], "branch differs from the sign the input was drawn with"
+
+    # device-side branch: a branch program per call reads the reduce-all's
+    # result on the device, so calls queue back to back (one sync per step)
+    gd = dvm.Graph(ctx, stream)
+
+    def dev_step():
+        for (r, _), c in zip(shapes, coin):
+            vx, vy = gd.input((xp if c else xn)[:r]), gd.input(yy[:r])
+            vs = gd.op("reduce_sum", vx, out=s, live=True, axis=0x7FFFFFFF)
+            gd.begin_branch(vs, 0.0)
+            gd.op("add", vx, vy, out=out[:r], live=True)
+            gd.else_branch()
+            gd.op("sub", vx, vy, out=out[:r], live=True)
+            gd.end_branch()
+        torch.cuda.synchronize()
+
+    dev_step()
+    n_log0 = len(gd.flush_log())
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        dev_step()
+    dt = (time.perf_counter() - t0) / steps
+    log = gd.flush_log(detail=True)[n_log0:]
     # device-only: the branch is known from the input's sign, so every call's
     # reduce-all (launched when it closes its graph) and branch program are
     # queued back to back with no host sync
@@ -635,9 +656,11 @@ def ifelse_bench(args):
             "steps": steps, "warmup": 1, "ms_per_step": round(dt * 1e3, 3),
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
             "config": {"workload": "if_else_add", "calls_per_step": len(shapes), "cols": C,
-                       "rows": "N ~ U{1..16384}, seed 0", "branch": "host-resolved after a reduce-all",
+                       "rows": "N ~ U{1..16384}, seed 0",
+                       "branch": "device-side: a branch program reads the reduce-all's result on the GPU",
                        "add_branch_calls": int(sum(coin))},
             "encode_us": encode_stats(log),
+            "e2e_host_branch_gbs": round(nbytes / dt_host / 1e9, 2),
             "device_only_gbs": round(kern, 2),
             "roofline": {"bound": "hbm", "achieved": round(kern, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": round(kern / HBM_PEAK_GBS, 4), "traffic": None, "kernel": "dvm_vm_vector",
@@ -740,7 +763,7 @@ def brief(res):
     keep = ("value", "unit", "ms_per_step", "steps", "config", "encode_us", "roofline", "device_only_gbs",
             "device_only_tflops", "kernel_us_warm", "kernel_us_cold", "device_only_gbs_cold", "effective_gbs",
             "graphs_per_step", "launches_per_step", "ops_per_step", "flush_reasons_per_step", "fuse_us_per_op",
-            "context", "note", "cpu_baseline")
+            "context", "note", "e2e_host_branch_gbs", "cpu_baseline")
     return {k: res[k] for k in keep if k in res}
 
 

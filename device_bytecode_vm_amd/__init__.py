@@ -280,6 +280,21 @@ class Graph:
         prog._keep = keep
         return prog
 
+    # -- device-side control flow -----------------------------------------
+    def begin_branch(self, cond: "Value", threshold: float = 0.0):
+        """Ops until else_branch() form the then-body, run iff cond > threshold
+        (cond: one fp32 value, read on the device)."""
+        check(lib.dvm_graph_begin_branch(self.h, cond.h, float(threshold)))
+
+    def else_branch(self):
+        check(lib.dvm_graph_else_branch(self.h))
+
+    def end_branch(self) -> bool:
+        """Encodes both bodies into one branch program and launches it."""
+        fl = C.c_int32(0)
+        check(lib.dvm_graph_end_branch(self.h, C.byref(fl)))
+        return bool(fl.value)
+
     def take_program(self):
         """The oldest program an encode-only context flushed implicitly (at a
         fusion boundary or a reduce-all), or None."""
@@ -320,7 +335,7 @@ class Graph:
         return {
             "graphs": s.graphs, "launches": s.launches, "ops": s.ops, "groups": s.groups,
             "unsupported": s.unsupported,
-            "flush_reason": {L.FLUSH_REASONS[i]: s.flush_reason[i] for i in range(7)},
+            "flush_reason": {L.FLUSH_REASONS[i]: s.flush_reason[i] for i in range(8)},
             "encode_us_total": s.encode_us_total, "encode_us_max": s.encode_us_max, "bytes": s.bytes,
             "fuse_us_total": s.fuse_us_total, "launch_us_total": s.launch_us_total,
         }

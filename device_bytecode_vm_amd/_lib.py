@@ -43,7 +43,7 @@ BINARY = set(OPS[:7])
 AXIS_ALL = 0x7FFFFFFF
 OUT_LIVE = 1
 
-FLUSH_REASONS = ["explicit", "sync", "reduce_all", "shape", "pattern", "dependence", "resource", "-"]
+FLUSH_REASONS = ["explicit", "sync", "reduce_all", "shape", "pattern", "dependence", "resource", "branch"]
 
 
 class DvmTensor(C.Structure):
@@ -90,6 +90,9 @@ _sigs = {
     "dvm_launch_noalloc": (C.c_int, [VP, VP, VP]),
     "dvm_launch_profiled": (C.c_int, [VP, VP, VP, VP, C.c_size_t]),
     "dvm_graph_flush_launch": (C.c_int, [VP, P(C.c_int32)]),
+    "dvm_graph_begin_branch": (C.c_int, [VP, C.c_int64, C.c_float]),
+    "dvm_graph_else_branch": (C.c_int, [VP]),
+    "dvm_graph_end_branch": (C.c_int, [VP, P(C.c_int32)]),
     "dvm_sync": (C.c_int, [VP]),
     "dvm_program_header": (C.c_int, [VP, P(DvmHeader)]),
     "dvm_program_words": (C.c_int, [VP, P(C.c_uint32), P(C.c_size_t)]),

@@ -21,7 +21,7 @@
 namespace dvmbc {
 
 constexpr uint32_t MAGIC = 0x314d5644u;  // "DVM1"
-constexpr uint32_t VERSION = 2;
+constexpr uint32_t VERSION = 3;
 
 // Device geometry constants: one workgroup of T lanes runs a tile; a tile row
 // is spread over g lanes, each holding up to NV_MAX chunks of V elements.  Two
@@ -40,7 +40,7 @@ constexpr int N_RREG = 4;             // row registers
 constexpr int N_LDSBUF = 8;           // cross-wave reduction buffers
 constexpr int MAX_WORDS = 1000;       // whole program, <= 4000 bytes of kernarg
 constexpr int PAD_WORDS = 2;          // unused words after the body (the VM reads one instruction ahead)
-constexpr int HDR_WORDS = 40;
+constexpr int HDR_WORDS = 44;
 constexpr int ARG_BASE = HDR_WORDS;
 constexpr int ARG_WORDS = 8;
 constexpr int MAX_ARGS = 32;
@@ -90,6 +90,10 @@ enum Hdr : int {
   H_PROF_LO = 37,    // profiling launches only: device address of the per-workgroup
   H_PROF_HI = 38,    //   cycle counters (5 x uint64 per workgroup)
   H_RED_OFF = 39,    // wide build: byte offset of the reduction buffers in dynamic LDS
+  H_COND_ARG = 40,   // branch programs (HF_BRANCH): arg index of the condition (0-d fp32)
+  H_COND_THR = 41,   //   the then-body runs iff condition > threshold (fp32 bits), strictly
+  H_ALT_BEGIN = 42,  //   word range of the else-body (the then-body is H_BODY_BEGIN..END)
+  H_ALT_END = 43,
 };
 
 // MIX kernel geometry: the output tile (header H_TR x H_TC) is one of the MIX
@@ -157,6 +161,11 @@ enum HdrFlag : uint32_t {
   // own throughput unchanged and shortens the wait of a host sync after a
   // launch, e.g. 9% end to end on the if-else stream.)
   HF_STREAM = 1u,
+  // a branch program: two bodies over one tiling, prologue and operand table;
+  // the VM reads the condition operand once and every tile runs the body it
+  // selects (device-side control flow: no host round trip between the launch
+  // that writes the condition and this one)
+  HF_BRANCH = 2u,
 };
 constexpr uint64_t STREAM_BYTES = 16ull << 20;
 enum ArgFlag : uint32_t {

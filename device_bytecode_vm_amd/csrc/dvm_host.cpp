@@ -408,7 +408,7 @@ bool is_reduce_all(const OpRec& o) { return is_reduce(o.op) && o.axis == DVM_AXI
 bool is_binary(int op) { return op <= DVM_OP_POW; }
 
 enum FlushReason { FR_EXPLICIT = 0, FR_SYNC = 1, FR_REDUCE_ALL = 2, FR_SHAPE = 3, FR_PATTERN = 4, FR_DEPENDENCE = 5,
-                   FR_RESOURCE = 6 };
+                   FR_RESOURCE = 6, FR_BRANCH = 7 };
 
 }  // namespace
 
@@ -458,6 +458,11 @@ struct dvm_graph {
   // here for dvm_graph_take_program (oldest first, at most MAX_HELD)
   std::deque<dvm_program*> held;
   std::vector<int32_t> remap;  // slot -> local index while a local view is built (-1 otherwise)
+  // a branch being captured: 1 then-ops, 2 else-ops (0 none)
+  int branch = 0;
+  int64_t branch_cond = -1;
+  float branch_thr = 0.f;
+  std::vector<OpRec> br[2];
   ~dvm_graph();
 };
 constexpr size_t MAX_HELD = 4096;
@@ -1852,28 +1857,15 @@ void simplify_ops(const dvm_graph* g, const std::vector<OpRec>& in, std::vector<
 // ===========================================================================
 // Flushing
 // ===========================================================================
-dvm_status encode_buffer(dvm_graph* g, dvm_program** out) {
+// Encodes one fused op list (after the bytecode clean-up); *out = NULL when no
+// op has an effect.  allow_wide: the wide VM build may be chosen.
+dvm_status encode_list(dvm_graph* g, const std::vector<OpRec>& list, bool allow_wide, dvm_program** out) {
   *out = nullptr;
-  if (g->buf.empty()) return DVM_OK;
-  auto t0 = std::chrono::steady_clock::now();
   std::vector<OpRec> ops;
   LocalView L;
-  make_local(g, g->buf, &L);
+  make_local(g, list, &L);
   simplify_ops(&L.lg, L.ops, &ops);
-  if (ops.empty()) {
-    // every op was dead: nothing to run, and nothing is stored
-    for (auto& o : g->buf) {
-      Val& v = g->vals[o.out];
-      v.pending = false;
-      v.stored = false;
-      v.lost = true;
-    }
-    std::vector<OpRec> done;
-    done.swap(g->buf);
-    drop_uses(g, done);
-    g->stats.graphs++;
-    return DVM_OK;
-  }
+  if (ops.empty()) return DVM_OK;  // every op was dead: nothing to run, nothing stored
   dvm_program* p = new (std::nothrow) dvm_program();
   if (!p) return fail(DVM_ERR_INTERNAL, "out of host memory");
   Encoder enc(&L.lg, ops, p);
@@ -1887,7 +1879,7 @@ dvm_status encode_buffer(dvm_graph* g, dvm_program** out) {
   // programs stay standard.
   const bool acc_only = st == DVM_OK && p->prog.w[H_KTYPE] == KT_VECTOR && enc.treg_hi == 0 &&
                         enc.plan.n_c == 1 && enc.plan.block_dim > 0 && enc.plan.tmpl == TM_ROWREDUCE;
-  if (acc_only || (st != DVM_OK && enc.plan_failed)) {
+  if (allow_wide && (acc_only || (st != DVM_OK && enc.plan_failed))) {
     const std::string err = g_err;
     dvm_program* q = new (std::nothrow) dvm_program();
     if (q) {
@@ -1909,30 +1901,113 @@ dvm_status encode_buffer(dvm_graph* g, dvm_program** out) {
       }
     }
   }
-  // the buffered values leave the buffer whatever the outcome
-  for (auto& o : g->buf) {
-    Val& v = g->vals[o.out];
-    v.pending = false;
-    const bool stored = st == DVM_OK && (v.live || !v.released) && v.t.data;
-    v.stored = stored;
-    v.lost = !stored;
-  }
-  std::vector<OpRec> done;
-  done.swap(g->buf);
-  drop_uses(g, done);
-  auto t1 = std::chrono::steady_clock::now();
-  const double us = std::chrono::duration<double, std::micro>(t1 - t0).count();
-  g->stats.graphs++;
-  g->stats.encode_us_total += us;
-  g->stats.encode_us_max = std::max(g->stats.encode_us_max, us);
-  if (!g->flush_log.empty()) g->flush_log.back().encode_us = (float)us;
   if (st != DVM_OK) {
     delete p;
     return st;
   }
-  g->stats.bytes += p->bytes;
-  if (!g->flush_log.empty()) g->flush_log.back().bytes = p->bytes;
   *out = p;
+  return DVM_OK;
+}
+
+// The ops leave the buffer: their values are stored (ran = a program that
+// computes them was produced) or lost; their input references are dropped.
+void retire(dvm_graph* g, std::vector<OpRec>& list, bool ran) {
+  for (auto& o : list) {
+    Val& v = g->vals[o.out];
+    v.pending = false;
+    const bool stored = ran && (v.live || !v.released) && v.t.data;
+    v.stored = stored;
+    v.lost = !stored;
+  }
+  drop_uses(g, list);
+}
+
+void note_encode(dvm_graph* g, std::chrono::steady_clock::time_point t0, const dvm_program* p) {
+  const double us = std::chrono::duration<double, std::micro>(std::chrono::steady_clock::now() - t0).count();
+  g->stats.graphs++;
+  g->stats.encode_us_total += us;
+  g->stats.encode_us_max = std::max(g->stats.encode_us_max, us);
+  if (!g->flush_log.empty()) g->flush_log.back().encode_us = (float)us;
+  if (p) {
+    g->stats.bytes += p->bytes;
+    if (!g->flush_log.empty()) g->flush_log.back().bytes = p->bytes;
+  }
+}
+
+dvm_status encode_buffer(dvm_graph* g, dvm_program** out) {
+  *out = nullptr;
+  if (g->buf.empty()) return DVM_OK;
+  const auto t0 = std::chrono::steady_clock::now();
+  dvm_program* p = nullptr;
+  const dvm_status st = encode_list(g, g->buf, true, &p);
+  // the buffered values leave the buffer whatever the outcome
+  std::vector<OpRec> done;
+  done.swap(g->buf);
+  retire(g, done, st == DVM_OK && p);
+  note_encode(g, t0, p);
+  if (st != DVM_OK) return st;
+  *out = p;
+  return DVM_OK;
+}
+
+// Branch program from the programs of the two bodies (DVM's dynamic control
+// flow, resolved on the device: the condition is read by the VM, not by the
+// host).  Both must share one tiling, operand table and prologue; the merged
+// program appends the condition operand to the table and the else-body after
+// the then-body.
+dvm_status merge_branch(const dvm_program* pt, const dvm_program* pe, const dvm_tensor& cond, float thr,
+                        dvm_program** out) {
+  const uint32_t* A = pt->prog.w;
+  const uint32_t* B = pe->prog.w;
+  static const int same[] = {H_KTYPE, H_TEMPLATE, H_BLOCK_DIM, H_BODY_TILE, H_GRID, H_TR, H_TC, H_G, H_NV, H_P,
+                             H_NC, H_NARGS, H_R_LO, H_R_HI, H_C_LO, H_C_HI, H_FLAGS, H_LDS_BYTES, H_PF_OFF0,
+                             H_PF_OFF1, H_INV_OFF0, H_INV_OFF1, H_INV_SHARED0, H_INV_SHARED1, H_RED_OFF};
+  for (int h : same)
+    if (A[h] != B[h]) return fail(DVM_ERR_UNSUPPORTED, "branch bodies differ in their tiling (header word %d)", h);
+  if (A[H_KTYPE] == KT_MIX || A[H_TEMPLATE] == TM_ALLREDUCE)
+    return fail(DVM_ERR_UNSUPPORTED, "branch bodies must be elementwise or row-reduce graphs");
+  const uint32_t n_args = A[H_NARGS];
+  for (uint32_t q = ARG_BASE; q < ARG_BASE + n_args * ARG_WORDS; ++q)
+    if (A[q] != B[q]) return fail(DVM_ERR_UNSUPPORTED, "branch bodies read or write different operands");
+  const uint32_t pro_n = A[H_PRO_END] - A[H_PRO_BEGIN];
+  if (pro_n != B[H_PRO_END] - B[H_PRO_BEGIN] ||
+      !std::equal(A + A[H_PRO_BEGIN], A + A[H_PRO_END], B + B[H_PRO_BEGIN]))
+    return fail(DVM_ERR_UNSUPPORTED, "branch bodies stage different operands");
+  if (n_args + 1 > (uint32_t)MAX_ARGS) return fail(DVM_ERR_RESOURCE, "too many operands");
+  const uint32_t then_n = A[H_BODY_END] - A[H_BODY_BEGIN], else_n = B[H_BODY_END] - B[H_BODY_BEGIN];
+  const uint32_t base = ARG_BASE + (n_args + 1) * ARG_WORDS;
+  if (base + pro_n + then_n + else_n + PAD_WORDS > (uint32_t)MAX_WORDS) return fail(DVM_ERR_RESOURCE, "program too large");
+  dvm_program* q = new (std::nothrow) dvm_program();
+  if (!q) return fail(DVM_ERR_INTERNAL, "out of host memory");
+  uint32_t* W = q->prog.w;
+  std::copy(A, A + ARG_BASE + n_args * ARG_WORDS, W);
+  uint32_t* c = W + ARG_BASE + n_args * ARG_WORDS;
+  const uint64_t cp = (uint64_t)(uintptr_t)cond.data;
+  c[A_PTR_LO] = (uint32_t)cp;
+  c[A_PTR_HI] = (uint32_t)(cp >> 32);
+  c[A_DTYPE] = DT_F32;
+  c[A_FLAGS] = arg_flags_word(0, 4);
+  c[A_EXTENT] = 4;
+  std::copy(A + A[H_PRO_BEGIN], A + A[H_PRO_END], W + base);
+  std::copy(A + A[H_BODY_BEGIN], A + A[H_BODY_END], W + base + pro_n);
+  std::copy(B + B[H_BODY_BEGIN], B + B[H_BODY_END], W + base + pro_n + then_n);
+  W[H_NARGS] = n_args + 1;
+  W[H_PRO_BEGIN] = base;
+  W[H_PRO_END] = W[H_BODY_BEGIN] = base + pro_n;
+  W[H_BODY_END] = W[H_ALT_BEGIN] = base + pro_n + then_n;
+  W[H_ALT_END] = base + pro_n + then_n + else_n;
+  W[H_FLAGS] |= HF_BRANCH;
+  W[H_COND_ARG] = n_args;
+  std::memcpy(&W[H_COND_THR], &thr, 4);
+  W[H_N_INSTR] = (pro_n + then_n + else_n) / 2;
+  q->n_words = W[H_ALT_END];
+  q->n_instr = W[H_N_INSTR];
+  q->R = pt->R;
+  q->C = pt->C;
+  q->pad = pt->pad;
+  q->grid_launch = pt->grid_launch;
+  q->bytes = std::max(pt->bytes, pe->bytes) + 4;
+  *out = q;
   return DVM_OK;
 }
 
@@ -2219,6 +2294,7 @@ dvm_status dvm_graph_input(dvm_graph* g, const dvm_tensor* t, dvm_value* out) {
 dvm_status dvm_graph_begin_group(dvm_graph* g) {
   if (!g) return fail(DVM_ERR_INVALID_ARG, "null graph");
   if (g->in_group) return fail(DVM_ERR_INVALID_ARG, "group already open");
+  if (g->branch) return fail(DVM_ERR_INVALID_ARG, "groups cannot open inside a branch");
   g->in_group = true;
   return DVM_OK;
 }
@@ -2296,6 +2372,11 @@ dvm_status dvm_graph_add_op(dvm_graph* g, int32_t op, const dvm_value* in, int32
   r.out = slot;
   *out_value = handle(g, slot);
   for (int k = 0; k < n_in; ++k) g->vals[r.in[k]].uses++;
+  if (g->branch) {
+    g->br[g->branch - 1].push_back(r);
+    g->stats.ops++;
+    return DVM_OK;
+  }
   g->grp.push_back(r);
   if (!g->in_group) {
     int32_t fl;
@@ -2316,6 +2397,7 @@ dvm_status dvm_graph_release(dvm_graph* g, dvm_value h) {
 
 dvm_status dvm_flush(dvm_graph* g, dvm_program** out) {
   if (!g || !out) return fail(DVM_ERR_INVALID_ARG, "null argument");
+  if (g->branch) return fail(DVM_ERR_INVALID_ARG, "branch still open");
   if (!g->buf.empty()) {
     g->stats.flush_reason[FR_EXPLICIT]++;
     g->flush_log.push_back({(int32_t)g->buf.size(), (int32_t)FR_EXPLICIT, 0.f, 0});
@@ -2378,15 +2460,104 @@ dvm_status dvm_launch_profiled(dvm_context* ctx, const dvm_program* p, void* str
   return DVM_OK;
 }
 
+dvm_status dvm_graph_begin_branch(dvm_graph* g, dvm_value cond, float threshold) {
+  if (!g) return fail(DVM_ERR_INVALID_ARG, "null graph");
+  FuseTimer ft(g);
+  if (g->in_group || g->branch) return fail(DVM_ERR_INVALID_ARG, "a group or a branch is open");
+  int64_t cs;
+  if (!resolve(g, cond, &cs)) return fail(DVM_ERR_INVALID_ARG, "unknown condition value");
+  {
+    const Val& v = g->vals[cs];
+    if (v.t.dtype != DVM_F32 || v.shape.numel() != 1)
+      return fail(DVM_ERR_INVALID_ARG, "the condition is one fp32 value");
+  }
+  // a branch is a fusion boundary: the buffered graph (which may compute the
+  // condition) runs first
+  dvm_status st = flush_launch(g, FR_BRANCH, nullptr);
+  if (st != DVM_OK) return st;
+  const Val& v = g->vals[cs];
+  if (v.lost || v.released || !v.t.data) return fail(DVM_ERR_INVALID_ARG, "the condition has no stored value");
+  g->vals[cs].uses++;
+  g->branch = 1;
+  g->branch_cond = cs;
+  g->branch_thr = threshold;
+  return DVM_OK;
+}
+
+dvm_status dvm_graph_else_branch(dvm_graph* g) {
+  if (!g) return fail(DVM_ERR_INVALID_ARG, "null graph");
+  if (g->branch != 1) return fail(DVM_ERR_INVALID_ARG, "no then-branch open");
+  g->branch = 2;
+  return DVM_OK;
+}
+
+dvm_status dvm_graph_end_branch(dvm_graph* g, int32_t* launched) {
+  if (launched) *launched = 0;
+  if (!g) return fail(DVM_ERR_INVALID_ARG, "null graph");
+  if (!g->branch) return fail(DVM_ERR_INVALID_ARG, "no branch open");
+  FuseTimer ft(g);
+  std::vector<OpRec> bt, be;
+  bt.swap(g->br[0]);
+  be.swap(g->br[1]);
+  const int64_t cs = g->branch_cond;
+  const float thr = g->branch_thr;
+  g->branch = 0;
+  g->branch_cond = -1;
+  dvm_status st = DVM_OK;
+  if (bt.empty() || be.empty()) st = fail(DVM_ERR_UNSUPPORTED, "both branch bodies must hold ops");
+  for (const std::vector<OpRec>* list : {&bt, &be}) {
+    if (st != DVM_OK) break;
+    LocalView L;
+    make_local(g, *list, &L);
+    Checker ck(&L.lg, L.ops);
+    if (ck.check(0) >= 0) st = fail(DVM_ERR_UNSUPPORTED, "a branch body is not one fusible graph");
+  }
+  g->stats.flush_reason[FR_BRANCH]++;
+  g->flush_log.push_back({(int32_t)(bt.size() + be.size()), (int32_t)FR_BRANCH, 0.f, 0});
+  const auto t0 = std::chrono::steady_clock::now();
+  dvm_program *pt = nullptr, *pe = nullptr, *pb = nullptr;
+  if (st == DVM_OK) st = encode_list(g, bt, false, &pt);
+  if (st == DVM_OK) st = encode_list(g, be, false, &pe);
+  if (st == DVM_OK && (!pt || !pe)) st = fail(DVM_ERR_UNSUPPORTED, "both branch bodies must store a result");
+  if (st == DVM_OK) st = merge_branch(pt, pe, g->vals[cs].t, thr, &pb);
+  delete pt;
+  delete pe;
+  retire(g, bt, st == DVM_OK);
+  retire(g, be, st == DVM_OK);
+  g->vals[cs].uses--;
+  maybe_recycle(g, cs);
+  note_encode(g, t0, pb);
+  if (st != DVM_OK) return st;
+  if (g->ctx->device < 0) {
+    if (g->held.size() >= MAX_HELD) {
+      delete g->held.front();
+      g->held.pop_front();
+    }
+    g->held.push_back(pb);
+    return DVM_OK;
+  }
+  const auto t1 = std::chrono::steady_clock::now();
+  st = launch(g->ctx, pb, g->stream);
+  g->stats.launch_us_total += std::chrono::duration<double, std::micro>(std::chrono::steady_clock::now() - t1).count();
+  if (st == DVM_OK) {
+    g->stats.launches++;
+    if (launched) *launched = 1;
+  }
+  delete pb;
+  return st;
+}
+
 dvm_status dvm_graph_flush_launch(dvm_graph* g, int32_t* launched) {
   if (!g) return fail(DVM_ERR_INVALID_ARG, "null graph");
   if (g->in_group) return fail(DVM_ERR_INVALID_ARG, "group still open");
+  if (g->branch) return fail(DVM_ERR_INVALID_ARG, "branch still open");
   return flush_launch(g, FR_EXPLICIT, launched);
 }
 
 dvm_status dvm_sync(dvm_graph* g) {
   if (!g) return fail(DVM_ERR_INVALID_ARG, "null graph");
   if (g->in_group) return fail(DVM_ERR_INVALID_ARG, "group still open");
+  if (g->branch) return fail(DVM_ERR_INVALID_ARG, "branch still open");
   dvm_status st = flush_launch(g, FR_SYNC, nullptr);
   if (st != DVM_OK) return st;
   if (g->ctx->device >= 0) {

@@ -1001,6 +1001,20 @@ __device__ __forceinline__ void vm_main(float (*s_red)[T_LANES / 64], int& s_las
   S.t_step = t_step;
   S.t_end = t_end;
 
+  // The body every tile runs.  A branch program reads its condition (a 0-d
+  // fp32 operand written by an earlier launch on the stream) once, with a
+  // wave-uniform load, and runs its else-body unless condition > threshold.
+  uint32_t body_begin = W[H_BODY_BEGIN], body_end = W[H_BODY_END];
+  if (W[H_FLAGS] & HF_BRANCH) {
+    const ArgD c = read_arg(W, W[H_COND_ARG]);
+    const Rsrc rc = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(c.p), 0, 4, RSRC_W3);
+    const float v = __uint_as_float(__builtin_amdgcn_readfirstlane(__builtin_amdgcn_raw_buffer_load_b32(rc, 0, 0, 0)));
+    if (!(v > __uint_as_float(W[H_COND_THR]))) {
+      body_begin = W[H_ALT_BEGIN];
+      body_end = W[H_ALT_END];
+    }
+  }
+
   Tile tl;
   uint32_t tile = t_begin;
   uint32_t pc = W[H_PRO_BEGIN], pc_end = W[H_PRO_END];
@@ -1025,8 +1039,8 @@ __device__ __forceinline__ void vm_main(float (*s_red)[T_LANES / 64], int& s_las
       else tile += t_step;
       if (tile >= t_end) break;
       tl = make_tile(G, tile);
-      pc = W[H_BODY_BEGIN];
-      pc_end = W[H_BODY_END];
+      pc = body_begin;
+      pc_end = body_end;
       fetch2(W, pc, nw0, nw1);
       if constexpr (PROF) p_tile += __builtin_amdgcn_s_memtime() - p_top;
       continue;

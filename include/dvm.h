@@ -113,7 +113,8 @@ typedef struct {
   uint64_t ops;               /* ops accepted */
   uint64_t groups;
   uint64_t unsupported;       /* groups rejected (caller ran them elsewhere) */
-  uint64_t flush_reason[8];   /* 0 explicit, 1 sync, 2 reduce_all, 3 shape, 4 pattern, 5 dependence, 6 resource */
+  uint64_t flush_reason[8];   /* 0 explicit, 1 sync, 2 reduce_all, 3 shape, 4 pattern, 5 dependence, 6 resource,
+                                 7 branch (a begin_branch flush or an encoded branch program) */
   double encode_us_total;     /* host time of encoding (tiling + bytecode), all graphs */
   double encode_us_max;
   uint64_t bytes;             /* physical bytes of the encoded graphs (dvm_header.bytes summed) */
@@ -241,6 +242,25 @@ dvm_status dvm_launch_noalloc(dvm_context* ctx, const dvm_program* p, void* stre
 #define DVM_PROF_COUNTERS 5
 dvm_status dvm_launch_profiled(dvm_context* ctx, const dvm_program* p, void* stream, uint64_t* counters,
                                size_t n_counters);
+
+/* Device-side control flow (the if-else of the DVM review page's dynamic
+ * control-flow workload, section 6.2; the MindSpore summary page, section 3.2,
+ * flushes at such points): ops added between begin_branch and else_branch
+ * form the then-body, ops between else_branch and end_branch the else-body.
+ * begin_branch flushes the buffered graph first (the condition may be its
+ * result); cond is one fp32 value with storage.  end_branch encodes one branch
+ * program holding both bodies and launches it on the graph's stream
+ * (*launched = 1); the VM reads cond when the program runs and every tile runs
+ * the then-body iff cond > threshold (strictly: a NaN or equal value runs the
+ * else-body), so no value travels to the host.  Each body must be one fusible
+ * graph, and the two must share one tiling, operand table and staging (the
+ * same operands in the same order, as in out = x + y versus out = x - y);
+ * otherwise DVM_ERR_UNSUPPORTED and the values of both bodies are lost.
+ * Groups cannot open inside a branch; flush, flush_launch and sync refuse
+ * while a branch is open. */
+dvm_status dvm_graph_begin_branch(dvm_graph* g, dvm_value cond, float threshold);
+dvm_status dvm_graph_else_branch(dvm_graph* g);
+dvm_status dvm_graph_end_branch(dvm_graph* g, int32_t* launched);
 
 /* dvm_flush + dvm_launch on the graph's stream (an explicit flush, MindSpore
  * summary page, section 3.2; no-op when nothing is encoded; *launched = 0

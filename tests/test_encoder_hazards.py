@@ -106,7 +106,7 @@ def test_reduce_all_program_has_no_scratch_address(ectx):
     """The reduce-all closes its graph; the encode-only context holds the
     program.  Its scratch operand has no address: each launch supplies its
     stream's own area, so programs on different streams never share it."""
-    ARG_BASE, ARG_WORDS, H_ALL_SCRATCH = 40, 8, 24
+    ARG_BASE, ARG_WORDS, H_ALL_SCRATCH = 44, 8, 24
     g = dvm.Graph(ectx)
     x = g.input(TD(1 << 30, "f32", (16384, 4096)))
     g.op("reduce_sum", x, out=TD(2 << 30, "f32", ()), live=True, axis=L.AXIS_ALL)
