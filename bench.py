@@ -54,6 +54,8 @@ def parse():
     ap.add_argument("--calls", type=int, default=0, help="calls per step for ifelse / matmul (0: default)")
     ap.add_argument("--motifs", type=int, default=10000, help="motifs per step for the op stream")
     ap.add_argument("--stream-steps", type=int, default=2, help="timed op-stream steps (seeds 0, 1, ...)")
+    ap.add_argument("--stacking", type=int, default=7,
+                    help="independent graphs packed into one launch (1: every graph launches alone)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=6.0, help="CPU work per baseline leg")
     ap.add_argument("--no-decode-split", action="store_true")
@@ -344,9 +346,9 @@ def layernorm_bench(args):
     xs = [W.device_normal((r, H), seed=1000 + i, dtype="bf16") for i, (r, _) in enumerate(shapes)]
     gam = W.device_normal((H,), seed=1, mu=1.0, sd=0.1)
     bet = W.device_normal((H,), seed=2, mu=0.0, sd=0.1)
-    rmax = max(r for r, _ in shapes)
-    ybuf = torch.empty((rmax, H), dtype=torch.bfloat16, device="cuda")
-    ys = [ybuf[:r] for r, _ in shapes]
+    # every call writes its own output (independent calls, as in a model's
+    # layers), so the stream's graphs may share launches
+    ys = [torch.empty((r, H), dtype=torch.bfloat16, device="cuda") for r, _ in shapes]
     call_bytes = [r * H * 2 * 2 + 2 * H * 4 for r, _ in shapes]
     step_bytes = float(sum(call_bytes))
     torch.cuda.synchronize()
@@ -357,6 +359,7 @@ def layernorm_bench(args):
         g.flush_launch()
 
     g = dvm.Graph(ctx, stream)
+    g.set_stacking(args.stacking)
     for _ in range(args.warmup):
         one_step(g)
     torch.cuda.synchronize()
@@ -375,7 +378,7 @@ def layernorm_bench(args):
     e2e_gbs = step_bytes * args.steps / (t1 - t0) / 1e9
     launches = s1["launches"] - s0["launches"]
     avg_launch_s = dev_ms * 1e-3 / max(launches, 1)
-    kern_gbs = step_bytes / len(shapes) / avg_launch_s / 1e9
+    kern_gbs = step_bytes * args.steps / (dev_ms * 1e-3) / 1e9      # = bytes per launch / launch time
     fuse_us = (s1["fuse_us_total"] - s0["fuse_us_total"]) / max(s1["ops"] - s0["ops"], 1)
 
     progs = []
@@ -403,14 +406,16 @@ def layernorm_bench(args):
         "graphs_per_step": (s1["graphs"] - s0["graphs"]) / args.steps,
         "roofline": {"bound": "hbm", "achieved": round(kern_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(kern_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "kernel": "dvm_vm_vector_wide + dvm_vm_vector", "launches_per_step": len(shapes),
+                     "kernel": "dvm_vm_vector_wide + dvm_vm_vector", "launches_per_step": launches / args.steps,
+                     "graphs_stacked_per_step": (s1["stacked"] - s0["stacked"]) / args.steps,
+                     "stacking": args.stacking,
                      "launches_by_kernel": {
                          "dvm_vm_vector_wide": sum(1 for p in progs if p.header()["kernel_type"] == 2),
                          "dvm_vm_vector": sum(1 for p in progs if p.header()["kernel_type"] == 0)},
                      "avg_launch_us": round(avg_launch_s * 1e6, 3),
                      "timing": "HIP events on the launch stream around the timed steps; avg launch = device span / "
                                "launches (gaps between back-to-back launches included)",
-                     "bytes_per_launch_avg": round(step_bytes / len(shapes), 1)},
+                     "bytes_per_launch_avg": round(step_bytes * args.steps / max(launches, 1), 1)},
         "largest_call_header": {k: hdr[k] for k in ("block_dim", "body_tile", "grid", "tr", "tc", "g", "nv",
                                                     "n_instr")},
         "decode_split": decode,
@@ -687,6 +692,7 @@ def stream_bench(args):
     bf = dict(dtype="bf16")
     w = W.device_normal((H,), seed=25, mu=1.0, sd=0.1)
     g = dvm.Graph(ctx, stream)
+    g.set_stacking(args.stacking)
 
     def run_step(seed):
         T, TKV, motifs = W.stream_step(seed, args.motifs)
@@ -724,6 +730,7 @@ def stream_bench(args):
         return {"T": T, "T_kv": TKV, "dt": dt, "phys": s1["bytes"] - s0["bytes"],
                 "motif_bytes": float(sum(mb[k] for k, _ in motifs)), "graphs": s1["graphs"] - s0["graphs"],
                 "launches": s1["launches"] - s0["launches"], "ops": s1["ops"] - s0["ops"],
+                "stacked": s1["stacked"] - s0["stacked"],
                 "fuse_us": s1["fuse_us_total"] - s0["fuse_us_total"],
                 "reasons": {k: s1["flush_reason"][k] - s0["flush_reason"][k] for k in s1["flush_reason"]},
                 "log": log, "n_motifs": len(motifs)}
@@ -748,6 +755,7 @@ def stream_bench(args):
             "effective_gbs": round(eff / dt / 1e9, 2),
             "graphs_per_step": sum(r["graphs"] for r in runs) / n,
             "launches_per_step": sum(r["launches"] for r in runs) / n,
+            "graphs_stacked_per_step": sum(r["stacked"] for r in runs) / n, "stacking": args.stacking,
             "ops_per_step": sum(r["ops"] for r in runs) / n,
             "flush_reasons_per_step": {k: sum(r["reasons"][k] for r in runs) / n for k in runs[0]["reasons"]},
             "encode_us": encode_stats(log),
@@ -762,7 +770,7 @@ def brief(res):
     """The fields of a workload's line that the combined line carries."""
     keep = ("value", "unit", "ms_per_step", "steps", "config", "encode_us", "roofline", "device_only_gbs",
             "device_only_tflops", "kernel_us_warm", "kernel_us_cold", "device_only_gbs_cold", "effective_gbs",
-            "graphs_per_step", "launches_per_step", "ops_per_step", "flush_reasons_per_step", "fuse_us_per_op",
+            "graphs_per_step", "launches_per_step", "graphs_stacked_per_step", "stacking", "ops_per_step", "flush_reasons_per_step", "fuse_us_per_op",
             "context", "note", "e2e_host_branch_gbs", "cpu_baseline")
     return {k: res[k] for k in keep if k in res}
 

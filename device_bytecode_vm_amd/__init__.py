@@ -14,7 +14,7 @@ from dataclasses import dataclass
 from . import _lib as L
 from ._lib import DvmError, check, lib
 
-__all__ = ["Context", "Graph", "Program", "Value", "TensorDesc", "DvmError", "lib"]
+__all__ = ["Context", "Graph", "Program", "Value", "TensorDesc", "DvmError", "lib", "stack_programs"]
 
 
 @dataclass
@@ -160,6 +160,17 @@ class Program:
             pass
 
 
+def stack_programs(programs) -> "Program":
+    """dvm_program_stack: one launch of 2..7 independent VECTOR programs."""
+    arr = (C.c_void_p * len(programs))(*[p.h.value if isinstance(p.h, C.c_void_p) else p.h for p in programs])
+    q = C.c_void_p()
+    check(lib.dvm_program_stack(arr, len(programs), C.byref(q)))
+    prog = Program(q, programs[0].ctx)
+    for p in programs:
+        prog._keep.extend(p._keep)
+    return prog
+
+
 def _stream_handle(stream):
     if stream is None:
         try:
@@ -280,6 +291,11 @@ class Graph:
         prog._keep = keep
         return prog
 
+    def set_stacking(self, max_segments: int):
+        """Pack up to max_segments independent encoded graphs into one launch
+        (1: launch every graph when it is flushed)."""
+        check(lib.dvm_graph_set_stacking(self.h, int(max_segments)))
+
     # -- device-side control flow -----------------------------------------
     def begin_branch(self, cond: "Value", threshold: float = 0.0):
         """Ops until else_branch() form the then-body, run iff cond > threshold
@@ -337,5 +353,5 @@ class Graph:
             "unsupported": s.unsupported,
             "flush_reason": {L.FLUSH_REASONS[i]: s.flush_reason[i] for i in range(8)},
             "encode_us_total": s.encode_us_total, "encode_us_max": s.encode_us_max, "bytes": s.bytes,
-            "fuse_us_total": s.fuse_us_total, "launch_us_total": s.launch_us_total,
+            "fuse_us_total": s.fuse_us_total, "launch_us_total": s.launch_us_total, "stacked": s.stacked,
         }

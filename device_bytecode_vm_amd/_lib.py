@@ -60,14 +60,14 @@ class DvmHeader(C.Structure):
                 ("body_tile", C.c_uint32), ("grid", C.c_uint32), ("tr", C.c_uint32), ("tc", C.c_uint32),
                 ("g", C.c_uint32), ("nv", C.c_uint32), ("p", C.c_uint32), ("R", C.c_int64), ("C", C.c_int64),
                 ("n_instr", C.c_uint32), ("n_args", C.c_uint32), ("pad", C.c_uint32), ("n_words", C.c_uint32),
-                ("bytes", C.c_uint64)]
+                ("bytes", C.c_uint64), ("segments", C.c_uint32)]
 
 
 class DvmStats(C.Structure):
     _fields_ = [("graphs", C.c_uint64), ("launches", C.c_uint64), ("ops", C.c_uint64), ("groups", C.c_uint64),
                 ("unsupported", C.c_uint64), ("flush_reason", C.c_uint64 * 8),
                 ("encode_us_total", C.c_double), ("encode_us_max", C.c_double), ("bytes", C.c_uint64),
-                ("fuse_us_total", C.c_double), ("launch_us_total", C.c_double)]
+                ("fuse_us_total", C.c_double), ("launch_us_total", C.c_double), ("stacked", C.c_uint64)]
 
 
 VP = C.c_void_p
@@ -90,6 +90,8 @@ _sigs = {
     "dvm_launch_noalloc": (C.c_int, [VP, VP, VP]),
     "dvm_launch_profiled": (C.c_int, [VP, VP, VP, VP, C.c_size_t]),
     "dvm_graph_flush_launch": (C.c_int, [VP, P(C.c_int32)]),
+    "dvm_graph_set_stacking": (C.c_int, [VP, C.c_int32]),
+    "dvm_program_stack": (C.c_int, [P(VP), C.c_size_t, P(VP)]),
     "dvm_graph_begin_branch": (C.c_int, [VP, C.c_int64, C.c_float]),
     "dvm_graph_else_branch": (C.c_int, [VP]),
     "dvm_graph_end_branch": (C.c_int, [VP, P(C.c_int32)]),

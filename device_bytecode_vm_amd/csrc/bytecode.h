@@ -283,6 +283,23 @@ __host__ __device__ constexpr uint32_t vmc_load(uint32_t w) { return ((w >> 12) 
 __host__ __device__ constexpr uint32_t vmc_bin(uint32_t w) { return ((w >> 8) & 0xfu) | (((w >> 12) & 0xfu) << 4); }
 constexpr uint32_t VMC_MAX = 63;
 
+// Stacked launches (the stacking-based fusion of the DVM review page, section
+// 5.1: independent graphs packed into one launch, each on its own
+// workgroups).  The kernel argument then starts with a directory instead of a
+// header: word 0 STACK_MAGIC, word 1 the number of segments, then per segment
+// s the word offset of its program (a complete program: header, operand
+// table, prologue, body, whose word indices are relative to its own start) and
+// the first workgroup that runs it.  Workgroup b belongs to the segment with
+// the largest first workgroup <= b and runs that program as workgroup b -
+// first of a grid that ends where the next segment starts.  Segment offsets
+// are even (instructions are fetched as 8-byte pairs) and each segment is
+// followed by PAD_WORDS spare words.
+constexpr uint32_t STACK_MAGIC = 0x4b545344u;  // "DSTK"
+constexpr int S_NSEG = 1;
+constexpr int S_DIR = 2;                        // (offset, first workgroup) pairs from here
+constexpr int MAX_SEGS = 7;
+constexpr int STACK_DIR_WORDS = S_DIR + 2 * MAX_SEGS;
+
 struct Program {
   uint32_t w[MAX_WORDS];
 };

@@ -25,10 +25,10 @@
 
 using namespace dvmbc;
 
-extern "C" hipError_t dvm_launch_vector_kernel(const Program* p, unsigned grid, hipStream_t s);
+extern "C" hipError_t dvm_launch_vector_kernel(const Program* p, unsigned grid, unsigned lds, hipStream_t s);
 extern "C" hipError_t dvm_launch_mix_kernel(const Program* p, unsigned grid, hipStream_t s);
 extern "C" hipError_t dvm_launch_vector_prof_kernel(const Program* p, unsigned grid, hipStream_t s);
-extern "C" hipError_t dvm_launch_vector_kernel_wide(const Program* p, unsigned grid, hipStream_t s);
+extern "C" hipError_t dvm_launch_vector_kernel_wide(const Program* p, unsigned grid, unsigned lds, hipStream_t s);
 extern "C" hipError_t dvm_launch_vector_prof_kernel_wide(const Program* p, unsigned grid, hipStream_t s);
 extern "C" hipError_t dvm_static_scratch_init(int device, void** ptr, size_t* bytes);
 extern "C" hipError_t dvm_static_scratch_clear(void* area, hipStream_t s);
@@ -429,6 +429,8 @@ struct dvm_context {
   hipError_t static_err = hipSuccess;
 };
 
+using Range = std::pair<uintptr_t, uint64_t>;  // (address, bytes spanned)
+
 struct dvm_program {
   Program prog;
   uint64_t bytes = 0;         // physical bytes: every operand read once, every stored output written once
@@ -437,6 +439,9 @@ struct dvm_program {
   int64_t R = 0, C = 0;
   uint32_t pad = 0;
   uint32_t grid_launch = 0;   // workgroups actually launched (reduce-all always launches >= 1)
+  uint32_t segments = 1;      // > 1: a stacked program (a directory, then the segments)
+  uint32_t lds = 0;           // dynamic LDS of the launch (bytes)
+  std::vector<Range> reads, writes;  // memory the program reads and writes (stacking independence)
 };
 
 struct dvm_graph {
@@ -458,6 +463,9 @@ struct dvm_graph {
   // here for dvm_graph_take_program (oldest first, at most MAX_HELD)
   std::deque<dvm_program*> held;
   std::vector<int32_t> remap;  // slot -> local index while a local view is built (-1 otherwise)
+  // stacking: up to stack_max independent programs wait here and launch as one
+  int stack_max = 1;
+  std::vector<dvm_program*> stack;
   // a branch being captured: 1 then-ops, 2 else-ops (0 none)
   int branch = 0;
   int64_t branch_cond = -1;
@@ -469,6 +477,7 @@ constexpr size_t MAX_HELD = 4096;
 
 dvm_graph::~dvm_graph() {
   for (dvm_program* p : held) delete p;
+  for (dvm_program* p : stack) delete p;
 }
 
 namespace {
@@ -916,6 +925,10 @@ struct Encoder {
     uint64_t b = 0;
     for (int64_t s : slots) b += (uint64_t)numel_of(g->vals[s].t) * (uint64_t)esize(g->vals[s].t.dtype);
     return b;
+  }
+
+  Range range_of(int64_t s) const {
+    return {(uintptr_t)g->vals[s].t.data, (uint64_t)extent_bytes(g->vals[s].t)};
   }
 
   // Every external operand the program reads must have storage: a value with
@@ -1575,6 +1588,9 @@ struct Encoder {
     n_args = 2;
     for (size_t q = 0; q < operands.size(); ++q) add_arg(operands[q], st[q].first, st[q].second);
     prog->bytes = tensor_bytes(operands) + tensor_bytes({mm.in[0], mm.in[1]});
+    prog->reads = {range_of(mm.in[0]), range_of(mm.in[1])};
+    for (int64_t q : ck.ext_operands()) prog->reads.push_back(range_of(q));
+    for (int64_t q : stored) prog->writes.push_back(range_of(q));
     cls.clear();
     ck.classes(&cls);
     cls[mm.out] = 1;
@@ -1626,6 +1642,7 @@ struct Encoder {
     prog->C = N;
     prog->pad = 0;
     prog->grid_launch = (uint32_t)plan.grid;
+    prog->lds = W[H_LDS_BYTES];
     return DVM_OK;
   }
 
@@ -1685,6 +1702,8 @@ struct Encoder {
     for (size_t q = 0; q < operands.size(); ++q) add_arg(operands[q], st[q].first, st[q].second);
     prog->bytes = tensor_bytes(operands);
     if (tm == TM_ALLREDUCE) prog->bytes += (uint64_t)esize(g->vals[ops.back().out].t.dtype);
+    for (size_t q = 0; q < operands.size(); ++q) (q < n_ext ? prog->reads : prog->writes).push_back(range_of(operands[q]));
+    if (tm == TM_ALLREDUCE) prog->writes.push_back(range_of(ops.back().out));
     cls.clear();
     ck.classes(&cls);
     {
@@ -1785,6 +1804,7 @@ struct Encoder {
     prog->pad = (uint32_t)plan.pad;
     prog->grid_launch = (uint32_t)plan.grid;
     if (tm == TM_ALLREDUCE && prog->grid_launch == 0) prog->grid_launch = 1;
+    prog->lds = W[H_LDS_BYTES];
     return DVM_OK;
   }
 };
@@ -2007,6 +2027,12 @@ dvm_status merge_branch(const dvm_program* pt, const dvm_program* pe, const dvm_
   q->pad = pt->pad;
   q->grid_launch = pt->grid_launch;
   q->bytes = std::max(pt->bytes, pe->bytes) + 4;
+  q->lds = pt->lds;
+  q->reads = pt->reads;
+  q->reads.insert(q->reads.end(), pe->reads.begin(), pe->reads.end());
+  q->reads.push_back({(uintptr_t)cond.data, 4});
+  q->writes = pt->writes;
+  q->writes.insert(q->writes.end(), pe->writes.begin(), pe->writes.end());
   *out = q;
   return DVM_OK;
 }
@@ -2034,7 +2060,7 @@ dvm_status stream_scratch(dvm_context* ctx, hipStream_t s, void** out) {
 }
 
 bool needs_scratch(const dvm_program* p) {
-  return p->prog.w[H_KTYPE] != KT_MIX && p->prog.w[H_TEMPLATE] == TM_ALLREDUCE;
+  return p->segments == 1 && p->prog.w[H_KTYPE] != KT_MIX && p->prog.w[H_TEMPLATE] == TM_ALLREDUCE;
 }
 
 // Points the program's reduce-all scratch operand at `area` of `bytes`.
@@ -2047,11 +2073,20 @@ void set_scratch(Program* q, void* area, uint64_t bytes) {
   b[A_EXTENT] = (uint32_t)bytes;
 }
 
-hipError_t launch_kernel(const Program* q, uint32_t grid, hipStream_t s) {
-  const uint32_t kt = q->w[H_KTYPE];
+hipError_t launch_words(const Program* q, uint32_t kt, uint32_t grid, uint32_t lds, hipStream_t s) {
   return kt == KT_MIX           ? dvm_launch_mix_kernel(q, grid, s)
-         : kt == KT_VECTOR_WIDE ? dvm_launch_vector_kernel_wide(q, grid, s)
-                                : dvm_launch_vector_kernel(q, grid, s);
+         : kt == KT_VECTOR_WIDE ? dvm_launch_vector_kernel_wide(q, grid, lds, s)
+                                : dvm_launch_vector_kernel(q, grid, lds, s);
+}
+
+// Kernel type of a program (a stacked program: that of its segments).
+uint32_t ktype_of(const dvm_program* p) {
+  const uint32_t* W = p->prog.w;
+  return p->segments > 1 ? W[W[S_DIR] + H_KTYPE] : W[H_KTYPE];
+}
+
+hipError_t launch_kernel(const dvm_program* p, const Program* q, hipStream_t s) {
+  return launch_words(q, ktype_of(p), p->grid_launch, p->lds, s);
 }
 
 dvm_status launch(dvm_context* ctx, const dvm_program* p, hipStream_t s) {
@@ -2064,12 +2099,149 @@ dvm_status launch(dvm_context* ctx, const dvm_program* p, hipStream_t s) {
     if (st != DVM_OK) return st;
     Program q = p->prog;  // the launch copies its argument: a stack copy is enough
     set_scratch(&q, area, SCRATCH_BYTES);
-    e = launch_kernel(&q, p->grid_launch, s);
+    e = launch_kernel(p, &q, s);
   } else {
-    e = launch_kernel(&p->prog, p->grid_launch, s);
+    e = launch_kernel(p, &p->prog, s);
   }
   if (e != hipSuccess) return fail(DVM_ERR_DEVICE, "launch failed: %s", hipGetErrorString(e));
   return DVM_OK;
+}
+
+// Runs a program: launches it on the graph's stream, or, in an encode-only
+// context, holds it for dvm_graph_take_program.  Takes ownership of p.
+dvm_status run_program(dvm_graph* g, dvm_program* p, int32_t* launched) {
+  if (g->ctx->device < 0) {
+    if (g->held.size() >= MAX_HELD) {
+      delete g->held.front();
+      g->held.pop_front();
+    }
+    g->held.push_back(p);
+    return DVM_OK;
+  }
+  const auto t0 = std::chrono::steady_clock::now();
+  const dvm_status st = launch(g->ctx, p, g->stream);
+  g->stats.launch_us_total += std::chrono::duration<double, std::micro>(std::chrono::steady_clock::now() - t0).count();
+  if (st == DVM_OK) {
+    g->stats.launches++;
+    if (launched) *launched = 1;
+  }
+  delete p;
+  return st;
+}
+
+// Stacking (DVM review page, section 5.1, stacking-based fusion): a program
+// may join the graph's stack if it runs on the same VM build as the stack,
+// is no reduce-all or branch program (those need the stream's scratch or a
+// condition written before them), fits the kernel argument beside the stack,
+// and is independent of every stacked program: it writes nothing they read
+// or write, and reads nothing they write.  Stacked programs run side by side
+// on disjoint workgroups, in one launch.
+bool stackable(const dvm_program* p) {
+  const uint32_t* W = p->prog.w;
+  return p->segments == 1 && p->grid_launch > 0 && (W[H_KTYPE] == KT_VECTOR || W[H_KTYPE] == KT_VECTOR_WIDE) &&
+         W[H_TEMPLATE] != TM_ALLREDUCE && !(W[H_FLAGS] & HF_BRANCH);
+}
+
+bool overlaps(const std::vector<Range>& a, const std::vector<Range>& b) {
+  for (const Range& x : a)
+    for (const Range& y : b)
+      if (x.second && y.second && x.first < y.first + y.second && y.first < x.first + x.second) return true;
+  return false;
+}
+
+uint32_t stack_words(const std::vector<dvm_program*>& ps) {
+  uint32_t n = STACK_DIR_WORDS;
+  for (const dvm_program* p : ps) n += p->n_words + PAD_WORDS;
+  return n;
+}
+
+bool fits_stack(const dvm_graph* g, const dvm_program* p) {
+  const std::vector<dvm_program*>& st = g->stack;
+  if (st.size() >= (size_t)MAX_SEGS || st[0]->prog.w[H_KTYPE] != p->prog.w[H_KTYPE]) return false;
+  if (stack_words(st) + p->n_words + PAD_WORDS > (uint32_t)MAX_WORDS) return false;
+  for (const dvm_program* q : st)
+    if (overlaps(p->writes, q->reads) || overlaps(p->writes, q->writes) || overlaps(p->reads, q->writes)) return false;
+  return true;
+}
+
+// One program from 2..MAX_SEGS programs of one VECTOR build: the directory,
+// then each program's words, with the workgroup ranges in launch order.
+dvm_status build_stack(const dvm_program* const* ps, size_t n, dvm_program** out) {
+  *out = nullptr;
+  if (n < 2 || n > (size_t)MAX_SEGS) return fail(DVM_ERR_INVALID_ARG, "a stack holds 2 to %d programs", MAX_SEGS);
+  const uint32_t kt = ps[0]->prog.w[H_KTYPE];
+  uint32_t words = STACK_DIR_WORDS;
+  for (size_t i = 0; i < n; ++i) {
+    const dvm_program* p = ps[i];
+    if (!p) return fail(DVM_ERR_INVALID_ARG, "null program");
+    if (p->segments != 1 || (kt != KT_VECTOR && kt != KT_VECTOR_WIDE) || p->prog.w[H_KTYPE] != kt)
+      return fail(DVM_ERR_UNSUPPORTED, "stacked programs share one VECTOR build");
+    if (p->prog.w[H_TEMPLATE] == TM_ALLREDUCE) return fail(DVM_ERR_UNSUPPORTED, "reduce-all programs do not stack");
+    words += p->n_words + PAD_WORDS;
+  }
+  if (words > (uint32_t)MAX_WORDS) return fail(DVM_ERR_RESOURCE, "stacked programs exceed %d words", MAX_WORDS);
+  dvm_program* q = new (std::nothrow) dvm_program();
+  if (!q) return fail(DVM_ERR_INTERNAL, "out of host memory");
+  uint32_t* W = q->prog.w;
+  W[0] = STACK_MAGIC;
+  W[S_NSEG] = (uint32_t)n;
+  uint32_t off = STACK_DIR_WORDS, wg = 0;
+  for (size_t i = 0; i < n; ++i) {
+    const dvm_program* p = ps[i];
+    W[S_DIR + 2 * i] = off;
+    W[S_DIR + 2 * i + 1] = wg;
+    std::copy(p->prog.w, p->prog.w + p->n_words, W + off);
+    off += p->n_words + PAD_WORDS;
+    wg += p->grid_launch;
+    q->lds = std::max(q->lds, p->lds);
+    q->bytes += p->bytes;
+    q->n_instr += p->n_instr;
+    q->reads.insert(q->reads.end(), p->reads.begin(), p->reads.end());
+    q->writes.insert(q->writes.end(), p->writes.begin(), p->writes.end());
+  }
+  q->segments = (uint32_t)n;
+  q->n_words = off;
+  q->grid_launch = wg;
+  q->R = ps[0]->R;
+  q->C = ps[0]->C;
+  *out = q;
+  return DVM_OK;
+}
+
+// Launches (or holds) what the graph's stack holds, as one program.
+dvm_status launch_stack(dvm_graph* g, int32_t* launched) {
+  std::vector<dvm_program*> st;
+  st.swap(g->stack);
+  if (st.empty()) return DVM_OK;
+  if (st.size() == 1) return run_program(g, st[0], launched);
+  dvm_program* q = nullptr;
+  dvm_status e = build_stack(st.data(), st.size(), &q);
+  for (dvm_program* p : st) delete p;
+  if (e != DVM_OK) return e;
+  g->stats.stacked += st.size();
+  return run_program(g, q, launched);
+}
+
+// A newly encoded program: joins the stack, or runs after what the stack held.
+dvm_status submit(dvm_graph* g, dvm_program* p, int32_t* launched) {
+  if (g->stack_max > 1 && stackable(p)) {
+    if (!g->stack.empty() && !fits_stack(g, p)) {
+      const dvm_status e = launch_stack(g, launched);
+      if (e != DVM_OK) {
+        delete p;
+        return e;
+      }
+    }
+    g->stack.push_back(p);
+    if (g->stack.size() >= (size_t)g->stack_max) return launch_stack(g, launched);
+    return DVM_OK;
+  }
+  const dvm_status e = launch_stack(g, launched);
+  if (e != DVM_OK) {
+    delete p;
+    return e;
+  }
+  return run_program(g, p, launched);
 }
 
 dvm_status flush_launch(dvm_graph* g, int reason, int32_t* launched) {
@@ -2080,23 +2252,7 @@ dvm_status flush_launch(dvm_graph* g, int reason, int32_t* launched) {
   dvm_program* p = nullptr;
   dvm_status st = encode_buffer(g, &p);
   if (st != DVM_OK || !p) return st;
-  if (g->ctx->device < 0) {
-    if (g->held.size() >= MAX_HELD) {
-      delete g->held.front();
-      g->held.pop_front();
-    }
-    g->held.push_back(p);
-    return DVM_OK;
-  }
-  const auto t0 = std::chrono::steady_clock::now();
-  st = launch(g->ctx, p, g->stream);
-  g->stats.launch_us_total += std::chrono::duration<double, std::micro>(std::chrono::steady_clock::now() - t0).count();
-  if (st == DVM_OK) {
-    g->stats.launches++;
-    if (launched) *launched = 1;
-  }
-  delete p;
-  return st;
+  return submit(g, p, launched);
 }
 
 // Host time of one fuser call (capture and fusion decisions), without the
@@ -2398,6 +2554,10 @@ dvm_status dvm_graph_release(dvm_graph* g, dvm_value h) {
 dvm_status dvm_flush(dvm_graph* g, dvm_program** out) {
   if (!g || !out) return fail(DVM_ERR_INVALID_ARG, "null argument");
   if (g->branch) return fail(DVM_ERR_INVALID_ARG, "branch still open");
+  // what the stack holds runs first, so the returned program, launched on the
+  // graph's stream, runs after it
+  dvm_status sl = launch_stack(g, nullptr);
+  if (sl != DVM_OK) return sl;
   if (!g->buf.empty()) {
     g->stats.flush_reason[FR_EXPLICIT]++;
     g->flush_log.push_back({(int32_t)g->buf.size(), (int32_t)FR_EXPLICIT, 0.f, 0});
@@ -2426,9 +2586,9 @@ dvm_status dvm_launch_noalloc(dvm_context* ctx, const dvm_program* p, void* stre
     Program q = p->prog;
     set_scratch(&q, ctx->static_scratch, ctx->static_bytes);
     e = dvm_static_scratch_clear(ctx->static_scratch, s);
-    if (e == hipSuccess) e = launch_kernel(&q, p->grid_launch, s);
+    if (e == hipSuccess) e = launch_kernel(p, &q, s);
   } else {
-    e = launch_kernel(&p->prog, p->grid_launch, s);
+    e = launch_kernel(p, &p->prog, s);
   }
   if (e != hipSuccess) return fail(DVM_ERR_DEVICE, "launch failed: %s", hipGetErrorString(e));
   return DVM_OK;
@@ -2439,7 +2599,8 @@ dvm_status dvm_launch_profiled(dvm_context* ctx, const dvm_program* p, void* str
   if (!ctx || !p) return fail(DVM_ERR_INVALID_ARG, "null argument");
   if (ctx->device < 0) return fail(DVM_ERR_DEVICE, "encode-only context cannot launch");
   const uint32_t kt = p->prog.w[H_KTYPE];
-  if (kt != KT_VECTOR && kt != KT_VECTOR_WIDE) return fail(DVM_ERR_UNSUPPORTED, "profiling covers VECTOR programs");
+  if (p->segments != 1 || (kt != KT_VECTOR && kt != KT_VECTOR_WIDE))
+    return fail(DVM_ERR_UNSUPPORTED, "profiling covers single VECTOR programs");
   if (p->grid_launch == 0) return DVM_OK;
   if (!counters) return fail(DVM_ERR_INVALID_ARG, "null counter buffer");
   const size_t need = (size_t)DVM_PROF_COUNTERS * p->grid_launch;
@@ -2528,30 +2689,33 @@ dvm_status dvm_graph_end_branch(dvm_graph* g, int32_t* launched) {
   maybe_recycle(g, cs);
   note_encode(g, t0, pb);
   if (st != DVM_OK) return st;
-  if (g->ctx->device < 0) {
-    if (g->held.size() >= MAX_HELD) {
-      delete g->held.front();
-      g->held.pop_front();
-    }
-    g->held.push_back(pb);
-    return DVM_OK;
-  }
-  const auto t1 = std::chrono::steady_clock::now();
-  st = launch(g->ctx, pb, g->stream);
-  g->stats.launch_us_total += std::chrono::duration<double, std::micro>(std::chrono::steady_clock::now() - t1).count();
-  if (st == DVM_OK) {
-    g->stats.launches++;
-    if (launched) *launched = 1;
-  }
-  delete pb;
-  return st;
+  return submit(g, pb, launched);  // after whatever the stack holds
 }
 
 dvm_status dvm_graph_flush_launch(dvm_graph* g, int32_t* launched) {
   if (!g) return fail(DVM_ERR_INVALID_ARG, "null graph");
   if (g->in_group) return fail(DVM_ERR_INVALID_ARG, "group still open");
   if (g->branch) return fail(DVM_ERR_INVALID_ARG, "branch still open");
-  return flush_launch(g, FR_EXPLICIT, launched);
+  if (launched) *launched = 0;
+  int32_t l1 = 0, l2 = 0;
+  dvm_status st = flush_launch(g, FR_EXPLICIT, &l1);
+  if (st == DVM_OK) st = launch_stack(g, &l2);
+  if (launched) *launched = l1 | l2;
+  return st;
+}
+
+dvm_status dvm_graph_set_stacking(dvm_graph* g, int32_t max_segments) {
+  if (!g) return fail(DVM_ERR_INVALID_ARG, "null graph");
+  if (max_segments < 1 || max_segments > MAX_SEGS)
+    return fail(DVM_ERR_INVALID_ARG, "max_segments %d outside 1..%d", max_segments, MAX_SEGS);
+  dvm_status st = launch_stack(g, nullptr);
+  g->stack_max = max_segments;
+  return st;
+}
+
+dvm_status dvm_program_stack(const dvm_program* const* programs, size_t n, dvm_program** out) {
+  if (!programs || !out) return fail(DVM_ERR_INVALID_ARG, "null argument");
+  return build_stack(programs, n, out);
 }
 
 dvm_status dvm_sync(dvm_graph* g) {
@@ -2559,6 +2723,7 @@ dvm_status dvm_sync(dvm_graph* g) {
   if (g->in_group) return fail(DVM_ERR_INVALID_ARG, "group still open");
   if (g->branch) return fail(DVM_ERR_INVALID_ARG, "branch still open");
   dvm_status st = flush_launch(g, FR_SYNC, nullptr);
+  if (st == DVM_OK) st = launch_stack(g, nullptr);
   if (st != DVM_OK) return st;
   if (g->ctx->device >= 0) {
     hipError_t e = hipStreamSynchronize(g->stream);
@@ -2569,7 +2734,8 @@ dvm_status dvm_sync(dvm_graph* g) {
 
 dvm_status dvm_program_header(const dvm_program* p, dvm_header* out) {
   if (!p || !out) return fail(DVM_ERR_INVALID_ARG, "null argument");
-  const uint32_t* W = p->prog.w;
+  // a stacked program reports its first segment's header
+  const uint32_t* W = p->segments > 1 ? p->prog.w + p->prog.w[S_DIR] : p->prog.w;
   out->kernel_type = W[H_KTYPE];
   out->tmpl = W[H_TEMPLATE];
   out->block_dim = W[H_BLOCK_DIM];
@@ -2587,6 +2753,8 @@ dvm_status dvm_program_header(const dvm_program* p, dvm_header* out) {
   out->pad = p->pad;
   out->n_words = p->n_words;
   out->bytes = p->bytes;
+  out->segments = p->segments;
+  if (p->segments > 1) out->grid = p->grid_launch;
   return DVM_OK;
 }
 
@@ -2604,6 +2772,7 @@ dvm_status dvm_program_debug_tilemap(const dvm_program* p, const dvm_tensor* til
                                      dvm_program** out) {
   if (!p || !tile_out || !wg_out || !out) return fail(DVM_ERR_INVALID_ARG, "null argument");
   const uint32_t kt = p->prog.w[H_KTYPE];
+  if (p->segments != 1) return fail(DVM_ERR_UNSUPPORTED, "tile maps of single programs only");
   if (kt != KT_VECTOR && kt != KT_VECTOR_WIDE && kt != KT_MIX) return fail(DVM_ERR_UNSUPPORTED, "unknown kernel type");
   for (const dvm_tensor* t : {tile_out, wg_out}) {
     if (t->dtype != DVM_F32 || t->ndim != 2 || t->shape[0] != p->R || t->shape[1] != p->C || t->stride[1] != 1 ||

@@ -961,9 +961,34 @@ __device__ __forceinline__ Ch& treg(Regs& r) {
 // execute (the handler, row-register runs inside it included) and tile
 // changes, written per workgroup at the end.  The product kernel is the
 // PROF = false instance, with no counter reads.
+// The program this workgroup runs and its place in that program's grid: the
+// whole kernel argument, or in a stacked launch the segment whose workgroup
+// range holds blockIdx.x (wave-uniform: every value comes from scalar loads).
+struct Seg {
+  KW* W;
+  uint32_t b, grid;
+};
+
+__device__ __forceinline__ Seg segment_of() {
+  KW* K = (KW*)__builtin_amdgcn_kernarg_segment_ptr();
+  Seg g{K, blockIdx.x, gridDim.x};
+  if (K[0] == STACK_MAGIC) {
+    const uint32_t n = K[S_NSEG];
+    uint32_t s = 0;
+    for (uint32_t k = 1; k < n; ++k)
+      if (blockIdx.x >= K[S_DIR + 2 * k + 1]) s = k;
+    const uint32_t b0 = K[S_DIR + 2 * s + 1];
+    const uint32_t b1 = s + 1 < n ? K[S_DIR + 2 * s + 3] : gridDim.x;
+    g.W = K + K[S_DIR + 2 * s];
+    g.b = blockIdx.x - b0;
+    g.grid = b1 - b0;
+  }
+  return g;
+}
+
 template <bool PROF>
-__device__ __forceinline__ void vm_main(float (*s_red)[T_LANES / 64], int& s_last, char* dlds) {
-  KW* W = (KW*)__builtin_amdgcn_kernarg_segment_ptr();
+__device__ __forceinline__ void vm_main(const Seg& sg, float (*s_red)[T_LANES / 64], int& s_last, char* dlds) {
+  KW* W = sg.W;
   uint64_t p_start = 0, p_top = 0, p_ent = 0, p_dec = 0, p_exe = 0, p_tile = 0, p_n = 0;
   if constexpr (PROF) p_start = __builtin_amdgcn_s_memtime();
 #define PROF_ENTER() \
@@ -986,8 +1011,8 @@ __device__ __forceinline__ void vm_main(float (*s_red)[T_LANES / 64], int& s_las
   // Workgroup b runs tiles b, b + grid, b + 2 grid, ... (at most body_tile of
   // them): at any moment the resident workgroups work on neighbouring tiles,
   // so the streams they read and write advance together through memory.
-  const uint32_t t_begin = blockIdx.x;
-  const uint32_t t_step = gridDim.x;
+  const uint32_t t_begin = sg.b;
+  const uint32_t t_step = sg.grid;
   const uint32_t t_end = block_dim;
 
   Regs R;
@@ -1277,7 +1302,7 @@ __device__ __forceinline__ void vm_main(float (*s_red)[T_LANES / 64], int& s_las
         break;
       }
       case HD_DBG: PROF_ENTER() {
-        const float v = f_sub(w0) == 0 ? (float)tl.id : (float)blockIdx.x;
+        const float v = f_sub(w0) == 0 ? (float)tl.id : (float)sg.b;
         if (f_dst(w0) == 0) fill(treg<0>(R), v);
         else if (f_dst(w0) == 1) fill(treg<1>(R), v);
         else fill(treg<2>(R), v);
@@ -1337,7 +1362,7 @@ __device__ __forceinline__ void vm_main(float (*s_red)[T_LANES / 64], int& s_las
     if (tid == 0) {
       __atomic_thread_fence(__ATOMIC_RELEASE);
       const uint32_t prev = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-      s_last = prev == gridDim.x - 1;
+      s_last = prev == sg.grid - 1;
     }
     __syncthreads();
     if (s_last) {
@@ -1382,14 +1407,14 @@ __device__ __forceinline__ void vm_main(float (*s_red)[T_LANES / 64], int& s_las
 // Cross-wave reduction buffers and the reduce-all flag: static arrays in the
 // standard build, a reserved part of the dynamic area in the wide build.
 #ifdef DVM_WIDE
-#define DVM_RED_BUFFERS()                                                                              \
+#define DVM_RED_BUFFERS(W)                                                                             \
   extern __shared__ __attribute__((aligned(16))) char dlds[];                                          \
-  const uint32_t red_off = ((KW*)__builtin_amdgcn_kernarg_segment_ptr())[H_RED_OFF];                 \
+  const uint32_t red_off = (W)[H_RED_OFF];                                                             \
   float(*s_red)[T_LANES / 64] = reinterpret_cast<float(*)[T_LANES / 64]>(dlds + red_off);             \
   int& s_last = *reinterpret_cast<int*>(dlds + red_off + N_LDSBUF * (T_LANES / 64) * 4);
 constexpr uint32_t LDS_CAP = LDS_BUDGET_WIDE;
 #else
-#define DVM_RED_BUFFERS()                                     \
+#define DVM_RED_BUFFERS(W)                                    \
   __shared__ float s_red[N_LDSBUF][T_LANES / 64];             \
   __shared__ int s_last;                                      \
   extern __shared__ __attribute__((aligned(16))) char dlds[];
@@ -1398,22 +1423,24 @@ constexpr uint32_t LDS_CAP = LDS_BUDGET;
 
 extern "C" __global__ void __launch_bounds__(T_LANES) __attribute__((amdgpu_waves_per_eu(2, 2)))
 DVM_SYM(dvm_vm_vector)(const Program prog) {
-  DVM_RED_BUFFERS()
+  const Seg sg = segment_of();
+  DVM_RED_BUFFERS(sg.W)
   (void)prog;
-  vm_main<false>(s_red, s_last, dlds);
+  vm_main<false>(sg, s_red, s_last, dlds);
 }
 
 // Profiling twin of dvm_vm_vector: same program, same results, plus the
 // per-workgroup cycle split at the address in header words H_PROF_LO/HI.
 extern "C" __global__ void __launch_bounds__(T_LANES) __attribute__((amdgpu_waves_per_eu(2, 2)))
 DVM_SYM(dvm_vm_vector_prof)(const Program prog) {
-  DVM_RED_BUFFERS()
+  const Seg sg = segment_of();
+  DVM_RED_BUFFERS(sg.W)
   (void)prog;
-  vm_main<true>(s_red, s_last, dlds);
+  vm_main<true>(sg, s_red, s_last, dlds);
 }
 
 // Host-side launch of the VECTOR VM kernel with one program as its argument.
-extern "C" hipError_t DVM_SYM(dvm_launch_vector_kernel)(const Program* p, unsigned grid, hipStream_t s) {
+extern "C" hipError_t DVM_SYM(dvm_launch_vector_kernel)(const Program* p, unsigned grid, unsigned lds, hipStream_t s) {
   static bool attr_set = false;
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute((const void*)DVM_SYM(dvm_vm_vector), hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -1421,7 +1448,7 @@ extern "C" hipError_t DVM_SYM(dvm_launch_vector_kernel)(const Program* p, unsign
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  hipLaunchKernelGGL(DVM_SYM(dvm_vm_vector), dim3(grid), dim3(T_LANES), p->w[H_LDS_BYTES], s, *p);
+  hipLaunchKernelGGL(DVM_SYM(dvm_vm_vector), dim3(grid), dim3(T_LANES), lds, s, *p);
   return hipGetLastError();
 }
 

@@ -105,6 +105,8 @@ typedef struct {
   uint32_t n_words;      /* program size in 32-bit words */
   uint64_t bytes;        /* physical bytes of the graph: each operand tensor read once and each
                             stored output written once (the least HBM traffic of a launch) */
+  uint32_t segments;     /* 1, or the programs a stacked program holds (the fields above are
+                            its first segment's, except grid and bytes: the whole launch's) */
 } dvm_header;
 
 typedef struct {
@@ -121,6 +123,7 @@ typedef struct {
   double fuse_us_total;       /* host time of capture and fusion decisions (input, add_op, end_group,
                                  release), without the encodes and launches they trigger */
   double launch_us_total;     /* host time of the launches of implicit and explicit flushes */
+  uint64_t stacked;           /* programs launched as segments of stacked launches */
 } dvm_stats;
 
 /* Contexts (the VM's code is loaded once and stays resident: MindSpore DVM
@@ -242,6 +245,26 @@ dvm_status dvm_launch_noalloc(dvm_context* ctx, const dvm_program* p, void* stre
 #define DVM_PROF_COUNTERS 5
 dvm_status dvm_launch_profiled(dvm_context* ctx, const dvm_program* p, void* stream, uint64_t* counters,
                                size_t n_counters);
+
+/* Stacking (the stacking-based fusion of the DVM review page, section 5.1,
+ * Figure 9: independent graphs packed into one launch).  With max_segments > 1
+ * a graph keeps up to that many encoded programs (at most 7) before launching
+ * them as one: each keeps its own header, tiling and workgroups, and they run
+ * side by side.  A program joins only if it runs on the same VECTOR build,
+ * is no reduce-all or branch program, fits the kernel argument (1000 words)
+ * and is independent of the stacked ones: it writes no memory they read or
+ * write and reads none they write.  Otherwise the stack launches first and
+ * the program starts a new one (or runs at once).  dvm_graph_flush_launch,
+ * dvm_sync and dvm_flush launch what the stack holds first; a graph destroyed
+ * with programs in its stack discards them.  Default 1 (every program
+ * launches when flushed).  Launches what the stack holds when called. */
+dvm_status dvm_graph_set_stacking(dvm_graph* g, int32_t max_segments);
+
+/* One stacked program from n (2..7) programs of one VECTOR build, none a
+ * reduce-all; the caller guarantees they are independent (see above).  The
+ * inputs stay the caller's.  DVM_ERR_UNSUPPORTED for other kernel types,
+ * DVM_ERR_RESOURCE when the words exceed the kernel argument. */
+dvm_status dvm_program_stack(const dvm_program* const* programs, size_t n, dvm_program** out);
 
 /* Device-side control flow (the if-else of the DVM review page's dynamic
  * control-flow workload, section 6.2; the MindSpore summary page, section 3.2,
