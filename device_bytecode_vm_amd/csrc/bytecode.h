@@ -239,7 +239,8 @@ enum Handler : uint32_t {
   HD_BIN_MEM = 156,  // ACC <- ACC (op) B for a memory operand, any ALU op (sub, FL_REV)
   HD_DIV_T = 157,    // ACC <- ACC / treg[b] (or treg[b] / ACC)
   HD_FMA_INV = 158,  // OP_FMA_INV
-  HD_COUNT = 159
+  HD_SILU = 159,     // ACC <- ACC / (exp(-ACC) + 1) (OP_UN, UN_SILU)
+  HD_COUNT = 160
 };
 enum BinForm : uint32_t { BF_T0 = 0, BF_T1 = 1, BF_T2 = 2, BF_SCALAR = 3, BF_MEM = 4, BF_REV = 5 };
 
@@ -250,6 +251,7 @@ enum Alu : uint32_t {
 enum Una : uint32_t {
   UN_SQRT = 0, UN_ABS = 1, UN_LOG = 2, UN_EXP = 3, UN_ROUND = 4, UN_FLOOR = 5, UN_ISFINITE = 6,
   UN_NEG = 7, UN_RECIP = 8, UN_TOBF16 = 9, UN_IDENT = 10,
+  UN_SILU = 11,  // z / (exp(-z) + 1): a fused SiLU chain, the chain's own operations in registers
 };
 enum BKind : uint32_t { BK_TREG = 0, BK_RREG = 1, BK_IMM = 2, BK_MEM = 3 };  // BK_MEM: B loaded from arg[w1]
 // RK_SUMSQ: sum of the squares of treg[a] (a reduce of x * x whose product is

@@ -403,6 +403,10 @@ struct OpRec {
   int64_t out = -1;  // value slot index
 };
 
+// Internal op of fused graphs (never added through the ABI): z / (exp(-z) + 1),
+// a SiLU chain the encoder fused (fuse_silu).
+constexpr int32_t OP_SILU = DVM_OP_COUNT;
+
 bool is_reduce(int op) { return op == DVM_OP_REDUCE_SUM || op == DVM_OP_REDUCE_MAX; }
 bool is_reduce_all(const OpRec& o) { return is_reduce(o.op) && o.axis == DVM_AXIS_ALL; }
 bool is_binary(int op) { return op <= DVM_OP_POW; }
@@ -1075,6 +1079,7 @@ struct Encoder {
       case DVM_OP_ISFINITE: return UN_ISFINITE;
       case DVM_OP_NEG: return UN_NEG;
       case DVM_OP_RECIP: return UN_RECIP;
+      case OP_SILU: return UN_SILU;
       default: return UN_IDENT;  // cast / copy: the dtype rounding follows
     }
   }
@@ -1460,7 +1465,7 @@ struct Encoder {
         if (a == 0 && dt(w1) == DT_F32) return HD_ST_F32;
         return HD_ST_DIR + a;
       case OP_COPY: return HD_COPY + 3 * d + a;
-      case OP_UN: return HD_UN + sub;
+      case OP_UN: return sub == UN_SILU ? (uint32_t)HD_SILU : HD_UN + sub;
       case OP_BIN: {
         const uint32_t bk = f_bk(w0);
         if (bk == BK_MEM) return HD_BIN_MEM;
@@ -1874,6 +1879,47 @@ void simplify_ops(const dvm_graph* g, const std::vector<OpRec>& in, std::vector<
     if (keep[i]) out->push_back(fw[i]);
 }
 
+// SiLU chains (the composite x / (1 + e^-x) written as n = -z, e = exp(n),
+// d = e + 1, s = z / d, with n, e and d fp32 values nobody else reads and
+// nobody stores) become one op on z.  The VM computes the same four
+// operations in registers, so every stored value is bit-identical; it saves
+// three dispatches and the copy that keeps z alive across the chain.
+void fuse_silu(const dvm_graph* g, std::vector<OpRec>& ops) {
+  if (ops.size() < 4) return;
+  std::vector<int> uses(g->vals.size(), 0);
+  for (const OpRec& o : ops)
+    for (int k = 0; k < o.n_in; ++k) uses[o.in[k]]++;
+  auto temp = [&](int64_t s) {
+    const Val& v = g->vals[s];
+    return v.t.dtype == DVM_F32 && !(v.live || !v.released) && uses[s] == 1;
+  };
+  auto scalar_op = [](const OpRec& o, int op, float c) {
+    return o.op == op && o.n_in == 1 && (o.scalar_pos == 0 || o.scalar_pos == 1) && o.scalar == c;
+  };
+  std::vector<OpRec> out;
+  out.reserve(ops.size());
+  for (size_t i = 0; i < ops.size(); ++i) {
+    if (i + 3 < ops.size()) {
+      const OpRec &a = ops[i], &b = ops[i + 1], &c = ops[i + 2], &d = ops[i + 3];
+      const bool neg = (a.op == DVM_OP_NEG && a.n_in == 1) || scalar_op(a, DVM_OP_MUL, -1.f);
+      if (neg && b.op == DVM_OP_EXP && b.in[0] == a.out && scalar_op(c, DVM_OP_ADD, 1.f) && c.in[0] == b.out &&
+          d.op == DVM_OP_DIV && d.n_in == 2 && d.in[0] == a.in[0] && d.in[1] == c.out && temp(a.out) &&
+          temp(b.out) && temp(c.out)) {
+        OpRec f = d;
+        f.op = OP_SILU;
+        f.n_in = 1;
+        f.in[1] = -1;
+        f.scalar_pos = -1;
+        out.push_back(f);
+        i += 3;
+        continue;
+      }
+    }
+    out.push_back(ops[i]);
+  }
+  ops.swap(out);
+}
+
 // ===========================================================================
 // Flushing
 // ===========================================================================
@@ -1886,6 +1932,7 @@ dvm_status encode_list(dvm_graph* g, const std::vector<OpRec>& list, bool allow_
   make_local(g, list, &L);
   simplify_ops(&L.lg, L.ops, &ops);
   if (ops.empty()) return DVM_OK;  // every op was dead: nothing to run, nothing stored
+  fuse_silu(&L.lg, ops);
   dvm_program* p = new (std::nothrow) dvm_program();
   if (!p) return fail(DVM_ERR_INTERNAL, "out of host memory");
   Encoder enc(&L.lg, ops, p);

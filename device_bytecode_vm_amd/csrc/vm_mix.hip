@@ -93,12 +93,18 @@ __device__ __forceinline__ uint32_t f2bf_pack(float lo, float hi) {
 }
 __device__ __forceinline__ float round_bf16(float x) { return bf2f(f2bf_pack(x, 0.f) & 0xffffu); }
 
+// Division in MIX epilogues: x times the hardware reciprocal of y (v_rcp_f32,
+// within 1 ulp), within 2 fp32 ulp of the correctly rounded quotient, two
+// instructions instead of about ten.  MatMul graphs are held to 1e-2 relative
+// error, far above this.
+__device__ __forceinline__ float div_mix(float x, float y) { return x * __builtin_amdgcn_rcpf(y); }
+
 __device__ __forceinline__ float alu_rt(uint32_t k, float x, float y) {
   switch (k) {
     case ALU_ADD: return x + y;
     case ALU_SUB: return x - y;
     case ALU_MUL: return x * y;
-    case ALU_DIV: return x / y;
+    case ALU_DIV: return div_mix(x, y);
     case ALU_MAX: return __builtin_elementwise_maximum(x, y);  // NaN-propagating
     case ALU_MIN: return __builtin_elementwise_minimum(x, y);
     default: return powf(x, y);
@@ -117,6 +123,7 @@ __device__ __forceinline__ float una_rt(uint32_t f, float x) {
     case UN_NEG: return -x;
     case UN_RECIP: return 1.f / x;
     case UN_TOBF16: return round_bf16(x);
+    case UN_SILU: return div_mix(x, __expf(-x) + 1.f);  // a fused SiLU chain: its own operations, in order
     default: return x;
   }
 }

@@ -269,6 +269,7 @@ __device__ __forceinline__ float una(float x) {
   else if constexpr (F == UN_NEG) return -x;
   else if constexpr (F == UN_RECIP) return 1.f / x;
   else if constexpr (F == UN_TOBF16) return round_bf16(x);
+  else if constexpr (F == UN_SILU) return x / (__expf(-x) + 1.f);  // the chain's operations, in order
   else return x;
 }
 
@@ -284,6 +285,7 @@ __device__ __forceinline__ float una_rt(uint32_t f, float x) {
     case UN_NEG: return -x;
     case UN_RECIP: return 1.f / x;
     case UN_TOBF16: return round_bf16(x);
+    case UN_SILU: return x / (__expf(-x) + 1.f);
     default: return x;
   }
 }
@@ -1184,6 +1186,7 @@ __device__ __forceinline__ void vm_main(const Seg& sg, float (*s_red)[T_LANES / 
       case HD_UN + UN_NEG: PROF_ENTER() un_c<UN_NEG>(treg<0>(R)); break;
       case HD_UN + UN_RECIP: PROF_ENTER() un_c<UN_RECIP>(treg<0>(R)); break;
       case HD_UN + UN_TOBF16: PROF_ENTER() un_c<UN_TOBF16>(treg<0>(R)); break;
+      case HD_SILU: PROF_ENTER() un_c<UN_SILU>(treg<0>(R)); break;
       CASE_BIN_COMM(ALU_ADD) CASE_BIN_NC(ALU_SUB) CASE_BIN_COMM(ALU_MUL)
       case HD_BIN + 10 * ALU_DIV + BF_SCALAR: PROF_ENTER() bin_cs<ALU_DIV, false>(treg<0>(R), SCALAR_B); break;
       case HD_BIN + 10 * ALU_DIV + BF_REV + BF_SCALAR: PROF_ENTER() bin_cs<ALU_DIV, true>(treg<0>(R), SCALAR_B); break;
