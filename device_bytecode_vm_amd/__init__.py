@@ -126,6 +126,20 @@ class Program:
         check(lib.dvm_program_words(self.h, buf, C.byref(cap)))
         return list(buf)
 
+    def verify(self):
+        """The bytecode verifier: None if the program passes, else the first
+        violation it finds."""
+        buf = C.create_string_buffer(512)
+        st = lib.dvm_program_verify(self.h, buf, 512)
+        return None if st == L.OK else buf.value.decode()
+
+    @staticmethod
+    def from_words(words, ctx=None) -> "Program":
+        arr = (C.c_uint32 * len(words))(*[int(w) & 0xFFFFFFFF for w in words])
+        q = C.c_void_p()
+        check(lib.dvm_program_from_words(arr, len(words), C.byref(q)))
+        return Program(q, ctx)
+
     def launch(self, stream=None, ctx=None):
         """Launch on `ctx` (default: the context that encoded the program)."""
         check(lib.dvm_launch((ctx or self.ctx).h, self.h, _stream_handle(stream)))
@@ -144,6 +158,13 @@ class Program:
         dispatch count."""
         check(lib.dvm_launch_profiled(self.ctx.h, self.h, _stream_handle(stream), C.c_void_p(counters.data_ptr()),
                                       counters.numel()))
+
+    def launch_stress(self, seed, counters, stream=None):
+        """Race-stress launch (profiling twin with seeded per-wave delays):
+        the same stored results as launch, for a correctly synchronised
+        program.  counters as for launch_profiled."""
+        check(lib.dvm_launch_stress(self.ctx.h, self.h, _stream_handle(stream), int(seed) & 0xFFFFFF,
+                                    C.c_void_p(counters.data_ptr()), counters.numel()))
 
     def debug_tilemap(self, tile_out, wg_out) -> "Program":
         q = C.c_void_p()
@@ -316,7 +337,11 @@ class Graph:
         fusion boundary or a reduce-all), or None."""
         q = C.c_void_p()
         check(lib.dvm_graph_take_program(self.h, C.byref(q)))
-        return Program(q, self.ctx) if q.value else None
+        if not q.value:
+            return None
+        prog = Program(q, self.ctx)
+        prog._keep = list(self._keep)   # the tensors it reads or writes stay alive with it
+        return prog
 
     def flush_launch(self) -> bool:
         fl = C.c_int32(0)

@@ -89,6 +89,7 @@ _sigs = {
     "dvm_launch": (C.c_int, [VP, VP, VP]),
     "dvm_launch_noalloc": (C.c_int, [VP, VP, VP]),
     "dvm_launch_profiled": (C.c_int, [VP, VP, VP, VP, C.c_size_t]),
+    "dvm_launch_stress": (C.c_int, [VP, VP, VP, C.c_uint32, VP, C.c_size_t]),
     "dvm_graph_flush_launch": (C.c_int, [VP, P(C.c_int32)]),
     "dvm_graph_set_stacking": (C.c_int, [VP, C.c_int32]),
     "dvm_program_stack": (C.c_int, [P(VP), C.c_size_t, P(VP)]),
@@ -99,6 +100,8 @@ _sigs = {
     "dvm_program_header": (C.c_int, [VP, P(DvmHeader)]),
     "dvm_program_words": (C.c_int, [VP, P(C.c_uint32), P(C.c_size_t)]),
     "dvm_program_free": (None, [VP]),
+    "dvm_program_verify": (C.c_int, [VP, C.c_char_p, C.c_size_t]),
+    "dvm_program_from_words": (C.c_int, [P(C.c_uint32), C.c_size_t, P(VP)]),
     "dvm_program_debug_tilemap": (C.c_int, [VP, P(DvmTensor), P(DvmTensor), P(VP)]),
     "dvm_graph_stats": (C.c_int, [VP, P(DvmStats)]),
     "dvm_graph_flush_log": (C.c_int, [VP, P(C.c_int32), P(C.c_int32), P(C.c_float), P(C.c_uint64),

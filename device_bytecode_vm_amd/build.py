@@ -8,7 +8,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libdvm.so")
 
-SOURCES = ["dvm_host.cpp", "vm_vector.hip", "vm_vector_wide.hip", "vm_mix.hip", "scratch_static.hip"]
+SOURCES = ["dvm_host.cpp", "verify.cpp", "vm_vector.hip", "vm_vector_wide.hip", "vm_mix.hip", "scratch_static.hip"]
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
          # no packed-fp32 VALU forms in device code
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

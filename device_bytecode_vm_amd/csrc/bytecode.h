@@ -166,6 +166,11 @@ enum HdrFlag : uint32_t {
   // selects (device-side control flow: no host round trip between the launch
   // that writes the condition and this one)
   HF_BRANCH = 2u,
+  // race-stress launches (profiling twin only): before every dispatch a wave
+  // sleeps a pseudo-random, wave-uniform number of intervals drawn from the
+  // seed in bits [31:8], so waves drift apart and a missing barrier shows as
+  // a changed result
+  HF_STRESS = 4u,
 };
 constexpr uint64_t STREAM_BYTES = 16ull << 20;
 enum ArgFlag : uint32_t {

@@ -13,6 +13,7 @@
 #include <chrono>
 #include <cmath>
 #include <cstdarg>
+#include <cstdlib>
 #include <cstdio>
 #include <cstring>
 #include <deque>
@@ -24,6 +25,10 @@
 #include "dvm.h"
 
 using namespace dvmbc;
+
+namespace dvmbc {
+bool verify_words(const uint32_t* W, uint32_t n_words, std::string* err);  // verify.cpp
+}
 
 extern "C" hipError_t dvm_launch_vector_kernel(const Program* p, unsigned grid, unsigned lds, hipStream_t s);
 extern "C" hipError_t dvm_launch_mix_kernel(const Program* p, unsigned grid, hipStream_t s);
@@ -863,7 +868,6 @@ struct Encoder {
   int n_red = 0;
   bool cross_wave = false;
   std::vector<int> pf_slot, inv_slot;   // slot -> LDS staging slot (-1 none)
-  bool pf_issued[2] = {false, false};
   struct Consume {
     size_t pos;      // word index of the instruction in body
     uint32_t slot;
@@ -1306,21 +1310,26 @@ struct Encoder {
     }
     if (pf_slot[s] >= 0) {
       *slot = (uint32_t)pf_slot[s];
-      uint32_t f = FL_PF;
-      if (!pf_issued[*slot]) {
-        pf_issued[*slot] = true;
-        f |= FL_ISSUE;
-      }
-      return f;
+      return FL_PF;  // the refill goes on the slot's last read (place_refills)
     }
     return 0;
   }
 
+  // Each prefetch slot is refilled with the next tile's data by its last read
+  // in the body: every read of the slot then sees this tile's data (a refill
+  // at an earlier read would hand the later reads the next tile's values).
+  void place_refills() {
+    long last[2] = {-1, -1};
+    for (const Consume& c : consumes) last[c.slot] = std::max(last[c.slot], (long)c.pos);
+    for (int k = 0; k < 2; ++k) {
+      issue_pos[k] = last[k];
+      if (last[k] >= 0) body[(size_t)last[k]] |= (uint32_t)FL_ISSUE << 28;
+    }
+  }
+
   void note_consume(uint32_t f, uint32_t slot, bool is_bin) {
     if (!(f & FL_PF)) return;
-    const size_t pos = body.size() - 2;
-    consumes.push_back({pos, slot, is_bin});
-    if (f & FL_ISSUE) issue_pos[slot] = (long)pos;
+    consumes.push_back({body.size() - 2, slot, is_bin});
   }
 
   void emit_load(int k, int64_t s) {
@@ -1754,6 +1763,7 @@ struct Encoder {
       }
       if (s != DVM_OK) return s;
     }
+    place_refills();
     patch_waits();
     fuse_scale_shift(body);
     // Sync at the end of the body when the next tile's first cross-wave
@@ -1923,6 +1933,24 @@ void fuse_silu(const dvm_graph* g, std::vector<OpRec>& ops) {
 // ===========================================================================
 // Flushing
 // ===========================================================================
+// DVM_VERIFY set in the environment (to anything but 0): every program the
+// library encodes, merges or stacks is verified before it is handed out or
+// launched; a violation fails the flush with DVM_ERR_INTERNAL.
+bool verify_on() {
+  static const bool on = [] {
+    const char* v = std::getenv("DVM_VERIFY");
+    return v && *v && std::strcmp(v, "0") != 0;
+  }();
+  return on;
+}
+
+dvm_status checked(dvm_program* p) {
+  if (!p || !verify_on()) return DVM_OK;
+  std::string e;
+  if (!verify_words(p->prog.w, p->n_words, &e)) return fail(DVM_ERR_INTERNAL, "bytecode verifier: %s", e.c_str());
+  return DVM_OK;
+}
+
 // Encodes one fused op list (after the bytecode clean-up); *out = NULL when no
 // op has an effect.  allow_wide: the wide VM build may be chosen.
 dvm_status encode_list(dvm_graph* g, const std::vector<OpRec>& list, bool allow_wide, dvm_program** out) {
@@ -1968,6 +1996,7 @@ dvm_status encode_list(dvm_graph* g, const std::vector<OpRec>& list, bool allow_
       }
     }
   }
+  if (st == DVM_OK) st = checked(p);
   if (st != DVM_OK) {
     delete p;
     return st;
@@ -2080,6 +2109,11 @@ dvm_status merge_branch(const dvm_program* pt, const dvm_program* pe, const dvm_
   q->reads.push_back({(uintptr_t)cond.data, 4});
   q->writes = pt->writes;
   q->writes.insert(q->writes.end(), pe->writes.begin(), pe->writes.end());
+  const dvm_status v = checked(q);
+  if (v != DVM_OK) {
+    delete q;
+    return v;
+  }
   *out = q;
   return DVM_OK;
 }
@@ -2251,6 +2285,11 @@ dvm_status build_stack(const dvm_program* const* ps, size_t n, dvm_program** out
   q->grid_launch = wg;
   q->R = ps[0]->R;
   q->C = ps[0]->C;
+  const dvm_status v = checked(q);
+  if (v != DVM_OK) {
+    delete q;
+    return v;
+  }
   *out = q;
   return DVM_OK;
 }
@@ -2641,8 +2680,21 @@ dvm_status dvm_launch_noalloc(dvm_context* ctx, const dvm_program* p, void* stre
   return DVM_OK;
 }
 
+dvm_status launch_twin(dvm_context* ctx, const dvm_program* p, void* stream, uint64_t* counters, size_t n_counters,
+                       uint32_t flags_or);
+
 dvm_status dvm_launch_profiled(dvm_context* ctx, const dvm_program* p, void* stream, uint64_t* counters,
                                size_t n_counters) {
+  return launch_twin(ctx, p, stream, counters, n_counters, 0u);
+}
+
+dvm_status dvm_launch_stress(dvm_context* ctx, const dvm_program* p, void* stream, uint32_t seed, uint64_t* counters,
+                             size_t n_counters) {
+  return launch_twin(ctx, p, stream, counters, n_counters, HF_STRESS | ((seed & 0xffffffu) << 8));
+}
+
+dvm_status launch_twin(dvm_context* ctx, const dvm_program* p, void* stream, uint64_t* counters, size_t n_counters,
+                       uint32_t flags_or) {
   if (!ctx || !p) return fail(DVM_ERR_INVALID_ARG, "null argument");
   if (ctx->device < 0) return fail(DVM_ERR_DEVICE, "encode-only context cannot launch");
   const uint32_t kt = p->prog.w[H_KTYPE];
@@ -2659,6 +2711,7 @@ dvm_status dvm_launch_profiled(dvm_context* ctx, const dvm_program* p, void* str
     if (st != DVM_OK) return st;
     set_scratch(&q, area, SCRATCH_BYTES);
   }
+  q.w[H_FLAGS] |= flags_or;
   const uint64_t a = (uint64_t)(uintptr_t)counters;
   q.w[H_PROF_LO] = (uint32_t)a;
   q.w[H_PROF_HI] = (uint32_t)(a >> 32);
@@ -2814,6 +2867,29 @@ dvm_status dvm_program_words(const dvm_program* p, uint32_t* buf, size_t* n_word
 }
 
 void dvm_program_free(dvm_program* p) { delete p; }
+
+dvm_status dvm_program_verify(const dvm_program* p, char* msg, size_t len) {
+  if (!p) return fail(DVM_ERR_INVALID_ARG, "null program");
+  std::string e;
+  const bool ok = verify_words(p->prog.w, p->n_words, &e);
+  if (msg && len) {
+    std::snprintf(msg, len, "%s", ok ? "" : e.c_str());
+  }
+  if (!ok) return fail(DVM_ERR_INTERNAL, "bytecode verifier: %s", e.c_str());
+  return DVM_OK;
+}
+
+dvm_status dvm_program_from_words(const uint32_t* words, size_t n_words, dvm_program** out) {
+  if (!words || !out) return fail(DVM_ERR_INVALID_ARG, "null argument");
+  *out = nullptr;
+  if (n_words < (size_t)HDR_WORDS || n_words > (size_t)MAX_WORDS) return fail(DVM_ERR_INVALID_ARG, "%zu words", n_words);
+  dvm_program* q = new (std::nothrow) dvm_program();
+  if (!q) return fail(DVM_ERR_INTERNAL, "out of host memory");
+  std::copy(words, words + n_words, q->prog.w);
+  q->n_words = (uint32_t)n_words;
+  *out = q;
+  return DVM_OK;
+}
 
 dvm_status dvm_program_debug_tilemap(const dvm_program* p, const dvm_tensor* tile_out, const dvm_tensor* wg_out,
                                      dvm_program** out) {

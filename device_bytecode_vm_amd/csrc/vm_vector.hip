@@ -1059,8 +1059,24 @@ __device__ __forceinline__ void vm_main(const Seg& sg, float (*s_red)[T_LANES / 
   uint32_t nw0, nw1;
   fetch2(W, pc, nw0, nw1);
 
+  // race-stress (profiling twin only): a seeded, wave-uniform delay per dispatch
+  uint32_t stress = 0;
+  if constexpr (PROF) {
+    if (W[H_FLAGS] & HF_STRESS)
+      stress = ((W[H_FLAGS] >> 8) * 0x9e3779b1u) ^ (sg.b * 0x85ebca6bu) ^
+               (uint32_t)__builtin_amdgcn_readfirstlane(wave) * 0xc2b2ae35u | 1u;
+  }
+
   while (true) {
-    if constexpr (PROF) p_top = __builtin_amdgcn_s_memtime();
+    if constexpr (PROF) {
+      p_top = __builtin_amdgcn_s_memtime();
+      if (stress) {
+        stress ^= stress << 13;
+        stress ^= stress >> 17;
+        stress ^= stress << 5;
+        for (uint32_t k = (stress >> 7) & 7u; k > 0; --k) __builtin_amdgcn_s_sleep(2);
+      }
+    }
     if (pc >= pc_end) {
       if (in_pro) in_pro = false;
       else tile += t_step;

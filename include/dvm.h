@@ -285,6 +285,17 @@ dvm_status dvm_graph_begin_branch(dvm_graph* g, dvm_value cond, float threshold)
 dvm_status dvm_graph_else_branch(dvm_graph* g);
 dvm_status dvm_graph_end_branch(dvm_graph* g, int32_t* launched);
 
+/* Race-stress launch of a single VECTOR program: the profiling twin (same
+ * results, same counters as dvm_launch_profiled) with a delay before every
+ * dispatch, a seeded pseudo-random number of sleep intervals that is uniform
+ * within a wave and differs between waves, so the waves of a workgroup drift
+ * apart.  Every synchronisation a program needs comes from the barriers the
+ * encoder inserted (DVM review page, section 4.3), so a correct program
+ * stores bit-identical results under any seed.  Arguments and errors as for
+ * dvm_launch_profiled.  Asynchronous. */
+dvm_status dvm_launch_stress(dvm_context* ctx, const dvm_program* p, void* stream, uint32_t seed, uint64_t* counters,
+                             size_t n_counters);
+
 /* dvm_flush + dvm_launch on the graph's stream (an explicit flush, MindSpore
  * summary page, section 3.2; no-op when nothing is encoded; *launched = 0
  * then). */
@@ -302,6 +313,25 @@ dvm_status dvm_program_header(const dvm_program* p, dvm_header* out);
  * NULL to query the size. */
 dvm_status dvm_program_words(const dvm_program* p, uint32_t* buf, size_t* n_words);
 void dvm_program_free(dvm_program* p);
+
+/* The bytecode verifier (the syncs and staging the encoder inserts, DVM review
+ * page, section 4.3, are what the VM relies on; this re-derives them from the
+ * words): layout and version, the tile's fit to its VM build and the header
+ * counts it implies, operand indices and access forms, registers read only
+ * after being written in the same tile, prefetch and invariant slots filled
+ * before they are read and refilled once per tile, and no cross-wave
+ * reduction buffer written before a barrier fences the previous reads of it
+ * (over consecutive tiles).  Stacked programs: the directory and each
+ * segment.  DVM_OK, or DVM_ERR_INTERNAL with the first violation (also copied
+ * into msg, at most len bytes, if msg is not NULL).  With DVM_VERIFY set in
+ * the environment (not "0"), the library verifies every program it encodes,
+ * merges or stacks and fails that flush with DVM_ERR_INTERNAL on a
+ * violation. */
+dvm_status dvm_program_verify(const dvm_program* p, char* msg, size_t len);
+
+/* A program from raw words (tests of the verifier; a program so made is never
+ * launched by the library unless the caller launches it). */
+dvm_status dvm_program_from_words(const uint32_t* words, size_t n_words, dvm_program** out);
 
 /* Debug program for tiling parity (the tile range and element-to-tile rules
  * of the DVM review page, sections 4.2 and 4.4): same header and tiling as p,

@@ -214,3 +214,31 @@ def test_reduce_all_on_two_streams(dvm, ctx):
         xh = host64(x)
         band = O.sum_guard_band(xh)
         assert abs(float(o.item()) - float(np.sum(xh))) <= band
+
+
+def test_prefetched_operand_read_twice(dvm, ctx):
+    """x is staged in a prefetch slot and read twice per tile (a = x - x,
+    b = x - a) with four tiles per workgroup: both reads must see this
+    tile's x (the slot is refilled for the next tile only by its last read).
+    Correctly rounded ops: bit-exact against the fp32-emulating oracle."""
+    import torch
+    say("prefetch_reuse")
+    x = W.normal(np.random.default_rng(8), (4096, 5120), 0, 1)
+    out = empty_dev(x.shape, "f32")
+    g = dvm.Graph(ctx)
+    vx = g.input(torch_dev(x, "f32"))
+    a = g.op("sub", vx, vx)
+    b = g.op("sub", vx, a)
+    c = g.op("mul", b, b)
+    g.op("add", c, c, out=out, live=True)
+    g.release(a, b, c)
+    p = g.flush()
+    assert p.header()["body_tile"] > 1
+    assert p.verify() is None
+    p.launch()
+    torch.cuda.synchronize()
+    ref, _ = evaluate([{"op": "sub", "in": ["x", "x"], "out": "a", "dtype": "f32"},
+                       {"op": "sub", "in": ["x", "a"], "out": "b", "dtype": "f32"},
+                       {"op": "mul", "in": ["b", "b"], "out": "c", "dtype": "f32"},
+                       {"op": "add", "in": ["c", "c"], "out": "o", "dtype": "f32"}], {"x": x}, emulate_f32=True)
+    assert np.array_equal(host64(out), ref["o"])
