@@ -14,7 +14,7 @@ from dataclasses import dataclass
 from . import _lib as L
 from ._lib import DvmError, check, lib
 
-__all__ = ["Context", "Graph", "Program", "Value", "TensorDesc", "DvmError", "lib", "stack_programs"]
+__all__ = ["Context", "Graph", "Program", "Value", "TensorDesc", "DvmError", "lib", "stack_programs", "Template"]
 
 
 @dataclass
@@ -380,3 +380,139 @@ class Graph:
             "encode_us_total": s.encode_us_total, "encode_us_max": s.encode_us_max, "bytes": s.bytes,
             "fuse_us_total": s.fuse_us_total, "launch_us_total": s.launch_us_total, "stacked": s.stacked,
         }
+
+
+class _TemplateGraph(Graph):
+    """The graph a template runs through (not owned: the template frees it)."""
+
+    def __init__(self, ctx, h):
+        self.ctx = ctx
+        self.h = h
+        self._in_group = False
+        self.flushes = 0
+        self._keep = []
+
+    def close(self):
+        self.h = None
+
+
+class Output:
+    """An output slot of a template op (out= in Template.op): its dtype; the
+    shape follows from the op."""
+
+    def __init__(self, dtype):
+        self.dtype = dtype
+
+
+class Template:
+    """Static-graph symbolic fusion: ops recorded once over symbolic dims
+    (strings) and concrete dims (ints); finalize() decides the fusion
+    partition once; run() binds tensors and only tiles, encodes and launches.
+    The interface of Graph for building (input / op / group / release), so the
+    composites build templates too."""
+
+    def __init__(self, ctx: Context, stream=None):
+        self.ctx = ctx
+        h = C.c_void_p()
+        check(lib.dvm_template_create(ctx.h, _stream_handle(stream) if ctx.device >= 0 else None, C.byref(h)))
+        self.h = h
+        gh = C.c_void_p()
+        check(lib.dvm_template_graph(h, C.byref(gh)))
+        self.graph = _TemplateGraph(ctx, gh)
+        self.symbols = {}
+        self.n_inputs = 0
+        self.n_outputs = 0
+
+    def close(self):
+        if self.h:
+            lib.dvm_template_destroy(self.h)
+            self.h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def _dims(self, dims):
+        out = []
+        for d in dims:
+            if isinstance(d, str):
+                k = self.symbols.setdefault(d, len(self.symbols))
+                out.append(-(k + 1))
+            else:
+                out.append(int(d))
+        return out
+
+    def input(self, dtype, dims=None) -> Value:
+        """A template input: input(dtype, dims), dims holding ints and symbol
+        names."""
+        dv = self._dims(dims or ())
+        arr = (C.c_int64 * max(len(dv), 1))(*dv)
+        v = C.c_int64()
+        check(lib.dvm_template_input(self.h, L.DTYPE_CODES[dtype], len(dv), arr, C.byref(v)))
+        self.n_inputs += 1
+        return Value(v.value, tuple(dims or ()), dtype)
+
+    def output(self, dtype) -> Output:
+        return Output(dtype)
+
+    def op(self, name, *ins, out=None, dtype=None, live=False, axis=-1) -> Value:
+        attrs = L.DvmAttrs(axis, -1, 0.0)
+        vals = []
+        for pos, x in enumerate(ins):
+            if isinstance(x, Value):
+                vals.append(x.h)
+            else:
+                attrs.scalar_pos = pos
+                attrs.scalar = float(x)
+        hs = (C.c_int64 * max(len(vals), 1))(*vals)
+        if isinstance(out, Output):
+            dtype = out.dtype
+            live = True
+        if dtype is None:
+            dtype = "u8" if name == "isfinite" else next(x.dtype for x in ins if isinstance(x, Value))
+        v = C.c_int64()
+        check(lib.dvm_template_add_op(self.h, L.OP_CODES[name], hs, len(vals), C.byref(attrs), L.DTYPE_CODES[dtype],
+                                      L.OUT_LIVE if live else 0, C.byref(v)))
+        if live:
+            self.n_outputs += 1
+        first = next(x for x in ins if isinstance(x, Value))
+        shape = first.shape
+        if name in ("reduce_sum", "reduce_max"):
+            shape = () if axis == L.AXIS_ALL else tuple(shape[:-1]) + (1,)
+        return Value(v.value, shape, dtype)
+
+    def release(self, *vals):
+        pass    # internal values are the template's to manage
+
+    @contextlib.contextmanager
+    def group(self):
+        check(lib.dvm_template_begin_group(self.h))
+        try:
+            yield self
+        finally:
+            check(lib.dvm_template_end_group(self.h))
+
+    def finalize(self) -> int:
+        n = C.c_int32(0)
+        check(lib.dvm_template_finalize(self.h, C.byref(n)))
+        return n.value
+
+    def partition(self):
+        """(graph index of every op, host microseconds finalize took)."""
+        n = C.c_size_t(0)
+        check(lib.dvm_template_partition(self.h, None, C.byref(n), None))
+        arr = (C.c_int32 * max(n.value, 1))()
+        cap = C.c_size_t(n.value)
+        us = C.c_double(0)
+        check(lib.dvm_template_partition(self.h, arr, C.byref(cap), C.byref(us)))
+        return [arr[i] for i in range(n.value)], us.value
+
+    def run(self, inputs, outputs) -> bool:
+        ia = (L.DvmTensor * max(len(inputs), 1))(*[to_c(x) for x in inputs])
+        oa = (L.DvmTensor * max(len(outputs), 1))(*[to_c(x) for x in outputs])
+        fl = C.c_int32(0)
+        check(lib.dvm_template_run(self.h, ia, len(inputs), oa, len(outputs), C.byref(fl)))
+        self.graph._keep.extend(list(inputs) + list(outputs))
+        return bool(fl.value)

@@ -106,6 +106,17 @@ _sigs = {
     "dvm_graph_stats": (C.c_int, [VP, P(DvmStats)]),
     "dvm_graph_flush_log": (C.c_int, [VP, P(C.c_int32), P(C.c_int32), P(C.c_float), P(C.c_uint64),
                                       P(C.c_size_t)]),
+    "dvm_template_create": (C.c_int, [VP, VP, P(VP)]),
+    "dvm_template_destroy": (None, [VP]),
+    "dvm_template_graph": (C.c_int, [VP, P(VP)]),
+    "dvm_template_input": (C.c_int, [VP, C.c_int32, C.c_int32, P(C.c_int64), P(C.c_int64)]),
+    "dvm_template_begin_group": (C.c_int, [VP]),
+    "dvm_template_end_group": (C.c_int, [VP]),
+    "dvm_template_add_op": (C.c_int, [VP, C.c_int32, P(C.c_int64), C.c_int32, P(DvmAttrs), C.c_int32, C.c_uint32,
+                                      P(C.c_int64)]),
+    "dvm_template_finalize": (C.c_int, [VP, P(C.c_int32)]),
+    "dvm_template_partition": (C.c_int, [VP, P(C.c_int32), P(C.c_size_t), P(C.c_double)]),
+    "dvm_template_run": (C.c_int, [VP, P(DvmTensor), C.c_int32, P(DvmTensor), C.c_int32, P(C.c_int32)]),
     "dvm_last_error": (C.c_char_p, []),
 }
 for _name, (_res, _args) in _sigs.items():

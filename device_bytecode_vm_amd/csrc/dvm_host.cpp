@@ -2459,6 +2459,93 @@ dvm_status end_group_impl(dvm_graph* g, int32_t* flushed) {
   return DVM_OK;
 }
 
+// ===========================================================================
+// Static-graph symbolic fusion (DVM review page, section 5.2, static-graph
+// fusion; section 7's table lists it beside the dynamic, streaming kind).
+//
+// A template is an op graph recorded once with symbolic dims.  finalize()
+// decides its fusion partition once, by running the streaming fuser's rules
+// on representative shapes: each symbol stands for one size shared by all its
+// occurrences and distinct from every other symbol and every concrete dim of
+// the template, so every shape equality and broadcast the rules test comes
+// out as it would for any binding.  Tensors get distinct, non-overlapping
+// stand-in addresses (a binding must not alias them: run() checks).  run()
+// binds concrete tensors and only tiles and encodes the precomputed graphs --
+// no per-op fusion decision.  Readings: symbols are >= 2 (a symbol is never a
+// broadcast dim); a tiling that exists for the representative shape may not
+// exist for a binding (run() then fails with DVM_ERR_RESOURCE); a value that
+// one graph produces and a later graph reads must be a template output (it
+// needs storage the caller owns).
+// ===========================================================================
+struct TmplVal {
+  int32_t dtype = 0;
+  int nd = 0;
+  int64_t dim[4] = {0, 0, 0, 0};  // >= 0 concrete, < 0 symbol -(k + 1)
+  int op = -1;                    // producing op (-1: an input)
+  int io = -1;                    // input or output index (-1: internal)
+};
+
+struct TmplOp {
+  int32_t op = 0;
+  int n_in = 0;
+  int64_t in[2] = {-1, -1};
+  dvm_attrs at{-1, -1, 0.f};
+  int64_t out = -1;
+  int group = 0;
+};
+
+}  // namespace
+
+struct dvm_template {
+  dvm_context* ctx = nullptr;
+  std::vector<TmplVal> vals;
+  std::vector<TmplOp> ops;
+  std::vector<int64_t> inputs, outputs;  // value ids in binding order
+  int n_groups = 0;
+  bool in_group = false;
+  bool finalized = false;
+  std::vector<int32_t> graph_of_op;
+  int32_t n_graphs = 0;
+  double finalize_us = 0.0;
+  dvm_graph* rg = nullptr;  // the graph runs encode and launch through
+};
+
+namespace {
+
+int64_t sym_dim(const dvm_template* t, int64_t d, const std::vector<int64_t>& rep) {
+  return d >= 0 ? d : rep[(size_t)(-d - 1)];
+}
+
+// One size per symbol: multiples of 8 (matmul operand forms), at least 1032,
+// distinct from one another and from every concrete dim of the template.
+std::vector<int64_t> representatives(const dvm_template* t) {
+  std::vector<int64_t> concrete;
+  int64_t n_sym = 0;
+  for (const TmplVal& v : t->vals)
+    for (int i = 0; i < v.nd; ++i) {
+      if (v.dim[i] >= 0) concrete.push_back(v.dim[i]);
+      else n_sym = std::max(n_sym, -v.dim[i]);
+    }
+  std::vector<int64_t> rep;
+  for (int64_t cand = 1032; (int64_t)rep.size() < n_sym; cand += 8)
+    if (std::find(concrete.begin(), concrete.end(), cand) == concrete.end()) rep.push_back(cand);
+  return rep;
+}
+
+dvm_tensor stand_in(const TmplVal& v, int64_t id, const std::vector<int64_t>& rep, const dvm_template* t) {
+  dvm_tensor x{};
+  x.data = (void*)(uintptr_t)(((uint64_t)id + 1) << 40);
+  x.dtype = v.dtype;
+  x.ndim = v.nd;
+  int64_t acc = 1;
+  for (int i = v.nd - 1; i >= 0; --i) {
+    x.shape[i] = sym_dim(t, v.dim[i], rep);
+    x.stride[i] = acc;
+    acc *= x.shape[i];
+  }
+  return x;
+}
+
 }  // namespace
 
 // ===========================================================================
@@ -2960,6 +3047,326 @@ dvm_status dvm_graph_flush_log(const dvm_graph* g, int32_t* n_ops, int32_t* reas
     if (bytes) bytes[i] = e.bytes;
   }
   return DVM_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Templates (static-graph symbolic fusion)
+// ---------------------------------------------------------------------------
+dvm_status dvm_template_create(dvm_context* ctx, void* stream, dvm_template** out) {
+  if (!ctx || !out) return fail(DVM_ERR_INVALID_ARG, "null argument");
+  dvm_template* t = new (std::nothrow) dvm_template();
+  if (!t) return fail(DVM_ERR_INTERNAL, "out of host memory");
+  t->ctx = ctx;
+  dvm_status st = dvm_graph_create(ctx, stream, &t->rg);
+  if (st != DVM_OK) {
+    delete t;
+    return st;
+  }
+  *out = t;
+  return DVM_OK;
+}
+
+void dvm_template_destroy(dvm_template* t) {
+  if (!t) return;
+  dvm_graph_destroy(t->rg);
+  delete t;
+}
+
+dvm_status dvm_template_graph(dvm_template* t, dvm_graph** out) {
+  if (!t || !out) return fail(DVM_ERR_INVALID_ARG, "null argument");
+  *out = t->rg;
+  return DVM_OK;
+}
+
+dvm_status dvm_template_input(dvm_template* t, int32_t dtype, int32_t ndim, const int64_t* dims, dvm_value* out) {
+  if (!t || !out || (ndim > 0 && !dims)) return fail(DVM_ERR_INVALID_ARG, "null argument");
+  if (t->finalized) return fail(DVM_ERR_INVALID_ARG, "template already finalized");
+  if (ndim < 0 || ndim > 4 || dtype < 0 || dtype > DVM_U8) return fail(DVM_ERR_INVALID_ARG, "bad dtype or ndim");
+  TmplVal v;
+  v.dtype = dtype;
+  v.nd = ndim;
+  for (int i = 0; i < ndim; ++i) v.dim[i] = dims[i];
+  v.io = (int)t->inputs.size();
+  t->inputs.push_back((int64_t)t->vals.size());
+  *out = (dvm_value)t->vals.size();
+  t->vals.push_back(v);
+  return DVM_OK;
+}
+
+dvm_status dvm_template_begin_group(dvm_template* t) {
+  if (!t || t->in_group || t->finalized) return fail(DVM_ERR_INVALID_ARG, "bad template state");
+  t->in_group = true;
+  return DVM_OK;
+}
+
+dvm_status dvm_template_end_group(dvm_template* t) {
+  if (!t || !t->in_group) return fail(DVM_ERR_INVALID_ARG, "no open group");
+  t->in_group = false;
+  ++t->n_groups;
+  return DVM_OK;
+}
+
+dvm_status dvm_template_add_op(dvm_template* t, int32_t op, const dvm_value* in, int32_t n_in, const dvm_attrs* attrs,
+                               int32_t out_dtype, uint32_t flags, dvm_value* out) {
+  if (!t || !out || (n_in > 0 && !in)) return fail(DVM_ERR_INVALID_ARG, "null argument");
+  if (t->finalized) return fail(DVM_ERR_INVALID_ARG, "template already finalized");
+  if (op < 0 || op >= DVM_OP_COUNT || n_in < 1 || n_in > 2) return fail(DVM_ERR_INVALID_ARG, "bad op");
+  if (out_dtype < 0 || out_dtype > DVM_U8) return fail(DVM_ERR_INVALID_ARG, "bad dtype");
+  TmplOp o;
+  o.op = op;
+  o.n_in = n_in;
+  if (attrs) o.at = *attrs;
+  for (int k = 0; k < n_in; ++k) {
+    if (in[k] < 0 || in[k] >= (int64_t)t->vals.size()) return fail(DVM_ERR_INVALID_ARG, "unknown value");
+    o.in[k] = in[k];
+  }
+  // symbolic shape inference: numpy broadcasting where equal symbols match
+  // and a symbol meets only itself or a 1
+  TmplVal v;
+  v.dtype = out_dtype;
+  const TmplVal& a = t->vals[(size_t)o.in[0]];
+  if (op == DVM_OP_MATMUL) {
+    const TmplVal& b = t->vals[(size_t)o.in[1]];
+    if (n_in != 2 || a.nd != 2 || b.nd != 2 || a.dim[1] != b.dim[0]) return fail(DVM_ERR_SHAPE, "matmul shapes");
+    v.nd = 2;
+    v.dim[0] = a.dim[0];
+    v.dim[1] = b.dim[1];
+  } else if (is_reduce(op)) {
+    if (o.at.axis == DVM_AXIS_ALL) {
+      v.nd = 0;
+    } else {
+      if (a.nd == 0) return fail(DVM_ERR_SHAPE, "row reduce of a scalar");
+      v = a;
+      v.dim[v.nd - 1] = 1;
+      v.dtype = out_dtype;
+    }
+  } else if (is_binary(op) && n_in == 2) {
+    const TmplVal& b = t->vals[(size_t)o.in[1]];
+    v.nd = std::max(a.nd, b.nd);
+    for (int i = 0; i < v.nd; ++i) {
+      const int ia = a.nd - v.nd + i, ib = b.nd - v.nd + i;
+      const int64_t da = ia >= 0 ? a.dim[ia] : 1, db = ib >= 0 ? b.dim[ib] : 1;
+      if (da != db && da != 1 && db != 1) return fail(DVM_ERR_SHAPE, "shapes do not broadcast");
+      v.dim[i] = da == 1 ? db : da;
+    }
+  } else {
+    v.nd = a.nd;
+    for (int i = 0; i < a.nd; ++i) v.dim[i] = a.dim[i];
+  }
+  v.op = (int)t->ops.size();
+  if (flags & DVM_OUT_LIVE) {
+    v.io = (int)t->outputs.size();
+    t->outputs.push_back((int64_t)t->vals.size());
+  }
+  o.out = (int64_t)t->vals.size();
+  o.group = t->in_group ? t->n_groups : t->n_groups++;
+  t->ops.push_back(o);
+  *out = (dvm_value)t->vals.size();
+  t->vals.push_back(v);
+  return DVM_OK;
+}
+
+dvm_status dvm_template_finalize(dvm_template* t, int32_t* n_graphs) {
+  if (!t) return fail(DVM_ERR_INVALID_ARG, "null template");
+  if (t->in_group) return fail(DVM_ERR_INVALID_ARG, "group still open");
+  if (t->finalized) return fail(DVM_ERR_INVALID_ARG, "template already finalized");
+  const auto t0 = std::chrono::steady_clock::now();
+  const std::vector<int64_t> rep = representatives(t);
+  // replay the groups through the streaming fuser of an encode-only graph on
+  // stand-in tensors; its flush log is the partition
+  dvm_context* ec = nullptr;
+  dvm_status st = dvm_context_create(-1, &ec);
+  if (st != DVM_OK) return st;
+  dvm_graph* fg = nullptr;
+  st = dvm_graph_create(ec, nullptr, &fg);
+  std::vector<dvm_value> h(t->vals.size(), -1);
+  std::vector<int> last_group(t->vals.size(), -1);
+  for (const TmplOp& o : t->ops)
+    for (int k = 0; k < o.n_in; ++k) last_group[(size_t)o.in[k]] = o.group;
+  for (size_t i = 0; st == DVM_OK && i < t->vals.size(); ++i)
+    if (t->vals[i].op < 0) {
+      const dvm_tensor x = stand_in(t->vals[i], (int64_t)i, rep, t);
+      st = dvm_graph_input(fg, &x, &h[i]);
+    }
+  for (size_t i = 0; st == DVM_OK && i < t->ops.size();) {
+    const int grp = t->ops[i].group;
+    st = dvm_graph_begin_group(fg);
+    for (; st == DVM_OK && i < t->ops.size() && t->ops[i].group == grp; ++i) {
+      const TmplOp& o = t->ops[i];
+      const dvm_tensor x = stand_in(t->vals[(size_t)o.out], o.out, rep, t);
+      dvm_value in[2] = {h[(size_t)o.in[0]], o.n_in > 1 ? h[(size_t)o.in[1]] : 0};
+      st = dvm_graph_add_op(fg, o.op, in, o.n_in, &o.at, &x, t->vals[(size_t)o.out].io >= 0 ? DVM_OUT_LIVE : 0u,
+                            &h[(size_t)o.out]);
+    }
+    if (st != DVM_OK) break;
+    int32_t fl = 0;
+    st = dvm_graph_end_group(fg, &fl);
+    // internal values are released after the group that reads them last
+    for (size_t v = 0; st == DVM_OK && v < t->vals.size(); ++v)
+      if (t->vals[v].op >= 0 && t->vals[v].io < 0 && h[v] >= 0 &&
+          (last_group[v] == grp || (last_group[v] < 0 && t->ops[(size_t)t->vals[v].op].group == grp)))
+        st = dvm_graph_release(fg, h[v]);
+  }
+  if (st == DVM_OK) st = dvm_graph_flush_launch(fg, nullptr);
+  if (st == DVM_OK) {
+    // the partition: graphs are runs of whole groups, in order
+    t->graph_of_op.assign(t->ops.size(), -1);
+    size_t i = 0;
+    int32_t gi = 0;
+    for (const dvm_graph::LogEntry& e : fg->flush_log) {
+      for (int32_t k = 0; k < e.ops && i < t->ops.size(); ++k) t->graph_of_op[i++] = gi;
+      ++gi;
+    }
+    if (i != t->ops.size()) st = fail(DVM_ERR_INTERNAL, "partition covers %zu of %zu ops", i, t->ops.size());
+    t->n_graphs = gi;
+    // a value read by a later graph than the one computing it needs storage
+    for (size_t k = 0; st == DVM_OK && k < t->ops.size(); ++k)
+      for (int q = 0; q < t->ops[k].n_in; ++q) {
+        const TmplVal& v = t->vals[(size_t)t->ops[k].in[q]];
+        if (v.op >= 0 && v.io < 0 && t->graph_of_op[(size_t)v.op] != t->graph_of_op[k])
+          st = fail(DVM_ERR_RESOURCE, "value %lld crosses fused graphs: make it a template output",
+                    (long long)t->ops[k].in[q]);
+      }
+  }
+  dvm_graph_destroy(fg);
+  dvm_context_destroy(ec);
+  if (st != DVM_OK) return st;
+  t->finalized = true;
+  t->finalize_us = std::chrono::duration<double, std::micro>(std::chrono::steady_clock::now() - t0).count();
+  if (n_graphs) *n_graphs = t->n_graphs;
+  return DVM_OK;
+}
+
+dvm_status dvm_template_partition(const dvm_template* t, int32_t* graph_of_op, size_t* n_ops, double* finalize_us) {
+  if (!t || !n_ops) return fail(DVM_ERR_INVALID_ARG, "null argument");
+  if (!t->finalized) return fail(DVM_ERR_INVALID_ARG, "template not finalized");
+  const size_t cap = *n_ops;
+  *n_ops = t->ops.size();
+  if (graph_of_op) std::copy(t->graph_of_op.begin(), t->graph_of_op.begin() + std::min(cap, t->ops.size()), graph_of_op);
+  if (finalize_us) *finalize_us = t->finalize_us;
+  return DVM_OK;
+}
+
+dvm_status dvm_template_run(dvm_template* t, const dvm_tensor* inputs, int32_t n_inputs, const dvm_tensor* outputs,
+                            int32_t n_outputs, int32_t* launched) {
+  if (launched) *launched = 0;
+  if (!t || (n_inputs && !inputs) || (n_outputs && !outputs)) return fail(DVM_ERR_INVALID_ARG, "null argument");
+  if (!t->finalized) return fail(DVM_ERR_INVALID_ARG, "template not finalized");
+  if (n_inputs != (int32_t)t->inputs.size() || n_outputs != (int32_t)t->outputs.size())
+    return fail(DVM_ERR_INVALID_ARG, "template takes %zu inputs and %zu outputs", t->inputs.size(), t->outputs.size());
+  dvm_graph* g = t->rg;
+  if (g->in_group || g->branch || !g->buf.empty()) return fail(DVM_ERR_INVALID_ARG, "the run graph is busy");
+  FuseTimer ft(g);
+  // bind the symbols and check every bound tensor against its symbolic shape
+  std::vector<int64_t> sym;
+  auto bind = [&](const TmplVal& v, const dvm_tensor& x) -> dvm_status {
+    dvm_status c = check_tensor(&x);
+    if (c != DVM_OK) return c;
+    if (x.dtype != v.dtype || x.ndim != v.nd) return fail(DVM_ERR_SHAPE, "bound tensor: dtype or rank");
+    for (int i = 0; i < v.nd; ++i) {
+      const int64_t d = v.dim[i];
+      if (d >= 0) {
+        if (x.shape[i] != d) return fail(DVM_ERR_SHAPE, "bound tensor: dim %d is %lld, not %lld", i, (long long)x.shape[i], (long long)d);
+        continue;
+      }
+      const size_t k = (size_t)(-d - 1);
+      if (sym.size() <= k) sym.resize(k + 1, -1);
+      if (sym[k] < 0) sym[k] = x.shape[i];
+      else if (sym[k] != x.shape[i]) return fail(DVM_ERR_SHAPE, "symbol %zu bound to %lld and %lld", k, (long long)sym[k], (long long)x.shape[i]);
+    }
+    return DVM_OK;
+  };
+  for (int32_t i = 0; i < n_inputs; ++i) {
+    dvm_status c = bind(t->vals[(size_t)t->inputs[(size_t)i]], inputs[i]);
+    if (c != DVM_OK) return c;
+  }
+  for (int32_t i = 0; i < n_outputs; ++i) {
+    dvm_status c = bind(t->vals[(size_t)t->outputs[(size_t)i]], outputs[i]);
+    if (c != DVM_OK) return c;
+    if (!outputs[i].data && numel_of(outputs[i]) > 0) return fail(DVM_ERR_INVALID_ARG, "output %d has no storage", i);
+  }
+  // the partition assumed no aliasing: no output overlaps an input or another output
+  auto rng = [](const dvm_tensor& x) { return Range{(uintptr_t)x.data, (uint64_t)extent_bytes(x)}; };
+  for (int32_t i = 0; i < n_outputs; ++i) {
+    std::vector<Range> o{rng(outputs[i])}, others;
+    for (int32_t j = 0; j < n_inputs; ++j) others.push_back(rng(inputs[j]));
+    for (int32_t j = 0; j < n_outputs; ++j)
+      if (j != i) others.push_back(rng(outputs[j]));
+    if (overlaps(o, others)) return fail(DVM_ERR_INVALID_ARG, "output %d aliases another bound tensor", i);
+  }
+  // values of this run in the run graph
+  std::vector<int64_t> slot(t->vals.size(), -1);
+  for (size_t i = 0; i < t->vals.size(); ++i) {
+    const TmplVal& tv = t->vals[i];
+    const int64_t s = new_slot(g);
+    slot[i] = s;
+    Val& v = g->vals[(size_t)s];
+    if (tv.op < 0) {
+      v.kind = VK_INPUT;
+      v.t = inputs[tv.io];
+      v.stored = true;
+    } else {
+      v.kind = VK_OP;
+      const TmplOp& o = t->ops[(size_t)tv.op];
+      int64_t ins[2] = {slot[(size_t)o.in[0]], o.n_in > 1 ? slot[(size_t)o.in[1]] : -1};
+      Shape sh;
+      if (!infer(g, o.op, ins, o.n_in, &o.at, &sh)) return fail(DVM_ERR_SHAPE, "op %d: shapes", tv.op);
+      if (tv.io >= 0) {
+        v.t = outputs[tv.io];
+        v.live = true;
+      } else {
+        v.t = dvm_tensor{};
+        v.t.dtype = tv.dtype;
+        v.t.ndim = sh.nd;
+        for (int d = 0; d < sh.nd; ++d) v.t.shape[d] = sh.d[d];
+        v.released = true;  // internal: never stored (it stays inside its graph)
+      }
+    }
+    g->vals[(size_t)s].shape = shape_of(g->vals[(size_t)s].t);
+  }
+  // the precomputed graphs, in order: tiling and encoding only
+  dvm_status st = DVM_OK;
+  int32_t any = 0;
+  for (int32_t gi = 0; st == DVM_OK && gi < t->n_graphs; ++gi) {
+    for (size_t k = 0; k < t->ops.size(); ++k) {
+      if (t->graph_of_op[k] != gi) continue;
+      const TmplOp& o = t->ops[k];
+      OpRec r;
+      r.op = o.op;
+      r.n_in = o.n_in;
+      for (int q = 0; q < o.n_in; ++q) {
+        r.in[q] = slot[(size_t)o.in[q]];
+        g->vals[(size_t)r.in[q]].uses++;
+      }
+      r.axis = o.at.axis;
+      r.scalar_pos = o.at.scalar_pos;
+      r.scalar = o.at.scalar;
+      r.out = slot[(size_t)o.out];
+      g->vals[(size_t)r.out].pending = true;
+      g->buf.push_back(r);
+      g->stats.ops++;
+    }
+    int32_t l = 0;
+    st = flush_launch(g, FR_EXPLICIT, &l);
+    any |= l;
+  }
+  if (st == DVM_OK) {
+    int32_t l = 0;
+    st = launch_stack(g, &l);
+    any |= l;
+  } else {
+    std::vector<OpRec> left;
+    left.swap(g->buf);
+    retire(g, left, false);
+  }
+  for (int64_t s : slot) {
+    Val& v = g->vals[(size_t)s];
+    v.released = true;
+    v.pending = false;
+    maybe_recycle(g, s);
+  }
+  if (launched) *launched = any;
+  return st;
 }
 
 dvm_status dvm_graph_stats(const dvm_graph* g, dvm_stats* out) {

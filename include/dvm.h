@@ -266,6 +266,44 @@ dvm_status dvm_graph_set_stacking(dvm_graph* g, int32_t max_segments);
  * DVM_ERR_RESOURCE when the words exceed the kernel argument. */
 dvm_status dvm_program_stack(const dvm_program* const* programs, size_t n, dvm_program** out);
 
+/* Static-graph symbolic fusion (DVM review page, section 5.2, static-graph
+ * fusion): a template is an op graph recorded once over symbolic dims;
+ * dvm_template_finalize decides its fusion partition once (the streaming
+ * fuser's rules, applied to shapes in which each symbol is one size shared by
+ * all its occurrences and distinct from every other dim), and every
+ * dvm_template_run binds concrete tensors and only tiles, encodes and
+ * launches the precomputed graphs, with no per-op fusion decision.
+ *
+ * dims: >= 0 a concrete size, < 0 the symbol -(dims[i] + 1).  Symbols stand
+ * for sizes >= 2.  Values are template-scoped handles.  Ops are added as with
+ * dvm_graph_add_op but name their output dtype; DVM_OUT_LIVE makes the value a
+ * template output (bound at run, in the order the outputs were added);
+ * every other op value is internal and never stored, so a value one fused
+ * graph computes and a later one reads must be an output (finalize fails with
+ * DVM_ERR_RESOURCE otherwise).  Groups as for graphs.
+ *
+ * dvm_template_run: inputs[] and outputs[] in the order added; their dims
+ * must match the template's (concrete dims exactly, each symbol one size);
+ * outputs must not overlap inputs or each other (DVM_ERR_INVALID_ARG).  The
+ * programs launch on the template's graph (dvm_template_graph: its stream,
+ * stats, flush log, stacking; on an encode-only context its programs wait
+ * for dvm_graph_take_program); DVM_ERR_RESOURCE when a bound shape has no
+ * feasible tiling.  dvm_template_partition: the graph index of every op and
+ * the host time finalize took. */
+typedef struct dvm_template dvm_template;
+dvm_status dvm_template_create(dvm_context* ctx, void* stream, dvm_template** out);
+void dvm_template_destroy(dvm_template* t);
+dvm_status dvm_template_graph(dvm_template* t, dvm_graph** out);
+dvm_status dvm_template_input(dvm_template* t, int32_t dtype, int32_t ndim, const int64_t* dims, dvm_value* out);
+dvm_status dvm_template_begin_group(dvm_template* t);
+dvm_status dvm_template_end_group(dvm_template* t);
+dvm_status dvm_template_add_op(dvm_template* t, int32_t op, const dvm_value* in, int32_t n_in, const dvm_attrs* attrs,
+                               int32_t out_dtype, uint32_t flags, dvm_value* out);
+dvm_status dvm_template_finalize(dvm_template* t, int32_t* n_graphs);
+dvm_status dvm_template_partition(const dvm_template* t, int32_t* graph_of_op, size_t* n_ops, double* finalize_us);
+dvm_status dvm_template_run(dvm_template* t, const dvm_tensor* inputs, int32_t n_inputs, const dvm_tensor* outputs,
+                            int32_t n_outputs, int32_t* launched);
+
 /* Device-side control flow (the if-else of the DVM review page's dynamic
  * control-flow workload, section 6.2; the MindSpore summary page, section 3.2,
  * flushes at such points): ops added between begin_branch and else_branch
