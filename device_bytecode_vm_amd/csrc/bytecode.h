@@ -119,10 +119,14 @@ __host__ __device__ constexpr int mm_lds_bytes(int tm, int tn) {
 //    by the same lane, which then issues the next tile's load into the same
 //    bytes (one buffer: the read completes before the refill is issued);
 //  * invariant slot: an operand that is the same for every tile, held as fp32,
-//    8 elements (32 bytes) per lane and chunk.  A slot shared by the row groups
-//    (the operand does not vary along rows) holds one row: NVK x g x 32
-//    bytes, indexed by the lane's position in its row; otherwise NVK x T x 32
-//    bytes, indexed by the lane.
+//    8 elements (32 bytes) per index and chunk, in 2 x NVK planes of 16-byte
+//    cells: index i's elements 4h..4h+3 of chunk j sit at ((2j + h) * stride
+//    + i) * 16.  A slot shared by the row groups (the operand does not vary
+//    along rows) holds one row: stride g, indexed by the lane's position in
+//    its row; otherwise stride T, indexed by the lane.  An fp32 operand with
+//    contiguous whole-chunk columns is staged with direct-to-LDS loads when
+//    each wave's indices are 64 consecutive values (lane-private slots, or
+//    g a multiple of 64); others go through registers.
 // The budget keeps two workgroups resident per compute unit (160 KB of LDS).
 constexpr uint32_t LDS_BUDGET = 76u * 1024u;
 // The wide build keeps its cross-wave reduction buffers (and the reduce-all

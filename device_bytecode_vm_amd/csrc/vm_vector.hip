@@ -672,12 +672,18 @@ __device__ __forceinline__ void pf_read(Ch& d, const char* slot, const Geo& G, i
 }
 
 // Invariant slot addressing: a shared slot is indexed by the lane's position
-// in its row (stride g), a lane-private one by the lane (stride T).
+// in its row (stride g), a lane-private one by the lane (stride T).  The slot
+// holds 2 NVK planes of stride x 16 bytes: plane 2j + h carries elements
+// 4h..4h+3 of every index's chunk j, so the 64 lanes of a wave touch 64
+// consecutive 16-byte cells (no bank conflicts, and a direct-to-LDS load of
+// one wave fills exactly the cells its lanes read back).
 __device__ __forceinline__ int inv_base(KW* W, uint32_t k, const Geo& G, const Lane& L, int* stride) {
   const bool shared = W[H_INV_SHARED0 + k] != 0;
   *stride = shared ? G.g : T_LANES;
   return shared ? L.lane : L.tid;
 }
+
+__device__ __forceinline__ int inv_cell(int j, int h, int stride, int idx) { return ((2 * j + h) * stride + idx) * 16; }
 
 __device__ __forceinline__ void inv_write(const Ch& c, char* slot, const Geo& G, int idx, int stride) {
 #pragma unroll
@@ -686,8 +692,42 @@ __device__ __forceinline__ void inv_write(const Ch& c, char* slot, const Geo& G,
       const V8 x = c.c[j];
       const f4 a = {x[0], x[1], x[2], x[3]};
       const f4 b = {x[4], x[5], x[6], x[7]};
-      *(f4*)(slot + (j * stride + idx) * 32) = a;
-      *(f4*)(slot + (j * stride + idx) * 32 + 16) = b;
+      *(f4*)(slot + inv_cell(j, 0, stride, idx)) = a;
+      *(f4*)(slot + inv_cell(j, 1, stride, idx)) = b;
+    }
+  }
+}
+
+// Stages an fp32 invariant operand whose columns are contiguous and whole
+// chunks straight into its slot with direct-to-LDS loads (no registers, no
+// wait here: the prologue ends with one wait for every load it issued).
+// Needs each wave's indices to be 64 consecutive values: a lane-private slot,
+// or a shared one whose rows span whole waves (g a multiple of 64).
+__device__ __forceinline__ bool inv_direct_ok(const ArgD& a, const Geo& G, const Tile& tl, int stride) {
+  return a.dt == DT_F32 && (a.fl & AF_VEC) && a.sc == 1 && (tl.tce & (VEC - 1)) == 0 &&
+         (stride == T_LANES || (G.g & 63) == 0);
+}
+
+__device__ __forceinline__ void inv_issue(char* slot, const ArgD& a, const Geo& G, const Tile& tl, const Lane& L,
+                                          int idx, int stride, bool any_row) {
+  const u4 rs = tile_rsrc_words(a, tl, 4);
+  const bool rok = any_row | L.rok;
+  const int roff = L.row * (int)a.sr;
+  // the wave's first index (its lanes hold it and the 63 after it)
+  const int idx0 = __builtin_amdgcn_readfirstlane(idx);
+  const uint32_t base = (uint32_t)(uintptr_t)(lds_void*)slot;
+#pragma unroll
+  for (int j = 0; j < NVK; ++j) {
+    const int ct = (j * G.g + L.lane) * VEC;
+    const int off = lane_off(rok & (ct + VEC <= tl.tce), (roff + ct) * 4);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const uint32_t dst = __builtin_amdgcn_readfirstlane(base + (uint32_t)inv_cell(j, h, stride, idx0));
+      const int o = off == OOB ? OOB : off + 16 * h;
+      asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                   :
+                   : "s"(dst), "v"(o), "s"(rs)
+                   : "memory", "m0");
     }
   }
 }
@@ -696,8 +736,8 @@ __device__ __forceinline__ void inv_read(Ch& c, const char* slot, const Geo& G, 
 #pragma unroll
   for (int j = 0; j < NVK; ++j) {
     const int jj = j;
-    const f4 a = *(const f4*)(slot + (jj * stride + idx) * 32);
-    const f4 b = *(const f4*)(slot + (jj * stride + idx) * 32 + 16);
+    const f4 a = *(const f4*)(slot + inv_cell(jj, 0, stride, idx));
+    const f4 b = *(const f4*)(slot + inv_cell(jj, 1, stride, idx));
     V8 r;
     r[0] = a.x; r[1] = a.y; r[2] = a.z; r[3] = a.w;
     r[4] = b.x; r[5] = b.y; r[6] = b.z; r[7] = b.w;
@@ -1078,8 +1118,15 @@ __device__ __forceinline__ void vm_main(const Seg& sg, float (*s_red)[T_LANES / 
       }
     }
     if (pc >= pc_end) {
-      if (in_pro) in_pro = false;
-      else tile += t_step;
+      if (in_pro) {
+        // the prologue's loads (direct-to-LDS invariant staging and the first
+        // tile's prefetch) were issued back to back; one wait covers them all
+        // before any body instruction reads a slot
+        in_pro = false;
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      } else {
+        tile += t_step;
+      }
       if (tile >= t_end) break;
       tl = make_tile(G, tile);
       pc = body_begin;
@@ -1238,8 +1285,8 @@ __device__ __forceinline__ void vm_main(const Seg& sg, float (*s_red)[T_LANES / 
 #pragma unroll
         for (int j = 0; j < NVK; ++j) {
           const int jj = j;
-          const f4 a0 = *(const f4*)(b1 + (jj * s1 + i1) * 32), a1 = *(const f4*)(b1 + (jj * s1 + i1) * 32 + 16);
-          const f4 c0 = *(const f4*)(b2 + (jj * s2 + i2) * 32), c1 = *(const f4*)(b2 + (jj * s2 + i2) * 32 + 16);
+          const f4 a0 = *(const f4*)(b1 + inv_cell(jj, 0, s1, i1)), a1 = *(const f4*)(b1 + inv_cell(jj, 1, s1, i1));
+          const f4 c0 = *(const f4*)(b2 + inv_cell(jj, 0, s2, i2)), c1 = *(const f4*)(b2 + inv_cell(jj, 1, s2, i2));
           const float sc[VEC] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
           const float sh[VEC] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
 #pragma unroll
@@ -1332,8 +1379,13 @@ __device__ __forceinline__ void vm_main(const Seg& sg, float (*s_red)[T_LANES / 
         const uint32_t k = f_dst(w0) & 1u;
         int stride;
         const int idx = inv_base(W, k, G, L, &stride);
+        const ArgD a = ARG;
+        if (inv_direct_ok(a, G, tl, stride)) {
+          inv_issue(S.inv(k), a, G, tl, L, idx, stride, stride != T_LANES);
+          break;
+        }
         Ch tmp;
-        load_any(tmp, ARG, G, tl, L, false, stride != T_LANES);  // reused by every tile: default policy
+        load_any(tmp, a, G, tl, L, false, stride != T_LANES);  // reused by every tile: default policy
         // every chunk's load has returned before the handler ends, the ones
         // past nv (not written to LDS) included: a load left in flight would
         // make later writes of its registers wait on the vector-memory
