@@ -56,6 +56,8 @@ def parse():
     ap.add_argument("--stream-steps", type=int, default=2, help="timed op-stream steps (seeds 0, 1, ...)")
     ap.add_argument("--stacking", type=int, default=7,
                     help="independent graphs packed into one launch (1: every graph launches alone)")
+    ap.add_argument("--stack-order", default="spatial", choices=["spatial", "temporal"],
+                    help="stacked segments on their own workgroups, or in sequence on every workgroup")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=6.0, help="CPU work per baseline leg")
     ap.add_argument("--no-decode-split", action="store_true")
@@ -359,7 +361,7 @@ def layernorm_bench(args):
         g.flush_launch()
 
     g = dvm.Graph(ctx, stream)
-    g.set_stacking(args.stacking)
+    g.set_stacking(args.stacking, args.stack_order == "temporal")
     for _ in range(args.warmup):
         one_step(g)
     torch.cuda.synchronize()
@@ -408,7 +410,7 @@ def layernorm_bench(args):
                      "frac": round(kern_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "kernel": "dvm_vm_vector_wide + dvm_vm_vector", "launches_per_step": launches / args.steps,
                      "graphs_stacked_per_step": (s1["stacked"] - s0["stacked"]) / args.steps,
-                     "stacking": args.stacking,
+                     "stacking": args.stacking, "stack_order": args.stack_order,
                      "launches_by_kernel": {
                          "dvm_vm_vector_wide": sum(1 for p in progs if p.header()["kernel_type"] == 2),
                          "dvm_vm_vector": sum(1 for p in progs if p.header()["kernel_type"] == 0)},
@@ -692,7 +694,7 @@ def stream_bench(args):
     bf = dict(dtype="bf16")
     w = W.device_normal((H,), seed=25, mu=1.0, sd=0.1)
     g = dvm.Graph(ctx, stream)
-    g.set_stacking(args.stacking)
+    g.set_stacking(args.stacking, args.stack_order == "temporal")
 
     def run_step(seed):
         T, TKV, motifs = W.stream_step(seed, args.motifs)
@@ -756,6 +758,7 @@ def stream_bench(args):
             "graphs_per_step": sum(r["graphs"] for r in runs) / n,
             "launches_per_step": sum(r["launches"] for r in runs) / n,
             "graphs_stacked_per_step": sum(r["stacked"] for r in runs) / n, "stacking": args.stacking,
+            "stack_order": args.stack_order,
             "ops_per_step": sum(r["ops"] for r in runs) / n,
             "flush_reasons_per_step": {k: sum(r["reasons"][k] for r in runs) / n for k in runs[0]["reasons"]},
             "encode_us": encode_stats(log),

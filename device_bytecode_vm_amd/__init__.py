@@ -181,11 +181,13 @@ class Program:
             pass
 
 
-def stack_programs(programs) -> "Program":
-    """dvm_program_stack: one launch of 2..7 independent VECTOR programs."""
+def stack_programs(programs, temporal: bool = False) -> "Program":
+    """dvm_program_stack (dvm_program_stack_temporal if temporal): one launch
+    of 2..7 independent VECTOR programs."""
     arr = (C.c_void_p * len(programs))(*[p.h.value if isinstance(p.h, C.c_void_p) else p.h for p in programs])
     q = C.c_void_p()
-    check(lib.dvm_program_stack(arr, len(programs), C.byref(q)))
+    fn = lib.dvm_program_stack_temporal if temporal else lib.dvm_program_stack
+    check(fn(arr, len(programs), C.byref(q)))
     prog = Program(q, programs[0].ctx)
     for p in programs:
         prog._keep.extend(p._keep)
@@ -312,10 +314,12 @@ class Graph:
         prog._keep = keep
         return prog
 
-    def set_stacking(self, max_segments: int):
+    def set_stacking(self, max_segments: int, temporal: bool = False):
         """Pack up to max_segments independent encoded graphs into one launch
-        (1: launch every graph when it is flushed)."""
+        (1: launch every graph when it is flushed); temporal: the launch runs
+        the segments in sequence on every workgroup (dvm_graph_set_stack_order)."""
         check(lib.dvm_graph_set_stacking(self.h, int(max_segments)))
+        check(lib.dvm_graph_set_stack_order(self.h, 1 if temporal else 0))
 
     # -- device-side control flow -----------------------------------------
     def begin_branch(self, cond: "Value", threshold: float = 0.0):

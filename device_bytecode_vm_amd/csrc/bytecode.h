@@ -306,6 +306,14 @@ constexpr uint32_t VMC_MAX = 63;
 // are even (instructions are fetched as 8-byte pairs) and each segment is
 // followed by PAD_WORDS spare words.
 constexpr uint32_t STACK_MAGIC = 0x4b545344u;  // "DSTK"
+// Temporal stacking (the same section: different graphs' tiles run on the same
+// core in sequence): word 0 TSTACK_MAGIC, the same directory layout with
+// each segment's second word the index of its first tile in one tile space
+// that numbers the segments' tiles in order (its first tile = the sum of the
+// earlier segments' block_dim).  A launch of G workgroups runs tile u of that
+// space on workgroup u mod G, so every workgroup walks the segments in order;
+// a barrier separates its segments.
+constexpr uint32_t TSTACK_MAGIC = 0x4b535454u;  // "TTSK"
 constexpr int S_NSEG = 1;
 constexpr int S_DIR = 2;                        // (offset, first workgroup) pairs from here
 constexpr int MAX_SEGS = 7;

@@ -474,6 +474,7 @@ struct dvm_graph {
   std::vector<int32_t> remap;  // slot -> local index while a local view is built (-1 otherwise)
   // stacking: up to stack_max independent programs wait here and launch as one
   int stack_max = 1;
+  bool stack_temporal = false;  // launch the stack temporally (segments in sequence per workgroup)
   std::vector<dvm_program*> stack;
   // a branch being captured: 1 then-ops, 2 else-ops (0 none)
   int branch = 0;
@@ -2246,8 +2247,11 @@ bool fits_stack(const dvm_graph* g, const dvm_program* p) {
 }
 
 // One program from 2..MAX_SEGS programs of one VECTOR build: the directory,
-// then each program's words, with the workgroup ranges in launch order.
-dvm_status build_stack(const dvm_program* const* ps, size_t n, dvm_program** out) {
+// then each program's words.  Spatial: each segment keeps its workgroups, in
+// launch order.  Temporal: one tile space over the segments in order, run by
+// min(G, total tiles) workgroups (tile u on workgroup u mod grid), each
+// walking the segments in sequence.
+dvm_status build_stack(const dvm_program* const* ps, size_t n, bool temporal, dvm_program** out) {
   *out = nullptr;
   if (n < 2 || n > (size_t)MAX_SEGS) return fail(DVM_ERR_INVALID_ARG, "a stack holds 2 to %d programs", MAX_SEGS);
   const uint32_t kt = ps[0]->prog.w[H_KTYPE];
@@ -2264,16 +2268,17 @@ dvm_status build_stack(const dvm_program* const* ps, size_t n, dvm_program** out
   dvm_program* q = new (std::nothrow) dvm_program();
   if (!q) return fail(DVM_ERR_INTERNAL, "out of host memory");
   uint32_t* W = q->prog.w;
-  W[0] = STACK_MAGIC;
+  W[0] = temporal ? TSTACK_MAGIC : STACK_MAGIC;
   W[S_NSEG] = (uint32_t)n;
-  uint32_t off = STACK_DIR_WORDS, wg = 0;
+  uint32_t off = STACK_DIR_WORDS, wg = 0, tiles = 0;
   for (size_t i = 0; i < n; ++i) {
     const dvm_program* p = ps[i];
     W[S_DIR + 2 * i] = off;
-    W[S_DIR + 2 * i + 1] = wg;
+    W[S_DIR + 2 * i + 1] = temporal ? tiles : wg;
     std::copy(p->prog.w, p->prog.w + p->n_words, W + off);
     off += p->n_words + PAD_WORDS;
     wg += p->grid_launch;
+    tiles += p->prog.w[H_BLOCK_DIM];
     q->lds = std::max(q->lds, p->lds);
     q->bytes += p->bytes;
     q->n_instr += p->n_instr;
@@ -2282,7 +2287,7 @@ dvm_status build_stack(const dvm_program* const* ps, size_t n, dvm_program** out
   }
   q->segments = (uint32_t)n;
   q->n_words = off;
-  q->grid_launch = wg;
+  q->grid_launch = temporal ? (uint32_t)std::min<int64_t>(tiling::G, tiles) : wg;
   q->R = ps[0]->R;
   q->C = ps[0]->C;
   const dvm_status v = checked(q);
@@ -2301,7 +2306,7 @@ dvm_status launch_stack(dvm_graph* g, int32_t* launched) {
   if (st.empty()) return DVM_OK;
   if (st.size() == 1) return run_program(g, st[0], launched);
   dvm_program* q = nullptr;
-  dvm_status e = build_stack(st.data(), st.size(), &q);
+  dvm_status e = build_stack(st.data(), st.size(), g->stack_temporal, &q);
   for (dvm_program* p : st) delete p;
   if (e != DVM_OK) return e;
   g->stats.stacked += st.size();
@@ -2900,9 +2905,22 @@ dvm_status dvm_graph_set_stacking(dvm_graph* g, int32_t max_segments) {
   return st;
 }
 
+dvm_status dvm_graph_set_stack_order(dvm_graph* g, int32_t temporal) {
+  if (!g) return fail(DVM_ERR_INVALID_ARG, "null graph");
+  if (temporal != 0 && temporal != 1) return fail(DVM_ERR_INVALID_ARG, "stack order %d is neither 0 nor 1", temporal);
+  dvm_status st = launch_stack(g, nullptr);
+  g->stack_temporal = temporal != 0;
+  return st;
+}
+
 dvm_status dvm_program_stack(const dvm_program* const* programs, size_t n, dvm_program** out) {
   if (!programs || !out) return fail(DVM_ERR_INVALID_ARG, "null argument");
-  return build_stack(programs, n, out);
+  return build_stack(programs, n, false, out);
+}
+
+dvm_status dvm_program_stack_temporal(const dvm_program* const* programs, size_t n, dvm_program** out) {
+  if (!programs || !out) return fail(DVM_ERR_INVALID_ARG, "null argument");
+  return build_stack(programs, n, true, out);
 }
 
 dvm_status dvm_sync(dvm_graph* g) {

@@ -342,7 +342,11 @@ bool verify_words(const uint32_t* W, uint32_t n_words, std::string* err) {
     *err = "program longer than the kernel argument";
     return false;
   }
-  if (W[0] != STACK_MAGIC) return verify_one(W, n_words, err);
+  if (W[0] != STACK_MAGIC && W[0] != TSTACK_MAGIC) return verify_one(W, n_words, err);
+  // spatial stacks list each segment's first workgroup, temporal ones its
+  // first tile in the stack's tile space: both the running sum over the
+  // segments before it
+  const bool temporal = W[0] == TSTACK_MAGIC;
   const uint32_t n = W[S_NSEG];
   if (n < 2 || n > (uint32_t)MAX_SEGS) {
     *err = "stack directory: segment count";
@@ -352,7 +356,7 @@ bool verify_words(const uint32_t* W, uint32_t n_words, std::string* err) {
   for (uint32_t s = 0; s < n; ++s) {
     const uint32_t off = W[S_DIR + 2 * s], first = W[S_DIR + 2 * s + 1];
     if ((off & 1u) || off < prev_end || off + HDR_WORDS > n_words || first != wg) {
-      *err = "stack directory: segment " + std::to_string(s) + " offset or first workgroup";
+      *err = "stack directory: segment " + std::to_string(s) + (temporal ? " offset or first tile" : " offset or first workgroup");
       return false;
     }
     const uint32_t* S = W + off;
@@ -367,7 +371,7 @@ bool verify_words(const uint32_t* W, uint32_t n_words, std::string* err) {
     }
     const uint32_t seg_end = (S[H_FLAGS] & HF_BRANCH) ? S[H_ALT_END] : S[H_BODY_END];
     prev_end = off + seg_end + PAD_WORDS;
-    wg += S[H_GRID];
+    wg += temporal ? S[H_BLOCK_DIM] : S[H_GRID];
   }
   return true;
 }

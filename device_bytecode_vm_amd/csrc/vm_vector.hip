@@ -1003,13 +1003,25 @@ __device__ __forceinline__ Ch& treg(Regs& r) {
 // execute (the handler, row-register runs inside it included) and tile
 // changes, written per workgroup at the end.  The product kernel is the
 // PROF = false instance, with no counter reads.
-// The program this workgroup runs and its place in that program's grid: the
-// whole kernel argument, or in a stacked launch the segment whose workgroup
-// range holds blockIdx.x (wave-uniform: every value comes from scalar loads).
+// The program this workgroup runs and its place in that program's tiles:
+// the first tile b and the stride grid (tiles b, b + grid, ... below
+// block_dim).  The whole kernel argument, or in a spatially stacked launch the
+// segment whose workgroup range holds blockIdx.x, with b and grid relative
+// to that range (wave-uniform: every value comes from scalar loads).
 struct Seg {
   KW* W;
   uint32_t b, grid;
 };
+
+// Temporally stacked launch: the segments' tiles form one space, numbered in
+// segment order from the directory's tile bases; workgroup b runs the tiles
+// b, b + G, b + 2G, ... of that space (G = gridDim.x), i.e. in segment s the
+// local tiles congruent to b - base_s modulo G, segment after segment.
+__device__ __forceinline__ Seg temporal_segment(KW* K, uint32_t s) {
+  const uint32_t G = gridDim.x;
+  const uint32_t base = K[S_DIR + 2 * s + 1] % G;
+  return Seg{K + K[S_DIR + 2 * s], (blockIdx.x + G - base) % G, G};
+}
 
 __device__ __forceinline__ Seg segment_of() {
   KW* K = (KW*)__builtin_amdgcn_kernarg_segment_ptr();
@@ -1476,38 +1488,57 @@ __device__ __forceinline__ void vm_main(const Seg& sg, float (*s_red)[T_LANES / 
 }
 
 // Cross-wave reduction buffers and the reduce-all flag: static arrays in the
-// standard build, a reserved part of the dynamic area in the wide build.
+// standard build, a reserved part of each program's dynamic area in the wide
+// build (its offset is a header word, so it is looked up per segment).
 #ifdef DVM_WIDE
-#define DVM_RED_BUFFERS(W)                                                                             \
-  extern __shared__ __attribute__((aligned(16))) char dlds[];                                          \
+#define DVM_LDS_DECL extern __shared__ __attribute__((aligned(16))) char dlds[];
+#define DVM_RED_PTRS(W)                                                                                \
   const uint32_t red_off = (W)[H_RED_OFF];                                                             \
   float(*s_red)[T_LANES / 64] = reinterpret_cast<float(*)[T_LANES / 64]>(dlds + red_off);             \
   int& s_last = *reinterpret_cast<int*>(dlds + red_off + N_LDSBUF * (T_LANES / 64) * 4);
 constexpr uint32_t LDS_CAP = LDS_BUDGET_WIDE;
 #else
-#define DVM_RED_BUFFERS(W)                                    \
-  __shared__ float s_red[N_LDSBUF][T_LANES / 64];             \
-  __shared__ int s_last;                                      \
+#define DVM_LDS_DECL                                          \
+  __shared__ float s_red_a[N_LDSBUF][T_LANES / 64];           \
+  __shared__ int s_last_a;                                    \
   extern __shared__ __attribute__((aligned(16))) char dlds[];
+#define DVM_RED_PTRS(W)                                       \
+  float(*s_red)[T_LANES / 64] = s_red_a;                      \
+  int& s_last = s_last_a;
 constexpr uint32_t LDS_CAP = LDS_BUDGET;
 #endif
 
+// One workgroup's run: its program (or its segment of a spatial stack), or
+// every segment of a temporal stack in order, with a workgroup barrier
+// between segments (the next segment's prologue rewrites LDS slots that waves
+// still on the previous one may be reading).  One call site of the
+// interpreter, so its code appears once per kernel.
+template <bool PROF>
+__device__ __forceinline__ void vm_kernel() {
+  KW* K = (KW*)__builtin_amdgcn_kernarg_segment_ptr();
+  DVM_LDS_DECL
+  const bool temporal = K[0] == TSTACK_MAGIC;
+  const uint32_t n = temporal ? K[S_NSEG] : 1u;
+  for (uint32_t s = 0; s < n; ++s) {
+    const Seg sg = temporal ? temporal_segment(K, s) : segment_of();
+    DVM_RED_PTRS(sg.W)
+    vm_main<PROF>(sg, s_red, s_last, dlds);
+    if (temporal) __syncthreads();
+  }
+}
+
 extern "C" __global__ void __launch_bounds__(T_LANES) __attribute__((amdgpu_waves_per_eu(2, 2)))
 DVM_SYM(dvm_vm_vector)(const Program prog) {
-  const Seg sg = segment_of();
-  DVM_RED_BUFFERS(sg.W)
   (void)prog;
-  vm_main<false>(sg, s_red, s_last, dlds);
+  vm_kernel<false>();
 }
 
 // Profiling twin of dvm_vm_vector: same program, same results, plus the
 // per-workgroup cycle split at the address in header words H_PROF_LO/HI.
 extern "C" __global__ void __launch_bounds__(T_LANES) __attribute__((amdgpu_waves_per_eu(2, 2)))
 DVM_SYM(dvm_vm_vector_prof)(const Program prog) {
-  const Seg sg = segment_of();
-  DVM_RED_BUFFERS(sg.W)
   (void)prog;
-  vm_main<true>(sg, s_red, s_last, dlds);
+  vm_kernel<true>();
 }
 
 // Host-side launch of the VECTOR VM kernel with one program as its argument.

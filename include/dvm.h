@@ -266,6 +266,23 @@ dvm_status dvm_graph_set_stacking(dvm_graph* g, int32_t max_segments);
  * DVM_ERR_RESOURCE when the words exceed the kernel argument. */
 dvm_status dvm_program_stack(const dvm_program* const* programs, size_t n, dvm_program** out);
 
+/* Temporal stacking (DVM review page, section 5.1, Figure 9: tiles of
+ * different graphs run on the same core in sequence).  With temporal = 1 the
+ * graph launches its stack temporally: the segments' tiles form one tile
+ * space in segment order, a launch of min(512, total tiles) workgroups runs
+ * tile u on workgroup u mod grid, and each workgroup walks the segments in
+ * order with a barrier between them (no launch, workgroup start or kernel
+ * entry between segments).  The same segments join as under spatial
+ * stacking (dvm_graph_set_stacking gives their number).  0 (default): spatial.
+ * Launches what the stack holds when called.  DVM_ERR_INVALID_ARG for other
+ * values. */
+dvm_status dvm_graph_set_stack_order(dvm_graph* g, int32_t temporal);
+
+/* dvm_program_stack, temporal: one program whose launch runs the n (2..7)
+ * programs' tiles as one tile space (see dvm_graph_set_stack_order).  Same
+ * requirements and errors as dvm_program_stack. */
+dvm_status dvm_program_stack_temporal(const dvm_program* const* programs, size_t n, dvm_program** out);
+
 /* Static-graph symbolic fusion (DVM review page, section 5.2, static-graph
  * fusion): a template is an op graph recorded once over symbolic dims;
  * dvm_template_finalize decides its fusion partition once (the streaming

@@ -364,6 +364,22 @@ def workgroup_tiles(b: int, grid: int, block_dim: int):
     return range(b, block_dim, grid)
 
 
+def temporal_stack_tiles(b: int, grid: int, block_dims):
+    """(segment, tile) pairs run, in order, by workgroup b of a temporally
+    stacked launch of `grid` workgroups over programs of block_dims tiles
+    (stacking-based fusion, temporal: tiles of different graphs run on one
+    core in sequence).  The segments' tiles are numbered as one space in
+    segment order; tile u of that space runs on workgroup u mod grid.  Inside
+    segment s workgroup b then plays workgroup (b - base_s) mod grid of the
+    segment's own strided order (base_s = tiles of the segments before it)."""
+    out, base = [], 0
+    for s, bd in enumerate(block_dims):
+        t0 = (b - base) % grid
+        out += [(s, t) for t in workgroup_tiles(t0, grid, bd)]
+        base += bd
+    return out
+
+
 def tile_box(tile_id: int, tr: int, tc: int, R: int, C: int, n_c: int):
     ir, ic = divmod(tile_id, n_c)
     return (ir * tr, min(ir * tr + tr, R)), (ic * tc, min(ic * tc + tc, C))

@@ -1,9 +1,11 @@
 """GPU parity of stacked launches (independent graphs packed into one launch,
-the stacking-based fusion of the DVM review page, section 5.1), through the C
-ABI.  A stacked program runs every segment on its own workgroups with its own
-header and tiling, so each output must equal, bit for bit, what the same
-graph computes when launched alone; LayerNorm outputs are also checked
-against the oracle.
+the stacking-based fusion of the DVM review page, section 5.1, spatial and
+temporal), through the C ABI.  A stacked program runs every segment with its
+own header and tiling (spatial: on its own workgroups; temporal: every
+workgroup walks the segments in sequence), so each output must equal, bit
+for bit, what the same graph computes when launched alone; LayerNorm outputs
+are also checked against the oracle, and the temporal tile map against the
+oracle's statement of it.
 """
 import numpy as np
 import pytest
@@ -11,6 +13,7 @@ import pytest
 import workloads as W
 from oracle import numerics as N
 from oracle import ops as O
+from oracle import tiling as TL
 from tests.dvm_helpers import empty_dev, host64
 
 pytestmark = pytest.mark.gpu
@@ -34,10 +37,10 @@ def say(*a):
     print("CASE", *a, flush=True)
 
 
-def run_layernorms(dvm, ctx, xs, gam, bet, stacking):
+def run_layernorms(dvm, ctx, xs, gam, bet, stacking, temporal=False):
     from device_bytecode_vm_amd import composites as CP
     g = dvm.Graph(ctx)
-    g.set_stacking(stacking)
+    g.set_stacking(stacking, temporal)
     ys = [empty_dev(x.shape, "bf16") for x in xs]
     for x, y in zip(xs, ys):
         CP.layer_norm(g, g.input(x), g.input(gam), g.input(bet), W.LN_EPS, out=y)
@@ -45,15 +48,15 @@ def run_layernorms(dvm, ctx, xs, gam, bet, stacking):
     return ys, g.stats()
 
 
-@pytest.mark.parametrize("stacking", [2, 7])
-def test_stacked_layernorm_stream(dvm, ctx, stacking):
+@pytest.mark.parametrize("stacking,temporal", [(2, False), (7, False), (2, True), (7, True)])
+def test_stacked_layernorm_stream(dvm, ctx, stacking, temporal):
     import torch
-    say("stacked_layernorm", stacking)
+    say("stacked_layernorm", stacking, "temporal" if temporal else "spatial")
     shapes = W.layernorm_shapes(0, 64)[:12]
     xs = [W.device_normal((min(r, 20000), W.H_LN), seed=1000 + i, dtype="bf16") for i, (r, _) in enumerate(shapes)]
     gam = W.device_normal((W.H_LN,), seed=1, mu=1.0, sd=0.1)
     bet = W.device_normal((W.H_LN,), seed=2, sd=0.1)
-    ys, st = run_layernorms(dvm, ctx, xs, gam, bet, stacking)
+    ys, st = run_layernorms(dvm, ctx, xs, gam, bet, stacking, temporal)
     ref, st1 = run_layernorms(dvm, ctx, xs, gam, bet, 1)
     assert st["stacked"] > 0 and st["launches"] < st1["launches"]
     for y, r in zip(ys, ref):
@@ -66,13 +69,14 @@ def test_stacked_layernorm_stream(dvm, ctx, stacking):
         assert ok, f"max ulp {d}"
 
 
-def test_stacked_op_stream_with_dependences(dvm, ctx):
+@pytest.mark.parametrize("temporal", [False, True])
+def test_stacked_op_stream_with_dependences(dvm, ctx, temporal):
     """A short transformer op stream (residual adds chained through h, SwiGLU
     and softmax writing shared outputs): stacking must keep every
     read-after-write, write-after-read and write-after-write order."""
     import torch
     from device_bytecode_vm_amd import composites as CP
-    say("stacked_op_stream")
+    say("stacked_op_stream", "temporal" if temporal else "spatial")
     T, TKV, motifs = W.stream_step(5, 300, tmax=300, tkv_max=700)
     H, F = 512, 1536
     bf = dict(dtype="bf16")
@@ -88,7 +92,7 @@ def test_stacked_op_stream_with_dependences(dvm, ctx):
         o_out = torch.zeros((T, F), dtype=torch.bfloat16, device="cuda")
         p_out = torch.zeros((4, T, TKV), dtype=torch.bfloat16, device="cuda")
         g = dvm.Graph(ctx)
-        g.set_stacking(stacking)
+        g.set_stacking(stacking, temporal and stacking > 1)
         cur = 0
         vh = g.input(hs[0])
         snaps = []
@@ -118,9 +122,10 @@ def test_stacked_op_stream_with_dependences(dvm, ctx):
             assert torch.equal(x, y)
 
 
-def test_program_stack_abi(dvm, ctx):
+@pytest.mark.parametrize("temporal", [False, True])
+def test_program_stack_abi(dvm, ctx, temporal):
     import torch
-    say("program_stack_abi")
+    say("program_stack_abi", "temporal" if temporal else "spatial")
     xs = [W.device_normal((300 + 100 * i, 777), seed=60 + i) for i in range(5)]
     outs = [torch.empty_like(x) for x in xs]
     refs = [torch.empty_like(x) for x in xs]
@@ -132,7 +137,7 @@ def test_program_stack_abi(dvm, ctx):
             g.op("sqrt", t, out=dst, live=True)
             g.release(t)
             lst.append(g.flush())
-    q = dvm.stack_programs(progs)
+    q = dvm.stack_programs(progs, temporal)
     assert q.header()["segments"] == 5
     q.launch()
     for p in singles:
@@ -141,3 +146,48 @@ def test_program_stack_abi(dvm, ctx):
     for o, r, x in zip(outs, refs, xs):
         assert torch.equal(o, r)
         assert torch.equal(o, torch.abs(x))       # sqrt(x * x) = |x| for these magnitudes
+
+
+@pytest.mark.parametrize("rows", [[3000, 17, 5000, 9000], [5, 9, 40]])
+def test_temporal_tilemap_bit_exact(dvm, ctx, rows):
+    """Tile maps of a temporally stacked launch: every segment's element ->
+    tile map is its own program's, and tile t of segment s runs on the
+    workgroup the oracle's temporal order names (reported as that
+    workgroup's place in the segment's strided order)."""
+    import torch
+    say("temporal_tilemap", rows)
+    dbgs, maps = [], []
+    for r in rows:
+        x = torch.zeros((r, 777), dtype=torch.float32, device="cuda")
+        g = dvm.Graph(ctx)
+        g.op("exp", g.input(x), out=empty_dev((r, 777), "f32"), live=True)
+        p = g.flush()
+        h = p.header()
+        tiles = empty_dev((h["R"], h["C"]), "f32")
+        wgs = empty_dev((h["R"], h["C"]), "f32")
+        dbgs.append(p.debug_tilemap(tiles, wgs))
+        maps.append((h, tiles, wgs))
+    assert len({d.header()["kernel_type"] for d in dbgs}) == 1
+    q = dvm.stack_programs(dbgs, temporal=True)
+    G = q.header()["grid"]
+    bds = [h["block_dim"] for h, _, _ in maps]
+    assert G == min(512, sum(bds))
+    q.launch()
+    torch.cuda.synchronize()
+    # expected: from the oracle's temporal order
+    base = [sum(bds[:i]) for i in range(len(bds))]
+    for s, (h, tiles, wgs) in enumerate(maps):
+        et = np.full((h["R"], h["C"]), -1.0)
+        ew = np.full((h["R"], h["C"]), -1.0)
+        n_c = -(-h["C"] // h["tc"])
+        for b in range(G):
+            for seg, t in TL.temporal_stack_tiles(b, G, bds):
+                if seg != s:
+                    continue
+                (r0, r1), (c0, c1) = TL.tile_box(t, h["tr"], h["tc"], h["R"], h["C"], n_c)
+                assert (et[r0:r1, c0:c1] == -1).all()
+                et[r0:r1, c0:c1] = t
+                ew[r0:r1, c0:c1] = (b - base[s]) % G
+        assert (et >= 0).all()
+        assert np.array_equal(host64(tiles), et)
+        assert np.array_equal(host64(wgs), ew)

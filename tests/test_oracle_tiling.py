@@ -224,3 +224,28 @@ def test_mix_element_map_covers_ragged_output():
     tiles, wgs = TL.mix_element_tile_map(p)
     assert (tiles >= 0).all() and (wgs >= 0).all()
     assert tiles[299, 999] == (p.n_r - 1) * p.n_c + p.n_c - 1
+
+
+@pytest.mark.parametrize("grid,bds", [(512, [3000, 1, 517, 9000]), (7, [3, 4, 5]), (5, [12]), (64, [0, 70, 0, 3])])
+def test_temporal_stack_tiles_cover_once_and_balance(grid, bds):
+    """Temporal stack order: every (segment, tile) runs exactly once; each
+    workgroup walks the segments in order; workgroups get the stack's tiles
+    as evenly as the count allows (floor or ceil of total / grid)."""
+    seen = {}
+    counts = []
+    for b in range(grid):
+        run = TL.temporal_stack_tiles(b, grid, bds)
+        assert [s for s, _ in run] == sorted(s for s, _ in run)
+        for st in run:
+            assert st not in seen
+            seen[st] = b
+        counts.append(len(run))
+    assert set(seen) == {(s, t) for s, bd in enumerate(bds) for t in range(bd)}
+    total = sum(bds)
+    assert min(counts) >= total // grid and max(counts) <= -(-total // grid)
+    # tile u of the stack's space runs on workgroup u mod grid
+    base = 0
+    for s, bd in enumerate(bds):
+        for t in range(bd):
+            assert seen[(s, t)] == (base + t) % grid
+        base += bd

@@ -120,3 +120,56 @@ def test_program_stack_abi(ectx):
         dvm.stack_programs(ps[:1])
     with pytest.raises(dvm.DvmError):
         g.set_stacking(8)
+
+
+TSTACK_MAGIC, H_BLOCK_DIM = 0x4B535454, 4
+
+
+def test_temporal_stack_directory(ectx):
+    """Temporal stacking: the directory lists each segment's first tile in
+    one tile space (the running sum of block_dim), and the launch has
+    min(512, total tiles) workgroups."""
+    g = dvm.Graph(ectx)
+    g.set_stacking(4, temporal=True)
+    for r in (3000, 5000, 7000, 9000):
+        layer_norm(g, r)
+    g.flush_launch()
+    (p,) = drain(g)
+    w = p.words()
+    assert w[0] == TSTACK_MAGIC and w[S_NSEG] == 4
+    bds = [w[w[S_DIR + 2 * i] + H_BLOCK_DIM] for i in range(4)]
+    assert [w[S_DIR + 2 * i + 1] for i in range(4)] == [0, bds[0], bds[0] + bds[1], sum(bds[:3])]
+    assert p.header()["segments"] == 4 and p.header()["grid"] == min(512, sum(bds))
+    assert p.verify() is None
+
+
+def test_temporal_stack_of_small_graphs(ectx):
+    """Few tiles in all: one workgroup per tile of the whole stack."""
+    g = dvm.Graph(ectx)
+    g.set_stacking(3, temporal=True)
+    for r in (8, 16, 24):
+        layer_norm(g, r)
+    g.flush_launch()
+    (p,) = drain(g)
+    w = p.words()
+    total = sum(w[w[S_DIR + 2 * i] + H_BLOCK_DIM] for i in range(3))
+    assert total < 512 and p.header()["grid"] == total
+
+
+def test_program_stack_temporal_abi(ectx):
+    progs = []
+    for r in (2000, 3000, 4000):                    # all on the wide build
+        g = dvm.Graph(ectx)
+        layer_norm(g, r)
+        progs.append(g.flush())
+    q = dvm.stack_programs(progs, temporal=True)
+    w = q.words()
+    assert w[0] == TSTACK_MAGIC and q.header()["segments"] == 3 and q.verify() is None
+    s = dvm.stack_programs(progs)
+    assert s.words()[0] == STACK_MAGIC
+
+
+def test_stack_order_is_checked(ectx):
+    g = dvm.Graph(ectx)
+    assert L.lib.dvm_graph_set_stack_order(g.h, 2) == L.ERR_INVALID_ARG
+    assert L.lib.dvm_graph_set_stack_order(g.h, 1) == 0

@@ -234,6 +234,22 @@ def test_planted_stack_directory_defect(ectx):
     assert msg and "directory" in msg
 
 
+def test_planted_temporal_directory_defect(ectx):
+    g = dvm.Graph(ectx)
+    g.set_stacking(3, temporal=True)
+    for r in (3000, 5000, 7000):
+        CP.layer_norm(g, g.input(TD(A(), "bf16", (r, 5120))), g.input(TD(A(), "f32", (5120,))),
+                      g.input(TD(A(), "f32", (5120,))), 1e-6, out=TD(A(), "bf16", (r, 5120)))
+    g.flush_launch()
+    (p,) = drain(g)
+    assert p.header()["segments"] == 3 and p.verify() is None
+
+    def bad_base(w):
+        w[S_DIR + 5] += 1                            # segment 2's first tile
+    msg = planted(p, bad_base).verify()
+    assert msg and "first tile" in msg
+
+
 def test_operand_reuse_fuzz_verifies(ectx):
     """Random fused groups whose ops reuse operands and intermediates (the
     case where one staged operand is read several times per tile)."""
