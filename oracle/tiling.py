@@ -69,7 +69,10 @@ design notes):
   entry.
 * Header: block_dim = n_tiles; body_tile = ceil(block_dim / min(G,
   block_dim)); grid = ceil(block_dim / body_tile).  Tile id -> (ir, ic) is
-  row-major with the column index fastest.
+  row-major with the column index fastest.  A wide-build plan (nv_max =
+  NV_WIDE) whose body_tile would exceed WIDE_WG_TILES = 8 is re-headed with
+  min(WIDE_GRID_MAX = 4096, block_dim // 8) in place of G: about 8 tiles per
+  workgroup and more workgroups than are resident (see the deviation below).
 
 Deviations from the page (stated here because the tile maps follow them):
 
@@ -80,6 +83,15 @@ Deviations from the page (stated here because the tile maps follow them):
   tiles, but at any moment the resident workgroups run neighbouring tiles, so
   their streams advance together through memory (on MI355X 6% faster on the
   LayerNorm stream and up to 14% on copy-like graphs).
+* More workgroups than cores for long wide-build programs.  The page's core
+  count is the grid.  On MI355X the two workgroups that share a compute unit
+  stream at different rates (the older one wins issue arbitration: measured
+  12% apart on a 126576-row LayerNorm), so equal static shares leave the
+  faster half idle at the end.  A wide-build program with more than 8 tiles
+  per workgroup therefore runs as up to 4096 workgroups of about 8 tiles,
+  and the hardware dispatcher hands the next one to whichever slot frees
+  first (LayerNorm stream +3 to 5%; standard-build and reduce-all programs
+  measured no better or worse, so they keep G).
 * MIX tile order.  The MIX kernel keeps block_dim, body_tile and grid, and
   walks the [M, N] output tiles in a grouped order for the L2 caches of the
   eight XCDs: row tiles go in groups of MM_GROUP = 8; inside a group the
@@ -100,6 +112,8 @@ NV_MAX = 5
 NV_WIDE = 10
 W_ALIGN = 64 * VEC
 G_WG = 512
+WIDE_WG_TILES = 8       # tiles per workgroup of a long wide-build program
+WIDE_GRID_MAX = 4096    # workgroups of such a program, at most
 A_TICKS = 78125
 A_MM_TICKS = 7812
 BYTE_TICKS = 1
@@ -314,6 +328,8 @@ def plan(template: str, R: int, C: int, ops, nv_max: int = NV_MAX) -> Plan:
     p.n_r, p.n_c = cdiv(R, p.tr), cdiv(C, p.tc)
     p.block_dim = p.n_r * p.n_c
     p.body_tile, p.grid = header(p.block_dim)
+    if nv_max == NV_WIDE and p.body_tile > WIDE_WG_TILES:
+        p.body_tile, p.grid = header(p.block_dim, min(WIDE_GRID_MAX, p.block_dim // WIDE_WG_TILES))
     return p
 
 

@@ -249,3 +249,44 @@ def test_temporal_stack_tiles_cover_once_and_balance(grid, bds):
         for t in range(bd):
             assert seen[(s, t)] == (base + t) % grid
         base += bd
+
+
+def test_wide_grid_rule_hand_worked():
+    """Long wide-build programs run as workgroups of about 8 tiles (up to
+    4096 of them).  Hand-worked: the 126576-row LayerNorm over 5120 columns
+    tiles as 4 x 5120 (31644 tiles); 31644 / 512 would give 62 tiles per
+    workgroup, more than 8, so the header is taken with min(4096, 31644 // 8)
+    = 3955 workgroups: ceil(31644 / 3955) = 9 tiles each (3955 * 8 = 31640 <
+    31644), ceil(31644 / 9) = 3516 workgroups."""
+    ops = [Operand(2, 5120, 1), Operand(4, 0, 1), Operand(4, 0, 1), Operand(2, 5120, 1)]
+    p = TL.plan(TL.ROWREDUCE, 126576, 5120, ops, TL.NV_WIDE)
+    assert (p.tr, p.tc, p.block_dim, p.body_tile, p.grid) == (4, 5120, 31644, 9, 3516)
+    # 16384 rows: 4096 tiles, 8 per workgroup at 512: the rule does not apply
+    p = TL.plan(TL.ROWREDUCE, 16384, 5120, ops, TL.NV_WIDE)
+    assert (p.block_dim, p.body_tile, p.grid) == (4096, 8, 512)
+    # 200000 rows: 50000 tiles, 4096 workgroups of ceil(50000 / 4096) = 13, 3847 of them used
+    p = TL.plan(TL.ROWREDUCE, 200000, 5120, ops, TL.NV_WIDE)
+    assert (p.block_dim, p.body_tile, p.grid) == (50000, 13, 3847)
+    # the standard build keeps G: 126576 x 1024 (one row per tile) stays at 512 workgroups
+    q = TL.plan(TL.ROWREDUCE, 126576, 1024, [Operand(2, 1024, 1), Operand(2, 1024, 1)])
+    assert q.grid <= TL.G_WG and q.body_tile > TL.WIDE_WG_TILES
+
+
+def test_wide_grid_rule_invariants():
+    g = np.random.default_rng(11)
+    for _ in range(60):
+        R = int(g.integers(1, 400000))
+        ops = [Operand(2, 5120, 1), Operand(4, 0, 1), Operand(2, 5120, 1)]
+        p = TL.plan(TL.ROWREDUCE, R, 5120, ops, TL.NV_WIDE)
+        if p.block_dim <= 8 * TL.G_WG:
+            assert p.grid <= TL.G_WG and p.body_tile <= TL.WIDE_WG_TILES
+        else:
+            assert TL.G_WG <= p.grid <= TL.WIDE_GRID_MAX
+            assert p.body_tile <= max(TL.WIDE_WG_TILES + 1, -(-p.block_dim // TL.WIDE_GRID_MAX))
+        # the strided sets still cover every tile once, at most body_tile each
+        seen = []
+        for b in range(p.grid):
+            ts = list(TL.workgroup_tiles(b, p.grid, p.block_dim))
+            assert 0 < len(ts) <= p.body_tile
+            seen.extend(ts)
+        assert sorted(seen) == list(range(p.block_dim))
