@@ -154,6 +154,12 @@ int64_t extent_bytes(const dvm_tensor& t) {
 // ===========================================================================
 namespace tiling {
 constexpr int64_t T = T_LANES, V = VEC, W = 64 * VEC, G = 512, A = 78125, A_MM = 7812, BT = 1;
+// A wide-build program with more than WIDE_WG_TILES tiles per workgroup
+// runs as min(WIDE_GRID_MAX, block_dim / WIDE_WG_TILES) workgroups, more than
+// are resident: the two workgroups sharing a compute unit stream at unequal
+// rates, and the dispatcher then hands the next workgroup to the slot that
+// frees first (measured on MI355X; standard-build programs keep G).
+constexpr int64_t WIDE_WG_TILES = 8, WIDE_GRID_MAX = 4096;
 
 struct Operand {
   int64_t esize, sr, sc, base_mod16;
@@ -375,6 +381,8 @@ bool plan(int tmpl, int64_t R, int64_t C, const std::vector<Operand>& ops, Plan*
   p->n_c = cdiv(C, p->tc);
   p->block_dim = p->n_r * p->n_c;
   header(p->block_dim, &p->body_tile, &p->grid);
+  if (nvm == NV_WIDE && p->body_tile > WIDE_WG_TILES)
+    header(p->block_dim, &p->body_tile, &p->grid, std::min(WIDE_GRID_MAX, p->block_dim / WIDE_WG_TILES));
   return true;
 }
 }  // namespace tiling

@@ -42,6 +42,8 @@ def test_tiling_constants_agree():
     assert const(ns, "A") == TL.A_TICKS
     assert const(ns, "A_MM") == TL.A_MM_TICKS
     assert const(ns, "BT") == TL.BYTE_TICKS
+    assert const(ns, "WIDE_WG_TILES") == TL.WIDE_WG_TILES
+    assert const(ns, "WIDE_GRID_MAX") == TL.WIDE_GRID_MAX
     assert eval(re.search(r"\bW = ([0-9 *A-Z_]+),", ns).group(1).replace("VEC", str(TL.VEC))) == TL.W_ALIGN
     menu = re.search(r"MM_TILES\[\] = \{(.*?)\};", ns).group(1)
     tiles = [tuple(int(x) for x in t.split(",")) for t in re.findall(r"\{([0-9, ]+)\}", menu)]

@@ -213,7 +213,7 @@ def _collapsed_operands(shape, n):
 @pytest.mark.parametrize("tmpl,shape", [("elemwise", (513, 1031)), ("rowreduce", (1000, 5120)),
                                         ("rowreduce", (280, 3001)), ("elemwise", (3, 9)),
                                         ("rowreduce", (777, 16)), ("rowreduce", (3000, 6484)),
-                                        ("rowreduce", (9, 15000))])
+                                        ("rowreduce", (9, 15000)), ("rowreduce", (20000, 5120))])
 def test_tilemap_bit_exact(dvm, ctx, tmpl, shape):
     """The VM's element -> tile and tile -> workgroup maps equal the oracle's."""
     import torch
