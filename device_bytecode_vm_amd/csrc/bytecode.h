@@ -89,7 +89,7 @@ enum Hdr : int {
   H_MM_B = 36,       // MIX: arg index of B [K, N] (bf16, unit stride along N)
   H_PROF_LO = 37,    // profiling launches only: device address of the per-workgroup
   H_PROF_HI = 38,    //   cycle counters (5 x uint64 per workgroup)
-  H_RED_OFF = 39,    // wide build: byte offset of the reduction buffers in dynamic LDS
+  H_RED_OFF = 39,    // byte offset of the cross-wave reduction buffers in dynamic LDS
   H_COND_ARG = 40,   // branch programs (HF_BRANCH): arg index of the condition (0-d fp32)
   H_COND_THR = 41,   //   the then-body runs iff condition > threshold (fp32 bits), strictly
   H_ALT_BEGIN = 42,  //   word range of the else-body (the then-body is H_BODY_BEGIN..END)
@@ -128,11 +128,10 @@ __host__ __device__ constexpr int mm_lds_bytes(int tm, int tn) {
 //    each wave's indices are 64 consecutive values (lane-private slots, or
 //    g a multiple of 64); others go through registers.
 // The budget keeps two workgroups resident per compute unit (160 KB of LDS).
-constexpr uint32_t LDS_BUDGET = 76u * 1024u;
-// The wide build keeps its cross-wave reduction buffers (and the reduce-all
+// Both VM builds keep their cross-wave reduction buffers (and the reduce-all
 // flag) in the dynamic area, reserved only by programs that use them, so two
-// of its workgroups may take the whole 160 KB.
-constexpr uint32_t LDS_BUDGET_WIDE = 80u * 1024u;
+// workgroups may take the whole 160 KB (two fp32 prefetch slots of 40 KB).
+constexpr uint32_t LDS_BUDGET = 80u * 1024u;
 constexpr uint32_t RED_LDS_BYTES = N_LDSBUF * (T_LANES / 64) * 4 + 16;
 
 // Argument table entry (8 words): pointer, dtype, flags, column stride, row

@@ -1414,17 +1414,12 @@ struct Encoder {
   void decide_lds(const std::vector<int64_t>& exts, const std::vector<std::pair<int64_t, int64_t>>& st) {
     uint32_t off = 0;
     int n_pf = 0, n_inv = 0;
-    // the wide build keeps its cross-wave reduction buffers in this area:
-    // reserved when a reduction may cross waves (rows wider than a wave, or
-    // a reduce-all)
-    bool need_red = false;
-    if (ktype == KT_VECTOR_WIDE) {
-      bool has_red = false;
-      for (const OpRec& o : ops) has_red = has_red || is_reduce(o.op);
-      need_red = has_red && (plan.g > 64 || ck.tmpl() == TM_ALLREDUCE);
-    }
-    const uint32_t budget =
-        ktype == KT_VECTOR_WIDE ? LDS_BUDGET_WIDE - (need_red ? RED_LDS_BYTES : 0u) : LDS_BUDGET;
+    // the cross-wave reduction buffers live in this area too: reserved when a
+    // reduction may cross waves (rows wider than a wave, or a reduce-all)
+    bool has_red = false;
+    for (const OpRec& o : ops) has_red = has_red || is_reduce(o.op);
+    const bool need_red = has_red && (plan.g > 64 || ck.tmpl() == TM_ALLREDUCE);
+    const uint32_t budget = LDS_BUDGET - (need_red ? RED_LDS_BYTES : 0u);
     if (plan.body_tile >= 2) {
       for (size_t q = 0; q < exts.size(); ++q) {
         const int64_t s = exts[q];

@@ -193,7 +193,7 @@ bool verify_vector(Ctx& c) {
     return c.fail("an empty iteration space with %u tiles", block_dim);
   }
   // LDS staging areas
-  const uint32_t budget = kt == KT_VECTOR_WIDE ? LDS_BUDGET_WIDE : LDS_BUDGET;
+  const uint32_t budget = LDS_BUDGET;
   if (W[H_LDS_BYTES] > budget) return c.fail("dynamic LDS %u exceeds %u", W[H_LDS_BYTES], budget);
   // prologue
   int pf_arg[2] = {-1, -1}, inv_arg[2] = {-1, -1};

@@ -1452,9 +1452,25 @@ __device__ __forceinline__ void vm_main(const Seg& sg, float (*s_red)[T_LANES / 
       __atomic_thread_fence(__ATOMIC_ACQUIRE);
       float acc = kind == RK_SUM ? 0.f : -__builtin_huge_valf();
       const uint32_t n_part = part_bytes(sa.extent, block_dim) / 4u;  // never past the area
-      for (uint32_t i = (uint32_t)tid; i < n_part; i += T_LANES) {
-        const float v = __hip_atomic_load(part + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        acc = kind == RK_SUM ? acc + v : comb<RK_MAX>(acc, v);
+      // Past the acquire fence the partials are read with plain loads (the
+      // fence invalidated this workgroup's caches, and every writer released
+      // its partial before counting itself in), eight per lane in flight at a
+      // time; each lane still folds its partials tid, tid + T, tid + 2T, ... in
+      // increasing order, so the sum is the same in every run.
+      const Rsrc rp = __builtin_amdgcn_make_buffer_rsrc(part, 0, (int)(n_part * 4u), RSRC_W3);
+      for (uint32_t i0 = 0; i0 < n_part; i0 += 8u * T_LANES) {
+        float v[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const uint32_t i = i0 + (uint32_t)(k * T_LANES + tid);
+          v[k] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rp, lane_off(i < n_part, (int)(i * 4u)), 0, 0));
+        }
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const bool ok = i0 + (uint32_t)(k * T_LANES + tid) < n_part;
+          const float c = kind == RK_SUM ? acc + v[k] : comb<RK_MAX>(acc, v[k]);
+          acc = ok ? c : acc;
+        }
       }
       acc = kind == RK_SUM ? group_reduce<RK_SUM>(acc, 64) : group_reduce<RK_MAX>(acc, 64);
       if ((tid & 63) == 0) s_red[0][wave] = acc;
@@ -1487,26 +1503,15 @@ __device__ __forceinline__ void vm_main(const Seg& sg, float (*s_red)[T_LANES / 
 #undef PROF_ENTER
 }
 
-// Cross-wave reduction buffers and the reduce-all flag: static arrays in the
-// standard build, a reserved part of each program's dynamic area in the wide
-// build (its offset is a header word, so it is looked up per segment).
-#ifdef DVM_WIDE
+// Cross-wave reduction buffers and the reduce-all flag: a reserved part of
+// each program's dynamic area (its offset is a header word, so it is looked up
+// per segment), present only in programs whose reductions cross waves.
 #define DVM_LDS_DECL extern __shared__ __attribute__((aligned(16))) char dlds[];
 #define DVM_RED_PTRS(W)                                                                                \
   const uint32_t red_off = (W)[H_RED_OFF];                                                             \
   float(*s_red)[T_LANES / 64] = reinterpret_cast<float(*)[T_LANES / 64]>(dlds + red_off);             \
   int& s_last = *reinterpret_cast<int*>(dlds + red_off + N_LDSBUF * (T_LANES / 64) * 4);
-constexpr uint32_t LDS_CAP = LDS_BUDGET_WIDE;
-#else
-#define DVM_LDS_DECL                                          \
-  __shared__ float s_red_a[N_LDSBUF][T_LANES / 64];           \
-  __shared__ int s_last_a;                                    \
-  extern __shared__ __attribute__((aligned(16))) char dlds[];
-#define DVM_RED_PTRS(W)                                       \
-  float(*s_red)[T_LANES / 64] = s_red_a;                      \
-  int& s_last = s_last_a;
 constexpr uint32_t LDS_CAP = LDS_BUDGET;
-#endif
 
 // One workgroup's run: its program (or its segment of a spatial stack), or
 // every segment of a temporal stack in order, with a workgroup barrier
