@@ -174,6 +174,13 @@ enum HdrFlag : uint32_t {
   // seed in bits [31:8], so waves drift apart and a missing barrier shows as
   // a changed result
   HF_STRESS = 4u,
+  // cross-wave reductions alternate between LDS buffers b and b ^ 1 by the
+  // parity of the workgroup's tile count: set instead of an end-of-body
+  // barrier when a tile has one cross-wave reduction, whose buffer the next
+  // tile's reduction would otherwise overwrite while slower waves still read
+  // it (the next tile's own barrier fences the reads before the buffer comes
+  // round again)
+  HF_RED_ALT = 8u,
 };
 constexpr uint64_t STREAM_BYTES = 16ull << 20;
 enum ArgFlag : uint32_t {

@@ -876,6 +876,7 @@ struct Encoder {
   tiling::Plan plan;
   int n_red = 0;
   bool cross_wave = false;
+  bool red_alt = false;  // one cross-wave reduction per tile: alternate buffers (HF_RED_ALT)
   std::vector<int> pf_slot, inv_slot;   // slot -> LDS staging slot (-1 none)
   struct Consume {
     size_t pos;      // word index of the instruction in body
@@ -1770,15 +1771,17 @@ struct Encoder {
     place_refills();
     patch_waits();
     fuse_scale_shift(body);
-    // Sync at the end of the body when the next tile's first cross-wave
-    // reduction could overwrite an LDS buffer some wave is still reading.
-    // Reduction k of a tile uses buffer k % N_LDSBUF and every reduction
-    // after the k-th ends in a barrier, so the reads of reduction k are
-    // fenced unless k is the tile's last.  The next tile's first reduction
-    // writes buffer 0: it races the last reduction's reads exactly when that
-    // one also used buffer 0, i.e. when (n_red - 1) % N_LDSBUF == 0 (n_red =
-    // 1, 9, 17, ...).
-    if (cross_wave && (n_red - 1) % N_LDSBUF == 0) emit(enc0(OP_SYNC, 0, 0, 0, 0, 0, 0), 0);
+    // The next tile's first cross-wave reduction could overwrite an LDS
+    // buffer some wave is still reading.  Reduction k of a tile uses buffer
+    // k % N_LDSBUF and every reduction after the k-th ends in a barrier, so
+    // the reads of reduction k are fenced unless k is the tile's last.  The
+    // next tile's first reduction writes buffer 0: it races the last
+    // reduction's reads exactly when that one also used buffer 0, i.e. when
+    // (n_red - 1) % N_LDSBUF == 0 (n_red = 1, 9, 17, ...).  With one
+    // reduction per tile the buffers alternate by tile parity instead
+    // (HF_RED_ALT: no barrier); otherwise the body ends with a sync.
+    if (cross_wave && n_red == 1) red_alt = true;
+    else if (cross_wave && (n_red - 1) % N_LDSBUF == 0) emit(enc0(OP_SYNC, 0, 0, 0, 0, 0, 0), 0);
     // header
     const uint32_t instr_base = ARG_BASE + (uint32_t)n_args * ARG_WORDS;
     const uint32_t body_base = instr_base + (uint32_t)pro.size();
@@ -1796,7 +1799,7 @@ struct Encoder {
       const uint32_t* a = W + ARG_BASE + q * ARG_WORDS;
       touched += arg_extent(a[A_FLAGS], a[A_EXTENT]);
     }
-    W[H_FLAGS] = tm != TM_ALLREDUCE && touched >= STREAM_BYTES ? HF_STREAM : 0u;
+    W[H_FLAGS] = (tm != TM_ALLREDUCE && touched >= STREAM_BYTES ? HF_STREAM : 0u) | (red_alt ? HF_RED_ALT : 0u);
     W[H_BLOCK_DIM] = (uint32_t)plan.block_dim;
     W[H_BODY_TILE] = (uint32_t)plan.body_tile;
     W[H_GRID] = (uint32_t)plan.grid;

@@ -223,6 +223,9 @@ bool verify_vector(Ctx& c) {
   }
   // the bodies: registers, staging and operands per tile; reduction buffers
   // over three consecutive tiles
+  // under HF_RED_ALT the workgroup's tiles alternate reduction buffers b and
+  // b ^ 1 (tile parity)
+  const bool red_alt = (W[H_FLAGS] & HF_RED_ALT) != 0;
   auto body = [&](uint32_t b0, uint32_t b1) -> bool {
     std::vector<int> reads_since_barrier;
     for (int tile = 0; tile < 3; ++tile) {
@@ -230,8 +233,12 @@ bool verify_vector(Ctx& c) {
       bool pf_done[2] = {false, false};
       for (uint32_t pc = b0; pc < b1; pc += 2) {
         const uint32_t w0 = W[pc], w1 = W[pc + 1];
-        const Effect e = effect(w0, w1);
+        Effect e = effect(w0, w1);
         if (!e.valid) return c.fail("word %u: unknown handler %u", pc, f_op(w0));
+        if (red_alt && (tile & 1)) {
+          if (e.buf_wr >= 0) e.buf_wr ^= 1;
+          if (e.buf_rd >= 0) e.buf_rd ^= 1;
+        }
         if (e.prologue_only) return c.fail("word %u: prologue handler %u in the body", pc, f_op(w0));
         if ((e.t_rd | e.t_wr) & ~treg_ok) return c.fail("word %u: tile register outside the build (handler %u)", pc, f_op(w0));
         if ((e.r_rd | e.r_wr) >> N_RREG) return c.fail("word %u: row register outside the file", pc);

@@ -773,6 +773,7 @@ struct Ctx {
   KW* W;
   char* lds;
   uint32_t tile, t_step, t_end;
+  uint32_t alt;  // reduction buffer toggle: tile parity under HF_RED_ALT, else 0
   __device__ __forceinline__ char* pf(uint32_t k) const { return lds + W[H_PF_OFF0 + k]; }
   __device__ __forceinline__ char* inv(uint32_t k) const { return lds + W[H_INV_OFF0 + k]; }
 };
@@ -1079,6 +1080,8 @@ __device__ __forceinline__ void vm_main(const Seg& sg, float (*s_red)[T_LANES / 
   S.lds = dlds;
   S.t_step = t_step;
   S.t_end = t_end;
+  S.alt = 0;
+  const uint32_t alt_on = (W[H_FLAGS] & HF_RED_ALT) ? 1u : 0u;
 
   // The body every tile runs.  A branch program reads its condition (a 0-d
   // fp32 operand written by an earlier launch on the stream) once, with a
@@ -1138,6 +1141,7 @@ __device__ __forceinline__ void vm_main(const Seg& sg, float (*s_red)[T_LANES / 
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       } else {
         tile += t_step;
+        S.alt ^= alt_on;  // this workgroup's next tile: the other reduction buffer
       }
       if (tile >= t_end) break;
       tl = make_tile(G, tile);
@@ -1208,7 +1212,7 @@ __device__ __forceinline__ void vm_main(const Seg& sg, float (*s_red)[T_LANES / 
       /* per-wave partial into LDS (after the 64-lane all-reduce every lane */             \
       /* holds it, so every lane stores it: no lane-dependent branch) */                   \
       acc = group_reduce<kind>(acc, 64);                                                   \
-      float* buf = s_red[f_b(w0)];                                                         \
+      float* buf = s_red[f_b(w0) ^ S.alt];                                                 \
       buf[wave] = acc;                                                                     \
       if (h == HD_REDX + 3 * kind + a) {                                                   \
         /* rows across waves: barrier, then combine the row's partials */                  \
@@ -1330,7 +1334,7 @@ __device__ __forceinline__ void vm_main(const Seg& sg, float (*s_red)[T_LANES / 
         // lane 0 alone stores the tile's partial, the others are masked by an
         // out-of-range offset
         const uint32_t kind = f_op(w0) - HD_ALL_FIN;
-        const float* buf = s_red[f_b(w0)];
+        const float* buf = s_red[f_b(w0) ^ S.alt];
         float acc = buf[0];
         for (int k = 1; k < T_LANES / 64; ++k) acc = kind == RK_SUM ? acc + buf[k] : comb<RK_MAX>(acc, buf[k]);
         // the partials' descriptor ends where the scratch operand ends (its

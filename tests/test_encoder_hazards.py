@@ -15,8 +15,9 @@ import device_bytecode_vm_amd as dvm
 from device_bytecode_vm_amd import TensorDesc as TD
 from device_bytecode_vm_amd import _lib as L
 
-H_BODY_BEGIN, H_BODY_END = 16, 17
+H_BODY_BEGIN, H_BODY_END, H_FLAGS = 16, 17, 26
 HD_REDX, HD_ALL, HD_SYNC = 127, 136, 149
+HF_RED_ALT = 8
 N_LDSBUF = 8
 
 
@@ -48,14 +49,16 @@ def chained_reductions(ectx, n_red, shape):
     return g.flush()
 
 
-def fenced(instrs, n_tiles=3):
+def fenced(instrs, n_tiles=3, alt=False):
     """Simulates n_tiles copies of the body and checks every write of a
     cross-wave buffer against the reads of the same buffer since the last
     barrier: a write may only follow reads that a barrier separates from it.
-    REDX = write, barrier, read; ALL = write (its SYNC and ALL_FIN follow)."""
+    REDX = write, barrier, read; ALL = write (its SYNC and ALL_FIN follow).
+    alt: the workgroup's odd tiles use buffer b ^ 1 (HF_RED_ALT)."""
     reads_since_barrier = set()
-    for _ in range(n_tiles):
+    for t in range(n_tiles):
         for h, b in instrs:
+            b = b ^ (t & 1) if alt else b
             if HD_REDX <= h < HD_REDX + 9:
                 if b in reads_since_barrier:
                     return False
@@ -79,9 +82,14 @@ def test_trailing_sync_fences_buffer_reuse(ectx, n_red, shape):
     ins = body(p)
     redx = [b for op, b in ins if HD_REDX <= op < HD_REDX + 9]
     assert redx == [k % N_LDSBUF for k in range(n_red)]
-    assert fenced(ins)
+    alt = bool(p.words()[H_FLAGS] & HF_RED_ALT)
+    assert alt == (n_red == 1)
+    assert fenced(ins, alt=alt)
     trailing = ins[-1][0] == HD_SYNC
-    assert trailing == ((n_red - 1) % N_LDSBUF == 0)
+    # one reduction per tile: buffers alternate instead of a trailing barrier
+    assert trailing == ((n_red - 1) % N_LDSBUF == 0 and n_red > 1)
+    if n_red == 1:
+        assert not fenced(ins, alt=False)    # without the alternation the body would race
 
 
 def test_failed_flush_drops_the_new_group(ectx):

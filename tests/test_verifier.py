@@ -290,3 +290,21 @@ def test_operand_reuse_fuzz_verifies(ectx):
         assert msg is None, f"trial {trial}: {msg}"
         n_prog += 1
     assert n_prog > 120
+
+
+def test_planted_missing_buffer_alternation(ectx):
+    """A reduce-all has one cross-wave reduction per tile: its buffers
+    alternate by tile parity (HF_RED_ALT) instead of an end-of-body barrier.
+    With the flag cleared the next tile's write races the last reads."""
+    H_FLAGS, HF_RED_ALT = 26, 8
+    g = dvm.Graph(ectx)
+    g.op("reduce_sum", g.input(TD(A(), "f32", (16384, 4096))), out=TD(A(), "f32", ()), live=True, axis=L.AXIS_ALL)
+    (p,) = drain(g)
+    w = p.words()
+    assert w[H_FLAGS] & HF_RED_ALT and w[w[H_BODY_END] - 2] & 0xFF != HD_SYNC
+    assert p.verify() is None
+
+    def clear_alt(w):
+        w[H_FLAGS] &= ~HF_RED_ALT
+    msg = planted(p, clear_alt).verify()
+    assert msg and "before every wave read it" in msg
