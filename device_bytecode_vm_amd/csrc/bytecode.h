@@ -174,12 +174,12 @@ enum HdrFlag : uint32_t {
   // seed in bits [31:8], so waves drift apart and a missing barrier shows as
   // a changed result
   HF_STRESS = 4u,
-  // cross-wave reductions alternate between LDS buffers b and b ^ 1 by the
+  // cross-wave reductions alternate between LDS buffers b and b ^ 2 by the
   // parity of the workgroup's tile count: set instead of an end-of-body
-  // barrier when a tile has one cross-wave reduction, whose buffer the next
-  // tile's reduction would otherwise overwrite while slower waves still read
-  // it (the next tile's own barrier fences the reads before the buffer comes
-  // round again)
+  // barrier when a tile's cross-wave reductions use only buffers 0 and 1 and
+  // its last one reads a buffer that the next tile's first one writes, which
+  // would otherwise overwrite it while slower waves still read it (the next
+  // tile's own barrier fences the reads before the buffers come round again)
   HF_RED_ALT = 8u,
 };
 constexpr uint64_t STREAM_BYTES = 16ull << 20;
@@ -255,7 +255,9 @@ enum Handler : uint32_t {
   HD_DIV_T = 157,    // ACC <- ACC / treg[b] (or treg[b] / ACC)
   HD_FMA_INV = 158,  // OP_FMA_INV
   HD_SILU = 159,     // ACC <- ACC / (exp(-ACC) + 1) (OP_UN, UN_SILU)
-  HD_COUNT = 160
+  HD_SOFTMAX = 160,  // ACC <- row softmax of ACC (OP_UN, UN_SOFTMAX); rows across waves use
+                     //   LDS buffers b and b + 1 and one barrier
+  HD_COUNT = 161
 };
 enum BinForm : uint32_t { BF_T0 = 0, BF_T1 = 1, BF_T2 = 2, BF_SCALAR = 3, BF_MEM = 4, BF_REV = 5 };
 
@@ -267,6 +269,12 @@ enum Una : uint32_t {
   UN_SQRT = 0, UN_ABS = 1, UN_LOG = 2, UN_EXP = 3, UN_ROUND = 4, UN_FLOOR = 5, UN_ISFINITE = 6,
   UN_NEG = 7, UN_RECIP = 8, UN_TOBF16 = 9, UN_IDENT = 10,
   UN_SILU = 11,  // z / (exp(-z) + 1): a fused SiLU chain, the chain's own operations in registers
+  // exp(z - max) / sum(exp(z - max)) over the row: a fused softmax chain.  Rows
+  // inside a wave: the chain's own operations in order.  Rows across waves:
+  // each wave's max m_w and sum s_w of exp(z - m_w) cross in one exchange;
+  // then M = max m_k, S = sum s_k exp(m_k - M) and the output exp(z - m_w)
+  // exp(m_w - M) / S (fp32 reordering only)
+  UN_SOFTMAX = 12,
 };
 enum BKind : uint32_t { BK_TREG = 0, BK_RREG = 1, BK_IMM = 2, BK_MEM = 3 };  // BK_MEM: B loaded from arg[w1]
 // RK_SUMSQ: sum of the squares of treg[a] (a reduce of x * x whose product is

@@ -876,7 +876,7 @@ struct Encoder {
   tiling::Plan plan;
   int n_red = 0;
   bool cross_wave = false;
-  bool red_alt = false;  // one cross-wave reduction per tile: alternate buffers (HF_RED_ALT)
+  bool red_alt = false;  // cross-wave buffers alternate with the tile parity (HF_RED_ALT)
   std::vector<int> pf_slot, inv_slot;   // slot -> LDS staging slot (-1 none)
   struct Consume {
     size_t pos;      // word index of the instruction in body
@@ -1479,7 +1479,7 @@ struct Encoder {
         if (a == 0 && dt(w1) == DT_F32) return HD_ST_F32;
         return HD_ST_DIR + a;
       case OP_COPY: return HD_COPY + 3 * d + a;
-      case OP_UN: return sub == UN_SILU ? (uint32_t)HD_SILU : HD_UN + sub;
+      case OP_UN: return sub == UN_SILU ? (uint32_t)HD_SILU : sub == UN_SOFTMAX ? (uint32_t)HD_SOFTMAX : HD_UN + sub;
       case OP_BIN: {
         const uint32_t bk = f_bk(w0);
         if (bk == BK_MEM) return HD_BIN_MEM;
@@ -1507,6 +1507,71 @@ struct Encoder {
       default: return HD_END;
     }
   }
+  // A softmax chain on the accumulator (row max into a row register, subtract
+  // it, exp, row sum, its reciprocal, multiply) whose row registers no later
+  // instruction reads -> one OP_UN UN_SOFTMAX.  Rows inside a wave (RED) run
+  // the same steps in the same order; rows across waves (REDX, the two
+  // reductions in consecutive buffers b, b + 1) exchange each wave's max and
+  // sum once, behind one barrier instead of two.  None of the six issues
+  // vector-memory instructions, so the patched waits stay valid.
+  static void fuse_softmax(std::vector<uint32_t>& v) {
+    auto rreg_reads = [](uint32_t w) -> uint32_t {
+      const uint32_t op = f_op(w);
+      if (op == OP_BIN && f_bk(w) == BK_RREG) return 1u << f_b(w);
+      if (op == OP_RBIN) return (1u << f_a(w)) | (f_bk(w) == BK_RREG ? 1u << f_b(w) : 0u);
+      if (op == OP_RUN || op == OP_BCAST || op == OP_STORE_ROW) return 1u << f_a(w);
+      if (op == OP_FMA_INV && f_bk(w) == BK_RREG) return 1u << f_dst(w);
+      return 0u;
+    };
+    auto rreg_writes = [](uint32_t w) -> uint32_t {
+      const uint32_t op = f_op(w);
+      if (op == OP_RED || op == OP_REDX || op == OP_RBIN || op == OP_RUN || op == OP_LOAD_ROW) return 1u << f_dst(w);
+      return 0u;
+    };
+    std::vector<uint32_t> out;
+    out.reserve(v.size());
+    for (size_t q = 0; q < v.size(); q += 2) {
+      if (q + 12 <= v.size()) {
+        const uint32_t m = v[q], d = v[q + 2], e = v[q + 4], r = v[q + 6], c = v[q + 8], y = v[q + 10];
+        const uint32_t red = f_op(m);
+        const bool ok =
+            (red == OP_RED || red == OP_REDX) && f_a(m) == 0 && f_sub(m) == RK_MAX &&
+            f_op(d) == OP_BIN && f_sub(d) == ALU_SUB && f_bk(d) == BK_RREG && f_b(d) == f_dst(m) &&
+            !(f_flags(d) & FL_REV) && f_op(e) == OP_UN && f_sub(e) == UN_EXP && f_op(r) == red && f_a(r) == 0 &&
+            f_sub(r) == RK_SUM && (red == OP_RED || f_b(r) == f_b(m) + 1) && f_op(c) == OP_RUN &&
+            f_sub(c) == UN_RECIP && f_a(c) == f_dst(r) && f_op(y) == OP_BIN && f_sub(y) == ALU_MUL &&
+            f_bk(y) == BK_RREG && f_b(y) == f_dst(c) && !(f_flags(y) & FL_REV);
+        if (ok) {
+          // the chain's row registers until each is written again (row
+          // registers do not outlive the tile)
+          uint32_t watch = (1u << f_dst(m)) | (1u << f_dst(r)) | (1u << f_dst(c));
+          bool read_later = false;
+          for (size_t t = q + 12; t < v.size() && watch && !read_later; t += 2) {
+            read_later = (rreg_reads(v[t]) & watch) != 0;
+            watch &= ~rreg_writes(v[t]);
+          }
+          if (!read_later) {
+            out.push_back(enc0(OP_UN, 0, 0, red == OP_REDX ? f_b(m) : 0u, UN_SOFTMAX, 0, 0));
+            out.push_back(0);
+            q += 10;
+            continue;
+          }
+        }
+      }
+      out.push_back(v[q]);
+      out.push_back(v[q + 1]);
+    }
+    v.swap(out);
+  }
+
+  // LDS reduction buffers a body instruction writes (and reads) across waves.
+  uint32_t red_bufs(uint32_t w) const {
+    const uint32_t op = f_op(w);
+    if (op == OP_REDX || op == OP_ALL) return 1u << f_b(w);
+    if (op == OP_UN && f_sub(w) == UN_SOFTMAX && plan.g > 64) return 3u << f_b(w);
+    return 0u;
+  }
+
   // ACC * inv[s1] followed by ACC + inv[s2] (both tile-invariant operands in
   // LDS, an f32 product: no rounding step between them) -> one OP_FMA_INV,
   // with a preceding ACC * row register folded in as its row scale.
@@ -1771,17 +1836,29 @@ struct Encoder {
     place_refills();
     patch_waits();
     fuse_scale_shift(body);
+    fuse_softmax(body);
     // The next tile's first cross-wave reduction could overwrite an LDS
-    // buffer some wave is still reading.  Reduction k of a tile uses buffer
-    // k % N_LDSBUF and every reduction after the k-th ends in a barrier, so
-    // the reads of reduction k are fenced unless k is the tile's last.  The
-    // next tile's first reduction writes buffer 0: it races the last
-    // reduction's reads exactly when that one also used buffer 0, i.e. when
-    // (n_red - 1) % N_LDSBUF == 0 (n_red = 1, 9, 17, ...).  With one
-    // reduction per tile the buffers alternate by tile parity instead
-    // (HF_RED_ALT: no barrier); otherwise the body ends with a sync.
-    if (cross_wave && n_red == 1) red_alt = true;
-    else if (cross_wave && (n_red - 1) % N_LDSBUF == 0) emit(enc0(OP_SYNC, 0, 0, 0, 0, 0, 0), 0);
+    // buffer some wave is still reading.  The reductions of a tile take
+    // buffers in order (k % N_LDSBUF; a fused softmax a pair), and every one
+    // after the k-th contains a barrier, so the reads of reduction k are
+    // fenced unless k is the tile's last.  The next tile's first reduction
+    // writes its buffers again: it races the last one's reads exactly when the
+    // two share a buffer (one reduction per tile; or 9, 17, ... of them).
+    // When the tile's reductions stay in buffers 0 and 1 the buffers
+    // alternate with 2 and 3 by tile parity instead (HF_RED_ALT: no barrier);
+    // otherwise the body ends with a sync.
+    uint32_t first_bufs = 0, last_bufs = 0, all_bufs = 0;
+    for (size_t q = 0; q < body.size(); q += 2) {
+      const uint32_t m = red_bufs(body[q]);
+      if (!m) continue;
+      if (!first_bufs) first_bufs = m;
+      last_bufs = m;
+      all_bufs |= m;
+    }
+    if (first_bufs & last_bufs) {
+      if (!(all_bufs & ~3u)) red_alt = true;
+      else emit(enc0(OP_SYNC, 0, 0, 0, 0, 0, 0), 0);
+    }
     // header
     const uint32_t instr_base = ARG_BASE + (uint32_t)n_args * ARG_WORDS;
     const uint32_t body_base = instr_base + (uint32_t)pro.size();

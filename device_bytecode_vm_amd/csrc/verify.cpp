@@ -39,7 +39,7 @@ struct Effect {
   int pf = -1;                  // prefetch slot read
   bool pf_issue = false;        // ... then refilled with the next tile
   int inv[2] = {-1, -1};        // invariant slots read
-  int buf_wr = -1, buf_rd = -1; // cross-wave reduction buffer written / read
+  unsigned buf_wr = 0, buf_rd = 0;  // cross-wave reduction buffers written / read (masks)
   bool barrier_mid = false;     // a barrier between the buffer write and read (REDX)
   bool barrier = false;         // a workgroup barrier (SYNC)
   bool prologue_only = false;
@@ -82,6 +82,13 @@ Effect effect(uint32_t w0, uint32_t w1) {
     e.t_wr = 1u << dd;
   } else if ((h >= HD_UN && h < HD_UN + 11) || h == HD_SILU) {
     e.t_rd = e.t_wr = 1u;
+  } else if (h == HD_SOFTMAX) {
+    // rows across waves (the caller drops these for rows inside a wave): the
+    // buffer pair b, b + 1 written, a barrier, both read
+    e.t_rd = e.t_wr = 1u;
+    if (b + 1 >= (uint32_t)N_LDSBUF) e.valid = false;
+    e.buf_wr = e.buf_rd = 3u << b;
+    e.barrier_mid = true;
   } else if (h >= HD_BIN && h < HD_BIN + 70) {
     const uint32_t form = ((h - HD_BIN) % 10) % 5;
     e.t_wr = 1u;
@@ -95,13 +102,13 @@ Effect effect(uint32_t w0, uint32_t w1) {
   } else if (h >= HD_REDX && h < HD_REDX + 9) {
     e.t_rd = 1u << ((h - HD_REDX) % 3);
     e.r_wr = 1u << d;
-    e.buf_wr = e.buf_rd = (int)b;
+    e.buf_wr = e.buf_rd = 1u << b;
     e.barrier_mid = true;
   } else if (h >= HD_ALL && h < HD_ALL + 6) {
     e.t_rd = 1u << ((h - HD_ALL) % 3);
-    e.buf_wr = (int)b;
+    e.buf_wr = 1u << b;
   } else if (h == HD_ALL_FIN || h == HD_ALL_FIN + 1) {
-    e.buf_rd = (int)b;
+    e.buf_rd = 1u << b;
   } else if (h >= HD_BCAST && h < HD_BCAST + 3) {
     e.r_rd = 1u << a;
     e.t_wr = 1u << (h - HD_BCAST);
@@ -224,10 +231,11 @@ bool verify_vector(Ctx& c) {
   // the bodies: registers, staging and operands per tile; reduction buffers
   // over three consecutive tiles
   // under HF_RED_ALT the workgroup's tiles alternate reduction buffers b and
-  // b ^ 1 (tile parity)
+  // b ^ 2 (tile parity)
   const bool red_alt = (W[H_FLAGS] & HF_RED_ALT) != 0;
+  auto swap2 = [](unsigned m) { return ((m & 0x33u) << 2) | ((m & 0xCCu) >> 2); };
   auto body = [&](uint32_t b0, uint32_t b1) -> bool {
-    std::vector<int> reads_since_barrier;
+    unsigned reads_since_barrier = 0;
     for (int tile = 0; tile < 3; ++tile) {
       unsigned t_def = 0, r_def = 0;
       bool pf_done[2] = {false, false};
@@ -235,9 +243,13 @@ bool verify_vector(Ctx& c) {
         const uint32_t w0 = W[pc], w1 = W[pc + 1];
         Effect e = effect(w0, w1);
         if (!e.valid) return c.fail("word %u: unknown handler %u", pc, f_op(w0));
+        if (f_op(w0) == HD_SOFTMAX && g <= 64) {  // rows inside a wave: no exchange
+          e.buf_wr = e.buf_rd = 0;
+          e.barrier_mid = false;
+        }
         if (red_alt && (tile & 1)) {
-          if (e.buf_wr >= 0) e.buf_wr ^= 1;
-          if (e.buf_rd >= 0) e.buf_rd ^= 1;
+          e.buf_wr = swap2(e.buf_wr);
+          e.buf_rd = swap2(e.buf_rd);
         }
         if (e.prologue_only) return c.fail("word %u: prologue handler %u in the body", pc, f_op(w0));
         if ((e.t_rd | e.t_wr) & ~treg_ok) return c.fail("word %u: tile register outside the build (handler %u)", pc, f_op(w0));
@@ -254,15 +266,12 @@ bool verify_vector(Ctx& c) {
         for (int k = 0; k < 2; ++k)
           if (e.inv[k] >= 0 && inv_arg[e.inv[k]] < 0)
             return c.fail("word %u: reads invariant slot %u that the prologue never loads", pc, (uint32_t)e.inv[k]);
-        if (e.buf_wr >= 0) {
-          for (int r : reads_since_barrier)
-            if (r == e.buf_wr)
-              return c.fail("word %u: writes reduction buffer %u before every wave read it (no barrier)", pc,
-                            (uint32_t)e.buf_wr);
-        }
-        if (e.barrier_mid) reads_since_barrier.clear();
-        if (e.buf_rd >= 0) reads_since_barrier.push_back(e.buf_rd);
-        if (e.barrier) reads_since_barrier.clear();
+        if (e.buf_wr & reads_since_barrier)
+          return c.fail("word %u: writes reduction buffer %u before every wave read it (no barrier)", pc,
+                        (uint32_t)__builtin_ctz(e.buf_wr & reads_since_barrier));
+        if (e.barrier_mid) reads_since_barrier = 0;
+        reads_since_barrier |= e.buf_rd;
+        if (e.barrier) reads_since_barrier = 0;
         t_def |= e.t_wr;
         r_def |= e.r_wr;
       }

@@ -1081,7 +1081,7 @@ __device__ __forceinline__ void vm_main(const Seg& sg, float (*s_red)[T_LANES / 
   S.t_step = t_step;
   S.t_end = t_end;
   S.alt = 0;
-  const uint32_t alt_on = (W[H_FLAGS] & HF_RED_ALT) ? 1u : 0u;
+  const uint32_t alt_on = (W[H_FLAGS] & HF_RED_ALT) ? 2u : 0u;
 
   // The body every tile runs.  A branch program reads its condition (a 0-d
   // fp32 operand written by an earlier launch on the stream) once, with a
@@ -1141,7 +1141,7 @@ __device__ __forceinline__ void vm_main(const Seg& sg, float (*s_red)[T_LANES / 
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       } else {
         tile += t_step;
-        S.alt ^= alt_on;  // this workgroup's next tile: the other reduction buffer
+        S.alt ^= alt_on;  // this workgroup's next tile: the other reduction buffers
       }
       if (tile >= t_end) break;
       tl = make_tile(G, tile);
@@ -1266,6 +1266,49 @@ __device__ __forceinline__ void vm_main(const Seg& sg, float (*s_red)[T_LANES / 
       case HD_UN + UN_RECIP: PROF_ENTER() un_c<UN_RECIP>(treg<0>(R)); break;
       case HD_UN + UN_TOBF16: PROF_ENTER() un_c<UN_TOBF16>(treg<0>(R)); break;
       case HD_SILU: PROF_ENTER() un_c<UN_SILU>(treg<0>(R)); break;
+      case HD_SOFTMAX: PROF_ENTER() {
+        // ACC <- softmax over its row (UN_SOFTMAX).  Rows inside a wave: the
+        // chain's own steps (row max, subtract, exp, row sum, reciprocal,
+        // multiply), bit for bit as the unfused program.  Rows across waves:
+        // each wave's max m_w and sum s_w of exp(z - m_w) cross in one
+        // exchange through buffers b and b + 1, then M = max m_k,
+        // S = sum_k s_k exp(m_k - M) in wave order, and the wave scales its
+        // exp(z - m_w) by exp(m_w - M) / S.  A wave whose elements are all
+        // -inf subtracts 0 instead: its sum is 0 and exp(-inf - M) = 0 drops
+        // it from S; a row with no finite maximum makes exp(-inf - (-inf))
+        // NaN everywhere, as the chain does.  The row index and width are
+        // made opaque so their products are formed here, not kept live
+        // across the interpreter loop.
+        const float ninf = -__builtin_huge_valf();
+        const float mw = group_reduce<RK_MAX>(lane_partial<RK_MAX>(treg<0>(R), G, tl, L), gs);
+        const bool across = G.g > 64;
+        bin_cs<ALU_SUB, false>(treg<0>(R), across && mw == ninf ? 0.f : mw);
+        un_c<UN_EXP>(treg<0>(R));
+        const float sw = group_reduce<RK_SUM>(lane_partial<RK_SUM>(treg<0>(R), G, tl, L), gs);
+        float scale;
+        if (!across) {
+          scale = 1.f / sw;
+        } else {
+          float* bm = s_red[f_b(w0) ^ S.alt];
+          float* bs = s_red[(f_b(w0) + 1) ^ S.alt];
+          bm[wave] = mw;
+          bs[wave] = sw;
+          asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+          __builtin_amdgcn_s_barrier();
+          asm volatile("" ::: "memory");
+          int nw = G.g >> 6, rowv = L.row;
+          asm volatile("" : "+v"(rowv), "+s"(nw));
+          const float* rm = bm + rowv * nw;
+          const float* rs = bs + rowv * nw;
+          float M = rm[0];
+          for (int k = 1; k < nw; ++k) M = comb<RK_MAX>(M, rm[k]);
+          float S_row = 0.f;
+          for (int k = 0; k < nw; ++k) S_row += rs[k] * __expf(rm[k] - M);
+          scale = __expf(mw - M) / S_row;
+        }
+        bin_cs<ALU_MUL, false>(treg<0>(R), scale);
+        break;
+      }
       CASE_BIN_COMM(ALU_ADD) CASE_BIN_NC(ALU_SUB) CASE_BIN_COMM(ALU_MUL)
       case HD_BIN + 10 * ALU_DIV + BF_SCALAR: PROF_ENTER() bin_cs<ALU_DIV, false>(treg<0>(R), SCALAR_B); break;
       case HD_BIN + 10 * ALU_DIV + BF_REV + BF_SCALAR: PROF_ENTER() bin_cs<ALU_DIV, true>(treg<0>(R), SCALAR_B); break;

@@ -54,11 +54,11 @@ def fenced(instrs, n_tiles=3, alt=False):
     cross-wave buffer against the reads of the same buffer since the last
     barrier: a write may only follow reads that a barrier separates from it.
     REDX = write, barrier, read; ALL = write (its SYNC and ALL_FIN follow).
-    alt: the workgroup's odd tiles use buffer b ^ 1 (HF_RED_ALT)."""
+    alt: the workgroup's odd tiles use buffer b ^ 2 (HF_RED_ALT)."""
     reads_since_barrier = set()
     for t in range(n_tiles):
         for h, b in instrs:
-            b = b ^ (t & 1) if alt else b
+            b = b ^ (2 * (t & 1)) if alt else b
             if HD_REDX <= h < HD_REDX + 9:
                 if b in reads_since_barrier:
                     return False

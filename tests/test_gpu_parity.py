@@ -415,6 +415,92 @@ def test_views_elementwise(dvm, ctx):
     assert np.all(got[:, 1::2] == 7.0)
 
 
+@pytest.mark.parametrize("cols", [6484, 12000, 3000, 777])
+def test_softmax_special_rows(dvm, ctx, cols):
+    """Softmax rows with -inf (a whole row; all of one wave's elements of a
+    row, following the lane layout: column c sits in lane (c // 8) mod g of
+    its row, wave ((c // 8) mod g) // 64), NaN and +inf entries, at widths
+    whose rows span waves (one exchange of each wave's max and sum) and fit
+    one wave.  NaN exactly where the oracle has NaN; the rest within 2 bf16
+    ulp."""
+    import torch
+    from device_bytecode_vm_amd import composites as CP
+    say("softmax_special", cols)
+    R = 64
+    dx = torch.zeros((R, cols), dtype=torch.bfloat16, device="cuda")
+    out = empty_dev((R, cols), "bf16")
+    g = dvm.Graph(ctx)
+    CP.softmax(g, g.input(dx), out=out)
+    p = g.flush()
+    gl = p.header()["g"]
+    wave_of = ((np.arange(cols) // 8) % gl) // 64
+    rg = np.random.default_rng(cols)
+    x = rg.normal(0, 3, (R, cols))
+    x[0] = -np.inf                                   # no finite maximum: a NaN row
+    x[1, wave_of == 0] = -np.inf                     # one wave's elements all -inf
+    x[2, cols // 3] = np.nan
+    x[3, cols - 5] = np.inf
+    x[4, wave_of != wave_of.max()] = -np.inf         # only the last wave of the row is finite
+    x[5] = -1e30
+    x[5, 7] = 0.0                                    # one finite spike far above the rest
+    x[6, :] = 88.0                                   # large equal values
+    xb = N.round_bf16(x)
+    dx.copy_(torch.tensor(xb, dtype=torch.float64).to(torch.bfloat16))
+    p.launch()
+    torch.cuda.synchronize()
+    got = host64(out)
+    with np.errstate(invalid="ignore", over="ignore"):
+        ref = O.softmax(xb)
+    assert np.array_equal(np.isnan(got), np.isnan(ref)), [int(r) for r in np.where(np.isnan(got) != np.isnan(ref))[0][:5]]
+    fin = ~np.isnan(ref).any(axis=1)
+    ok, d = N.check_bf16(got[fin], ref[fin])
+    assert ok, f"max ulp {d}"
+
+
+@pytest.mark.parametrize("cols,n_after", [(6484, 0), (6484, 1), (6484, 7), (12000, 2), (3000, 7)])
+def test_softmax_then_row_reductions(dvm, ctx, cols, n_after):
+    """A softmax followed in the same program by n_after row reductions of its
+    output (a row sum, then row maxes, each subtracted): 4096 rows, so each
+    workgroup runs many tiles and the cross-wave buffers of consecutive tiles
+    alternate or are fenced.  Sampled rows against the fp64 oracle graph, fp32
+    criterion."""
+    from device_bytecode_vm_amd import composites as CP
+    say("softmax_then_reductions", cols, n_after)
+    R = 4096
+    x = W.normal(np.random.default_rng(cols + n_after), (R, cols), 0, 2, "f32")
+    out = empty_dev((R, cols), "f32")
+    g = dvm.Graph(ctx)
+    v = y = CP.softmax(g, g.input(torch_dev(x, "f32")), out=out if n_after == 0 else None)
+    ops = [{"op": "reduce_max", "in": ["x"], "out": "m", "dtype": "f32"},
+           {"op": "sub", "in": ["x", "m"], "out": "d", "dtype": "f32"},
+           {"op": "exp", "in": ["d"], "out": "e", "dtype": "f32"},
+           {"op": "reduce_sum", "in": ["e"], "out": "s", "dtype": "f32"},
+           {"op": "div", "in": ["e", "s"], "out": "v0", "dtype": "f32"}]
+    for k in range(n_after):
+        kind = "reduce_sum" if k == 0 else "reduce_max"
+        r = g.op(kind, v)
+        last = k == n_after - 1
+        nv = g.op("sub", v, r, out=out if last else None, live=last)
+        g.release(r)
+        if k:
+            g.release(v)
+        v = nv
+        ops += [{"op": kind, "in": [f"v{k}"], "out": f"r{k}", "dtype": "f32"},
+                {"op": "sub", "in": [f"v{k}", f"r{k}"], "out": f"v{k + 1}", "dtype": "f32"}]
+    if n_after:
+        g.release(y)
+    p = g.flush()
+    assert p.header()["body_tile"] > 1
+    p.launch()
+    import torch
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([[0, 1, R - 1], np.random.default_rng(7).integers(0, R, 45)]))
+    ref, _ = evaluate(ops, {"x": x[rows]})
+    got = host64(out)[rows]
+    ok, e = N.check_f32(got, ref[f"v{n_after}"])
+    assert ok, f"rel err {e}"
+
+
 def test_views_layernorm_and_softmax(dvm, ctx):
     """Row reductions over views: LayerNorm of a column slice (row stride
     5200) and softmax over a transposed view (unit stride along rows)."""
