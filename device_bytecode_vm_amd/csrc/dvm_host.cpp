@@ -1351,25 +1351,26 @@ struct Encoder {
 
   // Vector-memory instructions one wave issues for an instruction in a full
   // tile (a lower bound: ragged tiles take the element paths and issue
-  // more).  Direct loads and stores run all NV_MAX chunks (out-of-range ones
-  // masked); prefetch refills issue the tile's nv chunks.
+  // more).  Vector (128-bit chunk) loads, stores and prefetch refills issue
+  // the tile's nv chunks; element loads and stores run all chunks of the
+  // build (out-of-range ones masked).
   uint32_t halves(uint32_t arg) const { return W[ARG_BASE + arg * ARG_WORDS + A_DTYPE] == DT_F32 ? 2u : 1u; }
   uint32_t load_ops(uint32_t arg) const {
     const uint32_t* a = W + ARG_BASE + arg * ARG_WORDS;
     const int32_t sc = (int32_t)a[A_SC];
     if (sc == 0) return 1u;
-    if ((a[A_FLAGS] & AF_VEC) && sc == 1) return (uint32_t)nvm * halves(arg);
+    if ((a[A_FLAGS] & AF_VEC) && sc == 1) return (uint32_t)plan.nv * halves(arg);
     return 8u * (uint32_t)nvm;
   }
   uint32_t store_ops(uint32_t arg) const {
     const uint32_t* a = W + ARG_BASE + arg * ARG_WORDS;
-    if ((a[A_FLAGS] & AF_VEC) && (int32_t)a[A_SC] == 1) return (uint32_t)nvm * halves(arg);
+    if ((a[A_FLAGS] & AF_VEC) && (int32_t)a[A_SC] == 1) return (uint32_t)plan.nv * halves(arg);
     return 8u * (uint32_t)nvm;
   }
   uint32_t src_ops(uint32_t w0, uint32_t w1) const {
     const uint32_t f = f_flags(w0);
     if (f & FL_INV) return 0;
-    if (f & FL_PF) return (f & FL_ISSUE) ? (uint32_t)nvm * halves(w1) : 0u;
+    if (f & FL_PF) return (f & FL_ISSUE) ? (uint32_t)plan.nv * halves(w1) : 0u;
     return load_ops(w1);
   }
   uint32_t vm_ops(uint32_t w0, uint32_t w1) const {
@@ -1379,15 +1380,18 @@ struct Encoder {
       case OP_STORE: return store_ops(w1);
       case OP_LOAD_ROW:
       case OP_STORE_ROW: return 1u;
-      case OP_PF: return (uint32_t)nvm * halves(w1);
+      case OP_PF: return (uint32_t)plan.nv * halves(w1);
       case OP_LDS_INV: return load_ops(w1);
       default: return 0u;
     }
   }
 
   // Wait counts of prefetch reads: instructions issued after the prefetch of
-  // the tile being read, counted over the end of the previous tile's body (or
-  // the prologue, for the first tile) plus this body up to the read.
+  // the tile being read, counted over the end of the previous tile's body
+  // plus this body up to the read.  A workgroup's first tile needs no count:
+  // the VM waits for every prologue load (its prefetch included) before the
+  // body starts, so the count only has to hold from the second tile on, and
+  // the previous tile's stores stay in flight while the next tile starts.
   void patch_waits() {
     auto sum = [&](const std::vector<uint32_t>& v, size_t lo, size_t hi) {
       uint32_t n = 0;
@@ -1397,11 +1401,7 @@ struct Encoder {
     for (const Consume& c : consumes) {
       const size_t ip = (size_t)issue_pos[c.slot];
       const uint32_t after_issue = sum(body, ip + 2, body.size());
-      size_t pp = 0;
-      for (size_t q = 0; q < pro.size(); q += 2)
-        if (f_op(pro[q]) == OP_PF && f_b(pro[q]) == c.slot) pp = q;
-      const uint32_t after_pro = sum(pro, pp + 2, pro.size());
-      uint32_t n = std::min(after_issue, after_pro) + sum(body, 0, c.pos);
+      uint32_t n = after_issue + sum(body, 0, c.pos);
       n = std::min<uint32_t>(n, VMC_MAX);
       uint32_t& w = body[c.pos];
       if (c.is_bin) w = (w & ~0xff00u) | ((n & 0xfu) << 8) | (((n >> 4) & 0xfu) << 12);

@@ -106,6 +106,17 @@ struct Geo {
   int64_t R, C;
 };
 
+// The tile's chunk count for a per-chunk pass, opaque to the optimiser so the
+// pass compares it chunk by chunk (one scalar branch each) instead of keeping
+// a condition per chunk live across the interpreter loop.  Chunks at or past
+// nv hold only columns past every row end: passes skip them, reductions mask
+// their columns, and the encoder's wait counts assume nv chunks per access.
+__device__ __forceinline__ int nv_pass(const Geo& G) {
+  int n = G.nv;
+  asm volatile("" : "+s"(n));
+  return n;
+}
+
 struct Tile {
   int64_t r0;   // first row of the tile
   int64_t c0;   // first column of the tile
@@ -213,6 +224,14 @@ __device__ __forceinline__ uint32_t f2bf_pack(float lo, float hi) {
 }
 
 __device__ __forceinline__ float round_bf16(float x) { return bf2f(f2bf_pack(x, 0.f) & 0xffffu); }
+
+// A chunk a pass skips: a fresh definition with no instructions (its value
+// is never used), so the register keeps no older value alive.
+__device__ __forceinline__ V8 skipped_chunk() {
+  V8 v;
+  asm volatile("" : "=v"(v));
+  return v;
+}
 
 __device__ __forceinline__ V8 unpack_bf16(u4 v) {
   V8 r;
@@ -459,6 +478,37 @@ __device__ __forceinline__ void store_tail(const Ch& s, const Rsrc& rs, int roff
 // Fill d (one tile register) from operand a for this tile.  `any_row` loads
 // as if every row of the tile existed (for operands that do not vary along
 // rows, whose row offset is zero).
+// The 128-bit chunk loads of load_dir: all chunks (ALL) or the first nv.
+template <uint32_t DT, int CP, bool ALL>
+__device__ __forceinline__ void load_chunks(Ch& d, const Rsrc& rs, int roff, bool rok, int lim, int nv, const Geo& G,
+                                            const Lane& L) {
+  constexpr int ES = esize_c<DT>();
+#pragma unroll
+  for (int j = 0; j < NVK; ++j) {
+    const int ct = (j * G.g + L.lane) * VEC;
+    const int off = lane_off(rok & (ct + VEC <= lim), (roff + ct) * ES);
+    if constexpr (DT == DT_F32) {
+      if (ALL || j < nv) {
+        const u4 v0 = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, CP);
+        const u4 v1 = __builtin_amdgcn_raw_buffer_load_b128(rs, off == OOB ? OOB : off + 16, 0, CP);
+        d.c[j] = unpack_f32(v0, v1);
+      } else {
+        d.c[j] = skipped_chunk();
+      }
+    } else if constexpr (DT == DT_BF16) {
+      if (ALL || j < nv) d.c[j] = unpack_bf16(__builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, CP));
+      else d.c[j] = skipped_chunk();
+    } else {
+      const u2 v = __builtin_amdgcn_raw_buffer_load_b64(rs, off, 0, CP);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        d.c[j][i] = (float)((v.x >> (8 * i)) & 0xffu);
+        d.c[j][4 + i] = (float)((v.y >> (8 * i)) & 0xffu);
+      }
+    }
+  }
+}
+
 template <uint32_t DT, int CP = CP_STREAM>
 __device__ __forceinline__ void load_dir(Ch& d, const ArgD& a, const Geo& G, const Tile& tl, const Lane& L,
                                          bool any_row = false) {
@@ -479,25 +529,9 @@ __device__ __forceinline__ void load_dir(Ch& d, const ArgD& a, const Geo& G, con
     // whole-chunk columns (the others are masked); a row-end chunk they do not
     // cover is completed element by element
     const int lim = chunk_cols(a, tl, ES, any_row ? (T_LANES >> G.lg) : tl.tre);
-#pragma unroll
-    for (int j = 0; j < NVK; ++j) {
-      const int ct = (j * G.g + L.lane) * VEC;
-      const int off = lane_off(rok & (ct + VEC <= lim), (roff + ct) * ES);
-      if constexpr (DT == DT_F32) {
-        const u4 v0 = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, CP);
-        const u4 v1 = __builtin_amdgcn_raw_buffer_load_b128(rs, off == OOB ? OOB : off + 16, 0, CP);
-        d.c[j] = unpack_f32(v0, v1);
-      } else if constexpr (DT == DT_BF16) {
-        d.c[j] = unpack_bf16(__builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, CP));
-      } else {
-        const u2 v = __builtin_amdgcn_raw_buffer_load_b64(rs, off, 0, CP);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          d.c[j][i] = (float)((v.x >> (8 * i)) & 0xffu);
-          d.c[j][4 + i] = (float)((v.y >> (8 * i)) & 0xffu);
-        }
-      }
-    }
+    const int nv = nv_pass(G);
+    if (nv >= NVK) load_chunks<DT, CP, true>(d, rs, roff, rok, lim, nv, G, L);
+    else load_chunks<DT, CP, false>(d, rs, roff, rok, lim, nv, G, L);
     if (lim < tl.tce) load_tail<DT>(d, rs, roff, G, tl, L, rok);
   } else {
     // element path: unaligned or strided operands
@@ -532,6 +566,44 @@ __device__ __forceinline__ void load_any(Ch& d, const ArgD& a, const Geo& G, con
   else load_any_cp<0>(d, a, G, tl, L, any_row);
 }
 
+// The 128-bit chunk stores of store_dir: all chunks (ALL) or the first nv.
+// The register comes by value: taken by reference from two instances, its
+// chunks were kept in private memory instead of registers.
+template <uint32_t DT, int CP, bool ALL>
+__device__ __forceinline__ void store_chunks(const Ch s, const Rsrc& rs, int roff, int nv, const Geo& G,
+                                             const Tile& tl, const Lane& L) {
+  constexpr int ES = esize_c<DT>();
+#pragma unroll
+  for (int j = 0; j < NVK; ++j) {
+    if (!ALL && j >= nv) continue;
+    const int ct = (j * G.g + L.lane) * VEC;
+    const int off = lane_off(L.rok & (ct + VEC <= tl.tce), (roff + ct) * ES);
+    const V8 x = s.c[j];
+    if constexpr (DT == DT_F32) {
+      u4 v0, v1;
+      v0.x = __float_as_uint(x[0]); v0.y = __float_as_uint(x[1]); v0.z = __float_as_uint(x[2]); v0.w = __float_as_uint(x[3]);
+      v1.x = __float_as_uint(x[4]); v1.y = __float_as_uint(x[5]); v1.z = __float_as_uint(x[6]); v1.w = __float_as_uint(x[7]);
+      __builtin_amdgcn_raw_buffer_store_b128(v0, rs, off, 0, CP);
+      __builtin_amdgcn_raw_buffer_store_b128(v1, rs, off == OOB ? OOB : off + 16, 0, CP);
+    } else if constexpr (DT == DT_BF16) {
+      u4 v;
+      v.x = f2bf_pack(x[0], x[1]);
+      v.y = f2bf_pack(x[2], x[3]);
+      v.z = f2bf_pack(x[4], x[5]);
+      v.w = f2bf_pack(x[6], x[7]);
+      __builtin_amdgcn_raw_buffer_store_b128(v, rs, off, 0, CP);
+    } else {
+      u2 v = {0u, 0u};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        v.x |= ((uint32_t)x[i] & 0xffu) << (8 * i);
+        v.y |= ((uint32_t)x[4 + i] & 0xffu) << (8 * i);
+      }
+      __builtin_amdgcn_raw_buffer_store_b64(v, rs, off, 0, CP);
+    }
+  }
+}
+
 template <uint32_t DT, int CP>
 __device__ __forceinline__ void store_dir_cp(const Ch& s, const ArgD& a, const Geo& G, const Tile& tl,
                                              const Lane& L) {
@@ -539,34 +611,9 @@ __device__ __forceinline__ void store_dir_cp(const Ch& s, const ArgD& a, const G
   const Rsrc rs = tile_rsrc(a, tl, ES);
   const int roff = L.row * (int)a.sr;
   if ((a.fl & AF_VEC) && a.sc == 1) {
-#pragma unroll
-    for (int j = 0; j < NVK; ++j) {
-      const int ct = (j * G.g + L.lane) * VEC;
-      const int off = lane_off(L.rok & (ct + VEC <= tl.tce), (roff + ct) * ES);
-      const V8 x = s.c[j];
-      if constexpr (DT == DT_F32) {
-        u4 v0, v1;
-        v0.x = __float_as_uint(x[0]); v0.y = __float_as_uint(x[1]); v0.z = __float_as_uint(x[2]); v0.w = __float_as_uint(x[3]);
-        v1.x = __float_as_uint(x[4]); v1.y = __float_as_uint(x[5]); v1.z = __float_as_uint(x[6]); v1.w = __float_as_uint(x[7]);
-        __builtin_amdgcn_raw_buffer_store_b128(v0, rs, off, 0, CP);
-        __builtin_amdgcn_raw_buffer_store_b128(v1, rs, off == OOB ? OOB : off + 16, 0, CP);
-      } else if constexpr (DT == DT_BF16) {
-        u4 v;
-        v.x = f2bf_pack(x[0], x[1]);
-        v.y = f2bf_pack(x[2], x[3]);
-        v.z = f2bf_pack(x[4], x[5]);
-        v.w = f2bf_pack(x[6], x[7]);
-        __builtin_amdgcn_raw_buffer_store_b128(v, rs, off, 0, CP);
-      } else {
-        u2 v = {0u, 0u};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          v.x |= ((uint32_t)x[i] & 0xffu) << (8 * i);
-          v.y |= ((uint32_t)x[4 + i] & 0xffu) << (8 * i);
-        }
-        __builtin_amdgcn_raw_buffer_store_b64(v, rs, off, 0, CP);
-      }
-    }
+    const int nv = nv_pass(G);
+    if (nv >= NVK) store_chunks<DT, CP, true>(s, rs, roff, nv, G, tl, L);
+    else store_chunks<DT, CP, false>(s, rs, roff, nv, G, tl, L);
     store_tail<DT>(s, rs, roff, G, tl, L);
   } else {
 #pragma unroll
@@ -614,9 +661,9 @@ __device__ __forceinline__ void store_any(const Ch& v, const ArgD& a, const Geo&
 // (the prefetch included).  Their completion is awaited explicitly, with the
 // counted wait before the slot is read; waits the compiler places for its own
 // loads stay correct (extra outstanding operations only make them stricter).
-template <uint32_t DT>
-__device__ __forceinline__ void pf_issue(char* slot, const ArgD& a, const Geo& G, const Tile& nt, const Lane& L,
-                                         bool keep) {
+template <uint32_t DT, bool ALL>
+__device__ __forceinline__ void pf_issue_n(char* slot, const ArgD& a, const Geo& G, const Tile& nt, const Lane& L,
+                                           bool keep, int nv) {
   constexpr int ES = esize_c<DT>();
   constexpr int HV = DT == DT_F32 ? 2 : 1;
   const u4 rs = tile_rsrc_words(a, nt, ES);
@@ -627,9 +674,9 @@ __device__ __forceinline__ void pf_issue(char* slot, const ArgD& a, const Geo& G
   const int lim = chunk_cols(a, nt, ES, nt.tre);
 #pragma unroll
   for (int j = 0; j < NVK; ++j) {
-    {
-      // all NVK chunks: those past the tile's columns are masked (their LDS
-      // bytes get zeros)
+    if (ALL || j < nv) {
+      // the tile's nv chunks; lanes past the tile's columns are masked (their
+      // LDS bytes get zeros)
       const int ct = (j * G.g + L.lane) * VEC;
       const int off = lane_off(rok & (ct + VEC <= lim), (roff + ct) * ES);  // whole chunks only
 #pragma unroll
@@ -652,14 +699,23 @@ __device__ __forceinline__ void pf_issue(char* slot, const ArgD& a, const Geo& G
 }
 
 template <uint32_t DT>
-__device__ __forceinline__ void pf_read(Ch& d, const char* slot, const Geo& G, int tid) {
+__device__ __forceinline__ void pf_issue(char* slot, const ArgD& a, const Geo& G, const Tile& nt, const Lane& L,
+                                         bool keep) {
+  const int nv = nv_pass(G);
+  if (nv >= NVK) pf_issue_n<DT, true>(slot, a, G, nt, L, keep, nv);
+  else pf_issue_n<DT, false>(slot, a, G, nt, L, keep, nv);
+}
+
+template <uint32_t DT, bool ALL>
+__device__ __forceinline__ void pf_read_n(Ch& d, const char* slot, int tid, int nv) {
   constexpr int HV = DT == DT_F32 ? 2 : 1;
 #pragma unroll
   for (int j = 0; j < NVK; ++j) {
-    // a chunk past nv re-reads chunk 0 (its values are masked downstream)
-    // every slot holds NVK chunks; those past nv hold values that are
-    // masked downstream (no per-chunk condition, so no per-chunk constants
-    // stay live across the interpreter loop)
+    // the slot's first nv chunks (the refill fills only those)
+    if (!ALL && j >= nv) {
+      d.c[j] = skipped_chunk();
+      continue;
+    }
     const int jj = j;
     const u4 v = *(const u4*)(slot + ((jj * HV) * T_LANES + tid) * 16);
     if constexpr (DT == DT_F32) {
@@ -669,6 +725,13 @@ __device__ __forceinline__ void pf_read(Ch& d, const char* slot, const Geo& G, i
       d.c[j] = unpack_bf16(v);
     }
   }
+}
+
+template <uint32_t DT>
+__device__ __forceinline__ void pf_read(Ch& d, const char* slot, const Geo& G, int tid) {
+  const int nv = nv_pass(G);
+  if (nv >= NVK) pf_read_n<DT, true>(d, slot, tid, nv);
+  else pf_read_n<DT, false>(d, slot, tid, nv);
 }
 
 // Invariant slot addressing: a shared slot is indexed by the lane's position
@@ -854,6 +917,35 @@ __device__ __forceinline__ void un_c(Ch& acc) {
     for (int i = 0; i < VEC; ++i) acc.c[j][i] = una<F>(acc.c[j][i]);
 }
 
+// The same over the tile's first nv chunks only (nv wave-uniform: one scalar
+// branch per chunk).  For the costly routines (transcendentals, divisions):
+// chunks at or past nv hold columns past every row end, which reductions
+// mask by column and stores skip, so they need no values.
+template <uint32_t F>
+__device__ __forceinline__ void un_cn(Ch& acc, int nv) {
+#pragma unroll
+  for (int j = 0; j < NVK; ++j) {
+    if (j < nv) {
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) acc.c[j][i] = una<F>(acc.c[j][i]);
+    }
+  }
+}
+
+template <uint32_t OPK, bool REV>
+__device__ __forceinline__ void bin_csn(Ch& acc, float s, int nv) {
+#pragma unroll
+  for (int j = 0; j < NVK; ++j) {
+    if (j < nv) {
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) {
+        const float x = acc.c[j][i];
+        acc.c[j][i] = REV ? alu<OPK>(s, x) : alu<OPK>(x, s);
+      }
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Cross-lane reductions: DPP and permlane swaps inside a wave, LDS across
 // waves.
@@ -911,11 +1003,19 @@ template <uint32_t KIND>
 __device__ __forceinline__ float lane_partial(const Ch& c, const Geo& G, const Tile& tl, const Lane& L) {
   const float id = KIND == RK_MAX ? -__builtin_huge_valf() : 0.f;
   float p[NVK];
-  if (tile_full(tl)) {
+  const int nv = nv_pass(G);
+  if (tile_full(tl) && nv >= NVK) {
 #pragma unroll
     for (int j = 0; j < NVK; ++j) {
       const int ct = (j * G.g + L.lane) * VEC;
       p[j] = lane_sel(L.rok & (ct < tl.tce), tree8<KIND>(lane_terms<KIND>(c.c[j])), id);
+    }
+  } else if (tile_full(tl)) {
+#pragma unroll
+    for (int j = 0; j < NVK; ++j) {
+      const int ct = (j * G.g + L.lane) * VEC;
+      p[j] = id;
+      if (j < nv) p[j] = lane_sel(L.rok & (ct < tl.tce), tree8<KIND>(lane_terms<KIND>(c.c[j])), id);
     }
   } else {
     // only the row-end slot (wave-uniform) needs a mask per element
@@ -1255,17 +1355,17 @@ __device__ __forceinline__ void vm_main(const Seg& sg, float (*s_red)[T_LANES / 
         break;
       }
       CASE_COPY(0, 1) CASE_COPY(0, 2) CASE_COPY(1, 0) CASE_COPY(1, 2) CASE_COPY(2, 0) CASE_COPY(2, 1)
-      case HD_UN + UN_SQRT: PROF_ENTER() un_c<UN_SQRT>(treg<0>(R)); break;
+      case HD_UN + UN_SQRT: PROF_ENTER() un_cn<UN_SQRT>(treg<0>(R), nv_pass(G)); break;
       case HD_UN + UN_ABS: PROF_ENTER() un_c<UN_ABS>(treg<0>(R)); break;
-      case HD_UN + UN_LOG: PROF_ENTER() un_c<UN_LOG>(treg<0>(R)); break;
-      case HD_UN + UN_EXP: PROF_ENTER() un_c<UN_EXP>(treg<0>(R)); break;
+      case HD_UN + UN_LOG: PROF_ENTER() un_cn<UN_LOG>(treg<0>(R), nv_pass(G)); break;
+      case HD_UN + UN_EXP: PROF_ENTER() un_cn<UN_EXP>(treg<0>(R), nv_pass(G)); break;
       case HD_UN + UN_ROUND: PROF_ENTER() un_c<UN_ROUND>(treg<0>(R)); break;
       case HD_UN + UN_FLOOR: PROF_ENTER() un_c<UN_FLOOR>(treg<0>(R)); break;
       case HD_UN + UN_ISFINITE: PROF_ENTER() un_c<UN_ISFINITE>(treg<0>(R)); break;
       case HD_UN + UN_NEG: PROF_ENTER() un_c<UN_NEG>(treg<0>(R)); break;
-      case HD_UN + UN_RECIP: PROF_ENTER() un_c<UN_RECIP>(treg<0>(R)); break;
+      case HD_UN + UN_RECIP: PROF_ENTER() un_cn<UN_RECIP>(treg<0>(R), nv_pass(G)); break;
       case HD_UN + UN_TOBF16: PROF_ENTER() un_c<UN_TOBF16>(treg<0>(R)); break;
-      case HD_SILU: PROF_ENTER() un_c<UN_SILU>(treg<0>(R)); break;
+      case HD_SILU: PROF_ENTER() un_cn<UN_SILU>(treg<0>(R), nv_pass(G)); break;
       case HD_SOFTMAX: PROF_ENTER() {
         // ACC <- softmax over its row (UN_SOFTMAX).  Rows inside a wave: the
         // chain's own steps (row max, subtract, exp, row sum, reciprocal,
@@ -1282,8 +1382,8 @@ __device__ __forceinline__ void vm_main(const Seg& sg, float (*s_red)[T_LANES / 
         const float ninf = -__builtin_huge_valf();
         const float mw = group_reduce<RK_MAX>(lane_partial<RK_MAX>(treg<0>(R), G, tl, L), gs);
         const bool across = G.g > 64;
-        bin_cs<ALU_SUB, false>(treg<0>(R), across && mw == ninf ? 0.f : mw);
-        un_c<UN_EXP>(treg<0>(R));
+        bin_csn<ALU_SUB, false>(treg<0>(R), across && mw == ninf ? 0.f : mw, nv_pass(G));
+        un_cn<UN_EXP>(treg<0>(R), nv_pass(G));
         const float sw = group_reduce<RK_SUM>(lane_partial<RK_SUM>(treg<0>(R), G, tl, L), gs);
         float scale;
         if (!across) {
@@ -1306,7 +1406,7 @@ __device__ __forceinline__ void vm_main(const Seg& sg, float (*s_red)[T_LANES / 
           for (int k = 0; k < nw; ++k) S_row += rs[k] * __expf(rm[k] - M);
           scale = __expf(mw - M) / S_row;
         }
-        bin_cs<ALU_MUL, false>(treg<0>(R), scale);
+        bin_csn<ALU_MUL, false>(treg<0>(R), scale, nv_pass(G));
         break;
       }
       CASE_BIN_COMM(ALU_ADD) CASE_BIN_NC(ALU_SUB) CASE_BIN_COMM(ALU_MUL)
