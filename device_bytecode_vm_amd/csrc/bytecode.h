@@ -202,8 +202,10 @@ enum Op : uint32_t {
   OP_RED = 10,       // row reduce of treg[a]: rreg[dst] (and LDS buffer b if the row spans waves)
   OP_RED_FIN = 11,   // (unused: cross-wave row reductions are OP_REDX)
   OP_SYNC = 12,      // workgroup barrier inserted by the encoder
-  OP_ALL = 13,       // reduce-all partial of treg[a] into LDS buffer b
-  OP_ALL_FIN = 14,   // tile partial from LDS buffer b -> scratch[tile]
+  OP_ALL = 13,       // reduce-all: treg[a]'s lane partial folded into the lane's running
+                     //   partial (the VM's reduce-all epilogue combines the lanes, waves
+                     //   and workgroups)
+  OP_ALL_FIN = 14,   // (retired: reduce-all partials are per workgroup, in the epilogue)
   OP_BCAST = 15,     // treg[dst] <- rreg[a] broadcast along the row (Broadcast)
   OP_DBG = 16,       // treg[dst] <- tile id (sub 0) / workgroup id (sub 1)
   OP_LDS_INV = 17,   // prologue: invariant slot dst <- arg[w1] (fp32, lane-private)
@@ -239,8 +241,8 @@ enum Handler : uint32_t {
                      //   have handlers of their own)
   HD_RED = 118,      // + 3 kind + a: row reduce of treg[a] into rreg[dst] (rows inside a wave)
   HD_REDX = 127,     // + 3 kind + a: OP_REDX (rows across waves)
-  HD_ALL = 136,      // + 3 kind + a: reduce-all partial of treg[a] into LDS buffer b (sum, max)
-  HD_ALL_FIN = 142,  // + kind
+  HD_ALL = 136,      // + 3 kind + a: OP_ALL (sum, max)
+  HD_ALL_FIN = 142,  // (retired with OP_ALL_FIN; the ids stay reserved)
   HD_BCAST = 144,    // + d
   HD_RBIN = 147,
   HD_RUN = 148,

@@ -1281,12 +1281,11 @@ struct Encoder {
     if (st != DVM_OK) return st;
     if (i_sq >= 0) free_dead(i_sq);
     if (o.axis == DVM_AXIS_ALL) {
-      const uint32_t buf = (uint32_t)(n_red++ % N_LDSBUF);
-      emit(enc0(OP_ALL, 0, k, buf, kind, 0, 0), 0);
-      emit(enc0(OP_SYNC, 0, 0, 0, 0, 0, 0), 0);
-      emit(enc0(OP_ALL_FIN, 0, 0, buf, kind, 0, 0), 0);
+      // each lane folds the tile into its running partial; the workgroup's
+      // partial and the combine of the workgroups' partials follow the body
+      // (the VM's reduce-all epilogue)
+      emit(enc0(OP_ALL, 0, k, 0, kind, 0, 0), 0);
       W[H_ALL_KIND] = kind;
-      cross_wave = true;
       free_dead(i);
       return DVM_OK;
     }
@@ -1493,7 +1492,6 @@ struct Encoder {
       case OP_RED: return HD_RED + 3 * sub + a;
       case OP_REDX: return HD_REDX + 3 * sub + a;
       case OP_ALL: return HD_ALL + 3 * sub + a;
-      case OP_ALL_FIN: return HD_ALL_FIN + sub;
       case OP_BCAST: return HD_BCAST + d;
       case OP_RBIN: return HD_RBIN;
       case OP_RUN: return HD_RUN;
@@ -1567,7 +1565,7 @@ struct Encoder {
   // LDS reduction buffers a body instruction writes (and reads) across waves.
   uint32_t red_bufs(uint32_t w) const {
     const uint32_t op = f_op(w);
-    if (op == OP_REDX || op == OP_ALL) return 1u << f_b(w);
+    if (op == OP_REDX) return 1u << f_b(w);
     if (op == OP_UN && f_sub(w) == UN_SOFTMAX && plan.g > 64) return 3u << f_b(w);
     return 0u;
   }
@@ -1810,13 +1808,14 @@ struct Encoder {
       // stream's scratch area); the program records the bytes it needs
       const int si = n_args++;
       uint32_t* b = W + ARG_BASE + si * ARG_WORDS;
-      const uint64_t need = SCRATCH_PART_OFF + 4u * (uint64_t)plan.block_dim;
+      // one partial per workgroup (an empty space still runs one)
+      const uint64_t need = SCRATCH_PART_OFF + 4u * (uint64_t)std::max<int64_t>(plan.grid, 1);
       b[A_DTYPE] = DT_F32;
       b[A_FLAGS] = arg_flags_word(0, need);
       b[A_EXTENT] = (uint32_t)need;
       W[H_ALL_SCRATCH] = (uint32_t)si;
       if (need > SCRATCH_BYTES)
-        return fail(DVM_ERR_RESOURCE, "reduce-all needs %lld partials", (long long)plan.block_dim);
+        return fail(DVM_ERR_RESOURCE, "reduce-all needs %lld partials", (long long)plan.grid);
     }
     for (size_t i = 0; i < ops.size(); ++i) {
       const OpRec& o = ops[i];
@@ -2840,10 +2839,11 @@ dvm_status dvm_launch_noalloc(dvm_context* ctx, const dvm_program* p, void* stre
   if (needs_scratch(p)) {
     if (!ctx->static_scratch)
       return fail(DVM_ERR_DEVICE, "static scratch unavailable: %s", hipGetErrorString(ctx->static_err));
-    const uint64_t need = SCRATCH_PART_OFF + 4u * (uint64_t)p->prog.w[H_BLOCK_DIM];
+    // one partial per launched workgroup
+    const uint64_t need = SCRATCH_PART_OFF + 4u * (uint64_t)p->grid_launch;
     if (need > ctx->static_bytes)
-      return fail(DVM_ERR_RESOURCE, "reduce-all over %u tiles: the static scratch holds %zu partials",
-                  p->prog.w[H_BLOCK_DIM], (ctx->static_bytes - SCRATCH_PART_OFF) / 4);
+      return fail(DVM_ERR_RESOURCE, "reduce-all over %u workgroups: the static scratch holds %zu partials",
+                  p->grid_launch, (ctx->static_bytes - SCRATCH_PART_OFF) / 4);
     Program q = p->prog;
     set_scratch(&q, ctx->static_scratch, ctx->static_bytes);
     e = dvm_static_scratch_clear(ctx->static_scratch, s);

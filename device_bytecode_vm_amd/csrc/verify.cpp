@@ -105,10 +105,8 @@ Effect effect(uint32_t w0, uint32_t w1) {
     e.buf_wr = e.buf_rd = 1u << b;
     e.barrier_mid = true;
   } else if (h >= HD_ALL && h < HD_ALL + 6) {
+    // the lane's running partial: no LDS buffer, no barrier
     e.t_rd = 1u << ((h - HD_ALL) % 3);
-    e.buf_wr = 1u << b;
-  } else if (h == HD_ALL_FIN || h == HD_ALL_FIN + 1) {
-    e.buf_rd = 1u << b;
   } else if (h >= HD_BCAST && h < HD_BCAST + 3) {
     e.r_rd = 1u << a;
     e.t_wr = 1u << (h - HD_BCAST);
@@ -282,6 +280,22 @@ bool verify_vector(Ctx& c) {
     return true;
   };
   if (!body(W[H_BODY_BEGIN], W[H_BODY_END])) return false;
+  // a reduce-all body folds exactly one operand into the lanes' running
+  // partials, of the kind the epilogue combines; an ALL in any other program
+  // would have no epilogue to deliver it
+  {
+    int n_all = 0;
+    bool kind_ok = true;
+    for (uint32_t pc = W[H_BODY_BEGIN]; pc + 1 < W[H_BODY_END]; pc += 2) {
+      const uint32_t h = f_op(W[pc]);
+      if (h >= HD_ALL && h < HD_ALL + 6) {
+        ++n_all;
+        kind_ok = kind_ok && (h - HD_ALL) / 3 == W[H_ALL_KIND];
+      }
+    }
+    if (W[H_TEMPLATE] == TM_ALLREDUCE ? n_all != 1 || !kind_ok : n_all != 0)
+      return c.fail("%d reduce-all instructions in a program of template %u", n_all, W[H_TEMPLATE]);
+  }
   if (W[H_FLAGS] & HF_BRANCH) {
     if (W[H_COND_ARG] >= c.n_args || c.W[ARG_BASE + W[H_COND_ARG] * ARG_WORDS + A_DTYPE] != DT_F32)
       return c.fail("the branch condition is no fp32 operand");

@@ -1182,6 +1182,8 @@ __device__ __forceinline__ void vm_main(const Seg& sg, float (*s_red)[T_LANES / 
   S.t_end = t_end;
   S.alt = 0;
   const uint32_t alt_on = (W[H_FLAGS] & HF_RED_ALT) ? 2u : 0u;
+  // reduce-all: each lane's running partial over the workgroup's tiles
+  float all_acc = W[H_ALL_KIND] == RK_MAX ? -__builtin_huge_valf() : 0.f;
 
   // The body every tile runs.  A branch program reads its condition (a 0-d
   // fp32 operand written by an earlier launch on the stream) once, with a
@@ -1298,7 +1300,12 @@ __device__ __forceinline__ void vm_main(const Seg& sg, float (*s_red)[T_LANES / 
   case HD_BIN + 10 * k + 5 * rev + BF_SCALAR: PROF_ENTER() bin_cs<k, rev>(treg<0>(R), SCALAR_B); break;
 #define CASE_BIN_COMM(k) CASE_BIN_DIR(k, false)
 #define CASE_BIN_NC(k) CASE_BIN_DIR(k, false) CASE_BIN_DIR(k, true)
-#define CASE_RED(kind, a) case HD_ALL + 3 * kind + a: PROF_ENTER() CASE_RED_ROW(kind, a)
+#define CASE_ALL(kind, a)                                                                  \
+  case HD_ALL + 3 * kind + a: PROF_ENTER()                                                  \
+    /* reduce-all: the lane's running partial over this workgroup's tiles */                \
+    all_acc = comb<kind>(all_acc, lane_partial<kind>(treg<a>(R), G, tl, L));               \
+    break;
+#define CASE_RED(kind, a) CASE_ALL(kind, a) CASE_RED_ROW(kind, a)
 #define CASE_RED_ROW(kind, a)                                                              \
   case HD_RED + 3 * kind + a: PROF_ENTER()                                                              \
   case HD_REDX + 3 * kind + a: PROF_ENTER() {                                                           \
@@ -1309,23 +1316,21 @@ __device__ __forceinline__ void vm_main(const Seg& sg, float (*s_red)[T_LANES / 
       rset(R.rw, f_dst(w0), group_reduce<kind>(acc, gs));                                  \
       ROW_RUN_TAIL();                                                                      \
     } else {                                                                               \
-      /* per-wave partial into LDS (after the 64-lane all-reduce every lane */             \
-      /* holds it, so every lane stores it: no lane-dependent branch) */                   \
+      /* rows across waves: per-wave partial into LDS (after the 64-lane */                \
+      /* all-reduce every lane holds it, so every lane stores it: no */                    \
+      /* lane-dependent branch), barrier, then combine the row's partials */               \
       acc = group_reduce<kind>(acc, 64);                                                   \
       float* buf = s_red[f_b(w0) ^ S.alt];                                                 \
       buf[wave] = acc;                                                                     \
-      if (h == HD_REDX + 3 * kind + a) {                                                   \
-        /* rows across waves: barrier, then combine the row's partials */                  \
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");                                 \
-        __builtin_amdgcn_s_barrier();                                                      \
-        asm volatile("" ::: "memory");                                                     \
-        const int nw = G.g >> 6;                                                           \
-        const float* rb = buf + L.row * nw;                                                \
-        float r = rb[0];                                                                   \
-        for (int k = 1; k < nw; ++k) r = comb<kind>(r, rb[k]);                             \
-        rset(R.rw, f_dst(w0), r);                                                          \
-        ROW_RUN_TAIL();                                                                    \
-      }                                                                                    \
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");                                   \
+      __builtin_amdgcn_s_barrier();                                                        \
+      asm volatile("" ::: "memory");                                                       \
+      const int nw = G.g >> 6;                                                             \
+      const float* rb = buf + L.row * nw;                                                  \
+      float r = rb[0];                                                                     \
+      for (int k = 1; k < nw; ++k) r = comb<kind>(r, rb[k]);                               \
+      rset(R.rw, f_dst(w0), r);                                                            \
+      ROW_RUN_TAIL();                                                                      \
     }                                                                                      \
     break;                                                                                 \
   }
@@ -1471,23 +1476,6 @@ __device__ __forceinline__ void vm_main(const Seg& sg, float (*s_red)[T_LANES / 
       CASE_RED(RK_SUM, 0) CASE_RED(RK_SUM, 1) CASE_RED(RK_SUM, 2)
       CASE_RED(RK_MAX, 0) CASE_RED(RK_MAX, 1) CASE_RED(RK_MAX, 2)
       CASE_RED_ROW(RK_SUMSQ, 0) CASE_RED_ROW(RK_SUMSQ, 1) CASE_RED_ROW(RK_SUMSQ, 2)
-      case HD_ALL_FIN + RK_SUM: PROF_ENTER()
-      case HD_ALL_FIN + RK_MAX: PROF_ENTER() {
-        // every lane combines the per-wave partials (LDS broadcast reads);
-        // lane 0 alone stores the tile's partial, the others are masked by an
-        // out-of-range offset
-        const uint32_t kind = f_op(w0) - HD_ALL_FIN;
-        const float* buf = s_red[f_b(w0) ^ S.alt];
-        float acc = buf[0];
-        for (int k = 1; k < T_LANES / 64; ++k) acc = kind == RK_SUM ? acc + buf[k] : comb<RK_MAX>(acc, buf[k]);
-        // the partials' descriptor ends where the scratch operand ends (its
-        // extent is the area the launch supplied)
-        const ArgD a = read_arg(W, W[H_ALL_SCRATCH]);
-        const Rsrc rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(a.p) + 256, 0,
-                                                          (int)part_bytes(a.extent, block_dim), RSRC_W3);
-        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc), rs, lane_off(tidv == 0, (int)(tl.id * 4u)), 0, 0);
-        break;
-      }
       case HD_SYNC: PROF_ENTER()
         // LDS exchange only: wait for this wave's LDS operations, then meet
         // the other waves (no wait on outstanding global loads, so prefetches
@@ -1581,15 +1569,28 @@ __device__ __forceinline__ void vm_main(const Seg& sg, float (*s_red)[T_LANES / 
 #undef CASE_RED
   }
 
-  // Reduce-all epilogue: the last workgroup to finish combines the per-tile
-  // partials in tile order (deterministic) and writes the scalar result.
+  // Reduce-all epilogue: each workgroup stores one partial (its lanes'
+  // running partials, each over the workgroup's tiles in order, combined
+  // across the wave, then the waves in order), and the last workgroup to
+  // finish combines the partials in workgroup order (deterministic) and
+  // writes the scalar result.
   if (W[H_TEMPLATE] == TM_ALLREDUCE) {
     const uint32_t kind = W[H_ALL_KIND];
     const ArgD sa = read_arg(W, W[H_ALL_SCRATCH]);
     uint32_t* counter = reinterpret_cast<uint32_t*>(const_cast<char*>(sa.p));
     float* part = reinterpret_cast<float*>(const_cast<char*>(sa.p) + 256);
+    // partials never go past the area the launch supplied
+    const uint32_t part_b = part_bytes(sa.extent, sg.grid);
+    {
+      const float wv = kind == RK_SUM ? group_reduce<RK_SUM>(all_acc, 64) : group_reduce<RK_MAX>(all_acc, 64);
+      if ((tid & 63) == 0) s_red[0][wave] = wv;
+    }
     __syncthreads();
     if (tid == 0) {
+      float r = s_red[0][0];
+      for (int k = 1; k < T_LANES / 64; ++k) r = kind == RK_SUM ? r + s_red[0][k] : comb<RK_MAX>(r, s_red[0][k]);
+      const Rsrc rw = __builtin_amdgcn_make_buffer_rsrc(part, 0, (int)part_b, RSRC_W3);
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(r), rw, (int)(sg.b * 4u), 0, 0);
       __atomic_thread_fence(__ATOMIC_RELEASE);
       const uint32_t prev = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
       s_last = prev == sg.grid - 1;
@@ -1598,7 +1599,7 @@ __device__ __forceinline__ void vm_main(const Seg& sg, float (*s_red)[T_LANES / 
     if (s_last) {
       __atomic_thread_fence(__ATOMIC_ACQUIRE);
       float acc = kind == RK_SUM ? 0.f : -__builtin_huge_valf();
-      const uint32_t n_part = part_bytes(sa.extent, block_dim) / 4u;  // never past the area
+      const uint32_t n_part = part_b / 4u;  // one per workgroup, never past the area
       // Past the acquire fence the partials are read with plain loads (the
       // fence invalidated this workgroup's caches, and every writer released
       // its partial before counting itself in), eight per lane in flight at a

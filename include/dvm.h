@@ -219,7 +219,8 @@ dvm_status dvm_launch(dvm_context* ctx, const dvm_program* p, void* stream);
  * reduce-alls launch exactly as with dvm_launch.  A reduce-all runs on the
  * library's static scratch array instead of the stream's allocated area: one
  * array per GPU, held until the process ends, of 256 + 4 * 65536 bytes (a
- * counter and at most 65536 tile partials); a program over more tiles returns
+ * counter and at most 65536 partials, one per workgroup; the tiling runs at
+ * most 4096 workgroups); a program launching more workgroups returns
  * DVM_ERR_RESOURCE without launching.  Before the program the call queues a
  * one-workgroup kernel that zeroes the counter, on the same stream.  Every call
  * on a GPU shares that GPU's array and it keeps the last call's contents:

@@ -16,7 +16,7 @@ from device_bytecode_vm_amd import TensorDesc as TD
 from device_bytecode_vm_amd import _lib as L
 
 H_BODY_BEGIN, H_BODY_END, H_FLAGS = 16, 17, 26
-HD_REDX, HD_ALL, HD_SYNC = 127, 136, 149
+HD_REDX, HD_SYNC = 127, 149
 HF_RED_ALT = 8
 N_LDSBUF = 8
 
@@ -53,7 +53,7 @@ def fenced(instrs, n_tiles=3, alt=False):
     """Simulates n_tiles copies of the body and checks every write of a
     cross-wave buffer against the reads of the same buffer since the last
     barrier: a write may only follow reads that a barrier separates from it.
-    REDX = write, barrier, read; ALL = write (its SYNC and ALL_FIN follow).
+    REDX = write, barrier, read (reduce-alls keep their partials in registers).
     alt: the workgroup's odd tiles use buffer b ^ 2 (HF_RED_ALT)."""
     reads_since_barrier = set()
     for t in range(n_tiles):
@@ -63,13 +63,8 @@ def fenced(instrs, n_tiles=3, alt=False):
                 if b in reads_since_barrier:
                     return False
                 reads_since_barrier = {b}          # its own barrier, then its read
-            elif HD_ALL <= h < HD_ALL + 6:
-                if b in reads_since_barrier:
-                    return False
             elif h == HD_SYNC:
                 reads_since_barrier = set()
-            elif h == 142 or h == 143:             # ALL_FIN reads its buffer
-                reads_since_barrier.add(b)
     return True
 
 
@@ -126,4 +121,4 @@ def test_reduce_all_program_has_no_scratch_address(ectx):
     assert h["tmpl"] == 2 and h["body_tile"] > 1
     a = ARG_BASE + w[H_ALL_SCRATCH] * ARG_WORDS
     assert w[a] == 0 and w[a + 1] == 0               # supplied per stream at launch
-    assert w[a + 7] == 256 + 4 * h["block_dim"]      # the bytes the program needs
+    assert w[a + 7] == 256 + 4 * h["grid"]           # the bytes the program needs: one partial per workgroup

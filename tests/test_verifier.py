@@ -293,13 +293,19 @@ def test_operand_reuse_fuzz_verifies(ectx):
 
 
 def test_planted_missing_buffer_alternation(ectx):
-    """A reduce-all has one cross-wave reduction per tile: its buffers
-    alternate by tile parity (HF_RED_ALT) instead of an end-of-body barrier.
-    With the flag cleared the next tile's write races the last reads."""
+    """A row sum whose rows span waves has one cross-wave reduction per
+    tile: its buffers alternate by tile parity (HF_RED_ALT) instead of an
+    end-of-body barrier.  With the flag cleared the next tile's write races
+    the last reads."""
     H_FLAGS, HF_RED_ALT = 26, 8
     g = dvm.Graph(ectx)
-    g.op("reduce_sum", g.input(TD(A(), "f32", (16384, 4096))), out=TD(A(), "f32", ()), live=True, axis=L.AXIS_ALL)
-    (p,) = drain(g)
+    shape = (4096, 6000)
+    x = g.input(TD(A(), "f32", shape))
+    s = g.op("reduce_sum", x)
+    g.op("sub", x, s, out=TD(A(), "f32", shape), live=True)
+    g.release(s)
+    p = g.flush()
+    assert p.header()["g"] > 64 and p.header()["body_tile"] > 1
     w = p.words()
     assert w[H_FLAGS] & HF_RED_ALT and w[w[H_BODY_END] - 2] & 0xFF != HD_SYNC
     assert p.verify() is None
@@ -308,3 +314,25 @@ def test_planted_missing_buffer_alternation(ectx):
         w[H_FLAGS] &= ~HF_RED_ALT
     msg = planted(p, clear_alt).verify()
     assert msg and "before every wave read it" in msg
+
+
+def test_reduce_all_body_and_planted_second_all(ectx):
+    """A reduce-all body folds its operand into the lanes' running partials:
+    one ALL instruction, no cross-wave buffer and no barrier per tile (the
+    workgroup's partial and the final combine are the VM's epilogue).  A
+    second ALL, or one of the other kind, is rejected."""
+    H_FLAGS, H_ALL_KIND = 26, 22
+    HD_ALL = 136
+    g = dvm.Graph(ectx)
+    g.op("reduce_sum", g.input(TD(A(), "f32", (16384, 4096))), out=TD(A(), "f32", ()), live=True, axis=L.AXIS_ALL)
+    (p,) = drain(g)
+    w = p.words()
+    hs = [w[i] & 0xFF for i in range(w[H_BODY_BEGIN], w[H_BODY_END], 2)]
+    assert sum(HD_ALL <= h < HD_ALL + 6 for h in hs) == 1 and HD_SYNC not in hs
+    assert not (w[H_FLAGS] & 8)
+    assert p.verify() is None
+
+    def other_kind(w):
+        w[H_ALL_KIND] = 1
+    msg = planted(p, other_kind).verify()
+    assert msg and "reduce-all instructions" in msg

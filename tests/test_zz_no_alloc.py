@@ -2,7 +2,7 @@
 dvm_launch, through the C ABI.
 
 Reduce-all programs are the ones whose kernels use scratch (a counter and one
-partial per tile).  Both entry points run the same kernel, tile order and
+partial per workgroup).  Both entry points run the same kernel, tile order and
 partial combine, so the results must be bit-identical.  Two calls in a row,
 the second over a smaller input, so the second call runs on an array that
 still holds the first call's partials and counter history.
@@ -83,16 +83,19 @@ def test_noalloc_elementwise_and_limit(dvm):
     g2.flush().launch(stream, ctx=dctx)
     torch.cuda.synchronize()
     assert torch.equal(out, ref)
-    # a reduce-all over more than 65536 tiles does not fit the static array:
-    # refused on the host, nothing launched
-    say("noalloc_limit")
-    big = torch.zeros((200000, 4096), dtype=torch.float32, device="cuda")   # 123077 tiles
+    # a reduce-all over more tiles than the static array has partial slots
+    # (65536) still fits: partials are per workgroup, and the tiling launches
+    # at most 4096 workgroups
+    say("noalloc_many_tiles")
+    big = np.random.default_rng(5).standard_normal((200000, 4096), dtype=np.float32)   # 123077 tiles
+    dbig = torch.from_numpy(big).cuda()
     s = torch.full((), 7.0, dtype=torch.float32, device="cuda")
-    p = encode_reduce_all(dvm, ectx, big, s, "reduce_sum")
-    assert p.header()["block_dim"] > 65536
-    with pytest.raises(dvm.DvmError) as e:
-        p.launch_noalloc(stream, ctx=dctx)
-    assert e.value.status == L.ERR_RESOURCE
+    s2 = torch.full((), 7.0, dtype=torch.float32, device="cuda")
+    p = encode_reduce_all(dvm, ectx, dbig, s, "reduce_sum")
+    assert p.header()["block_dim"] > 65536 and p.header()["grid"] <= 4096
+    p.launch_noalloc(stream, ctx=dctx)
+    encode_reduce_all(dvm, ectx, dbig, s2, "reduce_sum").launch(stream, ctx=dctx)
     torch.cuda.synchronize()
-    assert float(s.item()) == 7.0
-    del big
+    assert float(s.item()) == float(s2.item())
+    assert abs(float(s.item()) - float(np.sum(big, dtype=np.float64))) <= O.sum_guard_band(big)
+    del big, dbig
