@@ -1442,7 +1442,8 @@ struct Encoder {
           pro.push_back((uint32_t)arg_of[s]);
           ++n_inv;
         } else if (!invariant && n_pf < 2 && (a[A_FLAGS] & AF_VEC) && sc == 1 && (es == 2 || es == 4)) {
-          const uint32_t sz = (uint32_t)nvm * T_LANES * 16u * (uint32_t)(es / 2);
+          // the tile's nv chunks (the VM fills and reads no others)
+          const uint32_t sz = (uint32_t)plan.nv * T_LANES * 16u * (uint32_t)(es / 2);
           if (off + sz > budget) continue;
           pf_slot[s] = n_pf;
           W[H_PF_OFF0 + n_pf] = off;

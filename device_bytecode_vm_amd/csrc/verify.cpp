@@ -202,6 +202,8 @@ bool verify_vector(Ctx& c) {
   if (W[H_LDS_BYTES] > budget) return c.fail("dynamic LDS %u exceeds %u", W[H_LDS_BYTES], budget);
   // prologue
   int pf_arg[2] = {-1, -1}, inv_arg[2] = {-1, -1};
+  // staging areas [begin, end) in the dynamic LDS, checked disjoint below
+  std::vector<std::pair<uint32_t, uint32_t>> areas;
   for (uint32_t pc = W[H_PRO_BEGIN]; pc < W[H_PRO_END]; pc += 2) {
     const uint32_t w0 = W[pc], w1 = W[pc + 1];
     const uint32_t h = f_op(w0);
@@ -210,10 +212,13 @@ bool verify_vector(Ctx& c) {
       if (pf_arg[s] >= 0) return c.fail("word %u: prefetch slot %u filled twice", pc, (uint32_t)s);
       pf_arg[s] = (int)w1;
       if (w1 >= c.n_args) return c.fail("word %u: operand %u outside the table", pc, w1);
-      // nvk chunks x 256 lanes x 16 bytes per 16-bit half of the element
+      if (f_a(w0) != 0) return c.fail("word %u: a prefetch of a tile other than the workgroup's first", pc);
+      // the tile's nv chunks x 256 lanes x 16 bytes per 16-bit half of the element
       const uint32_t halves = W[ARG_BASE + w1 * ARG_WORDS + A_DTYPE] == DT_F32 ? 2u : 1u;
-      if (W[H_PF_OFF0 + s] + (uint32_t)nvk * T_LANES * 16u * halves > W[H_LDS_BYTES])
+      const uint32_t sz = W[H_NV] * T_LANES * 16u * halves;
+      if (W[H_PF_OFF0 + s] + sz > W[H_LDS_BYTES])
         return c.fail("prefetch slot %u outside the dynamic LDS (%u bytes)", (uint32_t)s, W[H_LDS_BYTES]);
+      areas.push_back({W[H_PF_OFF0 + s], W[H_PF_OFF0 + s] + sz});
     } else if (h == HD_LDS_INV) {
       const int s = (int)(f_dst(w0) & 1u);
       inv_arg[s] = (int)w1;
@@ -221,10 +226,33 @@ bool verify_vector(Ctx& c) {
       const uint32_t lanes = W[H_INV_SHARED0 + s] ? g : (uint32_t)T_LANES;
       if (W[H_INV_OFF0 + s] + (uint32_t)nvk * lanes * 32u > W[H_LDS_BYTES])
         return c.fail("invariant slot %u outside the dynamic LDS (%u bytes)", (uint32_t)s, W[H_LDS_BYTES]);
+      areas.push_back({W[H_INV_OFF0 + s], W[H_INV_OFF0 + s] + (uint32_t)nvk * lanes * 32u});
     } else {
       return c.fail("word %u: handler %u in the prologue", pc, h);
     }
     if (!check_arg_index(c, (int)w1, pc)) return false;
+  }
+  // the cross-wave reduction buffers (rows across waves, a fused softmax
+  // across waves, the reduce-all epilogue) need their area too
+  {
+    bool red = W[H_TEMPLATE] == TM_ALLREDUCE;
+    auto scan = [&](uint32_t b0, uint32_t b1) {
+      for (uint32_t pc = b0; pc + 1 < b1; pc += 2) {
+        const uint32_t h = f_op(W[pc]);
+        red = red || (h >= HD_REDX && h < HD_REDX + 9) || (h == HD_SOFTMAX && g > 64);
+      }
+    };
+    scan(W[H_BODY_BEGIN], W[H_BODY_END]);
+    if (W[H_FLAGS] & HF_BRANCH) scan(W[H_ALT_BEGIN], W[H_ALT_END]);
+    if (red) {
+      if (W[H_RED_OFF] + RED_LDS_BYTES > W[H_LDS_BYTES])
+        return c.fail("reduction buffers outside the dynamic LDS (%u bytes)", W[H_LDS_BYTES]);
+      areas.push_back({W[H_RED_OFF], W[H_RED_OFF] + RED_LDS_BYTES});
+    }
+    std::sort(areas.begin(), areas.end());
+    for (size_t k = 1; k < areas.size(); ++k)
+      if (areas[k].first < areas[k - 1].second)
+        return c.fail("LDS staging areas overlap at byte %u", areas[k].first);
   }
   // the bodies: registers, staging and operands per tile; reduction buffers
   // over three consecutive tiles

@@ -174,8 +174,8 @@ def test_encoder_tiling_equals_oracle_rowreduce(ectx):
         vec = base % al == 0 and (len(shape) == 1 or (cols * esz) % al == 0)
 
         def staged(pl, budget, nvk):
-            # slots hold the VM build's nvk chunks per lane
-            return pl.body_tile >= 2 and vec and nvk * 256 * 16 * (esz // 2) <= budget
+            # a prefetch slot holds the tile's nv chunks per lane
+            return pl.body_tile >= 2 and vec and pl.nv * 256 * 16 * (esz // 2) <= budget
 
         # the wide build's LDS budget is 80 KiB less its cross-wave reduction
         # buffers (144 bytes) when rows span waves; staging counts only where
@@ -204,11 +204,12 @@ def test_encoder_layernorm_workload_headers(ectx):
 
         def staged(pl, budget, nvk):
             # x prefetched (bf16), then gamma and beta held as one shared fp32
-            # row; slots hold the VM build's nvk chunks per lane
+            # row; a prefetch slot holds the tile's nv chunks per lane, an
+            # invariant slot the VM build's nvk
             if pl.body_tile < 2:
                 return 0, 0
             off, pf, inv = 0, 0, 0
-            for sz, kind in ((nvk * 256 * 16, "pf"), (nvk * pl.g * 32, "inv"), (nvk * pl.g * 32, "inv")):
+            for sz, kind in ((pl.nv * 256 * 16, "pf"), (nvk * pl.g * 32, "inv"), (nvk * pl.g * 32, "inv")):
                 if off + sz <= budget:
                     off += sz
                     pf, inv = (pf + 1, inv) if kind == "pf" else (pf, inv + 1)

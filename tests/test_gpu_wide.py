@@ -39,13 +39,13 @@ def ctx(dvm):
 
 # (rows, cols, kernel type for bf16 / fp32 input): a few rows of 6484 stay on
 # the standard VM (the cost model puts one row in a tile on either variant);
-# an fp32 row of 6484-8192 stays there too (the wide prefetch slot, 10
-# chunks of fp32 per lane, would not fit next to the reduction buffers, and
-# the standard plan stages it); rows of 10241 and more fit only the wide VM
-@pytest.mark.parametrize("rows,cols,kts", [(3, 6484, (0, 0)), (3000, 6484, (WIDE, 0)), (3000, 8192, (WIDE, 0)),
+# rows of 6484-8192 take the wide VM in both dtypes (a prefetch slot holds the
+# tile's nv chunks: 7-8 chunks of fp32 per lane fit next to the reduction
+# buffers); rows of 10241 and more fit only the wide VM
+@pytest.mark.parametrize("rows,cols,kts", [(3, 6484, (0, 0)), (3000, 6484, (WIDE, WIDE)), (3000, 8192, (WIDE, WIDE)),
                                            (64, 10241, (WIDE, WIDE)), (40, 16384, (WIDE, WIDE)),
-                                           (7, 20480, (WIDE, WIDE)), (3000, 6485, (WIDE, 0)),
-                                           (3000, 6487, (WIDE, 0)), (9, 12345, (WIDE, WIDE))])
+                                           (7, 20480, (WIDE, WIDE)), (3000, 6485, (WIDE, WIDE)),
+                                           (3000, 6487, (WIDE, WIDE)), (9, 12345, (WIDE, WIDE))])
 @pytest.mark.parametrize("dt", ["bf16", "f32"])
 def test_wide_softmax(dvm, ctx, rows, cols, kts, dt):
     kt = kts[0] if dt == "bf16" else kts[1]

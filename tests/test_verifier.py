@@ -336,3 +336,31 @@ def test_reduce_all_body_and_planted_second_all(ectx):
         w[H_ALL_KIND] = 1
     msg = planted(p, other_kind).verify()
     assert msg and "reduce-all instructions" in msg
+
+
+def test_planted_lds_area_overlap(ectx):
+    """Staging areas must be disjoint: a prefetch slot moved onto the
+    cross-wave reduction buffers, or reduction buffers past the dynamic LDS,
+    are rejected."""
+    H_LDS_BYTES, H_PF_OFF0, H_RED_OFF = 27, 28, 39
+    g = dvm.Graph(ectx)
+    shape = (4096, 6000)
+    x = g.input(TD(A(), "f32", shape))
+    s = g.op("reduce_sum", x)
+    g.op("sub", x, s, out=TD(A(), "f32", shape), live=True)
+    g.release(s)
+    p = g.flush()
+    w = p.words()
+    hs = [w[i] & 0xFF for i in range(w[14], w[15], 2)]
+    assert 154 in hs and w[H_RED_OFF] > 0           # a prefetch slot and the reduction area
+    assert p.verify() is None
+
+    def onto_red(w):
+        w[H_PF_OFF0] = w[H_RED_OFF]
+    msg = planted(p, onto_red).verify()
+    assert msg and ("overlap" in msg or "outside the dynamic LDS" in msg), msg
+
+    def red_past_end(w):
+        w[H_RED_OFF] = w[H_LDS_BYTES] - 8
+    msg = planted(p, red_past_end).verify()
+    assert msg and "reduction buffers outside the dynamic LDS" in msg, msg
