@@ -146,7 +146,7 @@ class Program:
 
     def launch_noalloc(self, stream=None, ctx=None):
         """dvm_launch_noalloc: no device allocation; a reduce-all uses the
-        library's static scratch array (at most 65536 tiles)."""
+        library's static scratch array (at most 65536 workgroup partials)."""
         check(lib.dvm_launch_noalloc((ctx or self.ctx).h, self.h, _stream_handle(stream)))
 
     PROF_COUNTERS = 5

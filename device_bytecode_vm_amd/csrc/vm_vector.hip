@@ -1591,13 +1591,18 @@ __device__ __forceinline__ void vm_main(const Seg& sg, float (*s_red)[T_LANES / 
       for (int k = 1; k < T_LANES / 64; ++k) r = kind == RK_SUM ? r + s_red[0][k] : comb<RK_MAX>(r, s_red[0][k]);
       const Rsrc rw = __builtin_amdgcn_make_buffer_rsrc(part, 0, (int)part_b, RSRC_W3);
       __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(r), rw, (int)(sg.b * 4u), 0, 0);
-      __atomic_thread_fence(__ATOMIC_RELEASE);
+      // the increment's release (device scope, which is all the partials
+      // need) orders the partial before it; a system-scope fence here would
+      // add a second write-back of the L2 per workgroup
       const uint32_t prev = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
       s_last = prev == sg.grid - 1;
     }
     __syncthreads();
     if (s_last) {
-      __atomic_thread_fence(__ATOMIC_ACQUIRE);
+      // thread 0's increment acquired every writer's release; the barrier
+      // carries that to this workgroup's other threads, and each thread's
+      // device-scope acquire drops stale cache lines before the reads
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
       float acc = kind == RK_SUM ? 0.f : -__builtin_huge_valf();
       const uint32_t n_part = part_b / 4u;  // one per workgroup, never past the area
       // Past the acquire fence the partials are read with plain loads (the
