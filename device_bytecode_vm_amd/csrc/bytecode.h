@@ -128,9 +128,10 @@ __host__ __device__ constexpr int mm_lds_bytes(int tm, int tn) {
 //    each wave's indices are 64 consecutive values (lane-private slots, or
 //    g a multiple of 64); others go through registers.
 // The budget keeps two workgroups resident per compute unit (160 KB of LDS).
-// Both VM builds keep their cross-wave reduction buffers (and the reduce-all
-// flag) in the dynamic area, reserved only by programs that use them, so two
-// workgroups may take the whole 160 KB (two fp32 prefetch slots of 40 KB).
+// Both VM builds keep their cross-wave reduction buffers in the dynamic area,
+// reserved only by programs that use them (16 bytes of the reservation are
+// spare), so two workgroups may take the whole 160 KB (two fp32 prefetch
+// slots of 40 KB).
 constexpr uint32_t LDS_BUDGET = 80u * 1024u;
 constexpr uint32_t RED_LDS_BYTES = N_LDSBUF * (T_LANES / 64) * 4 + 16;
 

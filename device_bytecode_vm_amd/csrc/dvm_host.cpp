@@ -36,7 +36,8 @@ extern "C" hipError_t dvm_launch_vector_prof_kernel(const Program* p, unsigned g
 extern "C" hipError_t dvm_launch_vector_kernel_wide(const Program* p, unsigned grid, unsigned lds, hipStream_t s);
 extern "C" hipError_t dvm_launch_vector_prof_kernel_wide(const Program* p, unsigned grid, hipStream_t s);
 extern "C" hipError_t dvm_static_scratch_init(int device, void** ptr, size_t* bytes);
-extern "C" hipError_t dvm_static_scratch_clear(void* area, hipStream_t s);
+extern "C" hipError_t dvm_launch_allreduce_combine(const float* part, uint32_t n_part, uint32_t kind, void* out,
+                                                   uint32_t out_dt, hipStream_t s);
 
 namespace {
 
@@ -2254,6 +2255,22 @@ hipError_t launch_kernel(const dvm_program* p, const Program* q, hipStream_t s) 
   return launch_words(q, ktype_of(p), p->grid_launch, p->lds, s);
 }
 
+// The second launch of a reduce-all program (q: its words with the scratch
+// area set): folds the workgroups' partials, which the stream orders before
+// it, into the scalar output.
+hipError_t launch_combine(const dvm_program* p, const Program* q, hipStream_t s) {
+  const uint32_t* W = q->w;
+  const uint32_t* sa = W + ARG_BASE + W[H_ALL_SCRATCH] * ARG_WORDS;
+  const uint32_t* oa = W + ARG_BASE + W[H_ALL_OUT] * ARG_WORDS;
+  const uint64_t area = ((uint64_t)sa[A_PTR_HI] << 32) | sa[A_PTR_LO];
+  const uint64_t out = ((uint64_t)oa[A_PTR_HI] << 32) | oa[A_PTR_LO];
+  // one partial per launched workgroup, never past the area
+  const uint64_t slots = sa[A_EXTENT] > SCRATCH_PART_OFF ? (sa[A_EXTENT] - SCRATCH_PART_OFF) / 4u : 0u;
+  const uint32_t n_part = (uint32_t)std::min<uint64_t>(p->grid_launch, slots);
+  return dvm_launch_allreduce_combine(reinterpret_cast<const float*>((uintptr_t)(area + SCRATCH_PART_OFF)), n_part,
+                                      W[H_ALL_KIND], reinterpret_cast<void*>((uintptr_t)out), oa[A_DTYPE], s);
+}
+
 dvm_status launch(dvm_context* ctx, const dvm_program* p, hipStream_t s) {
   if (!ctx || ctx->device < 0) return fail(DVM_ERR_DEVICE, "encode-only context cannot launch");
   if (p->grid_launch == 0) return DVM_OK;
@@ -2265,6 +2282,7 @@ dvm_status launch(dvm_context* ctx, const dvm_program* p, hipStream_t s) {
     Program q = p->prog;  // the launch copies its argument: a stack copy is enough
     set_scratch(&q, area, SCRATCH_BYTES);
     e = launch_kernel(p, &q, s);
+    if (e == hipSuccess) e = launch_combine(p, &q, s);
   } else {
     e = launch_kernel(p, &p->prog, s);
   }
@@ -2847,8 +2865,8 @@ dvm_status dvm_launch_noalloc(dvm_context* ctx, const dvm_program* p, void* stre
                   p->grid_launch, (ctx->static_bytes - SCRATCH_PART_OFF) / 4);
     Program q = p->prog;
     set_scratch(&q, ctx->static_scratch, ctx->static_bytes);
-    e = dvm_static_scratch_clear(ctx->static_scratch, s);
-    if (e == hipSuccess) e = launch_kernel(p, &q, s);
+    e = launch_kernel(p, &q, s);
+    if (e == hipSuccess) e = launch_combine(p, &q, s);
   } else {
     e = launch_kernel(p, &p->prog, s);
   }
@@ -2893,6 +2911,7 @@ dvm_status launch_twin(dvm_context* ctx, const dvm_program* p, void* stream, uin
   q.w[H_PROF_HI] = (uint32_t)(a >> 32);
   hipError_t e = kt == KT_VECTOR_WIDE ? dvm_launch_vector_prof_kernel_wide(&q, p->grid_launch, (hipStream_t)stream)
                                       : dvm_launch_vector_prof_kernel(&q, p->grid_launch, (hipStream_t)stream);
+  if (e == hipSuccess && needs_scratch(p)) e = launch_combine(p, &q, (hipStream_t)stream);
   if (e != hipSuccess) return fail(DVM_ERR_DEVICE, "launch failed: %s", hipGetErrorString(e));
   return DVM_OK;
 }

@@ -12,7 +12,8 @@
 
 #include <mutex>
 
-// a counter (4 bytes) at byte 0, the per-tile partials from byte 256: 65536 of them
+// the per-workgroup partials from byte 256 (the first 256 bytes are spare):
+// 65536 of them
 constexpr size_t DVM_STATIC_SCRATCH_BYTES = 256 + 4 * 65536;
 
 static __device__ __align__(256) unsigned char scratch[DVM_STATIC_SCRATCH_BYTES];
@@ -23,12 +24,6 @@ std::mutex g_mu;
 void* g_ptr[MAX_DEVICES];
 hipError_t g_err[MAX_DEVICES];
 bool g_done[MAX_DEVICES];
-
-// Zeroes the counter word (the one part of the area that must start at zero)
-// with a kernel rather than a memset, so a caller may capture the launch.
-__global__ void dvm_clear_scratch_counter(uint32_t* counter) {
-  if (threadIdx.x == 0) *counter = 0u;
-}
 }  // namespace
 
 // Device address of the array on `device`, which must be the current device.
@@ -46,10 +41,4 @@ extern "C" hipError_t dvm_static_scratch_init(int device, void** ptr, size_t* by
   }
   *ptr = g_ptr[device];
   return g_err[device];
-}
-
-// Queues the counter clear on stream s (area = the address from init).
-extern "C" hipError_t dvm_static_scratch_clear(void* area, hipStream_t s) {
-  hipLaunchKernelGGL(dvm_clear_scratch_counter, dim3(1), dim3(64), 0, s, static_cast<uint32_t*>(area));
-  return hipGetLastError();
 }

@@ -1142,7 +1142,7 @@ __device__ __forceinline__ Seg segment_of() {
 }
 
 template <bool PROF>
-__device__ __forceinline__ void vm_main(const Seg& sg, float (*s_red)[T_LANES / 64], int& s_last, char* dlds) {
+__device__ __forceinline__ void vm_main(const Seg& sg, float (*s_red)[T_LANES / 64], char* dlds) {
   KW* W = sg.W;
   uint64_t p_start = 0, p_top = 0, p_ent = 0, p_dec = 0, p_exe = 0, p_tile = 0, p_n = 0;
   if constexpr (PROF) p_start = __builtin_amdgcn_s_memtime();
@@ -1571,16 +1571,13 @@ __device__ __forceinline__ void vm_main(const Seg& sg, float (*s_red)[T_LANES / 
 
   // Reduce-all epilogue: each workgroup stores one partial (its lanes'
   // running partials, each over the workgroup's tiles in order, combined
-  // across the wave, then the waves in order), and the last workgroup to
-  // finish combines the partials in workgroup order (deterministic) and
-  // writes the scalar result.
+  // across the wave, then the waves in order).  The combine of the partials
+  // is a second launch on the same stream (dvm_allreduce_combine), so no
+  // workgroup waits for or publishes to another inside this one.
   if (W[H_TEMPLATE] == TM_ALLREDUCE) {
     const uint32_t kind = W[H_ALL_KIND];
     const ArgD sa = read_arg(W, W[H_ALL_SCRATCH]);
-    uint32_t* counter = reinterpret_cast<uint32_t*>(const_cast<char*>(sa.p));
     float* part = reinterpret_cast<float*>(const_cast<char*>(sa.p) + 256);
-    // partials never go past the area the launch supplied
-    const uint32_t part_b = part_bytes(sa.extent, sg.grid);
     {
       const float wv = kind == RK_SUM ? group_reduce<RK_SUM>(all_acc, 64) : group_reduce<RK_MAX>(all_acc, 64);
       if ((tid & 63) == 0) s_red[0][wave] = wv;
@@ -1589,55 +1586,9 @@ __device__ __forceinline__ void vm_main(const Seg& sg, float (*s_red)[T_LANES / 
     if (tid == 0) {
       float r = s_red[0][0];
       for (int k = 1; k < T_LANES / 64; ++k) r = kind == RK_SUM ? r + s_red[0][k] : comb<RK_MAX>(r, s_red[0][k]);
-      const Rsrc rw = __builtin_amdgcn_make_buffer_rsrc(part, 0, (int)part_b, RSRC_W3);
+      // partials never go past the area the launch supplied
+      const Rsrc rw = __builtin_amdgcn_make_buffer_rsrc(part, 0, (int)part_bytes(sa.extent, sg.grid), RSRC_W3);
       __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(r), rw, (int)(sg.b * 4u), 0, 0);
-      // the increment's release (device scope, which is all the partials
-      // need) orders the partial before it; a system-scope fence here would
-      // add a second write-back of the L2 per workgroup
-      const uint32_t prev = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-      s_last = prev == sg.grid - 1;
-    }
-    __syncthreads();
-    if (s_last) {
-      // thread 0's increment acquired every writer's release; the barrier
-      // carries that to this workgroup's other threads, and each thread's
-      // device-scope acquire drops stale cache lines before the reads
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-      float acc = kind == RK_SUM ? 0.f : -__builtin_huge_valf();
-      const uint32_t n_part = part_b / 4u;  // one per workgroup, never past the area
-      // Past the acquire fence the partials are read with plain loads (the
-      // fence invalidated this workgroup's caches, and every writer released
-      // its partial before counting itself in), eight per lane in flight at a
-      // time; each lane still folds its partials tid, tid + T, tid + 2T, ... in
-      // increasing order, so the sum is the same in every run.
-      const Rsrc rp = __builtin_amdgcn_make_buffer_rsrc(part, 0, (int)(n_part * 4u), RSRC_W3);
-      for (uint32_t i0 = 0; i0 < n_part; i0 += 8u * T_LANES) {
-        float v[8];
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          const uint32_t i = i0 + (uint32_t)(k * T_LANES + tid);
-          v[k] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rp, lane_off(i < n_part, (int)(i * 4u)), 0, 0));
-        }
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          const bool ok = i0 + (uint32_t)(k * T_LANES + tid) < n_part;
-          const float c = kind == RK_SUM ? acc + v[k] : comb<RK_MAX>(acc, v[k]);
-          acc = ok ? c : acc;
-        }
-      }
-      acc = kind == RK_SUM ? group_reduce<RK_SUM>(acc, 64) : group_reduce<RK_MAX>(acc, 64);
-      if ((tid & 63) == 0) s_red[0][wave] = acc;
-      __syncthreads();
-      if (tid == 0) {
-        float r = s_red[0][0];
-        for (int k = 1; k < T_LANES / 64; ++k) r = kind == RK_SUM ? r + s_red[0][k] : comb<RK_MAX>(r, s_red[0][k]);
-        const ArgD oa = read_arg(W, W[H_ALL_OUT]);
-        if (oa.dt == DT_BF16)
-          *reinterpret_cast<uint16_t*>(const_cast<char*>(oa.p)) = (uint16_t)(f2bf_pack(r, 0.f) & 0xffffu);
-        else
-          *reinterpret_cast<float*>(const_cast<char*>(oa.p)) = r;
-        __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
     }
   }
   if constexpr (PROF) {
@@ -1662,8 +1613,7 @@ __device__ __forceinline__ void vm_main(const Seg& sg, float (*s_red)[T_LANES / 
 #define DVM_LDS_DECL extern __shared__ __attribute__((aligned(16))) char dlds[];
 #define DVM_RED_PTRS(W)                                                                                \
   const uint32_t red_off = (W)[H_RED_OFF];                                                             \
-  float(*s_red)[T_LANES / 64] = reinterpret_cast<float(*)[T_LANES / 64]>(dlds + red_off);             \
-  int& s_last = *reinterpret_cast<int*>(dlds + red_off + N_LDSBUF * (T_LANES / 64) * 4);
+  float(*s_red)[T_LANES / 64] = reinterpret_cast<float(*)[T_LANES / 64]>(dlds + red_off);
 constexpr uint32_t LDS_CAP = LDS_BUDGET;
 
 // One workgroup's run: its program (or its segment of a spatial stack), or
@@ -1680,7 +1630,7 @@ __device__ __forceinline__ void vm_kernel() {
   for (uint32_t s = 0; s < n; ++s) {
     const Seg sg = temporal ? temporal_segment(K, s) : segment_of();
     DVM_RED_PTRS(sg.W)
-    vm_main<PROF>(sg, s_red, s_last, dlds);
+    vm_main<PROF>(sg, s_red, dlds);
     if (temporal) __syncthreads();
   }
 }
@@ -1698,6 +1648,51 @@ DVM_SYM(dvm_vm_vector_prof)(const Program prog) {
   (void)prog;
   vm_kernel<true>();
 }
+
+#ifndef DVM_WIDE
+// Reduce-all combine: the second launch of a reduce-all program, after the VM
+// kernel on the same stream (the stream orders the workgroups' partials
+// before it).  One workgroup folds the n_part partials in a fixed order (lane
+// t takes partials t, t + T, t + 2T, ... in increasing order, eight loads in
+// flight at a time; then the lanes of each wave, then the waves in order),
+// so the result is the same in every run, and writes the scalar output.
+extern "C" __global__ void __launch_bounds__(T_LANES)
+dvm_allreduce_combine(const float* part, uint32_t n_part, uint32_t kind, void* out, uint32_t out_dt) {
+  __shared__ float s_w[T_LANES / 64];
+  const int tid = (int)threadIdx.x, wave = tid >> 6;
+  float acc = kind == RK_SUM ? 0.f : -__builtin_huge_valf();
+  const Rsrc rp = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(part), 0, (int)(n_part * 4u), RSRC_W3);
+  for (uint32_t i0 = 0; i0 < n_part; i0 += 8u * T_LANES) {
+    float v[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const uint32_t i = i0 + (uint32_t)(k * T_LANES + tid);
+      v[k] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rp, lane_off(i < n_part, (int)(i * 4u)), 0, 0));
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const bool ok = i0 + (uint32_t)(k * T_LANES + tid) < n_part;
+      const float c = kind == RK_SUM ? acc + v[k] : comb<RK_MAX>(acc, v[k]);
+      acc = ok ? c : acc;
+    }
+  }
+  acc = kind == RK_SUM ? group_reduce<RK_SUM>(acc, 64) : group_reduce<RK_MAX>(acc, 64);
+  if ((tid & 63) == 0) s_w[wave] = acc;
+  __syncthreads();
+  if (tid == 0) {
+    float r = s_w[0];
+    for (int k = 1; k < T_LANES / 64; ++k) r = kind == RK_SUM ? r + s_w[k] : comb<RK_MAX>(r, s_w[k]);
+    if (out_dt == DT_BF16) *static_cast<uint16_t*>(out) = (uint16_t)(f2bf_pack(r, 0.f) & 0xffffu);
+    else *static_cast<float*>(out) = r;
+  }
+}
+
+extern "C" hipError_t dvm_launch_allreduce_combine(const float* part, uint32_t n_part, uint32_t kind, void* out,
+                                                   uint32_t out_dt, hipStream_t s) {
+  hipLaunchKernelGGL(dvm_allreduce_combine, dim3(1), dim3(T_LANES), 0, s, part, n_part, kind, out, out_dt);
+  return hipGetLastError();
+}
+#endif
 
 // Host-side launch of the VECTOR VM kernel with one program as its argument.
 extern "C" hipError_t DVM_SYM(dvm_launch_vector_kernel)(const Program* p, unsigned grid, unsigned lds, hipStream_t s) {

@@ -128,10 +128,10 @@ typedef struct {
 
 /* Contexts (the VM's code is loaded once and stays resident: MindSpore DVM
  * summary page, section 3.2).  device >= 0: the HIP device whose resident VM
- * kernels run the programs.  Reduce-all programs need a scratch area on the device (a counter
- * and one partial per tile): each stream gets its own 4 MiB area, allocated
- * and zeroed at the first reduce-all launched on it and freed with the
- * context, so launches on different streams never share it.
+ * kernels run the programs.  Reduce-all programs need a scratch area on the device (one
+ * partial per workgroup): each stream gets its own 4 MiB area, allocated and
+ * zeroed at the first reduce-all launched on it and freed with the context,
+ * so launches on different streams never share it.
  * device < 0: an encode-only context (tiling and bytecode, no launches). */
 dvm_status dvm_context_create(int device, dvm_context** out);
 void dvm_context_destroy(dvm_context* ctx);
@@ -209,8 +209,10 @@ dvm_status dvm_flush(dvm_graph* g, dvm_program** out);
 /* Launches a program on the resident VM kernel of its kernel type, on
  * stream (hipStream_t): each workgroup finds its tiles from the header and
  * interprets the body tile by tile (DVM review page, section 4.4).  The
- * program is copied into the launch.  Asynchronous; DVM_ERR_DEVICE for an
- * encode-only context or a failed launch. */
+ * program is copied into the launch.  A reduce-all is two launches on the
+ * stream: the VM kernel (one partial per workgroup) and a one-workgroup
+ * combine of the partials into the scalar output.  Asynchronous;
+ * DVM_ERR_DEVICE for an encode-only context or a failed launch. */
 dvm_status dvm_launch(dvm_context* ctx, const dvm_program* p, void* stream);
 
 /* dvm_launch for callers that cannot allocate device memory (code under HIP
@@ -218,11 +220,11 @@ dvm_status dvm_launch(dvm_context* ctx, const dvm_program* p, void* stream);
  * hipMalloc, hipFree or allocating library routine.  Programs other than
  * reduce-alls launch exactly as with dvm_launch.  A reduce-all runs on the
  * library's static scratch array instead of the stream's allocated area: one
- * array per GPU, held until the process ends, of 256 + 4 * 65536 bytes (a
- * counter and at most 65536 partials, one per workgroup; the tiling runs at
- * most 4096 workgroups); a program launching more workgroups returns
- * DVM_ERR_RESOURCE without launching.  Before the program the call queues a
- * one-workgroup kernel that zeroes the counter, on the same stream.  Every call
+ * array per GPU, held until the process ends, of 256 + 4 * 65536 bytes (at
+ * most 65536 partials, one per workgroup; the tiling runs at most 4096
+ * workgroups); a program launching more workgroups returns DVM_ERR_RESOURCE
+ * without launching.  Nothing in it needs to start at zero: every partial is
+ * written before the combine reads it.  Every call
  * on a GPU shares that GPU's array and it keeps the last call's contents:
  * calls whose launches overlap on one GPU (different streams, or graph
  * replays running concurrently) race on it; callers serialise them.

@@ -1,11 +1,11 @@
 """dvm_launch_noalloc (the launch for callers that cannot allocate) against
 dvm_launch, through the C ABI.
 
-Reduce-all programs are the ones whose kernels use scratch (a counter and one
-partial per workgroup).  Both entry points run the same kernel, tile order and
-partial combine, so the results must be bit-identical.  Two calls in a row,
-the second over a smaller input, so the second call runs on an array that
-still holds the first call's partials and counter history.
+Reduce-all programs are the ones whose kernels use scratch (one partial per
+workgroup, combined by a second launch).  Both entry points run the same
+kernels, tile order and partial combine, so the results must be
+bit-identical.  Two calls in a row, the second over a smaller input, so the
+second call runs on an array that still holds the first call's partials.
 """
 import numpy as np
 import pytest
