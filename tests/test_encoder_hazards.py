@@ -122,3 +122,42 @@ def test_reduce_all_program_has_no_scratch_address(ectx):
     a = ARG_BASE + w[H_ALL_SCRATCH] * ARG_WORDS
     assert w[a] == 0 and w[a + 1] == 0               # supplied per stream at launch
     assert w[a + 7] == 256 + 4 * h["grid"]           # the bytes the program needs: one partial per workgroup
+
+
+HD_LD_PF16 = 10
+
+
+def ld_pf_waits(p):
+    """(handler, wait count) of every prefetch read in the body: the count
+    sits in the a (low 4 bits) and sub (high 4 bits) fields."""
+    w = p.words()
+    out = []
+    for i in range(w[H_BODY_BEGIN], w[H_BODY_END], 2):
+        h = w[i] & 0xFF
+        if HD_LD_PF16 <= h < HD_LD_PF16 + 6:
+            out.append((h, ((w[i] >> 12) & 0xF) | (((w[i] >> 20) & 0xF) << 4)))
+    return out
+
+
+@pytest.mark.parametrize("kind", ["softmax", "layernorm"])
+def test_prefetch_wait_counts(ectx, kind):
+    """The wait before a prefetch read counts the vector-memory instructions
+    issued after that prefetch: the previous tile's instructions after its
+    refill plus this tile's before the read (a workgroup's first tile waits
+    for the whole prologue instead).  Softmax over rows of 6484 bf16 (wide
+    build, nv = 7): the body is prefetch read (its refill issues 7), softmax,
+    store (7 chunks), so the count is the 7 stores.  LayerNorm over 5120
+    (nv = 10): read, reductions, scale-and-shift, store (10), count 10.  A
+    larger count would let the read overtake its data."""
+    from device_bytecode_vm_amd import composites as CP
+    g = dvm.Graph(ectx)
+    if kind == "softmax":
+        CP.softmax(g, g.input(TD(1 << 36, "bf16", (139480, 6484))), out=TD(2 << 36, "bf16", (139480, 6484)))
+        want = 7
+    else:
+        CP.layer_norm(g, g.input(TD(1 << 36, "bf16", (16384, 5120))), g.input(TD(3 << 36, "f32", (5120,))),
+                      g.input(TD(4 << 36, "f32", (5120,))), 1e-6, out=TD(2 << 36, "bf16", (16384, 5120)))
+        want = 10
+    p = g.flush()
+    assert p.header()["body_tile"] > 1
+    assert [n for _, n in ld_pf_waits(p)] == [want]
