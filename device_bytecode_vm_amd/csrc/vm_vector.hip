@@ -1412,6 +1412,17 @@ __device__ __forceinline__ void vm_main(const Seg& sg, float (*s_red)[T_LANES / 
           scale = __expf(mw - M) / S_row;
         }
         bin_csn<ALU_MUL, false>(treg<0>(R), scale, nv_pass(G));
+        // a store of the result that follows runs here, without going back
+        // through the dispatch (the softmax body is read, softmax, store)
+        if (f_op(nw0) == HD_ST_BF16 || f_op(nw0) == HD_ST_F32) {
+          const uint32_t s0 = nw0, s1 = nw1;
+          pc += 2;
+          uint32_t pcs = pc;
+          asm volatile("" : "+s"(pcs) : "s"(s0), "s"(s1));
+          fetch2(W, pcs, nw0, nw1);
+          if (f_op(s0) == HD_ST_BF16) store_dir<DT_BF16>(treg<0>(R), read_arg(W, s1), G, tl, L, streaming(W));
+          else store_dir<DT_F32>(treg<0>(R), read_arg(W, s1), G, tl, L, streaming(W));
+        }
         break;
       }
       CASE_BIN_COMM(ALU_ADD) CASE_BIN_NC(ALU_SUB) CASE_BIN_COMM(ALU_MUL)
@@ -1455,6 +1466,17 @@ __device__ __forceinline__ void vm_main(const Seg& sg, float (*s_red)[T_LANES / 
           const float sh[VEC] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
 #pragma unroll
           for (int i = 0; i < VEC; ++i) treg<0>(R).c[j][i] = __builtin_fmaf(treg<0>(R).c[j][i] * r, sc[i], sh[i]);
+        }
+        // a bf16 store of the result that follows runs here, without going
+        // back through the dispatch (LayerNorm's body ends scale-and-shift,
+        // store)
+        if (f_op(nw0) == HD_ST_BF16) {
+          const uint32_t s1 = nw1;
+          pc += 2;
+          uint32_t pcs = pc;
+          asm volatile("" : "+s"(pcs) : "s"(s1));
+          fetch2(W, pcs, nw0, nw1);
+          store_dir<DT_BF16>(treg<0>(R), read_arg(W, s1), G, tl, L, streaming(W));
         }
         break;
       }
