@@ -160,7 +160,7 @@ constexpr int64_t T = T_LANES, V = VEC, W = 64 * VEC, G = 512, A = 78125, A_MM =
 // are resident: the two workgroups sharing a compute unit stream at unequal
 // rates, and the dispatcher then hands the next workgroup to the slot that
 // frees first (measured on MI355X; standard-build programs keep G).
-constexpr int64_t WIDE_WG_TILES = 8, WIDE_GRID_MAX = 4096;
+constexpr int64_t WIDE_WG_TILES = 8, WIDE_GRID_MAX = 8192;
 
 struct Operand {
   int64_t esize, sr, sc, base_mod16;

@@ -189,9 +189,9 @@ bool verify_vector(Ctx& c) {
     const int64_t n_r = cdiv(R, tr), n_c = cdiv(C, tc);
     if ((int64_t)block_dim != n_r * n_c || (int64_t)W[H_NC] != n_c) return c.fail("block_dim %u is not the tile count", block_dim);
     // 512 resident workgroups; a wide-build program with more than 8 tiles
-    // per workgroup runs as min(4096, block_dim / 8) workgroups instead
+    // per workgroup runs as min(8192, block_dim / 8) workgroups instead
     int64_t gp = std::min<int64_t>(512, block_dim);
-    if (W[H_KTYPE] == KT_VECTOR_WIDE && cdiv(block_dim, gp) > 8) gp = std::min<int64_t>(4096, block_dim / 8);
+    if (W[H_KTYPE] == KT_VECTOR_WIDE && cdiv(block_dim, gp) > 8) gp = std::min<int64_t>(8192, block_dim / 8);
     if ((int64_t)body_tile != cdiv(block_dim, gp) || (int64_t)grid != cdiv(block_dim, body_tile))
       return c.fail("body_tile %u / grid %u do not follow from block_dim", body_tile, grid);
   } else if (block_dim != 0) {

@@ -253,9 +253,9 @@ def test_temporal_stack_tiles_cover_once_and_balance(grid, bds):
 
 def test_wide_grid_rule_hand_worked():
     """Long wide-build programs run as workgroups of about 8 tiles (up to
-    4096 of them).  Hand-worked: the 126576-row LayerNorm over 5120 columns
+    8192 of them).  Hand-worked: the 126576-row LayerNorm over 5120 columns
     tiles as 4 x 5120 (31644 tiles); 31644 / 512 would give 62 tiles per
-    workgroup, more than 8, so the header is taken with min(4096, 31644 // 8)
+    workgroup, more than 8, so the header is taken with min(8192, 31644 // 8)
     = 3955 workgroups: ceil(31644 / 3955) = 9 tiles each (3955 * 8 = 31640 <
     31644), ceil(31644 / 9) = 3516 workgroups."""
     ops = [Operand(2, 5120, 1), Operand(4, 0, 1), Operand(4, 0, 1), Operand(2, 5120, 1)]
@@ -264,9 +264,13 @@ def test_wide_grid_rule_hand_worked():
     # 16384 rows: 4096 tiles, 8 per workgroup at 512: the rule does not apply
     p = TL.plan(TL.ROWREDUCE, 16384, 5120, ops, TL.NV_WIDE)
     assert (p.block_dim, p.body_tile, p.grid) == (4096, 8, 512)
-    # 200000 rows: 50000 tiles, 4096 workgroups of ceil(50000 / 4096) = 13, 3847 of them used
+    # 200000 rows: 50000 tiles, min(8192, 6250) = 6250 workgroups of 8
     p = TL.plan(TL.ROWREDUCE, 200000, 5120, ops, TL.NV_WIDE)
-    assert (p.block_dim, p.body_tile, p.grid) == (50000, 13, 3847)
+    assert (p.block_dim, p.body_tile, p.grid) == (50000, 8, 6250)
+    # 400000 rows: 100000 tiles, at the cap: 8192 workgroups of ceil(100000 / 8192) = 13,
+    # ceil(100000 / 13) = 7693 of them used
+    p = TL.plan(TL.ROWREDUCE, 400000, 5120, ops, TL.NV_WIDE)
+    assert (p.block_dim, p.body_tile, p.grid) == (100000, 13, 7693)
     # the standard build keeps G: 126576 x 1024 (one row per tile) stays at 512 workgroups
     q = TL.plan(TL.ROWREDUCE, 126576, 1024, [Operand(2, 1024, 1), Operand(2, 1024, 1)])
     assert q.grid <= TL.G_WG and q.body_tile > TL.WIDE_WG_TILES
