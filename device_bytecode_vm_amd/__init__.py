@@ -327,6 +327,17 @@ class Graph:
         (cond: one fp32 value, read on the device)."""
         check(lib.dvm_graph_begin_branch(self.h, cond.h, float(threshold)))
 
+    def begin_branch_reduce(self, x: "Value", out, threshold: float = 0.0, kind: str = "sum") -> "Value":
+        """A reduce-all of x ("sum" or "max") into the 0-d fp32 storage out,
+        then begin_branch on it (dvm_graph_begin_branch_reduce: the branch
+        program folds the reduce-all's partials itself).  Returns the value."""
+        self._keep.append(out)
+        d = to_c(out)
+        v = C.c_int64()
+        check(lib.dvm_graph_begin_branch_reduce(self.h, x.h, L.OP_CODES["reduce_" + kind], C.byref(d),
+                                                float(threshold), C.byref(v)))
+        return Value(v.value, (), "f32", out)
+
     def else_branch(self):
         check(lib.dvm_graph_else_branch(self.h))
 

@@ -96,6 +96,7 @@ _sigs = {
     "dvm_graph_set_stack_order": (C.c_int, [VP, C.c_int32]),
     "dvm_program_stack_temporal": (C.c_int, [P(VP), C.c_size_t, P(VP)]),
     "dvm_graph_begin_branch": (C.c_int, [VP, C.c_int64, C.c_float]),
+    "dvm_graph_begin_branch_reduce": (C.c_int, [VP, C.c_int64, C.c_int32, P(DvmTensor), C.c_float, P(C.c_int64)]),
     "dvm_graph_else_branch": (C.c_int, [VP]),
     "dvm_graph_end_branch": (C.c_int, [VP, P(C.c_int32)]),
     "dvm_sync": (C.c_int, [VP]),

@@ -72,9 +72,10 @@ enum Hdr : int {
   H_R_HI = 19,
   H_C_LO = 20,
   H_C_HI = 21,
-  H_ALL_KIND = 22,   // reduce-all: 0 sum, 1 max
+  H_ALL_KIND = 22,   // reduce-all: 0 sum, 1 max (and a branch program with HF_COND_FOLD)
   H_ALL_OUT = 23,    // reduce-all: arg index of the scalar output
-  H_ALL_SCRATCH = 24,// reduce-all: arg index of the scratch (counter + partials)
+  H_ALL_SCRATCH = 24,// reduce-all: arg index of the scratch (partials from byte 256);
+                     //   HF_COND_FOLD: arg index of the partials themselves
   H_N_INSTR = 25,
   H_FLAGS = 26,      // HF_* bits
   H_LDS_BYTES = 27,  // dynamic LDS of the launch (staging areas below)
@@ -182,6 +183,12 @@ enum HdrFlag : uint32_t {
   // would otherwise overwrite it while slower waves still read it (the next
   // tile's own barrier fences the reads before the buffers come round again)
   HF_RED_ALT = 8u,
+  // a branch program whose condition is the scalar of the reduce-all launched
+  // just before it, whose combine launch it replaces: each wave folds the
+  // workgroup partials (operand H_ALL_SCRATCH, at most 2 T_LANES of them, kind
+  // H_ALL_KIND) in the combine's order, and workgroup 0 writes the scalar to
+  // the condition operand
+  HF_COND_FOLD = 16u,
 };
 constexpr uint64_t STREAM_BYTES = 16ull << 20;
 enum ArgFlag : uint32_t {

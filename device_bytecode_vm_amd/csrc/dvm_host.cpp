@@ -437,10 +437,25 @@ enum FlushReason { FR_EXPLICIT = 0, FR_SYNC = 1, FR_REDUCE_ALL = 2, FR_SHAPE = 3
 constexpr size_t SCRATCH_BYTES = 4u << 20;
 constexpr size_t SCRATCH_PART_OFF = 256;
 
+// A reduce-all's combine held back on its stream: the branch program opened
+// on the reduce-all's scalar folds the partials itself (HF_COND_FOLD).
+struct HeldCombine {
+  hipStream_t s;
+  const float* part;
+  uint32_t n_part, kind;
+  void* out;
+  uint32_t out_dt;
+};
+
 struct dvm_context {
   int device = -1;
-  std::mutex mu;  // guards scratch (graphs of one context may run on separate threads)
+  std::mutex mu;  // guards scratch and held (graphs of one context may run on separate threads)
   std::vector<std::pair<hipStream_t, void*>> scratch;
+  // combines held back (at most one per stream), and the stream whose next
+  // reduce-all launch holds its combine back (set while a branch opens)
+  std::vector<HeldCombine> held;
+  hipStream_t hold_stream = nullptr;
+  bool hold = false;
   // the device's static scratch array (dvm_launch_noalloc), looked up at creation
   void* static_scratch = nullptr;
   size_t static_bytes = 0;
@@ -2136,8 +2151,10 @@ dvm_status encode_buffer(dvm_graph* g, dvm_program** out) {
 // host).  Both must share one tiling, operand table and prologue; the merged
 // program appends the condition operand to the table and the else-body after
 // the then-body.
+// fold: the combine held back for the condition (its partials are folded
+// by the branch program, HF_COND_FOLD), or null.
 dvm_status merge_branch(const dvm_program* pt, const dvm_program* pe, const dvm_tensor& cond, float thr,
-                        dvm_program** out) {
+                        const HeldCombine* fold, dvm_program** out) {
   const uint32_t* A = pt->prog.w;
   const uint32_t* B = pe->prog.w;
   static const int same[] = {H_KTYPE, H_TEMPLATE, H_BLOCK_DIM, H_BODY_TILE, H_GRID, H_TR, H_TC, H_G, H_NV, H_P,
@@ -2154,9 +2171,10 @@ dvm_status merge_branch(const dvm_program* pt, const dvm_program* pe, const dvm_
   if (pro_n != B[H_PRO_END] - B[H_PRO_BEGIN] ||
       !std::equal(A + A[H_PRO_BEGIN], A + A[H_PRO_END], B + B[H_PRO_BEGIN]))
     return fail(DVM_ERR_UNSUPPORTED, "branch bodies stage different operands");
-  if (n_args + 1 > (uint32_t)MAX_ARGS) return fail(DVM_ERR_RESOURCE, "too many operands");
+  const uint32_t n_extra = fold ? 2u : 1u;  // the condition, and the partials it is folded from
+  if (n_args + n_extra > (uint32_t)MAX_ARGS) return fail(DVM_ERR_RESOURCE, "too many operands");
   const uint32_t then_n = A[H_BODY_END] - A[H_BODY_BEGIN], else_n = B[H_BODY_END] - B[H_BODY_BEGIN];
-  const uint32_t base = ARG_BASE + (n_args + 1) * ARG_WORDS;
+  const uint32_t base = ARG_BASE + (n_args + n_extra) * ARG_WORDS;
   if (base + pro_n + then_n + else_n + PAD_WORDS > (uint32_t)MAX_WORDS) return fail(DVM_ERR_RESOURCE, "program too large");
   dvm_program* q = new (std::nothrow) dvm_program();
   if (!q) return fail(DVM_ERR_INTERNAL, "out of host memory");
@@ -2169,10 +2187,19 @@ dvm_status merge_branch(const dvm_program* pt, const dvm_program* pe, const dvm_
   c[A_DTYPE] = DT_F32;
   c[A_FLAGS] = arg_flags_word(0, 4);
   c[A_EXTENT] = 4;
+  if (fold) {
+    uint32_t* f = c + ARG_WORDS;
+    const uint64_t fp = (uint64_t)(uintptr_t)fold->part;
+    f[A_PTR_LO] = (uint32_t)fp;
+    f[A_PTR_HI] = (uint32_t)(fp >> 32);
+    f[A_DTYPE] = DT_F32;
+    f[A_FLAGS] = arg_flags_word(0, 4ull * fold->n_part);
+    f[A_EXTENT] = 4u * fold->n_part;
+  }
   std::copy(A + A[H_PRO_BEGIN], A + A[H_PRO_END], W + base);
   std::copy(A + A[H_BODY_BEGIN], A + A[H_BODY_END], W + base + pro_n);
   std::copy(B + B[H_BODY_BEGIN], B + B[H_BODY_END], W + base + pro_n + then_n);
-  W[H_NARGS] = n_args + 1;
+  W[H_NARGS] = n_args + n_extra;
   W[H_PRO_BEGIN] = base;
   W[H_PRO_END] = W[H_BODY_BEGIN] = base + pro_n;
   W[H_BODY_END] = W[H_ALT_BEGIN] = base + pro_n + then_n;
@@ -2180,6 +2207,11 @@ dvm_status merge_branch(const dvm_program* pt, const dvm_program* pe, const dvm_
   W[H_FLAGS] |= HF_BRANCH;
   W[H_COND_ARG] = n_args;
   std::memcpy(&W[H_COND_THR], &thr, 4);
+  if (fold) {
+    W[H_FLAGS] |= HF_COND_FOLD;
+    W[H_ALL_SCRATCH] = n_args + 1;
+    W[H_ALL_KIND] = fold->kind;
+  }
   W[H_N_INSTR] = (pro_n + then_n + else_n) / 2;
   q->n_words = W[H_ALT_END];
   q->n_instr = W[H_N_INSTR];
@@ -2187,13 +2219,17 @@ dvm_status merge_branch(const dvm_program* pt, const dvm_program* pe, const dvm_
   q->C = pt->C;
   q->pad = pt->pad;
   q->grid_launch = pt->grid_launch;
-  q->bytes = std::max(pt->bytes, pe->bytes) + 4;
+  q->bytes = std::max(pt->bytes, pe->bytes) + 4 + (fold ? 4ull * fold->n_part : 0);
   q->lds = pt->lds;
   q->reads = pt->reads;
   q->reads.insert(q->reads.end(), pe->reads.begin(), pe->reads.end());
   q->reads.push_back({(uintptr_t)cond.data, 4});
   q->writes = pt->writes;
   q->writes.insert(q->writes.end(), pe->writes.begin(), pe->writes.end());
+  if (fold) {
+    q->reads.push_back({(uintptr_t)fold->part, 4ull * fold->n_part});
+    q->writes.push_back({(uintptr_t)cond.data, 4});
+  }
   const dvm_status v = checked(q);
   if (v != DVM_OK) {
     delete q;
@@ -2258,7 +2294,7 @@ hipError_t launch_kernel(const dvm_program* p, const Program* q, hipStream_t s) 
 // The second launch of a reduce-all program (q: its words with the scratch
 // area set): folds the workgroups' partials, which the stream orders before
 // it, into the scalar output.
-hipError_t launch_combine(const dvm_program* p, const Program* q, hipStream_t s) {
+HeldCombine combine_of(const dvm_program* p, const Program* q, hipStream_t s) {
   const uint32_t* W = q->w;
   const uint32_t* sa = W + ARG_BASE + W[H_ALL_SCRATCH] * ARG_WORDS;
   const uint32_t* oa = W + ARG_BASE + W[H_ALL_OUT] * ARG_WORDS;
@@ -2266,15 +2302,59 @@ hipError_t launch_combine(const dvm_program* p, const Program* q, hipStream_t s)
   const uint64_t out = ((uint64_t)oa[A_PTR_HI] << 32) | oa[A_PTR_LO];
   // one partial per launched workgroup, never past the area
   const uint64_t slots = sa[A_EXTENT] > SCRATCH_PART_OFF ? (sa[A_EXTENT] - SCRATCH_PART_OFF) / 4u : 0u;
-  const uint32_t n_part = (uint32_t)std::min<uint64_t>(p->grid_launch, slots);
-  return dvm_launch_allreduce_combine(reinterpret_cast<const float*>((uintptr_t)(area + SCRATCH_PART_OFF)), n_part,
-                                      W[H_ALL_KIND], reinterpret_cast<void*>((uintptr_t)out), oa[A_DTYPE], s);
+  HeldCombine c;
+  c.s = s;
+  c.part = reinterpret_cast<const float*>((uintptr_t)(area + SCRATCH_PART_OFF));
+  c.n_part = (uint32_t)std::min<uint64_t>(p->grid_launch, slots);
+  c.kind = W[H_ALL_KIND];
+  c.out = reinterpret_cast<void*>((uintptr_t)out);
+  c.out_dt = oa[A_DTYPE];
+  return c;
+}
+
+hipError_t launch_held(const HeldCombine& c) {
+  return dvm_launch_allreduce_combine(c.part, c.n_part, c.kind, c.out, c.out_dt, c.s);
+}
+
+hipError_t launch_combine(const dvm_program* p, const Program* q, hipStream_t s) {
+  return launch_held(combine_of(p, q, s));
+}
+
+// Launches the combine held back on stream s, if any.  Every launch and sync
+// on a stream runs this first, so the scalar is written before anything
+// after it on the stream can read it, and before the next reduce-all on the
+// stream rewrites the partials.
+hipError_t settle(dvm_context* ctx, hipStream_t s) {
+  HeldCombine c;
+  {
+    std::lock_guard<std::mutex> lk(ctx->mu);
+    auto it = std::find_if(ctx->held.begin(), ctx->held.end(), [&](const HeldCombine& h) { return h.s == s; });
+    if (it == ctx->held.end()) return hipSuccess;
+    c = *it;
+    ctx->held.erase(it);
+  }
+  return launch_held(c);
+}
+
+// Takes the combine held back on stream s if it writes the fp32 scalar at
+// `out` (the branch program then folds the partials instead; the VM folds at
+// most 2 T_LANES partials, one per workgroup of a reduce-all's launch).
+bool take_held(dvm_context* ctx, hipStream_t s, const void* out, HeldCombine* c) {
+  std::lock_guard<std::mutex> lk(ctx->mu);
+  auto it = std::find_if(ctx->held.begin(), ctx->held.end(), [&](const HeldCombine& h) { return h.s == s; });
+  if (it == ctx->held.end() || it->out != out || it->out_dt != DT_F32 || it->n_part == 0 ||
+      it->n_part > 2u * T_LANES)
+    return false;
+  *c = *it;
+  ctx->held.erase(it);
+  return true;
 }
 
 dvm_status launch(dvm_context* ctx, const dvm_program* p, hipStream_t s) {
   if (!ctx || ctx->device < 0) return fail(DVM_ERR_DEVICE, "encode-only context cannot launch");
+  hipError_t e = settle(ctx, s);
+  if (e != hipSuccess) return fail(DVM_ERR_DEVICE, "launch failed: %s", hipGetErrorString(e));
   if (p->grid_launch == 0) return DVM_OK;
-  hipError_t e;
   if (needs_scratch(p)) {
     void* area;
     dvm_status st = stream_scratch(ctx, s, &area);
@@ -2282,7 +2362,16 @@ dvm_status launch(dvm_context* ctx, const dvm_program* p, hipStream_t s) {
     Program q = p->prog;  // the launch copies its argument: a stack copy is enough
     set_scratch(&q, area, SCRATCH_BYTES);
     e = launch_kernel(p, &q, s);
-    if (e == hipSuccess) e = launch_combine(p, &q, s);
+    if (e == hipSuccess) {
+      const HeldCombine c = combine_of(p, &q, s);
+      std::unique_lock<std::mutex> lk(ctx->mu);
+      if (ctx->hold && ctx->hold_stream == s) {
+        ctx->held.push_back(c);  // settle() above left none on s
+      } else {
+        lk.unlock();
+        e = launch_held(c);
+      }
+    }
   } else {
     e = launch_kernel(p, &p->prog, s);
   }
@@ -2699,7 +2788,11 @@ dvm_status dvm_graph_create(dvm_context* ctx, void* stream, dvm_graph** out) {
   return DVM_OK;
 }
 
-void dvm_graph_destroy(dvm_graph* g) { delete g; }
+void dvm_graph_destroy(dvm_graph* g) {
+  // a branch left open may hold back the combine that writes its condition
+  if (g && g->branch && g->ctx->device >= 0) (void)settle(g->ctx, g->stream);
+  delete g;
+}
 
 dvm_status dvm_graph_take_program(dvm_graph* g, dvm_program** out) {
   if (!g || !out) return fail(DVM_ERR_INVALID_ARG, "null argument");
@@ -2852,9 +2945,10 @@ dvm_status dvm_launch(dvm_context* ctx, const dvm_program* p, void* stream) {
 dvm_status dvm_launch_noalloc(dvm_context* ctx, const dvm_program* p, void* stream) {
   if (!ctx || !p) return fail(DVM_ERR_INVALID_ARG, "null argument");
   if (ctx->device < 0) return fail(DVM_ERR_DEVICE, "encode-only context cannot launch");
-  if (p->grid_launch == 0) return DVM_OK;
   const hipStream_t s = (hipStream_t)stream;
-  hipError_t e;
+  hipError_t e = settle(ctx, s);
+  if (e != hipSuccess) return fail(DVM_ERR_DEVICE, "launch failed: %s", hipGetErrorString(e));
+  if (p->grid_launch == 0) return DVM_OK;
   if (needs_scratch(p)) {
     if (!ctx->static_scratch)
       return fail(DVM_ERR_DEVICE, "static scratch unavailable: %s", hipGetErrorString(ctx->static_err));
@@ -2896,6 +2990,10 @@ dvm_status launch_twin(dvm_context* ctx, const dvm_program* p, void* stream, uin
     return fail(DVM_ERR_UNSUPPORTED, "profiling covers single VECTOR programs");
   if (p->grid_launch == 0) return DVM_OK;
   if (!counters) return fail(DVM_ERR_INVALID_ARG, "null counter buffer");
+  {
+    const hipError_t e0 = settle(ctx, (hipStream_t)stream);
+    if (e0 != hipSuccess) return fail(DVM_ERR_DEVICE, "launch failed: %s", hipGetErrorString(e0));
+  }
   const size_t need = (size_t)DVM_PROF_COUNTERS * p->grid_launch;
   if (n_counters < need) return fail(DVM_ERR_INVALID_ARG, "counter buffer holds %zu values, needs %zu", n_counters, need);
   Program q = p->prog;  // the launch copies its argument: a stack copy is enough
@@ -2928,16 +3026,73 @@ dvm_status dvm_graph_begin_branch(dvm_graph* g, dvm_value cond, float threshold)
       return fail(DVM_ERR_INVALID_ARG, "the condition is one fp32 value");
   }
   // a branch is a fusion boundary: the buffered graph (which may compute the
-  // condition) runs first
+  // condition) runs first.  If its last launch is a reduce-all writing the
+  // condition, that launch's combine is held back for the branch program.
+  dvm_context* ctx = g->ctx;
+  if (ctx->device >= 0) {
+    std::lock_guard<std::mutex> lk(ctx->mu);
+    ctx->hold = true;
+    ctx->hold_stream = g->stream;
+  }
   dvm_status st = flush_launch(g, FR_BRANCH, nullptr);
-  if (st != DVM_OK) return st;
+  if (ctx->device >= 0) {
+    std::lock_guard<std::mutex> lk(ctx->mu);
+    ctx->hold = false;
+    ctx->hold_stream = nullptr;
+  }
   const Val& v = g->vals[cs];
-  if (v.lost || v.released || !v.t.data) return fail(DVM_ERR_INVALID_ARG, "the condition has no stored value");
+  const bool stored = !v.lost && !v.released && v.t.data;
+  if (ctx->device >= 0) {
+    // keep a held combine only for a condition it writes
+    bool keep = false;
+    if (st == DVM_OK && stored) {
+      std::lock_guard<std::mutex> lk(ctx->mu);
+      for (const HeldCombine& h : ctx->held)
+        if (h.s == g->stream) keep = h.out == v.t.data;
+    }
+    if (!keep) {
+      const hipError_t e = settle(ctx, g->stream);
+      if (e != hipSuccess && st == DVM_OK) st = fail(DVM_ERR_DEVICE, "launch failed: %s", hipGetErrorString(e));
+    }
+  }
+  if (st != DVM_OK) return st;
+  if (!stored) return fail(DVM_ERR_INVALID_ARG, "the condition has no stored value");
   g->vals[cs].uses++;
   g->branch = 1;
   g->branch_cond = cs;
   g->branch_thr = threshold;
   return DVM_OK;
+}
+
+dvm_status dvm_graph_begin_branch_reduce(dvm_graph* g, dvm_value x, int32_t op, const dvm_tensor* out,
+                                         float threshold, dvm_value* cond) {
+  if (!g || !out || !cond) return fail(DVM_ERR_INVALID_ARG, "null argument");
+  if (op != DVM_OP_REDUCE_SUM && op != DVM_OP_REDUCE_MAX) return fail(DVM_ERR_INVALID_ARG, "op %d is no reduction", op);
+  if (out->dtype != DVM_F32 || out->ndim != 0) return fail(DVM_ERR_INVALID_ARG, "the condition is one fp32 value");
+  if (g->in_group || g->branch) return fail(DVM_ERR_INVALID_ARG, "a group or a branch is open");
+  // what is buffered runs first; then the reduce-all, which closes its own
+  // graph and launches at once, with its combine held back on the stream
+  dvm_status st = flush_launch(g, FR_BRANCH, nullptr);
+  if (st != DVM_OK) return st;
+  dvm_context* ctx = g->ctx;
+  if (ctx->device >= 0) {
+    std::lock_guard<std::mutex> lk(ctx->mu);
+    ctx->hold = true;
+    ctx->hold_stream = g->stream;
+  }
+  dvm_attrs at{};
+  at.axis = DVM_AXIS_ALL;
+  at.scalar_pos = -1;
+  st = dvm_graph_add_op(g, op, &x, 1, &at, out, DVM_OUT_LIVE, cond);
+  if (st == DVM_OK) st = flush_launch(g, FR_REDUCE_ALL, nullptr);  // (nothing, if the op flushed itself)
+  if (ctx->device >= 0) {
+    std::lock_guard<std::mutex> lk(ctx->mu);
+    ctx->hold = false;
+    ctx->hold_stream = nullptr;
+  }
+  if (st == DVM_OK) st = dvm_graph_begin_branch(g, *cond, threshold);
+  if (st != DVM_OK && ctx->device >= 0) (void)settle(ctx, g->stream);
+  return st;
 }
 
 dvm_status dvm_graph_else_branch(dvm_graph* g) {
@@ -2975,7 +3130,21 @@ dvm_status dvm_graph_end_branch(dvm_graph* g, int32_t* launched) {
   if (st == DVM_OK) st = encode_list(g, bt, false, &pt);
   if (st == DVM_OK) st = encode_list(g, be, false, &pe);
   if (st == DVM_OK && (!pt || !pe)) st = fail(DVM_ERR_UNSUPPORTED, "both branch bodies must store a result");
-  if (st == DVM_OK) st = merge_branch(pt, pe, g->vals[cs].t, thr, &pb);
+  // The combine of the reduce-all that wrote the condition, if it was held
+  // back, is folded into the branch program when the branch program is the
+  // next launch on the stream (nothing stacked before it) and its bodies do
+  // not read the condition (workgroup 0 writes it while other workgroups run).
+  HeldCombine fold;
+  bool folding = false;
+  if (st == DVM_OK && g->ctx->device >= 0 && g->stack.empty()) {
+    const uintptr_t cp = (uintptr_t)g->vals[cs].t.data;
+    bool reads_cond = false;
+    for (const dvm_program* b : {pt, pe})
+      for (const Range& r : b->reads) reads_cond = reads_cond || (r.first < cp + 4 && cp < r.first + r.second);
+    if (!reads_cond) folding = take_held(g->ctx, g->stream, g->vals[cs].t.data, &fold);
+  }
+  if (st == DVM_OK) st = merge_branch(pt, pe, g->vals[cs].t, thr, folding ? &fold : nullptr, &pb);
+  if (folding && st != DVM_OK) (void)launch_held(fold);
   delete pt;
   delete pe;
   retire(g, bt, st == DVM_OK);
@@ -3034,7 +3203,8 @@ dvm_status dvm_sync(dvm_graph* g) {
   if (st == DVM_OK) st = launch_stack(g, nullptr);
   if (st != DVM_OK) return st;
   if (g->ctx->device >= 0) {
-    hipError_t e = hipStreamSynchronize(g->stream);
+    hipError_t e = settle(g->ctx, g->stream);
+    if (e == hipSuccess) e = hipStreamSynchronize(g->stream);
     if (e != hipSuccess) return fail(DVM_ERR_DEVICE, "stream sync: %s", hipGetErrorString(e));
   }
   return DVM_OK;

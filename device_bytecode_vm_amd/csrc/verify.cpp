@@ -324,9 +324,21 @@ bool verify_vector(Ctx& c) {
     if (W[H_TEMPLATE] == TM_ALLREDUCE ? n_all != 1 || !kind_ok : n_all != 0)
       return c.fail("%d reduce-all instructions in a program of template %u", n_all, W[H_TEMPLATE]);
   }
+  if ((W[H_FLAGS] & HF_COND_FOLD) && !(W[H_FLAGS] & HF_BRANCH)) return c.fail("a folded condition without a branch");
   if (W[H_FLAGS] & HF_BRANCH) {
     if (W[H_COND_ARG] >= c.n_args || c.W[ARG_BASE + W[H_COND_ARG] * ARG_WORDS + A_DTYPE] != DT_F32)
       return c.fail("the branch condition is no fp32 operand");
+    if (W[H_FLAGS] & HF_COND_FOLD) {
+      // the partials: fp32, a whole number of them, at most 2 T_LANES (the
+      // VM folds them in one pass), not the condition the program writes
+      const uint32_t k = W[H_ALL_SCRATCH];
+      const uint32_t* a = c.W + ARG_BASE + k * ARG_WORDS;
+      const uint64_t ext = k < c.n_args ? arg_extent(a[A_FLAGS], a[A_EXTENT]) : 0;
+      if (k >= c.n_args || k == W[H_COND_ARG] || a[A_DTYPE] != DT_F32 || ext == 0 || ext % 4 ||
+          ext > 8u * T_LANES)
+        return c.fail("the folded partials are no fp32 operand of their own");
+      if (W[H_ALL_KIND] != RK_SUM && W[H_ALL_KIND] != RK_MAX) return c.fail("fold kind %u", W[H_ALL_KIND]);
+    }
     if (!body(W[H_ALT_BEGIN], W[H_ALT_END])) return false;
   }
   return true;

@@ -982,6 +982,50 @@ __device__ __forceinline__ float group_reduce(float acc, int gs) {
   return acc;
 }
 
+// The reduce-all scalar from its n_part workgroup partials, computed by one
+// wave in a fixed order: virtual lane t (of T_LANES) folds partials t,
+// t + T_LANES, t + 2 T_LANES, ... in increasing order; each virtual wave of 64
+// such lanes is combined by group_reduce; then the virtual waves in order.
+// The combine launch and a branch program that folds the partials itself both
+// take the scalar from here, so they agree bit for bit.  Every lane returns
+// the result; all 64 lanes must be active.
+// ONE: n_part <= 2 T_LANES, so the loop body runs once (straight-line code).
+template <bool ONE = false>
+__device__ __forceinline__ float fold_partials(const float* part, uint32_t n_part, uint32_t kind) {
+  constexpr int VW = T_LANES / 64;
+  const int lane = (int)(threadIdx.x & 63u);
+  const Rsrc rp = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(part), 0, (int)(n_part * 4u), RSRC_W3);
+  const float id = kind == RK_SUM ? 0.f : -__builtin_huge_valf();
+  float acc[VW];
+#pragma unroll
+  for (int w = 0; w < VW; ++w) acc[w] = id;
+  for (uint32_t i0 = 0; ONE ? i0 == 0 : i0 < n_part; i0 += 2u * T_LANES) {
+    float v[2][VW];
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int w = 0; w < VW; ++w) {
+        const uint32_t i = i0 + (uint32_t)(j * T_LANES + 64 * w + lane);
+        v[j][w] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rp, lane_off(i < n_part, (int)(i * 4u)), 0, 0));
+      }
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int w = 0; w < VW; ++w) {
+        const bool ok = i0 + (uint32_t)(j * T_LANES + 64 * w + lane) < n_part;
+        const float c = kind == RK_SUM ? acc[w] + v[j][w] : comb<RK_MAX>(acc[w], v[j][w]);
+        acc[w] = ok ? c : acc[w];
+      }
+  }
+  float r = 0.f;
+#pragma unroll
+  for (int w = 0; w < VW; ++w) {
+    const float rw = kind == RK_SUM ? group_reduce<RK_SUM>(acc[w], 64) : group_reduce<RK_MAX>(acc[w], 64);
+    r = w == 0 ? rw : kind == RK_SUM ? r + rw : comb<RK_MAX>(r, rw);
+  }
+  return r;
+}
+
 // Partial over this lane's valid elements, combined as a balanced pairwise
 // tree (a fixed order, so results are deterministic; short dependency
 // chains).  Full tiles mask whole chunks; only ragged tiles mask element by
@@ -1188,11 +1232,26 @@ __device__ __forceinline__ void vm_main(const Seg& sg, float (*s_red)[T_LANES / 
   // The body every tile runs.  A branch program reads its condition (a 0-d
   // fp32 operand written by an earlier launch on the stream) once, with a
   // wave-uniform load, and runs its else-body unless condition > threshold.
+  // With HF_COND_FOLD the condition is a reduce-all whose combine this
+  // program takes over: every wave folds the partials (operand
+  // H_ALL_SCRATCH) itself, and workgroup 0 writes the scalar to the
+  // condition operand, which no tile of this program reads.
   uint32_t body_begin = W[H_BODY_BEGIN], body_end = W[H_BODY_END];
   if (W[H_FLAGS] & HF_BRANCH) {
     const ArgD c = read_arg(W, W[H_COND_ARG]);
     const Rsrc rc = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(c.p), 0, 4, RSRC_W3);
-    const float v = __uint_as_float(__builtin_amdgcn_readfirstlane(__builtin_amdgcn_raw_buffer_load_b32(rc, 0, 0, 0)));
+    float v;
+    if (W[H_FLAGS] & HF_COND_FOLD) {
+      const ArgD pa = read_arg(W, W[H_ALL_SCRATCH]);
+      // (readfirstlane moves 32-bit integers: the value crosses as its bits)
+      v = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(
+          fold_partials<true>(reinterpret_cast<const float*>(pa.p), (uint32_t)(pa.extent / 4u), W[H_ALL_KIND]))));
+      // lane 0 of workgroup 0 stores (branch-free: the other lanes' offsets
+      // are out of range, so their stores are dropped)
+      if (sg.b == 0) __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), rc, lane_off(tid == 0, 0), 0, 0);
+    } else {
+      v = __uint_as_float(__builtin_amdgcn_readfirstlane(__builtin_amdgcn_raw_buffer_load_b32(rc, 0, 0, 0)));
+    }
     if (!(v > __uint_as_float(W[H_COND_THR]))) {
       body_begin = W[H_ALT_BEGIN];
       body_end = W[H_ALT_END];
@@ -1674,36 +1733,13 @@ DVM_SYM(dvm_vm_vector_prof)(const Program prog) {
 #ifndef DVM_WIDE
 // Reduce-all combine: the second launch of a reduce-all program, after the VM
 // kernel on the same stream (the stream orders the workgroups' partials
-// before it).  One workgroup folds the n_part partials in a fixed order (lane
-// t takes partials t, t + T, t + 2T, ... in increasing order, eight loads in
-// flight at a time; then the lanes of each wave, then the waves in order),
-// so the result is the same in every run, and writes the scalar output.
-extern "C" __global__ void __launch_bounds__(T_LANES)
+// before it).  One wave folds the n_part partials in fold_partials' fixed
+// order, so the result is the same in every run, and writes the scalar
+// output.
+extern "C" __global__ void __launch_bounds__(64)
 dvm_allreduce_combine(const float* part, uint32_t n_part, uint32_t kind, void* out, uint32_t out_dt) {
-  __shared__ float s_w[T_LANES / 64];
-  const int tid = (int)threadIdx.x, wave = tid >> 6;
-  float acc = kind == RK_SUM ? 0.f : -__builtin_huge_valf();
-  const Rsrc rp = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(part), 0, (int)(n_part * 4u), RSRC_W3);
-  for (uint32_t i0 = 0; i0 < n_part; i0 += 8u * T_LANES) {
-    float v[8];
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const uint32_t i = i0 + (uint32_t)(k * T_LANES + tid);
-      v[k] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rp, lane_off(i < n_part, (int)(i * 4u)), 0, 0));
-    }
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const bool ok = i0 + (uint32_t)(k * T_LANES + tid) < n_part;
-      const float c = kind == RK_SUM ? acc + v[k] : comb<RK_MAX>(acc, v[k]);
-      acc = ok ? c : acc;
-    }
-  }
-  acc = kind == RK_SUM ? group_reduce<RK_SUM>(acc, 64) : group_reduce<RK_MAX>(acc, 64);
-  if ((tid & 63) == 0) s_w[wave] = acc;
-  __syncthreads();
-  if (tid == 0) {
-    float r = s_w[0];
-    for (int k = 1; k < T_LANES / 64; ++k) r = kind == RK_SUM ? r + s_w[k] : comb<RK_MAX>(r, s_w[k]);
+  const float r = fold_partials(part, n_part, kind);
+  if (threadIdx.x == 0) {
     if (out_dt == DT_BF16) *static_cast<uint16_t*>(out) = (uint16_t)(f2bf_pack(r, 0.f) & 0xffffu);
     else *static_cast<float*>(out) = r;
   }
@@ -1711,7 +1747,7 @@ dvm_allreduce_combine(const float* part, uint32_t n_part, uint32_t kind, void* o
 
 extern "C" hipError_t dvm_launch_allreduce_combine(const float* part, uint32_t n_part, uint32_t kind, void* out,
                                                    uint32_t out_dt, hipStream_t s) {
-  hipLaunchKernelGGL(dvm_allreduce_combine, dim3(1), dim3(T_LANES), 0, s, part, n_part, kind, out, out_dt);
+  hipLaunchKernelGGL(dvm_allreduce_combine, dim3(1), dim3(64), 0, s, part, n_part, kind, out, out_dt);
   return hipGetLastError();
 }
 #endif

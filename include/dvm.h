@@ -340,6 +340,23 @@ dvm_status dvm_template_run(dvm_template* t, const dvm_tensor* inputs, int32_t n
  * Groups cannot open inside a branch; flush, flush_launch and sync refuse
  * while a branch is open. */
 dvm_status dvm_graph_begin_branch(dvm_graph* g, dvm_value cond, float threshold);
+
+/* begin_branch on a reduce-all that this call adds: op (DVM_OP_REDUCE_SUM or
+ * DVM_OP_REDUCE_MAX) over every element of x into the 0-d fp32 tensor out
+ * (a live value, returned in *cond), then a branch on it, as in the
+ * if-else-add workload (DVM review page, section 6.2: a sum, then a branch on
+ * its sign).  The reduce-all launches at once, like any reduce-all; its
+ * scalar is then folded from the workgroups' partials by the branch program
+ * itself (each of its workgroups folds them in the reduce-all's fixed order
+ * and workgroup 0 writes out), which saves the reduce-all's own combine
+ * launch.  out holds its value on the stream once the branch program has run.
+ * If the branch program does not take the fold (a body reads out, the
+ * branch fails, the graph is destroyed with the branch open) or anything else
+ * launches or syncs on the stream first, the combine launches before it, so
+ * the value is the same either way.  Errors: those of dvm_graph_add_op and
+ * dvm_graph_begin_branch; after an error no branch is open. */
+dvm_status dvm_graph_begin_branch_reduce(dvm_graph* g, dvm_value x, int32_t op, const dvm_tensor* out,
+                                         float threshold, dvm_value* cond);
 dvm_status dvm_graph_else_branch(dvm_graph* g);
 dvm_status dvm_graph_end_branch(dvm_graph* g, int32_t* launched);
 

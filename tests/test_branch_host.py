@@ -96,3 +96,46 @@ def test_branch_refusals(ectx):
     g.else_branch()
     g.op("sub", x, y, out=TD(4 << 34, "f32", (64, 64)), live=True)
     g.end_branch()
+
+
+def test_branch_on_its_own_reduce_all(ectx):
+    """begin_branch_reduce adds the reduce-all and opens the branch on it: the
+    same two programs as a reduce_sum op followed by begin_branch (an
+    encode-only context launches nothing, so no combine is held and the branch
+    reads the condition from memory)."""
+    shape = (4096, 4096)
+    g = dvm.Graph(ectx)
+    x = g.input(TD(1 << 34, "f32", shape))
+    y = g.input(TD(2 << 34, "f32", shape))
+    s = g.begin_branch_reduce(x, TD(3 << 34, "f32", ()), 0.5)
+    assert s.shape == () and s.dtype == "f32"
+    g.op("add", x, y, out=TD(4 << 34, "f32", shape), live=True)
+    g.else_branch()
+    g.op("sub", x, y, out=TD(4 << 34, "f32", shape), live=True)
+    g.end_branch()
+    red, br = g.take_program(), g.take_program()
+    ref = if_else(ectx, thr=0.5)
+    assert red.words() == ref.take_program().words()
+    assert br.words() == ref.take_program().words()
+    assert not br.words()[H_FLAGS] & 16        # HF_COND_FOLD: only on a device
+
+
+def test_branch_on_its_own_reduce_all_refusals(ectx):
+    g = dvm.Graph(ectx)
+    x = g.input(TD(1 << 34, "f32", (64, 64)))
+    y = g.input(TD(2 << 34, "f32", (64, 64)))
+    for out, kind in [(TD(3 << 34, "f32", (1,)), "sum"), (TD(3 << 34, "bf16", ()), "sum")]:
+        with pytest.raises(dvm.DvmError) as e:
+            g.begin_branch_reduce(x, out, 0.0, kind)
+        assert e.value.status == L.ERR_INVALID_ARG
+    # after a refusal no branch is open; a max reduce-all works
+    s = g.begin_branch_reduce(x, TD(3 << 34, "f32", ()), 0.0, "max")
+    with pytest.raises(dvm.DvmError):
+        g.begin_branch_reduce(x, TD(5 << 34, "f32", ()), 0.0)   # a branch is open
+    g.op("add", x, y, out=TD(4 << 34, "f32", (64, 64)), live=True)
+    g.else_branch()
+    g.op("sub", x, y, out=TD(4 << 34, "f32", (64, 64)), live=True)
+    g.end_branch()
+    red = g.take_program()
+    assert red.header()["tmpl"] == 2
+    assert g.take_program().words()[H_FLAGS] & HF_BRANCH
