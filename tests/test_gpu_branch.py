@@ -208,3 +208,54 @@ def test_other_graph_between_branch_open_and_close(dvm, ctx):
     assert np.float32(t.cpu().item()) == np.float32(sv + sv)
     ref, branch, _ = O.if_else_add(x, y)
     assert np.array_equal(host64(out), ref.astype(np.float32).astype(np.float64))
+
+
+def test_folded_branches_on_two_streams(dvm, ctx):
+    """Two graphs on two streams open their branches on reduce-alls they
+    issue before either closes: each stream holds its own combine and each
+    branch program folds its own reduce-all's partials (each stream has its
+    own scratch), so both scalars equal their combine's and both bodies are
+    right."""
+    import torch
+    say("folded_two_streams")
+    sa, sb = torch.cuda.Stream(), torch.cuda.Stream()
+    ins = [W.ifelse_inputs(n, 30 + n % 7, (n, 4096)) for n in (2500, 7000)]
+    devs = [(torch_dev(x, "f32"), torch_dev(y, "f32")) for x, y, _ in ins]
+    g0 = dvm.Graph(ctx)
+    bits = [_sum_by_combine(g0, dx) for dx, _ in devs]
+    ss = [empty_dev((), "f32") for _ in ins]
+    outs = [empty_dev(x.shape, "f32") for x, _, _ in ins]
+    torch.cuda.synchronize()
+    gs = [dvm.Graph(ctx, sa), dvm.Graph(ctx, sb)]
+    vals = []
+    for g, (dx, dy), s in zip(gs, devs, ss):
+        vx, vy = g.input(dx), g.input(dy)
+        g.begin_branch_reduce(vx, s, 0.0)
+        vals.append((vx, vy))
+    for g, (vx, vy), o in zip(gs, vals, outs):
+        g.op("add", vx, vy, out=o, live=True)
+        g.else_branch()
+        g.op("sub", vx, vy, out=o, live=True)
+        g.end_branch()
+    torch.cuda.synchronize()
+    for (x, y, _), s, o, b in zip(ins, ss, outs, bits):
+        assert s.cpu().view(torch.int32).item() == b
+        ref, _, _ = O.if_else_add(x, y)
+        assert np.array_equal(host64(o), ref.astype(np.float32).astype(np.float64))
+
+
+def test_open_branch_dropped_with_its_graph(dvm, ctx):
+    """A graph destroyed with its branch open (on a reduce-all it issued)
+    launches the held combine, so the scalar still lands."""
+    import torch
+    say("open_branch_destroyed")
+    x, y, _ = W.ifelse_inputs(1500, 12, (1500, 4096))
+    dx = torch_dev(x, "f32")
+    g0 = dvm.Graph(ctx)
+    bits = _sum_by_combine(g0, dx)
+    s = empty_dev((), "f32")
+    g = dvm.Graph(ctx)
+    g.begin_branch_reduce(g.input(dx), s, 0.0)
+    g.close()
+    torch.cuda.synchronize()
+    assert s.cpu().view(torch.int32).item() == bits
