@@ -2495,6 +2495,18 @@ dvm_status launch_stack(dvm_graph* g, int32_t* launched) {
   st.swap(g->stack);
   if (st.empty()) return DVM_OK;
   if (st.size() == 1) return run_program(g, st[0], launched);
+  // Spatial stacks put the segments with the most work per workgroup first:
+  // the dispatcher hands out workgroups in segment order, so the launch ends
+  // on the shortest ones (the stacked programs are independent, so the order
+  // does not change any result).
+  if (!g->stack_temporal)
+    std::stable_sort(st.begin(), st.end(), [](const dvm_program* a, const dvm_program* b) {
+      auto work = [](const dvm_program* p) {
+        const uint32_t* W = p->prog.w;
+        return W[H_BLOCK_DIM] ? (double)p->bytes * W[H_BODY_TILE] / W[H_BLOCK_DIM] : 0.0;
+      };
+      return work(a) > work(b);
+    });
   dvm_program* q = nullptr;
   dvm_status e = build_stack(st.data(), st.size(), g->stack_temporal, &q);
   for (dvm_program* p : st) delete p;

@@ -173,3 +173,27 @@ def test_stack_order_is_checked(ectx):
     g = dvm.Graph(ectx)
     assert L.lib.dvm_graph_set_stack_order(g.h, 2) == L.ERR_INVALID_ARG
     assert L.lib.dvm_graph_set_stack_order(g.h, 1) == 0
+
+
+def test_spatial_stack_orders_segments_by_work_per_workgroup(ectx):
+    """A spatial stack launches the segments with the most work per workgroup
+    first (bytes per tile times tiles per workgroup), so the launch ends on
+    its shortest workgroups; equal keys keep the program order."""
+    H_BLOCK_DIM, H_BODY_TILE, H_R_LO = 4, 5, 18
+    g = dvm.Graph(ectx)
+    g.set_stacking(7)
+    rows = (3000, 90000, 12000, 20000, 40000)   # all on the wide build
+    for r in rows:
+        layer_norm(g, r)
+    g.flush_launch()
+    (p,) = drain(g)
+    w = p.words()
+    assert w[S_NSEG] == len(rows)
+    segs = [w[S_DIR + 2 * i] for i in range(len(rows))]
+    got_rows = [w[o + H_R_LO] for o in segs]
+    assert sorted(got_rows) == sorted(rows)
+    # per-workgroup work of each segment, in launch order, never increases
+    work = [w[o + H_BODY_TILE] * (w[o + H_R_LO] * 5120 * 4 + 2 * 5120 * 4) / w[o + H_BLOCK_DIM] for o in segs]
+    assert all(a >= b for a, b in zip(work, work[1:])), list(zip(got_rows, work))
+    firsts = [w[S_DIR + 2 * i + 1] for i in range(len(rows))]
+    assert firsts == sorted(firsts) and firsts[0] == 0
